@@ -1,0 +1,365 @@
+// C ABI of libkvc: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued, so a call that
+// returns an error has touched no device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/kvc.h"
+#include "kvc_decode.h"
+#include "kvc_kernels.h"
+#include "kvc_laprox.h"
+
+namespace {
+
+constexpr int kHD = 128;
+constexpr int kTargetWorkgroups = 2048;   // split-K workgroups per launch to aim for
+constexpr int kMergeSplitsMax = 64;
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int ceil_div(int64_t a, int64_t b) { return int((a + b - 1) / b); }
+
+int validate_cache(const kvc_cache *c) {
+  if (!c || !c->k || !c->v || !c->pos || !c->len) return KVC_ERR_ARG;
+  if (c->dtype != KVC_BF16 && c->dtype != KVC_F32) return KVC_ERR_DTYPE;
+  if (c->head_dim != kHD) return KVC_ERR_UNSUPPORTED;
+  if (c->capacity <= 0 || c->n_scopes <= 0 || c->units_per_scope <= 0) return KVC_ERR_ARG;
+  if (c->scope_stride < 0 || c->unit_stride < 0) return KVC_ERR_ARG;
+  if (c->units_per_scope > 1 && c->unit_stride < c->capacity) return KVC_ERR_ARG;
+  if (c->n_scopes > 1 && c->scope_stride < int64_t(c->capacity)) return KVC_ERR_ARG;
+  if (!aligned16(c->k) || !aligned16(c->v)) return KVC_ERR_ALIGN;
+  return KVC_OK;
+}
+
+bool valid_G(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+// ------------------------------------------------------------ decode workspace
+struct DecodeLayout {
+  int n_splits, nsub_cap, merge_splits;
+  size_t status, counters, partM, partZ, partO, fac, subM, ews, flags, list, list2;
+  size_t merge_counters, merge_cos, merge_slot, total;
+};
+
+int split_count(int attn_units_total, int nsub) {
+  const int want = std::max(1, ceil_div(kTargetWorkgroups, attn_units_total));
+  return std::max(1, std::min(nsub, want));
+}
+
+DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
+  DecodeLayout d{};
+  const int CH = kvc::decode_chunk_tokens(c->dtype);
+  const int64_t nu = int64_t(c->n_scopes) * attn_units;
+  d.nsub_cap = ceil_div(c->capacity, CH);
+  d.n_splits = split_count(int(nu), d.nsub_cap);
+  d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
+  const int64_t cap = c->capacity;
+  size_t o = 0;
+  d.status = o;   o = align_up(o + 256);
+  d.counters = o; o = align_up(o + size_t(c->n_scopes) * 4);
+  d.merge_counters = o; o = align_up(o + size_t(c->n_scopes) * 4);
+  d.partM = o;    o = align_up(o + size_t(nu) * d.n_splits * G * 8);
+  d.partZ = o;    o = align_up(o + size_t(nu) * d.n_splits * G * 8);
+  d.partO = o;    o = align_up(o + size_t(nu) * d.n_splits * G * kHD * 4);
+  d.fac = o;      o = align_up(o + size_t(nu) * d.n_splits * G * 4);
+  d.subM = o;     o = align_up(o + size_t(nu) * d.nsub_cap * G * 8);
+  d.ews = o;      o = align_up(o + size_t(nu) * G * cap * 4);
+  d.flags = o;    o = align_up(o + size_t(c->n_scopes) * cap);
+  d.list = o;     o = align_up(o + size_t(c->n_scopes) * cap * 4);
+  d.list2 = o;    o = align_up(o + size_t(c->n_scopes) * cap * 4);
+  d.merge_cos = o;  o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 8);
+  d.merge_slot = o; o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 4);
+  d.total = o;
+  return d;
+}
+
+template <typename P>
+P *at(void *ws, size_t off) { return reinterpret_cast<P *>(static_cast<char *>(ws) + off); }
+
+kvc::CacheArgs cache_args(const kvc_cache *c) {
+  kvc::CacheArgs a{};
+  a.k = static_cast<char *>(c->k);
+  a.v = static_cast<char *>(c->v);
+  a.votes = c->votes;
+  a.pos = c->pos;
+  a.m = c->m;
+  a.len = c->len;
+  a.scope_stride = c->scope_stride;
+  a.unit_stride = c->unit_stride;
+  a.dtype = c->dtype;
+  a.capacity = c->capacity;
+  a.n_scopes = c->n_scopes;
+  a.units = c->units_per_scope;
+  return a;
+}
+
+int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t t, const void *q,
+               int32_t G, float scale, int mode, int rule, float alpha, int budget, int refresh,
+               float *out, float *lse, float *s, const kvc_moments *mom, const kvc_merge *merge,
+               uint8_t *evict_out, int attn_unit0, int attn_units, int32_t max_len, void *ws,
+               size_t ws_bytes, void *stream) {
+  int st = validate_cache(c);
+  if (st) return st;
+  if (!valid_G(G)) return KVC_ERR_UNSUPPORTED;
+  if (!q || !out || !lse) return KVC_ERR_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVC_ERR_ARG;
+  if (!aligned16(q) || (k_new && (!aligned16(k_new) || !aligned16(v_new)))) return KVC_ERR_ALIGN;
+  if (attn_units <= 0) {
+    attn_unit0 = 0;
+    attn_units = c->units_per_scope;
+  }
+  if (attn_unit0 < 0 || attn_unit0 + attn_units > c->units_per_scope) return KVC_ERR_ARG;
+  if (attn_units * G > 64) return KVC_ERR_UNSUPPORTED;
+  if (max_len > c->capacity) return KVC_ERR_CAPACITY;
+  if (max_len <= 0) max_len = c->capacity;
+  if (mode != 0) {
+    if (!c->m) return KVC_ERR_ARG;
+    if (budget < 0) return KVC_ERR_CAPACITY;
+    if (rule < KVC_RULE_SINGLE || rule > KVC_RULE_EMA) return KVC_ERR_ARG;
+    if (mom && (!mom->n || !mom->sk || !mom->sv || !mom->S)) return KVC_ERR_ARG;
+    if (merge) {
+      if (!merge->q || !aligned16(merge->q) || !valid_G(merge->G)) return KVC_ERR_ARG;
+      if (c->units_per_scope != 1 || mom) return KVC_ERR_UNSUPPORTED;
+    }
+  } else if (!c->m && k_new) {
+    return KVC_ERR_ARG;
+  }
+  if (!ws) return KVC_ERR_WORKSPACE;
+  const DecodeLayout d = decode_layout(c, G, attn_units);
+  if (ws_bytes < d.total) return KVC_ERR_WORKSPACE;
+
+  kvc::StepArgs a{};
+  a.k = static_cast<char *>(c->k);
+  a.v = static_cast<char *>(c->v);
+  a.votes = c->votes;
+  a.pos = c->pos;
+  a.m = c->m;
+  a.len = c->len;
+  a.scope_stride = c->scope_stride;
+  a.unit_stride = c->unit_stride;
+  a.capacity = c->capacity;
+  a.n_scopes = c->n_scopes;
+  a.units = c->units_per_scope;
+  a.attn_unit0 = attn_unit0;
+  a.attn_units = attn_units;
+  a.k_new = static_cast<const char *>(k_new);
+  a.v_new = static_cast<const char *>(v_new);
+  a.t = t;
+  a.append = k_new ? 1 : 0;
+  a.q = static_cast<const char *>(q);
+  a.scale = double(scale);
+  a.out = out;
+  a.lse = lse;
+  a.s = s;
+  a.mode = (mode != 0 && merge) ? 2 : mode;
+  a.rule = rule;
+  a.budget = budget;
+  a.refresh = mode == 0 ? 1 : (refresh ? 1 : 0);
+  a.alpha = alpha;
+  if (mom) {
+    a.mom_n = mom->n;
+    a.mom_sk = mom->sk;
+    a.mom_sv = mom->sv;
+    a.mom_S = mom->S;
+  }
+  a.evict_out = evict_out;
+  a.status = at<int32_t>(ws, d.status);
+  a.counters = at<int32_t>(ws, d.counters);
+  a.partM = at<double>(ws, d.partM);
+  a.partZ = at<double>(ws, d.partZ);
+  a.partO = at<float>(ws, d.partO);
+  a.fac = at<float>(ws, d.fac);
+  a.subM = at<double>(ws, d.subM);
+  a.ews = at<float>(ws, d.ews);
+  a.flags = at<uint8_t>(ws, d.flags);
+  a.list = at<int32_t>(ws, d.list);
+  a.list2 = at<int32_t>(ws, d.list2);
+  a.nsub_cap = d.nsub_cap;
+  const int CH = kvc::decode_chunk_tokens(c->dtype);
+  a.n_splits = split_count(c->n_scopes * attn_units, ceil_div(max_len, CH));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (kvc::launch_decode(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  if (a.mode == 2) {
+    kvc::MergeArgs mg{};
+    mg.q = static_cast<const char *>(merge->q);
+    mg.G = merge->G;
+    mg.scale = double(merge->scale);
+    mg.eps = merge->eps;
+    mg.n_splits = d.merge_splits;
+    mg.counters = at<int32_t>(ws, d.merge_counters);
+    mg.part_cos = at<double>(ws, d.merge_cos);
+    mg.part_slot = at<int32_t>(ws, d.merge_slot);
+    if (kvc::launch_merge(cache_args(c), a.flags, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  }
+  return KVC_OK;
+}
+
+// ------------------------------------------------------------ compact workspace
+struct CompactLayout {
+  int merge_splits;
+  size_t holes, counters, cos, slot, total;
+};
+
+CompactLayout compact_layout(const kvc_cache *c) {
+  CompactLayout l{};
+  l.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
+  size_t o = 0;
+  l.counters = o; o = align_up(o + size_t(c->n_scopes) * 4);
+  l.holes = o;    o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
+  l.cos = o;      o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 8);
+  l.slot = o;     o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 4);
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvc_version(void) { return KVC_VERSION; }
+
+const char *kvc_status_string(int32_t s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_ARG: return "invalid argument";
+    case KVC_ERR_DTYPE: return "unsupported dtype";
+    case KVC_ERR_UNSUPPORTED: return "unsupported shape";
+    case KVC_ERR_CAPACITY: return "capacity exceeded";
+    case KVC_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KVC_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVC_ERR_DEVICE: return "device launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t kvc_decode_workspace_size(const kvc_cache *cache, int32_t G, int32_t max_len) {
+  (void)max_len;
+  if (validate_cache(cache) || !valid_G(G)) return 0;
+  return decode_layout(cache, G, cache->units_per_scope).total;
+}
+
+size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity) {
+  (void)n_scopes;
+  (void)capacity;
+  return align_up(kvc::wide_state_bytes());
+}
+
+size_t kvc_compact_workspace_size(const kvc_cache *cache) {
+  if (validate_cache(cache)) return 0;
+  return compact_layout(cache).total;
+}
+
+int32_t kvc_workspace_status(void *ws, void *stream) {
+  if (!ws) return KVC_ERR_ARG;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(hs) != hipSuccess) return KVC_ERR_DEVICE;
+  int32_t v = 0;
+  if (hipMemcpy(&v, ws, 4, hipMemcpyDeviceToHost) != hipSuccess) return KVC_ERR_DEVICE;
+  if (v != 0) {
+    const int32_t zero = 0;
+    if (hipMemcpy(ws, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return KVC_ERR_DEVICE;
+  }
+  return v;
+}
+
+int32_t kvc_decode_attn_score(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,
+                              const void *q, int32_t G, float scale, float *out, float *lse, float *s,
+                              int32_t max_len, void *ws, size_t ws_bytes, void *stream) {
+  return run_decode(cache, k_new, v_new, t, q, G, scale, 0, 0, 0.f, 0, 1, out, lse, s, nullptr, nullptr,
+                    nullptr, 0, 0, max_len, ws, ws_bytes, stream);
+}
+
+int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,
+                        const void *q, int32_t G, float scale, int32_t rule, float alpha,
+                        int32_t budget, int32_t refresh, float *out, float *lse, float *s,
+                        const kvc_moments *mom, const kvc_merge *merge, uint8_t *evict_out,
+                        int32_t attn_unit0, int32_t attn_units, int32_t max_len, void *ws,
+                        size_t ws_bytes, void *stream) {
+  return run_decode(cache, k_new, v_new, t, q, G, scale, 1, rule, alpha, budget, refresh, out, lse, s,
+                    mom, merge, evict_out, attn_unit0, attn_units, max_len, ws, ws_bytes, stream);
+}
+
+int32_t kvc_ema_update(float *m, const float *s, const int32_t *len, int32_t n_scopes, int32_t capacity,
+                       int32_t rule, float alpha, void *stream) {
+  if (!m || !s || !len || n_scopes <= 0 || capacity <= 0) return KVC_ERR_ARG;
+  if (rule < KVC_RULE_SINGLE || rule > KVC_RULE_EMA) return KVC_ERR_ARG;
+  if (kvc::launch_ema_update(m, s, len, n_scopes, capacity, rule, alpha, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *len, int32_t n_scopes,
+                         int32_t capacity, int32_t budget, uint8_t *evict, int32_t *n_evict, void *ws,
+                         size_t ws_bytes, void *stream) {
+  if (!key || !evict || n_scopes <= 0 || capacity <= 0) return KVC_ERR_ARG;
+  if (budget < 0) return KVC_ERR_CAPACITY;
+  if (!ws || ws_bytes < kvc_select_workspace_size(n_scopes, capacity)) return KVC_ERR_WORKSPACE;
+  if (kvc::launch_select(key, pos, len, n_scopes, capacity, budget, evict, n_evict, ws,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kvc_moments *mom,
+                          void *stream) {
+  int st = validate_cache(cache);
+  if (st) return st;
+  if (!evict || !mom || !mom->n || !mom->sk || !mom->sv || !mom->S) return KVC_ERR_ARG;
+  if (kvc::launch_moment_update(cache_args(cache), evict, mom->n, mom->sk, mom->sv, mom->S,
+                                static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merge *merge, void *ws,
+                    size_t ws_bytes, void *stream) {
+  int st = validate_cache(cache);
+  if (st) return st;
+  if (!evict) return KVC_ERR_ARG;
+  if (!ws) return KVC_ERR_WORKSPACE;
+  const CompactLayout l = compact_layout(cache);
+  if (ws_bytes < l.total) return KVC_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (merge) {
+    if (!merge->q || !aligned16(merge->q) || !valid_G(merge->G)) return KVC_ERR_ARG;
+    if (cache->units_per_scope != 1) return KVC_ERR_UNSUPPORTED;
+    kvc::MergeArgs mg{};
+    mg.q = static_cast<const char *>(merge->q);
+    mg.G = merge->G;
+    mg.scale = double(merge->scale);
+    mg.eps = merge->eps;
+    mg.n_splits = l.merge_splits;
+    mg.counters = at<int32_t>(ws, l.counters);
+    mg.part_cos = at<double>(ws, l.cos);
+    mg.part_slot = at<int32_t>(ws, l.slot);
+    if (kvc::launch_merge(cache_args(cache), evict, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;
+    return KVC_OK;
+  }
+  if (kvc::launch_compact(cache_args(cache), evict, at<int32_t>(ws, l.holes), hs) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w, int32_t d,
+                                 int32_t D) {
+  return kvc::laprox_workspace_bytes(n_layers, H, n_kv, N, w, d, D);
+}
+
+int32_t kvc_laprox_score(const void *q_win, const void *k, const void *v, const void *w_o, int32_t n_layers,
+                         int32_t H, int32_t n_kv, int32_t N, int32_t w, int32_t d, int32_t D, float scale,
+                         float *score, void *ws, size_t ws_bytes, void *stream) {
+  if (!q_win || !k || !v || !w_o || !score) return KVC_ERR_ARG;
+  if (n_layers <= 0 || H <= 0 || n_kv <= 0 || N <= 0 || w <= 0 || D <= 0) return KVC_ERR_ARG;
+  if (d != kHD || H % n_kv != 0 || !valid_G(H / n_kv) || w > N) return KVC_ERR_UNSUPPORTED;
+  if (D % 128 != 0 || w > 64) return KVC_ERR_UNSUPPORTED;
+  if (!aligned16(q_win) || !aligned16(k) || !aligned16(v) || !aligned16(w_o)) return KVC_ERR_ALIGN;
+  if (!ws || ws_bytes < kvc::laprox_workspace_bytes(n_layers, H, n_kv, N, w, d, D)) return KVC_ERR_WORKSPACE;
+  if (kvc::launch_laprox(q_win, k, v, w_o, n_layers, H, n_kv, N, w, D, double(scale), score, ws,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// Device-side helpers shared by the kvc kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int HD = 128;      // head dimension handled by every kernel
+constexpr int WG = 256;      // threads per workgroup (4 waves of 64)
+
+struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+
+// ---------------------------------------------------------------- element types
+// Storage types of K/V/q: bf16 is carried as its 16-bit pattern.
+struct bf16_t { uint16_t b; };
+
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<bf16_t> {
+  static constexpr int EPV = 8;                   // elements per 16-byte vector
+  __device__ static __forceinline__ float get(const u32x4 &v, int j) {
+    uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
+    return (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+template <> struct ElemTraits<float> {
+  static constexpr int EPV = 4;
+  __device__ static __forceinline__ float get(const u32x4 &v, int j) {
+    uint32_t w = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+    return __uint_as_float(w);
+  }
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_elem(const T *p, int64_t i);
+template <> __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p, int64_t i) {
+  return bf16_to_f32(p[i].b);
+}
+template <> __device__ __forceinline__ float load_elem<float>(const float *p, int64_t i) { return p[i]; }
+
+template <typename T> __device__ __forceinline__ void store_elem(T *p, int64_t i, float x);
+template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_t i, float x) {
+  p[i].b = f32_to_bf16(x);
+}
+template <> __device__ __forceinline__ void store_elem<float>(float *p, int64_t i, float x) { p[i] = x; }
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// ---------------------------------------------------------------- cross-lane
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  int lo = __double2loint(x), hi = __double2hiint(x);
+  lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xf, 0xf, false);
+  hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over aligned groups of LANES lanes (16 or 32); every lane gets its group's sum.
+template <int LANES>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_f64<0x141>(x);   // row_half_mirror: pairs the two quads of each half-row
+  x += dpp_f64<0x140>(x);   // row_mirror: pairs the two halves of each 16-lane row
+  if constexpr (LANES == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// Reductions over lanes whose index differs only in bits >= log2(STRIDE) (STRIDE a power of 2).
+template <int STRIDE>
+__device__ __forceinline__ double wave_max_strided(double x) {
+#pragma unroll
+  for (int o = STRIDE; o < 64; o <<= 1) x = fmax(x, __shfl_xor(x, o));
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ double wave_sum_strided(double x) {
+#pragma unroll
+  for (int o = STRIDE; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ float wave_sum_strided_f32(float x) {
+#pragma unroll
+  for (int o = STRIDE; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int o) {
+  uint32_t lo = uint32_t(x), hi = uint32_t(x >> 32);
+  lo = __shfl_xor(lo, o);
+  hi = __shfl_xor(hi, o);
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint64_t y = shfl_xor_u64(x, o);
+    x = y < x ? y : x;
+  }
+  return x;
+}
+
+// Exclusive prefix count of a 0/1 predicate within the wave, and the wave total.
+__device__ __forceinline__ int wave_prefix_count(bool pred, int *total) {
+  uint64_t b = __ballot(pred);
+  *total = __popcll(b);
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), 0));
+}
+
+// ---------------------------------------------------------------- numerics
+// exp(x) for x in float64 to about one float32 ulp: x = hi + lo with hi the
+// nearest float; exp(hi) from the accurate float exp, times (1 + lo).
+__device__ __forceinline__ float exp_split(double x) {
+  if (!(x > -1.0e30)) return 0.0f;
+  float hi = float(x);
+  float lo = float(x - double(hi));
+  float eh = expf(hi);
+  return fmaf(eh, lo, eh);
+}
+
+// Total order key of (value, position): float bits mapped to an order-preserving
+// unsigned integer (-0 folded onto +0), position in the low 32 bits.
+__device__ __forceinline__ uint32_t orderable_f32(float f) {
+  uint32_t b = __float_as_uint(f);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t order_key(float value, uint32_t pos) {
+  return (uint64_t(orderable_f32(value)) << 32) | pos;
+}
+
+// ---------------------------------------------------------------- memory model
+// Release this thread's global writes to every workgroup on the device.
+__device__ __forceinline__ void release_device() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_device() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Workgroup-wide exclusive scan of small non-negative ints; returns this
+// thread's exclusive prefix and writes the total to *total. `red` is LDS of >= 4 ints.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int *red, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < WG / 64; ++w) {
+    int r = red[w];
+    if (w < wave) off += r;
+    tot += r;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
+}
+
+}  // namespace kvc

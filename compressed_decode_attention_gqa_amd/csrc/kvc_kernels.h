@@ -1,0 +1,40 @@
+// Launch arguments and launchers of the standalone entry-point kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+struct CacheArgs {
+  char *k, *v;
+  int32_t *votes, *pos;
+  float *m;
+  int32_t *len;
+  int64_t scope_stride, unit_stride;
+  int32_t dtype, capacity, n_scopes, units;
+};
+
+struct MergeArgs {
+  const char *q;
+  int32_t G;
+  double scale;
+  float eps;
+  int32_t n_splits;
+  int32_t *counters;
+  double *part_cos;
+  int32_t *part_slot;
+};
+
+size_t wide_state_bytes();
+hipError_t launch_select(const float *key, const int32_t *pos, const int32_t *len, int n_scopes,
+                         int cap, int budget, uint8_t *evict, int32_t *n_evict, void *ws,
+                         hipStream_t st);
+hipError_t launch_moment_update(const CacheArgs &c, const uint8_t *evict, int32_t *n, float *sk,
+                                float *sv, float *S, hipStream_t st);
+hipError_t launch_compact(const CacheArgs &c, const uint8_t *evict, int32_t *holes, hipStream_t st);
+hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st);
+hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
+                             int rule, float alpha, hipStream_t st);
+
+}  // namespace kvc

@@ -1,0 +1,15 @@
+// LaProx prefill scoring: launch interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvc {
+
+size_t laprox_workspace_bytes(int n_layers, int H, int n_kv, int N, int w, int d, int D);
+hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const void *w_o, int n_layers,
+                         int H, int n_kv, int N, int w, int D, double scale, float *score, void *ws,
+                         hipStream_t st);
+
+}  // namespace kvc

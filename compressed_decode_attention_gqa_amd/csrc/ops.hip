@@ -1,0 +1,416 @@
+// Standalone entry-point kernels: utility update, selection (per scope and
+// device-wide), moment fold, compaction and KeepKV ZIP merging.
+#include "kvc_ops.h"
+#include "kvc_kernels.h"
+
+namespace kvc {
+
+// ------------------------------------------------------------ utility update
+// InertiaKV §3.1 eqs. (2)-(4).
+__global__ __launch_bounds__(WG) void k_ema_update(float *m, const float *s, const int32_t *len,
+                                                  int cap, int rule, float alpha) {
+  const int scope = blockIdx.y;
+  const int i = blockIdx.x * WG + threadIdx.x;
+  const int L = len[scope];
+  if (i >= L || i >= cap) return;
+  const int64_t o = int64_t(scope) * cap + i;
+  const double sv = s[o], mo = m[o], al = alpha;
+  double r;
+  if (rule == 0) r = sv;
+  else if (rule == 1) r = mo + sv;
+  else r = al * mo + (1.0 - al) * sv;
+  m[o] = float(r);
+}
+
+// ------------------------------------------------------------ selection (one workgroup per scope)
+__global__ __launch_bounds__(WG) void k_select(const float *key, const int32_t *pos,
+                                              const int32_t *len, int cap, int budget,
+                                              uint8_t *evict, int32_t *n_evict) {
+  __shared__ SelectLds sh;
+  const int scope = blockIdx.x, tid = threadIdx.x;
+  const int64_t so = int64_t(scope) * cap;
+  const int n = len ? min(len[scope], cap) : cap;
+  const int k = max(0, n - budget);
+  const float *kk = key + so;
+  const int32_t *pp = pos ? pos + so : nullptr;
+  auto kf = [&](int i) -> uint64_t { return order_key(kk[i], pp ? uint32_t(pp[i]) : uint32_t(i)); };
+  if (k == 0) {
+    for (int i = tid; i < n; i += WG) evict[so + i] = 0;
+  } else if (k == 1) {
+    uint64_t best = ~0ull;
+    int slot = 0x7fffffff;
+    for (int i = tid; i < n; i += WG) {
+      const uint64_t x = kf(i);
+      if (x < best) {
+        best = x;
+        slot = i;
+      }
+    }
+    const int e = wg_argmin_finish(best, slot, sh);
+    for (int i = tid; i < n; i += WG) evict[so + i] = (i == e);
+  } else {
+    const SelectCut cut = wg_select_cut(kf, n, k, sh);
+    wg_apply_cut(kf, n, cut, evict + so, nullptr, nullptr, sh);
+  }
+  if (tid == 0 && n_evict) n_evict[scope] = k;
+}
+
+// ------------------------------------------------------------ selection (device-wide, one scope)
+// Radix select over n keys spread across many workgroups: per pass a global
+// 256-bin histogram of the keys matching the current prefix, then one
+// workgroup picks the digit. Keys must be distinct (distinct positions).
+struct WideState {
+  uint64_t prefix, mask;
+  int32_t krem, done, k, pad;
+  uint32_t hist[256];
+};
+
+__device__ __forceinline__ uint64_t wide_key(const float *key, const int32_t *pos, int64_t i) {
+  return order_key(key[i], pos ? uint32_t(pos[i]) : uint32_t(i));
+}
+
+__global__ __launch_bounds__(WG) void k_wide_hist(const float *key, const int32_t *pos, int64_t n,
+                                                 WideState *st, int shift) {
+  __shared__ uint32_t hist[256];
+  if (st->done) return;
+  hist[threadIdx.x] = 0;
+  __syncthreads();
+  const uint64_t prefix = st->prefix, mask = st->mask;
+  for (int64_t i = int64_t(blockIdx.x) * WG + threadIdx.x; i < n; i += int64_t(gridDim.x) * WG) {
+    const uint64_t kk = wide_key(key, pos, i);
+    if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  const uint32_t c = hist[threadIdx.x];
+  if (c) atomicAdd(&st->hist[threadIdx.x], c);
+}
+
+__global__ __launch_bounds__(WG) void k_wide_pick(WideState *st, int shift) {
+  __shared__ int red[8];
+  if (st->done) return;
+  const int tid = threadIdx.x;
+  const int c = int(st->hist[tid]);
+  int tot;
+  const int excl = wg_exclusive_scan(c, red, &tot);
+  const int krem = st->krem;
+  __syncthreads();
+  if (excl < krem && krem <= excl + c) {
+    st->prefix |= uint64_t(tid) << shift;
+    st->mask |= uint64_t(255) << shift;
+    st->krem = krem - excl;
+    if (c == krem - excl || shift == 0) st->done = 1;
+  }
+  __syncthreads();
+  st->hist[tid] = 0;
+}
+
+__global__ __launch_bounds__(WG) void k_wide_flags(const float *key, const int32_t *pos, int64_t n,
+                                                  const WideState *st, uint8_t *evict) {
+  const uint64_t thr = st->prefix, mask = st->mask;
+  for (int64_t i = int64_t(blockIdx.x) * WG + threadIdx.x; i < n; i += int64_t(gridDim.x) * WG)
+    evict[i] = (wide_key(key, pos, i) & mask) <= thr;
+}
+
+__global__ void k_wide_init(WideState *st, int k, int32_t *n_evict) {
+  if (threadIdx.x == 0) {
+    st->prefix = 0;
+    st->mask = 0;
+    st->krem = k;
+    st->k = k;
+    st->done = k == 0 ? 1 : 0;
+    if (n_evict) *n_evict = k;
+  }
+  st->hist[threadIdx.x] = 0;
+}
+
+__global__ void k_wide_clear(int64_t n, uint8_t *evict) {
+  for (int64_t i = int64_t(blockIdx.x) * WG + threadIdx.x; i < n; i += int64_t(gridDim.x) * WG) evict[i] = 0;
+}
+
+size_t wide_state_bytes() { return sizeof(WideState); }
+
+hipError_t launch_select(const float *key, const int32_t *pos, const int32_t *len, int n_scopes,
+                         int cap, int budget, uint8_t *evict, int32_t *n_evict, void *ws,
+                         hipStream_t st) {
+  if (n_scopes == 1 && len == nullptr && cap > (1 << 20)) {
+    WideState *w = reinterpret_cast<WideState *>(ws);
+    const int k = max(0, cap - budget);
+    const int grid = 2048;
+    hipLaunchKernelGGL(k_wide_init, dim3(1), dim3(256), 0, st, w, k, n_evict);
+    if (k == 0) {
+      hipLaunchKernelGGL(k_wide_clear, dim3(grid), dim3(WG), 0, st, int64_t(cap), evict);
+      return hipGetLastError();
+    }
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      hipLaunchKernelGGL(k_wide_hist, dim3(grid), dim3(WG), 0, st, key, pos, int64_t(cap), w, shift);
+      hipLaunchKernelGGL(k_wide_pick, dim3(1), dim3(WG), 0, st, w, shift);
+    }
+    hipLaunchKernelGGL(k_wide_flags, dim3(grid), dim3(WG), 0, st, key, pos, int64_t(cap), w, evict);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_select, dim3(n_scopes), dim3(WG), 0, st, key, pos, len, cap, budget, evict, n_evict);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ moment fold
+template <typename T>
+__global__ __launch_bounds__(WG) void k_moment_update(CacheArgs c, const uint8_t *evict, int32_t *n,
+                                                     float *sk, float *sv, float *S) {
+  __shared__ FoldLds sh;
+  const int scope = blockIdx.x / c.units, u = blockIdx.x - (blockIdx.x / c.units) * c.units;
+  const int L = c.len[scope];
+  const int64_t row0 = int64_t(scope) * c.scope_stride + int64_t(u) * c.unit_stride;
+  const T *Kb = reinterpret_cast<const T *>(c.k) + row0 * HD;
+  const T *Vb = reinterpret_cast<const T *>(c.v) + row0 * HD;
+  const int64_t mu = blockIdx.x;
+  fold_flagged<T>(Kb, Vb, evict + int64_t(scope) * c.capacity, L, n + mu, sk + mu * HD, sv + mu * HD,
+                  S + mu * HD * HD, sh);
+}
+
+hipError_t launch_moment_update(const CacheArgs &c, const uint8_t *evict, int32_t *n, float *sk,
+                                float *sv, float *S, hipStream_t st) {
+  dim3 grid(c.n_scopes * c.units);
+  if (c.dtype == 0) hipLaunchKernelGGL(k_moment_update<bf16_t>, grid, dim3(WG), 0, st, c, evict, n, sk, sv, S);
+  else hipLaunchKernelGGL(k_moment_update<float>, grid, dim3(WG), 0, st, c, evict, n, sk, sv, S);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ compaction (drop)
+__global__ __launch_bounds__(WG) void k_compact(CacheArgs c, const uint8_t *evict, int32_t *holes) {
+  __shared__ int red[8];
+  const int scope = blockIdx.x, tid = threadIdx.x;
+  const int64_t so = int64_t(scope) * c.capacity;
+  const int L = c.len[scope];
+  int k = 0;
+  for (int base = 0; base < L; base += WG) {
+    const int i = base + tid;
+    int tot;
+    wg_exclusive_scan((i < L && evict[so + i]) ? 1 : 0, red, &tot);
+    k += tot;
+  }
+  if (k == 0) return;
+  ScopeRows rows{c.k, c.v, int64_t(scope) * c.scope_stride, c.unit_stride, c.units,
+                 HD * (c.dtype == 0 ? 2 : 4), c.votes ? c.votes + so : nullptr, c.pos + so, c.m ? c.m + so : nullptr};
+  wg_compact_flags(rows, evict + so, L, k, holes + so, red);
+  if (tid == 0) c.len[scope] = L - k;
+}
+
+hipError_t launch_compact(const CacheArgs &c, const uint8_t *evict, int32_t *holes, hipStream_t st) {
+  hipLaunchKernelGGL(k_compact, dim3(c.n_scopes), dim3(WG), 0, st, c, evict, holes);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ ZIP merge
+// KeepKV eqs. (7)-(12): the single flagged entry e of each scope is merged into
+// its live partner c of largest cos(k_e, k_c) (ties to the lower position),
+// then dropped. Split kernel: partial argmax of the cosine over token ranges;
+// the last workgroup of the scope merges and compacts.
+struct MergeLds {
+  double ke[HD];
+  double best_cos[4];
+  int best_slot[4];
+  int red[8];
+  int e;
+  int last;
+  double lbar[2];
+  double wgt[4];
+};
+
+__device__ __forceinline__ bool cos_better(double c1, int p1, double c2, int p2) {
+  return c1 > c2 || (c1 == c2 && p1 < p2);
+}
+
+template <typename T>
+__global__ __launch_bounds__(WG) void k_merge(CacheArgs c, const uint8_t *evict, MergeArgs mg) {
+  __shared__ MergeLds sh;
+  constexpr int EPV = ElemTraits<T>::EPV, LPT = HD / EPV, TPI = 64 / LPT;
+  const int scope = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t so = int64_t(scope) * c.capacity;
+  const int L = c.len[scope];
+  const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
+  const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
+
+  // the flagged entry (exactly one per scope)
+  if (tid == 0) sh.e = -1;
+  __syncthreads();
+  for (int i = tid; i < L; i += WG)
+    if (evict[so + i]) atomicMax(&sh.e, i);
+  __syncthreads();
+  const int e = sh.e;
+  if (e < 0) {
+    // nothing flagged: still take part in the scope counter
+  } else if (tid < HD) {
+    sh.ke[tid] = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
+  }
+  __syncthreads();
+
+  double best = -INFINITY;
+  int bslot = -1, bpos = 0x7fffffff;
+  if (e >= 0) {
+    const int cb = lane % LPT, tg = lane / LPT;
+    double ke[EPV];
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) ke[j] = sh.ke[cb * EPV + j];
+    double ne = 0.0;
+    for (int j = 0; j < HD; ++j) ne += sh.ke[j] * sh.ke[j];
+    ne = sqrt(ne);
+    const int per = (L + gridDim.x - 1) / gridDim.x;
+    const int t0 = blockIdx.x * per, t1 = min(L, t0 + per);
+    for (int tok0 = t0 + wave * TPI; tok0 < t1; tok0 += 4 * TPI) {
+      const int tok = tok0 + tg;
+      double dot = 0.0, nn = 0.0;
+      if (tok < t1) {
+        const u32x4 kv = ld16(reinterpret_cast<const char *>(Kb + int64_t(tok) * HD) + 16 * cb);
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) {
+          const double x = double(ElemTraits<T>::get(kv, j));
+          dot = fma(ke[j], x, dot);
+          nn = fma(x, x, nn);
+        }
+      }
+      dot = group_sum_f64<LPT>(dot);
+      nn = group_sum_f64<LPT>(nn);
+      if (cb == 0 && tok < t1 && tok != e) {
+        const double den = ne * sqrt(nn);
+        const double cs = den > 0.0 ? dot / den : 0.0;
+        const int p = c.pos[so + tok];
+        if (cos_better(cs, p, best, bpos)) {
+          best = cs;
+          bslot = tok;
+          bpos = p;
+        }
+      }
+    }
+  }
+  // workgroup argmax
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double b2 = __shfl_xor(best, o);
+    const int s2 = __shfl_xor(bslot, o), p2 = __shfl_xor(bpos, o);
+    if (s2 >= 0 && (bslot < 0 || cos_better(b2, p2, best, bpos))) {
+      best = b2;
+      bslot = s2;
+      bpos = p2;
+    }
+  }
+  if (lane == 0) {
+    sh.best_cos[wave] = best;
+    sh.best_slot[wave] = bslot;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double b = -INFINITY;
+    int s = -1, p = 0x7fffffff;
+    for (int w = 0; w < 4; ++w) {
+      const int sw = sh.best_slot[w];
+      if (sw < 0) continue;
+      const int pw = c.pos[so + sw];
+      if (s < 0 || cos_better(sh.best_cos[w], pw, b, p)) {
+        b = sh.best_cos[w];
+        s = sw;
+        p = pw;
+      }
+    }
+    const int64_t pi = int64_t(scope) * gridDim.x + blockIdx.x;
+    mg.part_cos[pi] = b;
+    mg.part_slot[pi] = s;
+    release_device();
+    const int prev = atomicAdd(mg.counters + scope, 1);
+    sh.last = prev == int(gridDim.x) - 1;
+  }
+  __syncthreads();
+  if (!sh.last) return;
+  acquire_device();
+  if (tid == 0) mg.counters[scope] = 0;
+  if (e < 0) return;
+  if (tid == 0) {
+    double b = -INFINITY;
+    int s = -1, p = 0x7fffffff;
+    for (int sp = 0; sp < int(gridDim.x); ++sp) {
+      const int64_t pi = int64_t(scope) * gridDim.x + sp;
+      const int sw = mg.part_slot[pi];
+      if (sw < 0) continue;
+      const int pw = c.pos[so + sw];
+      if (s < 0 || cos_better(mg.part_cos[pi], pw, b, p)) {
+        b = mg.part_cos[pi];
+        s = sw;
+        p = pw;
+      }
+    }
+    sh.best_slot[0] = s;
+  }
+  __syncthreads();
+  const int cs = sh.best_slot[0];
+  if (cs < 0) return;   // a single live entry: nothing to merge into
+
+  // reference logits: mean over the G query heads of scale * q_g . k
+  if (wave < 2) {
+    const int x = wave == 0 ? e : cs;
+    const T *q = reinterpret_cast<const T *>(mg.q) + int64_t(scope) * mg.G * HD;
+    double acc = 0.0;
+    for (int j = lane; j < HD; j += 64) {
+      const double kx = double(load_elem<T>(Kb, int64_t(x) * HD + j));
+      double qs = 0.0;
+      for (int g = 0; g < mg.G; ++g) qs += double(load_elem<T>(q, g * HD + j)) * kx;
+      acc += qs;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) sh.lbar[wave] = acc * mg.scale / double(mg.G);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double le = sh.lbar[0], lc = sh.lbar[1];
+    const double mu = fmax(le, lc);
+    const double pe = c.votes ? double(c.votes[so + e]) : 1.0;
+    const double pc = c.votes ? double(c.votes[so + cs]) : 1.0;
+    const double we = pe * exp(le - mu), wc = pc * exp(lc - mu);
+    const double num = mu + log(we + wc) - log(pe + pc);
+    const double den = we * le + wc * lc;
+    const bool guarded = fabs(den) < double(mg.eps) * exp(-mu);
+    sh.wgt[0] = we / (we + wc);
+    sh.wgt[1] = wc / (we + wc);
+    sh.wgt[2] = guarded ? 0.5 : we * num / den;
+    sh.wgt[3] = guarded ? 0.5 : wc * num / den;
+  }
+  __syncthreads();
+  if (tid < HD) {   // each thread reads and rewrites only element tid of the two rows
+    T *Kw = reinterpret_cast<T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
+    T *Vw = reinterpret_cast<T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
+    const double kek = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
+    const double kck = double(load_elem<T>(Kb, int64_t(cs) * HD + tid));
+    const double vek = double(load_elem<T>(Vb, int64_t(e) * HD + tid));
+    const double vck = double(load_elem<T>(Vb, int64_t(cs) * HD + tid));
+    store_elem<T>(Kw, int64_t(cs) * HD + tid, float(sh.wgt[2] * kek + sh.wgt[3] * kck));
+    store_elem<T>(Vw, int64_t(cs) * HD + tid, float(sh.wgt[0] * vek + sh.wgt[1] * vck));
+  }
+  if (tid == 0) {
+    if (c.votes) c.votes[so + cs] = c.votes[so + e] + c.votes[so + cs];
+    if (c.m) c.m[so + cs] = c.m[so + cs] + c.m[so + e];
+  }
+  __threadfence_block();
+  __syncthreads();
+  // drop e: the last live slot fills its hole
+  ScopeRows rows{c.k, c.v, int64_t(scope) * c.scope_stride, c.unit_stride, 1,
+                 HD * int(sizeof(T)), c.votes ? c.votes + so : nullptr, c.pos + so, c.m ? c.m + so : nullptr};
+  if (e < L - 1) move_slot_wg(rows, L - 1, e);
+  if (tid == 0) c.len[scope] = L - 1;
+}
+
+hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st) {
+  dim3 grid(mg.n_splits, c.n_scopes);
+  if (c.dtype == 0) hipLaunchKernelGGL(k_merge<bf16_t>, grid, dim3(WG), 0, st, c, evict, mg);
+  else hipLaunchKernelGGL(k_merge<float>, grid, dim3(WG), 0, st, c, evict, mg);
+  return hipGetLastError();
+}
+
+}  // namespace kvc
+
+namespace kvc {
+hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
+                             int rule, float alpha, hipStream_t st) {
+  dim3 grid((cap + WG - 1) / WG, n_scopes);
+  hipLaunchKernelGGL(k_ema_update, grid, dim3(WG), 0, st, m, s, len, cap, rule, alpha);
+  return hipGetLastError();
+}
+}  // namespace kvc

@@ -1,0 +1,237 @@
+/*
+ * kvc.h -- fixed-budget KV-cache decode step (attend, score, aggregate, select,
+ * fold, compact) and LaProx prefill scoring, as hand-written HIP for MI355X
+ * (gfx950). C ABI: plain pointers and sizes, no C++ or torch types.
+ *
+ * Sources (the pages these operations are defined on):
+ *   MomentKV  -- "MOMENTKV: Closing the Directional Gap in KV Cache Eviction for
+ *                Long-Context Inference" (summary page): moment statistics §4.1,
+ *                Algorithm 1, Appendix A.1.
+ *   InertiaKV -- "Key factors of KV cache eviction under aggressive decoding:
+ *                temporal aggregation and rank preservation" (translated
+ *                article): per-token score §3.1 eq. (1), utility rules eqs. (2)-(4),
+ *                budget §3.
+ *   KeepKV    -- reading notes on "KeepKV: Achieving Periodic Lossless KV Cache
+ *                Compression": attention eq. (1), votes eqs. (6)-(7), ZIP merge
+ *                eqs. (8)-(12), numerical-stability guard, framework integration.
+ *   LaProx    -- notes on "Reformulating KV Cache Eviction Problem for
+ *                Long-Context LLM Inference": key designs 1-3, GQA paragraph.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership. Every array argument is DEVICE memory owned by the caller. The
+ *   library allocates nothing and keeps no state between calls; scratch lives
+ *   in a caller-provided workspace sized by the *_workspace_size helpers.
+ * Streams. `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *   Calls only enqueue work; results are ready when the stream reaches them.
+ * Errors. Each call returns KVC_OK (0) or a negative KVC_ERR_* code after
+ *   validating its host-visible arguments; a call that returns an error has
+ *   enqueued nothing. Conditions only the device can see (a live length that
+ *   exceeds the capacity) are recorded in the workspace status word, readable
+ *   with kvc_workspace_status().
+ * Units and scopes. A unit is one KV head of one layer of one sequence. A
+ *   scope is the set of units that share one slot set: votes, positions,
+ *   utilities and the live length are per scope; K and V rows are per unit.
+ *   Row r of a unit's K (or V) is at element offset (row_base + r) * head_dim,
+ *   with row_base = scope * scope_stride + unit * unit_stride.
+ * GQA. Query head h of a layer reads KV head h / G (consecutive grouping);
+ *   queries are laid out [scope][unit][G][head_dim].
+ * Head dimension. head_dim must be 128 (KVC_ERR_UNSUPPORTED otherwise).
+ * Alignment. K, V, q and new-row pointers must be 16-byte aligned (KVC_ERR_ALIGN).
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_VERSION 1
+
+enum kvc_status {
+  KVC_OK = 0,
+  KVC_ERR_ARG = -1,          /* null pointer, negative size, inconsistent sizes */
+  KVC_ERR_DTYPE = -2,        /* dtype is not KVC_BF16 / KVC_F32 */
+  KVC_ERR_UNSUPPORTED = -3,  /* head_dim != 128, G not in {1,2,4,8}, shape beyond limits */
+  KVC_ERR_CAPACITY = -4,     /* append into a full cache, max_len > capacity, budget < 0 */
+  KVC_ERR_ALIGN = -5,        /* K/V/q/new rows not 16-byte aligned */
+  KVC_ERR_WORKSPACE = -6,    /* workspace missing or smaller than required */
+  KVC_ERR_DEVICE = -7        /* HIP launch failure */
+};
+
+enum kvc_dtype { KVC_BF16 = 0, KVC_F32 = 1 };
+
+/* InertiaKV §3.1, eqs. (2)-(4). */
+enum kvc_rule { KVC_RULE_SINGLE = 0, KVC_RULE_CUMULATIVE = 1, KVC_RULE_EMA = 2 };
+
+/* Cache descriptor. All pointers are device pointers. */
+typedef struct kvc_cache {
+  int32_t dtype;            /* enum kvc_dtype of K and V (queries and new rows use it too) */
+  int32_t head_dim;         /* must be 128 */
+  int32_t capacity;         /* slots per scope */
+  int32_t n_scopes;
+  int32_t units_per_scope;  /* KV heads sharing one slot set (1: per-head scope) */
+  int32_t reserved;
+  int64_t scope_stride;     /* rows between the first units of consecutive scopes */
+  int64_t unit_stride;      /* rows between consecutive units of one scope */
+  void *k, *v;              /* [rows][head_dim] in dtype */
+  int32_t *votes;           /* [n_scopes][capacity] KeepKV votes, or NULL (every vote is 1) */
+  int32_t *pos;             /* [n_scopes][capacity] token positions (distinct among live slots) */
+  float *m;                 /* [n_scopes][capacity] utilities (fp32) */
+  int32_t *len;             /* [n_scopes] live slots; slots [0, len) are live */
+} kvc_cache;
+
+/* MomentKV running sums per unit (MomentKV §4.1): count, key sum, value sum
+ * and value-key outer-product sum S[a][b] = sum_e v_{e,a} k_{e,b}, fp32. */
+typedef struct kvc_moments {
+  int32_t *n;               /* [n_scopes][units_per_scope] */
+  float *sk;                /* [n_scopes][units_per_scope][head_dim] */
+  float *sv;                /* [n_scopes][units_per_scope][head_dim] */
+  float *S;                 /* [n_scopes][units_per_scope][head_dim][head_dim], row-major */
+} kvc_moments;
+
+/* KeepKV ZIP-merge parameters (eqs. (8)-(12), stability guard). The reference
+ * logit of an entry is the mean over the group's G query heads of
+ * scale * q_g . k, i.e. the logit of the group-mean query. */
+typedef struct kvc_merge {
+  const void *q;            /* [n_scopes][1][G][head_dim] in the cache dtype */
+  int32_t G;
+  float scale;
+  float eps;                /* guard: |w_e l_e + w_c l_c| < eps falls back to (k_e + k_c)/2 */
+  int32_t reserved;
+} kvc_merge;
+
+/* ---------------------------------------------------------------------------
+ * kvc_decode_attn_score -- append one token, then vote-weighted GQA decode
+ * attention and the head-averaged per-token score.
+ *
+ * KeepKV notes eq. (1) and eq. (6): o_g = sum_i p_i e^{l_{g,i}} v_i / sum_i p_i e^{l_{g,i}},
+ * l_{g,i} = scale * q_g . k_i (votes enter as ln p_i added to the logit).
+ * InertiaKV §3.1 eq. (1): s(i) = mean over the scope's units*G query heads of
+ * a_{g,i} = p_i e^{l_{g,i}} / Z_g.
+ *
+ * If k_new is non-NULL the new rows (k_new, v_new: [n_scopes][units][head_dim]
+ * in the cache dtype) are written at slot len of every scope with vote 1,
+ * position t and utility 0, and len is incremented; attention then covers
+ * slots [0, len). out: [n_scopes][units][G][head_dim] fp32; lse:
+ * [n_scopes][units][G] fp32 (ln Z_g, -inf when Z_g = 0); s: [n_scopes][capacity]
+ * fp32 or NULL (only slots < len are written). max_len is a host-side upper
+ * bound on the live length after the append, used to size the launch (<= 0:
+ * capacity); a device length beyond it is still handled correctly.
+ * ------------------------------------------------------------------------- */
+int32_t kvc_decode_attn_score(const kvc_cache *cache, const void *k_new, const void *v_new,
+                              int32_t t, const void *q, int32_t G, float scale,
+                              float *out, float *lse, float *s, int32_t max_len,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* kvc_ema_update -- InertiaKV §3.1 eqs. (2)-(4) on slots [0, len) of every
+ * scope: SINGLE m = s; CUMULATIVE m = m + s; EMA m = alpha m + (1 - alpha) s.
+ * m, s: [n_scopes][capacity] fp32; len: [n_scopes]. */
+int32_t kvc_ema_update(float *m, const float *s, const int32_t *len, int32_t n_scopes,
+                       int32_t capacity, int32_t rule, float alpha, void *stream);
+
+/* kvc_select_evict -- InertiaKV §3.1: when a scope holds more than `budget`
+ * live entries, the k = len - budget entries of lowest key are evicted;
+ * MomentKV Algorithm 1 phase 1 (one at a time) selects the same set when the
+ * key does not depend on the evicted set. Ties: (key, pos) ascending, so the
+ * lower position goes first; pos NULL uses the slot index. LaProx key design 3
+ * (model-wide Top-K) is this call with one scope over the flattened scores and
+ * budget = K.
+ * key: [n_scopes][capacity] fp32 (finite); len NULL means every slot is live.
+ * evict: [n_scopes][capacity] u8, set to 1 on the selected slots and 0 on every
+ * other slot < len; n_evict: [n_scopes] int32 or NULL. */
+int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *len,
+                         int32_t n_scopes, int32_t capacity, int32_t budget,
+                         uint8_t *evict, int32_t *n_evict, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* kvc_moment_update -- MomentKV §4.1 / Appendix A.1 / Algorithm 1 steps 11-13:
+ * for every slot < len flagged in evict (u8 [n_scopes][capacity]), fold its
+ * rows into every unit's sums: n += 1, sk += k, sv += v, S += v k^T (fp32).
+ * Must run before kvc_compact overwrites the evicted rows. */
+int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kvc_moments *mom,
+                          void *stream);
+
+/* kvc_compact -- remove the flagged entries of every scope (MomentKV Algorithm 1
+ * step 14; InertiaKV §3: eviction is irreversible). Survivors end in slots
+ * [0, len - n_evicted): the j-th evicted slot below the new length receives the
+ * j-th surviving slot at or above it (rows of every unit, vote, position and
+ * utility move together; slot order is not preserved). len is updated.
+ * With merge non-NULL each scope must hold exactly one flagged entry e (per-head
+ * scopes only); it is first ZIP-merged into the live entry c of largest
+ * cos(k_e, k_c) (ties to the lower position): KeepKV eqs. (7), (10), (12):
+ * v_c <- (w_e v_e + w_c v_c)/(w_e + w_c), k_c <- eq. (12) with the guard,
+ * p_c <- p_e + p_c, m_c <- m_e + m_c, with w_x = p_x e^{l_x}. Merged rows are
+ * rounded to the cache dtype (nearest even). */
+int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merge *merge,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* kvc_decode_step -- the whole decode step in one launch per call, in the
+ * order append -> attend -> score -> utility -> select -> fold -> compact
+ * (MomentKV Algorithm 1; KeepKV decode steps 6a-6f; InertiaKV §3.1), with the
+ * semantics of kvc_decode_attn_score, kvc_ema_update, kvc_select_evict,
+ * kvc_moment_update and kvc_compact applied in turn. refresh = 0 skips the
+ * score and utility update for this step (lazy refresh: eviction still holds
+ * the budget with the stale utility; the appended entry has utility 0).
+ * mom NULL skips the fold. evict_out: [n_scopes][capacity] u8 or NULL; when
+ * given it receives the flags of the evicted slots as they were before
+ * compaction. s may be NULL. Merge mode is kvc_compact's (merge non-NULL).
+ *
+ * Attention group. Only units [attn_unit0, attn_unit0 + attn_units) of each
+ * scope attend and score in this call (attn_units <= 0: every unit); q, out and
+ * lse are then [n_scopes][attn_units][G][head_dim] ([..][G] for lse), while
+ * the append (k_new, v_new: every unit), the fold and the compaction act on
+ * every unit of the scope. This is how one slot set shared by all layers of a
+ * sequence is driven layer by layer (InertiaKV §3.1: the utility is updated
+ * after every compressed layer); a call whose scope is already within budget
+ * only attends, scores and updates the utility. */
+int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,
+                        const void *q, int32_t G, float scale, int32_t rule, float alpha,
+                        int32_t budget, int32_t refresh, float *out, float *lse, float *s,
+                        const kvc_moments *mom, const kvc_merge *merge, uint8_t *evict_out,
+                        int32_t attn_unit0, int32_t attn_units, int32_t max_len,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* kvc_laprox_score -- LaProx prefill score (key design 1), per-layer
+ * normalisation (key design 2) and GQA group mean (training-strategy paragraph).
+ * For layer l, KV head h, token i < N:
+ *   c_i = || mean_{g in group(h)} A_g[:, i] ||_2 over the w window rows, where
+ *         window row j sits at position N - w + j and A_g[j, :] is the causal
+ *         softmax of scale * q_{g,j} . k_i over i <= N - w + j;
+ *   r_i = || v_i W_bar_h ||_2, W_bar_h = sum_{g in group(h)} W_O^g (d x D),
+ *         computed on MFMA;
+ *   score[l][h][i] = c_i r_i / sum_{h', i'} c_{i'} r_{i'} over layer l.
+ * q_win: [n_layers][H][w][d] bf16; k, v: [n_layers][n_kv][N][d] bf16;
+ * w_o: [n_layers][H][d][D] bf16; score: [n_layers][n_kv][N] fp32.
+ * The model-wide Top-K (key design 3) is kvc_select_evict on score with one
+ * scope of n_layers*n_kv*N entries and budget K. */
+int32_t kvc_laprox_score(const void *q_win, const void *k, const void *v, const void *w_o,
+                         int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,
+                         int32_t d, int32_t D, float scale, float *score,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace sizes in bytes. The decode workspace must be zero-filled once
+ * before its first use; the library returns its counters to zero after every
+ * call, so one workspace can serve any number of calls on one stream
+ * (concurrent calls need separate workspaces). */
+size_t kvc_decode_workspace_size(const kvc_cache *cache, int32_t G, int32_t max_len);
+size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity);
+size_t kvc_compact_workspace_size(const kvc_cache *cache);
+size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,
+                                 int32_t d, int32_t D);
+
+/* Synchronises `stream`, returns the device status word of a workspace
+ * (KVC_OK or KVC_ERR_CAPACITY when a device length exceeded its capacity)
+ * and clears it. */
+int32_t kvc_workspace_status(void *ws, void *stream);
+
+const char *kvc_status_string(int32_t status);
+int32_t kvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H */

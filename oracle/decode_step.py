@@ -79,6 +79,8 @@ class StepResult:
     s_pos: list = field(default_factory=list)      # per group: positions the s entries belong to
     evicted_pos: list = field(default_factory=list)  # per group: sorted evicted positions
     merges: list = field(default_factory=list)     # per group: (pos_e, pos_c, guarded) or None
+    m_pre: list = field(default_factory=list)      # per group: utility of every live entry before removal
+    m_pos: list = field(default_factory=list)      # per group: positions of those entries
 
 
 def _round_rows(x, row_dtype):
@@ -127,6 +129,8 @@ def decode_step(state: ScopeState, new_k, new_v, new_pos, q, prm: StepParams):
             res.s.append(None)
             res.s_pos.append(None)
 
+        res.m_pre.append(st.m.copy())
+        res.m_pos.append(st.pos.copy())
         k = st.length - prm.budget
         if k <= 0:
             res.evicted_pos.append(np.zeros(0, dtype=np.int64))

@@ -28,9 +28,10 @@ def fold_moments(mom: dict, K_E, V_E) -> dict:
     K_E = np.asarray(K_E, dtype=np.float64)
     V_E = np.asarray(V_E, dtype=np.float64)
     k = K_E.shape[1]
-    out = {"n": mom["n"] + k, "sk": mom["sk"] + K_E.sum(axis=1), "sv": mom["sv"] + V_E.sum(axis=1),
-           "S": mom["S"] + np.einsum("uea,ueb->uab", V_E, K_E)}
-    return out
+    S = mom["S"].copy()
+    for u in range(K_E.shape[0]):
+        S[u] += V_E[u].T @ K_E[u]          # sum_e v_e k_e^T as one matmul
+    return {"n": mom["n"] + k, "sk": mom["sk"] + K_E.sum(axis=1), "sv": mom["sv"] + V_E.sum(axis=1), "S": S}
 
 
 def centred_moments(mom: dict):

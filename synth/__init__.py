@@ -121,3 +121,44 @@ def output_projection(n_layers: int, H: int, d: int, D: int, seed: int, device="
 def window_queries(n_layers: int, H: int, w: int, d: int, seed: int, device="cpu") -> torch.Tensor:
     """Observation-window queries (the last w prompt positions): [n_layers, H, w, d] bf16 ~ N(0,1)."""
     return _randn((n_layers, H, w, d), seed, S_QWIN, None, device).to(torch.bfloat16)
+
+
+def cache_tensors(wl: Workload, device="cpu", capacity: int | None = None, initial_len: int | None = None):
+    """Device tensors of a workload's cache before its first decode step.
+
+    k, v: [n_scopes, units_per_scope, capacity, d] in the cache dtype, the first
+    `initial_len` rows drawn as in kv_rows (unit order: scope-major); pos:
+    [n_scopes, capacity] int32 (0..L0-1, or a sorted sample of the context when
+    the cache starts compressed); m: zeros; length: [n_scopes] int32; votes:
+    1 + Poisson(2) when the workload starts from prior merges, else None;
+    scales: per-unit key channel scales [n_units, d] or None."""
+    cap = capacity or wl.capacity
+    L0 = wl.initial_len if initial_len is None else initial_len
+    S, U, d = wl.n_scopes, wl.units_per_scope, wl.d
+    dt = _DTYPES[wl.dtype]
+    scales = key_scales(wl.n_units, d, wl.seed, device) if wl.key_scales else None
+    k = torch.zeros((S, U, cap, d), dtype=dt, device=device)
+    v = torch.zeros_like(k)
+    K0, V0 = kv_rows(wl.n_units, L0, d, wl.dtype, wl.seed, device, scales)
+    k[:, :, :L0] = K0.view(S, U, L0, d)
+    v[:, :, :L0] = V0.view(S, U, L0, d)
+    del K0, V0
+    pos = torch.zeros((S, cap), dtype=torch.int32, device=device)
+    if wl.prior_votes:
+        pos[:, :L0] = initial_positions(S, L0, wl.context, wl.seed, device)
+        votes = torch.zeros((S, cap), dtype=torch.int32, device=device)
+        votes[:, :L0] = prior_votes(S, L0, wl.seed, device=device)
+    else:
+        pos[:, :L0] = torch.arange(L0, dtype=torch.int32, device=device)
+        votes = None
+    m = torch.zeros((S, cap), dtype=torch.float32, device=device)
+    length = torch.full((S,), L0, dtype=torch.int32, device=device)
+    return {"k": k, "v": v, "pos": pos, "m": m, "length": length, "votes": votes, "scales": scales}
+
+
+def step_inputs(wl: Workload, step: int, scales=None, device="cpu"):
+    """Query heads [n_scopes, units, G, d] and new rows [n_scopes, units, d] of decode step `step` (1-based)."""
+    S, U = wl.n_scopes, wl.units_per_scope
+    q = step_query(step, wl.n_units, wl.G, wl.d, wl.dtype, wl.seed, device).view(S, U, wl.G, wl.d)
+    kn, vn = step_new_kv(step, wl.n_units, wl.d, wl.dtype, wl.seed, device, scales)
+    return q, kn.view(S, U, wl.d), vn.view(S, U, wl.d)

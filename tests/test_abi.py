@@ -1,0 +1,95 @@
+"""The C ABI: libkvc.so loads, exports every function include/kvc.h declares, and
+rejects bad arguments on the host before enqueuing anything (CPU only: no call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_decode_attention_gqa_amd import kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(kvc.LIB_PATH), reason="libkvc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for fn in ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
+               "kvc_moment_update", "kvc_laprox_score", "kvc_decode_step"):
+        assert fn in names
+    assert set(names) == set(kvc.EXPORTED)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    h = ctypes.CDLL(kvc.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(h, fn), fn
+    assert kvc.lib().kvc_version() == 1
+    assert kvc.status_string(0) == "ok"
+    assert kvc.status_string(-6).startswith("workspace")
+
+
+def _fake_cache(**over):
+    fields = dict(dtype=0, head_dim=128, capacity=100, n_scopes=2, units_per_scope=1, reserved=0,
+                  scope_stride=100, unit_stride=100, k=0x1000, v=0x2000, votes=None, pos=0x3000, m=0x4000,
+                  len=0x5000)
+    fields.update(over)
+    return kvc._Cache(**fields)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=64), -3), (dict(dtype=5), -2), (dict(k=0x1008), -5), (dict(capacity=0), -1),
+    (dict(pos=None), -1), (dict(units_per_scope=2, unit_stride=10), -1)])
+def test_decode_step_rejects_bad_cache(over, code):
+    c = _fake_cache(**over)
+    r = kvc.lib().kvc_decode_step(ctypes.byref(c), None, None, 0, 0x6000, 4, 0.1, 2, 0.9, 10, 1, 0x7000,
+                                  0x8000, None, None, None, None, 0, 0, 0, 0x9000, 1 << 30, None)
+    assert r == code
+
+
+@needs_lib
+def test_decode_step_host_checks():
+    c = _fake_cache()
+    L = kvc.lib()
+    args = lambda **kw: dict(dict(q=0x6000, G=4, budget=10, max_len=0, ws=0x9000, wsb=1 << 30, kn=None, vn=None), **kw)
+
+    def call(a):
+        return L.kvc_decode_step(ctypes.byref(c), a["kn"], a["vn"], 0, a["q"], a["G"], 0.1, 2, 0.9, a["budget"], 1,
+                                 0x7000, 0x8000, None, None, None, None, 0, 0, a["max_len"], a["ws"], a["wsb"], None)
+    assert call(args(G=3)) == -3
+    assert call(args(q=None)) == -1
+    assert call(args(q=0x6004)) == -5
+    assert call(args(budget=-1)) == -4
+    assert call(args(max_len=101)) == -4
+    assert call(args(ws=None)) == -6
+    assert call(args(wsb=16)) == -6
+    assert call(args(kn=0x100)) == -1          # new key without new value
+    need = L.kvc_decode_workspace_size(ctypes.byref(c), 4, 0)
+    assert need > 0 and L.kvc_decode_workspace_size(ctypes.byref(c), 3, 0) == 0
+
+
+@needs_lib
+def test_other_entry_points_reject_bad_arguments():
+    L = kvc.lib()
+    assert L.kvc_ema_update(None, 0x10, 0x20, 1, 10, 2, 0.9, None) == -1
+    assert L.kvc_ema_update(0x10, 0x10, 0x20, 1, 10, 7, 0.9, None) == -1
+    assert L.kvc_select_evict(0x10, None, None, 1, 10, -1, 0x20, None, 0x30, 4096, None) == -4
+    assert L.kvc_select_evict(0x10, None, None, 1, 10, 3, 0x20, None, None, 0, None) == -6
+    c = _fake_cache()
+    assert L.kvc_compact(ctypes.byref(c), None, None, 0x30, 1 << 20, None) == -1
+    assert L.kvc_moment_update(ctypes.byref(c), 0x10, None, None) == -1
+    assert L.kvc_laprox_score(0x10, 0x20, 0x30, 0x40, 1, 32, 8, 100, 4, 64, 4096, 0.1, 0x50, 0x60, 1 << 30,
+                              None) == -3
+    assert L.kvc_laprox_score(0x10, 0x20, 0x30, 0x40, 1, 30, 8, 100, 4, 128, 4096, 0.1, 0x50, 0x60, 1 << 30,
+                              None) == -3

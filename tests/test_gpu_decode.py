@@ -1,0 +1,172 @@
+"""GPU parity of the fused decode step and the attention entry point (MI355X).
+
+Every test calls the HIP library through the C ABI (ctypes) and compares with
+the fp64 oracle on the same bytes; see kvc_parity.py for the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from compressed_decode_attention_gqa_amd import kvc
+from kvc_parity import DeviceRun, bits, check_step, f32, lockstep, oracle_state
+
+pytestmark = pytest.mark.gpu
+
+C1 = synth.WORKLOADS["c1_head_f32_4k"]
+C2 = synth.WORKLOADS["c2_llama8b_layer_32k"]
+C2X32 = synth.WORKLOADS["c2x32_llama8b_32layers_32k"]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("dtype,G,L,votes", [("bf16", 4, 1000, True), ("bf16", 4, 129, False),
+                                              ("f32", 1, 777, False), ("bf16", 1, 300, True),
+                                              ("bf16", 8, 260, False), ("f32", 4, 65, True)])
+def test_attn_score_matches_oracle(dtype, G, L, votes):
+    _say("attn_score", dtype, G, L, votes)
+    wl = C2.scaled(dtype=dtype, G=G, context=L, budget=L, n_kv=3, key_scales=True, prior_votes=False)
+    run = DeviceRun(wl, capacity=L + 5)
+    if votes:
+        run.cache.votes = torch.randint(0, 4, (wl.n_scopes, run.cache.capacity), dtype=torch.int32, device="cuda")
+        run.cache.votes[:, 0] = 1
+    pre = run.snapshot(list(range(wl.n_scopes)))
+    q, kn, vn = run.inputs(1)
+    kvc.kvc_decode_attn_score(run.cache, kn, vn, wl.context, q, G, run.scale, run.out, run.lse, run.s, 0, run.ws)
+    torch.cuda.synchronize()
+    post = run.snapshot(list(range(wl.n_scopes)))
+    out, lse, s = bits(run.out), bits(run.lse), bits(run.s)
+    for sc in range(wl.n_scopes):
+        st = oracle_state(pre, sc, dtype)
+        K = np.concatenate([st.K, oracle.to_f64(bits(kn)[sc], dtype)[:, None]], 1)
+        V = np.concatenate([st.V, oracle.to_f64(bits(vn)[sc], dtype)[:, None]], 1)
+        p = np.append(st.votes, 1)
+        _, a, o, l = oracle.attend_unit(oracle.to_f64(bits(q)[sc, 0], dtype), K[0], V[0], p, run.scale)
+        tol = 2e-3 if dtype == "bf16" else 1e-5 * np.abs(o).max()
+        assert np.abs(out[sc, 0] - o).max() <= tol
+        assert np.abs(lse[sc, 0] - l).max() <= (2e-3 if dtype == "bf16" else 1e-5 * np.abs(l).max() + 1e-6)
+        s_ref = oracle.scope_score([a])
+        assert np.all(np.abs(s[sc, :L + 1] - s_ref) <= 1e-5 * s_ref + 1e-12)
+        assert post["len"][sc] == L + 1
+        assert post["pos"][sc, L] == wl.context and post["m"][sc, L] == 0
+        assert np.array_equal(post["k"][sc][:, L], bits(kn)[sc])
+        if votes:
+            assert post["votes"][sc, L] == 1
+
+
+def test_decode_step_c1_lockstep():
+    """Single fp32 head, 4096 tokens to a 128 budget, 64 steps, every step checked."""
+    run = DeviceRun(C1)
+    rep = lockstep(run, C1.steps, lambda t: [0])
+    _say("c1", rep)
+
+
+def test_decode_step_c2_reduced_lockstep():
+    wl = C2.scaled(context=2000, budget=200, steps=12)
+    run = DeviceRun(wl)
+    rep = lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)))
+    _say("c2 reduced", rep)
+
+
+@pytest.mark.parametrize("rule", ["single", "cumulative"])
+def test_decode_step_other_rules(rule):
+    wl = C2.scaled(context=1500, budget=300, steps=5, rule=rule, n_kv=4)
+    run = DeviceRun(wl)
+    lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)))
+
+
+def test_decode_step_lazy_refresh():
+    wl = C2.scaled(context=1200, budget=1100, steps=9, n_kv=2)
+    run = DeviceRun(wl)
+    lockstep(run, wl.steps, lambda t: [0, 1], refresh_for_step=lambda t: (t - 1) % 4 == 0)
+
+
+def test_decode_step_c2_full_size():
+    """One Llama-3.1-8B layer, 32768 -> 3276 at step 1 (29493 evictions per head), then steady steps."""
+    run = DeviceRun(C2, max_len=C2.context + 1)
+    checked = {1, 2, 3, 16}
+    rep = lockstep(run, 16, lambda t: list(range(C2.n_scopes)) if t in checked else [])
+    _say("c2 full", rep)
+
+
+def test_decode_step_c2x32_sampled():
+    """The 32-layer stack in one launch per step, at the benchmark's launch shape; sampled scopes."""
+    rng = np.random.default_rng(5)
+    run = DeviceRun(C2X32, max_len=C2X32.context + 1)
+
+    def scopes(t):
+        if t in (1, 2, 8):
+            return sorted(rng.choice(C2X32.n_scopes, size=24, replace=False).tolist())
+        return []
+    rep = lockstep(run, 8, scopes)
+    _say("c2x32", rep)
+
+
+def test_determinism():
+    wl = C2.scaled(context=900, budget=100, steps=3, n_kv=3)
+    states = []
+    for _ in range(2):
+        run = DeviceRun(wl)
+        for step in range(1, wl.steps + 1):
+            run.step(step, *run.inputs(step))
+        torch.cuda.synchronize()
+        states.append([bits(x) for x in (run.cache.k, run.cache.m, run.cache.pos, run.mom.S, run.out, run.lse)])
+    for a, b in zip(*states):
+        assert np.array_equal(a, b)
+
+
+def test_empty_cache_and_within_budget():
+    wl = C2.scaled(context=0, budget=5, steps=7, n_kv=2, moments=True)
+    run = DeviceRun(wl, capacity=8)
+    lockstep(run, wl.steps, lambda t: [0, 1])
+
+
+def test_capacity_overflow_is_reported():
+    wl = C2.scaled(context=10, budget=20, n_kv=1)
+    run = DeviceRun(wl, capacity=11)
+    run.step(1, *run.inputs(1))          # fills the last slot
+    run.step(2, *run.inputs(2))          # no slot left: device status
+    assert kvc.kvc_workspace_status(run.ws) == -4
+    assert int(run.cache.length[0]) == 11
+    assert kvc.kvc_workspace_status(run.ws) == 0
+
+
+def test_select_evict_matches_oracle():
+    rng = np.random.default_rng(3)
+    n_scopes, cap = 5, 3000
+    ws = kvc.workspace(kvc.kvc_select_workspace_size(n_scopes, cap))
+    for trial in range(4):
+        vals = rng.choice(np.array([0.0, 1e-3, 2.5e-3, 7.0, 1e-40], dtype=np.float32), size=(n_scopes, cap))
+        vals = np.where(rng.random((n_scopes, cap)) < 0.5, rng.random((n_scopes, cap)).astype(np.float32), vals)
+        pos = np.stack([rng.permutation(100000)[:cap] for _ in range(n_scopes)]).astype(np.int32)
+        lens = rng.integers(1, cap + 1, size=n_scopes).astype(np.int32)
+        budget = int(rng.integers(0, cap))
+        key = torch.from_numpy(vals).cuda()
+        evict = torch.zeros((n_scopes, cap), dtype=torch.uint8, device="cuda")
+        nev = torch.zeros(n_scopes, dtype=torch.int32, device="cuda")
+        kvc.kvc_select_evict(key, torch.from_numpy(pos).cuda(), torch.from_numpy(lens).cuda(), n_scopes, cap,
+                             budget, evict, nev, ws)
+        ev = bits(evict)
+        for s in range(n_scopes):
+            L = lens[s]
+            E = oracle.bottom_k(vals[s, :L].astype(np.float64), pos[s, :L], L - budget)
+            assert np.array_equal(np.flatnonzero(ev[s, :L]), E)
+            assert int(bits(nev)[s]) == max(0, L - budget)
+
+
+def test_select_evict_device_wide_top_k():
+    """One scope of 2^21 flattened scores keeping the top 4096 (LaProx model-wide Top-K form)."""
+    rng = np.random.default_rng(11)
+    n, K = 1 << 21, 4096
+    vals = rng.random(n).astype(np.float32) ** 3
+    vals[rng.choice(n, 5000, replace=False)] = vals[7]          # a heavy tie
+    key = torch.from_numpy(vals).cuda()
+    evict = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = kvc.workspace(kvc.kvc_select_workspace_size(1, n))
+    kvc.kvc_select_evict(key, None, None, 1, n, K, evict, None, ws)
+    keep = bits(evict) == 0
+    ref = oracle.top_k_keep(vals.astype(np.float64), K)
+    assert np.array_equal(keep, ref)
