@@ -1,0 +1,207 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decode-attend-score-evict step on one MI355X.
+
+Workload (default): one Llama-3.1-8B-shaped layer (32 query / 8 KV heads,
+d = 128, bf16 cache) at 32K context compressed to a 10% budget (3276 slots
+per KV head), stacked over the model's 32 layers so one launch per step
+covers 256 KV heads; EMA utility (alpha 0.9) and MomentKV moments on. The
+first decode step (bulk compression of 32769 -> 3276 per head) runs before
+the timed region; every timed step attends over 3277 live tokens per head,
+scores them, updates the utility, evicts one token per head, folds it into
+the moments and compacts.
+
+Prints one JSON line. `value` is cached tokens attended+scored+evicted per
+second (live K/V rows the step processes, summed over KV heads); inputs of
+every step are resident in HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth  # noqa: E402
+from compressed_decode_attention_gqa_amd import kvc  # noqa: E402
+from compressed_decode_attention_gqa_amd import roofline as rf  # noqa: E402
+
+METRIC = "cached tokens attended+scored+evicted/sec and % peak HBM GB/s at 32K ctx"
+KERNEL_SOURCES = ["decode.hip", "kvc_ops.h", "kvc_device.h", "kvc_decode.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2x32_traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "compressed_decode_attention_gqa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch: float):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def host_scopes(cache, scopes, dtype, q, kn, vn):
+    """Host copies of some scopes' current state and of the next step's inputs, as oracle input."""
+    import oracle
+
+    def h(x):
+        x = x.detach().cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+    lens = cache.length.cpu().numpy()
+    states = []
+    for sc in scopes:
+        L = int(lens[sc])
+        votes = (h(cache.votes[sc, :L]).astype(np.int64) if cache.votes is not None
+                 else np.ones(L, dtype=np.int64))
+        states.append(oracle.ScopeState(K=oracle.to_f64(h(cache.k[sc, :, :L]), dtype),
+                                        V=oracle.to_f64(h(cache.v[sc, :, :L]), dtype), votes=votes,
+                                        pos=h(cache.pos[sc, :L]).astype(np.int64),
+                                        m=h(cache.m[sc, :L]).astype(np.float64)))
+    conv = lambda x: [oracle.to_f64(h(x[sc]), dtype) for sc in scopes]
+    return states, conv(q), conv(kn), conv(vn)
+
+
+def cpu_baseline(run_state, wl, seconds: float):
+    """The fp64 oracle's decode step timed on the host over a bounded sample."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    states, q, kn, vn, t = run_state
+    prm = oracle.StepParams(scale=float(np.float32(1 / np.sqrt(wl.d))), rule=wl.rule,
+                            alpha=float(np.float32(wl.alpha)), budget=wl.budget)
+    tokens, steps = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for j, st in enumerate(states):
+            _, res = oracle.decode_step(st, kn[j], vn[j], t, q[j], prm)
+            tokens += st.length + 1
+            steps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} per-KV-head steady steps of {wl.name} (L={wl.budget + 1}, G={wl.G}, "
+                      f"k=1, moments on) in {dt:.1f} s, numpy float64 oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the decode step on a single "
+              "MI355X; run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S, U, G, d, B = wl.n_scopes, wl.units_per_scope, wl.G, wl.d, wl.budget
+    t = synth.cache_tensors(wl, dev)
+    cache = kvc.Cache(k=t["k"], v=t["v"], pos=t["pos"], m=t["m"], length=t["length"], votes=t["votes"])
+    mom = kvc.Moments.zeros(S, U, d, dev) if wl.moments else None
+    out = torch.empty((S, U, G, d), device=dev)
+    lse = torch.empty((S, U, G), device=dev)
+    s = torch.empty((S, cache.capacity), device=dev)
+    ws = kvc.workspace(kvc.kvc_decode_workspace_size(cache, G, 0), dev)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    alpha = float(np.float32(wl.alpha))
+    n_steps = 1 + args.warmup + args.steps
+    q_all, kn_all, vn_all = [], [], []
+    for step in range(1, n_steps + 1):
+        q, kn, vn = synth.step_inputs(wl, step, t["scales"], dev)
+        q_all.append(q)
+        kn_all.append(kn)
+        vn_all.append(vn)
+    pos0 = wl.context
+
+    def step_call(i, max_len):
+        kvc.kvc_decode_step(cache, kn_all[i], vn_all[i], pos0 + i, q_all[i], G, scale, wl.rule, alpha, B,
+                            out, lse, s, mom, None, None, max_len=max_len, ws=ws)
+
+    step_call(0, wl.initial_len + 1)            # first step: bulk compression to the budget
+    for i in range(1, 1 + args.warmup):
+        step_call(i, B + 1)
+    torch.cuda.synchronize()
+    assert int(cache.length.min()) == B and int(cache.length.max()) == B
+
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for j in range(args.steps):
+        ev0[j].record()
+        step_call(1 + args.warmup + j, B + 1)
+        ev1[j].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+    status = kvc.kvc_workspace_status(ws)
+    if status != 0:
+        raise SystemExit(f"device status {status} after the timed steps")
+
+    L = B + 1
+    tokens_per_step = S * U * L
+    ms_per_step = total_ms / args.steps
+    value = tokens_per_step / (ms_per_step / 1e3)
+    ub = rf.unit_step_bytes(L=L, k=1, G=G, d=d, elem=2 if wl.dtype == "bf16" else 4,
+                            votes=wl.prior_votes, moments=wl.moments, write_score=True)
+    bytes_per_launch = ub.total * S * U
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    traffic = measured_traffic(bytes_per_launch)
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "kv_heads": wl.n_kv,
+                   "q_heads": wl.n_kv * G, "head_dim": d, "context": wl.context, "budget": B,
+                   "live_tokens_per_head": L, "rule": wl.rule, "alpha": wl.alpha, "moments": wl.moments,
+                   "logits": "f64 accumulate", "values": "f32 accumulate", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": rf.MI355X_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / rf.MI355X_HBM_GBPS, "traffic": traffic,
+                     "bytes_per_launch": bytes_per_launch, "launch_ms": launch_ms,
+                     "wall_GBps": bytes_per_launch / (ms_per_step / 1e3) / 1e9},
+    }
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        i = 1 + args.warmup + args.steps     # inputs of the next step, applied to the current state
+        q, kn, vn = synth.step_inputs(wl, i + 1, t["scales"], dev)
+        state = host_scopes(cache, list(range(min(S, 32))), wl.dtype, q, kn, vn)
+        result["cpu_baseline"] = cpu_baseline(state + (pos0 + i,), wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 
-#include "../../include/kvc.h"
+#include "kvc.h"
 #include "kvc_decode.h"
 #include "kvc_kernels.h"
 #include "kvc_laprox.h"
@@ -16,6 +16,18 @@ namespace {
 constexpr int kHD = 128;
 constexpr int kTargetWorkgroups = 2048;   // split-K workgroups per launch to aim for
 constexpr int kMergeSplitsMax = 64;
+// One workgroup per scope (no split-K) once there are this many single-unit
+// scopes to spread over the 256 CUs and each scope's live length is bounded.
+constexpr int kUnitMinScopes = 128;
+constexpr size_t kUnitStaticLds = 20 * 1024;   // static LDS of the per-scope kernel (upper bound)
+
+// LDS a workgroup may allocate on the current device (160 KB on gfx950).
+size_t device_lds_per_block() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  return size_t(v);
+}
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -51,8 +63,9 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   DecodeLayout d{};
   const int CH = kvc::decode_chunk_tokens(c->dtype);
   const int64_t nu = int64_t(c->n_scopes) * attn_units;
-  d.nsub_cap = ceil_div(c->capacity, CH);
-  d.n_splits = split_count(int(nu), d.nsub_cap);
+  const int CHW = kvc::decode_unit_chunk_tokens(c->dtype);
+  d.nsub_cap = ceil_div(c->capacity, std::min(CH, CHW));
+  d.n_splits = std::max(kvc::kUnitWaves, split_count(int(nu), ceil_div(c->capacity, CH)));
   d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
   const int64_t cap = c->capacity;
   size_t o = 0;
@@ -177,9 +190,20 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.list2 = at<int32_t>(ws, d.list2);
   a.nsub_cap = d.nsub_cap;
   const int CH = kvc::decode_chunk_tokens(c->dtype);
-  a.n_splits = split_count(c->n_scopes * attn_units, ceil_div(max_len, CH));
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (kvc::launch_decode(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  bool per_scope = attn_units == 1 && c->n_scopes >= kUnitMinScopes;
+  if (per_scope) {
+    const size_t lds = kvc::decode_unit_lds_bytes(c->dtype, G, max_len) + kUnitStaticLds;
+    per_scope = lds <= device_lds_per_block();
+  }
+  if (per_scope) {
+    a.n_splits = kvc::kUnitWaves;
+    a.lds_len = max_len;
+    if (kvc::launch_decode_unit(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  } else {
+    a.n_splits = split_count(c->n_scopes * attn_units, ceil_div(max_len, CH));
+    if (kvc::launch_decode(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  }
   if (a.mode == 2) {
     kvc::MergeArgs mg{};
     mg.q = static_cast<const char *>(merge->q);

@@ -9,6 +9,8 @@
 // sub-chunk maximum, the weights p_i exp(l - M) and the value sums. The last
 // workgroup of a scope to finish (device-scope counter) combines the partials
 // and runs the scope's score -> utility -> select -> fold -> compact epilogue.
+#include <type_traits>
+
 #include "kvc_decode.h"
 #include "kvc_ops.h"
 
@@ -53,9 +55,14 @@ struct EpiLds {
 };
 
 // ---------------------------------------------------------------- epilogue
-template <typename T, int G>
-__device__ void decode_epilogue(const StepArgs &a, const int scope, const int L, EpiLds &sh) {
-  constexpr int CH = Geometry<T>::CH;
+// CH: tokens per sub-chunk, the granularity at which the streaming phase
+// recorded its running maxima (subM) for the per-token weights.
+// ew: per-token weights exp(l - M_sub) of the scope's first attention unit,
+// [ua][g][ew_ld]; fm: sub-chunk maxima [ua][fm_ld][g], replaced in place by the
+// score factors.
+template <typename T, int G, int CH>
+__device__ void decode_epilogue(const StepArgs &a, const int scope, const int L, EpiLds &sh,
+                                const float *ew, int64_t ew_ld, double *fm, int64_t fm_ld) {
   const int tid = threadIdx.x;
   const int Ua = a.attn_units, cap = a.capacity, ns = a.n_splits;
   const int gu0 = scope * Ua;
@@ -99,7 +106,7 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
     for (int idx = tid; idx < Ua * nsubL * G; idx += WG) {
       const int ua = idx / (nsubL * G), rem = idx - ua * (nsubL * G);
       const int c = rem / G, g = rem - (rem / G) * G;
-      double *p = a.subM + (int64_t(gu0 + ua) * a.nsub_cap + c) * G + g;
+      double *p = fm + (int64_t(ua) * fm_ld + c) * G + g;
       const double Z = sh.Z[ua * G + g];
       *p = Z > 0.0 ? exp(*p - sh.M[ua * G + g]) / Z : 0.0;
     }
@@ -121,10 +128,9 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
       const int c = i / CH;
       double acc = 0.0;
       for (int ua = 0; ua < Ua; ++ua) {
-        const int gu = gu0 + ua;
 #pragma unroll
         for (int g = 0; g < G; ++g)
-          acc += double(a.ews[(int64_t(gu) * G + g) * cap + i]) * a.subM[(int64_t(gu) * a.nsub_cap + c) * G + g];
+          acc += double(ew[(int64_t(ua) * G + g) * ew_ld + i]) * fm[(int64_t(ua) * fm_ld + c) * G + g];
       }
       const double sv = double(pv) * acc * inv_heads;
       if (a.s) a.s[sc + i] = float(sv);
@@ -457,8 +463,236 @@ __global__ __launch_bounds__(WG) void k_decode(const StepArgs a) {
     }
     return;
   }
-  decode_epilogue<T, G>(a, scope, L, lds.ep);
+  decode_epilogue<T, G, CH>(a, scope, L, lds.ep, a.ews + int64_t(scope) * a.attn_units * G * cap, cap,
+                            a.subM + int64_t(scope) * a.attn_units * a.nsub_cap * G, a.nsub_cap);
   if (tid == 0) a.counters[scope] = 0;
+}
+
+// ---------------------------------------------------------------- one workgroup per scope
+// For launches with one attention unit per scope and enough scopes to fill
+// the device. The workgroup streams its unit's whole cache: each of the four
+// waves takes every fourth sub-chunk of CHW tokens and keeps PF sub-chunks of
+// 16-byte loads in flight, so waves never wait on each other while streaming.
+// A wave forms float64 logits, reduces them so each lane holds one head's
+// logit (transposed reduction), keeps a running per-head maximum (rescaling
+// its value sums only when the maximum moves) and records the maximum of
+// every sub-chunk for the per-token weights. The four waves' partials then
+// feed the same epilogue as the split kernel, inside this workgroup: no
+// counters, no device-scope fences.
+template <typename T>
+struct UnitGeometry {
+  static constexpr int EPV = ElemTraits<T>::EPV;
+  static constexpr int LPT = HD / EPV;
+  static constexpr int TPI = 64 / LPT;
+  static constexpr int UNR = 4;            // iterations per sub-chunk
+  static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
+  static constexpr int PF = 4;             // sub-chunks of loads in flight per wave
+  static constexpr int NW = WG / 64;       // waves
+};
+
+int decode_unit_chunk_tokens(int dtype) {
+  return dtype == 0 ? UnitGeometry<bf16_t>::CHW : UnitGeometry<float>::CHW;
+}
+
+template <typename T, int G>
+struct UnitWave {
+  using Geo = UnitGeometry<T>;
+  static constexpr int UNR = Geo::UNR, TPI = Geo::TPI, LPT = Geo::LPT, EPV = Geo::EPV, CHW = Geo::CHW;
+
+  const char *Kb, *Vb, *Kn, *Vn;
+  const int32_t *vrow;    // the scope's votes, or any valid int row when votes are absent
+  int L, append, cb, tg, lane;
+
+  // Loads of sub-chunk c (token index clamped into the live range, so every
+  // call issues the same loads and the wait counts stay exact).
+  __device__ __forceinline__ void issue(u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], int (&vt)[UNR], int c) const {
+#pragma unroll
+    for (int it = 0; it < UNR; ++it) {
+      const int tok = min(c * CHW + it * TPI + tg, L - 1);
+      const bool isnew = append && tok == L - 1;
+      const char *ks = isnew ? Kn : Kb + int64_t(tok) * (HD * int64_t(sizeof(T)));
+      const char *vs = isnew ? Vn : Vb + int64_t(tok) * (HD * int64_t(sizeof(T)));
+      kr[it] = ld16(ks + 16 * cb);
+      vr[it] = ld16(vs + 16 * cb);
+      const int vote = vrow[tok];          // slot L-1 holds no vote yet when it is the appended token
+      vt[it] = isnew ? 1 : vote;
+    }
+  }
+};
+
+template <typename T, int G>
+__global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
+  using TR = ElemTraits<T>;
+  using Geo = UnitGeometry<T>;
+  constexpr int EPV = Geo::EPV, LPT = Geo::LPT, TPI = Geo::TPI, UNR = Geo::UNR;
+  constexpr int CHW = Geo::CHW, PF = Geo::PF, NW = Geo::NW;
+
+  __shared__ union {
+    float w[NW][UNR][TPI][G];
+    EpiLds ep;
+  } lds;
+  // dynamic LDS: weights e[G][lds_len] (float), then sub-chunk maxima [nsub][G] (double)
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  const int lds_len = a.lds_len;
+  float *e_lds = reinterpret_cast<float *>(dyn);
+  double *m_lds = reinterpret_cast<double *>(dyn + size_t(G) * lds_len * 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.x, gu = scope;
+  const int unit = a.attn_unit0;
+  const int cap = a.capacity;
+  int L = a.len[scope] + a.append;
+  const bool overflow = L > cap || L > lds_len;
+  if (overflow) L = 0;
+
+  UnitWave<T, G> W;
+  {
+    const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(unit) * a.unit_stride;
+    W.Kb = a.k + row0 * (HD * int64_t(sizeof(T)));
+    W.Vb = a.v + row0 * (HD * int64_t(sizeof(T)));
+    W.Kn = a.k_new + (int64_t(scope) * a.units + unit) * (HD * int64_t(sizeof(T)));
+    W.Vn = a.v_new + (int64_t(scope) * a.units + unit) * (HD * int64_t(sizeof(T)));
+    W.vrow = (a.votes ? a.votes : a.pos) + int64_t(scope) * cap;
+    W.L = L;
+    W.append = a.append;
+    W.cb = lane % LPT;
+    W.tg = lane / LPT;
+    W.lane = lane;
+  }
+  const int cb = W.cb, tg = W.tg;
+  const int myh = lane_head<LPT, G>(lane);
+  const bool leader = head_leader<LPT, G>(lane);
+
+  double qf[G][EPV];
+  {
+    const T *qp = reinterpret_cast<const T *>(a.q) + int64_t(gu) * G * HD;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) qf[g][j] = double(load_elem<T>(qp, g * HD + cb * EPV + j));
+  }
+  float oacc[G][EPV];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) oacc[g][j] = 0.f;
+  double Mrun = -INFINITY, Zrun = 0.0;
+
+  const int nsub = L > 0 ? (L + CHW - 1) / CHW : 0;
+  u32x4 kr[PF][UNR], vr[PF][UNR];
+  int vt[PF][UNR];
+  if (nsub > 0) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) W.issue(kr[s], vr[s], vt[s], wave + NW * s);
+  }
+  const bool has_votes = a.votes != nullptr;
+  for (int base = wave; base < nsub; base += NW * PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int c = base + NW * s;
+      if (c < nsub) {
+        // logits: lane ends with head myh of token (c*CHW + it*TPI + tg)
+        double lg[UNR];
+#pragma unroll
+        for (int it = 0; it < UNR; ++it) {
+          double acc[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) acc[g] = 0.0;
+#pragma unroll
+          for (int j = 0; j < EPV; ++j) {
+            const double kj = double(TR::get(kr[s][it], j));
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = fma(qf[g][j], kj, acc[g]);
+          }
+          const double l = treduce<LPT, G, 0>(acc, lane) * a.scale;
+          lg[it] = (c * CHW + it * TPI + tg < L) ? l : -INFINITY;
+        }
+        double mx = lg[0];
+#pragma unroll
+        for (int it = 1; it < UNR; ++it) mx = fmax(mx, lg[it]);
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o));
+        const double Mnew = fmax(Mrun, mx);
+        if (__ballot(Mnew > Mrun)) {
+          const double f = Mrun > -INFINITY ? exp(Mrun - Mnew) : 0.0;
+          Zrun *= f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float fg = float(readlane_f64(f, head_rep_lane<LPT, G>(g)));
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) oacc[g][j] *= fg;
+          }
+          Mrun = Mnew;
+        }
+        if (tg == 0 && leader) m_lds[c * G + myh] = Mrun;
+        // weights p_i exp(l - M): one lane per (token, head) publishes
+#pragma unroll
+        for (int it = 0; it < UNR; ++it) {
+          const int tok = c * CHW + it * TPI + tg;
+          const float e = exp_split(lg[it] - Mrun);
+          const float w = (has_votes ? float(vt[s][it]) : 1.f) * e;
+          Zrun += double(w);
+          if (leader) {
+            lds.w[wave][it][tg][myh] = w;
+            if (tok < L) e_lds[myh * lds_len + tok] = e;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < UNR; ++it) {
+          float wv[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) wv[g] = lds.w[wave][it][tg][g];
+#pragma unroll
+          for (int j = 0; j < EPV; ++j) {
+            const float vj = TR::get(vr[s][it], j);
+#pragma unroll
+            for (int g = 0; g < G; ++g) oacc[g][j] = fmaf(wv[g], vj, oacc[g][j]);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      W.issue(kr[s], vr[s], vt[s], c + NW * PF);
+    }
+  }
+
+  // this wave's partials: (M, Z) per head and the value sums
+  double zt = Zrun;
+#pragma unroll
+  for (int o = LPT; o < 64; o <<= 1) zt += __shfl_xor(zt, o);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      float x = oacc[g][j];
+#pragma unroll
+      for (int o = LPT; o < 64; o <<= 1) x += __shfl_xor(x, o);
+      oacc[g][j] = x;
+    }
+  const int64_t pbase = int64_t(gu) * a.n_splits + wave;
+  if (lane < LPT) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) a.partO[(pbase * G + g) * HD + cb * EPV + j] = oacc[g][j];
+  }
+  if (tg == 0 && leader) {
+    a.partM[pbase * G + myh] = Mrun;
+    a.partZ[pbase * G + myh] = zt;
+  }
+  __threadfence_block();
+  __syncthreads();
+  if (overflow) {
+    if (tid == 0) a.status[0] = -4;
+    return;
+  }
+  decode_epilogue<T, G, CHW>(a, scope, L, lds.ep, e_lds, lds_len, m_lds, 0);
+}
+
+// Dynamic LDS of the per-scope kernel for caches of up to lds_len live tokens.
+size_t decode_unit_lds_bytes(int dtype, int G, int lds_len) {
+  const int chw = decode_unit_chunk_tokens(dtype);
+  return size_t(G) * lds_len * 4 + size_t((lds_len + chw - 1) / chw) * G * 8;
 }
 
 template <typename T>
@@ -473,9 +707,34 @@ static hipError_t launch_g(const StepArgs &a, int G, dim3 grid, hipStream_t st) 
   return hipGetLastError();
 }
 
+template <typename T, int G>
+static hipError_t launch_unit_tg(const StepArgs &a, hipStream_t st) {
+  const size_t dyn = decode_unit_lds_bytes(std::is_same<T, float>::value ? 1 : 0, G, a.lds_len);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_decode_unit<T, G>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_unit<T, G>), dim3(a.n_scopes), dim3(WG), dyn, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_unit_g(const StepArgs &a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_unit_tg<T, 1>(a, st);
+    case 2: return launch_unit_tg<T, 2>(a, st);
+    case 4: return launch_unit_tg<T, 4>(a, st);
+    case 8: return launch_unit_tg<T, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st) {
   dim3 grid(a.n_splits, a.n_scopes * a.attn_units);
   return dtype == 0 ? launch_g<bf16_t>(a, G, grid, st) : launch_g<float>(a, G, grid, st);
+}
+
+hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st) {
+  return dtype == 0 ? launch_unit_g<bf16_t>(a, G, st) : launch_unit_g<float>(a, G, st);
 }
 
 }  // namespace kvc

@@ -169,3 +169,81 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int *red, int *total) {
 }
 
 }  // namespace kvc
+
+namespace kvc {
+
+// ---------------------------------------------------------------- transposed group reduction
+// A token row is spread over LPT lanes (16 or 32); each lane holds partial dot
+// products for the G heads. The reduction halves the head set at each of the
+// first log2(G) exchange stages (a lane keeps the half selected by its lane
+// bit and sends the other half to its partner), then sums the single
+// remaining value over the rest. Every lane ends with the full dot product of
+// one head, lane_head<LPT, G>(lane); the stages are DPP row mirrors / quad
+// permutes (and a cross-row shuffle for 32-lane rows).
+template <int LPT>
+__device__ __forceinline__ double xchg_stage(double x, int stage) {
+  constexpr int off = LPT == 32 ? 1 : 0;
+  if (LPT == 32 && stage == 0) return __shfl_xor(x, 16);
+  switch (stage - off) {
+    case 0: return dpp_f64<0x140>(x);   // row_mirror: flips lane bit 3 (and bits 0-2)
+    case 1: return dpp_f64<0x141>(x);   // row_half_mirror: flips bit 2 (and bits 0-1)
+    case 2: return dpp_f64<0x4E>(x);    // quad_perm [2,3,0,1]: flips bit 1
+    default: return dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]: flips bit 0
+  }
+}
+
+template <int LPT, int N, int STAGE>
+__device__ __forceinline__ double treduce(const double (&v)[N], int lane) {
+  constexpr int NST = LPT == 32 ? 5 : 4;
+  if constexpr (N == 1) {
+    double x = v[0];
+#pragma unroll
+    for (int s = STAGE; s < NST; ++s) x += xchg_stage<LPT>(x, s);
+    return x;
+  } else {
+    constexpr int bit = NST - 1 - STAGE;
+    const bool up = (lane >> bit) & 1;
+    double w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const double send = up ? v[i] : v[N / 2 + i];
+      const double keep = up ? v[N / 2 + i] : v[i];
+      w[i] = keep + xchg_stage<LPT>(send, STAGE);
+    }
+    return treduce<LPT, N / 2, STAGE + 1>(w, lane);
+  }
+}
+
+template <int LPT, int G>
+__device__ __forceinline__ int lane_head(int lane) {
+  constexpr int NST = LPT == 32 ? 5 : 4;
+  int h = 0;
+#pragma unroll
+  for (int s = 0; (1 << s) < G; ++s) h = 2 * h + ((lane >> (NST - 1 - s)) & 1);
+  return h;
+}
+
+// A lane holding head g's value, and whether this lane is the first of its
+// (token, head) group.
+template <int LPT, int G>
+__device__ __forceinline__ int head_rep_lane(int g) {
+  constexpr int NST = LPT == 32 ? 5 : 4;
+  int gb = 0;
+  while ((1 << gb) < G) ++gb;
+  return g << (NST - gb);
+}
+template <int LPT, int G>
+__device__ __forceinline__ bool head_leader(int lane) {
+  constexpr int NST = LPT == 32 ? 5 : 4;
+  int gb = 0;
+  while ((1 << gb) < G) ++gb;
+  return (lane & ((1 << (NST - gb)) - 1)) == 0;
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+  return __hiloint2double(hi, lo);
+}
+
+}  // namespace kvc

@@ -60,10 +60,11 @@ class DeviceRun:
     def inputs(self, step):
         return synth.step_inputs(self.wl, step, self.scales, self.cache.k.device)
 
-    def step(self, step, q, kn, vn, refresh=True, merge=None):
+    def step(self, step, q, kn, vn, refresh=True, merge=None, max_len=None):
+        ml = self.max_len if max_len is None else max_len
         kvc.kvc_decode_step(self.cache, kn, vn, self.t, q, self.G, self.scale, self.wl.rule, self.alpha,
                             self.wl.budget, self.out, self.lse, self.s, self.mom, merge, self.evict,
-                            refresh=refresh, max_len=self.max_len, ws=self.ws)
+                            refresh=refresh, max_len=ml, ws=self.ws)
         self.t += 1
 
     # ---------------------------------------------------------- host snapshots
@@ -185,7 +186,8 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
     return stats
 
 
-def lockstep(run: DeviceRun, steps, scopes_for_step, refresh_for_step=lambda t: True, merge=None):
+def lockstep(run: DeviceRun, steps, scopes_for_step, refresh_for_step=lambda t: True, merge=None,
+             max_len_for_step=lambda t: None):
     """Run `steps` decode steps; check the ones for which scopes_for_step(step) is non-empty."""
     report = {}
     for step in range(1, steps + 1):
@@ -196,7 +198,7 @@ def lockstep(run: DeviceRun, steps, scopes_for_step, refresh_for_step=lambda t: 
         if scopes:
             pre = run.snapshot(scopes)
         mg = kvc.merge_desc(q, run.G, run.scale) if merge else None
-        run.step(step, q, kn, vn, refresh=refresh, merge=mg)
+        run.step(step, q, kn, vn, refresh=refresh, merge=mg, max_len=max_len_for_step(step))
         if scopes:
             torch.cuda.synchronize()
             post = run.snapshot(scopes)

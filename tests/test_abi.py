@@ -93,3 +93,40 @@ def test_other_entry_points_reject_bad_arguments():
                               None) == -3
     assert L.kvc_laprox_score(0x10, 0x20, 0x30, 0x40, 1, 30, 8, 100, 4, 128, 4096, 0.1, 0x50, 0x60, 1 << 30,
                               None) == -3
+
+
+# ------------------------------------------------------------ host logic: bytes model
+def _golden(name):
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", name)):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append(line.split())
+    return rows
+
+
+def test_keepkv_memory_arithmetic_matches_page_figures():
+    """KeepKV notes' memory table worked example (LLaMA-3-8B, 32 layers, 32 heads as
+    the page counts them, d = 128, L = 32768, B = 3277) and background KV-size example."""
+    from compressed_decode_attention_gqa_amd import roofline as rf
+    mem = rf.keepkv_memory(32, 32, 3277, 32768, 128)
+    mem["llama70b_kv_bytes"] = rf.kv_cache_bytes(80, 8, 128, 8192, 128) / 2 ** 30
+    for name, val, unit, tol in _golden("keepkv_memory_arithmetic.txt"):
+        got = mem[name]
+        assert abs(got - float(val)) <= float(tol) * float(val), (name, got, val)
+
+
+def test_budget_floor_matches_printed_budget():
+    """InertiaKV §3 budget floor((1 - rho) L0) vs the KeepKV notes' printed B = 3277."""
+    import synth
+    for L0, B_printed in _golden("inertiakv_budgets.txt"):
+        B = synth.budget_for(int(L0))
+        assert B == int(L0) // 10 and abs(B - int(B_printed)) <= 1
+
+
+def test_step_bytes_model():
+    from compressed_decode_attention_gqa_amd import roofline as rf
+    b = rf.unit_step_bytes(L=3277, k=1, G=4)
+    assert b.kv == 3277 * 512
+    assert b.moments == 2 * 128 * 128 * 4 + 2 * 2 * 128 * 4 + 8
+    assert 1_850_000 < b.total < 1_860_000          # ~566 bytes per cached token

@@ -93,16 +93,33 @@ def test_decode_step_c2_full_size():
 
 
 def test_decode_step_c2x32_sampled():
-    """The 32-layer stack in one launch per step, at the benchmark's launch shape; sampled scopes."""
+    """The 32-layer stack in one launch per step at the benchmark's launch shape (step 1 bulk
+    compression over 32769 tokens per head, then steady steps with max_len = budget + 1, which
+    take the one-workgroup-per-head kernel); sampled scopes."""
     rng = np.random.default_rng(5)
     run = DeviceRun(C2X32, max_len=C2X32.context + 1)
 
     def scopes(t):
-        if t in (1, 2, 8):
+        if t in (1, 2, 3, 8):
             return sorted(rng.choice(C2X32.n_scopes, size=24, replace=False).tolist())
         return []
-    rep = lockstep(run, 8, scopes)
+    rep = lockstep(run, 8, scopes, max_len_for_step=lambda t: None if t == 1 else C2X32.budget + 1)
     _say("c2x32", rep)
+
+
+@pytest.mark.parametrize("dtype,G,votes,rule", [("bf16", 4, False, "ema"), ("bf16", 4, True, "single"),
+                                                ("f32", 1, False, "ema"), ("bf16", 2, True, "cumulative"),
+                                                ("bf16", 8, False, "ema")])
+def test_decode_step_per_head_kernel(dtype, G, votes, rule):
+    """Enough single-head scopes (136) and a short cache: every step runs one workgroup per head."""
+    wl = C2.scaled(dtype=dtype, G=G, n_layers=17, context=700, budget=130, steps=5, rule=rule,
+                   key_scales=dtype == "bf16", prior_votes=votes)
+    if votes:
+        wl = wl.scaled(budget=wl.context // 10 * 9)
+    run = DeviceRun(wl, max_len=wl.initial_len + 1)
+    assert wl.n_scopes >= 128
+    rep = lockstep(run, wl.steps, lambda t: list(range(0, wl.n_scopes, 3)))
+    _say("per-head", dtype, G, votes, rule, rep)
 
 
 def test_determinism():
