@@ -34,7 +34,7 @@ from compressed_decode_attention_gqa_amd import kvc  # noqa: E402
 from compressed_decode_attention_gqa_amd import roofline as rf  # noqa: E402
 
 METRIC = "cached tokens attended+scored+evicted/sec and % peak HBM GB/s at 32K ctx"
-KERNEL_SOURCES = ["decode.hip", "kvc_ops.h", "kvc_device.h", "kvc_decode.h"]
+KERNEL_SOURCES = ["decode_unit.hip", "kvc_epilogue.h", "kvc_ops.h", "kvc_device.h", "kvc_decode.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2x32_traffic.json")
 
 

@@ -191,7 +191,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.nsub_cap = d.nsub_cap;
   const int CH = kvc::decode_chunk_tokens(c->dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  bool per_scope = attn_units == 1 && c->n_scopes >= kUnitMinScopes;
+  bool per_scope = c->units_per_scope == 1 && c->n_scopes >= kUnitMinScopes;
   if (per_scope) {
     const size_t lds = kvc::decode_unit_lds_bytes(c->dtype, G, max_len) + kUnitStaticLds;
     per_scope = lds <= device_lds_per_block();

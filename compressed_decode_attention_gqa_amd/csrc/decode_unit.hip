@@ -1,0 +1,577 @@
+// Decode step with one workgroup per scope, for launches with one attention
+// unit per scope and enough scopes to fill the device (the layer stack of a
+// model: 256 KV heads).
+//
+// Streaming: each of the four waves takes every fourth sub-chunk of CHW
+// tokens and keeps PF sub-chunks of 16-byte K/V loads in flight. Full
+// sub-chunks are addressed as one uniform base plus the lane's 16-byte
+// offset; only the last sub-chunk clamps per lane and substitutes the
+// appended row. Logits are float64 (exact bf16/fp32 products); the
+// transposed reduction leaves one head's logit in each lane; the per-head
+// running maximum is rescaled only when it moves; each lane forms one weight
+// exp(l - M) (float64 argument split into float hi + lo), and the maximum of
+// every sub-chunk is kept so the epilogue can turn weights into normalised
+// per-token weights. Per-token weights, utilities and votes of the scope live
+// in LDS.
+//
+// Epilogue (same workgroup): combine the four waves' partials, write o and
+// lse, score every token, update the utility, take the single eviction by
+// argmin over (m, pos), fold it into the moments and fill its slot with the
+// last one. The moment sums and the last row are loaded before scoring so
+// the fold does not wait on memory. A step that evicts more than one entry
+// takes the general epilogue.
+#include <type_traits>
+
+#include "kvc_epilogue.h"
+
+namespace kvc {
+
+template <typename T>
+struct UnitGeometry {
+  static constexpr int EPV = ElemTraits<T>::EPV;
+  static constexpr int LPT = HD / EPV;     // lanes per token row
+  static constexpr int TPI = 64 / LPT;     // tokens per wave iteration
+  static constexpr int UNR = 4;            // iterations per sub-chunk
+  static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
+  static constexpr int PF = 4;             // sub-chunks of loads in flight per wave
+  static constexpr int NW = WG / 64;       // waves
+  static constexpr int RB = HD * int(sizeof(T));
+};
+
+int decode_unit_chunk_tokens(int dtype) {
+  return dtype == 0 ? UnitGeometry<bf16_t>::CHW : UnitGeometry<float>::CHW;
+}
+
+// Dynamic LDS: per-token weights e[G][ld], sub-chunk maxima [nsub][G] (double),
+// utilities m[ld] and votes[ld]; ld = lds_len rounded up to whole sub-chunks.
+struct UnitLdsLayout {
+  int ld;
+  size_t e, f, m, v, total;
+};
+
+__host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds_len) {
+  UnitLdsLayout l{};
+  l.ld = (lds_len + chw - 1) / chw * chw;
+  size_t o = 0;
+  l.e = o;
+  o += size_t(G) * l.ld * 4;
+  o = (o + 15) & ~size_t(15);
+  l.f = o;
+  o += size_t(l.ld / chw) * G * 8;
+  l.m = o;
+  o += size_t(l.ld) * 4;
+  l.v = o;
+  o += size_t(l.ld) * 4;
+  l.total = (o + 15) & ~size_t(15);
+  return l;
+}
+
+size_t decode_unit_lds_bytes(int dtype, int G, int lds_len) {
+  return unit_lds_layout(decode_unit_chunk_tokens(dtype), G, lds_len).total;
+}
+
+template <typename T, int G>
+struct UnitLds {
+  using Geo = UnitGeometry<T>;
+  union {
+    float w[Geo::NW][Geo::UNR][Geo::TPI][G];      // streaming: weights for the value sums
+    struct {
+      double pM[Geo::NW][G], pZ[Geo::NW][G];
+      float pO[Geo::NW][G][HD];
+      double M[G], Z[G];
+      float fac[Geo::NW][G];
+      uint64_t wkey[Geo::NW];
+      int wslot[Geo::NW];
+      int ties, tie_pos, tie_slot, best;
+      float rowk[HD], rowv[HD];
+    } ep;
+    EpiLds gen;
+  };
+};
+
+// Loads of one sub-chunk: K and V rows, and the per-token utility and vote.
+template <typename T, bool VOTES>
+struct UnitStream {
+  using Geo = UnitGeometry<T>;
+  static constexpr int UNR = Geo::UNR, TPI = Geo::TPI, CHW = Geo::CHW, RB = Geo::RB;
+  const char *Kb, *Vb, *Kn, *Vn;
+  const float *mrow;
+  const int32_t *vrow;
+  int L, Lold, append, lane, cb, tg;
+
+  __device__ __forceinline__ void issue(u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], float &mv, int &vv, int c) const {
+    if ((c + 1) * CHW <= Lold) {
+      // every token of the sub-chunk is an old, live entry: uniform base + lane offset
+      const char *kb = Kb + int64_t(c) * CHW * RB + 16 * lane;
+      const char *vb = Vb + int64_t(c) * CHW * RB + 16 * lane;
+#pragma unroll
+      for (int it = 0; it < UNR; ++it) {
+        kr[it] = ld16(kb + it * TPI * RB);
+        vr[it] = ld16(vb + it * TPI * RB);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < UNR; ++it) {
+        const int tok = min(c * CHW + it * TPI + tg, L - 1);
+        const bool isnew = append && tok == L - 1;
+        const char *ks = isnew ? Kn : Kb + int64_t(tok) * RB;
+        const char *vs = isnew ? Vn : Vb + int64_t(tok) * RB;
+        kr[it] = ld16(ks + 16 * cb);
+        vr[it] = ld16(vs + 16 * cb);
+      }
+    }
+    const int t1 = min(c * CHW + (lane % CHW), max(Lold - 1, 0));
+    mv = mrow[t1];
+    if (VOTES) vv = vrow[t1];
+  }
+};
+
+template <typename T, int G, bool VOTES>
+__global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
+  using TR = ElemTraits<T>;
+  using Geo = UnitGeometry<T>;
+  constexpr int EPV = Geo::EPV, LPT = Geo::LPT, TPI = Geo::TPI, UNR = Geo::UNR;
+  constexpr int CHW = Geo::CHW, PF = Geo::PF, NW = Geo::NW, RB = Geo::RB;
+  constexpr int D = LPT / G;                         // lanes sharing one (token, head) logit
+  constexpr int ITL = (UNR + D - 1) / D;             // weights a lane forms per sub-chunk
+
+  __shared__ UnitLds<T, G> sh;
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  const int lds_len = a.lds_len;
+  const UnitLdsLayout lay = unit_lds_layout(CHW, G, lds_len);
+  const int ld = lay.ld;
+  float *e_lds = reinterpret_cast<float *>(dyn + lay.e);
+  double *f_lds = reinterpret_cast<double *>(dyn + lay.f);
+  float *m_lds = reinterpret_cast<float *>(dyn + lay.m);
+  int *v_lds = reinterpret_cast<int *>(dyn + lay.v);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.x, gu = scope;
+  const int unit = a.attn_unit0;
+  const int cap = a.capacity;
+  const int64_t sc = int64_t(scope) * cap;
+  int L = a.len[scope] + a.append;
+  const bool overflow = L > cap || L > lds_len;
+  if (overflow) L = 0;
+  const int Lold = L - (L > 0 ? a.append : 0);
+
+  UnitStream<T, VOTES> W;
+  {
+    const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(unit) * a.unit_stride;
+    W.Kb = a.k + row0 * RB;
+    W.Vb = a.v + row0 * RB;
+    W.Kn = a.k_new + (int64_t(scope) * a.units + unit) * RB;
+    W.Vn = a.v_new + (int64_t(scope) * a.units + unit) * RB;
+    W.mrow = a.m + sc;
+    W.vrow = VOTES ? a.votes + sc : nullptr;
+    W.L = L;
+    W.Lold = Lold;
+    W.append = a.append;
+    W.lane = lane;
+    W.cb = lane % LPT;
+    W.tg = lane / LPT;
+  }
+  const int cb = W.cb, tg = W.tg;
+  const int myh = lane_head<LPT, G>(lane);
+  const int dup = lane & (D - 1);
+
+  // queries scaled by tau (exact in float64: bf16/fp32 times a float)
+  double qf[G][EPV];
+  {
+    const T *qp = reinterpret_cast<const T *>(a.q) + int64_t(gu) * G * HD;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) qf[g][j] = double(load_elem<T>(qp, g * HD + cb * EPV + j)) * a.scale;
+  }
+  float oacc[G][EPV];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) oacc[g][j] = 0.f;
+  double Mrun = -INFINITY, Zrun = 0.0;
+
+  const int nsub = L > 0 ? (L + CHW - 1) / CHW : 0;
+  u32x4 kr[PF][UNR], vr[PF][UNR];
+  float mv[PF];
+  int vv[PF];
+  if (nsub > 0) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) W.issue(kr[s], vr[s], mv[s], vv[s], wave + NW * s);
+  }
+  for (int base = wave; base < nsub; base += NW * PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int c = base + NW * s;
+      if (c < nsub) {
+        const bool tail = (c + 1) * CHW > L;
+        // scope arrays of this sub-chunk into LDS
+        if (lane < CHW) {
+          m_lds[c * CHW + lane] = mv[s];
+          if (VOTES) v_lds[c * CHW + lane] = vv[s];
+        }
+        double lg[UNR];
+#pragma unroll
+        for (int it = 0; it < UNR; ++it) {
+          double acc[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) acc[g] = 0.0;
+#pragma unroll
+          for (int j = 0; j < EPV; ++j) {
+            const double kj = double(TR::get(kr[s][it], j));
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = fma(qf[g][j], kj, acc[g]);
+          }
+          lg[it] = treduce<LPT, G, 0>(acc, lane);
+          if (tail && c * CHW + it * TPI + tg >= L) lg[it] = -INFINITY;
+        }
+        double mx = lg[0];
+#pragma unroll
+        for (int it = 1; it < UNR; ++it) mx = fmax(mx, lg[it]);
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o));
+        if (__ballot(mx > Mrun)) {
+          const double Mnew = fmax(Mrun, mx);
+          const double f = Mrun > -INFINITY ? exp(Mrun - Mnew) : 0.0;
+          Zrun *= f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float fg = float(readlane_f64(f, head_rep_lane<LPT, G>(g)));
+#pragma unroll
+            for (int j = 0; j < EPV; ++j) oacc[g][j] *= fg;
+          }
+          Mrun = Mnew;
+        }
+        if (tg == 0 && dup == 0) f_lds[c * G + myh] = Mrun;
+        __builtin_amdgcn_wave_barrier();
+        // one weight per (token, head): lane `dup` takes iterations dup, dup + D, ...
+#pragma unroll
+        for (int r = 0; r < ITL; ++r) {
+          const int it = dup + D * r;
+          if (it < UNR) {
+            double x = lg[0];
+#pragma unroll
+            for (int i2 = 1; i2 < UNR; ++i2) x = it == i2 ? lg[i2] : x;
+            const int tok = c * CHW + it * TPI + tg;
+            const float e = exp_split(x - Mrun);
+            float p = 1.f;
+            if (VOTES) p = (a.append && tok == L - 1) ? 1.f : float(v_lds[min(tok, L - 1)]);
+            const float w = p * e;
+            Zrun += double(w);
+            sh.w[wave][it][tg][myh] = w;
+            if (tok < L) e_lds[myh * ld + tok] = e;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < UNR; ++it) {
+          float wv[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) wv[g] = sh.w[wave][it][tg][g];
+#pragma unroll
+          for (int j = 0; j < EPV; ++j) {
+            const float vj = TR::get(vr[s][it], j);
+#pragma unroll
+            for (int g = 0; g < G; ++g) oacc[g][j] = fmaf(wv[g], vj, oacc[g][j]);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      W.issue(kr[s], vr[s], mv[s], vv[s], c + NW * PF);
+    }
+  }
+
+  // ---- this wave's partials (M, Z per head; value sums) into LDS
+  double zt = Zrun;
+#pragma unroll
+  for (int o = 1; o < D; o <<= 1) zt += __shfl_xor(zt, o);
+#pragma unroll
+  for (int o = LPT; o < 64; o <<= 1) zt += __shfl_xor(zt, o);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      float x = oacc[g][j];
+#pragma unroll
+      for (int o = LPT; o < 64; o <<= 1) x += __shfl_xor(x, o);
+      oacc[g][j] = x;
+    }
+  __syncthreads();   // the weight scratch becomes the epilogue's space
+  if (lane < LPT) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) sh.ep.pO[wave][g][cb * EPV + j] = oacc[g][j];
+  }
+  if (tg == 0 && dup == 0) {
+    sh.ep.pM[wave][myh] = Mrun;
+    sh.ep.pZ[wave][myh] = zt;
+  }
+  __syncthreads();
+  if (overflow) {
+    if (tid == 0) a.status[0] = -4;
+    return;
+  }
+
+  const bool step = a.mode != 0;
+  const int k = step ? max(0, L - a.budget) : 0;
+  if (k > 1) {
+    // several evictions: hand the partials to the general epilogue
+    for (int idx = tid; idx < NW * G * HD; idx += WG) {
+      const int w = idx / (G * HD), r = idx - w * (G * HD);
+      a.partO[(int64_t(gu) * a.n_splits + w) * G * HD + r] = (&sh.ep.pO[0][0][0])[idx];
+    }
+    if (tid < NW * G) {
+      a.partM[int64_t(gu) * a.n_splits * G + tid] = (&sh.ep.pM[0][0])[tid];
+      a.partZ[int64_t(gu) * a.n_splits * G + tid] = (&sh.ep.pZ[0][0])[tid];
+    }
+    __threadfence_block();
+    __syncthreads();
+    decode_epilogue<T, G, CHW>(a, scope, L, sh.gen, e_lds, ld, f_lds, 0);
+    return;
+  }
+
+  // ---- loads the rest of the epilogue needs, issued before scoring
+  const bool fold = step && k == 1 && a.mom_S != nullptr;
+  const int64_t mu = int64_t(scope) * a.units + unit;
+  float4 Sreg[16];
+  float skv = 0.f;
+  if (fold) {
+    const float4 *S4 = reinterpret_cast<const float4 *>(a.mom_S + mu * HD * HD);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) Sreg[j] = S4[tid + WG * j];
+    skv = tid < HD ? a.mom_sk[mu * HD + tid] : a.mom_sv[mu * HD + tid - HD];
+  }
+  // the last live row (the appended one when appending): one 16-byte vector per
+  // thread, K in threads [0, NV), V in [NV, 2 NV)
+  constexpr int NV = RB / 16;
+  const int lastc = tid % NV;
+  const bool lastK = tid < NV, lastV = tid >= NV && tid < 2 * NV;
+  u32x4 lastrow = u32x4(0u);
+  if (L > 0 && (lastK || lastV)) {
+    const char *src = a.append ? (lastK ? W.Kn : W.Vn) : (lastK ? W.Kb : W.Vb) + int64_t(L - 1) * RB;
+    lastrow = ld16(src + 16 * lastc);
+  }
+  int last_pos = a.t;
+  if (!a.append && L > 0) last_pos = a.pos[sc + L - 1];
+
+  // ---- combine the waves
+  if (tid < G) {
+    double M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmax(M, sh.ep.pM[w][tid]);
+    double Z = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (sh.ep.pM[w][tid] > -INFINITY) Z += sh.ep.pZ[w][tid] * exp(sh.ep.pM[w][tid] - M);
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      sh.ep.fac[w][tid] = (Z > 0.0 && sh.ep.pM[w][tid] > -INFINITY) ? float(exp(sh.ep.pM[w][tid] - M) / Z) : 0.f;
+    sh.ep.M[tid] = M;
+    sh.ep.Z[tid] = Z;
+    a.lse[int64_t(gu) * G + tid] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * HD; idx += WG) {
+    const int g = idx / HD, e = idx - (idx / HD) * HD;
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc = fmaf(sh.ep.pO[w][g][e], sh.ep.fac[w][g], acc);
+    a.out[(int64_t(gu) * G + g) * HD + e] = acc;
+  }
+  const bool score = a.refresh && (step || a.s != nullptr);
+  const int nsubL = (L + CHW - 1) / CHW;
+  if (score) {
+    for (int idx = tid; idx < nsubL * G; idx += WG) {
+      const int g = idx % G;
+      const double Z = sh.ep.Z[g];
+      f_lds[idx] = Z > 0.0 ? exp(f_lds[idx] - sh.ep.M[g]) / Z : 0.0;
+    }
+  }
+  __syncthreads();
+
+  // ---- score, utility, argmin over (m, slot)
+  const double inv_heads = 1.0 / double(G);
+  const double alpha = double(a.alpha);
+  uint32_t bestm = 0xffffffffu;
+  int bslot = 0x7fffffff;
+  for (int i = tid; i < L; i += WG) {
+    const bool isnew = a.append && i == L - 1;
+    float mval = isnew ? 0.f : m_lds[i];
+    if (score) {
+      const int c = i / CHW;
+      double acc = 0.0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc += double(e_lds[g * ld + i]) * f_lds[c * G + g];
+      if (VOTES && !isnew) acc *= double(v_lds[i]);
+      const double sv = acc * inv_heads;
+      if (a.s) a.s[sc + i] = float(sv);
+      if (step) mval = float(apply_rule(a.rule, alpha, double(mval), sv));
+    }
+    if ((step && score) || isnew) a.m[sc + i] = mval;
+    m_lds[i] = mval;
+    const uint32_t om = orderable_f32(mval);
+    if (om < bestm) {
+      bestm = om;
+      bslot = i;
+    }
+  }
+  int e1 = -1;
+  if (k == 1) {
+    // (m, slot) minimum, then break exact utility ties by position
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t m2 = __shfl_xor(bestm, o);
+      const int s2 = __shfl_xor(bslot, o);
+      if (m2 < bestm || (m2 == bestm && s2 < bslot)) {
+        bestm = m2;
+        bslot = s2;
+      }
+    }
+    if (lane == 0) {
+      sh.ep.wkey[wave] = bestm;
+      sh.ep.wslot[wave] = bslot;
+    }
+    if (tid == 0) sh.ep.ties = 0;
+    __syncthreads();
+    uint32_t mmin = uint32_t(sh.ep.wkey[0]);
+    int smin = sh.ep.wslot[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const uint32_t m2 = uint32_t(sh.ep.wkey[w]);
+      if (m2 < mmin || (m2 == mmin && sh.ep.wslot[w] < smin)) {
+        mmin = m2;
+        smin = sh.ep.wslot[w];
+      }
+    }
+    int nt = 0;
+    for (int i = tid; i < L; i += WG) nt += orderable_f32(m_lds[i]) == mmin;
+    if (nt) atomicAdd(&sh.ep.ties, nt);
+    __syncthreads();
+    if (sh.ep.ties > 1) {
+      if (tid == 0) {
+        sh.ep.tie_pos = 0x7fffffff;
+        sh.ep.tie_slot = 0x7fffffff;
+      }
+      __syncthreads();
+      for (int i = tid; i < L; i += WG) {
+        if (orderable_f32(m_lds[i]) == mmin) {
+          const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
+          atomicMin(&sh.ep.tie_pos, p);
+        }
+      }
+      __syncthreads();
+      for (int i = tid; i < L; i += WG) {
+        if (orderable_f32(m_lds[i]) == mmin) {
+          const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
+          if (p == sh.ep.tie_pos) atomicMin(&sh.ep.tie_slot, i);
+        }
+      }
+      __syncthreads();
+      smin = sh.ep.tie_slot;
+    }
+    e1 = smin;
+  }
+
+  // ---- append: the new row, vote and position at slot L - 1
+  if (a.append && L > 0) {
+    if (lastK) st16(const_cast<char *>(W.Kb) + int64_t(L - 1) * RB + 16 * lastc, lastrow);
+    if (lastV) st16(const_cast<char *>(W.Vb) + int64_t(L - 1) * RB + 16 * lastc, lastrow);
+    if (tid == 0) {
+      if (a.votes) a.votes[sc + L - 1] = 1;
+      a.pos[sc + L - 1] = a.t;
+    }
+  }
+  if (!step || k == 0) {
+    for (int i = tid; i < L; i += WG) {
+      if (a.evict_out) a.evict_out[sc + i] = 0;
+      if (a.mode == 2) a.flags[sc + i] = 0;
+    }
+    if (tid == 0) a.len[scope] = L;
+    return;
+  }
+
+  // ---- one eviction: flags, fold, fill the hole with the last slot
+  for (int i = tid; i < L; i += WG) {
+    if (a.evict_out) a.evict_out[sc + i] = (i == e1);
+    if (a.mode == 2) a.flags[sc + i] = (i == e1);
+  }
+  if (tid == 0) a.list[sc] = e1;
+  if (fold) {
+    if (e1 == L - 1) {
+      if (lastK || lastV) {
+        float *dst = lastK ? sh.ep.rowk : sh.ep.rowv;
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) dst[lastc * EPV + j] = TR::get(lastrow, j);
+      }
+    } else if (lastK || lastV) {
+      const u32x4 r = ld16((lastK ? W.Kb : W.Vb) + int64_t(e1) * RB + 16 * lastc);
+      float *dst = lastK ? sh.ep.rowk : sh.ep.rowv;
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) dst[lastc * EPV + j] = TR::get(r, j);
+    }
+    __syncthreads();
+    const int col = 4 * (tid & 31), row0 = tid >> 5;
+    const float4 k4 = *reinterpret_cast<const float4 *>(&sh.ep.rowk[col]);
+    float4 *S4 = reinterpret_cast<float4 *>(a.mom_S + mu * HD * HD);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float va = sh.ep.rowv[row0 + 8 * j];
+      float4 x = Sreg[j];
+      x.x = fmaf(va, k4.x, x.x);
+      x.y = fmaf(va, k4.y, x.y);
+      x.z = fmaf(va, k4.z, x.z);
+      x.w = fmaf(va, k4.w, x.w);
+      S4[tid + WG * j] = x;
+    }
+    if (tid < HD) a.mom_sk[mu * HD + tid] = skv + sh.ep.rowk[tid];
+    else a.mom_sv[mu * HD + tid - HD] = skv + sh.ep.rowv[tid - HD];
+    if (tid == 0) a.mom_n[mu] += 1;
+  }
+  if (a.mode == 2) {
+    if (tid == 0) a.len[scope] = L;
+    return;
+  }
+  if (e1 < L - 1) {
+    // the last slot's row (held in registers) moves into the hole
+    if (lastK || lastV) st16(const_cast<char *>(lastK ? W.Kb : W.Vb) + int64_t(e1) * RB + 16 * lastc, lastrow);
+    if (tid == 0) {
+      if (a.votes) a.votes[sc + e1] = a.append ? 1 : v_lds[L - 1];
+      a.pos[sc + e1] = last_pos;
+      a.m[sc + e1] = m_lds[L - 1];
+    }
+  }
+  if (tid == 0) a.len[scope] = L - 1;
+}
+
+template <typename T, int G, bool VOTES>
+static hipError_t launch_unit_tgv(const StepArgs &a, hipStream_t st) {
+  const size_t dyn = decode_unit_lds_bytes(std::is_same<T, float>::value ? 1 : 0, G, a.lds_len);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_decode_unit<T, G, VOTES>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_unit<T, G, VOTES>), dim3(a.n_scopes), dim3(WG), dyn, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int G>
+static hipError_t launch_unit_tg(const StepArgs &a, hipStream_t st) {
+  return a.votes ? launch_unit_tgv<T, G, true>(a, st) : launch_unit_tgv<T, G, false>(a, st);
+}
+
+template <typename T>
+static hipError_t launch_unit_g(const StepArgs &a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_unit_tg<T, 1>(a, st);
+    case 2: return launch_unit_tg<T, 2>(a, st);
+    case 4: return launch_unit_tg<T, 4>(a, st);
+    case 8: return launch_unit_tg<T, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st) {
+  return dtype == 0 ? launch_unit_g<bf16_t>(a, G, st) : launch_unit_g<float>(a, G, st);
+}
+
+}  // namespace kvc

@@ -9,7 +9,8 @@ namespace kvc {
 constexpr int HD = 128;      // head dimension handled by every kernel
 constexpr int WG = 256;      // threads per workgroup (4 waves of 64)
 
-struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+// 16-byte vector: one global/LDS access of 16 bytes per lane.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- element types
 // Storage types of K/V/q: bf16 is carried as its 16-bit pattern.
