@@ -17,9 +17,9 @@ constexpr int kHD = 128;
 constexpr int kTargetWorkgroups = 2048;   // split-K workgroups per launch to aim for
 constexpr int kMergeSplitsMax = 64;
 // One workgroup per scope (no split-K) once there are this many single-unit
-// scopes to spread over the 256 CUs and each scope's live length is bounded.
+// scopes to spread over the 256 CUs, each scope's live length is bounded so
+// its per-token state fits in LDS, and a step evicts at most one entry.
 constexpr int kUnitMinScopes = 128;
-constexpr size_t kUnitStaticLds = 20 * 1024;   // static LDS of the per-scope kernel (upper bound)
 
 // LDS a workgroup may allocate on the current device (160 KB on gfx950).
 size_t device_lds_per_block() {
@@ -65,7 +65,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   const int64_t nu = int64_t(c->n_scopes) * attn_units;
   const int CHW = kvc::decode_unit_chunk_tokens(c->dtype);
   d.nsub_cap = ceil_div(c->capacity, std::min(CH, CHW));
-  d.n_splits = std::max(kvc::kUnitWaves, split_count(int(nu), ceil_div(c->capacity, CH)));
+  d.n_splits = split_count(int(nu), ceil_div(c->capacity, CH));
   d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
   const int64_t cap = c->capacity;
   size_t o = 0;
@@ -191,13 +191,14 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.nsub_cap = d.nsub_cap;
   const int CH = kvc::decode_chunk_tokens(c->dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  bool per_scope = c->units_per_scope == 1 && c->n_scopes >= kUnitMinScopes;
+  bool per_scope = c->units_per_scope == 1 && c->n_scopes >= kUnitMinScopes &&
+                   (a.mode == 0 || int64_t(max_len) <= int64_t(budget) + 1);
   if (per_scope) {
-    const size_t lds = kvc::decode_unit_lds_bytes(c->dtype, G, max_len) + kUnitStaticLds;
+    const size_t lds = kvc::decode_unit_lds_bytes(c->dtype, G, max_len, c->votes != nullptr);
     per_scope = lds <= device_lds_per_block();
   }
   if (per_scope) {
-    a.n_splits = kvc::kUnitWaves;
+    a.n_splits = 1;
     a.lds_len = max_len;
     if (kvc::launch_decode_unit(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
   } else {

@@ -1,41 +1,49 @@
 // Decode step with one workgroup per scope, for launches with one attention
-// unit per scope and enough scopes to fill the device (the layer stack of a
-// model: 256 KV heads).
+// unit per scope, enough scopes to fill the device (the layer stack of a model:
+// 256 KV heads) and at most one eviction per scope (the steady state of a
+// fixed budget).
 //
-// Streaming: each of the four waves takes every fourth sub-chunk of CHW
-// tokens and keeps PF sub-chunks of 16-byte K/V loads in flight. Full
-// sub-chunks are addressed as one uniform base plus the lane's 16-byte
-// offset; only the last sub-chunk clamps per lane and substitutes the
-// appended row. Logits are float64 (exact bf16/fp32 products); the
-// transposed reduction leaves one head's logit in each lane; the per-head
-// running maximum is rescaled only when it moves; each lane forms one weight
-// exp(l - M) (float64 argument split into float hi + lo), and the maximum of
-// every sub-chunk is kept so the epilogue can turn weights into normalised
-// per-token weights. Per-token weights, utilities and votes of the scope live
-// in LDS.
+// Streaming: eight waves (two per SIMD, so one wave's arithmetic overlaps the
+// other's memory waits; four for eight-head groups) each take every NW-th
+// sub-chunk of CHW tokens and keep PF sub-chunks of 16-byte K/V loads in
+// flight. Full sub-chunks are
+// addressed as one uniform base plus the lane's 16-byte offset; only the last
+// sub-chunk clamps per lane and substitutes the appended row. Logits are
+// float64 (exact bf16/fp32 products); each lane keeps its query heads in the
+// lane-permuted order of preduce, so the transposed reduction leaves one
+// head's logit per lane without selects; the per-head running maximum is
+// rescaled only when it moves; each lane forms one weight exp(l - M) (float64
+// argument split into float hi + lo), and the maximum of every sub-chunk is
+// kept so the epilogue can turn weights into normalised per-token weights.
+// Per-token weights, utilities and votes of the scope live in LDS.
 //
-// Epilogue (same workgroup): combine the four waves' partials, write o and
-// lse, score every token, update the utility, take the single eviction by
-// argmin over (m, pos), fold it into the moments and fill its slot with the
-// last one. The moment sums and the last row are loaded before scoring so
-// the fold does not wait on memory. A step that evicts more than one entry
-// takes the general epilogue.
+// Epilogue (same workgroup): combine the waves' partials (one lane per
+// (wave, head)), write o and lse, score every token, update the utility, take
+// the eviction by argmin over (m, slot) with a tie count carried through the
+// same reduction (ties are broken by position), fold it into the moments and
+// fill its slot with the last one. The moment sums and the last row are
+// loaded before scoring so the fold does not wait on memory.
 #include <type_traits>
 
 #include "kvc_epilogue.h"
 
 namespace kvc {
 
-template <typename T>
+// Eight waves (two per SIMD, at most 256 registers each) up to four heads per
+// group; eight heads need more query and accumulator registers than that and
+// run four waves with deeper prefetch.
+template <typename T, int G = 1>
 struct UnitGeometry {
   static constexpr int EPV = ElemTraits<T>::EPV;
   static constexpr int LPT = HD / EPV;     // lanes per token row
   static constexpr int TPI = 64 / LPT;     // tokens per wave iteration
   static constexpr int UNR = 4;            // iterations per sub-chunk
   static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
-  static constexpr int PF = 4;             // sub-chunks of loads in flight per wave
-  static constexpr int NW = WG / 64;       // waves
+  static constexpr int NW = G >= 8 ? 4 : 8;   // waves
+  static constexpr int PF = 16 / NW;       // sub-chunks of loads in flight per wave
+  static constexpr int NT = 64 * NW;       // threads
   static constexpr int RB = HD * int(sizeof(T));
+  static constexpr int NS4 = HD * HD / 4 / NT;   // float4 of the moment matrix per thread
 };
 
 int decode_unit_chunk_tokens(int dtype) {
@@ -49,7 +57,7 @@ struct UnitLdsLayout {
   size_t e, f, m, v, total;
 };
 
-__host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds_len) {
+__host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds_len, bool votes) {
   UnitLdsLayout l{};
   l.ld = (lds_len + chw - 1) / chw * chw;
   size_t o = 0;
@@ -61,38 +69,48 @@ __host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds
   l.m = o;
   o += size_t(l.ld) * 4;
   l.v = o;
-  o += size_t(l.ld) * 4;
+  if (votes) o += size_t(l.ld) * 4;
   l.total = (o + 15) & ~size_t(15);
   return l;
 }
 
-size_t decode_unit_lds_bytes(int dtype, int G, int lds_len) {
-  return unit_lds_layout(decode_unit_chunk_tokens(dtype), G, lds_len).total;
-}
-
 template <typename T, int G>
 struct UnitLds {
-  using Geo = UnitGeometry<T>;
+  using Geo = UnitGeometry<T, G>;
   union {
     float w[Geo::NW][Geo::UNR][Geo::TPI][G];      // streaming: weights for the value sums
     struct {
       double pM[Geo::NW][G], pZ[Geo::NW][G];
       float pO[Geo::NW][G][HD];
-      double M[G], Z[G];
+      double M[G], iZ[G];
       float fac[Geo::NW][G];
-      uint64_t wkey[Geo::NW];
-      int wslot[Geo::NW];
-      int ties, tie_pos, tie_slot, best;
+      uint32_t wkey[Geo::NW];
+      int wslot[Geo::NW], wcnt[Geo::NW];
+      int tie_pos, tie_slot;
       float rowk[HD], rowv[HD];
     } ep;
-    EpiLds gen;
   };
 };
+
+template <typename T>
+static size_t unit_static_lds(int G) {
+  switch (G) {
+    case 1: return sizeof(UnitLds<T, 1>);
+    case 2: return sizeof(UnitLds<T, 2>);
+    case 4: return sizeof(UnitLds<T, 4>);
+    default: return sizeof(UnitLds<T, 8>);
+  }
+}
+
+size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes) {
+  const size_t st = dtype == 0 ? unit_static_lds<bf16_t>(G) : unit_static_lds<float>(G);
+  return st + unit_lds_layout(decode_unit_chunk_tokens(dtype), G, lds_len, votes).total;
+}
 
 // Loads of one sub-chunk: K and V rows, and the per-token utility and vote.
 template <typename T, bool VOTES>
 struct UnitStream {
-  using Geo = UnitGeometry<T>;
+  using Geo = UnitGeometry<T, 1>;
   static constexpr int UNR = Geo::UNR, TPI = Geo::TPI, CHW = Geo::CHW, RB = Geo::RB;
   const char *Kb, *Vb, *Kn, *Vn;
   const float *mrow;
@@ -127,18 +145,19 @@ struct UnitStream {
 };
 
 template <typename T, int G, bool VOTES>
-__global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
+__global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(const StepArgs a) {
   using TR = ElemTraits<T>;
-  using Geo = UnitGeometry<T>;
+  using Geo = UnitGeometry<T, G>;
   constexpr int EPV = Geo::EPV, LPT = Geo::LPT, TPI = Geo::TPI, UNR = Geo::UNR;
-  constexpr int CHW = Geo::CHW, PF = Geo::PF, NW = Geo::NW, RB = Geo::RB;
+  constexpr int CHW = Geo::CHW, PF = Geo::PF, NW = Geo::NW, NT = Geo::NT, RB = Geo::RB;
   constexpr int D = LPT / G;                         // lanes sharing one (token, head) logit
   constexpr int ITL = (UNR + D - 1) / D;             // weights a lane forms per sub-chunk
+  static_assert(NW * G <= 64, "the combine runs in one wave");
 
   __shared__ UnitLds<T, G> sh;
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int lds_len = a.lds_len;
-  const UnitLdsLayout lay = unit_lds_layout(CHW, G, lds_len);
+  const UnitLdsLayout lay = unit_lds_layout(CHW, G, lds_len, VOTES);
   const int ld = lay.ld;
   float *e_lds = reinterpret_cast<float *>(dyn + lay.e);
   double *f_lds = reinterpret_cast<double *>(dyn + lay.f);
@@ -172,17 +191,19 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
     W.tg = lane / LPT;
   }
   const int cb = W.cb, tg = W.tg;
-  const int myh = lane_head<LPT, G>(lane);
+  const int myh = perm_head<LPT, G>(cb);
   const int dup = lane & (D - 1);
 
-  // queries scaled by tau (exact in float64: bf16/fp32 times a float)
+  // queries scaled by tau (exact in float64: bf16/fp32 times a float), slot i
+  // holding head i ^ myh
   double qf[G][EPV];
   {
     const T *qp = reinterpret_cast<const T *>(a.q) + int64_t(gu) * G * HD;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int i = 0; i < G; ++i)
 #pragma unroll
-      for (int j = 0; j < EPV; ++j) qf[g][j] = double(load_elem<T>(qp, g * HD + cb * EPV + j)) * a.scale;
+      for (int j = 0; j < EPV; ++j)
+        qf[i][j] = double(load_elem<T>(qp, (i ^ myh) * HD + cb * EPV + j)) * a.scale;
   }
   float oacc[G][EPV];
 #pragma unroll
@@ -222,7 +243,7 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g] = fma(qf[g][j], kj, acc[g]);
           }
-          lg[it] = treduce<LPT, G, 0>(acc, lane);
+          lg[it] = preduce<LPT, G, 0>(acc);
           if (tail && c * CHW + it * TPI + tg >= L) lg[it] = -INFINITY;
         }
         double mx = lg[0];
@@ -236,7 +257,7 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
           Zrun *= f;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const float fg = float(readlane_f64(f, head_rep_lane<LPT, G>(g)));
+            const float fg = float(readlane_f64(f, perm_rep_lane<LPT, G>(g)));
 #pragma unroll
             for (int j = 0; j < EPV; ++j) oacc[g][j] *= fg;
           }
@@ -308,39 +329,25 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
     sh.ep.pZ[wave][myh] = zt;
   }
   __syncthreads();
-  if (overflow) {
-    if (tid == 0) a.status[0] = -4;
-    return;
-  }
-
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
-  if (k > 1) {
-    // several evictions: hand the partials to the general epilogue
-    for (int idx = tid; idx < NW * G * HD; idx += WG) {
-      const int w = idx / (G * HD), r = idx - w * (G * HD);
-      a.partO[(int64_t(gu) * a.n_splits + w) * G * HD + r] = (&sh.ep.pO[0][0][0])[idx];
-    }
-    if (tid < NW * G) {
-      a.partM[int64_t(gu) * a.n_splits * G + tid] = (&sh.ep.pM[0][0])[tid];
-      a.partZ[int64_t(gu) * a.n_splits * G + tid] = (&sh.ep.pZ[0][0])[tid];
-    }
-    __threadfence_block();
-    __syncthreads();
-    decode_epilogue<T, G, CHW>(a, scope, L, sh.gen, e_lds, ld, f_lds, 0);
+  if (overflow || k > 1) {
+    // k > 1 cannot happen: the host launches this kernel only when
+    // lds_len <= budget + 1, and L <= lds_len here
+    if (tid == 0) a.status[0] = overflow ? -4 : -3;
     return;
   }
 
   // ---- loads the rest of the epilogue needs, issued before scoring
   const bool fold = step && k == 1 && a.mom_S != nullptr;
   const int64_t mu = int64_t(scope) * a.units + unit;
-  float4 Sreg[16];
+  float4 Sreg[Geo::NS4];
   float skv = 0.f;
   if (fold) {
     const float4 *S4 = reinterpret_cast<const float4 *>(a.mom_S + mu * HD * HD);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Sreg[j] = S4[tid + WG * j];
-    skv = tid < HD ? a.mom_sk[mu * HD + tid] : a.mom_sv[mu * HD + tid - HD];
+    for (int j = 0; j < Geo::NS4; ++j) Sreg[j] = S4[tid + NT * j];
+    if (tid < 2 * HD) skv = tid < HD ? a.mom_sk[mu * HD + tid] : a.mom_sv[mu * HD + tid - HD];
   }
   // the last live row (the appended one when appending): one 16-byte vector per
   // thread, K in threads [0, NV), V in [NV, 2 NV)
@@ -355,24 +362,28 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
   int last_pos = a.t;
   if (!a.append && L > 0) last_pos = a.pos[sc + L - 1];
 
-  // ---- combine the waves
-  if (tid < G) {
-    double M = -INFINITY;
+  // ---- combine the waves: lane w * G + g of wave 0 takes wave w's partials of head g
+  if (wave == 0) {
+    constexpr int NC = NW * G;
+    const int w = lane / G, g = lane % G;
+    const bool act = lane < NC;
+    const double pm = act ? sh.ep.pM[w][g] : -INFINITY;
+    double M = pm;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmax(M, sh.ep.pM[w][tid]);
-    double Z = 0.0;
+    for (int o = G; o < NC; o <<= 1) M = fmax(M, __shfl_xor(M, o));
+    const double ew = pm > -INFINITY ? exp(pm - M) : 0.0;
+    double Z = act ? sh.ep.pZ[w][g] * ew : 0.0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-      if (sh.ep.pM[w][tid] > -INFINITY) Z += sh.ep.pZ[w][tid] * exp(sh.ep.pM[w][tid] - M);
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-      sh.ep.fac[w][tid] = (Z > 0.0 && sh.ep.pM[w][tid] > -INFINITY) ? float(exp(sh.ep.pM[w][tid] - M) / Z) : 0.f;
-    sh.ep.M[tid] = M;
-    sh.ep.Z[tid] = Z;
-    a.lse[int64_t(gu) * G + tid] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
+    for (int o = G; o < NC; o <<= 1) Z += __shfl_xor(Z, o);
+    if (act) sh.ep.fac[w][g] = Z > 0.0 ? float(ew / Z) : 0.f;
+    if (lane < G) {
+      sh.ep.M[g] = M;
+      sh.ep.iZ[g] = Z > 0.0 ? 1.0 / Z : 0.0;
+      a.lse[int64_t(gu) * G + g] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * HD; idx += WG) {
+  for (int idx = tid; idx < G * HD; idx += NT) {
     const int g = idx / HD, e = idx - (idx / HD) * HD;
     float acc = 0.f;
 #pragma unroll
@@ -382,20 +393,20 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
   const bool score = a.refresh && (step || a.s != nullptr);
   const int nsubL = (L + CHW - 1) / CHW;
   if (score) {
-    for (int idx = tid; idx < nsubL * G; idx += WG) {
+    for (int idx = tid; idx < nsubL * G; idx += NT) {
       const int g = idx % G;
-      const double Z = sh.ep.Z[g];
-      f_lds[idx] = Z > 0.0 ? exp(f_lds[idx] - sh.ep.M[g]) / Z : 0.0;
+      const double iz = sh.ep.iZ[g];
+      f_lds[idx] = iz > 0.0 ? exp(f_lds[idx] - sh.ep.M[g]) * iz : 0.0;
     }
   }
   __syncthreads();
 
-  // ---- score, utility, argmin over (m, slot)
+  // ---- score, utility; per thread the smallest (m, slot) and how many slots hold that m
   const double inv_heads = 1.0 / double(G);
   const double alpha = double(a.alpha);
   uint32_t bestm = 0xffffffffu;
-  int bslot = 0x7fffffff;
-  for (int i = tid; i < L; i += WG) {
+  int bslot = 0x7fffffff, bcnt = 0;
+  for (int i = tid; i < L; i += NT) {
     const bool isnew = a.append && i == L - 1;
     float mval = isnew ? 0.f : m_lds[i];
     if (score) {
@@ -414,54 +425,61 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
     if (om < bestm) {
       bestm = om;
       bslot = i;
+      bcnt = 1;
+    } else if (om == bestm) {
+      ++bcnt;
     }
   }
   int e1 = -1;
   if (k == 1) {
-    // (m, slot) minimum, then break exact utility ties by position
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const uint32_t m2 = __shfl_xor(bestm, o);
       const int s2 = __shfl_xor(bslot, o);
-      if (m2 < bestm || (m2 == bestm && s2 < bslot)) {
+      const int c2 = __shfl_xor(bcnt, o);
+      if (m2 < bestm) {
         bestm = m2;
         bslot = s2;
+        bcnt = c2;
+      } else if (m2 == bestm) {
+        bslot = min(bslot, s2);
+        bcnt += c2;
       }
     }
     if (lane == 0) {
       sh.ep.wkey[wave] = bestm;
       sh.ep.wslot[wave] = bslot;
+      sh.ep.wcnt[wave] = bcnt;
     }
-    if (tid == 0) sh.ep.ties = 0;
+    if (tid == 0) {
+      sh.ep.tie_pos = 0x7fffffff;
+      sh.ep.tie_slot = 0x7fffffff;
+    }
     __syncthreads();
-    uint32_t mmin = uint32_t(sh.ep.wkey[0]);
-    int smin = sh.ep.wslot[0];
+    uint32_t mmin = sh.ep.wkey[0];
+    int smin = sh.ep.wslot[0], ties = sh.ep.wcnt[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      const uint32_t m2 = uint32_t(sh.ep.wkey[w]);
-      if (m2 < mmin || (m2 == mmin && sh.ep.wslot[w] < smin)) {
+      const uint32_t m2 = sh.ep.wkey[w];
+      if (m2 < mmin) {
         mmin = m2;
         smin = sh.ep.wslot[w];
+        ties = sh.ep.wcnt[w];
+      } else if (m2 == mmin) {
+        smin = min(smin, sh.ep.wslot[w]);
+        ties += sh.ep.wcnt[w];
       }
     }
-    int nt = 0;
-    for (int i = tid; i < L; i += WG) nt += orderable_f32(m_lds[i]) == mmin;
-    if (nt) atomicAdd(&sh.ep.ties, nt);
-    __syncthreads();
-    if (sh.ep.ties > 1) {
-      if (tid == 0) {
-        sh.ep.tie_pos = 0x7fffffff;
-        sh.ep.tie_slot = 0x7fffffff;
-      }
-      __syncthreads();
-      for (int i = tid; i < L; i += WG) {
+    if (ties > 1) {
+      // exact utility ties: the smallest position among them goes
+      for (int i = tid; i < L; i += NT) {
         if (orderable_f32(m_lds[i]) == mmin) {
           const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
           atomicMin(&sh.ep.tie_pos, p);
         }
       }
       __syncthreads();
-      for (int i = tid; i < L; i += WG) {
+      for (int i = tid; i < L; i += NT) {
         if (orderable_f32(m_lds[i]) == mmin) {
           const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
           if (p == sh.ep.tie_pos) atomicMin(&sh.ep.tie_slot, i);
@@ -478,12 +496,12 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
     if (lastK) st16(const_cast<char *>(W.Kb) + int64_t(L - 1) * RB + 16 * lastc, lastrow);
     if (lastV) st16(const_cast<char *>(W.Vb) + int64_t(L - 1) * RB + 16 * lastc, lastrow);
     if (tid == 0) {
-      if (a.votes) a.votes[sc + L - 1] = 1;
+      if (VOTES) a.votes[sc + L - 1] = 1;
       a.pos[sc + L - 1] = a.t;
     }
   }
   if (!step || k == 0) {
-    for (int i = tid; i < L; i += WG) {
+    for (int i = tid; i < L; i += NT) {
       if (a.evict_out) a.evict_out[sc + i] = 0;
       if (a.mode == 2) a.flags[sc + i] = 0;
     }
@@ -492,7 +510,7 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
   }
 
   // ---- one eviction: flags, fold, fill the hole with the last slot
-  for (int i = tid; i < L; i += WG) {
+  for (int i = tid; i < L; i += NT) {
     if (a.evict_out) a.evict_out[sc + i] = (i == e1);
     if (a.mode == 2) a.flags[sc + i] = (i == e1);
   }
@@ -511,21 +529,23 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
       for (int j = 0; j < EPV; ++j) dst[lastc * EPV + j] = TR::get(r, j);
     }
     __syncthreads();
+    // S[r][c] += v_e[r] k_e[c]: thread tid owns columns 4 (tid % 32) .. + 3 of
+    // rows tid / 32 + (NT / 32) j
     const int col = 4 * (tid & 31), row0 = tid >> 5;
     const float4 k4 = *reinterpret_cast<const float4 *>(&sh.ep.rowk[col]);
     float4 *S4 = reinterpret_cast<float4 *>(a.mom_S + mu * HD * HD);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float va = sh.ep.rowv[row0 + 8 * j];
+    for (int j = 0; j < Geo::NS4; ++j) {
+      const float va = sh.ep.rowv[row0 + (NT / 32) * j];
       float4 x = Sreg[j];
       x.x = fmaf(va, k4.x, x.x);
       x.y = fmaf(va, k4.y, x.y);
       x.z = fmaf(va, k4.z, x.z);
       x.w = fmaf(va, k4.w, x.w);
-      S4[tid + WG * j] = x;
+      S4[tid + NT * j] = x;
     }
     if (tid < HD) a.mom_sk[mu * HD + tid] = skv + sh.ep.rowk[tid];
-    else a.mom_sv[mu * HD + tid - HD] = skv + sh.ep.rowv[tid - HD];
+    else if (tid < 2 * HD) a.mom_sv[mu * HD + tid - HD] = skv + sh.ep.rowv[tid - HD];
     if (tid == 0) a.mom_n[mu] += 1;
   }
   if (a.mode == 2) {
@@ -536,7 +556,7 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
     // the last slot's row (held in registers) moves into the hole
     if (lastK || lastV) st16(const_cast<char *>(lastK ? W.Kb : W.Vb) + int64_t(e1) * RB + 16 * lastc, lastrow);
     if (tid == 0) {
-      if (a.votes) a.votes[sc + e1] = a.append ? 1 : v_lds[L - 1];
+      if (VOTES) a.votes[sc + e1] = a.append ? 1 : v_lds[L - 1];
       a.pos[sc + e1] = last_pos;
       a.m[sc + e1] = m_lds[L - 1];
     }
@@ -546,11 +566,12 @@ __global__ __launch_bounds__(WG, 1) void k_decode_unit(const StepArgs a) {
 
 template <typename T, int G, bool VOTES>
 static hipError_t launch_unit_tgv(const StepArgs &a, hipStream_t st) {
-  const size_t dyn = decode_unit_lds_bytes(std::is_same<T, float>::value ? 1 : 0, G, a.lds_len);
+  using Geo = UnitGeometry<T, G>;
+  const size_t dyn = unit_lds_layout(Geo::CHW, G, a.lds_len, VOTES).total;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_decode_unit<T, G, VOTES>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_decode_unit<T, G, VOTES>), dim3(a.n_scopes), dim3(WG), dyn, st, a);
+  hipLaunchKernelGGL((k_decode_unit<T, G, VOTES>), dim3(a.n_scopes), dim3(Geo::NT), dyn, st, a);
   return hipGetLastError();
 }
 

@@ -36,14 +36,14 @@ struct StepArgs {
   uint8_t *flags;
   int32_t *list, *list2;
   int32_t n_splits, nsub_cap;
-  int32_t lds_len;   // per-scope kernel: live tokens its LDS holds
+  int32_t lds_len;   // per-scope kernel: live tokens its LDS holds (at most budget + 1)
 };
 
 int decode_chunk_tokens(int dtype);
 int decode_unit_chunk_tokens(int dtype);
-constexpr int kUnitWaves = 4;   // partial sets per unit written by the one-workgroup-per-scope kernel
 hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st);
 hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st);
-size_t decode_unit_lds_bytes(int dtype, int G, int lds_len);
+// LDS (static + dynamic) of the per-scope kernel for lds_len live tokens
+size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes);
 
 }  // namespace kvc

@@ -60,8 +60,8 @@ __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cas
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
   int lo = __double2loint(x), hi = __double2hiint(x);
-  lo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xf, 0xf, false);
-  hi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xf, 0xf, false);
+  lo = __builtin_amdgcn_mov_dpp(lo, CTRL, 0xf, 0xf, true);
+  hi = __builtin_amdgcn_mov_dpp(hi, CTRL, 0xf, 0xf, true);
   return __hiloint2double(hi, lo);
 }
 
@@ -239,6 +239,56 @@ __device__ __forceinline__ bool head_leader(int lane) {
   int gb = 0;
   while ((1 << gb) < G) ++gb;
   return (lane & ((1 << (NST - gb)) - 1)) == 0;
+}
+
+// ---------------------------------------------- lane-permuted transposed reduction
+// Variant of treduce without per-lane selects. Lane l of a token row keeps in
+// register slot i the partial sum of head i ^ perm_head(l), where perm_head is
+// linear over the lane bits and chosen so that, at each exchange stage, the
+// partner lane's upper-half slots hold the heads of this lane's lower-half
+// slots; slot i then simply adds the partner's slot N/2 + i. The stages pair
+// lanes l and l ^ 16 (32-lane rows only), l ^ 15, l ^ 7, l ^ 2 and l ^ 1, so
+// perm_head must map those masks to G/2, G/4, ... for the first log2(G)
+// stages and to 0 afterwards; its coefficients below solve exactly that.
+template <int G>
+__host__ __device__ constexpr int stage_head_bit(int s) {
+  return (s < (G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0)) ? (G >> (s + 1)) : 0;
+}
+
+template <int LPT, int G>
+__host__ __device__ constexpr int perm_head(int lane) {
+  constexpr int off = LPT == 32 ? 1 : 0;
+  const int c0 = stage_head_bit<G>(off + 3);
+  const int c1 = stage_head_bit<G>(off + 2);
+  const int c2 = stage_head_bit<G>(off + 1) ^ c0 ^ c1;
+  const int c3 = stage_head_bit<G>(off) ^ stage_head_bit<G>(off + 1);
+  const int c4 = LPT == 32 ? stage_head_bit<G>(0) : 0;
+  return ((lane & 1) ? c0 : 0) ^ ((lane & 2) ? c1 : 0) ^ ((lane & 4) ? c2 : 0) ^ ((lane & 8) ? c3 : 0) ^
+         ((lane & 16) ? c4 : 0);
+}
+
+// First lane of a token row whose reduced value is head g's.
+template <int LPT, int G>
+__host__ __device__ constexpr int perm_rep_lane(int g) {
+  for (int l = 0; l < LPT; ++l)
+    if (perm_head<LPT, G>(l) == g) return l;
+  return 0;
+}
+
+template <int LPT, int N, int STAGE>
+__device__ __forceinline__ double preduce(const double (&v)[N]) {
+  constexpr int NST = LPT == 32 ? 5 : 4;
+  if constexpr (N == 1) {
+    double x = v[0];
+#pragma unroll
+    for (int s = STAGE; s < NST; ++s) x += xchg_stage<LPT>(x, s);
+    return x;
+  } else {
+    double w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) w[i] = v[i] + xchg_stage<LPT>(v[N / 2 + i], STAGE);
+    return preduce<LPT, N / 2, STAGE + 1>(w);
+  }
 }
 
 __device__ __forceinline__ double readlane_f64(double x, int lane) {

@@ -23,12 +23,16 @@ def _say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("dtype,G,L,votes", [("bf16", 4, 1000, True), ("bf16", 4, 129, False),
-                                              ("f32", 1, 777, False), ("bf16", 1, 300, True),
-                                              ("bf16", 8, 260, False), ("f32", 4, 65, True)])
-def test_attn_score_matches_oracle(dtype, G, L, votes):
-    _say("attn_score", dtype, G, L, votes)
-    wl = C2.scaled(dtype=dtype, G=G, context=L, budget=L, n_kv=3, key_scales=True, prior_votes=False)
+@pytest.mark.parametrize("dtype,G,L,votes,layers", [("bf16", 4, 1000, True, 1), ("bf16", 4, 129, False, 1),
+                                                     ("f32", 1, 777, False, 1), ("bf16", 1, 300, True, 1),
+                                                     ("bf16", 8, 260, False, 1), ("f32", 4, 65, True, 1),
+                                                     # 136 scopes: one workgroup per head
+                                                     ("bf16", 4, 517, True, 46), ("bf16", 8, 300, False, 46),
+                                                     ("f32", 2, 201, False, 46), ("bf16", 1, 90, True, 46)])
+def test_attn_score_matches_oracle(dtype, G, L, votes, layers):
+    _say("attn_score", dtype, G, L, votes, layers)
+    wl = C2.scaled(dtype=dtype, G=G, context=L, budget=L, n_kv=3, n_layers=layers, key_scales=True,
+                   prior_votes=False)
     run = DeviceRun(wl, capacity=L + 5)
     if votes:
         run.cache.votes = torch.randint(0, 4, (wl.n_scopes, run.cache.capacity), dtype=torch.int32, device="cuda")
@@ -111,14 +115,16 @@ def test_decode_step_c2x32_sampled():
                                                 ("f32", 1, False, "ema"), ("bf16", 2, True, "cumulative"),
                                                 ("bf16", 8, False, "ema")])
 def test_decode_step_per_head_kernel(dtype, G, votes, rule):
-    """Enough single-head scopes (136) and a short cache: every step runs one workgroup per head."""
+    """Enough single-head scopes (136) and a short cache: steady steps run one workgroup per head."""
     wl = C2.scaled(dtype=dtype, G=G, n_layers=17, context=700, budget=130, steps=5, rule=rule,
                    key_scales=dtype == "bf16", prior_votes=votes)
     if votes:
         wl = wl.scaled(budget=wl.context // 10 * 9)
     run = DeviceRun(wl, max_len=wl.initial_len + 1)
     assert wl.n_scopes >= 128
-    rep = lockstep(run, wl.steps, lambda t: list(range(0, wl.n_scopes, 3)))
+    # step 1 compresses in bulk (split kernel); later steps evict one entry each
+    rep = lockstep(run, wl.steps, lambda t: list(range(0, wl.n_scopes, 3)),
+                   max_len_for_step=lambda t: None if t == 1 else wl.budget + 1)
     _say("per-head", dtype, G, votes, rule, rep)
 
 
