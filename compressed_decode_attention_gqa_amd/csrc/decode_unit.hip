@@ -22,7 +22,10 @@
 // the eviction by argmin over (m, slot) with a tie count carried through the
 // same reduction (ties are broken by position), fold it into the moments and
 // fill its slot with the last one. The moment sums and the last row are
-// loaded before scoring so the fold does not wait on memory.
+// loaded before scoring so the fold does not wait on memory. Barriers order
+// LDS only, so those loads (and the streaming's last, unused prefetches) stay
+// in flight across them; no global location is written by one thread and
+// read or rewritten by another.
 #include <type_traits>
 
 #include "kvc_epilogue.h"
@@ -41,6 +44,9 @@ struct UnitGeometry {
   static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
   static constexpr int NW = G >= 8 ? 4 : 8;   // waves
   static constexpr int PF = 16 / NW;       // sub-chunks of loads in flight per wave
+  // (Waves 0-3 finish streaming well before waves 4-7: a SIMD's issue
+  // arbiter favours the older of its two waves. Giving them a larger share
+  // of sub-chunks moves the imbalance without shortening the makespan.)
   static constexpr int NT = 64 * NW;       // threads
   static constexpr int RB = HD * int(sizeof(T));
   static constexpr int NS4 = HD * HD / 4 / NT;   // float4 of the moment matrix per thread
@@ -317,7 +323,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       for (int o = LPT; o < 64; o <<= 1) x += __shfl_xor(x, o);
       oacc[g][j] = x;
     }
-  __syncthreads();   // the weight scratch becomes the epilogue's space
+  lds_barrier();   // the weight scratch becomes the epilogue's space
   if (lane < LPT) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -328,7 +334,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     sh.ep.pM[wave][myh] = Mrun;
     sh.ep.pZ[wave][myh] = zt;
   }
-  __syncthreads();
+  lds_barrier();
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
   if (overflow || k > 1) {
@@ -382,7 +388,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       a.lse[int64_t(gu) * G + g] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int idx = tid; idx < G * HD; idx += NT) {
     const int g = idx / HD, e = idx - (idx / HD) * HD;
     float acc = 0.f;
@@ -399,7 +405,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       f_lds[idx] = iz > 0.0 ? exp(f_lds[idx] - sh.ep.M[g]) * iz : 0.0;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- score, utility; per thread the smallest (m, slot) and how many slots hold that m
   const double inv_heads = 1.0 / double(G);
@@ -455,7 +461,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       sh.ep.tie_pos = 0x7fffffff;
       sh.ep.tie_slot = 0x7fffffff;
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t mmin = sh.ep.wkey[0];
     int smin = sh.ep.wslot[0], ties = sh.ep.wcnt[0];
 #pragma unroll
@@ -478,14 +484,14 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
           atomicMin(&sh.ep.tie_pos, p);
         }
       }
-      __syncthreads();
+      lds_barrier();
       for (int i = tid; i < L; i += NT) {
         if (orderable_f32(m_lds[i]) == mmin) {
           const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
           if (p == sh.ep.tie_pos) atomicMin(&sh.ep.tie_slot, i);
         }
       }
-      __syncthreads();
+      lds_barrier();
       smin = sh.ep.tie_slot;
     }
     e1 = smin;
@@ -528,7 +534,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
 #pragma unroll
       for (int j = 0; j < EPV; ++j) dst[lastc * EPV + j] = TR::get(r, j);
     }
-    __syncthreads();
+    lds_barrier();
     // S[r][c] += v_e[r] k_e[c]: thread tid owns columns 4 (tid % 32) .. + 3 of
     // rows tid / 32 + (NT / 32) j
     const int col = 4 * (tid & 31), row0 = tid >> 5;
@@ -558,8 +564,9 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     if (tid == 0) {
       if (VOTES) a.votes[sc + e1] = a.append ? 1 : v_lds[L - 1];
       a.pos[sc + e1] = last_pos;
-      a.m[sc + e1] = m_lds[L - 1];
     }
+    // the thread that stored slot e1's utility in the score pass overwrites it
+    if (tid == e1 % NT) a.m[sc + e1] = m_lds[L - 1];
   }
   if (tid == 0) a.len[scope] = L - 1;
 }

@@ -140,6 +140,15 @@ __device__ __forceinline__ uint64_t order_key(float value, uint32_t pos) {
   return (uint64_t(orderable_f32(value)) << 32) | pos;
 }
 
+// Workgroup barrier that orders LDS only: global loads and stores in flight
+// stay in flight across it (__syncthreads also waits for them). Global memory
+// written by one thread and read or rewritten by another needs __syncthreads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- memory model
 // Release this thread's global writes to every workgroup on the device.
 __device__ __forceinline__ void release_device() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
