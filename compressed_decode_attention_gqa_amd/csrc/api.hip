@@ -377,8 +377,7 @@ int32_t kvc_laprox_score(const void *q_win, const void *k, const void *v, const 
                          float *score, void *ws, size_t ws_bytes, void *stream) {
   if (!q_win || !k || !v || !w_o || !score) return KVC_ERR_ARG;
   if (n_layers <= 0 || H <= 0 || n_kv <= 0 || N <= 0 || w <= 0 || D <= 0) return KVC_ERR_ARG;
-  if (d != kHD || H % n_kv != 0 || !valid_G(H / n_kv) || w > N) return KVC_ERR_UNSUPPORTED;
-  if (D % 128 != 0 || w > 64) return KVC_ERR_UNSUPPORTED;
+  if (d != kHD || !kvc::laprox_shape_supported(H, n_kv, N, w, D)) return KVC_ERR_UNSUPPORTED;
   if (!aligned16(q_win) || !aligned16(k) || !aligned16(v) || !aligned16(w_o)) return KVC_ERR_ALIGN;
   if (!ws || ws_bytes < kvc::laprox_workspace_bytes(n_layers, H, n_kv, N, w, d, D)) return KVC_ERR_WORKSPACE;
   if (kvc::launch_laprox(q_win, k, v, w_o, n_layers, H, n_kv, N, w, D, double(scale), score, ws,

@@ -7,6 +7,9 @@
 
 namespace kvc {
 
+// Shapes the kernels take: G = H / n_kv in {1, 2, 4, 8}, G w a multiple of 8,
+// 0 < w <= N, D a positive multiple of 64 (head_dim is 128).
+bool laprox_shape_supported(int H, int n_kv, int N, int w, int D);
 size_t laprox_workspace_bytes(int n_layers, int H, int n_kv, int N, int w, int d, int D);
 hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const void *w_o, int n_layers,
                          int H, int n_kv, int N, int w, int D, double scale, float *score, void *ws,

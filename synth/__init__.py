@@ -18,7 +18,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .workloads import Workload, WORKLOADS, budget_for  # noqa: F401  (re-export)
+from .workloads import LAPROX_WORKLOADS, LaproxWorkload, Workload, WORKLOADS, budget_for  # noqa: F401  (re-export)
 
 S_K, S_V, S_SCALE, S_OUTLIER, S_Q, S_NEWK, S_NEWV, S_VOTES, S_WO, S_QWIN, S_POS = range(11)
 
@@ -121,6 +121,17 @@ def output_projection(n_layers: int, H: int, d: int, D: int, seed: int, device="
 def window_queries(n_layers: int, H: int, w: int, d: int, seed: int, device="cpu") -> torch.Tensor:
     """Observation-window queries (the last w prompt positions): [n_layers, H, w, d] bf16 ~ N(0,1)."""
     return _randn((n_layers, H, w, d), seed, S_QWIN, None, device).to(torch.bfloat16)
+
+
+def laprox_inputs(lw, device="cpu"):
+    """Prefill tensors of a LaProx workload: q_win [n_layers, H, w, d], k and v
+    [n_layers, n_kv, N, d] (K, V ~ N(0,1) as in kv_rows, unit order
+    layer-major), w_o [n_layers, H, d, D] ~ N(0, 0.02^2); all bf16."""
+    units = lw.n_layers * lw.n_kv
+    k, v = kv_rows(units, lw.N, lw.d, "bf16", lw.seed, device)
+    return {"q_win": window_queries(lw.n_layers, lw.H, lw.w, lw.d, lw.seed, device),
+            "k": k.view(lw.n_layers, lw.n_kv, lw.N, lw.d), "v": v.view(lw.n_layers, lw.n_kv, lw.N, lw.d),
+            "w_o": output_projection(lw.n_layers, lw.H, lw.d, lw.D, lw.seed, device)}
 
 
 def cache_tensors(wl: Workload, device="cpu", capacity: int | None = None, initial_len: int | None = None):

@@ -95,6 +95,39 @@ def test_other_entry_points_reject_bad_arguments():
                               None) == -3
 
 
+@needs_lib
+@pytest.mark.parametrize("H,n_kv,N,w,D,code", [
+    (32, 8, 100, 1, 4096, -3),     # G w = 4: not a whole number of 8-row waves
+    (32, 8, 100, 4, 4000, -3),     # D not a multiple of 64
+    (32, 8, 3, 4, 4096, -3),       # window longer than the prompt
+    (48, 8, 100, 4, 4096, -3),     # G = 6
+    (32, 8, 100, 4, 4096, 0)])     # supported
+def test_laprox_shape_checks(H, n_kv, N, w, D, code):
+    L = kvc.lib()
+    need = L.kvc_laprox_workspace_size(2, H, n_kv, N, w, 128, D)
+    assert (need == 0) == (code != 0)
+    if code:
+        assert L.kvc_laprox_score(0x10, 0x20, 0x30, 0x40, 2, H, n_kv, N, w, 128, D, 0.1, 0x50, 0x60, 1 << 40,
+                                  None) == code
+    else:
+        # the workspace must cover the layout; pointers are checked first
+        assert L.kvc_laprox_score(0x10, 0x20, 0x30, 0x40, 2, H, n_kv, N, w, 128, D, 0.1, 0x50, 0x60, need - 1,
+                                  None) == -6
+        assert L.kvc_laprox_score(None, 0x20, 0x30, 0x40, 2, H, n_kv, N, w, 128, D, 0.1, 0x50, 0x60, need,
+                                  None) == -1
+        assert L.kvc_laprox_score(0x18, 0x20, 0x30, 0x40, 2, H, n_kv, N, w, 128, D, 0.1, 0x50, 0x60, need,
+                                  None) == -5
+
+
+@needs_lib
+def test_laprox_workspace_covers_the_full_size_prefill():
+    # 36 layers x 8 KV heads, N = 65536, w = 32, D = 4096: W_bar hi/lo (2 x 302 MB) dominates
+    need = kvc.kvc_laprox_workspace_size(36, 32, 8, 65536, 32, 128, 4096)
+    units = 36 * 8
+    assert need >= 2 * units * 4096 * 128 * 2 + units * 2 * 65536 * 4 + units * 65536 * 4
+    assert need < 1.2e9
+
+
 # ------------------------------------------------------------ host logic: bytes model
 def _golden(name):
     rows = []
