@@ -103,6 +103,100 @@ def cpu_baseline(run_state, wl, seconds: float):
                       f"k=1, moments on) in {dt:.1f} s, numpy float64 oracle"}
 
 
+LAPROX_STAGES = ["wbar_prep", "window_pass1", "row_combine", "window_pass2", "v_wbar_mfma", "product",
+                 "normalise"]
+
+
+def laprox_cpu_baseline(lw, inp, scale, seconds: float):
+    """The fp64 oracle's per-unit LaProx work (column norms and value-output norms) timed on
+    the host over as many units of the workload as fit in `seconds`."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    G = lw.H // lw.n_kv
+    t0 = time.perf_counter()
+    units = 0
+    while time.perf_counter() - t0 < seconds and units < lw.n_layers * lw.n_kv:
+        l, h = divmod(units, lw.n_kv)
+        f = lambda x: x.float().cpu().numpy().astype(np.float64)
+        Qw = f(inp["q_win"][l, h * G:(h + 1) * G])
+        oracle.window_column_norms(Qw, f(inp["k"][l, h]), scale)
+        oracle.value_output_norms(f(inp["v"][l, h]), f(inp["w_o"][l, h * G:(h + 1) * G]))
+        units += 1
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": units * lw.N / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{units} KV heads of {lw.name} (N={lw.N}, G={G}, w={lw.w}, D={lw.D}): column norms "
+                      f"and value-output norms in {dt:.1f} s, numpy float64 oracle (device-to-host "
+                      f"copies of each head's inputs inside the timed loop)"}
+
+
+def run_laprox(args):
+    lw = synth.LAPROX_WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    inp = synth.laprox_inputs(lw, dev)
+    units = lw.n_layers * lw.n_kv
+    G = lw.H // lw.n_kv
+    scale = float(np.float32(1 / np.sqrt(lw.d)))
+    score = torch.empty((lw.n_layers, lw.n_kv, lw.N), dtype=torch.float32, device=dev)
+    ws = kvc.workspace(kvc.kvc_laprox_workspace_size(lw.n_layers, lw.H, lw.n_kv, lw.N, lw.w, lw.d, lw.D), dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(LAPROX_STAGES) + 1)]
+    for e in marks:
+        e.record()
+
+    def call(ev=None):
+        kvc.kvc_laprox_score(inp["q_win"], inp["k"], inp["v"], inp["w_o"], lw.n_layers, lw.H, lw.n_kv, lw.N,
+                             lw.w, lw.d, lw.D, scale, score, ws, events=ev)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_call = start.elapsed_time(end) / args.steps
+    stage_ms = np.zeros(len(LAPROX_STAGES))
+    for _ in range(args.steps):
+        call(marks)
+        torch.cuda.synchronize()
+        stage_ms += [marks[i].elapsed_time(marks[i + 1]) for i in range(len(LAPROX_STAGES))]
+    stage_ms /= args.steps
+    R = G * lw.w
+    logit_flops = 2.0 * R * lw.N * lw.d * units                  # one window pass
+    vw_flops = 2.0 * lw.N * lw.d * lw.D * units                  # V W_bar, one product
+    stages = {}
+    for name, ms in zip(LAPROX_STAGES, stage_ms):
+        stages[name] = {"ms": float(ms)}
+    for name in ("window_pass1", "window_pass2"):
+        ach = logit_flops / (stages[name]["ms"] / 1e3) / 1e12
+        stages[name].update(bound="alu", achieved=ach, peak=rf.MI355X_FP64_VALU_TFLOPS, unit="TFLOP/s",
+                            frac=ach / rf.MI355X_FP64_VALU_TFLOPS, flops="2 R N d per unit, float64 FMA")
+    ach = vw_flops / (stages["v_wbar_mfma"]["ms"] / 1e3) / 1e12
+    stages["v_wbar_mfma"].update(bound="mfma", achieved=ach, peak=rf.MI355X_BF16_TFLOPS, unit="TFLOP/s",
+                                 frac=ach / rf.MI355X_BF16_TFLOPS,
+                                 flops="2 N d D per unit (executed twice: W_bar as bf16 hi + lo)")
+    dom = max(("window_pass1", "window_pass2", "v_wbar_mfma"), key=lambda n: stages[n]["ms"])
+    d = stages[dom]
+    result = {
+        "metric": "LaProx prefill: tokens scored/sec (model-wide scores of every layer and KV head)",
+        "value": units * lw.N / (ms_per_call / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_call, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 inputs; f64 logits; bf16 MFMA (fp32 acc)", "data": "synthetic",
+        "config": {"workload": lw.name, "layers": lw.n_layers, "q_heads": lw.H, "kv_heads": lw.n_kv,
+                   "head_dim": lw.d, "hidden": lw.D, "prompt": lw.N, "window": lw.w,
+                   "keep_total": lw.keep_total, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
+                     "unit": d["unit"], "frac": d["frac"], "traffic": None, "launch_ms": d["ms"]},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = laprox_cpu_baseline(lw, inp, scale, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +213,11 @@ def main():
               "MI355X; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload in synth.LAPROX_WORKLOADS:
+        if args.steps == 200 and args.warmup == 20:
+            args.steps, args.warmup = 5, 1
+        run_laprox(args)
+        return
     wl = synth.WORKLOADS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)

@@ -375,13 +375,23 @@ size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int3
 int32_t kvc_laprox_score(const void *q_win, const void *k, const void *v, const void *w_o, int32_t n_layers,
                          int32_t H, int32_t n_kv, int32_t N, int32_t w, int32_t d, int32_t D, float scale,
                          float *score, void *ws, size_t ws_bytes, void *stream) {
+  return kvc_laprox_score_marked(q_win, k, v, w_o, n_layers, H, n_kv, N, w, d, D, scale, score, ws, ws_bytes,
+                                 stream, nullptr, 0);
+}
+
+int32_t kvc_laprox_score_marked(const void *q_win, const void *k, const void *v, const void *w_o,
+                                int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w, int32_t d,
+                                int32_t D, float scale, float *score, void *ws, size_t ws_bytes, void *stream,
+                                void *const *events, int32_t n_events) {
+  if (events && n_events != kvc::kLaproxStages + 1) return KVC_ERR_ARG;
   if (!q_win || !k || !v || !w_o || !score) return KVC_ERR_ARG;
   if (n_layers <= 0 || H <= 0 || n_kv <= 0 || N <= 0 || w <= 0 || D <= 0) return KVC_ERR_ARG;
   if (d != kHD || !kvc::laprox_shape_supported(H, n_kv, N, w, D)) return KVC_ERR_UNSUPPORTED;
   if (!aligned16(q_win) || !aligned16(k) || !aligned16(v) || !aligned16(w_o)) return KVC_ERR_ALIGN;
   if (!ws || ws_bytes < kvc::laprox_workspace_bytes(n_layers, H, n_kv, N, w, d, D)) return KVC_ERR_WORKSPACE;
+  hipEvent_t *marks = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
   if (kvc::launch_laprox(q_win, k, v, w_o, n_layers, H, n_kv, N, w, D, double(scale), score, ws,
-                         static_cast<hipStream_t>(stream)) != hipSuccess)
+                         static_cast<hipStream_t>(stream), marks) != hipSuccess)
     return KVC_ERR_DEVICE;
   return KVC_OK;
 }

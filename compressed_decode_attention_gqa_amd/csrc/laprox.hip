@@ -464,7 +464,7 @@ size_t laprox_workspace_bytes(int n_layers, int H, int n_kv, int N, int w, int /
 
 hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const void *w_o, int n_layers,
                          int H, int n_kv, int N, int w, int D, double scale, float *score, void *ws,
-                         hipStream_t st) {
+                         hipStream_t st, hipEvent_t *marks) {
   const LapLayout L = lap_layout(n_layers, H, n_kv, N, w, D);
   char *base = static_cast<char *>(ws);
   LapArgs a{};
@@ -496,21 +496,25 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   a.psum = reinterpret_cast<double *>(base + L.psum);
   const int units = n_layers * n_kv;
 
-  hipLaunchKernelGGL(k_lap_wprep, dim3(D / 64, HD / 64, units), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
+  // marks (optional): an event before the first kernel and after each of the seven
+  auto mark = [&](int i) { return marks ? hipEventRecord(marks[i], st) : hipSuccess; };
+  hipError_t e = mark(0);
   if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_lap_wprep, dim3(D / 64, HD / 64, units), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
   const dim3 wgrid(a.ntiles, a.nh, units);
-  if ((e = window_pass(a, wgrid, st, 1)) != hipSuccess) return e;
+  if ((e = window_pass(a, wgrid, st, 1)) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
   const int n_rows = units * a.R;
   hipLaunchKernelGGL(k_lap_rowfin, dim3((n_rows + 255) / 256), dim3(256), 0, st, a, n_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = window_pass(a, wgrid, st, 2)) != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
+  if ((e = window_pass(a, wgrid, st, 2)) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_lap_vw, dim3((N + VW_TOK - 1) / VW_TOK, units), dim3(VW_NT), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_lap_p, dim3(a.nchunks, units), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_lap_norm, dim3(a.nchunks, units), dim3(256), 0, st, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(7);
 }
 
 }  // namespace kvc

@@ -21,7 +21,8 @@ RULES = {"single": 0, "cumulative": 1, "ema": 2}
 DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
 EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
-            "kvc_moment_update", "kvc_laprox_score", "kvc_decode_step", "kvc_decode_workspace_size",
+            "kvc_moment_update", "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
+            "kvc_decode_workspace_size",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_laprox_workspace_size",
             "kvc_workspace_status", "kvc_status_string", "kvc_version")
 
@@ -60,6 +61,7 @@ _SIGS = {
     "kvc_moment_update": (_I, [_P, _P, _P, _P]),
     "kvc_compact": (_I, [_P, _P, _P, _P, _SZ, _P]),
     "kvc_laprox_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
+    "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
     "kvc_select_workspace_size": (_SZ, [_I, _I]),
     "kvc_compact_workspace_size": (_SZ, [_P]),
@@ -240,7 +242,16 @@ def kvc_compact(cache: Cache, evict, merge: _Merge | None, ws: torch.Tensor, str
                                             _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def kvc_laprox_score(q_win, k, v, w_o, n_layers, H, n_kv, N, w, d, D, scale, score, ws, stream=None):
-    _check("kvc_laprox_score", lib().kvc_laprox_score(
+def kvc_laprox_score(q_win, k, v, w_o, n_layers, H, n_kv, N, w, d, D, scale, score, ws, stream=None,
+                     events=None):
+    """events: None, or 8 recorded-once torch.cuda.Event(enable_timing=True) objects; they are
+    re-recorded on the launch stream around the seven stages."""
+    if events is None:
+        _check("kvc_laprox_score", lib().kvc_laprox_score(
+            _ptr(q_win), _ptr(k), _ptr(v), _ptr(w_o), n_layers, H, n_kv, N, w, d, D, scale, _ptr(score),
+            _ptr(ws), ws.numel(), _stream(stream)))
+        return
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("kvc_laprox_score_marked", lib().kvc_laprox_score_marked(
         _ptr(q_win), _ptr(k), _ptr(v), _ptr(w_o), n_layers, H, n_kv, N, w, d, D, scale, _ptr(score),
-        _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(ws), ws.numel(), _stream(stream), handles, len(events)))
