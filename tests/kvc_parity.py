@@ -143,15 +143,18 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
         ppos = post["pos"][j, :Lp].astype(np.int64)
         alive = sorted(set(pos_all.tolist()) - E_gpu)
         assert sorted(ppos.tolist()) == alive, f"scope {sc}: surviving positions differ"
-        pm = post["m"][j, :Lp].astype(np.float64)
-        mref = np.array([m_ref[p] for p in ppos])
+        merged_pos = None
+        if merge and res.merges[0]:
+            merged_pos = _check_merge(run, sc, j, st, post_ref, res, pre, post, E_gpu, t, knh[sc], vnh[sc], stats)
+        keep_m = ppos != (merged_pos if merged_pos is not None else -1)
+        pm = post["m"][j, :Lp].astype(np.float64)[keep_m]
+        mref = np.array([m_ref[p] for p in ppos[keep_m]])
         dm = np.abs(pm - mref)
         assert np.all(dm <= 1e-5 * np.abs(mref) + 1e-12), f"scope {sc}: rel dm {(dm / (np.abs(mref) + 1e-30)).max()}"
         stats["max_rel_m"] = max(stats["max_rel_m"], float((dm / (np.abs(mref) + 1e-30)).max()))
         slot_of = {p: i for i, p in enumerate(st.pos.tolist())}
         krows_pre = pre["k"][j]
         vrows_pre = pre["v"][j]
-        merged_pos = res.merges[0][1] if (merge and res.merges[0]) else None
         for i, p in enumerate(ppos.tolist()):
             if p == merged_pos:
                 continue
@@ -182,8 +185,52 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
             assert np.all(np.abs(post["sv"][j] - ref["sv"]) <= 1e-5 * mag_v + 1e-6), f"scope {sc}: sv"
     if report is not None:
         for key, val in stats.items():
-            report[key] = max(report.get(key, 0), val) if key != "near_tie_flips" else report.get(key, 0) + val
+            counts = ("near_tie_flips", "partner_tie_flips", "merged_rows_exact")
+            report[key] = report.get(key, 0) + val if key in counts else max(report.get(key, 0), val)
     return stats
+
+
+def _check_merge(run, sc, j, st, post_ref, res, pre, post, E_gpu, t, kn_bits, vn_bits, stats):
+    """The ZIP merge of one scope (KeepKV eqs. (7), (10), (12)): the GPU's partner c is the
+    oracle's unless the two cosines tie within 1e-6; merged rows agree with the oracle's
+    bf16-rounded rows within one bf16 ulp, votes add exactly, utilities add. Returns the
+    position whose row the merge rewrote (skipped by the row-identity check)."""
+    dtype = run.wl.dtype
+    pe_ref, pc_ref, _ = res.merges[0]
+    Lp = int(post["len"][j])
+    ppos = post["pos"][j, :Lp].astype(np.int64)
+    pvotes = post["votes"][j, :Lp].astype(np.int64)
+    pre_votes = np.append(pre["votes"][j, :st.length].astype(np.int64), 1)
+    pos_all = np.append(st.pos, t)
+    vote_of = dict(zip(pos_all.tolist(), pre_votes.tolist()))
+    grown = [p for p, v in zip(ppos.tolist(), pvotes.tolist()) if v != vote_of[p]]
+    assert len(grown) == 1, f"scope {sc}: {len(grown)} entries changed vote"
+    pc = grown[0]
+    (pe,) = tuple(E_gpu)
+    assert int(pvotes[ppos.tolist().index(pc)]) == vote_of[pc] + vote_of[pe]
+    if pe != pe_ref:
+        stats["near_tie_flips"] += 0     # already counted by the evicted-set check
+        return pc
+    if pc != pc_ref:
+        K = np.concatenate([oracle.to_f64(pre["k"][j][0, :st.length], dtype),
+                            oracle.to_f64(kn_bits[0], dtype)[None]], 0)
+        cos = K @ K[list(pos_all).index(pe)] / (np.linalg.norm(K, axis=1) + 1e-300)
+        cg, cr = cos[list(pos_all).index(pc)], cos[list(pos_all).index(pc_ref)]
+        assert abs(cg - cr) <= 1e-6 * abs(cr), f"scope {sc}: merge partner {pc} vs {pc_ref}"
+        stats["partner_tie_flips"] = stats.get("partner_tie_flips", 0) + 1
+        return pc
+    i_gpu = ppos.tolist().index(pc)
+    i_ref = post_ref.pos.tolist().index(pc)
+    for name, ref_rows in (("k", post_ref.K), ("v", post_ref.V)):
+        got = oracle.to_f64(post[name][j][:, i_gpu], dtype)
+        want = ref_rows[:, i_ref]
+        ulp = np.abs(want) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23) + 1e-30
+        assert np.all(np.abs(got - want) <= ulp), f"scope {sc}: merged {name} row off by >1 ulp"
+        stats["merged_rows_exact"] = stats.get("merged_rows_exact", 0) + int(np.array_equal(got, want))
+    m_got = float(post["m"][j, i_gpu])
+    m_want = float(post_ref.m[i_ref])
+    assert abs(m_got - m_want) <= 1e-5 * abs(m_want) + 1e-12, f"scope {sc}: merged utility"
+    return pc
 
 
 def lockstep(run: DeviceRun, steps, scopes_for_step, refresh_for_step=lambda t: True, merge=None,

@@ -193,3 +193,179 @@ def test_select_evict_device_wide_top_k():
     keep = bits(evict) == 0
     ref = oracle.top_k_keep(vals.astype(np.float64), K)
     assert np.array_equal(keep, ref)
+
+
+# ---------------------------------------------------------------- KeepKV: votes and ZIP merge
+C4 = synth.WORKLOADS["c4_keepkv_votes_64k"]
+
+
+def test_decode_step_c4_merge_reduced():
+    """Vote-weighted decode with a ZIP merge every step (KeepKV eqs. (7)-(12)), every scope checked."""
+    wl = C4.scaled(batch=1, n_kv=5, context=3000, budget=300, steps=10)
+    run = DeviceRun(wl)
+    rep = lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)), merge=True)
+    _say("c4 reduced", rep)
+    assert rep.get("merged_rows_exact", 0) > 0
+
+
+def test_decode_step_c4_full_size_sampled():
+    """64 scopes of 6553 voted entries (10% of 64K), merge every step; sampled scopes."""
+    rng = np.random.default_rng(9)
+    run = DeviceRun(C4)
+    rep = lockstep(run, 8, lambda t: sorted(rng.choice(C4.n_scopes, 12, replace=False).tolist())
+                   if t in (1, 2, 5, 8) else [], merge=True)
+    _say("c4 full", rep)
+
+
+def test_merge_keeps_the_reference_output():
+    """KeepKV's single-step check: after the merge, attention of the reference (group-mean)
+    query over the merged cache equals attention over the unmerged cache with the new token."""
+    wl = C4.scaled(batch=1, n_kv=3, context=2000, budget=200, steps=1, G=4)
+    run = DeviceRun(wl)
+    q, kn, vn = run.inputs(1)
+    qbar = q.float().mean(dim=2, keepdim=True).to(q.dtype).contiguous()     # [S, 1, 1, d]
+    # reference output on the unmerged cache: append only (attend, no eviction)
+    snap = DeviceRun(wl)
+    out0 = torch.empty((wl.n_scopes, 1, 1, wl.d), device="cuda")
+    lse0 = torch.empty((wl.n_scopes, 1, 1), device="cuda")
+    kvc.kvc_decode_attn_score(snap.cache, kn, vn, snap.t, qbar, 1, run.scale, out0, lse0, None, 0, snap.ws)
+    run.step(1, q, kn, vn, merge=kvc.merge_desc(q, run.G, run.scale))
+    out1 = torch.empty_like(out0)
+    lse1 = torch.empty_like(lse0)
+    kvc.kvc_decode_attn_score(run.cache, None, None, run.t, qbar, 1, run.scale, out1, lse1, None, 0, run.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(run.cache.length, snap.cache.length - 1)
+    # lossless in exact arithmetic for the mean logit; here the query is its bf16 rounding and
+    # the merged rows are rounded to bf16
+    assert (out1 - out0).abs().max().item() <= 2e-3
+    assert (lse1 - lse0).abs().max().item() <= 2e-3
+
+
+# ---------------------------------------------------------------- model scope (InertiaKV)
+C3 = synth.WORKLOADS["c3_llama8b_model_16k"]
+
+
+def _c3_step(run, step, q, kn, vn, refresh, max_len=None):
+    """One decode step of a model-scope cache: layer by layer, each layer's KV heads attend,
+    score (mean over the layer's query heads), update the shared utility and evict; the new
+    token's rows of every layer are appended by the first layer's call."""
+    wl = run.wl
+    S = wl.n_scopes
+    out_l = torch.empty((S, wl.n_kv, run.G, wl.d), device="cuda")
+    lse_l = torch.empty((S, wl.n_kv, run.G), device="cuda")
+    for l in range(wl.n_layers):
+        u0 = l * wl.n_kv
+        kvc.kvc_decode_step(run.cache, kn if l == 0 else None, vn if l == 0 else None, run.t,
+                            q[:, u0:u0 + wl.n_kv].contiguous(), run.G, run.scale, wl.rule, run.alpha, wl.budget,
+                            out_l, lse_l, run.s, run.mom, None, run.evict if l == 0 else None, refresh=refresh,
+                            attn_unit0=u0, attn_units=wl.n_kv, max_len=max_len or 0, ws=run.ws)
+        run.out[:, u0:u0 + wl.n_kv] = out_l
+        run.lse[:, u0:u0 + wl.n_kv] = lse_l
+    run.t += 1
+
+
+def _c3_check(run, scopes, pre, post, q, kn, vn, t, refresh):
+    wl = run.wl
+    dtype = wl.dtype
+    prm = oracle.StepParams(scale=run.scale, rule=wl.rule, alpha=run.alpha, budget=wl.budget,
+                            groups=wl.n_layers, score=refresh, row_dtype=dtype)
+    idx = torch.as_tensor(scopes, device="cuda")
+    out, lse, s_gpu = bits(run.out[idx]), bits(run.lse[idx]), bits(run.s[idx])
+    qh, knh, vnh = bits(q), bits(kn), bits(vn)
+    worst = 0.0
+    for j, sc in enumerate(scopes):
+        st = oracle_state(pre, j, dtype)
+        post_ref, res = oracle.decode_step(st, oracle.to_f64(knh[sc], dtype), oracle.to_f64(vnh[sc], dtype), t,
+                                           oracle.to_f64(qh[sc], dtype), prm)
+        assert np.abs(out[j] - res.o).max() <= 2e-3 and np.abs(lse[j] - res.lse).max() <= 2e-3
+        Lp = int(post["len"][j])
+        assert Lp == post_ref.length
+        ppos = post["pos"][j, :Lp].astype(np.int64)
+        assert sorted(ppos.tolist()) == sorted(post_ref.pos.tolist()), f"scope {sc}: surviving positions"
+        # the last layer's scores over the final live set
+        if refresh:
+            s_ref = res.s[-1]
+            s_pos = res.s_pos[-1]
+            got = {int(p): float(v) for p, v in zip(ppos, s_gpu[j, :Lp])}
+            for p, v in zip(s_pos.tolist(), s_ref.tolist()):
+                if p in got:
+                    assert abs(got[p] - v) <= 1e-5 * abs(v) + 1e-12, f"scope {sc}: s at pos {p}"
+        m_ref = dict(zip(post_ref.pos.tolist(), post_ref.m.tolist()))
+        pm = post["m"][j, :Lp].astype(np.float64)
+        dm = np.array([abs(a - m_ref[int(p)]) / (abs(m_ref[int(p)]) + 1e-30) for a, p in zip(pm, ppos)])
+        worst = max(worst, float(dm.max()))
+        assert np.all(dm <= 1e-5 + 1e-12), f"scope {sc}: utilities"
+        slot_of = {p: i for i, p in enumerate(st.pos.tolist())}
+        for i, p in enumerate(ppos.tolist()):
+            if p == t:
+                assert np.array_equal(post["k"][j][:, i], knh[sc]) and np.array_equal(post["v"][j][:, i], vnh[sc])
+            else:
+                assert np.array_equal(post["k"][j][:, i], pre["k"][j][:, slot_of[p]])
+    return worst
+
+
+@pytest.mark.parametrize("lazy", [0, 3])
+def test_decode_step_c3_model_scope_reduced(lazy):
+    """One slot set per sequence shared by every layer: score and evict after each layer."""
+    wl = C3.scaled(n_layers=4, batch=2, n_kv=3, context=700, budget=70, steps=7, lazy_refresh=lazy)
+    run = DeviceRun(wl)
+    worst = 0.0
+    for step in range(1, wl.steps + 1):
+        q, kn, vn = run.inputs(step)
+        refresh = lazy == 0 or (step - 1) % lazy == 0
+        scopes = list(range(wl.n_scopes))
+        pre = run.snapshot(scopes)
+        t = run.t
+        _c3_step(run, step, q, kn, vn, refresh)
+        torch.cuda.synchronize()
+        worst = max(worst, _c3_check(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, refresh))
+    assert kvc.kvc_workspace_status(run.ws) == 0
+    _say("c3 reduced lazy=%d: max rel dm %.2e" % (lazy, worst))
+
+
+# ---------------------------------------------------------------- the entry points composed
+def test_entry_points_compose_to_the_step():
+    """attn_score -> ema_update -> select_evict -> moment_update -> compact equals the oracle's
+    step (and the fused step's checks)."""
+    wl = C2.scaled(context=900, budget=90, steps=4, n_kv=5, moments=True)
+    run = DeviceRun(wl)
+    sel_ws = kvc.workspace(kvc.kvc_select_workspace_size(wl.n_scopes, run.cache.capacity))
+    cmp_ws = kvc.workspace(kvc.kvc_compact_workspace_size(run.cache))
+    n_ev = torch.zeros(wl.n_scopes, dtype=torch.int32, device="cuda")
+    rep = {}
+    for step in range(1, wl.steps + 1):
+        q, kn, vn = run.inputs(step)
+        scopes = list(range(wl.n_scopes))
+        pre = run.snapshot(scopes)
+        t = run.t
+        c = run.cache
+        kvc.kvc_decode_attn_score(c, kn, vn, t, q, run.G, run.scale, run.out, run.lse, run.s, 0, run.ws)
+        kvc.kvc_ema_update(c.m, run.s, c.length, wl.n_scopes, c.capacity, wl.rule, run.alpha)
+        run.evict.zero_()
+        kvc.kvc_select_evict(c.m, c.pos, c.length, wl.n_scopes, c.capacity, wl.budget, run.evict, n_ev, sel_ws)
+        kvc.kvc_moment_update(c, run.evict, run.mom)
+        kvc.kvc_compact(c, run.evict, None, cmp_ws)
+        run.t += 1
+        torch.cuda.synchronize()
+        check_step(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, report=rep)
+        assert np.array_equal(n_ev.cpu().numpy(), bits(run.evict).sum(axis=1).astype(np.int32))
+    _say("composed", rep)
+
+
+def test_decode_step_c3_full_size_sampled():
+    """16 sequences x 32 layers x 8 KV heads sharing one slot set per sequence, 16384 -> 1638:
+    the bulk first step and two steady steps, one sequence checked against the oracle."""
+    run = DeviceRun(C3)
+    for step in range(1, 4):
+        q, kn, vn = run.inputs(step)
+        scopes = [5] if step in (1, 3) else []
+        if scopes:
+            pre = run.snapshot(scopes)
+        t = run.t
+        _c3_step(run, step, q, kn, vn, True)
+        if scopes:
+            torch.cuda.synchronize()
+            worst = _c3_check(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, True)
+            _say("c3 full step %d: max rel dm %.2e" % (step, worst))
+    assert int(run.cache.length.min()) == C3.budget == int(run.cache.length.max())
+    assert kvc.kvc_workspace_status(run.ws) == 0
