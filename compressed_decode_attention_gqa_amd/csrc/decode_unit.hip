@@ -8,11 +8,10 @@
 // sub-chunk of CHW tokens and keep PF sub-chunks of 16-byte K/V loads in
 // flight. Full sub-chunks are
 // addressed as one uniform base plus the lane's 16-byte offset; only the last
-// sub-chunk clamps per lane and substitutes the appended row. Logits: a
-// lane's eight bf16 products per head are summed by fp32 dot2 instructions
-// (fp32 caches: float64 FMAs), the sixteen lane sums of a row in float64;
-// each lane keeps its query heads in the lane-permuted order of preduce, so
-// the transposed reduction leaves one head's logit per lane without selects; the per-head running maximum is
+// sub-chunk clamps per lane and substitutes the appended row. Logits are
+// float64 (exact bf16/fp32 products); each lane keeps its query heads in the
+// lane-permuted order of preduce, so the transposed reduction leaves one
+// head's logit per lane without selects; the per-head running maximum is
 // rescaled only when it moves; each lane forms one weight exp(l - M) (float64
 // argument split into float hi + lo), and the maximum of every sub-chunk is
 // kept so the epilogue can turn weights into normalised per-token weights.
@@ -33,29 +32,24 @@
 
 namespace kvc {
 
-#ifndef KVC_UNIT_WAVES
-#define KVC_UNIT_WAVES 8
-#endif
-// Waves per workgroup: eight (two per SIMD, at most 256 registers each) up to
-// four heads per group; eight-head groups need more accumulator registers
-// and run four waves with deeper prefetch.
+// Eight waves (two per SIMD, at most 256 registers each) up to four heads per
+// group; eight heads need more query and accumulator registers than that and
+// run four waves with deeper prefetch.
 template <typename T, int G = 1>
 struct UnitGeometry {
-  static constexpr bool DOT2 = std::is_same<T, bf16_t>::value;
   static constexpr int EPV = ElemTraits<T>::EPV;
   static constexpr int LPT = HD / EPV;     // lanes per token row
   static constexpr int TPI = 64 / LPT;     // tokens per wave iteration
   static constexpr int UNR = 4;            // iterations per sub-chunk
   static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
-  static constexpr int NW = G >= 8 ? 4 : KVC_UNIT_WAVES;   // waves
-  static constexpr int PF = NW >= 16 ? 1 : 16 / NW;   // sub-chunks of loads in flight per wave
-  // (With two waves per SIMD the older wave finishes streaming well before
-  // the younger: the issue arbiter favours it. Giving it a larger share of
-  // sub-chunks moves the imbalance without shortening the makespan.)
+  static constexpr int NW = G >= 8 ? 4 : 8;   // waves
+  static constexpr int PF = 16 / NW;       // sub-chunks of loads in flight per wave
+  // (Waves 0-3 finish streaming well before waves 4-7: a SIMD's issue
+  // arbiter favours the older of its two waves. Giving them a larger share
+  // of sub-chunks moves the imbalance without shortening the makespan.)
   static constexpr int NT = 64 * NW;       // threads
   static constexpr int RB = HD * int(sizeof(T));
   static constexpr int NS4 = HD * HD / 4 / NT;   // float4 of the moment matrix per thread
-  static_assert(NW == 4 || NW == 8 || NW == 16, "the fold maps the moment matrix onto 4, 8 or 16 waves");
 };
 
 int decode_unit_chunk_tokens(int dtype) {
@@ -206,34 +200,16 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   const int myh = perm_head<LPT, G>(cb);
   const int dup = lane & (D - 1);
 
-  // Queries, slot i holding head i ^ myh. bf16: the raw bf16 pairs; each
-  // lane's eight products per head are summed by a chain of four fp32 dot2
-  // instructions (products exact, error at most 2.5 * 2^-24 of the summed
-  // magnitudes per instruction), the sum over lanes in float64, then scaled by
-  // tau. fp32: float64 queries pre-scaled by tau (exact) and float64 FMAs.
-  constexpr bool DOT2 = Geo::DOT2;
-  uint32_t qb[G][4];
+  // queries scaled by tau (exact in float64: bf16/fp32 times a float), slot i
+  // holding head i ^ myh
   double qf[G][EPV];
   {
     const T *qp = reinterpret_cast<const T *>(a.q) + int64_t(gu) * G * HD;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      if constexpr (DOT2) {
-        const u32x4 x = ld16(qp + (i ^ myh) * HD + cb * EPV);
-        qb[i][0] = x.x;
-        qb[i][1] = x.y;
-        qb[i][2] = x.z;
-        qb[i][3] = x.w;
-      } else {
+    for (int i = 0; i < G; ++i)
 #pragma unroll
-        for (int j = 0; j < EPV; ++j)
-          qf[i][j] = double(load_elem<T>(qp, (i ^ myh) * HD + cb * EPV + j)) * a.scale;
-      }
-    }
-    // The query loads complete here, before the streaming loads queue up behind
-    // them: a query load still in flight at the loop would make every sub-chunk
-    // wait for all of its loads (the memory counter is in order).
-    __builtin_amdgcn_s_waitcnt(0);
+      for (int j = 0; j < EPV; ++j)
+        qf[i][j] = double(load_elem<T>(qp, (i ^ myh) * HD + cb * EPV + j)) * a.scale;
   }
   float oacc[G][EPV];
 #pragma unroll
@@ -265,28 +241,15 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
 #pragma unroll
         for (int it = 0; it < UNR; ++it) {
           double acc[G];
-          if constexpr (DOT2) {
-            const u32x4 kv = kr[s][it];
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-              float f = dot2_bf16(kv.x, qb[g][0], 0.f);
-              f = dot2_bf16(kv.y, qb[g][1], f);
-              f = dot2_bf16(kv.z, qb[g][2], f);
-              f = dot2_bf16(kv.w, qb[g][3], f);
-              acc[g] = double(f);
-            }
-            lg[it] = preduce<LPT, G, 0>(acc) * a.scale;
-          } else {
+          for (int g = 0; g < G; ++g) acc[g] = 0.0;
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = 0.0;
+          for (int j = 0; j < EPV; ++j) {
+            const double kj = double(TR::get(kr[s][it], j));
 #pragma unroll
-            for (int j = 0; j < EPV; ++j) {
-              const double kj = double(TR::get(kr[s][it], j));
-#pragma unroll
-              for (int g = 0; g < G; ++g) acc[g] = fma(qf[g][j], kj, acc[g]);
-            }
-            lg[it] = preduce<LPT, G, 0>(acc);
+            for (int g = 0; g < G; ++g) acc[g] = fma(qf[g][j], kj, acc[g]);
           }
+          lg[it] = preduce<LPT, G, 0>(acc);
           if (tail && c * CHW + it * TPI + tg >= L) lg[it] = -INFINITY;
         }
         double mx = lg[0];

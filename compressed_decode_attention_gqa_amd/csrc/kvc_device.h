@@ -53,15 +53,6 @@ template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_
 }
 template <> __device__ __forceinline__ void store_elem<float>(float *p, int64_t i, float x) { p[i] = x; }
 
-// a.bf16[0] * b.bf16[0] + a.bf16[1] * b.bf16[1] + c in fp32 (v_dot2c_f32_bf16):
-// the bf16 products are exact; the result errs by at most 2.5 * 2^-24 of
-// |a0 b0| + |a1 b1| + |c| (measured over 2^20 random cases on gfx950).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                         false);
-}
-
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
