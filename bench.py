@@ -250,19 +250,19 @@ def main():
     torch.cuda.synchronize()
     assert int(cache.length.min()) == B and int(cache.length.max()) == B
 
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # The timed region is K back-to-back launches of the one step kernel on the launch
+    # stream (torch's current stream), bracketed by two HIP events: the average launch
+    # duration of the kernel is the region's length over K (events between launches
+    # would add their own cost to every step).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for j in range(args.steps):
-        ev0[j].record()
         step_call(1 + args.warmup + j, B + 1)
-        ev1[j].record()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
+    launch_ms = total_ms / args.steps
     status = kvc.kvc_workspace_status(ws)
     if status != 0:
         raise SystemExit(f"device status {status} after the timed steps")
