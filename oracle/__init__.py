@@ -9,7 +9,8 @@ only in the seeded inputs of synth/.
 Every function writes out the definition it follows and cites the page, and
 the section or equation on it, that gives that definition:
 
-  * MomentKV (papercache.org summary, arXiv 2606.01563) -- moment statistics.
+  * MomentKV (papercache.org summary, arXiv 2606.01563) -- moment statistics
+    and the normalisation-corrected output (Algorithm 1, phase 2).
   * InertiaKV (translated article, arXiv 2609.03515) -- head-averaged
     last-query score and single / cumulative / EMA utility.
   * KeepKV (reading notes, arXiv 2504.09936) -- vote-weighted attention and
@@ -38,6 +39,7 @@ from .attention import attend_unit, scope_score  # noqa: F401
 from .utility import SINGLE, CUMULATIVE, EMA, RULES, update_utility  # noqa: F401
 from .selection import bottom_k, bottom_k_one_at_a_time, top_k_keep  # noqa: F401
 from .moments import fold_moments, centred_moments, empty_moments  # noqa: F401
+from .moment_correct import corrected_output, evicted_estimates  # noqa: F401
 from .compaction import compact  # noqa: F401
 from .zip_merge import cosine_partner, zip_merge  # noqa: F401
 from .decode_step import ScopeState, StepParams, decode_step  # noqa: F401
