@@ -338,6 +338,20 @@ int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kv
   return KVC_OK;
 }
 
+int32_t kvc_moment_correct(const kvc_moments *mom, int32_t n_units, const void *q, int32_t dtype, int32_t G,
+                           float scale, const float *f_R, const float *lse_R, float *out, void *stream) {
+  if (!mom || !mom->n || !mom->sk || !mom->sv || !mom->S || !q || !f_R || !lse_R || !out) return KVC_ERR_ARG;
+  if (n_units <= 0) return KVC_ERR_ARG;
+  if (dtype != KVC_BF16 && dtype != KVC_F32) return KVC_ERR_DTYPE;
+  if (!valid_G(G)) return KVC_ERR_UNSUPPORTED;
+  if (!aligned16(mom->S)) return KVC_ERR_ALIGN;
+  kvc::MomentArgs m{mom->n, mom->sk, mom->sv, mom->S};
+  if (kvc::launch_moment_correct(m, n_units, q, dtype, G, double(scale), f_R, lse_R, out,
+                                 static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
 int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merge *merge, void *ws,
                     size_t ws_bytes, void *stream) {
   int st = validate_cache(cache);

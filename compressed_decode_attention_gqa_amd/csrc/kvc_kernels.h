@@ -26,6 +26,11 @@ struct MergeArgs {
   int32_t *part_slot;
 };
 
+struct MomentArgs {
+  const int32_t *n;
+  const float *sk, *sv, *S;
+};
+
 size_t wide_state_bytes();
 hipError_t launch_select(const float *key, const int32_t *pos, const int32_t *len, int n_scopes,
                          int cap, int budget, uint8_t *evict, int32_t *n_evict, void *ws,
@@ -34,6 +39,8 @@ hipError_t launch_moment_update(const CacheArgs &c, const uint8_t *evict, int32_
                                 float *sv, float *S, hipStream_t st);
 hipError_t launch_compact(const CacheArgs &c, const uint8_t *evict, int32_t *holes, hipStream_t st);
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st);
+hipError_t launch_moment_correct(const MomentArgs &m, int n_units, const void *q, int dtype, int G, double scale,
+                                 const float *f_R, const float *lse_R, float *out, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);
 

@@ -21,7 +21,7 @@ RULES = {"single": 0, "cumulative": 1, "ema": 2}
 DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
 EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
-            "kvc_moment_update", "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
+            "kvc_moment_update", "kvc_moment_correct", "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
             "kvc_decode_workspace_size",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_laprox_workspace_size",
             "kvc_workspace_status", "kvc_status_string", "kvc_version")
@@ -60,6 +60,7 @@ _SIGS = {
     "kvc_select_evict": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "kvc_moment_update": (_I, [_P, _P, _P, _P]),
     "kvc_compact": (_I, [_P, _P, _P, _P, _SZ, _P]),
+    "kvc_moment_correct": (_I, [_P, _I, _P, _I, _I, _F, _P, _P, _P, _P]),
     "kvc_laprox_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
@@ -233,6 +234,13 @@ def kvc_moment_update(cache: Cache, evict, moments: Moments, stream=None):
     mom = moments.desc()
     _check("kvc_moment_update", lib().kvc_moment_update(ctypes.byref(d), _ptr(evict), ctypes.byref(mom),
                                                         _stream(stream)))
+
+
+def kvc_moment_correct(moments: Moments, n_units: int, q, G: int, scale: float, f_R, lse_R, out, stream=None):
+    mom = moments.desc()
+    dtype = KVC_BF16 if q.dtype == torch.bfloat16 else KVC_F32
+    _check("kvc_moment_correct", lib().kvc_moment_correct(ctypes.byref(mom), n_units, _ptr(q), dtype, G, scale,
+                                                          _ptr(f_R), _ptr(lse_R), _ptr(out), _stream(stream)))
 
 
 def kvc_compact(cache: Cache, evict, merge: _Merge | None, ws: torch.Tensor, stream=None):

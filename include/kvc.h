@@ -155,6 +155,23 @@ int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *le
 int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kvc_moments *mom,
                           void *stream);
 
+/* kvc_moment_correct -- MomentKV normalisation-corrected output (summary page,
+ * Algorithm 1 phase 2, §4.2, with the first-order estimate of §4.1). For each
+ * unit u (scope-major unit order, as in kvc_moments) and query head g:
+ *   if n_e = 0: out = f_R;
+ *   else, with k_bar = s_k/n_e, v_bar = s_v/n_e, S_tilde = S - s_v s_k^T/n_e:
+ *     Z_E_hat = n_e exp(scale q.k_bar)   (Jensen lower bound of Z_E),
+ *     f_E_hat = v_bar + scale S_tilde q / n_e,
+ *     w_R = Z_R / (Z_R + Z_E_hat) with Z_R = exp(lse_R),
+ *     out = w_R f_R + (1 - w_R) f_E_hat.
+ * f_R, lse_R: the attention output and log-partition over the retained set
+ * (e.g. kvc_decode_attn_score on the cache after eviction), [n_units][G][128]
+ * and [n_units][G] fp32; q: [n_units][G][128] in `dtype` (KVC_BF16 or KVC_F32);
+ * out: [n_units][G][128] fp32, may be f_R itself. Arithmetic in float64; the
+ * moment matrix must be 16-byte aligned. */
+int32_t kvc_moment_correct(const kvc_moments *mom, int32_t n_units, const void *q, int32_t dtype, int32_t G,
+                           float scale, const float *f_R, const float *lse_R, float *out, void *stream);
+
 /* kvc_compact -- remove the flagged entries of every scope (MomentKV Algorithm 1
  * step 14; InertiaKV §3: eviction is irreversible). Survivors end in slots
  * [0, len - n_evicted): the j-th evicted slot below the new length receives the
