@@ -6,14 +6,17 @@
 //   ln Z_E_hat = ln n_e + tau (s_k . q) / n_e,
 //   w_R = Z_R / (Z_R + Z_E_hat) = 1 / (1 + exp(ln Z_E_hat - lse_R)),
 //   out = w_R f_R + (1 - w_R) f_E_hat.
-// One 256-thread workgroup per unit: thread pair (2a, 2a + 1) forms row a of
-// S q for every head from 64 contiguous floats each (float64 sums); the moment
-// matrix is read once (64 KB per unit: the kernel is HBM-bound).
+// Four 256-thread workgroups per unit, each owning 32 rows of S (and of the
+// output): eight threads form one row of S q for every head from 16 contiguous
+// floats each (float64 sums). The moment matrix is read once (64 KB per unit:
+// the kernel is HBM-bound).
 #include "kvc_device.h"
 #include "kvc_kernels.h"
 
 namespace kvc {
 namespace {
+
+constexpr int RPB = 32;   // rows of the moment matrix (and of the output) per workgroup
 
 template <typename T, int G>
 __global__ __launch_bounds__(WG) void k_moment_correct(const int32_t *mom_n, const float *mom_sk,
@@ -21,27 +24,30 @@ __global__ __launch_bounds__(WG) void k_moment_correct(const int32_t *mom_n, con
                                                        double scale, const float *f_R, const float *lse_R,
                                                        float *out) {
   __shared__ double qs[G][HD];
-  __shared__ double sq[G][HD];
+  __shared__ double sq[G][RPB];
   __shared__ double kq[G];
-  const int u = blockIdx.x, tid = threadIdx.x;
+  const int a0 = blockIdx.y * RPB, u = blockIdx.x, tid = threadIdx.x;
   const int n = mom_n[u];
   const int64_t o0 = int64_t(u) * G * HD;
   if (n <= 0) {
-    for (int idx = tid; idx < G * HD; idx += WG) out[o0 + idx] = f_R[o0 + idx];
+    for (int idx = tid; idx < G * RPB; idx += WG) {
+      const int64_t o = o0 + (idx / RPB) * HD + a0 + idx % RPB;
+      out[o] = f_R[o];
+    }
     return;
   }
   for (int idx = tid; idx < G * HD; idx += WG) (&qs[0][0])[idx] = double(load_elem<T>(q, o0 + idx));
   __syncthreads();
-  // row a = tid / 2, columns [64 h, 64 h + 64) with h = tid % 2
-  const int a = tid >> 1, h = tid & 1;
-  const float4 *row = reinterpret_cast<const float4 *>(mom_S + (int64_t(u) * HD + a) * HD + 64 * h);
+  // row a0 + tid / 8, columns [16 h, 16 h + 16) with h = tid % 8
+  const int r = tid >> 3, h = tid & 7;
+  const float4 *row = reinterpret_cast<const float4 *>(mom_S + (int64_t(u) * HD + a0 + r) * HD + 16 * h);
   double acc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = 0.0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const float4 s4 = row[j];
-    const int b = 64 * h + 4 * j;
+    const int b = 16 * h + 4 * j;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       acc[g] = fma(double(s4.x), qs[g][b], acc[g]);
@@ -52,8 +58,9 @@ __global__ __launch_bounds__(WG) void k_moment_correct(const int32_t *mom_n, con
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    acc[g] += __shfl_xor(acc[g], 1);
-    if (h == 0) sq[g][a] = acc[g];
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) acc[g] += __shfl_xor(acc[g], o);
+    if (h == 0) sq[g][r] = acc[g];
   }
   if (tid < G) {
     double d = 0.0;
@@ -63,13 +70,14 @@ __global__ __launch_bounds__(WG) void k_moment_correct(const int32_t *mom_n, con
   __syncthreads();
   const double inv_n = 1.0 / double(n);
   const double ln_n = log(double(n));
-  for (int idx = tid; idx < G * HD; idx += WG) {
-    const int g = idx / HD, r = idx - g * HD;
-    const double sv = double(mom_sv[int64_t(u) * HD + r]);
-    const double fE = sv * inv_n + scale * (sq[g][r] - sv * kq[g] * inv_n) * inv_n;
+  for (int idx = tid; idx < G * RPB; idx += WG) {
+    const int g = idx / RPB, rr = idx - g * RPB, a = a0 + rr;
+    const double sv = double(mom_sv[int64_t(u) * HD + a]);
+    const double fE = sv * inv_n + scale * (sq[g][rr] - sv * kq[g] * inv_n) * inv_n;
     const double x = ln_n + scale * kq[g] * inv_n - double(lse_R[int64_t(u) * G + g]);   // ln(Z_E_hat / Z_R)
     const double wR = x > 0.0 ? exp(-x) / (1.0 + exp(-x)) : 1.0 / (1.0 + exp(x));
-    out[o0 + idx] = float(wR * double(f_R[o0 + idx]) + (1.0 - wR) * fE);
+    const int64_t o = o0 + int64_t(g) * HD + a;
+    out[o] = float(wR * double(f_R[o]) + (1.0 - wR) * fE);
   }
 }
 
@@ -78,10 +86,10 @@ hipError_t launch_t(const MomentArgs &m, int n_units, const void *q, int G, doub
                     const float *lse_R, float *out, hipStream_t st) {
   const T *qq = static_cast<const T *>(q);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_moment_correct<T, 1>), dim3(n_units), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
-    case 2: hipLaunchKernelGGL((k_moment_correct<T, 2>), dim3(n_units), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
-    case 4: hipLaunchKernelGGL((k_moment_correct<T, 4>), dim3(n_units), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
-    case 8: hipLaunchKernelGGL((k_moment_correct<T, 8>), dim3(n_units), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
+    case 1: hipLaunchKernelGGL((k_moment_correct<T, 1>), dim3(n_units, HD / RPB), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
+    case 2: hipLaunchKernelGGL((k_moment_correct<T, 2>), dim3(n_units, HD / RPB), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
+    case 4: hipLaunchKernelGGL((k_moment_correct<T, 4>), dim3(n_units, HD / RPB), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
+    case 8: hipLaunchKernelGGL((k_moment_correct<T, 8>), dim3(n_units, HD / RPB), dim3(WG), 0, st, m.n, m.sk, m.sv, m.S, qq, scale, f_R, lse_R, out); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

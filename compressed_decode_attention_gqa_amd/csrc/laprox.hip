@@ -48,7 +48,7 @@ constexpr int VW_WAVES = 8;         // V W_bar workgroup: 8 waves x 64 tokens
 constexpr int VW_NT = 64 * VW_WAVES;
 constexpr int VW_MB = 4;            // 16-token M blocks per wave
 constexpr int VW_TOK = VW_WAVES * VW_MB * 16;   // tokens per workgroup (512)
-constexpr int VW_NB = 16;           // columns per B block
+constexpr int VW_NS = 32;           // columns per LDS stage of W_bar^T
 constexpr int VW_LDS_ROW = HD + 8;  // bf16 per LDS row of a B block (padded)
 
 constexpr int P_CHUNK = 4096;       // tokens per partial sum of p
@@ -270,11 +270,12 @@ __global__ __launch_bounds__(256) void k_lap_rowfin(const LapArgs a, int n_rows)
 // ---------------------------------------------------------------- V W_bar on MFMA
 // grid (ceil(N / 512), units), 512 threads. Wave w holds the A fragments (V
 // rows) of tokens t0 + 64 w + 16 mb + (lane % 16), d elements 32 ks + 8 (lane / 16) ..
-// + 7. B blocks of 16 columns (hi and lo, [n][d] with a padded row) are
-// staged in LDS, double-buffered; every thread loads one 16-byte vector of
-// the next block while the current one is multiplied.
+// + 7. W_bar^T (hi and lo) is staged through LDS in stages of 32 columns
+// ([hi/lo][column][d], rows padded against bank conflicts), double-buffered,
+// with each thread's two 16-byte vectors of a stage loaded three stages
+// ahead; one barrier per stage.
 __global__ __launch_bounds__(VW_NT, 1) void k_lap_vw(const LapArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t bt[2][2][VW_NB][VW_LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint16_t bt[2][2][VW_NS][VW_LDS_ROW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u = blockIdx.y;
   const int N = a.N, D = a.D;
@@ -294,13 +295,27 @@ __global__ __launch_bounds__(VW_NT, 1) void k_lap_vw(const LapArgs a) {
       }
     }
   }
-  // the B vector this thread stages: hi/lo hl, column nn, d elements 8 ee .. + 7
-  const int hl = tid >> 8, nn = (tid >> 4) & 15, ee = tid & 15;
-  const uint16_t *src = (hl ? a.wt_lo : a.wt_hi) + int64_t(u) * D * HD + ee * 8;
-  const int nblk = D / VW_NB;
-  u32x4 stage = ld16(src + int64_t(nn) * HD);
-  *reinterpret_cast<u32x4 *>(&bt[0][hl][nn][ee * 8]) = stage;
-  if (nblk > 1) stage = ld16(src + int64_t(VW_NB + nn) * HD);
+  // the two B vectors this thread stages per stage: the hi and the lo vector of
+  // column tid / 16 of the stage, d elements 8 (tid % 16) .. + 7
+  const int nn = (tid >> 4) & 31, ee = tid & 15;
+  const uint16_t *src_hi = a.wt_hi + int64_t(u) * D * HD + ee * 8;
+  const uint16_t *src_lo = a.wt_lo + int64_t(u) * D * HD + ee * 8;
+  const int nst = D / VW_NS;
+  constexpr int PD = 3;                  // stages of loads in flight
+  u32x4 sreg[PD][2];
+  auto load_stage = [&](u32x4 (&r)[2], int st) {
+    const int col = min(st, nst - 1) * VW_NS + nn;
+    r[0] = ld16(src_hi + int64_t(col) * HD);
+    r[1] = ld16(src_lo + int64_t(col) * HD);
+  };
+  auto store_stage = [&](const u32x4 (&r)[2], int buf) {
+    *reinterpret_cast<u32x4 *>(&bt[buf][0][nn][ee * 8]) = r[0];
+    *reinterpret_cast<u32x4 *>(&bt[buf][1][nn][ee * 8]) = r[1];
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load_stage(sreg[p], p);
+  store_stage(sreg[0], 0);
+  load_stage(sreg[0], PD);
   __syncthreads();
 
   double rs[VW_MB][4];
@@ -309,32 +324,43 @@ __global__ __launch_bounds__(VW_NT, 1) void k_lap_vw(const LapArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rs[mb][i] = 0.0;
 
-  for (int nb = 0; nb < nblk; ++nb) {
-    const int cur = nb & 1;
-    f32x4 acc[VW_MB];
+  for (int sb = 0; sb < nst; sb += PD) {
 #pragma unroll
-    for (int mb = 0; mb < VW_MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < PD; ++p) {
+      const int st = sb + p;
+      if (st < nst) {
+        const int cur = st & 1;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int half = 0; half < VW_NS / 16; ++half) {
+          f32x4 acc[VW_MB];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const u32x4 bx = *reinterpret_cast<const u32x4 *>(&bt[cur][p][m][32 * ks + 8 * kq]);
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, bx);
+          for (int mb = 0; mb < VW_MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mb = 0; mb < VW_MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb][ks], bv, acc[mb], 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              const u32x4 bx = *reinterpret_cast<const u32x4 *>(&bt[cur][q][16 * half + m][32 * ks + 8 * kq]);
+              const bf16x8 bv = __builtin_bit_cast(bf16x8, bx);
+#pragma unroll
+              for (int mb = 0; mb < VW_MB; ++mb)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb][ks], bv, acc[mb], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int mb = 0; mb < VW_MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rs[mb][i] = fma(double(acc[mb][i]), double(acc[mb][i]), rs[mb][i]);
+        }
+        // stage st + 1 (loaded PD - 1 stages ago) into the other buffer, whose
+        // readers finished before the last barrier; its registers take stage st + 1 + PD
+        const int nxt = (p + 1) % PD;
+        if (st + 1 < nst) {
+          store_stage(sreg[nxt], cur ^ 1);
+          load_stage(sreg[nxt], st + 1 + PD);
+        }
+        __syncthreads();
       }
     }
-    // next block into the other buffer (its readers finished before the last barrier)
-    if (nb + 1 < nblk) {
-      *reinterpret_cast<u32x4 *>(&bt[cur ^ 1][hl][nn][ee * 8]) = stage;
-      if (nb + 2 < nblk) stage = ld16(src + int64_t((nb + 2) * VW_NB + nn) * HD);
-    }
-#pragma unroll
-    for (int mb = 0; mb < VW_MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs[mb][i] = fma(double(acc[mb][i]), double(acc[mb][i]), rs[mb][i]);
-    __syncthreads();
   }
   // rs[mb][i]: token 16 mb + 4 (lane / 16) + i, columns = lane % 16 (mod 16):
   // sum over the 16 lanes of each row of lanes
