@@ -20,6 +20,9 @@ constexpr int kMergeSplitsMax = 64;
 // scopes to spread over the 256 CUs, each scope's live length is bounded so
 // its per-token state fits in LDS, and a step evicts at most one entry.
 constexpr int kUnitMinScopes = 128;
+// Bulk eviction (k > 1): fold workgroups per launch to aim for, and the most per unit.
+constexpr int kFoldWorkgroups = 1024;
+constexpr int kFoldSplitsMax = 64;
 
 // LDS a workgroup may allocate on the current device (160 KB on gfx950).
 size_t device_lds_per_block() {
@@ -50,8 +53,9 @@ bool valid_G(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 // ------------------------------------------------------------ decode workspace
 struct DecodeLayout {
   int n_splits, nsub_cap, merge_splits;
+  int bulk_chunks, bulk_chunk, fold_splits, move_blocks;
   size_t status, counters, partM, partZ, partO, fac, subM, ews, flags, list, list2;
-  size_t merge_counters, merge_cos, merge_slot, total;
+  size_t merge_counters, merge_cos, merge_slot, bulk_state, bulk_cnt, fpart, total;
 };
 
 int split_count(int attn_units_total, int nsub) {
@@ -67,6 +71,12 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.nsub_cap = ceil_div(c->capacity, std::min(CH, CHW));
   d.n_splits = split_count(int(nu), ceil_div(c->capacity, CH));
   d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
+  // bulk eviction: slot chunks per scope (<= 256), fold splits per unit, move blocks per scope
+  d.bulk_chunks = std::max(1, std::min({ceil_div(kTargetWorkgroups, c->n_scopes), 256, ceil_div(c->capacity, 256)}));
+  d.bulk_chunk = ceil_div(ceil_div(c->capacity, d.bulk_chunks), 256) * 256;
+  const int64_t units_total = int64_t(c->n_scopes) * c->units_per_scope;
+  d.fold_splits = int(std::max<int64_t>(1, std::min<int64_t>(kFoldSplitsMax, (kFoldWorkgroups + units_total - 1) / units_total)));
+  d.move_blocks = std::max(1, std::min(64, ceil_div(kTargetWorkgroups, c->n_scopes)));
   const int64_t cap = c->capacity;
   size_t o = 0;
   d.status = o;   o = align_up(o + 256);
@@ -83,6 +93,10 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.list2 = o;    o = align_up(o + size_t(c->n_scopes) * cap * 4);
   d.merge_cos = o;  o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 8);
   d.merge_slot = o; o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 4);
+  d.bulk_state = o; o = align_up(o + size_t(c->n_scopes) * sizeof(kvc::BulkScope));
+  d.bulk_cnt = o;   o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 8);
+  d.fpart = o;
+  if (d.fold_splits > 1) o = align_up(o + size_t(units_total) * d.fold_splits * kvc::bulk_part_floats() * 4);
   d.total = o;
   return d;
 }
@@ -202,8 +216,23 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
     a.lds_len = max_len;
     if (kvc::launch_decode_unit(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
   } else {
+    // a step that may evict more than one entry per scope hands those scopes to
+    // the device-wide bulk kernels
+    const bool bulk = a.mode == 1 && int64_t(max_len) > int64_t(budget) + 1;
+    if (bulk) a.bulk = at<kvc::BulkScope>(ws, d.bulk_state);
     a.n_splits = split_count(c->n_scopes * attn_units, ceil_div(max_len, CH));
     if (kvc::launch_decode(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+    if (bulk) {
+      kvc::BulkArgs b{};
+      b.st = a.bulk;
+      b.cnt = at<int32_t>(ws, d.bulk_cnt);
+      b.fpart = at<float>(ws, d.fpart);
+      b.n_chunks = d.bulk_chunks;
+      b.chunk = d.bulk_chunk;
+      b.fold_splits = d.fold_splits;
+      b.move_blocks = d.move_blocks;
+      if (kvc::launch_bulk(a, b, c->dtype, hs) != hipSuccess) return KVC_ERR_DEVICE;
+    }
   }
   if (a.mode == 2) {
     kvc::MergeArgs mg{};

@@ -1,0 +1,372 @@
+// Device-wide eviction of k > 1 entries per scope (the first, bulk step that
+// compresses a prefilled cache down to its budget, or any step whose scopes
+// are far over budget). The attention kernel has already written the new
+// utilities and appended the token; these kernels finish the step over the
+// whole grid instead of one workgroup per scope:
+//
+//   hist x 8   radix select of the k lowest (utility, position) keys: per pass
+//              a per-scope 256-bin histogram of the keys under the current
+//              prefix; the last workgroup of the scope to finish picks the digit
+//              (InertiaKV §3.1: lowest utility first, ties to the lower position)
+//   flags      evicted flags and per-chunk counts of evicted slots and movers
+//   lists      evicted slots ascending; survivors at or above L - k ascending
+//   fold       MomentKV §4.1 / Appendix A.1 moment sums of the evicted rows,
+//              split over several workgroups per unit, partials summed in a
+//              fixed order by a reduce kernel
+//   move       hole filling: mover j goes to evicted slot j (the evicted slots
+//              below L - k come first in the ascending list), then len = L - k
+//
+// Keys are distinct because live positions are distinct, so the final cut
+// takes its bin whole: slot i is evicted iff (key(i) & mask) <= prefix.
+#include "kvc_decode.h"
+#include "kvc_device.h"
+
+namespace kvc {
+
+namespace {
+
+constexpr int FOLD_NB = 16;                     // evicted rows staged per batch
+constexpr int PART_STRIDE = HD * HD + 2 * HD;   // floats per fold partial: S, s_k, s_v
+
+__device__ __forceinline__ uint64_t slot_key(const StepArgs &a, int64_t sc, int i) {
+  return order_key(a.m[sc + i], uint32_t(a.pos[sc + i]));
+}
+
+// ------------------------------------------------------------ radix select pass
+__global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkArgs b, const int shift) {
+  __shared__ uint32_t hist[256];
+  __shared__ int red[8];
+  __shared__ int s_last;
+  const int scope = blockIdx.y, tid = threadIdx.x;
+  BulkScope &st = b.st[scope];
+  if (st.k <= 1 || st.done) return;     // the same for every workgroup of the scope
+  const int L = st.L;
+  const uint64_t prefix = st.prefix, mask = st.mask;
+  const int krem = st.krem;
+  hist[tid] = 0u;
+  __syncthreads();
+  const int64_t sc = int64_t(scope) * a.capacity;
+  const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
+  for (int i = i0 + tid; i < i1; i += WG) {
+    const uint64_t key = slot_key(a, sc, i);
+    if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  const uint32_t c = hist[tid];
+  if (c) atomicAdd(&st.hist[tid], c);
+  release_device();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&st.arrived, 1) == int(gridDim.x) - 1;
+  __syncthreads();
+  if (!s_last) return;
+  acquire_device();
+  // last workgroup of the scope: the bin holding the krem-th key
+  const int cnt = int(__hip_atomic_load(&st.hist[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  int tot;
+  const int excl = wg_exclusive_scan(cnt, red, &tot);
+  if (excl < krem && krem <= excl + cnt) {
+    st.prefix = prefix | (uint64_t(tid) << shift);
+    st.mask = mask | (uint64_t(255) << shift);
+    st.krem = krem - excl;
+    if (cnt == krem - excl || shift == 0) st.done = 1;
+  }
+  st.hist[tid] = 0u;
+  if (tid == 0) st.arrived = 0;
+}
+
+// ------------------------------------------------------------ flags and chunk counts
+__global__ __launch_bounds__(WG) void k_bulk_flags(const StepArgs a, const BulkArgs b) {
+  __shared__ int red[8];
+  const int scope = blockIdx.y, tid = threadIdx.x;
+  const BulkScope &st = b.st[scope];
+  if (st.k <= 1) return;
+  const int L = st.L, B = st.L - st.k;
+  const uint64_t prefix = st.prefix, mask = st.mask;
+  const int64_t sc = int64_t(scope) * a.capacity;
+  const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
+  int n_ev = 0, n_mv = 0;
+  for (int i = i0 + tid; i < i1; i += WG) {
+    const bool ev = (slot_key(a, sc, i) & mask) <= prefix;
+    a.flags[sc + i] = ev ? 1 : 0;
+    if (a.evict_out) a.evict_out[sc + i] = ev ? 1 : 0;
+    n_ev += ev ? 1 : 0;
+    n_mv += (!ev && i >= B) ? 1 : 0;
+  }
+  int te, tm;
+  wg_exclusive_scan(n_ev, red, &te);
+  wg_exclusive_scan(n_mv, red, &tm);
+  if (tid == 0) {
+    int32_t *c = b.cnt + (int64_t(scope) * b.n_chunks + blockIdx.x) * 2;
+    c[0] = te;
+    c[1] = tm;
+  }
+}
+
+// ------------------------------------------------------------ evicted and mover lists
+// a.list: evicted slots ascending (k entries); a.list2: movers ascending.
+__global__ __launch_bounds__(WG) void k_bulk_lists(const StepArgs a, const BulkArgs b) {
+  __shared__ int red[8];
+  const int scope = blockIdx.y, tid = threadIdx.x;
+  BulkScope &st = b.st[scope];
+  if (st.k <= 1) return;
+  const int L = st.L, B = st.L - st.k;
+  const int64_t sc = int64_t(scope) * a.capacity;
+  // bases: counts of the chunks before this one (n_chunks <= 256)
+  int pe = 0, pm = 0;
+  if (tid < int(blockIdx.x)) {
+    const int32_t *c = b.cnt + (int64_t(scope) * b.n_chunks + tid) * 2;
+    pe = c[0];
+    pm = c[1];
+  }
+  int te, tm;
+  wg_exclusive_scan(pe, red, &te);
+  wg_exclusive_scan(pm, red, &tm);
+  int base_e = te, base_m = tm;
+  const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
+  for (int base = i0; base < i1; base += WG) {
+    const int i = base + tid;
+    const bool ev = i < i1 && a.flags[sc + i];
+    const bool mv = i < i1 && !ev && i >= B;
+    int tot;
+    const int r = wg_exclusive_scan((ev ? 1 : 0) | ((mv ? 1 : 0) << 16), red, &tot);
+    if (ev) a.list[sc + base_e + (r & 0xffff)] = i;
+    if (mv) a.list2[sc + base_m + (r >> 16)] = i;
+    base_e += tot & 0xffff;
+    base_m += tot >> 16;
+  }
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) st.n_pairs = base_m;
+}
+
+// ------------------------------------------------------------ moment fold
+// Workgroup f of a unit folds evicted-list entries [f*per, (f+1)*per). Thread t
+// owns S rows {4r..4r+3, 64+4r..64+4r+3} x columns {4c..4c+3, 64+4c..64+4c+3}
+// (r = t/16, c = t%16): per evicted row it reads 8 values of v and 8 of k from
+// LDS (16-byte reads, consecutive lanes on consecutive addresses) for 64 fp32
+// FMAs. Rows are staged 16 at a time, fp32 in LDS, double-buffered: the global
+// loads of batch j+1 are in flight while batch j is folded.
+struct BulkFoldLds {
+  float kb[2][FOLD_NB][HD];
+  float vb[2][FOLD_NB][HD];
+  int32_t slots[WG];
+};
+
+template <typename T>
+struct FoldStage {
+  static constexpr int EPV = ElemTraits<T>::EPV;        // elements per 16 bytes
+  static constexpr int CPR = HD / EPV;                  // 16-byte chunks per row
+  static constexpr int NLD = FOLD_NB * CPR / WG;        // chunks per thread per matrix
+};
+
+template <typename T>
+__device__ __forceinline__ void fold_load(u32x4 (&rk)[FoldStage<T>::NLD], u32x4 (&rv)[FoldStage<T>::NLD],
+                                          const char *Kb, const char *Vb, const int32_t *slots, int e0,
+                                          int ne) {
+  using FS = FoldStage<T>;
+#pragma unroll
+  for (int h = 0; h < FS::NLD; ++h) {
+    const int q = threadIdx.x + WG * h, e = q / FS::CPR, c = q % FS::CPR;
+    if (e < ne) {
+      const int64_t off = int64_t(slots[e0 + e]) * (HD * int64_t(sizeof(T))) + 16 * c;
+      rk[h] = ld16(Kb + off);
+      rv[h] = ld16(Vb + off);
+    } else {
+      rk[h] = u32x4(0u);
+      rv[h] = u32x4(0u);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void fold_stage(const u32x4 (&rk)[FoldStage<T>::NLD],
+                                           const u32x4 (&rv)[FoldStage<T>::NLD], float (*kb)[HD],
+                                           float (*vb)[HD]) {
+  using FS = FoldStage<T>;
+  using TR = ElemTraits<T>;
+#pragma unroll
+  for (int h = 0; h < FS::NLD; ++h) {
+    const int q = threadIdx.x + WG * h, e = q / FS::CPR, c = q % FS::CPR;
+#pragma unroll
+    for (int j = 0; j < FS::EPV; j += 4) {
+      *reinterpret_cast<float4 *>(&kb[e][c * FS::EPV + j]) =
+          make_float4(TR::get(rk[h], j), TR::get(rk[h], j + 1), TR::get(rk[h], j + 2), TR::get(rk[h], j + 3));
+      *reinterpret_cast<float4 *>(&vb[e][c * FS::EPV + j]) =
+          make_float4(TR::get(rv[h], j), TR::get(rv[h], j + 1), TR::get(rv[h], j + 2), TR::get(rv[h], j + 3));
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(WG) void k_bulk_fold(const StepArgs a, const BulkArgs b) {
+  using FS = FoldStage<T>;
+  __shared__ BulkFoldLds sh;
+  const int tid = threadIdx.x;
+  const int scope = blockIdx.y / a.units, u = blockIdx.y - scope * a.units;
+  const BulkScope &st = b.st[scope];
+  if (st.k <= 1) return;
+  const int k = st.k;
+  const int per = (k + b.fold_splits - 1) / b.fold_splits;
+  const int j0 = min(k, int(blockIdx.x) * per), j1 = min(k, j0 + per);
+  const int64_t sc = int64_t(scope) * a.capacity;
+  const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride;
+  const char *Kb = a.k + row0 * (HD * int64_t(sizeof(T)));
+  const char *Vb = a.v + row0 * (HD * int64_t(sizeof(T)));
+  const int r4 = 4 * (tid >> 4), c4 = 4 * (tid & 15);
+
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  float lin = 0.f;   // threads < HD: s_k element tid; others: s_v element tid - HD
+
+  for (int w0 = j0; w0 < j1; w0 += WG) {
+    const int nw = min(WG, j1 - w0);
+    if (tid < nw) sh.slots[tid] = a.list[sc + w0 + tid];
+    __syncthreads();
+    const int nb = (nw + FOLD_NB - 1) / FOLD_NB;
+    u32x4 rk[FS::NLD], rv[FS::NLD];
+    fold_load<T>(rk, rv, Kb, Vb, sh.slots, 0, min(FOLD_NB, nw));
+    for (int bt = 0; bt < nb; ++bt) {
+      const int buf = bt & 1;
+      const int ne = min(FOLD_NB, nw - bt * FOLD_NB);
+      fold_stage<T>(rk, rv, sh.kb[buf], sh.vb[buf]);
+      __syncthreads();
+      if (bt + 1 < nb)
+        fold_load<T>(rk, rv, Kb, Vb, sh.slots, (bt + 1) * FOLD_NB, min(FOLD_NB, nw - (bt + 1) * FOLD_NB));
+      const float(*kb)[HD] = sh.kb[buf];
+      const float(*vb)[HD] = sh.vb[buf];
+#pragma unroll 2
+      for (int e = 0; e < ne; ++e) {
+        const float4 va = *reinterpret_cast<const float4 *>(&vb[e][r4]);
+        const float4 vc = *reinterpret_cast<const float4 *>(&vb[e][64 + r4]);
+        const float4 ka = *reinterpret_cast<const float4 *>(&kb[e][c4]);
+        const float4 kc = *reinterpret_cast<const float4 *>(&kb[e][64 + c4]);
+        const float vv[8] = {va.x, va.y, va.z, va.w, vc.x, vc.y, vc.z, vc.w};
+        const float kk[8] = {ka.x, ka.y, ka.z, ka.w, kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(vv[i], kk[j], acc[i][j]);
+        lin += tid < HD ? kb[e][tid] : vb[e][tid - HD];
+      }
+    }
+    __syncthreads();
+  }
+
+  // partial (or, with one split, the moment sums themselves)
+  const int64_t mu = blockIdx.y;
+  const bool direct = b.fold_splits == 1;
+  float *S = direct ? a.mom_S + mu * HD * HD
+                    : b.fpart + (int64_t(blockIdx.y) * b.fold_splits + blockIdx.x) * PART_STRIDE;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = i < 4 ? r4 + i : 64 + r4 + (i - 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float4 *p = reinterpret_cast<float4 *>(S + row * HD + (h ? 64 + c4 : c4));
+      float4 x = make_float4(acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]);
+      if (direct) {
+        const float4 o = *p;
+        x.x += o.x;
+        x.y += o.y;
+        x.z += o.z;
+        x.w += o.w;
+      }
+      *p = x;
+    }
+  }
+  if (direct) {
+    if (tid < HD) a.mom_sk[mu * HD + tid] += lin;
+    else a.mom_sv[mu * HD + tid - HD] += lin;
+    if (tid == 0) a.mom_n[mu] += k;
+  } else {
+    S[HD * HD + tid] = lin;   // s_k then s_v
+  }
+}
+
+// Sum of a unit's fold partials in split order, added to its moment sums.
+__global__ __launch_bounds__(WG) void k_bulk_fold_reduce(const StepArgs a, const BulkArgs b) {
+  const int tid = threadIdx.x;
+  const int scope = blockIdx.x / a.units;
+  const BulkScope &st = b.st[scope];
+  if (st.k <= 1) return;
+  const int64_t mu = blockIdx.x;
+  const float *P = b.fpart + mu * b.fold_splits * PART_STRIDE;
+  constexpr int N4 = PART_STRIDE / 4;
+  const int per = (N4 + gridDim.y - 1) / gridDim.y;
+  const int q0 = blockIdx.y * per, q1 = min(N4, q0 + per);
+  for (int q = q0 + tid; q < q1; q += WG) {
+    float4 s = reinterpret_cast<const float4 *>(P)[q];
+    for (int f = 1; f < b.fold_splits; ++f) {
+      const float4 x = reinterpret_cast<const float4 *>(P + int64_t(f) * PART_STRIDE)[q];
+      s.x += x.x;
+      s.y += x.y;
+      s.z += x.z;
+      s.w += x.w;
+    }
+    float4 *dst = q < HD * HD / 4 ? reinterpret_cast<float4 *>(a.mom_S + mu * HD * HD) + q
+                  : q < HD * HD / 4 + HD / 4
+                      ? reinterpret_cast<float4 *>(a.mom_sk + mu * HD) + (q - HD * HD / 4)
+                      : reinterpret_cast<float4 *>(a.mom_sv + mu * HD) + (q - HD * HD / 4 - HD / 4);
+    float4 o = *dst;
+    o.x += s.x;
+    o.y += s.y;
+    o.z += s.z;
+    o.w += s.w;
+    *dst = o;
+  }
+  if (blockIdx.y == 0 && tid == 0) a.mom_n[mu] += st.k;
+}
+
+// ------------------------------------------------------------ hole-filling moves
+__global__ __launch_bounds__(WG) void k_bulk_move(const StepArgs a, const BulkArgs b, const int row_bytes) {
+  const int scope = blockIdx.y, tid = threadIdx.x;
+  const BulkScope &st = b.st[scope];
+  if (st.k <= 1) return;
+  const int np = st.n_pairs;
+  const int64_t sc = int64_t(scope) * a.capacity;
+  const int cpr = row_bytes / 16;
+  const int64_t items = int64_t(np) * a.units * 2 * cpr;
+  for (int64_t idx = int64_t(blockIdx.x) * WG + tid; idx < items; idx += int64_t(gridDim.x) * WG) {
+    const int c = int(idx % cpr);
+    int64_t rest = idx / cpr;
+    const int kv = int(rest & 1);
+    rest >>= 1;
+    const int u = int(rest % a.units);
+    const int j = int(rest / a.units);
+    const int src = a.list2[sc + j], dst = a.list[sc + j];
+    char *base = (kv ? a.v : a.k) + (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride) * row_bytes;
+    st16(base + int64_t(dst) * row_bytes + 16 * c, ld16(base + int64_t(src) * row_bytes + 16 * c));
+  }
+  for (int j = blockIdx.x * WG + tid; j < np; j += gridDim.x * WG) {
+    const int src = a.list2[sc + j], dst = a.list[sc + j];
+    if (a.votes) a.votes[sc + dst] = a.votes[sc + src];
+    a.pos[sc + dst] = a.pos[sc + src];
+    a.m[sc + dst] = a.m[sc + src];
+  }
+  if (blockIdx.x == 0 && tid == 0) a.len[scope] = st.L - st.k;
+}
+
+}  // namespace
+
+hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st) {
+  const dim3 chunks(b.n_chunks, a.n_scopes);
+  for (int shift = 56; shift >= 0; shift -= 8)
+    hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, a, b, shift);
+  hipLaunchKernelGGL(k_bulk_flags, chunks, dim3(WG), 0, st, a, b);
+  hipLaunchKernelGGL(k_bulk_lists, chunks, dim3(WG), 0, st, a, b);
+  if (a.mom_S) {
+    const dim3 fg(b.fold_splits, a.n_scopes * a.units);
+    if (dtype == 0) hipLaunchKernelGGL(k_bulk_fold<bf16_t>, fg, dim3(WG), 0, st, a, b);
+    else hipLaunchKernelGGL(k_bulk_fold<float>, fg, dim3(WG), 0, st, a, b);
+    if (b.fold_splits > 1)
+      hipLaunchKernelGGL(k_bulk_fold_reduce, dim3(a.n_scopes * a.units, 4), dim3(WG), 0, st, a, b);
+  }
+  const int row_bytes = HD * (dtype == 0 ? 2 : 4);
+  hipLaunchKernelGGL(k_bulk_move, dim3(b.move_blocks, a.n_scopes), dim3(WG), 0, st, a, b, row_bytes);
+  return hipGetLastError();
+}
+
+size_t bulk_part_floats() { return size_t(PART_STRIDE); }
+
+}  // namespace kvc

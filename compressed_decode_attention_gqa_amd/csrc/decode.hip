@@ -245,6 +245,7 @@ __global__ __launch_bounds__(WG) void k_decode(const StepArgs a) {
     if (tid == 0) {
       a.status[0] = -4;
       a.counters[scope] = 0;
+      if (a.bulk) a.bulk[scope].k = 0;
     }
     return;
   }

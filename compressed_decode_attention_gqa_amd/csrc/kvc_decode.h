@@ -6,6 +6,28 @@
 
 namespace kvc {
 
+// Per-scope state of a device-wide eviction of k > 1 entries (the bulk path:
+// radix select, evicted and mover lists, split fold and row moves run as
+// separate grid-wide kernels after the attention kernel).
+struct BulkScope {
+  uint64_t prefix, mask;   // cut: a slot is evicted iff (key & mask) <= prefix once done
+  int32_t krem;            // rank of the k-th smallest key inside the current bin
+  int32_t done;            // the cut is final
+  int32_t L, k;            // live length before eviction, evicted count (k <= 1: not bulk)
+  int32_t arrived;         // workgroups of the current histogram pass that finished
+  int32_t n_pairs;         // hole-filling moves
+  uint32_t hist[256];
+};
+
+struct BulkArgs {
+  BulkScope *st;           // [n_scopes]
+  int32_t *cnt;            // [n_scopes][n_chunks][2]: evicted slots, movers (survivors >= L - k)
+  float *fpart;            // [n_scopes * units][fold_splits][HD*HD + 2*HD] fold partials (fold_splits > 1)
+  int32_t n_chunks, chunk; // slot chunks of the histogram, flag and list kernels
+  int32_t fold_splits;     // workgroups folding one unit's evicted rows
+  int32_t move_blocks;     // workgroups moving one scope's rows
+};
+
 struct StepArgs {
   // cache (scope of `units` units; attention covers units [attn_unit0, attn_unit0 + attn_units))
   char *k, *v;
@@ -37,6 +59,7 @@ struct StepArgs {
   int32_t *list, *list2;
   int32_t n_splits, nsub_cap;
   int32_t lds_len;   // per-scope kernel: live tokens its LDS holds (at most budget + 1)
+  BulkScope *bulk;   // non-null: scopes evicting k > 1 stop after the utility update
 };
 
 int decode_chunk_tokens(int dtype);
@@ -45,5 +68,9 @@ hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st);
 hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st);
 // LDS (static + dynamic) of the per-scope kernel for lds_len live tokens
 size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes);
+// Device-wide select -> flags -> lists -> fold -> moves for the scopes the
+// attention kernel handed over (BulkScope::k > 1).
+hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st);
+size_t bulk_part_floats();   // floats of one fold partial
 
 }  // namespace kvc

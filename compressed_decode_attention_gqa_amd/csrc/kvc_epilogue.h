@@ -141,6 +141,25 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
   __threadfence_block();
   __syncthreads();
 
+  if (a.bulk) {   // k > 1: the device-wide kernels launched after this one take over
+    BulkScope &b = a.bulk[scope];
+    if (k > 1) {
+      b.hist[tid] = 0u;
+      if (tid == 0) {
+        b.prefix = 0;
+        b.mask = 0;
+        b.krem = k;
+        b.done = 0;
+        b.L = L;
+        b.k = k;
+        b.arrived = 0;
+        b.n_pairs = 0;
+      }
+      return;
+    }
+    if (tid == 0) b.k = 0;
+  }
+
   if (!step) {
     if (tid == 0) a.len[scope] = L;
     return;
