@@ -284,6 +284,179 @@ __global__ __launch_bounds__(WG) void k_bulk_fold(const StepArgs a, const BulkAr
   }
 }
 
+// bf16 caches: the same fold on MFMA. S = V_E^T K_E is a d x k x d contraction
+// over the evicted rows, so each stage of 32 rows is one 16x16x32 bf16 MFMA
+// reduction step; the operands are the cache's own bf16 values, their products
+// are exact in fp32 and the accumulation is fp32, as on the VALU. Wave w owns
+// the 64 x 64 quadrant (rows 64*(w/2).., columns 64*(w%2)..) as 4 x 4 tiles.
+// Rows are staged row-major in LDS with a 264-byte stride, so the eight
+// 2-byte reads that build a fragment (rows 8g..8g+7 of one column for the four
+// lane groups g) fall on distinct banks. s_v and s_k come from two more MFMAs
+// per tile row / column with a fragment of ones (waves of the first quadrant
+// column and row).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int MF_ROWS = 32;   // evicted rows per stage: the MFMA reduction depth
+constexpr int MF_RS = 132;    // LDS row stride, bf16 elements
+constexpr int MF_WIN = 1024;  // evicted-list entries staged in LDS per window
+
+struct MfmaFoldLds {
+  uint16_t kr[2][MF_ROWS][MF_RS];
+  uint16_t vr[2][MF_ROWS][MF_RS];
+  int32_t slots[MF_WIN];
+};
+
+// Stage rows e0.. of the window: chunk q = tid + 256 h is row q / 16, 16-byte chunk q % 16.
+// Rows past ne load row e0 again (every load unconditional, so the loads of the
+// next stage stay in flight) and are zeroed when staged.
+__device__ __forceinline__ void mf_load(u32x4 (&rk)[2], u32x4 (&rv)[2], const char *Kb, const char *Vb,
+                                        const int32_t *slots, int e0, int ne) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = threadIdx.x + WG * h, e = q >> 4, c = q & 15;
+    const int64_t off = int64_t(slots[e0 + (e < ne ? e : 0)]) * (HD * 2) + 16 * c;
+    rk[h] = ld16(Kb + off);
+    rv[h] = ld16(Vb + off);
+  }
+}
+
+__device__ __forceinline__ void mf_stage(const u32x4 (&rk)[2], const u32x4 (&rv)[2], int ne,
+                                         uint16_t (*kr)[MF_RS], uint16_t (*vr)[MF_RS]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = threadIdx.x + WG * h, e = q >> 4, c = q & 15;
+    const u32x4 zk = e < ne ? rk[h] : u32x4(0u), zv = e < ne ? rv[h] : u32x4(0u);
+    uint2 *pk = reinterpret_cast<uint2 *>(&kr[e][8 * c]);
+    uint2 *pv = reinterpret_cast<uint2 *>(&vr[e][8 * c]);
+    pk[0] = make_uint2(zk.x, zk.y);
+    pk[1] = make_uint2(zk.z, zk.w);
+    pv[0] = make_uint2(zv.x, zv.y);
+    pv[1] = make_uint2(zv.z, zv.w);
+  }
+}
+
+// Fragment of column `col` over rows 8g..8g+7 of a staged matrix.
+__device__ __forceinline__ bf16x8 mf_frag(const uint16_t (*m)[MF_RS], int g, int col) {
+  u16x8 x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = m[8 * g + e][col];
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+__global__ __launch_bounds__(WG) void k_bulk_fold_mfma(const StepArgs a, const BulkArgs b) {
+  __shared__ MfmaFoldLds sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.y / a.units, u = blockIdx.y - scope * a.units;
+  const BulkScope &st = b.st[scope];
+  if (st.k <= 1) return;
+  const int k = st.k;
+  const int per = (k + b.fold_splits - 1) / b.fold_splits;
+  const int j0 = min(k, int(blockIdx.x) * per), j1 = min(k, j0 + per);
+  const int64_t sc = int64_t(scope) * a.capacity;
+  const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride;
+  const char *Kb = a.k + row0 * (HD * 2);
+  const char *Vb = a.v + row0 * (HD * 2);
+  const int iq = wave >> 1, jq = wave & 1;
+  const int g = lane >> 4, l16 = lane & 15;
+
+  f32x4 acc[4][4], accv[4], acck[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    accv[i] = f32x4(0.f);
+    acck[i] = f32x4(0.f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4(0.f);
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u16x8(uint16_t(0x3f80)));
+
+  for (int w0 = j0; w0 < j1; w0 += MF_WIN) {
+    const int nw = min(MF_WIN, j1 - w0);
+    for (int e = tid; e < nw; e += WG) sh.slots[e] = a.list[sc + w0 + e];
+    __syncthreads();
+    const int nst = (nw + MF_ROWS - 1) / MF_ROWS;
+    // two stages of loads in flight: stage s is staged from register set s & 1,
+    // which then takes the loads of stage s + 2
+    u32x4 rk[2][2], rv[2][2];
+    // (loads past the last stage repeat it, so every step issues the same loads and
+    // the waits stay exact: stage s waits only for its own set)
+    auto load_stage = [&](int s, u32x4 (&qk)[2], u32x4 (&qv)[2]) {
+      s = min(s, nst - 1);
+      mf_load(qk, qv, Kb, Vb, sh.slots, s * MF_ROWS, min(MF_ROWS, nw - s * MF_ROWS));
+    };
+    load_stage(0, rk[0], rv[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(1, rk[1], rv[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    auto step = [&](const int s, u32x4 (&qk)[2], u32x4 (&qv)[2]) {
+      const int buf = s & 1;
+      mf_stage(qk, qv, min(MF_ROWS, nw - s * MF_ROWS), sh.kr[buf], sh.vr[buf]);
+      __syncthreads();
+      load_stage(s + 2, qk, qv);
+      __builtin_amdgcn_sched_barrier(0);   // keep the next loads ahead of this stage's MFMAs
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[t] = mf_frag(sh.vr[buf], g, 64 * iq + 16 * t + l16);
+        bf[t] = mf_frag(sh.kr[buf], g, 64 * jq + 16 * t + l16);
+      }
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj)
+          acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bf[tj], acc[ti][tj], 0, 0, 0);
+      // (every wave forms both sums, branch-free; only one quadrant row / column stores them)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        accv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t], ones, accv[t], 0, 0, 0);
+        acck[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bf[t], acck[t], 0, 0, 0);
+      }
+    };
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {   // straight-line body: the same loads pending on every trip
+      step(s, rk[0], rv[0]);
+      step(s + 1, rk[1], rv[1]);
+    }
+    if (s < nst) step(s, rk[0], rv[0]);
+    __syncthreads();
+  }
+
+  // D layout of a 16x16 tile: lane l holds rows 4(l/16)..+3, column l%16
+  const int64_t mu = blockIdx.y;
+  const bool direct = b.fold_splits == 1;
+  float *P = direct ? nullptr : b.fpart + (int64_t(blockIdx.y) * b.fold_splits + blockIdx.x) * PART_STRIDE;
+  float *S = direct ? a.mom_S + mu * HD * HD : P;
+  float *skd = direct ? a.mom_sk + mu * HD : P + HD * HD;
+  float *svd = direct ? a.mom_sv + mu * HD : P + HD * HD + HD;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float *p = S + (64 * iq + 16 * ti + 4 * g + r) * HD + 64 * jq + 16 * tj + l16;
+        *p = direct ? *p + acc[ti][tj][r] : acc[ti][tj][r];
+      }
+  if (jq == 0 && l16 == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float *p = svd + 64 * iq + 16 * t + 4 * g + r;
+        *p = direct ? *p + accv[t][r] : accv[t][r];
+      }
+  }
+  if (iq == 0 && g == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float *p = skd + 64 * jq + 16 * t + l16;
+      *p = direct ? *p + acck[t][0] : acck[t][0];
+    }
+  }
+  if (direct && tid == 0) a.mom_n[mu] += k;
+}
+
 // Sum of a unit's fold partials in split order, added to its moment sums.
 __global__ __launch_bounds__(WG) void k_bulk_fold_reduce(const StepArgs a, const BulkArgs b) {
   const int tid = threadIdx.x;
@@ -357,7 +530,7 @@ hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStrea
   hipLaunchKernelGGL(k_bulk_lists, chunks, dim3(WG), 0, st, a, b);
   if (a.mom_S) {
     const dim3 fg(b.fold_splits, a.n_scopes * a.units);
-    if (dtype == 0) hipLaunchKernelGGL(k_bulk_fold<bf16_t>, fg, dim3(WG), 0, st, a, b);
+    if (dtype == 0) hipLaunchKernelGGL(k_bulk_fold_mfma, fg, dim3(WG), 0, st, a, b);
     else hipLaunchKernelGGL(k_bulk_fold<float>, fg, dim3(WG), 0, st, a, b);
     if (b.fold_splits > 1)
       hipLaunchKernelGGL(k_bulk_fold_reduce, dim3(a.n_scopes * a.units, 4), dim3(WG), 0, st, a, b);

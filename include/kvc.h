@@ -186,8 +186,8 @@ int32_t kvc_moment_correct(const kvc_moments *mom, int32_t n_units, const void *
 int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merge *merge,
                     void *ws, size_t ws_bytes, void *stream);
 
-/* kvc_decode_step -- the whole decode step in one launch per call, in the
- * order append -> attend -> score -> utility -> select -> fold -> compact
+/* kvc_decode_step -- the whole decode step, in the order
+ * append -> attend -> score -> utility -> select -> fold -> compact
  * (MomentKV Algorithm 1; KeepKV decode steps 6a-6f; InertiaKV §3.1), with the
  * semantics of kvc_decode_attn_score, kvc_ema_update, kvc_select_evict,
  * kvc_moment_update and kvc_compact applied in turn. refresh = 0 skips the
@@ -204,7 +204,15 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
  * every unit of the scope. This is how one slot set shared by all layers of a
  * sequence is driven layer by layer (InertiaKV §3.1: the utility is updated
  * after every compressed layer); a call whose scope is already within budget
- * only attends, scores and updates the utility. */
+ * only attends, scores and updates the utility.
+ *
+ * Launches. max_len <= budget + 1 (at most one eviction per scope, the steady
+ * state) runs the whole step in one launch. A larger max_len (e.g. the first
+ * step after prefill, which compresses to the budget) adds a fixed sequence
+ * of device-wide kernels for the scopes that evict more than one entry:
+ * radix select, flags, lists, moment fold and row moves; scopes that evict
+ * at most one entry finish inside the first launch and the later kernels
+ * skip them. */
 int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,
                         const void *q, int32_t G, float scale, int32_t rule, float alpha,
                         int32_t budget, int32_t refresh, float *out, float *lse, float *s,
