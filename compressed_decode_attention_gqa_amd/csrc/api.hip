@@ -231,7 +231,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
       b.chunk = d.bulk_chunk;
       b.fold_splits = d.fold_splits;
       b.move_blocks = d.move_blocks;
-      if (kvc::launch_bulk(a, b, c->dtype, hs) != hipSuccess) return KVC_ERR_DEVICE;
+      if (kvc::launch_bulk(a, b, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
     }
   }
   if (a.mode == 2) {

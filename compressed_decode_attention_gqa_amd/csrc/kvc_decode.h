@@ -68,9 +68,9 @@ hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st);
 hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st);
 // LDS (static + dynamic) of the per-scope kernel for lds_len live tokens
 size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes);
-// Device-wide select -> flags -> lists -> fold -> moves for the scopes the
-// attention kernel handed over (BulkScope::k > 1).
-hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st);
+// Device-wide score -> select -> flags -> lists -> fold -> moves for the scopes
+// the attention kernel handed over (BulkScope::k > 1).
+hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, int G, hipStream_t st);
 size_t bulk_part_floats();   // floats of one fold partial
 
 }  // namespace kvc

@@ -82,9 +82,25 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
   }
   __syncthreads();
 
-  // (3) score s(i), utility m(i) and, for a single eviction, the argmin key.
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
+  if (a.bulk && k > 1) {   // the grid-wide kernels launched after this one take over from (3)
+    BulkScope &b = a.bulk[scope];
+    b.hist[tid] = 0u;
+    if (tid == 0) {
+      b.prefix = 0;
+      b.mask = 0;
+      b.krem = k;
+      b.done = 0;
+      b.L = L;
+      b.k = k;
+      b.arrived = 0;
+      b.n_pairs = 0;
+    }
+    return;
+  }
+
+  // (3) score s(i), utility m(i) and, for a single eviction, the argmin key.
   const double inv_heads = 1.0 / double(Ua * G);
   const double alpha = double(a.alpha);
   uint64_t best = ~0ull;
@@ -141,24 +157,7 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
   __threadfence_block();
   __syncthreads();
 
-  if (a.bulk) {   // k > 1: the device-wide kernels launched after this one take over
-    BulkScope &b = a.bulk[scope];
-    if (k > 1) {
-      b.hist[tid] = 0u;
-      if (tid == 0) {
-        b.prefix = 0;
-        b.mask = 0;
-        b.krem = k;
-        b.done = 0;
-        b.L = L;
-        b.k = k;
-        b.arrived = 0;
-        b.n_pairs = 0;
-      }
-      return;
-    }
-    if (tid == 0) b.k = 0;
-  }
+  if (a.bulk && tid == 0) a.bulk[scope].k = 0;   // finished here: the bulk kernels skip this scope
 
   if (!step) {
     if (tid == 0) a.len[scope] = L;
