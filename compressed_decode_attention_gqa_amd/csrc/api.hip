@@ -14,7 +14,9 @@
 namespace {
 
 constexpr int kHD = 128;
-constexpr int kTargetWorkgroups = 2048;   // split-K workgroups per launch to aim for
+constexpr int kTargetWorkgroups = 2048;   // workgroups per launch to aim for (merge, bulk chunks)
+constexpr int kSplitWorkgroups = 1024;    // split-K attention workgroups (512 threads) per launch
+constexpr int kMinSubChunksPerSplit = 16;
 constexpr int kMergeSplitsMax = 64;
 // One workgroup per scope (no split-K) once there are this many single-unit
 // scopes to spread over the 256 CUs, each scope's live length is bounded so
@@ -58,9 +60,13 @@ struct DecodeLayout {
   size_t merge_counters, merge_cos, merge_slot, bulk_state, bulk_cnt, fpart, total;
 };
 
+// Split-K workgroups per attention unit: about kSplitWorkgroups in the launch,
+// each streaming at least kMinSubChunksPerSplit sub-chunks (two per wave at
+// the deepest prefetch) so its loads stay in flight.
 int split_count(int attn_units_total, int nsub) {
-  const int want = std::max(1, ceil_div(kTargetWorkgroups, attn_units_total));
-  return std::max(1, std::min(nsub, want));
+  const int want = std::max(1, ceil_div(kSplitWorkgroups, attn_units_total));
+  const int most = std::max(1, nsub / kMinSubChunksPerSplit);
+  return std::max(1, std::min(want, most));
 }
 
 DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {

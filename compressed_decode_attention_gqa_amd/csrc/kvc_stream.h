@@ -1,0 +1,67 @@
+// Streaming geometry and sub-chunk loads shared by the decode kernels that
+// stream K/V rows with 16-byte lanes (the per-scope and the split kernel).
+#pragma once
+
+#include "kvc_device.h"
+
+namespace kvc {
+
+// Eight waves (two per SIMD, at most 256 registers each) up to four heads per
+// group; eight heads need more query and accumulator registers than that and
+// run four waves with deeper prefetch.
+template <typename T, int G = 1>
+struct UnitGeometry {
+  static constexpr int EPV = ElemTraits<T>::EPV;
+  static constexpr int LPT = HD / EPV;     // lanes per token row
+  static constexpr int TPI = 64 / LPT;     // tokens per wave iteration
+  static constexpr int UNR = 4;            // iterations per sub-chunk
+  static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
+  static constexpr int NW = G >= 8 ? 4 : 8;   // waves
+  static constexpr int PF = 16 / NW;       // sub-chunks of loads in flight per wave
+  // (Waves 0-3 finish streaming well before waves 4-7: a SIMD's issue
+  // arbiter favours the older of its two waves. Giving them a larger share
+  // of sub-chunks moves the imbalance without shortening the makespan.)
+  static constexpr int NT = 64 * NW;       // threads
+  static constexpr int RB = HD * int(sizeof(T));
+  static constexpr int NS4 = HD * HD / 4 / NT;   // float4 of the moment matrix per thread
+};
+
+// Loads of one sub-chunk: K and V rows, and (MROW) the per-token utility and
+// (VOTES) the vote.
+template <typename T, bool VOTES, bool MROW = true>
+struct UnitStream {
+  using Geo = UnitGeometry<T, 1>;
+  static constexpr int UNR = Geo::UNR, TPI = Geo::TPI, CHW = Geo::CHW, RB = Geo::RB;
+  const char *Kb, *Vb, *Kn, *Vn;
+  const float *mrow;        // utilities of the scope (MROW)
+  const int32_t *vrow;
+  int L, Lold, append, lane, cb, tg;
+
+  __device__ __forceinline__ void issue(u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], float &mv, int &vv, int c) const {
+    if ((c + 1) * CHW <= Lold) {
+      // every token of the sub-chunk is an old, live entry: uniform base + lane offset
+      const char *kb = Kb + int64_t(c) * CHW * RB + 16 * lane;
+      const char *vb = Vb + int64_t(c) * CHW * RB + 16 * lane;
+#pragma unroll
+      for (int it = 0; it < UNR; ++it) {
+        kr[it] = ld16(kb + it * TPI * RB);
+        vr[it] = ld16(vb + it * TPI * RB);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < UNR; ++it) {
+        const int tok = min(c * CHW + it * TPI + tg, L - 1);
+        const bool isnew = append && tok == L - 1;
+        const char *ks = isnew ? Kn : Kb + int64_t(tok) * RB;
+        const char *vs = isnew ? Vn : Vb + int64_t(tok) * RB;
+        kr[it] = ld16(ks + 16 * cb);
+        vr[it] = ld16(vs + 16 * cb);
+      }
+    }
+    const int t1 = min(c * CHW + (lane % CHW), max(Lold - 1, 0));
+    mv = MROW ? mrow[t1] : 0.f;
+    if (VOTES) vv = vrow[t1];
+  }
+};
+
+}  // namespace kvc
