@@ -61,6 +61,32 @@ def test_attn_score_matches_oracle(dtype, G, L, votes, layers):
             assert post["votes"][sc, L] == 1
 
 
+@pytest.mark.parametrize("layers", [1, 46])
+def test_attn_score_without_utilities(layers):
+    """Attention only, no appended row and no utility array (m = NULL): the per-head kernel
+    (46 layers x 3 heads = 138 scopes) and the split kernel read no utilities."""
+    _say("attn_score without m", layers)
+    L = 400
+    wl = C2.scaled(context=L, budget=L, n_kv=3, n_layers=layers, key_scales=True, prior_votes=False)
+    run = DeviceRun(wl, capacity=L + 3)
+    pre = run.snapshot(list(range(wl.n_scopes)))
+    run.cache.m = None
+    q, _, _ = run.inputs(1)
+    kvc.kvc_decode_attn_score(run.cache, None, None, 0, q, wl.G, run.scale, run.out, run.lse, run.s, L,
+                              run.ws)
+    torch.cuda.synchronize()
+    out, lse, s = bits(run.out), bits(run.lse), bits(run.s)
+    for sc in range(0, wl.n_scopes, 7):
+        st = oracle_state(pre, sc, "bf16")
+        _, a, o, l = oracle.attend_unit(oracle.to_f64(bits(q)[sc, 0], "bf16"), st.K[0], st.V[0], st.votes,
+                                        run.scale)
+        assert np.abs(out[sc, 0] - o).max() <= 2e-3
+        assert np.abs(lse[sc, 0] - l).max() <= 2e-3
+        s_ref = oracle.scope_score([a])
+        assert np.all(np.abs(s[sc, :L] - s_ref) <= 1e-5 * s_ref + 1e-12)
+    assert np.all(run.cache.length.cpu().numpy() == L)
+
+
 def test_decode_step_c1_lockstep():
     """Single fp32 head, 4096 tokens to a 128 budget, 64 steps, every step checked."""
     run = DeviceRun(C1)
