@@ -56,8 +56,8 @@ bool valid_G(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 struct DecodeLayout {
   int n_splits, nsub_cap, merge_splits;
   int bulk_chunks, bulk_chunk, fold_splits, move_blocks;
-  size_t status, counters, partM, partZ, partO, fac, subM, ews, flags, list, list2;
-  size_t merge_counters, merge_cos, merge_slot, bulk_state, bulk_cnt, fpart, total;
+  size_t status, partM, partZ, partO, fac, subM, ews, flags, list, list2;
+  size_t merge_cos, merge_slot, bulk_state, bulk_cnt, bulk_hist, fpart, total;
 };
 
 // Split-K workgroups per attention unit: about kSplitWorkgroups in the launch,
@@ -86,8 +86,6 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   const int64_t cap = c->capacity;
   size_t o = 0;
   d.status = o;   o = align_up(o + 256);
-  d.counters = o; o = align_up(o + size_t(c->n_scopes) * 4);
-  d.merge_counters = o; o = align_up(o + size_t(c->n_scopes) * 4);
   d.partM = o;    o = align_up(o + size_t(nu) * d.n_splits * G * 8);
   d.partZ = o;    o = align_up(o + size_t(nu) * d.n_splits * G * 8);
   d.partO = o;    o = align_up(o + size_t(nu) * d.n_splits * G * kHD * 4);
@@ -101,6 +99,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.merge_slot = o; o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 4);
   d.bulk_state = o; o = align_up(o + size_t(c->n_scopes) * sizeof(kvc::BulkScope));
   d.bulk_cnt = o;   o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 8);
+  d.bulk_hist = o;  o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 256 * 4);
   d.fpart = o;
   if (d.fold_splits > 1) o = align_up(o + size_t(units_total) * d.fold_splits * kvc::bulk_part_floats() * 4);
   d.total = o;
@@ -198,7 +197,6 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   }
   a.evict_out = evict_out;
   a.status = at<int32_t>(ws, d.status);
-  a.counters = at<int32_t>(ws, d.counters);
   a.partM = at<double>(ws, d.partM);
   a.partZ = at<double>(ws, d.partZ);
   a.partO = at<float>(ws, d.partO);
@@ -232,6 +230,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
       kvc::BulkArgs b{};
       b.st = a.bulk;
       b.cnt = at<int32_t>(ws, d.bulk_cnt);
+      b.hpart = at<uint32_t>(ws, d.bulk_hist);
       b.fpart = at<float>(ws, d.fpart);
       b.n_chunks = d.bulk_chunks;
       b.chunk = d.bulk_chunk;
@@ -247,7 +246,6 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
     mg.scale = double(merge->scale);
     mg.eps = merge->eps;
     mg.n_splits = d.merge_splits;
-    mg.counters = at<int32_t>(ws, d.merge_counters);
     mg.part_cos = at<double>(ws, d.merge_cos);
     mg.part_slot = at<int32_t>(ws, d.merge_slot);
     if (kvc::launch_merge(cache_args(c), a.flags, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;
@@ -258,14 +256,13 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
 // ------------------------------------------------------------ compact workspace
 struct CompactLayout {
   int merge_splits;
-  size_t holes, counters, cos, slot, total;
+  size_t holes, cos, slot, total;
 };
 
 CompactLayout compact_layout(const kvc_cache *c) {
   CompactLayout l{};
   l.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
   size_t o = 0;
-  l.counters = o; o = align_up(o + size_t(c->n_scopes) * 4);
   l.holes = o;    o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
   l.cos = o;      o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 8);
   l.slot = o;     o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 4);
@@ -405,7 +402,6 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
     mg.scale = double(merge->scale);
     mg.eps = merge->eps;
     mg.n_splits = l.merge_splits;
-    mg.counters = at<int32_t>(ws, l.counters);
     mg.part_cos = at<double>(ws, l.cos);
     mg.part_slot = at<int32_t>(ws, l.slot);
     if (kvc::launch_merge(cache_args(cache), evict, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;

@@ -5,10 +5,11 @@
 // the step over the whole grid instead of one workgroup per scope:
 //
 //   score      per-token score, utility update, appended row
-//   hist x 8   radix select of the k lowest (utility, position) keys: per pass
-//              a per-scope 256-bin histogram of the keys under the current
-//              prefix; the last workgroup of the scope to finish picks the digit
-//              (InertiaKV §3.1: lowest utility first, ties to the lower position)
+//   hist, pick x 8   radix select of the k lowest (utility, position) keys:
+//              per pass a 256-bin histogram of each chunk's keys under the
+//              current prefix, then one workgroup per scope sums the chunks and
+//              picks the digit (InertiaKV §3.1: lowest utility first, ties to
+//              the lower position)
 //   flags      evicted flags and per-chunk counts of evicted slots and movers
 //   lists      evicted slots ascending; survivors at or above L - k ascending
 //   fold       MomentKV §4.1 / Appendix A.1 moment sums of the evicted rows,
@@ -88,16 +89,16 @@ __global__ __launch_bounds__(WG) void k_bulk_score(const StepArgs a, const BulkA
 }
 
 // ------------------------------------------------------------ radix select pass
+// Each workgroup histograms the digit at `shift` of the keys of its chunk that
+// match the current prefix and stores the 256 counts (plain stores: no
+// device-scope atomics or fences); the pick kernel sums the chunks' counts.
 __global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkArgs b, const int shift) {
   __shared__ uint32_t hist[256];
-  __shared__ int red[8];
-  __shared__ int s_last;
   const int scope = blockIdx.y, tid = threadIdx.x;
-  BulkScope &st = b.st[scope];
+  const BulkScope &st = b.st[scope];
   if (st.k <= 1 || st.done) return;     // the same for every workgroup of the scope
   const int L = st.L;
   const uint64_t prefix = st.prefix, mask = st.mask;
-  const int krem = st.krem;
   hist[tid] = 0u;
   __syncthreads();
   const int64_t sc = int64_t(scope) * a.capacity;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkAr
     // one atomic each, then the remaining lanes add one by one.
     uint64_t rem = __ballot(hit);
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int q = 0; q < 2; ++q) {
       if (!rem) break;
       const int first = __builtin_ctzll(rem);
       const uint32_t b0 = __shfl(bin, first);
@@ -128,16 +129,20 @@ __global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkAr
     if ((rem >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
   }
   __syncthreads();
-  const uint32_t c = hist[tid];
-  if (c) atomicAdd(&st.hist[tid], c);
-  release_device();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&st.arrived, 1) == int(gridDim.x) - 1;
-  __syncthreads();
-  if (!s_last) return;
-  acquire_device();
-  // last workgroup of the scope: the bin holding the krem-th key
-  const int cnt = int(__hip_atomic_load(&st.hist[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  b.hpart[(int64_t(scope) * b.n_chunks + blockIdx.x) * 256 + tid] = hist[tid];
+}
+
+// One workgroup per scope: the bin holding the krem-th key under the prefix.
+__global__ __launch_bounds__(WG) void k_bulk_pick(const BulkArgs b, const int shift) {
+  __shared__ int red[8];
+  const int scope = blockIdx.x, tid = threadIdx.x;
+  BulkScope &st = b.st[scope];
+  if (st.k <= 1 || st.done) return;
+  const uint64_t prefix = st.prefix, mask = st.mask;
+  const int krem = st.krem;
+  const uint32_t *h = b.hpart + int64_t(scope) * b.n_chunks * 256;
+  int cnt = 0;
+  for (int c = 0; c < b.n_chunks; ++c) cnt += int(h[c * 256 + tid]);
   int tot;
   const int excl = wg_exclusive_scan(cnt, red, &tot);
   if (excl < krem && krem <= excl + cnt) {
@@ -146,8 +151,6 @@ __global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkAr
     st.krem = krem - excl;
     if (cnt == krem - excl || shift == 0) st.done = 1;
   }
-  st.hist[tid] = 0u;
-  if (tid == 0) st.arrived = 0;
 }
 
 // ------------------------------------------------------------ flags and chunk counts
@@ -609,8 +612,10 @@ hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, int G, h
     case 8: hipLaunchKernelGGL(k_bulk_score<8>, chunks, dim3(WG), 0, st, a, b, CH, row_bytes); break;
     default: return hipErrorInvalidValue;
   }
-  for (int shift = 56; shift >= 0; shift -= 8)
+  for (int shift = 56; shift >= 0; shift -= 8) {
     hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, a, b, shift);
+    hipLaunchKernelGGL(k_bulk_pick, dim3(a.n_scopes), dim3(WG), 0, st, b, shift);
+  }
   hipLaunchKernelGGL(k_bulk_flags, chunks, dim3(WG), 0, st, a, b);
   hipLaunchKernelGGL(k_bulk_lists, chunks, dim3(WG), 0, st, a, b);
   if (a.mom_S) {

@@ -14,13 +14,13 @@ struct BulkScope {
   int32_t krem;            // rank of the k-th smallest key inside the current bin
   int32_t done;            // the cut is final
   int32_t L, k;            // live length before eviction, evicted count (k <= 1: not bulk)
-  int32_t arrived;         // workgroups of the current histogram pass that finished
   int32_t n_pairs;         // hole-filling moves
-  uint32_t hist[256];
+  int32_t pad;
 };
 
 struct BulkArgs {
   BulkScope *st;           // [n_scopes]
+  uint32_t *hpart;         // [n_scopes][n_chunks][256] radix histogram of each chunk (current pass)
   int32_t *cnt;            // [n_scopes][n_chunks][2]: evicted slots, movers (survivors >= L - k)
   float *fpart;            // [n_scopes * units][fold_splits][HD*HD + 2*HD] fold partials (fold_splits > 1)
   int32_t n_chunks, chunk; // slot chunks of the histogram, flag and list kernels
@@ -50,7 +50,7 @@ struct StepArgs {
   float *mom_sk, *mom_sv, *mom_S;
   uint8_t *evict_out;
   // workspace
-  int32_t *status, *counters;
+  int32_t *status;
   double *partM, *partZ;
   float *partO, *fac;
   double *subM;

@@ -149,10 +149,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// ---------------------------------------------------------------- memory model
-// Release this thread's global writes to every workgroup on the device.
-__device__ __forceinline__ void release_device() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_device() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Workgroup-wide exclusive scan of small non-negative ints; returns this
 // thread's exclusive prefix and writes the total to *total. `red` is LDS of >= 4 ints.

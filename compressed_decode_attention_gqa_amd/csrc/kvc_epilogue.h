@@ -85,16 +85,14 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
   if (a.bulk && k > 1) {   // the grid-wide kernels launched after this one take over from (3)
-    BulkScope &b = a.bulk[scope];
-    b.hist[tid] = 0u;
     if (tid == 0) {
+      BulkScope &b = a.bulk[scope];
       b.prefix = 0;
       b.mask = 0;
       b.krem = k;
       b.done = 0;
       b.L = L;
       b.k = k;
-      b.arrived = 0;
       b.n_pairs = 0;
     }
     return;

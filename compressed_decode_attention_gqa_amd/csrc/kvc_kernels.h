@@ -21,7 +21,6 @@ struct MergeArgs {
   double scale;
   float eps;
   int32_t n_splits;
-  int32_t *counters;
   double *part_cos;
   int32_t *part_slot;
 };

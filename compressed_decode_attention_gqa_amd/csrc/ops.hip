@@ -203,15 +203,14 @@ hipError_t launch_compact(const CacheArgs &c, const uint8_t *evict, int32_t *hol
 // ------------------------------------------------------------ ZIP merge
 // KeepKV eqs. (7)-(12): the single flagged entry e of each scope is merged into
 // its live partner c of largest cos(k_e, k_c) (ties to the lower position),
-// then dropped. Split kernel: partial argmax of the cosine over token ranges;
-// the last workgroup of the scope merges and compacts.
+// then dropped. k_merge_part: each workgroup takes a token range and stores its
+// best (cosine, slot); k_merge_finish: one workgroup per scope picks the
+// partner over the ranges, merges and compacts.
 struct MergeLds {
   double ke[HD];
   double best_cos[4];
   int best_slot[4];
-  int red[8];
   int e;
-  int last;
   double lbar[2];
   double wgt[4];
 };
@@ -220,28 +219,26 @@ __device__ __forceinline__ bool cos_better(double c1, int p1, double c2, int p2)
   return c1 > c2 || (c1 == c2 && p1 < p2);
 }
 
+// The flagged slot of the scope (the largest one if several), or -1.
+__device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &sh_e) {
+  if (threadIdx.x == 0) sh_e = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < L; i += WG)
+    if (flags[i]) atomicMax(&sh_e, i);
+  __syncthreads();
+  return sh_e;
+}
+
 template <typename T>
-__global__ __launch_bounds__(WG) void k_merge(CacheArgs c, const uint8_t *evict, MergeArgs mg) {
+__global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *evict, MergeArgs mg) {
   __shared__ MergeLds sh;
   constexpr int EPV = ElemTraits<T>::EPV, LPT = HD / EPV, TPI = 64 / LPT;
   const int scope = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t so = int64_t(scope) * c.capacity;
   const int L = c.len[scope];
   const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
-  const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
-
-  // the flagged entry (exactly one per scope)
-  if (tid == 0) sh.e = -1;
-  __syncthreads();
-  for (int i = tid; i < L; i += WG)
-    if (evict[so + i]) atomicMax(&sh.e, i);
-  __syncthreads();
-  const int e = sh.e;
-  if (e < 0) {
-    // nothing flagged: still take part in the scope counter
-  } else if (tid < HD) {
-    sh.ke[tid] = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
-  }
+  const int e = merge_flagged(evict + so, L, sh.e);
+  if (e >= 0 && tid < HD) sh.ke[tid] = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
   __syncthreads();
 
   double best = -INFINITY;
@@ -314,20 +311,24 @@ __global__ __launch_bounds__(WG) void k_merge(CacheArgs c, const uint8_t *evict,
     const int64_t pi = int64_t(scope) * gridDim.x + blockIdx.x;
     mg.part_cos[pi] = b;
     mg.part_slot[pi] = s;
-    release_device();
-    const int prev = atomicAdd(mg.counters + scope, 1);
-    sh.last = prev == int(gridDim.x) - 1;
   }
-  __syncthreads();
-  if (!sh.last) return;
-  acquire_device();
-  if (tid == 0) mg.counters[scope] = 0;
+}
+
+template <typename T>
+__global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t *evict, MergeArgs mg) {
+  __shared__ MergeLds sh;
+  const int scope = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t so = int64_t(scope) * c.capacity;
+  const int L = c.len[scope];
+  const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
+  const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
+  const int e = merge_flagged(evict + so, L, sh.e);
   if (e < 0) return;
   if (tid == 0) {
     double b = -INFINITY;
     int s = -1, p = 0x7fffffff;
-    for (int sp = 0; sp < int(gridDim.x); ++sp) {
-      const int64_t pi = int64_t(scope) * gridDim.x + sp;
+    for (int sp = 0; sp < mg.n_splits; ++sp) {
+      const int64_t pi = int64_t(scope) * mg.n_splits + sp;
       const int sw = mg.part_slot[pi];
       if (sw < 0) continue;
       const int pw = c.pos[so + sw];
@@ -398,9 +399,14 @@ __global__ __launch_bounds__(WG) void k_merge(CacheArgs c, const uint8_t *evict,
 }
 
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st) {
-  dim3 grid(mg.n_splits, c.n_scopes);
-  if (c.dtype == 0) hipLaunchKernelGGL(k_merge<bf16_t>, grid, dim3(WG), 0, st, c, evict, mg);
-  else hipLaunchKernelGGL(k_merge<float>, grid, dim3(WG), 0, st, c, evict, mg);
+  const dim3 grid(mg.n_splits, c.n_scopes);
+  if (c.dtype == 0) {
+    hipLaunchKernelGGL(k_merge_part<bf16_t>, grid, dim3(WG), 0, st, c, evict, mg);
+    hipLaunchKernelGGL(k_merge_finish<bf16_t>, dim3(c.n_scopes), dim3(WG), 0, st, c, evict, mg);
+  } else {
+    hipLaunchKernelGGL(k_merge_part<float>, grid, dim3(WG), 0, st, c, evict, mg);
+    hipLaunchKernelGGL(k_merge_finish<float>, dim3(c.n_scopes), dim3(WG), 0, st, c, evict, mg);
+  }
   return hipGetLastError();
 }
 

@@ -186,7 +186,7 @@ def kvc_laprox_workspace_size(n_layers, H, n_kv, N, w, d, D) -> int:
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace (the library keeps its counters at zero between calls)."""
+    """A zero-filled workspace (its first word is the device status word)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 

@@ -254,9 +254,10 @@ int32_t kvc_laprox_score_marked(const void *q_win, const void *k, const void *v,
                                 size_t ws_bytes, void *stream, void *const *events, int32_t n_events);
 
 /* Workspace sizes in bytes. The decode workspace must be zero-filled once
- * before its first use; the library returns its counters to zero after every
- * call, so one workspace can serve any number of calls on one stream
- * (concurrent calls need separate workspaces). */
+ * before its first use (its first word is the device status word, see
+ * kvc_workspace_status); every other byte is written by a call before that
+ * call reads it, so one workspace can serve any number of calls on one
+ * stream (concurrent calls need separate workspaces). */
 size_t kvc_decode_workspace_size(const kvc_cache *cache, int32_t G, int32_t max_len);
 size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity);
 size_t kvc_compact_workspace_size(const kvc_cache *cache);
