@@ -34,7 +34,7 @@ from compressed_decode_attention_gqa_amd import kvc  # noqa: E402
 from compressed_decode_attention_gqa_amd import roofline as rf  # noqa: E402
 
 METRIC = "cached tokens attended+scored+evicted/sec and % peak HBM GB/s at 32K ctx"
-KERNEL_SOURCES = ["decode_unit.hip", "kvc_epilogue.h", "kvc_ops.h", "kvc_device.h", "kvc_decode.h"]
+KERNEL_SOURCES = ["decode_unit.hip", "kvc_stream.h", "kvc_epilogue.h", "kvc_ops.h", "kvc_device.h", "kvc_decode.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2x32_traffic.json")
 
 
@@ -259,6 +259,91 @@ def run_moment_correct(args):
     print(json.dumps(result), flush=True)
 
 
+def run_first_step(args):
+    """The first decode step after prefill: attend and score over the whole context, then
+    compress every KV head to its budget (k = context + 1 - budget evictions per head: select,
+    moment fold, compaction). The cache is restored from an HBM copy before each repetition;
+    only the step call itself is inside the events."""
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S, U, G, d, B = wl.n_scopes, wl.units_per_scope, wl.G, wl.d, wl.budget
+    t = synth.cache_tensors(wl, dev)
+    cache = kvc.Cache(k=t["k"], v=t["v"], pos=t["pos"], m=t["m"], length=t["length"], votes=t["votes"])
+    mom = kvc.Moments.zeros(S, U, d, dev) if wl.moments else None
+    out = torch.empty((S, U, G, d), device=dev)
+    lse = torch.empty((S, U, G), device=dev)
+    s = torch.empty((S, cache.capacity), device=dev)
+    evict = torch.zeros((S, cache.capacity), dtype=torch.uint8, device=dev)
+    ws = kvc.workspace(kvc.kvc_decode_workspace_size(cache, G, 0), dev)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    alpha = float(np.float32(wl.alpha))
+    fields = [cache.k, cache.v, cache.pos, cache.m, cache.length] + ([cache.votes] if cache.votes is not None else [])
+    saved = [x.clone() for x in fields]
+    q, kn, vn = synth.step_inputs(wl, 1, t["scales"], dev)
+    L0 = wl.initial_len + 1
+    times = []
+    for rep in range(args.warmup + args.steps):
+        for x, y in zip(fields, saved):
+            x.copy_(y)
+        if mom is not None:
+            for x in (mom.n, mom.sk, mom.sv, mom.S):
+                x.zero_()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        kvc.kvc_decode_step(cache, kn, vn, wl.context, q, G, scale, wl.rule, alpha, B, out, lse, s, mom, None,
+                            evict, max_len=L0, ws=ws)
+        end.record()
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            times.append(start.elapsed_time(end))
+    assert int(cache.length.min()) == B and int(cache.length.max()) == B
+    status = kvc.kvc_workspace_status(ws)
+    if status != 0:
+        raise SystemExit(f"device status {status} after the first step")
+    ms = float(np.median(times))
+    k = L0 - B
+    esz = 2 if wl.dtype == "bf16" else 4
+    row = 2 * d * esz
+    ev = evict[:, :L0].bool()
+    moved = int((~ev[:, B:]).sum())                       # survivors above the budget fill the holes
+    per_token = row + 12 + 8 + (4 if wl.prior_votes else 0)   # K/V, m r/w + s, select keys, votes
+    bytes_step = (S * U * L0 * row + S * L0 * (per_token - row)
+                  + S * U * k * row                       # evicted rows re-read by the fold
+                  + moved * (2 * U * row + 24)            # moved rows and slot arrays (read + write)
+                  + (S * U * (2 * d * d * 4 + 4 * d * 4) if wl.moments else 0))
+    achieved = bytes_step / (ms / 1e3) / 1e9
+    result = {"metric": "first decode step: cached tokens attended+scored, compressed to the budget, per sec",
+              "value": S * U * L0 / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+              "config": {"workload": wl.name + " first step", "kv_heads": S * U, "live_tokens_per_head": L0,
+                         "budget": B, "evicted_per_head": k, "moved_rows": moved, "moments": wl.moments},
+              "roofline": {"bound": "hbm", "achieved": achieved, "peak": rf.MI355X_HBM_GBPS, "unit": "GB/s",
+                           "frac": achieved / rf.MI355X_HBM_GBPS, "traffic": None, "bytes_per_step": bytes_step,
+                           "ms_all": times}}
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_info
+        for x, y in zip(fields, saved):
+            x.copy_(y)
+        prm = oracle.StepParams(scale=scale, rule=wl.rule, alpha=alpha, budget=B)
+        states, qh, knh, vnh = host_scopes(cache, [0], wl.dtype, q, kn, vn)
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 20.0) or done == 0:
+            oracle.decode_step(states[0], knh[0], vnh[0], wl.context, qh[0], prm)
+            done += 1
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        result["cpu_baseline"] = {"value": done * U * L0 / dt, "unit": "tokens/s", "cores": int(threads),
+                                  "kind": "oracle",
+                                  "sample": f"{done} first steps of KV head 0 of {wl.name} (L={L0}, k={k}) "
+                                            f"in {dt:.1f} s, numpy float64 oracle"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,8 +351,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="step", choices=["step", "moment_correct"],
-                    help="step: the fused decode step (default); moment_correct: MomentKV's corrected output")
+    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct"],
+                    help="step: the fused decode step (default); first_step: the bulk compression step "
+                         "after prefill; moment_correct: MomentKV's corrected output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter scaling)")
@@ -279,6 +365,11 @@ def main():
 
     if args.op == "moment_correct":
         run_moment_correct(args)
+        return
+    if args.op == "first_step":
+        if args.steps == 200 and args.warmup == 20:
+            args.steps, args.warmup = 5, 1
+        run_first_step(args)
         return
     if args.workload in synth.LAPROX_WORKLOADS:
         if args.steps == 200 and args.warmup == 20:
