@@ -46,15 +46,15 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch: float):
+def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; otherwise None."""
+    taken on this workload and the current kernel source; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != kernel_source_sha():
+    if t.get("source_sha") != kernel_source_sha() or not t.get("workload", "").startswith(workload + " "):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -86,21 +86,59 @@ def cpu_baseline(run_state, wl, seconds: float):
     from threadpoolctl import threadpool_info
     states, q, kn, vn, t = run_state
     prm = oracle.StepParams(scale=float(np.float32(1 / np.sqrt(wl.d))), rule=wl.rule,
-                            alpha=float(np.float32(wl.alpha)), budget=wl.budget)
+                            alpha=float(np.float32(wl.alpha)), budget=wl.budget,
+                            groups=wl.n_layers if wl.scope == "model" else 1, merge=wl.merge,
+                            row_dtype=wl.dtype)
     tokens, steps = 0, 0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for j, st in enumerate(states):
             _, res = oracle.decode_step(st, kn[j], vn[j], t, q[j], prm)
-            tokens += st.length + 1
+            tokens += scope_tokens(wl, st.length + 1)
             steps += 1
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    what = ("per-sequence steady steps (all layers, one slot set)" if wl.scope == "model"
+            else "per-KV-head steady steps")
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} per-KV-head steady steps of {wl.name} (L={wl.budget + 1}, G={wl.G}, "
-                      f"k=1, moments on) in {dt:.1f} s, numpy float64 oracle"}
+            "sample": f"{steps} {what} of {wl.name} (L={wl.budget + 1}, G={wl.G}, k=1, "
+                      f"moments {'on' if wl.moments else 'off'}{', ZIP merge' if wl.merge else ''}) "
+                      f"in {dt:.1f} s, numpy float64 oracle"}
+
+
+def scope_tokens(wl, L: int) -> int:
+    """Cached tokens one steady step of one scope attends over: every unit's live rows; with
+    one slot set shared by the layers, layer 1 sees L and evicts one, the others see L - 1."""
+    if wl.scope == "model":
+        return wl.n_kv * (L + (wl.n_layers - 1) * (L - 1))
+    return L
+
+
+def step_bytes(wl, L: int) -> int:
+    """Algorithmic bytes of one steady step over the whole workload (L = live tokens of a scope
+    after the append). Per KV head: rf.unit_step_bytes (K/V, utility, score, q, o, append, one
+    moved row, moment fold); a ZIP merge adds the cosine pass over the scope's keys and the
+    merged rows; with one slot set per sequence every layer's call reads and rewrites the
+    shared utility and score and only layer 1 appends and moves."""
+    elem = 2 if wl.dtype == "bf16" else 4
+    d, G, row = wl.d, wl.G, wl.d * (2 if wl.dtype == "bf16" else 4)
+    if wl.scope == "model":
+        total = 0
+        for layer in range(wl.n_layers):
+            Ll = L if layer == 0 else L - 1
+            per_scope = (wl.n_kv * Ll * 2 * row + Ll * (12 + (4 if wl.prior_votes else 0))
+                         + wl.n_kv * (G * row + G * d * 4 + G * 4))
+            if layer == 0:
+                U = wl.n_layers * wl.n_kv
+                per_scope += U * 4 * row + 12 + U * 4 * row + 24
+            total += per_scope * wl.n_scopes
+        return total
+    ub = rf.unit_step_bytes(L=L, k=1, G=G, d=d, elem=elem, votes=wl.prior_votes, moments=wl.moments,
+                            write_score=True)
+    extra = (L * row + 6 * row) if wl.merge else 0
+    return (ub.total + extra) * wl.n_scopes * wl.units_per_scope
 
 
 LAPROX_STAGES = ["wbar_prep", "window_pass1", "row_combine", "window_pass2", "v_wbar_mfma", "product",
@@ -396,11 +434,29 @@ def main():
         q_all.append(q)
         kn_all.append(kn)
         vn_all.append(vn)
-    pos0 = wl.context
+    pos0 = wl.context                           # the next token's position (prior entries lie below it)
 
-    def step_call(i, max_len):
-        kvc.kvc_decode_step(cache, kn_all[i], vn_all[i], pos0 + i, q_all[i], G, scale, wl.rule, alpha, B,
-                            out, lse, s, mom, None, None, max_len=max_len, ws=ws)
+    if wl.scope == "model":
+        # one call per layer (the layer's KV heads attend and score, the shared utility is
+        # updated and the scope evicts); the first layer's call appends every layer's rows
+        nkv = wl.n_kv
+        q_layers = [[q[:, l * nkv:(l + 1) * nkv].contiguous() for l in range(wl.n_layers)] for q in q_all]
+        out_layers = [torch.empty((S, nkv, G, d), device=dev) for _ in range(wl.n_layers)]
+        lse_layers = [torch.empty((S, nkv, G), device=dev) for _ in range(wl.n_layers)]
+
+        def step_call(i, max_len):
+            refresh = wl.lazy_refresh == 0 or i % wl.lazy_refresh == 0
+            for l in range(wl.n_layers):
+                kvc.kvc_decode_step(cache, kn_all[i] if l == 0 else None, vn_all[i] if l == 0 else None,
+                                    pos0 + i, q_layers[i][l], G, scale, wl.rule, alpha, B, out_layers[l],
+                                    lse_layers[l], s, mom, None, None, refresh=refresh, attn_unit0=l * nkv,
+                                    attn_units=nkv, max_len=max_len, ws=ws)
+    else:
+        merges = [kvc.merge_desc(q, G, scale) for q in q_all] if wl.merge else None
+
+        def step_call(i, max_len):
+            kvc.kvc_decode_step(cache, kn_all[i], vn_all[i], pos0 + i, q_all[i], G, scale, wl.rule, alpha, B,
+                                out, lse, s, mom, merges[i] if merges else None, None, max_len=max_len, ws=ws)
 
     step_call(0, wl.initial_len + 1)            # first step: bulk compression to the budget
     for i in range(1, 1 + args.warmup):
@@ -408,10 +464,11 @@ def main():
     torch.cuda.synchronize()
     assert int(cache.length.min()) == B and int(cache.length.max()) == B
 
-    # The timed region is K back-to-back launches of the one step kernel on the launch
-    # stream (torch's current stream), bracketed by two HIP events: the average launch
-    # duration of the kernel is the region's length over K (events between launches
-    # would add their own cost to every step).
+    # The timed region is K back-to-back steps on the launch stream (torch's current
+    # stream), bracketed by two HIP events: for the per-head workloads a step is one
+    # kernel launch, so the region's length over K is that kernel's average duration
+    # (events between launches would add their own cost to every step); a model-scope
+    # step is one call per layer.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -426,14 +483,12 @@ def main():
         raise SystemExit(f"device status {status} after the timed steps")
 
     L = B + 1
-    tokens_per_step = S * U * L
+    tokens_per_step = S * scope_tokens(wl, L) if wl.scope == "model" else S * U * L
     ms_per_step = total_ms / args.steps
     value = tokens_per_step / (ms_per_step / 1e3)
-    ub = rf.unit_step_bytes(L=L, k=1, G=G, d=d, elem=2 if wl.dtype == "bf16" else 4,
-                            votes=wl.prior_votes, moments=wl.moments, write_score=True)
-    bytes_per_launch = ub.total * S * U
+    bytes_per_launch = step_bytes(wl, L)
     achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
-    traffic = measured_traffic(bytes_per_launch)
+    traffic = measured_traffic(wl.name)
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
@@ -455,7 +510,7 @@ def main():
     if not args.no_cpu_baseline:
         i = 1 + args.warmup + args.steps     # inputs of the next step, applied to the current state
         q, kn, vn = synth.step_inputs(wl, i + 1, t["scales"], dev)
-        state = host_scopes(cache, list(range(min(S, 32))), wl.dtype, q, kn, vn)
+        state = host_scopes(cache, list(range(min(S, 2 if wl.scope == "model" else 32))), wl.dtype, q, kn, vn)
         result["cpu_baseline"] = cpu_baseline(state + (pos0 + i,), wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -15,8 +15,13 @@ namespace {
 
 constexpr int kHD = 128;
 constexpr int kTargetWorkgroups = 2048;   // workgroups per launch to aim for (merge, bulk chunks)
-constexpr int kSplitWorkgroups = 1024;    // split-K attention workgroups (512 threads) per launch
+constexpr int kSplitWorkgroups = 256;     // split-K attention workgroups (512 threads) per launch
 constexpr int kMinSubChunksPerSplit = 16;
+constexpr int kMaxSubChunksPerSplit = 512;
+// Epilogue score chunks: about kScoreWork (token, head) weights per workgroup,
+// at least kScoreChunkMin tokens (the factor cache of a chunk then fits in LDS).
+constexpr int kScoreWork = 8192;
+constexpr int kScoreChunkMin = 64;
 constexpr int kMergeSplitsMax = 64;
 // One workgroup per scope (no split-K) once there are this many single-unit
 // scopes to spread over the 256 CUs, each scope's live length is bounded so
@@ -56,15 +61,18 @@ bool valid_G(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 struct DecodeLayout {
   int n_splits, nsub_cap, merge_splits;
   int bulk_chunks, bulk_chunk, fold_splits, move_blocks;
-  size_t status, partM, partZ, partO, fac, subM, ews, flags, list, list2;
+  size_t status, partM, partZ, partO, fac, subM, ews, flags, list, list2, cand_key, cand_slot;
+  int n_score_chunks;
   size_t merge_cos, merge_slot, bulk_state, bulk_cnt, bulk_hist, fpart, total;
 };
 
-// Split-K workgroups per attention unit: about kSplitWorkgroups in the launch,
-// each streaming at least kMinSubChunksPerSplit sub-chunks (two per wave at
-// the deepest prefetch) so its loads stay in flight.
+// Split-K workgroups per attention unit: one round of workgroups over the CUs
+// (kSplitWorkgroups, one 512-thread workgroup per CU), more when a split would
+// stream over kMaxSubChunksPerSplit sub-chunks (a shorter tail), and never so
+// many that a split streams fewer than kMinSubChunksPerSplit (two per wave at
+// the deepest prefetch) and its loads cannot stay in flight.
 int split_count(int attn_units_total, int nsub) {
-  const int want = std::max(1, ceil_div(kSplitWorkgroups, attn_units_total));
+  const int want = std::max(ceil_div(kSplitWorkgroups, attn_units_total), ceil_div(nsub, kMaxSubChunksPerSplit));
   const int most = std::max(1, nsub / kMinSubChunksPerSplit);
   return std::max(1, std::min(want, most));
 }
@@ -97,6 +105,9 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.list2 = o;    o = align_up(o + size_t(c->n_scopes) * cap * 4);
   d.merge_cos = o;  o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 8);
   d.merge_slot = o; o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 4);
+  d.n_score_chunks = ceil_div(c->capacity, kScoreChunkMin);
+  d.cand_key = o;   o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 8);
+  d.cand_slot = o;  o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 4);
   d.bulk_state = o; o = align_up(o + size_t(c->n_scopes) * sizeof(kvc::BulkScope));
   d.bulk_cnt = o;   o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 8);
   d.bulk_hist = o;  o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 256 * 4);
@@ -207,6 +218,16 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.list = at<int32_t>(ws, d.list);
   a.list2 = at<int32_t>(ws, d.list2);
   a.nsub_cap = d.nsub_cap;
+  a.row_bytes = kHD * (c->dtype == KVC_BF16 ? 2 : 4);
+  a.max_len = max_len;
+  a.n_score_chunks = d.n_score_chunks;
+  a.cand_key = at<uint64_t>(ws, d.cand_key);
+  a.cand_slot = at<int32_t>(ws, d.cand_slot);
+  {
+    const int heads = attn_units * G;   // <= 64
+    const int chunk = std::max(kScoreChunkMin, kScoreWork / heads);
+    a.score_chunk = chunk / kScoreChunkMin * kScoreChunkMin;
+  }
   const int CH = kvc::decode_chunk_tokens(c->dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   bool per_scope = c->units_per_scope == 1 && c->n_scopes >= kUnitMinScopes &&
@@ -236,7 +257,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
       b.chunk = d.bulk_chunk;
       b.fold_splits = d.fold_splits;
       b.move_blocks = d.move_blocks;
-      if (kvc::launch_bulk(a, b, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+      if (kvc::launch_bulk(a, b, c->dtype, hs) != hipSuccess) return KVC_ERR_DEVICE;
     }
   }
   if (a.mode == 2) {
@@ -246,6 +267,8 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
     mg.scale = double(merge->scale);
     mg.eps = merge->eps;
     mg.n_splits = d.merge_splits;
+    mg.e_slot = a.list;               // the epilogue's choice, list[0] of each scope
+    mg.e_stride = c->capacity;
     mg.part_cos = at<double>(ws, d.merge_cos);
     mg.part_slot = at<int32_t>(ws, d.merge_slot);
     if (kvc::launch_merge(cache_args(c), a.flags, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;

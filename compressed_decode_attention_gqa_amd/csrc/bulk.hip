@@ -1,10 +1,9 @@
 // Device-wide eviction of k > 1 entries per scope (the first, bulk step that
 // compresses a prefilled cache down to its budget, or any step whose scopes
-// are far over budget). The attention kernel has already written the outputs
-// and the per-token weights with their sub-chunk factors; these kernels finish
-// the step over the whole grid instead of one workgroup per scope:
+// are far over budget). The epilogue kernels have already written the outputs,
+// the new utilities and the appended row; these kernels finish the step over
+// the whole grid instead of one workgroup per scope:
 //
-//   score      per-token score, utility update, appended row
 //   hist, pick x 8   radix select of the k lowest (utility, position) keys:
 //              per pass a 256-bin histogram of each chunk's keys under the
 //              current prefix, then one workgroup per scope sums the chunks and
@@ -32,60 +31,6 @@ constexpr int PART_STRIDE = HD * HD + 2 * HD;   // floats per fold partial: S, s
 
 __device__ __forceinline__ uint64_t slot_key(const StepArgs &a, int64_t sc, int i) {
   return order_key(a.m[sc + i], uint32_t(a.pos[sc + i]));
-}
-
-// ------------------------------------------------------------ score, utility, append
-// InertiaKV §3.1 eqs. (1)-(4) for the scopes handed over: s(i) is the vote-weighted
-// per-token weight exp(l - M_sub) times the factor exp(M_sub - M) / Z of its
-// sub-chunk, averaged over the scope's attention heads; then the utility rule.
-// The first workgroup of the scope also writes the appended token's rows.
-template <int G>
-__global__ __launch_bounds__(WG) void k_bulk_score(const StepArgs a, const BulkArgs b, const int CH,
-                                                  const int row_bytes) {
-  const int scope = blockIdx.y, tid = threadIdx.x;
-  const BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
-  const int L = st.L, Ua = a.attn_units, cap = a.capacity;
-  const int64_t sc = int64_t(scope) * cap;
-  const float *ew = a.ews + int64_t(scope) * Ua * G * cap;
-  const double *fm = a.subM + int64_t(scope) * Ua * a.nsub_cap * G;
-  const double inv_heads = 1.0 / double(Ua * G);
-  const double alpha = double(a.alpha);
-  const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
-  for (int i = i0 + tid; i < i1; i += WG) {
-    const bool isnew = a.append && i == L - 1;
-    if (a.refresh) {
-      const int pv = isnew ? 1 : (a.votes ? a.votes[sc + i] : 1);
-      const int c = i / CH;
-      double acc = 0.0;
-      for (int ua = 0; ua < Ua; ++ua) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          acc += double(ew[(int64_t(ua) * G + g) * cap + i]) * fm[(int64_t(ua) * a.nsub_cap + c) * G + g];
-      }
-      const double sv = double(pv) * acc * inv_heads;
-      if (a.s) a.s[sc + i] = float(sv);
-      const double mo = isnew ? 0.0 : double(a.m[sc + i]);
-      const double r = a.rule == 0 ? sv : a.rule == 1 ? mo + sv : alpha * mo + (1.0 - alpha) * sv;
-      a.m[sc + i] = float(r);
-    } else if (isnew) {
-      a.m[sc + i] = 0.f;
-    }
-  }
-  if (a.append && blockIdx.x == 0) {
-    const int nv = row_bytes / 16;
-    for (int idx = tid; idx < a.units * nv; idx += WG) {
-      const int u = idx / nv, c = idx - u * nv;
-      const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * row_bytes;
-      const int64_t src = (int64_t(scope) * a.units + u) * row_bytes;
-      st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
-      st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
-    }
-    if (tid == 0) {
-      if (a.votes) a.votes[sc + L - 1] = 1;
-      a.pos[sc + L - 1] = a.t;
-    }
-  }
 }
 
 // ------------------------------------------------------------ radix select pass
@@ -601,17 +546,9 @@ __global__ __launch_bounds__(WG) void k_bulk_move(const StepArgs a, const BulkAr
 
 }  // namespace
 
-hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, int G, hipStream_t st) {
+hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st) {
   const dim3 chunks(b.n_chunks, a.n_scopes);
-  const int CH = decode_chunk_tokens(dtype);
   const int row_bytes = HD * (dtype == 0 ? 2 : 4);
-  switch (G) {
-    case 1: hipLaunchKernelGGL(k_bulk_score<1>, chunks, dim3(WG), 0, st, a, b, CH, row_bytes); break;
-    case 2: hipLaunchKernelGGL(k_bulk_score<2>, chunks, dim3(WG), 0, st, a, b, CH, row_bytes); break;
-    case 4: hipLaunchKernelGGL(k_bulk_score<4>, chunks, dim3(WG), 0, st, a, b, CH, row_bytes); break;
-    case 8: hipLaunchKernelGGL(k_bulk_score<8>, chunks, dim3(WG), 0, st, a, b, CH, row_bytes); break;
-    default: return hipErrorInvalidValue;
-  }
   for (int shift = 56; shift >= 0; shift -= 8) {
     hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, a, b, shift);
     hipLaunchKernelGGL(k_bulk_pick, dim3(a.n_scopes), dim3(WG), 0, st, b, shift);

@@ -13,9 +13,12 @@
 // the epilogue can normalise them into attention weights; the waves'
 // (M, Z, value sums) are combined into the workgroup's split partial.
 //
-// k_decode_epi: one workgroup per scope combines the split partials into o
-// and lse and runs score -> utility -> select -> fold -> compact (or hands
-// scopes that evict more than one entry to the grid-wide bulk kernels).
+// k_epi_score (token chunks x scopes) then k_epi_finish (one workgroup per
+// scope): the scope epilogue (score, utility, then select -> fold -> compact,
+// or a hand-over of scopes that evict more than one entry to the grid-wide
+// bulk kernels).
+#include <algorithm>
+
 #include "kvc_epilogue.h"
 #include "kvc_stream.h"
 
@@ -249,23 +252,17 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
   }
 }
 
-// ---------------------------------------------------------------- epilogue launch
+// ---------------------------------------------------------------- epilogue launches
+template <int G, int CH>
+__global__ __launch_bounds__(WG) void k_epi_score(const StepArgs a) {
+  __shared__ ScoreLds sh;
+  epi_score<G, CH>(a, sh);
+}
+
 template <typename T, int G>
-__global__ __launch_bounds__(WG) void k_decode_epi(const StepArgs a) {
-  __shared__ EpiLds ep;
-  const int scope = blockIdx.x;
-  const int L = a.len[scope] + a.append;
-  if (L > a.capacity) {
-    if (threadIdx.x == 0) {
-      a.status[0] = -4;
-      if (a.bulk) a.bulk[scope].k = 0;
-    }
-    return;
-  }
-  constexpr int CHW = UnitGeometry<T, G>::CHW;
-  const int64_t cap = a.capacity;
-  decode_epilogue<T, G, CHW>(a, scope, L, ep, a.ews + int64_t(scope) * a.attn_units * G * cap, cap,
-                             a.subM + int64_t(scope) * a.attn_units * a.nsub_cap * G, a.nsub_cap);
+__global__ __launch_bounds__(WG) void k_epi_finish(const StepArgs a) {
+  __shared__ EpiLds sh;
+  epi_finish<T, G>(a, sh);
 }
 
 template <typename T, int G>
@@ -274,7 +271,9 @@ static hipError_t launch_split_tg(const StepArgs &a, hipStream_t st) {
   const dim3 grid(a.n_splits, a.n_scopes * a.attn_units);
   if (a.votes) hipLaunchKernelGGL((k_decode_split<T, G, true>), grid, dim3(Geo::NT), 0, st, a);
   else hipLaunchKernelGGL((k_decode_split<T, G, false>), grid, dim3(Geo::NT), 0, st, a);
-  hipLaunchKernelGGL((k_decode_epi<T, G>), dim3(a.n_scopes), dim3(WG), 0, st, a);
+  const int chunks = std::max(1, std::min(a.n_score_chunks, (a.max_len + a.score_chunk - 1) / a.score_chunk));
+  hipLaunchKernelGGL((k_epi_score<G, Geo::CHW>), dim3(chunks, a.n_scopes), dim3(WG), 0, st, a);
+  hipLaunchKernelGGL((k_epi_finish<T, G>), dim3(a.n_scopes), dim3(WG), 0, st, a);
   return hipGetLastError();
 }
 

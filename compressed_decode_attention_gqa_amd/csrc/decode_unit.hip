@@ -288,7 +288,10 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   if (overflow || k > 1) {
     // k > 1 cannot happen: the host launches this kernel only when
     // lds_len <= budget + 1, and L <= lds_len here
-    if (tid == 0) a.status[0] = overflow ? -4 : -3;
+    if (tid == 0) {
+      a.status[0] = overflow ? -4 : -3;
+      if (a.mode == 2) a.list[sc] = -1;
+    }
     return;
   }
 
@@ -455,19 +458,18 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     }
   }
   if (!step || k == 0) {
-    for (int i = tid; i < L; i += NT) {
-      if (a.evict_out) a.evict_out[sc + i] = 0;
-      if (a.mode == 2) a.flags[sc + i] = 0;
+    if (a.evict_out)
+      for (int i = tid; i < L; i += NT) a.evict_out[sc + i] = 0;
+    if (tid == 0) {
+      if (a.mode == 2) a.list[sc] = -1;   // nothing for the merge kernels
+      a.len[scope] = L;
     }
-    if (tid == 0) a.len[scope] = L;
     return;
   }
 
   // ---- one eviction: flags, fold, fill the hole with the last slot
-  for (int i = tid; i < L; i += NT) {
-    if (a.evict_out) a.evict_out[sc + i] = (i == e1);
-    if (a.mode == 2) a.flags[sc + i] = (i == e1);
-  }
+  if (a.evict_out)
+    for (int i = tid; i < L; i += NT) a.evict_out[sc + i] = (i == e1);
   if (tid == 0) a.list[sc] = e1;
   if (fold) {
     if (e1 == L - 1) {

@@ -59,6 +59,12 @@ struct StepArgs {
   int32_t *list, *list2;
   int32_t n_splits, nsub_cap;
   int32_t lds_len;   // per-scope kernel: live tokens its LDS holds (at most budget + 1)
+  int32_t row_bytes; // bytes of one K (or V) row
+  int32_t max_len;   // live length the launch is sized for (a longer device length is still handled)
+  // split path: score chunks and each chunk's lowest (m, pos) key
+  int32_t score_chunk, n_score_chunks;   // tokens per chunk; chunks per scope the arrays hold
+  uint64_t *cand_key;
+  int32_t *cand_slot;
   BulkScope *bulk;   // non-null: scopes evicting k > 1 stop after the utility update
 };
 
@@ -68,9 +74,9 @@ hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st);
 hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st);
 // LDS (static + dynamic) of the per-scope kernel for lds_len live tokens
 size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes);
-// Device-wide score -> select -> flags -> lists -> fold -> moves for the scopes
-// the attention kernel handed over (BulkScope::k > 1).
-hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, int G, hipStream_t st);
+// Device-wide select -> flags -> lists -> fold -> moves for the scopes the
+// epilogue handed over (BulkScope::k > 1).
+hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st);
 size_t bulk_part_floats();   // floats of one fold partial
 
 }  // namespace kvc

@@ -1,5 +1,11 @@
-// Scope epilogue of the decode step (combine split partials, score, utility,
-// select, moment fold, compaction), shared by the decode kernels.
+// Scope epilogue of the split-K decode step, as two grid launches after the
+// attention kernel:
+//   score  (workgroups x scopes): per-token score s(i) and utility m(i) over
+//          token chunks of every scope, the lowest (m, pos) key of each chunk,
+//          the appended token's rows;
+//   finish (one workgroup per scope): combine the split partials into o and
+//          lse, then select -> fold -> compact, or hand a scope that evicts
+//          more than one entry to the grid-wide bulk kernels.
 #pragma once
 
 #include "kvc_decode.h"
@@ -13,183 +19,318 @@ __device__ __forceinline__ double apply_rule(int rule, double alpha, double m_ol
   return alpha * m_old + (1.0 - alpha) * s;                 // EMA
 }
 
+// Largest (sub-chunks touched by one score chunk) x (attention heads of a
+// scope): the host sizes score chunks so a chunk's factors fit.
+constexpr int SCORE_FAC_MAX = 1280;
+// Split partials (heads x splits) the score kernel stages in LDS at once.
+constexpr int SCORE_PAIR_MAX = 1024;
+
+struct ScoreLds {
+  double M[64], iZ[64];
+  double fac[SCORE_FAC_MAX];
+  double pm[SCORE_PAIR_MAX];   // split maxima; then the splits' output weights exp(pm - M) / Z
+  double pz[SCORE_PAIR_MAX];
+  uint64_t wkey[WG / 64];
+  int wslot[WG / 64];
+};
+
 struct EpiLds {
   union {
     SelectLds sel;
     FoldLds fold;
   };
-  double M[64], Z[64];
-  int red[8];
-  int best_slot;
+  uint64_t ckey[WG / 64];
+  int cslot[WG / 64];
 };
 
-// ---------------------------------------------------------------- epilogue
-// CH: tokens per sub-chunk, the granularity at which the streaming phase
-// recorded its running maxima (subM) for the per-token weights.
-// ew: per-token weights exp(l - M_sub) of the scope's first attention unit,
-// [ua][g][ew_ld]; fm: sub-chunk maxima [ua][fm_ld][g], replaced in place by the
-// score factors.
-template <typename T, int G, int CH>
-__device__ void decode_epilogue(const StepArgs &a, const int scope, const int L, EpiLds &sh,
-                                const float *ew, int64_t ew_ld, double *fm, int64_t fm_ld) {
-  const int tid = threadIdx.x;
-  const int Ua = a.attn_units, cap = a.capacity, ns = a.n_splits;
-  const int gu0 = scope * Ua;
-  const int64_t sc = int64_t(scope) * cap;
-  const int row_bytes = HD * int(sizeof(T));
+// M and Z of attention head (gu, g) over the split partials.
+template <int G>
+__device__ __forceinline__ void combine_head(const StepArgs &a, int gu, int g, double &M, double &Z) {
+  const int ns = a.n_splits;
+  M = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) M = fmax(M, a.partM[(int64_t(gu) * ns + sp) * G + g]);
+  Z = 0.0;
+  for (int sp = 0; sp < ns; ++sp) {
+    const double pm = a.partM[(int64_t(gu) * ns + sp) * G + g];
+    if (pm > -INFINITY) Z += a.partZ[(int64_t(gu) * ns + sp) * G + g] * exp(pm - M);
+  }
+}
 
-  // (1) combine split partials: per attention head M, Z, lse, o.
-  if (tid < Ua * G) {
-    const int gu = gu0 + tid / G, g = tid % G;
-    double M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmax(M, a.partM[(int64_t(gu) * ns + sp) * G + g]);
-    double Z = 0.0;
-    for (int sp = 0; sp < ns; ++sp) {
-      const double pm = a.partM[(int64_t(gu) * ns + sp) * G + g];
-      if (pm > -INFINITY) Z += a.partZ[(int64_t(gu) * ns + sp) * G + g] * exp(pm - M);
+// ---------------------------------------------------------------- score
+// InertiaKV §3.1 eq. (1): s(i) = mean over the scope's Ua*G attention heads of
+// a_{h,i} = p_i e_{h,i} F_{h,c(i)}, where e = exp(l - M_sub) is the weight the
+// attention kernel stored and F = exp(M_sub - M) / Z the factor of its
+// CH-token sub-chunk; then eqs. (2)-(4) for m(i). For a step that evicts one
+// entry, each chunk also reports its lowest (m, pos) key. Workgroups stride
+// over the scope's chunks, so any live length is covered.
+template <int G, int CH>
+__device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.y;
+  const int Ua = a.attn_units, cap = a.capacity, H = Ua * G;
+  const int L = a.len[scope] + a.append;
+  if (L > cap) return;   // reported by the finish kernel
+  const int64_t sc = int64_t(scope) * cap;
+  const int gu0 = scope * Ua;
+  const bool step = a.mode != 0;
+  const bool score = a.refresh && (step || a.s != nullptr);
+  const int k = step ? max(0, L - a.budget) : 0;
+  const double inv_heads = 1.0 / double(H);
+  const double alpha = double(a.alpha);
+  const float *ews = a.ews + int64_t(gu0) * G * cap;
+  const int chunk = a.score_chunk;
+
+  // per attention head M and Z over the split partials (staged in LDS when they fit)
+  const int ns = a.n_splits, P = H * ns;
+  const bool staged = P <= SCORE_PAIR_MAX;
+  if (staged) {
+    for (int idx = tid; idx < P; idx += WG) {
+      const int h = idx / ns, sp = idx - (idx / ns) * ns;
+      const int64_t pi = (int64_t(gu0 + h / G) * ns + sp) * G + h % G;
+      sh.pm[idx] = a.partM[pi];
+      sh.pz[idx] = a.partZ[pi];
     }
-    for (int sp = 0; sp < ns; ++sp) {
-      const double pm = a.partM[(int64_t(gu) * ns + sp) * G + g];
-      a.fac[(int64_t(gu) * ns + sp) * G + g] = (Z > 0.0 && pm > -INFINITY) ? float(exp(pm - M) / Z) : 0.f;
+    __syncthreads();
+  }
+  if (tid < H) {
+    double M, Z;
+    if (staged) {
+      M = -INFINITY;
+      for (int sp = 0; sp < ns; ++sp) M = fmax(M, sh.pm[tid * ns + sp]);
+      Z = 0.0;
+      for (int sp = 0; sp < ns; ++sp) {
+        const double pm = sh.pm[tid * ns + sp];
+        if (pm > -INFINITY) Z += sh.pz[tid * ns + sp] * exp(pm - M);
+      }
+    } else {
+      combine_head<G>(a, gu0 + tid / G, tid % G, M, Z);
     }
     sh.M[tid] = M;
-    sh.Z[tid] = Z;
-    a.lse[int64_t(gu) * G + g] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
+    sh.iZ[tid] = Z > 0.0 ? 1.0 / Z : 0.0;
+    if (blockIdx.x == tid % gridDim.x) a.lse[int64_t(gu0) * G + tid] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
   }
   __syncthreads();
-  for (int idx = tid; idx < Ua * G * HD; idx += WG) {
-    const int pair = idx / HD, e = idx - (idx / HD) * HD;
-    const int gu = gu0 + pair / G, g = pair % G;
+  // the attention output of the heads h = blockIdx.x (mod gridDim.x): o = sum over
+  // splits of the split's value sums times exp(M_split - M) / Z
+  if (staged) {
+    for (int idx = tid; idx < P; idx += WG) {
+      const int h = idx / ns;
+      const double pm = sh.pm[idx];
+      sh.pm[idx] = (sh.iZ[h] > 0.0 && pm > -INFINITY) ? exp(pm - sh.M[h]) * sh.iZ[h] : 0.0;
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < H * HD; idx += WG) {
+    const int h = idx / HD, e = idx - (idx / HD) * HD;
+    if (h % gridDim.x != blockIdx.x) continue;
+    const int64_t gh = int64_t(gu0) * G + h;   // (gu0 + h / G) * G + h % G
     float acc = 0.f;
     for (int sp = 0; sp < ns; ++sp) {
-      const int64_t pi = (int64_t(gu) * ns + sp) * G + g;
-      acc = fmaf(a.partO[pi * HD + e], a.fac[pi], acc);
+      const int64_t pi = (int64_t(gu0 + h / G) * ns + sp) * G + h % G;
+      double wgt;
+      if (staged) {
+        wgt = sh.pm[h * ns + sp];
+      } else {
+        const double pm = a.partM[pi];
+        wgt = (sh.iZ[h] > 0.0 && pm > -INFINITY) ? exp(pm - sh.M[h]) * sh.iZ[h] : 0.0;
+      }
+      acc = fmaf(a.partO[pi * HD + e], float(wgt), acc);
     }
-    a.out[(int64_t(gu) * G + g) * HD + e] = acc;
+    a.out[gh * HD + e] = acc;
   }
-
-  // (2) score factors F = exp(M_sub - M) / Z, in place of the sub-chunk maxima.
-  const bool score = a.refresh && (a.mode != 0 || a.s != nullptr);
-  const int nsubL = (L + CH - 1) / CH;
-  if (score) {
-    for (int idx = tid; idx < Ua * nsubL * G; idx += WG) {
-      const int ua = idx / (nsubL * G), rem = idx - ua * (nsubL * G);
-      const int c = rem / G, g = rem - (rem / G) * G;
-      double *p = fm + (int64_t(ua) * fm_ld + c) * G + g;
-      const double Z = sh.Z[ua * G + g];
-      *p = Z > 0.0 ? exp(*p - sh.M[ua * G + g]) / Z : 0.0;
+  for (int i0 = blockIdx.x * chunk; i0 < L; i0 += gridDim.x * chunk) {
+    const int i1 = min(L, i0 + chunk);
+    const int c0 = i0 / CH, nsc = (i1 - 1) / CH - c0 + 1;
+    __syncthreads();
+    if (score) {
+      for (int idx = tid; idx < nsc * H; idx += WG) {
+        const int c = c0 + idx / H, h = idx - (idx / H) * H;
+        const double m = a.subM[(int64_t(gu0 + h / G) * a.nsub_cap + c) * G + h % G];
+        sh.fac[idx] = sh.iZ[h] > 0.0 ? exp(m - sh.M[h]) * sh.iZ[h] : 0.0;
+      }
+    }
+    __syncthreads();
+    uint64_t best = ~0ull;
+    int bslot = 0x7fffffff;
+    for (int i = i0 + tid; i < i1; i += WG) {
+      const bool isnew = a.append && i == L - 1;
+      float mval = 0.f;
+      if (score) {
+        const int pv = isnew ? 1 : (a.votes ? a.votes[sc + i] : 1);
+        const double *f = sh.fac + (i / CH - c0) * H;
+        double acc = 0.0;
+        for (int ua = 0; ua < Ua; ++ua) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) acc += double(ews[(int64_t(ua) * G + g) * cap + i]) * f[ua * G + g];
+        }
+        const double sv = double(pv) * acc * inv_heads;
+        if (a.s) a.s[sc + i] = float(sv);
+        if (step) {
+          const double mo = isnew ? 0.0 : double(a.m[sc + i]);
+          mval = float(apply_rule(a.rule, alpha, mo, sv));
+          a.m[sc + i] = mval;
+        }
+      } else if (step) {
+        mval = isnew ? 0.f : a.m[sc + i];
+      }
+      if (isnew && !(score && step)) a.m[sc + i] = 0.f;
+      if (k == 1) {
+        const uint64_t key = order_key(mval, uint32_t(isnew ? a.t : a.pos[sc + i]));
+        if (key < best) {
+          best = key;
+          bslot = i;
+        }
+      }
+    }
+    if (k == 1) {   // keys are distinct (distinct positions): the minimum names one slot
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t b2 = shfl_xor_u64(best, o);
+        const int s2 = __shfl_xor(bslot, o);
+        if (b2 < best) {
+          best = b2;
+          bslot = s2;
+        }
+      }
+      if (lane == 0) {
+        sh.wkey[wave] = best;
+        sh.wslot[wave] = bslot;
+      }
+      __syncthreads();
+      if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < WG / 64; ++w) {
+          if (sh.wkey[w] < best) {
+            best = sh.wkey[w];
+            bslot = sh.wslot[w];
+          }
+        }
+        const int64_t ci = int64_t(scope) * a.n_score_chunks + i0 / chunk;
+        a.cand_key[ci] = best;
+        a.cand_slot[ci] = bslot;
+      }
+    }
+    // the appended token's rows and slot arrays, by the chunk that holds it
+    if (a.append && i0 <= L - 1 && L - 1 < i1) {
+      const int row_bytes = a.row_bytes, nv = row_bytes / 16;
+      for (int idx = tid; idx < a.units * nv; idx += WG) {
+        const int u = idx / nv, c = idx - (idx / nv) * nv;
+        const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * row_bytes;
+        const int64_t src = (int64_t(scope) * a.units + u) * row_bytes;
+        st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
+        st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
+      }
+      if (tid == 0) {
+        if (a.votes) a.votes[sc + L - 1] = 1;
+        a.pos[sc + L - 1] = a.t;
+      }
     }
   }
-  __syncthreads();
+}
 
-  const bool step = a.mode != 0;
-  const int k = step ? max(0, L - a.budget) : 0;
-  if (a.bulk && k > 1) {   // the grid-wide kernels launched after this one take over from (3)
+// ---------------------------------------------------------------- finish
+template <typename T, int G>
+__device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.x;
+  const int cap = a.capacity;
+  const int64_t sc = int64_t(scope) * cap;
+  const int row_bytes = HD * int(sizeof(T));
+  const int L = a.len[scope] + a.append;
+  if (L > cap) {
     if (tid == 0) {
-      BulkScope &b = a.bulk[scope];
-      b.prefix = 0;
-      b.mask = 0;
-      b.krem = k;
-      b.done = 0;
-      b.L = L;
-      b.k = k;
-      b.n_pairs = 0;
+      a.status[0] = -4;
+      if (a.bulk) a.bulk[scope].k = 0;
     }
     return;
   }
 
-  // (3) score s(i), utility m(i) and, for a single eviction, the argmin key.
-  const double inv_heads = 1.0 / double(Ua * G);
-  const double alpha = double(a.alpha);
-  uint64_t best = ~0ull;
-  int best_slot = 0x7fffffff;
-  for (int i = tid; i < L; i += WG) {
-    const bool isnew = a.append && i == L - 1;
-    float mval = 0.f;
-    if (score) {
-      const int pv = isnew ? 1 : (a.votes ? a.votes[sc + i] : 1);
-      const int c = i / CH;
-      double acc = 0.0;
-      for (int ua = 0; ua < Ua; ++ua) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          acc += double(ew[(int64_t(ua) * G + g) * ew_ld + i]) * fm[(int64_t(ua) * fm_ld + c) * G + g];
+  const bool step = a.mode != 0;
+  const int k = step ? max(0, L - a.budget) : 0;
+  if (a.bulk) {
+    if (k > 1) {   // the grid-wide kernels launched after this one take over
+      if (tid == 0) {
+        BulkScope &b = a.bulk[scope];
+        b.prefix = 0;
+        b.mask = 0;
+        b.krem = k;
+        b.done = 0;
+        b.L = L;
+        b.k = k;
+        b.n_pairs = 0;
       }
-      const double sv = double(pv) * acc * inv_heads;
-      if (a.s) a.s[sc + i] = float(sv);
-      if (step) {
-        const double mo = isnew ? 0.0 : double(a.m[sc + i]);
-        mval = float(apply_rule(a.rule, alpha, mo, sv));
-        a.m[sc + i] = mval;
-      }
-    } else if (step) {
-      mval = isnew ? 0.f : a.m[sc + i];
+      return;
     }
-    if (isnew && !(score && step)) a.m[sc + i] = 0.f;
-    if (k == 1) {
-      const uint32_t pi = uint32_t(isnew ? a.t : a.pos[sc + i]);
-      const uint64_t key = order_key(mval, pi);
-      if (key < best) {
-        best = key;
-        best_slot = i;
-      }
-    }
+    if (tid == 0) a.bulk[scope].k = 0;
   }
-
-  // (4) the appended token's rows and slot arrays.
-  if (a.append) {
-    const int nv = row_bytes / 16;
-    for (int idx = tid; idx < a.units * nv; idx += WG) {
-      const int u = idx / nv, c = idx - (idx / nv) * nv;
-      const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * row_bytes;
-      const int64_t src = (int64_t(scope) * a.units + u) * row_bytes;
-      st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
-      st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
-    }
-    if (tid == 0) {
-      if (a.votes) a.votes[sc + L - 1] = 1;
-      a.pos[sc + L - 1] = a.t;
-    }
-  }
-  if (k == 1) best_slot = wg_argmin_finish(best, best_slot, sh.sel);
-  __threadfence_block();
-  __syncthreads();
-
-  if (a.bulk && tid == 0) a.bulk[scope].k = 0;   // finished here: the bulk kernels skip this scope
-
   if (!step) {
     if (tid == 0) a.len[scope] = L;
     return;
   }
+  // merge mode: list[0] of the scope names the entry the merge kernels take (-1: none)
   if (k <= 0) {
-    for (int i = tid; i < L; i += WG) {
-      if (a.evict_out) a.evict_out[sc + i] = 0;
-      if (a.mode == 2) a.flags[sc + i] = 0;
+    if (a.evict_out)
+      for (int i = tid; i < L; i += WG) a.evict_out[sc + i] = 0;
+    if (tid == 0) {
+      if (a.mode == 2) a.list[sc] = -1;
+      a.len[scope] = L;
     }
-    if (tid == 0) a.len[scope] = L;
     return;
   }
   if (a.mode == 2 && k > 1) {     // a merge handles one eviction per step
     if (tid == 0) {
       a.status[0] = -3;
+      a.list[sc] = -1;
       a.len[scope] = L;
     }
-    for (int i = tid; i < L; i += WG) a.flags[sc + i] = 0;
     return;
   }
 
-  // (5) selection of the k lowest (m, pos).
+  // selection of the k lowest (m, pos)
   uint8_t *flags = a.flags + sc;
   int32_t *list = a.list + sc;
   int e1 = -1;
   if (k == 1) {
-    e1 = best_slot;
-    for (int i = tid; i < L; i += WG) {
-      if (a.evict_out) a.evict_out[sc + i] = (i == e1);
-      if (a.mode == 2) flags[i] = (i == e1);
+    // the lowest of the score chunks' keys
+    const int nch = (L + a.score_chunk - 1) / a.score_chunk;
+    uint64_t best = ~0ull;
+    int bslot = 0x7fffffff;
+    for (int c = tid; c < nch; c += WG) {
+      const uint64_t key = a.cand_key[int64_t(scope) * a.n_score_chunks + c];
+      if (key < best) {
+        best = key;
+        bslot = a.cand_slot[int64_t(scope) * a.n_score_chunks + c];
+      }
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t b2 = shfl_xor_u64(best, o);
+      const int s2 = __shfl_xor(bslot, o);
+      if (b2 < best) {
+        best = b2;
+        bslot = s2;
+      }
+    }
+    if (lane == 0) {
+      sh.ckey[wave] = best;
+      sh.cslot[wave] = bslot;
+    }
+    __syncthreads();
+    best = sh.ckey[0];
+    e1 = sh.cslot[0];
+#pragma unroll
+    for (int w = 1; w < WG / 64; ++w) {
+      if (sh.ckey[w] < best) {
+        best = sh.ckey[w];
+        e1 = sh.cslot[w];
+      }
+    }
+    if (a.evict_out)
+      for (int i = tid; i < L; i += WG) a.evict_out[sc + i] = (i == e1);
     if (tid == 0) list[0] = e1;
   } else {
+    // more than one eviction without the bulk kernels (a launch sized for at most
+    // one, on a longer device length): one workgroup selects, folds and compacts
     const float *mm = a.m + sc;
     const int32_t *pp = a.pos + sc;
     auto key = [&](int i) -> uint64_t { return order_key(mm[i], uint32_t(pp[i])); };
@@ -199,7 +340,7 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
   __threadfence_block();
   __syncthreads();
 
-  // (6) moment fold of the evicted rows, before they are overwritten.
+  // moment fold of the evicted rows, before they are overwritten
   if (a.mom_S) {
     for (int u = 0; u < a.units; ++u) {
       const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride;
@@ -226,13 +367,13 @@ __device__ void decode_epilogue(const StepArgs &a, const int scope, const int L,
     return;
   }
 
-  // (7) hole-filling compaction.
+  // hole-filling compaction
   ScopeRows rows{a.k, a.v, int64_t(scope) * a.scope_stride, a.unit_stride, a.units, row_bytes,
                  a.votes ? a.votes + sc : nullptr, a.pos + sc, a.m + sc};
   if (k == 1) {
     if (e1 < L - 1) move_slot_wg(rows, L - 1, e1);
   } else {
-    wg_compact_flags(rows, flags, L, k, a.list2 + sc, sh.red);
+    wg_compact_flags(rows, flags, L, k, a.list2 + sc, sh.fold.red);
   }
   if (tid == 0) a.len[scope] = L - k;
 }

@@ -16,6 +16,8 @@ struct CacheArgs {
 };
 
 struct MergeArgs {
+  const int32_t *e_slot;    // entry to merge per scope at e_slot[scope * e_stride] (-1: none), or
+  int64_t e_stride;         // null: the single flagged slot of the evict flags
   const char *q;
   int32_t G;
   double scale;

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
   const int64_t so = int64_t(scope) * c.capacity;
   const int L = c.len[scope];
   const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
-  const int e = merge_flagged(evict + so, L, sh.e);
+  const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
   if (e >= 0 && tid < HD) sh.ke[tid] = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
   __syncthreads();
 
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   const int L = c.len[scope];
   const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
   const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
-  const int e = merge_flagged(evict + so, L, sh.e);
+  const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
   if (e < 0) return;
   if (tid == 0) {
     double b = -INFINITY;
