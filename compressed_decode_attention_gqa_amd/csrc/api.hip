@@ -20,7 +20,7 @@ constexpr int kMinSubChunksPerSplit = 16;
 constexpr int kMaxSubChunksPerSplit = 512;
 // Epilogue score chunks: about kScoreWork (token, head) weights per workgroup,
 // at least kScoreChunkMin tokens (the factor cache of a chunk then fits in LDS).
-constexpr int kScoreWork = 8192;
+constexpr int kScoreWork = 2048;
 constexpr int kScoreChunkMin = 64;
 constexpr int kMergeSplitsMax = 64;
 // One workgroup per scope (no split-K) once there are this many single-unit

@@ -324,10 +324,10 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
   const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
   if (e < 0) return;
-  if (tid == 0) {
+  if (wave == 0) {   // the partner over the ranges' partials: lanes take partials, then a wave argmax
     double b = -INFINITY;
     int s = -1, p = 0x7fffffff;
-    for (int sp = 0; sp < mg.n_splits; ++sp) {
+    for (int sp = lane; sp < mg.n_splits; sp += 64) {
       const int64_t pi = int64_t(scope) * mg.n_splits + sp;
       const int sw = mg.part_slot[pi];
       if (sw < 0) continue;
@@ -338,7 +338,17 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
         p = pw;
       }
     }
-    sh.best_slot[0] = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double b2 = __shfl_xor(b, o);
+      const int s2 = __shfl_xor(s, o), p2 = __shfl_xor(p, o);
+      if (s2 >= 0 && (s < 0 || cos_better(b2, p2, b, p))) {
+        b = b2;
+        s = s2;
+        p = p2;
+      }
+    }
+    if (lane == 0) sh.best_slot[0] = s;
   }
   __syncthreads();
   const int cs = sh.best_slot[0];
