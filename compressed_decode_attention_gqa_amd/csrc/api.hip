@@ -77,6 +77,31 @@ int split_count(int attn_units_total, int nsub) {
   return std::max(1, std::min(want, most));
 }
 
+// Slot chunks per scope of the grid-wide select / count / list kernels: about
+// kTargetWorkgroups per launch, at most 256 per scope, whole multiples of 256 slots.
+void bulk_chunking(int n_scopes, int capacity, int &n_chunks, int &chunk) {
+  n_chunks = std::max(1, std::min({ceil_div(kTargetWorkgroups, n_scopes), 256, ceil_div(capacity, 256)}));
+  chunk = ceil_div(ceil_div(capacity, n_chunks), 256) * 256;
+}
+
+// Workspace of the grid-wide select (and compaction): per-scope state, chunk
+// histograms and chunk counts.
+struct SelectLayout {
+  int n_chunks, chunk;
+  size_t state, hist, cnt, total;
+};
+
+SelectLayout select_layout(int n_scopes, int capacity, size_t base = 0) {
+  SelectLayout l{};
+  bulk_chunking(n_scopes, capacity, l.n_chunks, l.chunk);
+  size_t o = base;
+  l.state = o; o = align_up(o + size_t(n_scopes) * sizeof(kvc::BulkScope));
+  l.hist = o;  o = align_up(o + size_t(n_scopes) * l.n_chunks * 256 * 4);
+  l.cnt = o;   o = align_up(o + size_t(n_scopes) * l.n_chunks * 8);
+  l.total = o;
+  return l;
+}
+
 DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   DecodeLayout d{};
   const int CH = kvc::decode_chunk_tokens(c->dtype);
@@ -86,8 +111,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.n_splits = split_count(int(nu), ceil_div(c->capacity, CH));
   d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
   // bulk eviction: slot chunks per scope (<= 256), fold splits per unit, move blocks per scope
-  d.bulk_chunks = std::max(1, std::min({ceil_div(kTargetWorkgroups, c->n_scopes), 256, ceil_div(c->capacity, 256)}));
-  d.bulk_chunk = ceil_div(ceil_div(c->capacity, d.bulk_chunks), 256) * 256;
+  bulk_chunking(c->n_scopes, c->capacity, d.bulk_chunks, d.bulk_chunk);
   const int64_t units_total = int64_t(c->n_scopes) * c->units_per_scope;
   d.fold_splits = int(std::max<int64_t>(1, std::min<int64_t>(kFoldSplitsMax, (kFoldWorkgroups + units_total - 1) / units_total)));
   d.move_blocks = std::max(1, std::min(64, ceil_div(kTargetWorkgroups, c->n_scopes)));
@@ -253,6 +277,14 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
       b.cnt = at<int32_t>(ws, d.bulk_cnt);
       b.hpart = at<uint32_t>(ws, d.bulk_hist);
       b.fpart = at<float>(ws, d.fpart);
+      b.key = c->m;
+      b.pos = c->pos;
+      b.flags = a.flags;
+      b.flags2 = evict_out;
+      b.list = a.list;
+      b.list2 = a.list2;
+      b.cap = c->capacity;
+      b.n_scopes = c->n_scopes;
       b.n_chunks = d.bulk_chunks;
       b.chunk = d.bulk_chunk;
       b.fold_splits = d.fold_splits;
@@ -279,17 +311,20 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
 // ------------------------------------------------------------ compact workspace
 struct CompactLayout {
   int merge_splits;
-  size_t holes, cos, slot, total;
+  size_t list, list2, cos, slot, total;
+  SelectLayout sel;
 };
 
 CompactLayout compact_layout(const kvc_cache *c) {
   CompactLayout l{};
   l.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
   size_t o = 0;
-  l.holes = o;    o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
+  l.list = o;     o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
+  l.list2 = o;    o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
   l.cos = o;      o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 8);
   l.slot = o;     o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 4);
-  l.total = o;
+  l.sel = select_layout(c->n_scopes, c->capacity, o);
+  l.total = l.sel.total;
   return l;
 }
 
@@ -320,9 +355,8 @@ size_t kvc_decode_workspace_size(const kvc_cache *cache, int32_t G, int32_t max_
 }
 
 size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity) {
-  (void)n_scopes;
-  (void)capacity;
-  return align_up(kvc::wide_state_bytes());
+  if (n_scopes <= 0 || capacity <= 0) return 0;
+  return std::max(align_up(kvc::wide_state_bytes()), select_layout(n_scopes, capacity).total);
 }
 
 size_t kvc_compact_workspace_size(const kvc_cache *cache) {
@@ -376,9 +410,28 @@ int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *le
   if (!key || !evict || n_scopes <= 0 || capacity <= 0) return KVC_ERR_ARG;
   if (budget < 0) return KVC_ERR_CAPACITY;
   if (!ws || ws_bytes < kvc_select_workspace_size(n_scopes, capacity)) return KVC_ERR_WORKSPACE;
-  if (kvc::launch_select(key, pos, len, n_scopes, capacity, budget, evict, n_evict, ws,
-                         static_cast<hipStream_t>(stream)) != hipSuccess)
-    return KVC_ERR_DEVICE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (n_scopes == 1 && len == nullptr && capacity > (1 << 20)) {   // one model-wide Top-K
+    if (kvc::launch_select_wide(key, pos, capacity, budget, evict, n_evict, ws, hs) != hipSuccess)
+      return KVC_ERR_DEVICE;
+    return KVC_OK;
+  }
+  const SelectLayout l = select_layout(n_scopes, capacity);
+  kvc::BulkArgs b{};
+  b.st = at<kvc::BulkScope>(ws, l.state);
+  b.hpart = at<uint32_t>(ws, l.hist);
+  b.cnt = at<int32_t>(ws, l.cnt);
+  b.key = key;
+  b.pos = pos;
+  b.flags = evict;
+  b.len = len;
+  b.n_evict = n_evict;
+  b.cap = capacity;
+  b.budget = budget;
+  b.n_scopes = n_scopes;
+  b.n_chunks = l.n_chunks;
+  b.chunk = l.chunk;
+  if (kvc::launch_bulk_select(b, hs) != hipSuccess) return KVC_ERR_DEVICE;
   return KVC_OK;
 }
 
@@ -387,9 +440,11 @@ int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kv
   int st = validate_cache(cache);
   if (st) return st;
   if (!evict || !mom || !mom->n || !mom->sk || !mom->sv || !mom->S) return KVC_ERR_ARG;
-  if (kvc::launch_moment_update(cache_args(cache), evict, mom->n, mom->sk, mom->sv, mom->S,
-                                static_cast<hipStream_t>(stream)) != hipSuccess)
-    return KVC_ERR_DEVICE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = cache->dtype == KVC_BF16
+                           ? kvc::launch_moment_update_mfma(cache_args(cache), evict, mom->n, mom->sk, mom->sv, mom->S, hs)
+                           : kvc::launch_moment_update(cache_args(cache), evict, mom->n, mom->sk, mom->sv, mom->S, hs);
+  if (e != hipSuccess) return KVC_ERR_DEVICE;
   return KVC_OK;
 }
 
@@ -430,8 +485,31 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
     if (kvc::launch_merge(cache_args(cache), evict, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;
     return KVC_OK;
   }
-  if (kvc::launch_compact(cache_args(cache), evict, at<int32_t>(ws, l.holes), hs) != hipSuccess)
-    return KVC_ERR_DEVICE;
+  kvc::StepArgs a{};
+  a.k = static_cast<char *>(cache->k);
+  a.v = static_cast<char *>(cache->v);
+  a.votes = cache->votes;
+  a.pos = cache->pos;
+  a.m = cache->m;
+  a.len = cache->len;
+  a.scope_stride = cache->scope_stride;
+  a.unit_stride = cache->unit_stride;
+  a.capacity = cache->capacity;
+  a.n_scopes = cache->n_scopes;
+  a.units = cache->units_per_scope;
+  kvc::BulkArgs b{};
+  b.st = at<kvc::BulkScope>(ws, l.sel.state);
+  b.cnt = at<int32_t>(ws, l.sel.cnt);
+  b.flags = const_cast<uint8_t *>(evict);   // read only on this path
+  b.list = at<int32_t>(ws, l.list);
+  b.list2 = at<int32_t>(ws, l.list2);
+  b.len = cache->len;
+  b.cap = cache->capacity;
+  b.n_scopes = cache->n_scopes;
+  b.n_chunks = l.sel.n_chunks;
+  b.chunk = l.sel.chunk;
+  b.move_blocks = std::max(1, std::min(64, ceil_div(kTargetWorkgroups, cache->n_scopes)));
+  if (kvc::launch_bulk_compact(a, b, cache->dtype, hs) != hipSuccess) return KVC_ERR_DEVICE;
   return KVC_OK;
 }
 

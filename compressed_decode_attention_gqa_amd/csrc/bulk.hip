@@ -21,6 +21,7 @@
 // takes its bin whole: slot i is evicted iff (key(i) & mask) <= prefix.
 #include "kvc_decode.h"
 #include "kvc_device.h"
+#include "kvc_kernels.h"
 
 namespace kvc {
 
@@ -29,24 +30,104 @@ namespace {
 constexpr int FOLD_NB = 16;                     // evicted rows staged per batch
 constexpr int PART_STRIDE = HD * HD + 2 * HD;   // floats per fold partial: S, s_k, s_v
 
-__device__ __forceinline__ uint64_t slot_key(const StepArgs &a, int64_t sc, int i) {
-  return order_key(a.m[sc + i], uint32_t(a.pos[sc + i]));
+__device__ __forceinline__ uint64_t slot_key(const BulkArgs &b, int64_t sc, int i) {
+  return order_key(b.key[sc + i], b.pos ? uint32_t(b.pos[sc + i]) : uint32_t(i));
+}
+
+// ------------------------------------------------------------ standalone set-up
+// Selection of the k = L - budget lowest keys of every scope (L = len or cap).
+__global__ __launch_bounds__(WG) void k_bulk_sel_init(const BulkArgs b) {
+  const int scope = blockIdx.x * WG + threadIdx.x;
+  if (scope >= b.n_scopes) return;
+  const int L = b.len ? min(b.len[scope], b.cap) : b.cap;
+  const int k = max(0, L - b.budget);
+  BulkScope &st = b.st[scope];
+  st.prefix = 0;
+  st.mask = 0;
+  st.krem = k;
+  st.done = k == 0 ? 1 : 0;
+  st.L = L;
+  st.k = k;
+  st.B = L - k;
+  st.n_pairs = 0;
+  st.run = 1;
+  if (b.n_evict) b.n_evict[scope] = k;
+}
+
+// Given evicted flags: the live length of every scope; k and B follow from the counts.
+__global__ __launch_bounds__(WG) void k_bulk_len_init(const BulkArgs b) {
+  const int scope = blockIdx.x * WG + threadIdx.x;
+  if (scope >= b.n_scopes) return;
+  BulkScope &st = b.st[scope];
+  st.L = b.len ? min(b.len[scope], b.cap) : b.cap;
+  st.k = 0;
+  st.B = st.L;
+  st.n_pairs = 0;
+  st.run = 1;
+}
+
+// Per chunk: flagged slots below L.
+__global__ __launch_bounds__(WG) void k_bulk_count(const BulkArgs b) {
+  __shared__ int red[8];
+  const int scope = blockIdx.y, tid = threadIdx.x;
+  const BulkScope &st = b.st[scope];
+  if (!st.run) return;
+  const int64_t sc = int64_t(scope) * b.cap;
+  const int i0 = blockIdx.x * b.chunk, i1 = min(st.L, i0 + b.chunk);
+  int n = 0;
+  for (int i = i0 + tid; i < i1; i += WG) n += b.flags[sc + i] ? 1 : 0;
+  int tot;
+  wg_exclusive_scan(n, red, &tot);
+  if (tid == 0) b.cnt[(int64_t(scope) * b.n_chunks + blockIdx.x) * 2] = tot;
+}
+
+// One workgroup per scope: k = sum of the chunk counts; B = L - k when the
+// evicted slots are to be removed (compact), L when they are only folded.
+__global__ __launch_bounds__(WG) void k_bulk_total(const BulkArgs b, const int compact) {
+  __shared__ int red[8];
+  const int scope = blockIdx.x, tid = threadIdx.x;
+  BulkScope &st = b.st[scope];
+  if (!st.run) return;
+  int n = 0;
+  for (int c = tid; c < b.n_chunks; c += WG) n += b.cnt[(int64_t(scope) * b.n_chunks + c) * 2];
+  int tot;
+  wg_exclusive_scan(n, red, &tot);
+  if (tid == 0) {
+    st.k = tot;
+    st.B = compact ? st.L - tot : st.L;
+    if (tot == 0) st.run = 0;
+  }
+}
+
+// Per chunk: survivors at or above B (they fill the holes below B).
+__global__ __launch_bounds__(WG) void k_bulk_movers(const BulkArgs b) {
+  __shared__ int red[8];
+  const int scope = blockIdx.y, tid = threadIdx.x;
+  const BulkScope &st = b.st[scope];
+  if (!st.run) return;
+  const int64_t sc = int64_t(scope) * b.cap;
+  const int i0 = max(st.B, int(blockIdx.x) * b.chunk), i1 = min(st.L, int(blockIdx.x) * b.chunk + b.chunk);
+  int n = 0;
+  for (int i = i0 + tid; i < i1; i += WG) n += b.flags[sc + i] ? 0 : 1;
+  int tot;
+  wg_exclusive_scan(n, red, &tot);
+  if (tid == 0) b.cnt[(int64_t(scope) * b.n_chunks + blockIdx.x) * 2 + 1] = tot;
 }
 
 // ------------------------------------------------------------ radix select pass
 // Each workgroup histograms the digit at `shift` of the keys of its chunk that
 // match the current prefix and stores the 256 counts (plain stores: no
 // device-scope atomics or fences); the pick kernel sums the chunks' counts.
-__global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkArgs b, const int shift) {
+__global__ __launch_bounds__(WG) void k_bulk_hist(const BulkArgs b, const int shift) {
   __shared__ uint32_t hist[256];
   const int scope = blockIdx.y, tid = threadIdx.x;
   const BulkScope &st = b.st[scope];
-  if (st.k <= 1 || st.done) return;     // the same for every workgroup of the scope
+  if (!st.run || st.done) return;     // the same for every workgroup of the scope
   const int L = st.L;
   const uint64_t prefix = st.prefix, mask = st.mask;
   hist[tid] = 0u;
   __syncthreads();
-  const int64_t sc = int64_t(scope) * a.capacity;
+  const int64_t sc = int64_t(scope) * b.cap;
   const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
   const int lane = tid & 63;
   for (int base = i0; base < i1; base += WG) {
@@ -54,7 +135,7 @@ __global__ __launch_bounds__(WG) void k_bulk_hist(const StepArgs a, const BulkAr
     uint32_t bin = 0;
     bool hit = false;
     if (i < i1) {
-      const uint64_t key = slot_key(a, sc, i);
+      const uint64_t key = slot_key(b, sc, i);
       hit = (key & mask) == prefix;
       bin = uint32_t(key >> shift) & 255u;
     }
@@ -82,7 +163,7 @@ __global__ __launch_bounds__(WG) void k_bulk_pick(const BulkArgs b, const int sh
   __shared__ int red[8];
   const int scope = blockIdx.x, tid = threadIdx.x;
   BulkScope &st = b.st[scope];
-  if (st.k <= 1 || st.done) return;
+  if (!st.run || st.done) return;
   const uint64_t prefix = st.prefix, mask = st.mask;
   const int krem = st.krem;
   const uint32_t *h = b.hpart + int64_t(scope) * b.n_chunks * 256;
@@ -99,20 +180,21 @@ __global__ __launch_bounds__(WG) void k_bulk_pick(const BulkArgs b, const int sh
 }
 
 // ------------------------------------------------------------ flags and chunk counts
-__global__ __launch_bounds__(WG) void k_bulk_flags(const StepArgs a, const BulkArgs b) {
+__global__ __launch_bounds__(WG) void k_bulk_flags(const BulkArgs b) {
   __shared__ int red[8];
   const int scope = blockIdx.y, tid = threadIdx.x;
   const BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
-  const int L = st.L, B = st.L - st.k;
+  if (!st.run) return;
+  const int L = st.L, B = st.B;
+  const bool any = st.k > 0;
   const uint64_t prefix = st.prefix, mask = st.mask;
-  const int64_t sc = int64_t(scope) * a.capacity;
+  const int64_t sc = int64_t(scope) * b.cap;
   const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
   int n_ev = 0, n_mv = 0;
   for (int i = i0 + tid; i < i1; i += WG) {
-    const bool ev = (slot_key(a, sc, i) & mask) <= prefix;
-    a.flags[sc + i] = ev ? 1 : 0;
-    if (a.evict_out) a.evict_out[sc + i] = ev ? 1 : 0;
+    const bool ev = any && (slot_key(b, sc, i) & mask) <= prefix;
+    if (b.flags) b.flags[sc + i] = ev ? 1 : 0;
+    if (b.flags2) b.flags2[sc + i] = ev ? 1 : 0;
     n_ev += ev ? 1 : 0;
     n_mv += (!ev && i >= B) ? 1 : 0;
   }
@@ -127,14 +209,14 @@ __global__ __launch_bounds__(WG) void k_bulk_flags(const StepArgs a, const BulkA
 }
 
 // ------------------------------------------------------------ evicted and mover lists
-// a.list: evicted slots ascending (k entries); a.list2: movers ascending.
-__global__ __launch_bounds__(WG) void k_bulk_lists(const StepArgs a, const BulkArgs b) {
+// b.list: evicted slots ascending (k entries); b.list2: movers (survivors at or above B) ascending.
+__global__ __launch_bounds__(WG) void k_bulk_lists(const BulkArgs b) {
   __shared__ int red[8];
   const int scope = blockIdx.y, tid = threadIdx.x;
   BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
-  const int L = st.L, B = st.L - st.k;
-  const int64_t sc = int64_t(scope) * a.capacity;
+  if (!st.run) return;
+  const int L = st.L, B = st.B;
+  const int64_t sc = int64_t(scope) * b.cap;
   // bases: counts of the chunks before this one (n_chunks <= 256)
   int pe = 0, pm = 0;
   if (tid < int(blockIdx.x)) {
@@ -149,12 +231,12 @@ __global__ __launch_bounds__(WG) void k_bulk_lists(const StepArgs a, const BulkA
   const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
   for (int base = i0; base < i1; base += WG) {
     const int i = base + tid;
-    const bool ev = i < i1 && a.flags[sc + i];
+    const bool ev = i < i1 && b.flags[sc + i];
     const bool mv = i < i1 && !ev && i >= B;
     int tot;
     const int r = wg_exclusive_scan((ev ? 1 : 0) | ((mv ? 1 : 0) << 16), red, &tot);
-    if (ev) a.list[sc + base_e + (r & 0xffff)] = i;
-    if (mv) a.list2[sc + base_m + (r >> 16)] = i;
+    if (ev) b.list[sc + base_e + (r & 0xffff)] = i;
+    if (mv) b.list2[sc + base_m + (r >> 16)] = i;
     base_e += tot & 0xffff;
     base_m += tot >> 16;
   }
@@ -226,7 +308,7 @@ __global__ __launch_bounds__(WG) void k_bulk_fold(const StepArgs a, const BulkAr
   const int tid = threadIdx.x;
   const int scope = blockIdx.y / a.units, u = blockIdx.y - scope * a.units;
   const BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
+  if (!st.run || st.k <= 0) return;
   const int k = st.k;
   const int per = (k + b.fold_splits - 1) / b.fold_splits;
   const int j0 = min(k, int(blockIdx.x) * per), j1 = min(k, j0 + per);
@@ -245,7 +327,7 @@ __global__ __launch_bounds__(WG) void k_bulk_fold(const StepArgs a, const BulkAr
 
   for (int w0 = j0; w0 < j1; w0 += WG) {
     const int nw = min(WG, j1 - w0);
-    if (tid < nw) sh.slots[tid] = a.list[sc + w0 + tid];
+    if (tid < nw) sh.slots[tid] = b.list[sc + w0 + tid];
     __syncthreads();
     const int nb = (nw + FOLD_NB - 1) / FOLD_NB;
     u32x4 rk[FS::NLD], rv[FS::NLD];
@@ -369,90 +451,82 @@ __device__ __forceinline__ bf16x8 mf_frag(const uint16_t (*m)[MF_RS], int g, int
   return __builtin_bit_cast(bf16x8, x);
 }
 
-__global__ __launch_bounds__(WG) void k_bulk_fold_mfma(const StepArgs a, const BulkArgs b) {
-  __shared__ MfmaFoldLds sh;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int scope = blockIdx.y / a.units, u = blockIdx.y - scope * a.units;
-  const BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
-  const int k = st.k;
-  const int per = (k + b.fold_splits - 1) / b.fold_splits;
-  const int j0 = min(k, int(blockIdx.x) * per), j1 = min(k, j0 + per);
-  const int64_t sc = int64_t(scope) * a.capacity;
-  const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride;
-  const char *Kb = a.k + row0 * (HD * 2);
-  const char *Vb = a.v + row0 * (HD * 2);
-  const int iq = wave >> 1, jq = wave & 1;
-  const int g = lane >> 4, l16 = lane & 15;
-
+// Accumulators of one workgroup's MFMA fold: wave w owns the 64 x 64 quadrant
+// of S at rows 64*(w/2), columns 64*(w%2) as 4 x 4 tiles; accv / acck collect
+// s_v / s_k.
+struct MfmaAcc {
   f32x4 acc[4][4], accv[4], acck[4];
+};
+
+__device__ __forceinline__ void mf_zero(MfmaAcc &f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    accv[i] = f32x4(0.f);
-    acck[i] = f32x4(0.f);
+    f.accv[i] = f32x4(0.f);
+    f.acck[i] = f32x4(0.f);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4(0.f);
+    for (int j = 0; j < 4; ++j) f.acc[i][j] = f32x4(0.f);
   }
+}
+
+// Fold the nw rows whose slots are in sh.slots[0, nw) (unit rows at Kb, Vb).
+__device__ __forceinline__ void mf_window(MfmaAcc &f, MfmaFoldLds &sh, const int nw, const char *Kb,
+                                          const char *Vb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int iq = wave >> 1, jq = wave & 1, g = lane >> 4, l16 = lane & 15;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u16x8(uint16_t(0x3f80)));
-
-  for (int w0 = j0; w0 < j1; w0 += MF_WIN) {
-    const int nw = min(MF_WIN, j1 - w0);
-    for (int e = tid; e < nw; e += WG) sh.slots[e] = a.list[sc + w0 + e];
+  const int nst = (nw + MF_ROWS - 1) / MF_ROWS;
+  // two stages of loads in flight: stage s is staged from register set s & 1,
+  // which then takes the loads of stage s + 2
+  u32x4 rk[2][2], rv[2][2];
+  // (loads past the last stage repeat it, so every step issues the same loads and
+  // the waits stay exact: stage s waits only for its own set)
+  auto load_stage = [&](int s, u32x4 (&qk)[2], u32x4 (&qv)[2]) {
+    s = min(s, nst - 1);
+    mf_load(qk, qv, Kb, Vb, sh.slots, s * MF_ROWS, min(MF_ROWS, nw - s * MF_ROWS));
+  };
+  load_stage(0, rk[0], rv[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_stage(1, rk[1], rv[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  auto step = [&](const int s, u32x4 (&qk)[2], u32x4 (&qv)[2]) {
+    const int buf = s & 1;
+    mf_stage(qk, qv, min(MF_ROWS, nw - s * MF_ROWS), sh.kr[buf], sh.vr[buf]);
     __syncthreads();
-    const int nst = (nw + MF_ROWS - 1) / MF_ROWS;
-    // two stages of loads in flight: stage s is staged from register set s & 1,
-    // which then takes the loads of stage s + 2
-    u32x4 rk[2][2], rv[2][2];
-    // (loads past the last stage repeat it, so every step issues the same loads and
-    // the waits stay exact: stage s waits only for its own set)
-    auto load_stage = [&](int s, u32x4 (&qk)[2], u32x4 (&qv)[2]) {
-      s = min(s, nst - 1);
-      mf_load(qk, qv, Kb, Vb, sh.slots, s * MF_ROWS, min(MF_ROWS, nw - s * MF_ROWS));
-    };
-    load_stage(0, rk[0], rv[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    load_stage(1, rk[1], rv[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    auto step = [&](const int s, u32x4 (&qk)[2], u32x4 (&qv)[2]) {
-      const int buf = s & 1;
-      mf_stage(qk, qv, min(MF_ROWS, nw - s * MF_ROWS), sh.kr[buf], sh.vr[buf]);
-      __syncthreads();
-      load_stage(s + 2, qk, qv);
-      __builtin_amdgcn_sched_barrier(0);   // keep the next loads ahead of this stage's MFMAs
-      bf16x8 af[4], bf[4];
+    load_stage(s + 2, qk, qv);
+    __builtin_amdgcn_sched_barrier(0);   // keep the next loads ahead of this stage's MFMAs
+    bf16x8 af[4], bf[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = mf_frag(sh.vr[buf], g, 64 * iq + 16 * t + l16);
-        bf[t] = mf_frag(sh.kr[buf], g, 64 * jq + 16 * t + l16);
-      }
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-        for (int tj = 0; tj < 4; ++tj)
-          acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bf[tj], acc[ti][tj], 0, 0, 0);
-      // (every wave forms both sums, branch-free; only one quadrant row / column stores them)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        accv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t], ones, accv[t], 0, 0, 0);
-        acck[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bf[t], acck[t], 0, 0, 0);
-      }
-    };
-    int s = 0;
-    for (; s + 1 < nst; s += 2) {   // straight-line body: the same loads pending on every trip
-      step(s, rk[0], rv[0]);
-      step(s + 1, rk[1], rv[1]);
+    for (int t = 0; t < 4; ++t) {
+      af[t] = mf_frag(sh.vr[buf], g, 64 * iq + 16 * t + l16);
+      bf[t] = mf_frag(sh.kr[buf], g, 64 * jq + 16 * t + l16);
     }
-    if (s < nst) step(s, rk[0], rv[0]);
-    __syncthreads();
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj)
+        f.acc[ti][tj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ti], bf[tj], f.acc[ti][tj], 0, 0, 0);
+    // (every wave forms both sums, branch-free; only one quadrant row / column stores them)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f.accv[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t], ones, f.accv[t], 0, 0, 0);
+      f.acck[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bf[t], f.acck[t], 0, 0, 0);
+    }
+  };
+  int s = 0;
+  for (; s + 1 < nst; s += 2) {   // straight-line body: the same loads pending on every trip
+    step(s, rk[0], rv[0]);
+    step(s + 1, rk[1], rv[1]);
   }
+  if (s < nst) step(s, rk[0], rv[0]);
+  __syncthreads();
+}
 
-  // D layout of a 16x16 tile: lane l holds rows 4(l/16)..+3, column l%16
-  const int64_t mu = blockIdx.y;
-  const bool direct = b.fold_splits == 1;
-  float *P = direct ? nullptr : b.fpart + (int64_t(blockIdx.y) * b.fold_splits + blockIdx.x) * PART_STRIDE;
-  float *S = direct ? a.mom_S + mu * HD * HD : P;
-  float *skd = direct ? a.mom_sk + mu * HD : P + HD * HD;
-  float *svd = direct ? a.mom_sv + mu * HD : P + HD * HD + HD;
+// Store (ADD false) or add (ADD true) the sums: S row-major, then s_k, s_v.
+// D layout of a 16x16 tile: lane l holds rows 4(l/16)..+3, column l%16.
+template <bool ADD>
+__device__ __forceinline__ void mf_commit(const MfmaAcc &f, float *S, float *skd, float *svd) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int iq = wave >> 1, jq = wave & 1, g = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -460,7 +534,7 @@ __global__ __launch_bounds__(WG) void k_bulk_fold_mfma(const StepArgs a, const B
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float *p = S + (64 * iq + 16 * ti + 4 * g + r) * HD + 64 * jq + 16 * tj + l16;
-        *p = direct ? *p + acc[ti][tj][r] : acc[ti][tj][r];
+        *p = ADD ? *p + f.acc[ti][tj][r] : f.acc[ti][tj][r];
       }
   if (jq == 0 && l16 == 0) {
 #pragma unroll
@@ -468,17 +542,90 @@ __global__ __launch_bounds__(WG) void k_bulk_fold_mfma(const StepArgs a, const B
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float *p = svd + 64 * iq + 16 * t + 4 * g + r;
-        *p = direct ? *p + accv[t][r] : accv[t][r];
+        *p = ADD ? *p + f.accv[t][r] : f.accv[t][r];
       }
   }
   if (iq == 0 && g == 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       float *p = skd + 64 * jq + 16 * t + l16;
-      *p = direct ? *p + acck[t][0] : acck[t][0];
+      *p = ADD ? *p + f.acck[t][0] : f.acck[t][0];
     }
   }
-  if (direct && tid == 0) a.mom_n[mu] += k;
+}
+
+// Workgroup f of a unit folds evicted-list entries [f*per, (f+1)*per).
+__global__ __launch_bounds__(WG, 2) void k_bulk_fold_mfma(const StepArgs a, const BulkArgs b) {
+  __shared__ MfmaFoldLds sh;
+  const int tid = threadIdx.x;
+  const int scope = blockIdx.y / a.units, u = blockIdx.y - scope * a.units;
+  const BulkScope &st = b.st[scope];
+  if (!st.run || st.k <= 0) return;
+  const int k = st.k;
+  const int per = (k + b.fold_splits - 1) / b.fold_splits;
+  const int j0 = min(k, int(blockIdx.x) * per), j1 = min(k, j0 + per);
+  const int64_t sc = int64_t(scope) * a.capacity;
+  const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride;
+  const char *Kb = a.k + row0 * (HD * 2);
+  const char *Vb = a.v + row0 * (HD * 2);
+  MfmaAcc f;
+  mf_zero(f);
+  for (int w0 = j0; w0 < j1; w0 += MF_WIN) {
+    const int nw = min(MF_WIN, j1 - w0);
+    for (int e = tid; e < nw; e += WG) sh.slots[e] = b.list[sc + w0 + e];
+    __syncthreads();
+    mf_window(f, sh, nw, Kb, Vb);
+  }
+  const int64_t mu = blockIdx.y;
+  if (b.fold_splits == 1) {
+    mf_commit<true>(f, a.mom_S + mu * HD * HD, a.mom_sk + mu * HD, a.mom_sv + mu * HD);
+    if (tid == 0) a.mom_n[mu] += k;
+  } else {
+    float *P = b.fpart + (int64_t(blockIdx.y) * b.fold_splits + blockIdx.x) * PART_STRIDE;
+    mf_commit<false>(f, P, P + HD * HD, P + HD * HD + HD);
+  }
+}
+
+// kvc_moment_update on bf16 caches: one workgroup per unit folds every flagged
+// slot below the scope's length, the slots gathered window by window from the
+// flags (no workspace).
+__global__ __launch_bounds__(WG, 2) void k_moment_update_mfma(const CacheArgs c, const uint8_t *evict, int32_t *n,
+                                                          float *sk, float *sv, float *S) {
+  __shared__ MfmaFoldLds sh;
+  __shared__ int red[8];
+  const int tid = threadIdx.x;
+  const int scope = blockIdx.x / c.units, u = blockIdx.x - scope * c.units;
+  const int L = min(c.len[scope], c.capacity);
+  const uint8_t *fl = evict + int64_t(scope) * c.capacity;
+  const int64_t row0 = int64_t(scope) * c.scope_stride + int64_t(u) * c.unit_stride;
+  const char *Kb = c.k + row0 * (HD * 2);
+  const char *Vb = c.v + row0 * (HD * 2);
+  constexpr int PER = MF_WIN / WG;   // slots a thread examines per window
+  MfmaAcc f;
+  mf_zero(f);
+  int total = 0;
+  for (int w0 = 0; w0 < L; w0 += MF_WIN) {
+    bool hit[PER];
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int i = w0 + tid * PER + r;
+      hit[r] = i < L && fl[i];
+      cnt += hit[r] ? 1 : 0;
+    }
+    int nw;
+    int at = wg_exclusive_scan(cnt, red, &nw);
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+      if (hit[r]) sh.slots[at++] = w0 + tid * PER + r;
+    __syncthreads();
+    if (nw > 0) mf_window(f, sh, nw, Kb, Vb);
+    total += nw;
+  }
+  if (total == 0) return;
+  const int64_t mu = blockIdx.x;
+  mf_commit<true>(f, S + mu * HD * HD, sk + mu * HD, sv + mu * HD);
+  if (tid == 0) n[mu] += total;
 }
 
 // Sum of a unit's fold partials in split order, added to its moment sums.
@@ -486,7 +633,7 @@ __global__ __launch_bounds__(WG) void k_bulk_fold_reduce(const StepArgs a, const
   const int tid = threadIdx.x;
   const int scope = blockIdx.x / a.units;
   const BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
+  if (!st.run || st.k <= 0) return;
   const int64_t mu = blockIdx.x;
   const float *P = b.fpart + mu * b.fold_splits * PART_STRIDE;
   constexpr int N4 = PART_STRIDE / 4;
@@ -519,7 +666,7 @@ __global__ __launch_bounds__(WG) void k_bulk_fold_reduce(const StepArgs a, const
 __global__ __launch_bounds__(WG) void k_bulk_move(const StepArgs a, const BulkArgs b, const int row_bytes) {
   const int scope = blockIdx.y, tid = threadIdx.x;
   const BulkScope &st = b.st[scope];
-  if (st.k <= 1) return;
+  if (!st.run) return;
   const int np = st.n_pairs;
   const int64_t sc = int64_t(scope) * a.capacity;
   const int cpr = row_bytes / 16;
@@ -531,30 +678,35 @@ __global__ __launch_bounds__(WG) void k_bulk_move(const StepArgs a, const BulkAr
     rest >>= 1;
     const int u = int(rest % a.units);
     const int j = int(rest / a.units);
-    const int src = a.list2[sc + j], dst = a.list[sc + j];
+    const int src = b.list2[sc + j], dst = b.list[sc + j];
     char *base = (kv ? a.v : a.k) + (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride) * row_bytes;
     st16(base + int64_t(dst) * row_bytes + 16 * c, ld16(base + int64_t(src) * row_bytes + 16 * c));
   }
   for (int j = blockIdx.x * WG + tid; j < np; j += gridDim.x * WG) {
-    const int src = a.list2[sc + j], dst = a.list[sc + j];
+    const int src = b.list2[sc + j], dst = b.list[sc + j];
     if (a.votes) a.votes[sc + dst] = a.votes[sc + src];
     a.pos[sc + dst] = a.pos[sc + src];
-    a.m[sc + dst] = a.m[sc + src];
+    if (a.m) a.m[sc + dst] = a.m[sc + src];
   }
   if (blockIdx.x == 0 && tid == 0) a.len[scope] = st.L - st.k;
 }
 
 }  // namespace
 
+static void launch_radix(const BulkArgs &b, hipStream_t st) {
+  const dim3 chunks(b.n_chunks, b.n_scopes);
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, b, shift);
+    hipLaunchKernelGGL(k_bulk_pick, dim3(b.n_scopes), dim3(WG), 0, st, b, shift);
+  }
+  hipLaunchKernelGGL(k_bulk_flags, chunks, dim3(WG), 0, st, b);
+}
+
 hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st) {
   const dim3 chunks(b.n_chunks, a.n_scopes);
   const int row_bytes = HD * (dtype == 0 ? 2 : 4);
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, a, b, shift);
-    hipLaunchKernelGGL(k_bulk_pick, dim3(a.n_scopes), dim3(WG), 0, st, b, shift);
-  }
-  hipLaunchKernelGGL(k_bulk_flags, chunks, dim3(WG), 0, st, a, b);
-  hipLaunchKernelGGL(k_bulk_lists, chunks, dim3(WG), 0, st, a, b);
+  launch_radix(b, st);
+  hipLaunchKernelGGL(k_bulk_lists, chunks, dim3(WG), 0, st, b);
   if (a.mom_S) {
     const dim3 fg(b.fold_splits, a.n_scopes * a.units);
     if (dtype == 0) hipLaunchKernelGGL(k_bulk_fold_mfma, fg, dim3(WG), 0, st, a, b);
@@ -563,6 +715,32 @@ hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStrea
       hipLaunchKernelGGL(k_bulk_fold_reduce, dim3(a.n_scopes * a.units, 4), dim3(WG), 0, st, a, b);
   }
   hipLaunchKernelGGL(k_bulk_move, dim3(b.move_blocks, a.n_scopes), dim3(WG), 0, st, a, b, row_bytes);
+  return hipGetLastError();
+}
+
+// kvc_select_evict over many scopes: the radix select above for every scope.
+hipError_t launch_bulk_select(const BulkArgs &b, hipStream_t st) {
+  hipLaunchKernelGGL(k_bulk_sel_init, dim3((b.n_scopes + WG - 1) / WG), dim3(WG), 0, st, b);
+  launch_radix(b, st);
+  return hipGetLastError();
+}
+
+// kvc_compact (drop) from given flags: counts, lists and moves over the grid.
+hipError_t launch_bulk_compact(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st) {
+  const dim3 chunks(b.n_chunks, b.n_scopes);
+  hipLaunchKernelGGL(k_bulk_len_init, dim3((b.n_scopes + WG - 1) / WG), dim3(WG), 0, st, b);
+  hipLaunchKernelGGL(k_bulk_count, chunks, dim3(WG), 0, st, b);
+  hipLaunchKernelGGL(k_bulk_total, dim3(b.n_scopes), dim3(WG), 0, st, b, 1);
+  hipLaunchKernelGGL(k_bulk_movers, chunks, dim3(WG), 0, st, b);
+  hipLaunchKernelGGL(k_bulk_lists, chunks, dim3(WG), 0, st, b);
+  hipLaunchKernelGGL(k_bulk_move, dim3(b.move_blocks, b.n_scopes), dim3(WG), 0, st, a, b, HD * (dtype == 0 ? 2 : 4));
+  return hipGetLastError();
+}
+
+// kvc_moment_update on bf16 caches: one workgroup per unit on MFMA.
+hipError_t launch_moment_update_mfma(const CacheArgs &c, const uint8_t *evict, int32_t *n, float *sk, float *sv,
+                                     float *S, hipStream_t st) {
+  hipLaunchKernelGGL(k_moment_update_mfma, dim3(c.n_scopes * c.units), dim3(WG), 0, st, c, evict, n, sk, sv, S);
   return hipGetLastError();
 }
 

@@ -13,17 +13,26 @@ struct BulkScope {
   uint64_t prefix, mask;   // cut: a slot is evicted iff (key & mask) <= prefix once done
   int32_t krem;            // rank of the k-th smallest key inside the current bin
   int32_t done;            // the cut is final
-  int32_t L, k;            // live length before eviction, evicted count (k <= 1: not bulk)
+  int32_t L, k;            // live length before eviction, evicted count
+  int32_t B;               // survivors at or above B move into the evicted slots below it
   int32_t n_pairs;         // hole-filling moves
+  int32_t run;             // the grid-wide kernels act on this scope
   int32_t pad;
 };
 
 struct BulkArgs {
   BulkScope *st;           // [n_scopes]
   uint32_t *hpart;         // [n_scopes][n_chunks][256] radix histogram of each chunk (current pass)
-  int32_t *cnt;            // [n_scopes][n_chunks][2]: evicted slots, movers (survivors >= L - k)
+  int32_t *cnt;            // [n_scopes][n_chunks][2]: evicted slots, movers
   float *fpart;            // [n_scopes * units][fold_splits][HD*HD + 2*HD] fold partials (fold_splits > 1)
-  int32_t n_chunks, chunk; // slot chunks of the histogram, flag and list kernels
+  const float *key;        // selection keys [n_scopes][cap] and positions (null: the slot index)
+  const int32_t *pos;
+  uint8_t *flags, *flags2; // [n_scopes][cap] evicted flags (selection writes both, if non-null)
+  int32_t *list, *list2;   // [n_scopes][cap]: evicted slots ascending; movers ascending
+  const int32_t *len;      // live lengths for the standalone paths (null: cap)
+  int32_t *n_evict;        // [n_scopes] or null
+  int32_t cap, budget, n_scopes;
+  int32_t n_chunks, chunk; // slot chunks of the histogram, flag, count and list kernels
   int32_t fold_splits;     // workgroups folding one unit's evicted rows
   int32_t move_blocks;     // workgroups moving one scope's rows
 };
@@ -78,5 +87,9 @@ size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes);
 // epilogue handed over (BulkScope::k > 1).
 hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st);
 size_t bulk_part_floats();   // floats of one fold partial
+// Standalone entry points on the same grid-wide kernels (BulkArgs: key/pos,
+// flags, lists, len, budget, n_evict and the chunking filled by the caller).
+hipError_t launch_bulk_select(const BulkArgs &b, hipStream_t st);
+hipError_t launch_bulk_compact(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st);
 
 }  // namespace kvc

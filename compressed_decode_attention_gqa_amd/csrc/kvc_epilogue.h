@@ -240,7 +240,7 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
   if (L > cap) {
     if (tid == 0) {
       a.status[0] = -4;
-      if (a.bulk) a.bulk[scope].k = 0;
+      if (a.bulk) a.bulk[scope].run = 0;
     }
     return;
   }
@@ -257,11 +257,13 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
         b.done = 0;
         b.L = L;
         b.k = k;
+        b.B = L - k;
         b.n_pairs = 0;
+        b.run = 1;
       }
       return;
     }
-    if (tid == 0) a.bulk[scope].k = 0;
+    if (tid == 0) a.bulk[scope].run = 0;
   }
   if (!step) {
     if (tid == 0) a.len[scope] = L;

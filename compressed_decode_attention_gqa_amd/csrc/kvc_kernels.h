@@ -33,12 +33,13 @@ struct MomentArgs {
 };
 
 size_t wide_state_bytes();
-hipError_t launch_select(const float *key, const int32_t *pos, const int32_t *len, int n_scopes,
-                         int cap, int budget, uint8_t *evict, int32_t *n_evict, void *ws,
-                         hipStream_t st);
+// One scope of more than 2^20 keys (len = NULL): a device-wide radix select.
+hipError_t launch_select_wide(const float *key, const int32_t *pos, int cap, int budget, uint8_t *evict,
+                              int32_t *n_evict, void *ws, hipStream_t st);
 hipError_t launch_moment_update(const CacheArgs &c, const uint8_t *evict, int32_t *n, float *sk,
                                 float *sv, float *S, hipStream_t st);
-hipError_t launch_compact(const CacheArgs &c, const uint8_t *evict, int32_t *holes, hipStream_t st);
+hipError_t launch_moment_update_mfma(const CacheArgs &c, const uint8_t *evict, int32_t *n, float *sk, float *sv,
+                                     float *S, hipStream_t st);
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st);
 hipError_t launch_moment_correct(const MomentArgs &m, int n_units, const void *q, int dtype, int G, double scale,
                                  const float *f_R, const float *lse_R, float *out, hipStream_t st);

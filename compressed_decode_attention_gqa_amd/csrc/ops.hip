@@ -1,5 +1,7 @@
-// Standalone entry-point kernels: utility update, selection (per scope and
-// device-wide), moment fold, compaction and KeepKV ZIP merging.
+// Standalone entry-point kernels: utility update, the selection of one very
+// large scope (a model-wide Top-K), the fp32 moment fold and KeepKV ZIP
+// merging. (Selection and compaction over many scopes, and the bf16 moment
+// fold, run on the grid-wide kernels of bulk.hip.)
 #include "kvc_ops.h"
 #include "kvc_kernels.h"
 
@@ -20,39 +22,6 @@ __global__ __launch_bounds__(WG) void k_ema_update(float *m, const float *s, con
   else if (rule == 1) r = mo + sv;
   else r = al * mo + (1.0 - al) * sv;
   m[o] = float(r);
-}
-
-// ------------------------------------------------------------ selection (one workgroup per scope)
-__global__ __launch_bounds__(WG) void k_select(const float *key, const int32_t *pos,
-                                              const int32_t *len, int cap, int budget,
-                                              uint8_t *evict, int32_t *n_evict) {
-  __shared__ SelectLds sh;
-  const int scope = blockIdx.x, tid = threadIdx.x;
-  const int64_t so = int64_t(scope) * cap;
-  const int n = len ? min(len[scope], cap) : cap;
-  const int k = max(0, n - budget);
-  const float *kk = key + so;
-  const int32_t *pp = pos ? pos + so : nullptr;
-  auto kf = [&](int i) -> uint64_t { return order_key(kk[i], pp ? uint32_t(pp[i]) : uint32_t(i)); };
-  if (k == 0) {
-    for (int i = tid; i < n; i += WG) evict[so + i] = 0;
-  } else if (k == 1) {
-    uint64_t best = ~0ull;
-    int slot = 0x7fffffff;
-    for (int i = tid; i < n; i += WG) {
-      const uint64_t x = kf(i);
-      if (x < best) {
-        best = x;
-        slot = i;
-      }
-    }
-    const int e = wg_argmin_finish(best, slot, sh);
-    for (int i = tid; i < n; i += WG) evict[so + i] = (i == e);
-  } else {
-    const SelectCut cut = wg_select_cut(kf, n, k, sh);
-    wg_apply_cut(kf, n, cut, evict + so, nullptr, nullptr, sh);
-  }
-  if (tid == 0 && n_evict) n_evict[scope] = k;
 }
 
 // ------------------------------------------------------------ selection (device-wide, one scope)
@@ -129,26 +98,21 @@ __global__ void k_wide_clear(int64_t n, uint8_t *evict) {
 
 size_t wide_state_bytes() { return sizeof(WideState); }
 
-hipError_t launch_select(const float *key, const int32_t *pos, const int32_t *len, int n_scopes,
-                         int cap, int budget, uint8_t *evict, int32_t *n_evict, void *ws,
-                         hipStream_t st) {
-  if (n_scopes == 1 && len == nullptr && cap > (1 << 20)) {
-    WideState *w = reinterpret_cast<WideState *>(ws);
-    const int k = max(0, cap - budget);
-    const int grid = 2048;
-    hipLaunchKernelGGL(k_wide_init, dim3(1), dim3(256), 0, st, w, k, n_evict);
-    if (k == 0) {
-      hipLaunchKernelGGL(k_wide_clear, dim3(grid), dim3(WG), 0, st, int64_t(cap), evict);
-      return hipGetLastError();
-    }
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hipLaunchKernelGGL(k_wide_hist, dim3(grid), dim3(WG), 0, st, key, pos, int64_t(cap), w, shift);
-      hipLaunchKernelGGL(k_wide_pick, dim3(1), dim3(WG), 0, st, w, shift);
-    }
-    hipLaunchKernelGGL(k_wide_flags, dim3(grid), dim3(WG), 0, st, key, pos, int64_t(cap), w, evict);
+hipError_t launch_select_wide(const float *key, const int32_t *pos, int cap, int budget, uint8_t *evict,
+                              int32_t *n_evict, void *ws, hipStream_t st) {
+  WideState *w = reinterpret_cast<WideState *>(ws);
+  const int k = max(0, cap - budget);
+  const int grid = 2048;
+  hipLaunchKernelGGL(k_wide_init, dim3(1), dim3(256), 0, st, w, k, n_evict);
+  if (k == 0) {
+    hipLaunchKernelGGL(k_wide_clear, dim3(grid), dim3(WG), 0, st, int64_t(cap), evict);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_select, dim3(n_scopes), dim3(WG), 0, st, key, pos, len, cap, budget, evict, n_evict);
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(k_wide_hist, dim3(grid), dim3(WG), 0, st, key, pos, int64_t(cap), w, shift);
+    hipLaunchKernelGGL(k_wide_pick, dim3(1), dim3(WG), 0, st, w, shift);
+  }
+  hipLaunchKernelGGL(k_wide_flags, dim3(grid), dim3(WG), 0, st, key, pos, int64_t(cap), w, evict);
   return hipGetLastError();
 }
 
@@ -172,31 +136,6 @@ hipError_t launch_moment_update(const CacheArgs &c, const uint8_t *evict, int32_
   dim3 grid(c.n_scopes * c.units);
   if (c.dtype == 0) hipLaunchKernelGGL(k_moment_update<bf16_t>, grid, dim3(WG), 0, st, c, evict, n, sk, sv, S);
   else hipLaunchKernelGGL(k_moment_update<float>, grid, dim3(WG), 0, st, c, evict, n, sk, sv, S);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ compaction (drop)
-__global__ __launch_bounds__(WG) void k_compact(CacheArgs c, const uint8_t *evict, int32_t *holes) {
-  __shared__ int red[8];
-  const int scope = blockIdx.x, tid = threadIdx.x;
-  const int64_t so = int64_t(scope) * c.capacity;
-  const int L = c.len[scope];
-  int k = 0;
-  for (int base = 0; base < L; base += WG) {
-    const int i = base + tid;
-    int tot;
-    wg_exclusive_scan((i < L && evict[so + i]) ? 1 : 0, red, &tot);
-    k += tot;
-  }
-  if (k == 0) return;
-  ScopeRows rows{c.k, c.v, int64_t(scope) * c.scope_stride, c.unit_stride, c.units,
-                 HD * (c.dtype == 0 ? 2 : 4), c.votes ? c.votes + so : nullptr, c.pos + so, c.m ? c.m + so : nullptr};
-  wg_compact_flags(rows, evict + so, L, k, holes + so, red);
-  if (tid == 0) c.len[scope] = L - k;
-}
-
-hipError_t launch_compact(const CacheArgs &c, const uint8_t *evict, int32_t *holes, hipStream_t st) {
-  hipLaunchKernelGGL(k_compact, dim3(c.n_scopes), dim3(WG), 0, st, c, evict, holes);
   return hipGetLastError();
 }
 

@@ -350,10 +350,12 @@ def test_decode_step_c3_model_scope_reduced(lazy):
 
 
 # ---------------------------------------------------------------- the entry points composed
-def test_entry_points_compose_to_the_step():
+@pytest.mark.parametrize("context,budget,steps,n_kv", [(900, 90, 4, 5), (32768, 3276, 2, 8)])
+def test_entry_points_compose_to_the_step(context, budget, steps, n_kv):
     """attn_score -> ema_update -> select_evict -> moment_update -> compact equals the oracle's
-    step (and the fused step's checks)."""
-    wl = C2.scaled(context=900, budget=90, steps=4, n_kv=5, moments=True)
+    step (and the fused step's checks); the second case is one full Llama-3.1-8B layer, whose
+    first step evicts 29493 entries per head through the standalone calls."""
+    wl = C2.scaled(context=context, budget=budget, steps=steps, n_kv=n_kv, moments=True)
     run = DeviceRun(wl)
     sel_ws = kvc.workspace(kvc.kvc_select_workspace_size(wl.n_scopes, run.cache.capacity))
     cmp_ws = kvc.workspace(kvc.kvc_compact_workspace_size(run.cache))
