@@ -9,8 +9,9 @@ only in the seeded inputs of synth/.
 Every function writes out the definition it follows and cites the page, and
 the section or equation on it, that gives that definition:
 
-  * MomentKV (papercache.org summary, arXiv 2606.01563) -- moment statistics
-    and the normalisation-corrected output (Algorithm 1, phase 2).
+  * MomentKV (papercache.org summary, arXiv 2606.01563) -- moment statistics,
+    moment-informed eviction (§4.2, Algorithm 1 phase 1) and the
+    normalisation-corrected output (Algorithm 1, phase 2).
   * InertiaKV (translated article, arXiv 2609.03515) -- head-averaged
     last-query score and single / cumulative / EMA utility.
   * KeepKV (reading notes, arXiv 2504.09936) -- vote-weighted attention and
@@ -27,6 +28,7 @@ Pins (tests/test_oracle_*.py) tie each function to something other than
 itself: textbook attention, duplicated-token brute force, the eviction
 identity o' = (o - A_e v_e)/(1 - A_e), the retained/evicted split, EMA closed
 forms, exhaustive subset enumeration, the centred-covariance identity, the
+moment model's exactness on affine values under an isotropic evicted set, the
 ZIP lossless property and the pages' worked numbers.
 
 Parity unpinned (these follow from readings of the pages, not from printed
@@ -40,6 +42,7 @@ from .utility import SINGLE, CUMULATIVE, EMA, RULES, update_utility  # noqa: F40
 from .selection import bottom_k, bottom_k_one_at_a_time, top_k_keep  # noqa: F401
 from .moments import fold_moments, centred_moments, empty_moments  # noqa: F401
 from .moment_correct import corrected_output, evicted_estimates  # noqa: F401
+from .moment_evict import moment_residuals, moment_scores, moment_informed_evict  # noqa: F401
 from .compaction import compact  # noqa: F401
 from .zip_merge import cosine_partner, zip_merge  # noqa: F401
 from .decode_step import ScopeState, StepParams, decode_step  # noqa: F401
