@@ -297,6 +297,78 @@ def run_moment_correct(args):
     print(json.dumps(result), flush=True)
 
 
+def run_moment_evict(args):
+    """MomentKV moment-informed eviction at the decode steady state: every KV head holds
+    budget + 1 tokens and evicts the one of lowest alpha ||r|| against the moment model, then
+    folds it into its sums (kvc_moment_evict: score kernel + pick/fold kernel). Inputs resident
+    in HBM; the sums keep growing by one token per repetition, which leaves the work unchanged."""
+    import oracle
+    from oracle.moment_evict import moment_scores
+    name = args.workload if args.workload.startswith("m1_") else "m1_momentkv_llama8b_32layers_b1024"
+    wl = synth.WORKLOADS[name]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S, d, B = wl.n_scopes, wl.d, wl.budget
+    L = B + 1
+    scales = synth.key_scales(S, d, wl.seed, dev) if wl.key_scales else None
+    K, V = synth.kv_rows(S, L, d, wl.dtype, wl.seed, dev, scales)
+    pos = torch.arange(L, dtype=torch.int32, device=dev).repeat(S, 1).contiguous()
+    cache = kvc.Cache(k=K.view(S, 1, L, d).contiguous(), v=V.view(S, 1, L, d).contiguous(), pos=pos,
+                      m=torch.zeros((S, L), device=dev), length=torch.full((S,), L, dtype=torch.int32, device=dev))
+    n_e = wl.context - B
+    ms = synth.moment_sums(S, d, n_e, wl.seed, dev)
+    mom = kvc.Moments(ms["n"].view(S, 1).contiguous(), ms["sk"].view(S, 1, d).contiguous(),
+                      ms["sv"].view(S, 1, d).contiguous(), ms["S"].view(S, 1, d, d).contiguous())
+    alpha = synth.token_weights(S, L, wl.seed, dev)
+    evict = torch.zeros((S, L), dtype=torch.uint8, device=dev)
+    ws = kvc.workspace(kvc.kvc_moment_evict_workspace_size(cache), dev)
+    scale = float(np.float32(1 / np.sqrt(d)))
+
+    def call():
+        kvc.kvc_moment_evict(cache, mom, alpha, scale, B, evict, max_len=L, ws=ws)
+
+    for _ in range(args.warmup):
+        call()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    flops = rf.moment_evict_flops(S, L, d)
+    achieved = flops / (ms_step / 1e3) / 1e12
+    result = {"metric": "MomentKV moment-scored tokens/sec (live tokens scored, one eviction per head)",
+              "value": S * L / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+              "config": {"workload": wl.name + " steady eviction", "heads": S, "live_tokens_per_head": L,
+                         "budget": B, "n_e": n_e, "cache": wl.dtype},
+              "roofline": {"bound": "mfma", "achieved": achieved, "peak": rf.MI355X_FP64_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / rf.MI355X_FP64_TFLOPS, "traffic": None, "launch_ms": ms_step,
+                           "flops_per_launch": flops}}
+    if not args.no_cpu_baseline:
+        Kh = oracle.to_f64(K.view(torch.int16).cpu().numpy().view(np.uint16), wl.dtype) if wl.dtype == "bf16" \
+            else K.cpu().double().numpy()
+        Vh = oracle.to_f64(V.view(torch.int16).cpu().numpy().view(np.uint16), wl.dtype) if wl.dtype == "bf16" \
+            else V.cpu().double().numpy()
+        ah = alpha.cpu().double().numpy()
+        mh = {k: v.cpu().double().numpy() for k, v in ms.items()}
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            sc = done % S
+            moment_scores(Kh[sc], Vh[sc], ah[sc], {"n": n_e, "sk": mh["sk"][sc], "sv": mh["sv"][sc],
+                                                   "S": mh["S"][sc]}, scale)
+            done += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": done * L / dt, "unit": "tokens/s", "cores": torch.get_num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{done} heads of {wl.name} (L={L}) scored in {dt:.1f} s, numpy float64"}
+    print(json.dumps(result), flush=True)
+
+
 def run_first_step(args):
     """The first decode step after prefill: attend and score over the whole context, then
     compress every KV head to its budget (k = context + 1 - budget evictions per head: select,
@@ -389,7 +461,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct"],
+    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict"],
                     help="step: the fused decode step (default); first_step: the bulk compression step "
                          "after prefill; moment_correct: MomentKV's corrected output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -401,6 +473,8 @@ def main():
               "MI355X; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.op == "moment_evict":
+        return run_moment_evict(args)
     if args.op == "moment_correct":
         run_moment_correct(args)
         return

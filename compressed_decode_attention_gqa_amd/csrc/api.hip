@@ -328,6 +328,28 @@ CompactLayout compact_layout(const kvc_cache *c) {
   return l;
 }
 
+// ------------------------------------------------------- moment-informed eviction
+// Candidates per (scope, chunk of at least kMomentTile tokens), after the status word.
+constexpr int kMomentTile = 64;
+constexpr int kMomentWorkgroups = 256;   // one 128 KB-LDS workgroup per CU
+
+struct MomentEvictLayout {
+  size_t status, score, pos, slot, total;
+  int n_chunks;
+};
+
+MomentEvictLayout moment_evict_layout(int n_scopes, int cap) {
+  MomentEvictLayout l{};
+  l.n_chunks = ceil_div(cap, kMomentTile);
+  size_t o = 0;
+  l.status = o; o = align_up(o + 256);
+  l.score = o;  o = align_up(o + size_t(n_scopes) * l.n_chunks * 8);
+  l.pos = o;    o = align_up(o + size_t(n_scopes) * l.n_chunks * 4);
+  l.slot = o;   o = align_up(o + size_t(n_scopes) * l.n_chunks * 4);
+  l.total = o;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -458,6 +480,58 @@ int32_t kvc_moment_correct(const kvc_moments *mom, int32_t n_units, const void *
   kvc::MomentArgs m{mom->n, mom->sk, mom->sv, mom->S};
   if (kvc::launch_moment_correct(m, n_units, q, dtype, G, double(scale), f_R, lse_R, out,
                                  static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+size_t kvc_moment_evict_workspace_size(const kvc_cache *cache) {
+  if (validate_cache(cache)) return 0;
+  return moment_evict_layout(cache->n_scopes, cache->capacity).total;
+}
+
+int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const float *alpha, float scale,
+                         int32_t budget, int32_t max_len, uint8_t *evict, int32_t *order, float *score_out,
+                         int32_t *n_evict, void *ws, size_t ws_bytes, void *stream) {
+  int st = validate_cache(cache);
+  if (st) return st;
+  if (cache->units_per_scope != 1) return KVC_ERR_UNSUPPORTED;
+  if (!mom || !mom->n || !mom->sk || !mom->sv || !mom->S || !alpha || !evict || !ws) return KVC_ERR_ARG;
+  if (!aligned16(mom->S)) return KVC_ERR_ALIGN;
+  if (budget < 0 || max_len > cache->capacity) return KVC_ERR_CAPACITY;
+  const MomentEvictLayout l = moment_evict_layout(cache->n_scopes, cache->capacity);
+  if (ws_bytes < l.total) return KVC_ERR_WORKSPACE;
+  const int ml = max_len > 0 ? max_len : cache->capacity;
+  kvc::MomentEvictArgs p{};
+  p.k = static_cast<const char *>(cache->k);
+  p.v = static_cast<const char *>(cache->v);
+  p.scope_stride = cache->scope_stride;
+  p.pos = cache->pos;
+  p.len = cache->len;
+  p.mom_n = mom->n;
+  p.sk = mom->sk;
+  p.sv = mom->sv;
+  p.S = mom->S;
+  p.alpha = alpha;
+  p.scale = double(scale);
+  p.capacity = cache->capacity;
+  p.n_scopes = cache->n_scopes;
+  p.budget = budget;
+  p.rounds = std::max(1, ml - budget);
+  // chunks of whole 64-token tiles, about kMomentWorkgroups workgroups over the scopes
+  const int tiles = ceil_div(ml, kMomentTile);
+  const int per_scope = std::max(1, std::min(tiles, ceil_div(kMomentWorkgroups, cache->n_scopes)));
+  p.chunk = kMomentTile * ceil_div(tiles, per_scope);
+  p.n_chunks = l.n_chunks;
+  p.n_chunks_used = ceil_div(cache->capacity, p.chunk);   // chunks past a scope's live length exit at once
+  p.evict = evict;
+  p.order = order;
+  p.n_evict = n_evict;
+  p.score_out = score_out;
+  p.cand_score = at<double>(ws, l.score);
+  p.cand_pos = at<int32_t>(ws, l.pos);
+  p.cand_slot = at<int32_t>(ws, l.slot);
+  p.status = at<int32_t>(ws, l.status);
+  if (kvc::launch_moment_evict(p, cache->dtype, p.rounds, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KVC_ERR_DEVICE;
   return KVC_OK;
 }

@@ -32,6 +32,27 @@ struct MomentArgs {
   const float *sk, *sv, *S;
 };
 
+// MomentKV moment-informed eviction on per-KV-head scopes (one unit per scope).
+struct MomentEvictArgs {
+  const char *k, *v;
+  int64_t scope_stride;
+  const int32_t *pos, *len;
+  int32_t *mom_n;
+  float *sk, *sv, *S;
+  const float *alpha;
+  double scale;
+  int32_t capacity, n_scopes, budget, rounds;
+  int32_t n_chunks;         // candidate stride per scope
+  int32_t n_chunks_used;    // chunks launched per scope
+  int32_t chunk;            // tokens per chunk (a multiple of 64)
+  uint8_t *evict;
+  int32_t *order, *n_evict;
+  float *score_out;
+  double *cand_score;
+  int32_t *cand_pos, *cand_slot;
+  int32_t *status;
+};
+
 size_t wide_state_bytes();
 // One scope of more than 2^20 keys (len = NULL): a device-wide radix select.
 hipError_t launch_select_wide(const float *key, const int32_t *pos, int cap, int budget, uint8_t *evict,
@@ -43,6 +64,7 @@ hipError_t launch_moment_update_mfma(const CacheArgs &c, const uint8_t *evict, i
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st);
 hipError_t launch_moment_correct(const MomentArgs &m, int n_units, const void *q, int dtype, int G, double scale,
                                  const float *f_R, const float *lse_R, float *out, hipStream_t st);
+hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);
 

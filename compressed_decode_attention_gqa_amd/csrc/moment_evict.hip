@@ -1,0 +1,326 @@
+// MomentKV moment-informed eviction (summary page, §4.2 "moment residual" and
+// "moment-aware eviction score", Algorithm 1 phase 1) on per-KV-head scopes.
+//
+// For every live token j of a head, with the evicted set known through its sums
+// (n_e, s_k, s_v, S):
+//   r_j = v_j - v_bar - tau S_tilde (k_j - k_bar) / n_e = v_j - c - A k_j,
+//   A = tau S_tilde / n_e,  c = v_bar - A k_bar,  S_tilde = S - s_v s_k^T / n_e,
+//   score(j) = alpha_j ||r_j||  (r_j = v_j when n_e = 0),
+// and the lowest score is evicted and folded into the sums before the next
+// round. All residual arithmetic is float64.
+//
+// One round is two kernels:
+//   k_me_score  (grid: chunks x scopes) stages -A in LDS as float64 MFMA
+//               A-fragments (128 KB), then each wave contracts it with 16
+//               keys at a time on v_mfma_f64_16x16x4 (256 MFMAs per tile),
+//               starting from the accumulator v_j - c, squares and sums the
+//               residual rows, scores, and keeps its lowest candidate;
+//   k_me_pick   (grid: scopes) takes the lowest chunk candidate (ties to the
+//               lower position), flags it and folds its rows into the sums.
+//
+// Index permutation. The contraction index b and the output row a are both
+// permuted so that every lane reads 64 contiguous bytes of its key row and of
+// its value row: at MFMA step s the lane group g = lane / 16 carries
+// b = 32 g + s, and output row i of row tile rt is a = 32 (i % 4) + 4 rt + i / 4,
+// so the accumulator rows a lane holds (i = g + 4 r) are a = 32 g + 4 rt + r.
+#include "kvc_device.h"
+#include "kvc_kernels.h"
+
+namespace kvc {
+namespace {
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+typedef double d2 __attribute__((ext_vector_type(2)));
+
+constexpr int ME_TILE = 16;     // tokens per wave tile (MFMA N)
+constexpr int ME_RT = 8;        // 16-row tiles of the 128 output rows
+constexpr int ME_S2 = 16;       // pairs of MFMA k-steps (32 steps of 4)
+constexpr int ME_WAVES = WG / 64;
+
+struct MeLds {
+  d2 a[ME_S2][ME_RT][64];       // -A fragments, swizzled lane position (128 KB)
+  double c[HD];                 // c = v_bar - A k_bar (zero when n_e = 0)
+  double best[ME_WAVES];
+  int best_pos[ME_WAVES], best_slot[ME_WAVES];
+};
+
+// Swizzled position of lane l's fragment pair for pair-step s2: a bijection on
+// 0..63 that keeps each 16-lane phase of a read on distinct 16-byte bank groups
+// and spreads the staging writes.
+__device__ __forceinline__ int me_swz(int s2, int l) { return l ^ (((s2 >> 1) ^ ((l >> 4) << 2)) & 15); }
+
+// (score, pos) ascending; +inf for no candidate.
+__device__ __forceinline__ bool me_less(double s, int p, double s2, int p2) {
+  return s < s2 || (s == s2 && p < p2);
+}
+
+template <typename T>
+struct MeRow;
+template <>
+struct MeRow<bf16_t> {
+  u32x4 w[4];   // 32 bf16
+  __device__ __forceinline__ void load(const char *base) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = ld16(base + 16 * q);
+  }
+  __device__ __forceinline__ double get(int e) const { return double(ElemTraits<bf16_t>::get(w[e >> 3], e & 7)); }
+};
+template <>
+struct MeRow<float> {
+  u32x4 w[8];   // 32 fp32
+  __device__ __forceinline__ void load(const char *base) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = ld16(base + 16 * q);
+  }
+  __device__ __forceinline__ double get(int e) const { return double(ElemTraits<float>::get(w[e >> 2], e & 3)); }
+};
+
+template <typename T>
+__global__ __launch_bounds__(WG, 1) void k_me_score(MomentEvictArgs p, int iter) {
+  __shared__ MeLds sh;
+  const int sc = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = min(p.len[sc], p.capacity);
+  const int k_sc = L - p.budget;
+  if (iter > 0 && iter >= k_sc) return;
+  const int j_begin = blockIdx.x * p.chunk;
+  if (j_begin >= L) return;
+  const int j_end = min(L, j_begin + p.chunk);
+
+  // ---- stage -A = -tau S_tilde / n_e as fragments, and c = v_bar - A k_bar
+  const int n = p.mom_n[sc];
+  const float *S = p.S + int64_t(sc) * HD * HD;
+  const float *sk = p.sk + int64_t(sc) * HD;
+  const float *sv = p.sv + int64_t(sc) * HD;
+  const double inv_n = n > 0 ? 1.0 / double(n) : 0.0;
+  const double f = -p.scale * inv_n;
+  for (int e4 = tid; e4 < HD * HD / 4; e4 += WG) {
+    const int a = e4 >> 5, b0 = (e4 & 31) * 4;
+    const float4 s4 = *reinterpret_cast<const float4 *>(S + a * HD + b0);
+    const double sva = double(sv[a]) * inv_n;
+    const int i = (a >> 5) + 4 * (a & 3), rt = (a & 31) >> 2, g = b0 >> 5;
+    const int l = i + 16 * g;
+    double dot = 0.0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int b = b0 + t, s = b & 31;
+      const double skb = double(sk[b]);
+      const double sab = t == 0 ? s4.x : t == 1 ? s4.y : t == 2 ? s4.z : s4.w;
+      const double an = n > 0 ? f * (sab - sva * skb) : 0.0;   // -A[a][b]
+      sh.a[s >> 1][rt][me_swz(s >> 1, l)][s & 1] = an;
+      dot = fma(an, skb * inv_n, dot);
+    }
+    // the 32 lanes of one row a hold its 128 columns: c[a] = v_bar[a] + sum_b (-A[a][b]) k_bar[b]
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o);
+    if ((lane & 31) == 0) sh.c[a] = n > 0 ? sva + dot : 0.0;
+  }
+  __syncthreads();
+
+  // ---- residual tiles: wave w takes tiles w, w + 4, ...
+  const int g = lane >> 4, jl = lane & 15;
+  const int64_t row0 = int64_t(sc) * p.scope_stride;
+  const char *kb = p.k, *vb = p.v;
+  constexpr int ES = sizeof(T);
+  double best = __builtin_inf();
+  int best_pos = 0x7fffffff, best_slot = -1;
+  const int n_tiles = (j_end - j_begin + ME_TILE - 1) / ME_TILE;
+  // rows of the wave's first tile; each tile prefetches the next one's rows (clamped, unconditional)
+  MeRow<T> kr, vr;
+  {
+    const int jc = min(j_begin + wave * ME_TILE + jl, j_end - 1);
+    const int64_t off = ((row0 + jc) * HD + 32 * g) * ES;
+    kr.load(kb + off);
+    vr.load(vb + off);
+  }
+  for (int tile = wave; tile < n_tiles; tile += ME_WAVES) {
+    const int j = j_begin + tile * ME_TILE + jl;
+    double x[32];
+#pragma unroll
+    for (int s = 0; s < 32; ++s) x[s] = kr.get(s);
+    d4 acc[ME_RT];
+#pragma unroll
+    for (int rt = 0; rt < ME_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[rt][r] = vr.get(4 * rt + r) - sh.c[32 * g + 4 * rt + r];
+    {
+      const int jn = min(j + ME_WAVES * ME_TILE, j_end - 1);
+      const int64_t off = ((row0 + jn) * HD + 32 * g) * ES;
+      kr.load(kb + off);
+      vr.load(vb + off);
+    }
+    d2 af[2][ME_RT];
+#pragma unroll
+    for (int rt = 0; rt < ME_RT; ++rt) af[0][rt] = sh.a[0][rt][me_swz(0, lane)];
+#pragma unroll
+    for (int s2 = 0; s2 < ME_S2; ++s2) {
+      const int cur = s2 & 1;
+      if (s2 + 1 < ME_S2) {
+        const int pl = me_swz(s2 + 1, lane);
+#pragma unroll
+        for (int rt = 0; rt < ME_RT; ++rt) af[cur ^ 1][rt] = sh.a[s2 + 1][rt][pl];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rt = 0; rt < ME_RT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[cur][rt].x, x[2 * s2], acc[rt], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < ME_RT; ++rt)
+        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[cur][rt].y, x[2 * s2 + 1], acc[rt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int rt = 0; rt < ME_RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss = fma(acc[rt][r], acc[rt][r], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    bool live = j < j_end;
+    if (live && iter > 0) live = p.evict[int64_t(sc) * p.capacity + j] == 0;
+    if (live) {
+      const int64_t slot = int64_t(sc) * p.capacity + j;
+      const double score = double(p.alpha[slot]) * sqrt(ss);
+      if (iter == 0 && g == 0) {
+        p.evict[slot] = 0;
+        if (p.score_out) p.score_out[slot] = float(score);
+      }
+      const int ps = p.pos[slot];
+      if (me_less(score, ps, best, best_pos)) {
+        best = score;
+        best_pos = ps;
+        best_slot = j;
+      }
+    }
+  }
+  // ---- lowest (score, pos) of the workgroup
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double ob = __shfl_xor(best, o);
+    const int op = __shfl_xor(best_pos, o), os = __shfl_xor(best_slot, o);
+    if (me_less(ob, op, best, best_pos)) {
+      best = ob;
+      best_pos = op;
+      best_slot = os;
+    }
+  }
+  if (lane == 0) {
+    sh.best[wave] = best;
+    sh.best_pos[wave] = best_pos;
+    sh.best_slot[wave] = best_slot;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < ME_WAVES; ++w)
+      if (me_less(sh.best[w], sh.best_pos[w], best, best_pos)) {
+        best = sh.best[w];
+        best_pos = sh.best_pos[w];
+        best_slot = sh.best_slot[w];
+      }
+    const int64_t ci = int64_t(sc) * p.n_chunks + blockIdx.x;
+    p.cand_score[ci] = best;
+    p.cand_pos[ci] = best_pos;
+    p.cand_slot[ci] = best_slot;
+  }
+}
+
+// Lowest chunk candidate of the scope -> evicted; fold its rows into the sums
+// (Algorithm 1 steps 11-13: n_e += 1, s_k += k, s_v += v, S += v k^T, fp32).
+template <typename T>
+__global__ __launch_bounds__(WG) void k_me_pick(MomentEvictArgs p, int iter) {
+  __shared__ double wb[ME_WAVES];
+  __shared__ int wp[ME_WAVES], ws[ME_WAVES];
+  __shared__ int pick;
+  const int sc = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = min(p.len[sc], p.capacity);
+  const int k_sc = L - p.budget;
+  if (iter == 0 && tid == 0) {
+    // a live length beyond the capacity, or more evictions than the host bound allows rounds for
+    if (p.len[sc] > p.capacity || k_sc > p.rounds) p.status[0] = -4;
+    if (p.n_evict) p.n_evict[sc] = min(max(k_sc, 0), p.rounds);
+  }
+  if (iter >= k_sc) return;
+  const int n_ch = (L + p.chunk - 1) / p.chunk;
+  double best = __builtin_inf();
+  int best_pos = 0x7fffffff, best_slot = -1;
+  for (int c = tid; c < n_ch; c += WG) {
+    const int64_t ci = int64_t(sc) * p.n_chunks + c;
+    const double s = p.cand_score[ci];
+    const int ps = p.cand_pos[ci], sl = p.cand_slot[ci];
+    if (sl >= 0 && me_less(s, ps, best, best_pos)) {
+      best = s;
+      best_pos = ps;
+      best_slot = sl;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double ob = __shfl_xor(best, o);
+    const int op = __shfl_xor(best_pos, o), os = __shfl_xor(best_slot, o);
+    if (os >= 0 && (best_slot < 0 || me_less(ob, op, best, best_pos))) {
+      best = ob;
+      best_pos = op;
+      best_slot = os;
+    }
+  }
+  if (lane == 0) {
+    wb[wave] = best;
+    wp[wave] = best_pos;
+    ws[wave] = best_slot;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < ME_WAVES; ++w)
+      if (ws[w] >= 0 && (best_slot < 0 || me_less(wb[w], wp[w], best, best_pos))) {
+        best = wb[w];
+        best_pos = wp[w];
+        best_slot = ws[w];
+      }
+    pick = best_slot;
+    if (best_slot >= 0) {
+      p.evict[int64_t(sc) * p.capacity + best_slot] = 1;
+      if (p.order) p.order[int64_t(sc) * p.capacity + iter] = best_slot;
+      p.mom_n[sc] += 1;
+    }
+  }
+  __syncthreads();
+  const int e = pick;
+  if (e < 0) return;
+  const int64_t row = int64_t(sc) * p.scope_stride + e;
+  const T *kr = reinterpret_cast<const T *>(p.k) + row * HD;
+  const T *vr = reinterpret_cast<const T *>(p.v) + row * HD;
+  if (tid < HD) {
+    p.sk[int64_t(sc) * HD + tid] += load_elem<T>(kr, tid);
+    p.sv[int64_t(sc) * HD + tid] += load_elem<T>(vr, tid);
+  }
+  float *S = p.S + int64_t(sc) * HD * HD;
+  for (int e4 = tid; e4 < HD * HD / 4; e4 += WG) {
+    const int a = e4 >> 5, b0 = (e4 & 31) * 4;
+    const float va = load_elem<T>(vr, a);
+    float4 s4 = *reinterpret_cast<float4 *>(S + a * HD + b0);
+    s4.x = fmaf(va, load_elem<T>(kr, b0), s4.x);
+    s4.y = fmaf(va, load_elem<T>(kr, b0 + 1), s4.y);
+    s4.z = fmaf(va, load_elem<T>(kr, b0 + 2), s4.z);
+    s4.w = fmaf(va, load_elem<T>(kr, b0 + 3), s4.w);
+    *reinterpret_cast<float4 *>(S + a * HD + b0) = s4;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st) {
+  const dim3 sgrid(p.n_chunks_used, p.n_scopes);
+  for (int it = 0; it < rounds; ++it) {
+    if (dtype == 0) {
+      hipLaunchKernelGGL(k_me_score<bf16_t>, sgrid, dim3(WG), 0, st, p, it);
+      hipLaunchKernelGGL(k_me_pick<bf16_t>, dim3(p.n_scopes), dim3(WG), 0, st, p, it);
+    } else {
+      hipLaunchKernelGGL(k_me_score<float>, sgrid, dim3(WG), 0, st, p, it);
+      hipLaunchKernelGGL(k_me_pick<float>, dim3(p.n_scopes), dim3(WG), 0, st, p, it);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvc

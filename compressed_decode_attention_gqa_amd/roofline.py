@@ -16,6 +16,7 @@ MI355X_HBM_GBPS = 8000.0          # published HBM3E bandwidth, GB/s
 MI355X_BF16_TFLOPS = 2500.0       # published dense bf16 MFMA, TFLOP/s
 MI355X_FP32_VALU_TFLOPS = 157.3
 MI355X_FP64_VALU_TFLOPS = 78.6
+MI355X_FP64_TFLOPS = 78.6          # published dense fp64 MFMA (same rate as the fp64 vector units)
 
 
 @dataclass(frozen=True)
@@ -77,3 +78,11 @@ def laprox_flops(n_layers: int, n_kv: int, N: int, d: int, D: int, G: int, w: in
     window logits and weights (2 G w N d per pass)."""
     units = n_layers * n_kv
     return {"vw": units * 2 * N * d * D, "window_qk_per_pass": units * 2 * G * w * N * d}
+
+
+def moment_evict_flops(heads: int, L: int, d: int = 128) -> int:
+    """Algorithmic flops of one moment-informed eviction round: per head the model
+    A = tau S_tilde / n_e and c = v_bar - A k_bar (3 d^2 + 2 d^2), then for every live
+    token the contraction A k_j (2 d^2) and the residual and its squared norm (4 d)."""
+    return heads * (5 * d * d + L * (2 * d * d + 4 * d))
+

@@ -172,6 +172,36 @@ int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kv
 int32_t kvc_moment_correct(const kvc_moments *mom, int32_t n_units, const void *q, int32_t dtype, int32_t G,
                            float scale, const float *f_R, const float *lse_R, float *out, void *stream);
 
+/* kvc_moment_evict -- MomentKV moment-informed eviction (summary page, §4.2
+ * "moment residual" and "moment-aware eviction score", Algorithm 1 phase 1),
+ * per-KV-head scopes only (units_per_scope = 1, else KVC_ERR_UNSUPPORTED).
+ * While a scope holds more than `budget` live entries, every live entry j is
+ * scored against the moment model of the evicted set,
+ *   r_j = v_j - v_bar - scale S_tilde (k_j - k_bar) / n_e   (r_j = v_j if n_e = 0),
+ *   score(j) = alpha_j ||r_j||_2,
+ * with k_bar = s_k/n_e, v_bar = s_v/n_e, S_tilde = S - s_v s_k^T/n_e; the
+ * lowest score (ties: lower position) is evicted and folded into the sums
+ * (n_e += 1, s_k += k, s_v += v, S += v k^T, fp32) before the next one is
+ * scored. Do not call kvc_moment_update for these flags again; remove the
+ * entries with kvc_compact afterwards.
+ * alpha: [n_scopes][capacity] fp32 attention weights of the live entries (e.g.
+ * the s of kvc_decode_attn_score after the append; renormalising alpha over
+ * the entries left scales every score alike, so it is not redone per round).
+ * evict: [n_scopes][capacity] u8, 1 on the evicted slots and 0 on every other
+ * slot < len. order: [n_scopes][capacity] int32 or NULL; entry i of a scope
+ * receives the slot evicted in round i. score_out: [n_scopes][capacity] fp32
+ * or NULL; the first round's scores of slots < len. n_evict: [n_scopes] or NULL.
+ * Arithmetic: residuals, norms and scores in float64 (float64 MFMA).
+ * Rounds. max_len (<= 0: capacity) bounds the live length on the host; the
+ * call runs max(1, max_len - budget) rounds of two kernels, so it is meant for
+ * the decode steady state (one eviction per step) and small refresh batches.
+ * A scope that needs more rounds than that evicts only as many and sets the
+ * workspace status to KVC_ERR_CAPACITY. The moment matrix must be 16-byte
+ * aligned. Workspace: kvc_moment_evict_workspace_size. */
+int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const float *alpha, float scale,
+                         int32_t budget, int32_t max_len, uint8_t *evict, int32_t *order, float *score_out,
+                         int32_t *n_evict, void *ws, size_t ws_bytes, void *stream);
+
 /* kvc_compact -- remove the flagged entries of every scope (MomentKV Algorithm 1
  * step 14; InertiaKV §3: eviction is irreversible). Survivors end in slots
  * [0, len - n_evicted): the j-th evicted slot below the new length receives the
@@ -261,6 +291,7 @@ int32_t kvc_laprox_score_marked(const void *q_win, const void *k, const void *v,
 size_t kvc_decode_workspace_size(const kvc_cache *cache, int32_t G, int32_t max_len);
 size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity);
 size_t kvc_compact_workspace_size(const kvc_cache *cache);
+size_t kvc_moment_evict_workspace_size(const kvc_cache *cache);
 size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,
                                  int32_t d, int32_t D);
 

@@ -11,7 +11,7 @@ oracle a host copy of the tensors the GPU consumed, never a regenerated copy.
 
 Streams (ids fixed so that adding a stream never changes another one):
 K, V, channel scales, outlier channels, query stream, new keys, new values,
-votes, W_O, window queries, initial positions.
+votes, W_O, window queries, initial positions, moment sums, weights.
 """
 from __future__ import annotations
 
@@ -20,7 +20,7 @@ import torch
 
 from .workloads import LAPROX_WORKLOADS, LaproxWorkload, Workload, WORKLOADS, budget_for  # noqa: F401  (re-export)
 
-S_K, S_V, S_SCALE, S_OUTLIER, S_Q, S_NEWK, S_NEWV, S_VOTES, S_WO, S_QWIN, S_POS = range(11)
+S_K, S_V, S_SCALE, S_OUTLIER, S_Q, S_NEWK, S_NEWV, S_VOTES, S_WO, S_QWIN, S_POS, S_MOM, S_ALPHA = range(13)
 
 _DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -107,6 +107,27 @@ def initial_positions(n_scopes: int, n_slots: int, context: int, seed: int, devi
     for s in range(n_scopes):
         out[s] = torch.sort(torch.randperm(context, generator=g)[:n_slots]).values.to(torch.int32)
     return out.to(device)
+
+
+def moment_sums(n_units: int, d: int, n_evicted, seed: int, device="cpu", s_scale: float = 1.0):
+    """Running sums of an evicted set, drawn at the size a sum of n unit-normal rows has:
+    n [n_units] int32 (n_evicted, an int or a per-unit list), s_k and s_v [n_units, d]
+    ~ sqrt(n) N(0,1), S [n_units, d, d] ~ s_scale sqrt(n) N(0,1); all fp32. They are not
+    the sums of any particular rows (every fp32 value is a valid input of the moment model);
+    s_scale > 1 makes the key-dependent part of the model as large as the values."""
+    n = torch.as_tensor(n_evicted, dtype=torch.int32).expand(n_units).contiguous()
+    r = torch.sqrt(n.to(torch.float32))
+    sk = _randn((n_units, d), seed, S_MOM, 0, device) * r[:, None].to(device)
+    sv = _randn((n_units, d), seed, S_MOM, 1, device) * r[:, None].to(device)
+    S = _randn((n_units, d, d), seed, S_MOM, 2, device) * (s_scale * r)[:, None, None].to(device)
+    return {"n": n.to(device), "sk": sk, "sv": sv, "S": S}
+
+
+def token_weights(n_scopes: int, n_slots: int, seed: int, device="cpu", spread: float = 2.0):
+    """Positive per-token weights that sum to one per scope, shaped like attention
+    weights: exp(spread * N(0,1)) normalised; fp32 [n_scopes, n_slots]."""
+    z = torch.exp(spread * _randn((n_scopes, n_slots), seed, S_ALPHA, None, "cpu").double())
+    return (z / z.sum(dim=1, keepdim=True)).float().to(device)
 
 
 def output_projection(n_layers: int, H: int, d: int, D: int, seed: int, device="cpu",

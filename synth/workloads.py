@@ -110,6 +110,11 @@ WORKLOADS = {
         n_kv=8, context=65536, budget=budget_for(65536), steps=64, rule="single", alpha=0.0,
         key_scales=True, merge=True, prior_votes=True),
 }
+# MomentKV's setting: Llama-3.1-8B (32 layers x 8 KV heads), per-head budget 1024 (the largest
+# budget the page reports), a 32K context, moment-informed eviction every decode step.
+WORKLOADS["m1_momentkv_llama8b_32layers_b1024"] = Workload(
+    name="m1_momentkv_llama8b_32layers_b1024", seed=6, dtype="bf16", d=128, G=4, n_layers=32, batch=1,
+    n_kv=8, context=32768, budget=1024, steps=64, rule="single", alpha=0.0, moments=True, key_scales=True)
 WORKLOADS["c3_llama8b_model_16k_lazy8"] = WORKLOADS["c3_llama8b_model_16k"].scaled(
     name="c3_llama8b_model_16k_lazy8", lazy_refresh=8)
 

@@ -96,6 +96,29 @@ def test_other_entry_points_reject_bad_arguments():
 
 
 @needs_lib
+def test_moment_evict_host_checks():
+    L = kvc.lib()
+    mom = kvc._Moments(n=0x100, sk=0x200, sv=0x300, S=0x400)
+    c = _fake_cache()
+    need = L.kvc_moment_evict_workspace_size(ctypes.byref(c))
+    assert need > 0
+
+    def call(cache=c, m=mom, alpha=0x500, budget=10, max_len=0, evict=0x600, ws=0x700, wsb=need):
+        return L.kvc_moment_evict(ctypes.byref(cache), ctypes.byref(m) if m is not None else None, alpha, 0.1,
+                                  budget, max_len, evict, None, None, None, ws, wsb, None)
+    assert call(cache=_fake_cache(units_per_scope=2, unit_stride=100, scope_stride=200)) == -3
+    assert call(cache=_fake_cache(head_dim=64)) == -3
+    assert call(m=None) == -1
+    assert call(m=kvc._Moments(n=0x100, sk=0x200, sv=0x300, S=0x408)) == -5
+    assert call(alpha=None) == -1
+    assert call(evict=None) == -1
+    assert call(budget=-1) == -4
+    assert call(max_len=101) == -4
+    assert call(ws=None) == -1
+    assert call(wsb=need - 1) == -6
+
+
+@needs_lib
 @pytest.mark.parametrize("H,n_kv,N,w,D,code", [
     (32, 8, 100, 1, 4096, -3),     # G w = 4: not a whole number of 8-row waves
     (32, 8, 100, 4, 4000, -3),     # D not a multiple of 64
