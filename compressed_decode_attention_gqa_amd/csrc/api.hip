@@ -496,7 +496,7 @@ int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const f
   if (st) return st;
   if (cache->units_per_scope != 1) return KVC_ERR_UNSUPPORTED;
   if (!mom || !mom->n || !mom->sk || !mom->sv || !mom->S || !alpha || !evict || !ws) return KVC_ERR_ARG;
-  if (!aligned16(mom->S)) return KVC_ERR_ALIGN;
+  if (!aligned16(mom->S) || !aligned16(mom->sk)) return KVC_ERR_ALIGN;
   if (budget < 0 || max_len > cache->capacity) return KVC_ERR_CAPACITY;
   const MomentEvictLayout l = moment_evict_layout(cache->n_scopes, cache->capacity);
   if (ws_bytes < l.total) return KVC_ERR_WORKSPACE;
@@ -523,6 +523,7 @@ int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const f
   p.chunk = kMomentTile * ceil_div(tiles, per_scope);
   p.n_chunks = l.n_chunks;
   p.n_chunks_used = ceil_div(cache->capacity, p.chunk);   // chunks past a scope's live length exit at once
+  p.fused_pick = p.chunk >= cache->capacity;
   p.evict = evict;
   p.order = order;
   p.n_evict = n_evict;

@@ -45,6 +45,7 @@ struct MomentEvictArgs {
   int32_t n_chunks;         // candidate stride per scope
   int32_t n_chunks_used;    // chunks launched per scope
   int32_t chunk;            // tokens per chunk (a multiple of 64)
+  int32_t fused_pick;       // chunk >= capacity: the score kernel picks and folds
   uint8_t *evict;
   int32_t *order, *n_evict;
   float *score_out;

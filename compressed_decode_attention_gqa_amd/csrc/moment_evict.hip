@@ -10,13 +10,15 @@
 // round. All residual arithmetic is float64.
 //
 // One round is two kernels:
-//   k_me_score  (grid: chunks x scopes) stages -A in LDS as float64 MFMA
-//               A-fragments (128 KB), then each wave contracts it with 16
+//   k_me_score  (grid: chunks x scopes, 8 waves) stages -A in LDS as float64
+//               MFMA A-fragments (128 KB), then each wave contracts it with 16
 //               keys at a time on v_mfma_f64_16x16x4 (256 MFMAs per tile),
 //               starting from the accumulator v_j - c, squares and sums the
 //               residual rows, scores, and keeps its lowest candidate;
 //   k_me_pick   (grid: scopes) takes the lowest chunk candidate (ties to the
 //               lower position), flags it and folds its rows into the sums.
+// When one chunk covers every scope (chunk >= capacity) the score kernel's
+// workgroup picks and folds itself and the second kernel is not launched.
 //
 // Index permutation. The contraction index b and the output row a are both
 // permuted so that every lane reads 64 contiguous bytes of its key row and of
@@ -35,13 +37,17 @@ typedef double d2 __attribute__((ext_vector_type(2)));
 constexpr int ME_TILE = 16;     // tokens per wave tile (MFMA N)
 constexpr int ME_RT = 8;        // 16-row tiles of the 128 output rows
 constexpr int ME_S2 = 16;       // pairs of MFMA k-steps (32 steps of 4)
+constexpr int ME_SWG = 512;     // score workgroup: 8 waves, two per SIMD, so one wave's
+                                // per-tile vector work overlaps the other's MFMAs
+constexpr int ME_SWAVES = ME_SWG / 64;
 constexpr int ME_WAVES = WG / 64;
+constexpr int ME_CPAD = 36;     // c is stored [g][36]: the four lane groups read distinct banks
 
 struct MeLds {
   d2 a[ME_S2][ME_RT][64];       // -A fragments, swizzled lane position (128 KB)
-  double c[HD];                 // c = v_bar - A k_bar (zero when n_e = 0)
-  double best[ME_WAVES];
-  int best_pos[ME_WAVES], best_slot[ME_WAVES];
+  double c[4 * ME_CPAD];        // c = v_bar - A k_bar (zero when n_e = 0), row a at (a/32)*36 + a%32
+  double best[ME_SWAVES];
+  int best_pos[ME_SWAVES], best_slot[ME_SWAVES];
 };
 
 // Swizzled position of lane l's fragment pair for pair-step s2: a bijection on
@@ -75,65 +81,119 @@ struct MeRow<float> {
   __device__ __forceinline__ double get(int e) const { return double(ElemTraits<float>::get(w[e >> 2], e & 3)); }
 };
 
+// Algorithm 1 steps 12-13 for evicted slot e of scope sc (fp32 sums, one fused
+// multiply-add per element): s_k += k_e, s_v += v_e, S += v_e k_e^T, by NT threads.
+template <typename T, int NT>
+__device__ __forceinline__ void me_fold(const MomentEvictArgs &p, int sc, int e, int tid) {
+  const int64_t row = int64_t(sc) * p.scope_stride + e;
+  const T *kr = reinterpret_cast<const T *>(p.k) + row * HD;
+  const T *vr = reinterpret_cast<const T *>(p.v) + row * HD;
+  float *S = p.S + int64_t(sc) * HD * HD;
+  constexpr int PER = HD * HD / 4 / NT;
+  const int b0 = (tid & 31) * 4;   // every iteration covers the same four columns
+  float4 s4[PER];
+  float va[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int a = (tid + it * NT) >> 5;
+    s4[it] = *reinterpret_cast<const float4 *>(S + a * HD + b0);
+    va[it] = load_elem<T>(vr, a);
+  }
+  const float k0 = load_elem<T>(kr, b0), k1 = load_elem<T>(kr, b0 + 1), k2 = load_elem<T>(kr, b0 + 2),
+              k3 = load_elem<T>(kr, b0 + 3);
+  if (tid < HD) {
+    p.sk[int64_t(sc) * HD + tid] += load_elem<T>(kr, tid);
+    p.sv[int64_t(sc) * HD + tid] += load_elem<T>(vr, tid);
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int a = (tid + it * NT) >> 5;
+    s4[it].x = fmaf(va[it], k0, s4[it].x);
+    s4[it].y = fmaf(va[it], k1, s4[it].y);
+    s4[it].z = fmaf(va[it], k2, s4[it].z);
+    s4[it].w = fmaf(va[it], k3, s4[it].w);
+    *reinterpret_cast<float4 *>(S + a * HD + b0) = s4[it];
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(WG, 1) void k_me_score(MomentEvictArgs p, int iter) {
+__global__ __launch_bounds__(ME_SWG, 1) void k_me_score(MomentEvictArgs p, int iter) {
   __shared__ MeLds sh;
   const int sc = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = min(p.len[sc], p.capacity);
   const int k_sc = L - p.budget;
+  if (p.fused_pick && iter == 0 && tid == 0) {
+    // a live length beyond the capacity, or more evictions than the host bound allows rounds for
+    if (p.len[sc] > p.capacity || k_sc > p.rounds) p.status[0] = -4;
+    if (p.n_evict) p.n_evict[sc] = min(max(k_sc, 0), p.rounds);
+  }
   if (iter > 0 && iter >= k_sc) return;
   const int j_begin = blockIdx.x * p.chunk;
   if (j_begin >= L) return;
   const int j_end = min(L, j_begin + p.chunk);
 
   // ---- stage -A = -tau S_tilde / n_e as fragments, and c = v_bar - A k_bar
-  const int n = p.mom_n[sc];
-  const float *S = p.S + int64_t(sc) * HD * HD;
-  const float *sk = p.sk + int64_t(sc) * HD;
-  const float *sv = p.sv + int64_t(sc) * HD;
-  const double inv_n = n > 0 ? 1.0 / double(n) : 0.0;
-  const double f = -p.scale * inv_n;
-  for (int e4 = tid; e4 < HD * HD / 4; e4 += WG) {
-    const int a = e4 >> 5, b0 = (e4 & 31) * 4;
-    const float4 s4 = *reinterpret_cast<const float4 *>(S + a * HD + b0);
-    const double sva = double(sv[a]) * inv_n;
-    const int i = (a >> 5) + 4 * (a & 3), rt = (a & 31) >> 2, g = b0 >> 5;
-    const int l = i + 16 * g;
-    double dot = 0.0;
+  {
+    constexpr int PER = HD * HD / 4 / ME_SWG;   // float4 of S per thread
+    const int n = p.mom_n[sc];
+    const float *S = p.S + int64_t(sc) * HD * HD;
+    const float *sk = p.sk + int64_t(sc) * HD;
+    const float *sv = p.sv + int64_t(sc) * HD;
+    float4 s4[PER];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int b = b0 + t, s = b & 31;
-      const double skb = double(sk[b]);
-      const double sab = t == 0 ? s4.x : t == 1 ? s4.y : t == 2 ? s4.z : s4.w;
-      const double an = n > 0 ? f * (sab - sva * skb) : 0.0;   // -A[a][b]
-      sh.a[s >> 1][rt][me_swz(s >> 1, l)][s & 1] = an;
-      dot = fma(an, skb * inv_n, dot);
+    for (int it = 0; it < PER; ++it) {
+      const int e4 = tid + it * ME_SWG;
+      s4[it] = *reinterpret_cast<const float4 *>(S + (e4 >> 5) * HD + (e4 & 31) * 4);
     }
-    // the 32 lanes of one row a hold its 128 columns: c[a] = v_bar[a] + sum_b (-A[a][b]) k_bar[b]
+    // this thread's four columns are the same in every iteration
+    const int b0 = (tid & 31) * 4, g = b0 >> 5;
+    float4 sk4 = *reinterpret_cast<const float4 *>(sk + b0);
+    const double inv_n = n > 0 ? 1.0 / double(n) : 0.0;
+    const double f = -p.scale * inv_n;
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o);
-    if ((lane & 31) == 0) sh.c[a] = n > 0 ? sva + dot : 0.0;
+    for (int it = 0; it < PER; ++it) {
+      const int a = (tid + it * ME_SWG) >> 5;
+      const double sva = double(sv[a]) * inv_n;
+      const int i = (a >> 5) + 4 * (a & 3), rt = (a & 31) >> 2;
+      const int l = i + 16 * g;
+      double dot = 0.0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int s = (b0 + t) & 31;
+        const double skb = t == 0 ? sk4.x : t == 1 ? sk4.y : t == 2 ? sk4.z : sk4.w;
+        const double sab = t == 0 ? s4[it].x : t == 1 ? s4[it].y : t == 2 ? s4[it].z : s4[it].w;
+        const double an = n > 0 ? f * (sab - sva * skb) : 0.0;   // -A[a][b]
+        sh.a[s >> 1][rt][me_swz(s >> 1, l)][s & 1] = an;
+        dot = fma(an, skb * inv_n, dot);
+      }
+      // the 32 lanes of one row a hold its 128 columns: c[a] = v_bar[a] + sum_b (-A[a][b]) k_bar[b]
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) dot += __shfl_xor(dot, o);
+      if ((lane & 31) == 0) sh.c[(a >> 5) * ME_CPAD + (a & 31)] = n > 0 ? sva + dot : 0.0;
+    }
   }
   __syncthreads();
 
-  // ---- residual tiles: wave w takes tiles w, w + 4, ...
+  // ---- residual tiles: wave w takes tiles w, w + 8, ...
   const int g = lane >> 4, jl = lane & 15;
   const int64_t row0 = int64_t(sc) * p.scope_stride;
   const char *kb = p.k, *vb = p.v;
   constexpr int ES = sizeof(T);
+  const double *cg = sh.c + g * ME_CPAD;
   double best = __builtin_inf();
   int best_pos = 0x7fffffff, best_slot = -1;
   const int n_tiles = (j_end - j_begin + ME_TILE - 1) / ME_TILE;
-  // rows of the wave's first tile; each tile prefetches the next one's rows (clamped, unconditional)
-  MeRow<T> kr, vr;
-  {
-    const int jc = min(j_begin + wave * ME_TILE + jl, j_end - 1);
+  for (int tile = wave; tile < n_tiles; tile += ME_SWAVES) {
+    const int j = j_begin + tile * ME_TILE + jl;
+    const int jc = min(j, j_end - 1);
+    const int64_t slot = int64_t(sc) * p.capacity + jc;
+    const float al_t = p.alpha[slot];
+    const int ps_t = p.pos[slot];
+    const int ev_t = iter > 0 ? p.evict[slot] : 0;
     const int64_t off = ((row0 + jc) * HD + 32 * g) * ES;
+    MeRow<T> kr, vr;
     kr.load(kb + off);
     vr.load(vb + off);
-  }
-  for (int tile = wave; tile < n_tiles; tile += ME_WAVES) {
-    const int j = j_begin + tile * ME_TILE + jl;
     double x[32];
 #pragma unroll
     for (int s = 0; s < 32; ++s) x[s] = kr.get(s);
@@ -141,31 +201,19 @@ __global__ __launch_bounds__(WG, 1) void k_me_score(MomentEvictArgs p, int iter)
 #pragma unroll
     for (int rt = 0; rt < ME_RT; ++rt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[rt][r] = vr.get(4 * rt + r) - sh.c[32 * g + 4 * rt + r];
-    {
-      const int jn = min(j + ME_WAVES * ME_TILE, j_end - 1);
-      const int64_t off = ((row0 + jn) * HD + 32 * g) * ES;
-      kr.load(kb + off);
-      vr.load(vb + off);
-    }
-    d2 af[2][ME_RT];
-#pragma unroll
-    for (int rt = 0; rt < ME_RT; ++rt) af[0][rt] = sh.a[0][rt][me_swz(0, lane)];
+      for (int r = 0; r < 4; ++r) acc[rt][r] = vr.get(4 * rt + r) - cg[4 * rt + r];
 #pragma unroll
     for (int s2 = 0; s2 < ME_S2; ++s2) {
-      const int cur = s2 & 1;
-      if (s2 + 1 < ME_S2) {
-        const int pl = me_swz(s2 + 1, lane);
+      d2 af[ME_RT];
+      const int pl = me_swz(s2, lane);
 #pragma unroll
-        for (int rt = 0; rt < ME_RT; ++rt) af[cur ^ 1][rt] = sh.a[s2 + 1][rt][pl];
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int rt = 0; rt < ME_RT; ++rt) af[rt] = sh.a[s2][rt][pl];
 #pragma unroll
       for (int rt = 0; rt < ME_RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[cur][rt].x, x[2 * s2], acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rt].x, x[2 * s2], acc[rt], 0, 0, 0);
 #pragma unroll
       for (int rt = 0; rt < ME_RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[cur][rt].y, x[2 * s2 + 1], acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rt].y, x[2 * s2 + 1], acc[rt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     double ss = 0.0;
@@ -175,19 +223,15 @@ __global__ __launch_bounds__(WG, 1) void k_me_score(MomentEvictArgs p, int iter)
       for (int r = 0; r < 4; ++r) ss = fma(acc[rt][r], acc[rt][r], ss);
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    bool live = j < j_end;
-    if (live && iter > 0) live = p.evict[int64_t(sc) * p.capacity + j] == 0;
-    if (live) {
-      const int64_t slot = int64_t(sc) * p.capacity + j;
-      const double score = double(p.alpha[slot]) * sqrt(ss);
+    if (j < j_end && ev_t == 0) {
+      const double score = double(al_t) * sqrt(ss);
       if (iter == 0 && g == 0) {
         p.evict[slot] = 0;
         if (p.score_out) p.score_out[slot] = float(score);
       }
-      const int ps = p.pos[slot];
-      if (me_less(score, ps, best, best_pos)) {
+      if (me_less(score, ps_t, best, best_pos)) {
         best = score;
-        best_pos = ps;
+        best_pos = ps_t;
         best_slot = j;
       }
     }
@@ -210,17 +254,32 @@ __global__ __launch_bounds__(WG, 1) void k_me_score(MomentEvictArgs p, int iter)
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < ME_WAVES; ++w)
+    for (int w = 1; w < ME_SWAVES; ++w)
       if (me_less(sh.best[w], sh.best_pos[w], best, best_pos)) {
         best = sh.best[w];
         best_pos = sh.best_pos[w];
         best_slot = sh.best_slot[w];
       }
-    const int64_t ci = int64_t(sc) * p.n_chunks + blockIdx.x;
-    p.cand_score[ci] = best;
-    p.cand_pos[ci] = best_pos;
-    p.cand_slot[ci] = best_slot;
+    if (!p.fused_pick) {
+      const int64_t ci = int64_t(sc) * p.n_chunks + blockIdx.x;
+      p.cand_score[ci] = best;
+      p.cand_pos[ci] = best_pos;
+      p.cand_slot[ci] = best_slot;
+    } else {
+      // one chunk holds the whole scope: this workgroup's lowest is the scope's
+      const bool take = iter < k_sc && best_slot >= 0;
+      sh.best_slot[0] = take ? best_slot : -1;
+      if (take) {
+        p.evict[int64_t(sc) * p.capacity + best_slot] = 1;
+        if (p.order) p.order[int64_t(sc) * p.capacity + iter] = best_slot;
+        p.mom_n[sc] += 1;
+      }
+    }
   }
+  if (!p.fused_pick) return;
+  __syncthreads();
+  const int e = sh.best_slot[0];
+  if (e >= 0) me_fold<T, ME_SWG>(p, sc, e, tid);
 }
 
 // Lowest chunk candidate of the scope -> evicted; fold its rows into the sums
@@ -284,25 +343,7 @@ __global__ __launch_bounds__(WG) void k_me_pick(MomentEvictArgs p, int iter) {
   }
   __syncthreads();
   const int e = pick;
-  if (e < 0) return;
-  const int64_t row = int64_t(sc) * p.scope_stride + e;
-  const T *kr = reinterpret_cast<const T *>(p.k) + row * HD;
-  const T *vr = reinterpret_cast<const T *>(p.v) + row * HD;
-  if (tid < HD) {
-    p.sk[int64_t(sc) * HD + tid] += load_elem<T>(kr, tid);
-    p.sv[int64_t(sc) * HD + tid] += load_elem<T>(vr, tid);
-  }
-  float *S = p.S + int64_t(sc) * HD * HD;
-  for (int e4 = tid; e4 < HD * HD / 4; e4 += WG) {
-    const int a = e4 >> 5, b0 = (e4 & 31) * 4;
-    const float va = load_elem<T>(vr, a);
-    float4 s4 = *reinterpret_cast<float4 *>(S + a * HD + b0);
-    s4.x = fmaf(va, load_elem<T>(kr, b0), s4.x);
-    s4.y = fmaf(va, load_elem<T>(kr, b0 + 1), s4.y);
-    s4.z = fmaf(va, load_elem<T>(kr, b0 + 2), s4.z);
-    s4.w = fmaf(va, load_elem<T>(kr, b0 + 3), s4.w);
-    *reinterpret_cast<float4 *>(S + a * HD + b0) = s4;
-  }
+  if (e >= 0) me_fold<T, WG>(p, sc, e, tid);
 }
 
 }  // namespace
@@ -311,11 +352,11 @@ hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, 
   const dim3 sgrid(p.n_chunks_used, p.n_scopes);
   for (int it = 0; it < rounds; ++it) {
     if (dtype == 0) {
-      hipLaunchKernelGGL(k_me_score<bf16_t>, sgrid, dim3(WG), 0, st, p, it);
-      hipLaunchKernelGGL(k_me_pick<bf16_t>, dim3(p.n_scopes), dim3(WG), 0, st, p, it);
+      hipLaunchKernelGGL(k_me_score<bf16_t>, sgrid, dim3(ME_SWG), 0, st, p, it);
+      if (!p.fused_pick) hipLaunchKernelGGL(k_me_pick<bf16_t>, dim3(p.n_scopes), dim3(WG), 0, st, p, it);
     } else {
-      hipLaunchKernelGGL(k_me_score<float>, sgrid, dim3(WG), 0, st, p, it);
-      hipLaunchKernelGGL(k_me_pick<float>, dim3(p.n_scopes), dim3(WG), 0, st, p, it);
+      hipLaunchKernelGGL(k_me_score<float>, sgrid, dim3(ME_SWG), 0, st, p, it);
+      if (!p.fused_pick) hipLaunchKernelGGL(k_me_pick<float>, dim3(p.n_scopes), dim3(WG), 0, st, p, it);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -196,8 +196,8 @@ int32_t kvc_moment_correct(const kvc_moments *mom, int32_t n_units, const void *
  * call runs max(1, max_len - budget) rounds of two kernels, so it is meant for
  * the decode steady state (one eviction per step) and small refresh batches.
  * A scope that needs more rounds than that evicts only as many and sets the
- * workspace status to KVC_ERR_CAPACITY. The moment matrix must be 16-byte
- * aligned. Workspace: kvc_moment_evict_workspace_size. */
+ * workspace status to KVC_ERR_CAPACITY. The moment matrix and the key sums
+ * must be 16-byte aligned. Workspace: kvc_moment_evict_workspace_size. */
 int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const float *alpha, float scale,
                          int32_t budget, int32_t max_len, uint8_t *evict, int32_t *order, float *score_out,
                          int32_t *n_evict, void *ws, size_t ws_bytes, void *stream);

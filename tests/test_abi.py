@@ -110,6 +110,7 @@ def test_moment_evict_host_checks():
     assert call(cache=_fake_cache(head_dim=64)) == -3
     assert call(m=None) == -1
     assert call(m=kvc._Moments(n=0x100, sk=0x200, sv=0x300, S=0x408)) == -5
+    assert call(m=kvc._Moments(n=0x100, sk=0x204, sv=0x300, S=0x400)) == -5
     assert call(alpha=None) == -1
     assert call(evict=None) == -1
     assert call(budget=-1) == -4

@@ -156,6 +156,23 @@ def test_several_rounds_rescore_after_each_fold(dtype):
     print(f"several rounds {dtype}: near-tie flips {flips}", flush=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_one_chunk_per_scope_picks_inside_the_score_kernel(dtype):
+    """More scopes than CUs: each scope is one chunk, and the score kernel's workgroup
+    picks and folds itself (no second kernel); ragged lengths, up to 4 rounds, empty scopes."""
+    budget, S = 150, 260
+    rng = np.random.default_rng(3)
+    lens = [int(x) for x in rng.integers(0, budget + 5, size=S)]
+    lens[:6] = [0, budget, budget + 1, budget + 4, 1, budget + 2]
+    n_e = [int(x) for x in rng.integers(0, 3000, size=S)]
+    cache, mom, alpha = _make(lens, budget + 4, dtype, n_e, seed=31, s_scale=15.0)
+    h = _host(cache, mom, alpha, dtype)
+    evict, order, score, n_ev, ws = _run(cache, mom, alpha, budget, budget + 4)
+    flips = _check(h, mom, budget, evict, order, score, n_ev)
+    assert kvc.kvc_workspace_status(ws) == 0
+    print(f"one chunk per scope {dtype}: near-tie flips {flips}", flush=True)
+
+
 def test_too_few_rounds_sets_the_status():
     """max_len below a scope's live length: that scope evicts as many as the rounds allow."""
     budget = 64
