@@ -6,6 +6,7 @@
  * Sources (the pages these operations are defined on):
  *   MomentKV  -- "MOMENTKV: Closing the Directional Gap in KV Cache Eviction for
  *                Long-Context Inference" (summary page): moment statistics §4.1,
+ *                moment-informed eviction and corrected inference §4.2,
  *                Algorithm 1, Appendix A.1.
  *   InertiaKV -- "Key factors of KV cache eviction under aggressive decoding:
  *                temporal aggregation and rank preservation" (translated
