@@ -6,9 +6,10 @@
 // Per unit (layer l, KV head h) with G query heads and w window queries, the
 // R = G w window rows (g, j) attend causally: row j sits at position
 // N - w + j. Kernels, in launch order:
-//   k_lap_wprep    W_bar = sum of the group's W_O^g blocks, summed in float64
-//                  and split into bf16 hi + lo (residual below 2^-17 of each
-//                  element), stored transposed [D][d] for the MFMA B operand.
+//   k_lap_gram     M = W_bar W_bar^T (d x d, float64) on v_mfma_f64_16x16x4,
+//                  W_bar = sum of the group's W_O^g blocks summed in float64
+//                  while its column blocks are staged in LDS; two halves of D
+//                  per unit, summed when M is staged.
 //   k_lap_window<1> per token tile: float64 logits of 8 rows per wave
 //                  (lane-permuted transposed reduction), per-row running max
 //                  and sum of exp -> partials per tile.
@@ -16,20 +17,17 @@
 //   k_lap_window<2> recomputes the logits; A = exp(l - M) / Z; the group mean
 //                  over the G heads of each window row by DPP sums; its square
 //                  summed over the rows of the workgroup -> c^2 partials.
-//   k_lap_vw       r_i^2 = ||v_i W_bar||^2 on MFMA (16x16x32 bf16, fp32
-//                  accumulate; hi and lo both accumulate into the same tile),
-//                  squares summed in float64; B tiles staged in LDS.
+//   k_lap_r2       r_i^2 = ||v_i W_bar||^2 = v_i M v_i^T (the Gram identity:
+//                  a d x d instead of a d x D contraction per token) on the
+//                  float64 MFMA operator of kvc_f64mfma.h, M staged in LDS.
 //   k_lap_p        p_i = c_i r_i (float64) and per-chunk partial sums.
 //   k_lap_norm     per-layer sum in fixed order, score = p / sum.
 // The model-wide Top-K (key design 3) is kvc_select_evict over the scores.
-#include "kvc_device.h"
+#include "kvc_f64mfma.h"
 #include "kvc_laprox.h"
 
 namespace kvc {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- geometry
 constexpr int LW = 8;               // waves per window workgroup
@@ -44,12 +42,13 @@ constexpr int LCH = LTPI * LUNR;
 constexpr int LPF = 2;              // sub-chunks of loads in flight
 constexpr int RB = HD * 2;          // bytes per bf16 row
 
-constexpr int VW_WAVES = 8;         // V W_bar workgroup: 8 waves x 64 tokens
-constexpr int VW_NT = 64 * VW_WAVES;
-constexpr int VW_MB = 4;            // 16-token M blocks per wave
-constexpr int VW_TOK = VW_WAVES * VW_MB * 16;   // tokens per workgroup (512)
-constexpr int VW_NS = 32;           // columns per LDS stage of W_bar^T
-constexpr int VW_LDS_ROW = HD + 8;  // bf16 per LDS row of a B block (padded)
+constexpr int GR_KS = 2;            // halves of D per unit in the Gram kernel
+constexpr int GR_NT = 512;          // Gram workgroup: 8 waves, wave w owns output rows 16 w .. + 15
+constexpr int GR_KB = 32;           // columns of W_bar per LDS block
+constexpr int GR_LD = GR_KB + 2;    // doubles per LDS row (34: 16-byte reads of a 16-lane phase hit distinct banks)
+
+constexpr int R2_NT = 512;          // r^2 workgroup: 8 waves, two per SIMD
+constexpr int R2_TOK = 2048;        // tokens per r^2 workgroup (16 tiles per wave)
 
 constexpr int P_CHUNK = 4096;       // tokens per partial sum of p
 
@@ -58,7 +57,7 @@ struct LapArgs {
   int n_layers, H, n_kv, N, w, D, G, R, nh, ntiles, nchunks;
   double scale;
   float *score;
-  uint16_t *wt_hi, *wt_lo;    // [units][D][d]
+  double *gram;               // [units][GR_KS][d][d]
   double *tM, *tZ;            // [units][R][ntiles]
   double *rM, *rZ;            // [units][R]
   float *c2;                  // [units][nh][N]
@@ -66,35 +65,84 @@ struct LapArgs {
   double *psum;               // [units][nchunks]
 };
 
-// ---------------------------------------------------------------- W_bar
-// grid (D / 64, d / 64, units), 256 threads: a 64 x 64 tile of W_bar, summed
-// over the group in float64, split hi/lo and written transposed.
-__global__ __launch_bounds__(256) void k_lap_wprep(const LapArgs a) {
-  __shared__ float hi_t[64][65], lo_t[64][65];
-  const int n0 = blockIdx.x * 64, r0 = blockIdx.y * 64, u = blockIdx.z;
+// ---------------------------------------------------------------- Gram matrix
+// grid (units, GR_KS), 512 threads: partial M[a][c] = sum over this half of D of
+// W_bar[a][b] W_bar[c][b]. Blocks of 32 columns of W_bar (all 128 rows) are
+// summed over the group in float64 and staged in LDS (double-buffered, one
+// barrier per block); in a block, lane group kg = lane / 16 carries columns
+// 8 kg + s' at MFMA step s' (the contraction order is free), so each lane reads
+// 64 contiguous bytes per row. Wave w computes output rows 16 w .. + 15 against
+// all eight 16-column tiles.
+__global__ __launch_bounds__(GR_NT, 1) void k_lap_gram(const LapArgs a) {
+  __shared__ __attribute__((aligned(16))) double blk[2][HD][GR_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int u = blockIdx.x, half = blockIdx.y;
   const int l = u / a.n_kv, h = u % a.n_kv;
-  const int tid = threadIdx.x;
+  const int D = a.D, Dh = D / GR_KS, nblk = Dh / GR_KB;
   const uint16_t *wo = reinterpret_cast<const uint16_t *>(a.wo);
-  for (int idx = tid; idx < 64 * 64; idx += 256) {
-    const int rr = idx / 64, nn = idx % 64;   // W row (d index) rr, column nn: coalesced over nn
-    double s = 0.0;
-    for (int g = 0; g < a.G; ++g) {
-      const int64_t head = int64_t(l) * a.H + h * a.G + g;
-      s += double(bf16_to_f32(wo[(head * HD + r0 + rr) * a.D + n0 + nn]));
+  // staging task: row tid / 4, columns 8 (tid % 4) .. + 7 of the block
+  const int srow = tid >> 2, scol = (tid & 3) * 8;
+  u32x4 raw[8];   // the group's G 16-byte vectors (G <= 8)
+  auto fetch = [&](int b) {
+    const int col = half * Dh + b * GR_KB + scol;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < a.G) {
+        const int64_t head = int64_t(l) * a.H + h * a.G + g;
+        raw[g] = ld16(wo + (head * HD + srow) * D + col);
+      }
+  };
+  auto stage = [&](int buf) {
+    double sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = 0.0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < a.G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] += double(ElemTraits<bf16_t>::get(raw[g], e));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) *reinterpret_cast<fm_d2 *>(&blk[buf][srow][scol + e]) = fm_d2{sum[e], sum[e + 1]};
+  };
+  fm_d4 acc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = fm_d4{0.0, 0.0, 0.0, 0.0};
+  const int m = lane & 15, kg = lane >> 4;
+  fetch(0);
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    stage(buf);
+    __syncthreads();
+    if (b + 1 < nblk) fetch(b + 1);
+    const double *arow = &blk[buf][16 * wave + m][8 * kg];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {          // steps 4 sh .. 4 sh + 3
+      const fm_d2 a0 = *reinterpret_cast<const fm_d2 *>(arow + 4 * sh);
+      const fm_d2 a1 = *reinterpret_cast<const fm_d2 *>(arow + 4 * sh + 2);
+      fm_d2 bq[8][2];
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const double *brow = &blk[buf][16 * ct + m][8 * kg + 4 * sh];
+        bq[ct][0] = *reinterpret_cast<const fm_d2 *>(brow);
+        bq[ct][1] = *reinterpret_cast<const fm_d2 *>(brow + 2);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, bq[ct][0].x, acc[ct], 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, bq[ct][0].y, acc[ct], 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, bq[ct][1].x, acc[ct], 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, bq[ct][1].y, acc[ct], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const uint16_t hb = f32_to_bf16(float(s));
-    const double hv = double(bf16_to_f32(hb));
-    const uint16_t lb = f32_to_bf16(float(s - hv));
-    hi_t[rr][nn] = __uint_as_float(uint32_t(hb));
-    lo_t[rr][nn] = __uint_as_float(uint32_t(lb));
   }
-  __syncthreads();
-  for (int idx = tid; idx < 64 * 64; idx += 256) {
-    const int nn = idx / 64, rr = idx % 64;   // transposed: coalesced over rr
-    const int64_t o = (int64_t(u) * a.D + n0 + nn) * HD + r0 + rr;
-    a.wt_hi[o] = uint16_t(__float_as_uint(hi_t[rr][nn]));
-    a.wt_lo[o] = uint16_t(__float_as_uint(lo_t[rr][nn]));
-  }
+  // D[16 wave + kg + 4 r][16 ct + m]
+  double *out = a.gram + (int64_t(u) * GR_KS + half) * HD * HD;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(16 * wave + kg + 4 * r) * HD + 16 * ct + m] = acc[ct][r];
 }
 
 // ---------------------------------------------------------------- window passes
@@ -267,122 +315,49 @@ __global__ __launch_bounds__(256) void k_lap_rowfin(const LapArgs a, int n_rows)
   a.rZ[r] = Z;
 }
 
-// ---------------------------------------------------------------- V W_bar on MFMA
-// grid (ceil(N / 512), units), 512 threads. Wave w holds the A fragments (V
-// rows) of tokens t0 + 64 w + 16 mb + (lane % 16), d elements 32 ks + 8 (lane / 16) ..
-// + 7. W_bar^T (hi and lo) is staged through LDS in stages of 32 columns
-// ([hi/lo][column][d], rows padded against bank conflicts), double-buffered,
-// with each thread's two 16-byte vectors of a stage loaded three stages
-// ahead; one barrier per stage.
-__global__ __launch_bounds__(VW_NT, 1) void k_lap_vw(const LapArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t bt[2][2][VW_NS][VW_LDS_ROW];
+// ---------------------------------------------------------------- r^2 = v M v^T on float64 MFMA
+// grid (ceil(N / R2_TOK), units), 512 threads. M (the sum of the two Gram
+// halves) is staged as the float64 MFMA operator; wave w takes the 16-token
+// tiles w, w + 8, ... of the workgroup's range. A lane's B values are elements
+// [32 g, 32 g + 32) of its token's value row, and its accumulator rows are
+// the same elements of M v, so r^2 = sum over its 32 products, then over g.
+__global__ __launch_bounds__(R2_NT, 1) void k_lap_r2(const LapArgs a) {
+  __shared__ FmOperator op;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int u = blockIdx.y;
-  const int N = a.N, D = a.D;
-  const int t0 = blockIdx.x * VW_TOK + wave * (VW_MB * 16);
-  const int m = lane & 15, kq = lane >> 4;
-
-  bf16x8 av[VW_MB][4];
+  const int u = blockIdx.y, N = a.N;
+  const int t0 = blockIdx.x * R2_TOK, t1 = min(N, t0 + R2_TOK);
   {
-    const char *Vb = a.v + int64_t(u) * N * RB;
+    const double *M0 = a.gram + int64_t(u) * GR_KS * HD * HD;
+    for (int e = tid; e < HD * HD; e += R2_NT) {
+      double m = 0.0;
 #pragma unroll
-    for (int mb = 0; mb < VW_MB; ++mb) {
-      const int tok = min(t0 + 16 * mb + m, N - 1);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 x = ld16(Vb + int64_t(tok) * RB + (32 * ks + 8 * kq) * 2);
-        av[mb][ks] = __builtin_bit_cast(bf16x8, x);
-      }
+      for (int k = 0; k < GR_KS; ++k) m += M0[k * HD * HD + e];
+      fm_put(op, e >> 7, e & 127, m);
     }
   }
-  // the two B vectors this thread stages per stage: the hi and the lo vector of
-  // column tid / 16 of the stage, d elements 8 (tid % 16) .. + 7
-  const int nn = (tid >> 4) & 31, ee = tid & 15;
-  const uint16_t *src_hi = a.wt_hi + int64_t(u) * D * HD + ee * 8;
-  const uint16_t *src_lo = a.wt_lo + int64_t(u) * D * HD + ee * 8;
-  const int nst = D / VW_NS;
-  constexpr int PD = 3;                  // stages of loads in flight
-  u32x4 sreg[PD][2];
-  auto load_stage = [&](u32x4 (&r)[2], int st) {
-    const int col = min(st, nst - 1) * VW_NS + nn;
-    r[0] = ld16(src_hi + int64_t(col) * HD);
-    r[1] = ld16(src_lo + int64_t(col) * HD);
-  };
-  auto store_stage = [&](const u32x4 (&r)[2], int buf) {
-    *reinterpret_cast<u32x4 *>(&bt[buf][0][nn][ee * 8]) = r[0];
-    *reinterpret_cast<u32x4 *>(&bt[buf][1][nn][ee * 8]) = r[1];
-  };
-#pragma unroll
-  for (int p = 0; p < PD; ++p) load_stage(sreg[p], p);
-  store_stage(sreg[0], 0);
-  load_stage(sreg[0], PD);
   __syncthreads();
-
-  double rs[VW_MB][4];
+  const int g = lane >> 4, jl = lane & 15;
+  const char *Vb = a.v + int64_t(u) * N * RB;
+  const int n_tiles = (t1 - t0 + FM_TILE - 1) / FM_TILE;
+  for (int tile = wave; tile < n_tiles; tile += R2_NT / 64) {
+    const int j = t0 + tile * FM_TILE + jl;
+    FmRow<bf16_t> vr;
+    vr.load(Vb + int64_t(min(j, t1 - 1)) * RB + 64 * g);
+    double x[32];
 #pragma unroll
-  for (int mb = 0; mb < VW_MB; ++mb)
+    for (int s = 0; s < 32; ++s) x[s] = vr.get(s);
+    fm_d4 acc[FM_RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rs[mb][i] = 0.0;
-
-  for (int sb = 0; sb < nst; sb += PD) {
+    for (int rt = 0; rt < FM_RT; ++rt) acc[rt] = fm_d4{0.0, 0.0, 0.0, 0.0};
+    fm_apply(op, lane, x, acc);
+    double r2 = 0.0;
 #pragma unroll
-    for (int p = 0; p < PD; ++p) {
-      const int st = sb + p;
-      if (st < nst) {
-        const int cur = st & 1;
+    for (int rt = 0; rt < FM_RT; ++rt)
 #pragma unroll
-        for (int half = 0; half < VW_NS / 16; ++half) {
-          f32x4 acc[VW_MB];
-#pragma unroll
-          for (int mb = 0; mb < VW_MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-              const u32x4 bx = *reinterpret_cast<const u32x4 *>(&bt[cur][q][16 * half + m][32 * ks + 8 * kq]);
-              const bf16x8 bv = __builtin_bit_cast(bf16x8, bx);
-#pragma unroll
-              for (int mb = 0; mb < VW_MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb][ks], bv, acc[mb], 0, 0, 0);
-            }
-          }
-#pragma unroll
-          for (int mb = 0; mb < VW_MB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rs[mb][i] = fma(double(acc[mb][i]), double(acc[mb][i]), rs[mb][i]);
-        }
-        // stage st + 1 (loaded PD - 1 stages ago) into the other buffer, whose
-        // readers finished before the last barrier; its registers take stage st + 1 + PD
-        const int nxt = (p + 1) % PD;
-        if (st + 1 < nst) {
-          store_stage(sreg[nxt], cur ^ 1);
-          load_stage(sreg[nxt], st + 1 + PD);
-        }
-        __syncthreads();
-      }
-    }
-  }
-  // rs[mb][i]: token 16 mb + 4 (lane / 16) + i, columns = lane % 16 (mod 16):
-  // sum over the 16 lanes of each row of lanes
-#pragma unroll
-  for (int mb = 0; mb < VW_MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      double x = rs[mb][i];
-      x += dpp_f64<0xB1>(x);
-      x += dpp_f64<0x4E>(x);
-      x += dpp_f64<0x141>(x);
-      x += dpp_f64<0x140>(x);
-      rs[mb][i] = x;
-    }
-  if (m == 0) {
-#pragma unroll
-    for (int mb = 0; mb < VW_MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * mb + 4 * kq + i;
-        if (tok < N) a.r2[int64_t(u) * N + tok] = float(rs[mb][i]);
-      }
+      for (int r = 0; r < 4; ++r) r2 = fma(x[4 * rt + r], acc[rt][r], r2);
+    r2 += __shfl_xor(r2, 16);
+    r2 += __shfl_xor(r2, 32);
+    if (g == 0 && j < t1) a.r2[int64_t(u) * N + j] = float(r2);
   }
 }
 
@@ -433,7 +408,7 @@ __global__ __launch_bounds__(256) void k_lap_norm(const LapArgs a) {
 }
 
 struct LapLayout {
-  size_t wt_hi, wt_lo, tM, tZ, rM, rZ, c2, r2, psum, total;
+  size_t gram, tM, tZ, rM, rZ, c2, r2, psum, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -444,8 +419,7 @@ LapLayout lap_layout(int n_layers, int H, int n_kv, int N, int w, int D) {
   const int nh = (R + RPG - 1) / RPG, ntiles = (N + TILE - 1) / TILE, nchunks = (N + P_CHUNK - 1) / P_CHUNK;
   LapLayout L{};
   size_t o = 0;
-  L.wt_hi = o; o = align256(o + size_t(units) * D * HD * 2);
-  L.wt_lo = o; o = align256(o + size_t(units) * D * HD * 2);
+  L.gram = o;  o = align256(o + size_t(units) * GR_KS * HD * HD * 8);
   L.tM = o;    o = align256(o + size_t(units) * R * ntiles * 8);
   L.tZ = o;    o = align256(o + size_t(units) * R * ntiles * 8);
   L.rM = o;    o = align256(o + size_t(units) * R * 8);
@@ -511,8 +485,7 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   a.nchunks = (N + P_CHUNK - 1) / P_CHUNK;
   a.scale = scale;
   a.score = score;
-  a.wt_hi = reinterpret_cast<uint16_t *>(base + L.wt_hi);
-  a.wt_lo = reinterpret_cast<uint16_t *>(base + L.wt_lo);
+  a.gram = reinterpret_cast<double *>(base + L.gram);
   a.tM = reinterpret_cast<double *>(base + L.tM);
   a.tZ = reinterpret_cast<double *>(base + L.tZ);
   a.rM = reinterpret_cast<double *>(base + L.rM);
@@ -526,7 +499,7 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   auto mark = [&](int i) { return marks ? hipEventRecord(marks[i], st) : hipSuccess; };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lap_wprep, dim3(D / 64, HD / 64, units), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_lap_gram, dim3(units, GR_KS), dim3(GR_NT), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
   const dim3 wgrid(a.ntiles, a.nh, units);
   if ((e = window_pass(a, wgrid, st, 1)) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
@@ -534,7 +507,7 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   hipLaunchKernelGGL(k_lap_rowfin, dim3((n_rows + 255) / 256), dim3(256), 0, st, a, n_rows);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
   if ((e = window_pass(a, wgrid, st, 2)) != hipSuccess || (e = mark(4)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lap_vw, dim3((N + VW_TOK - 1) / VW_TOK, units), dim3(VW_NT), 0, st, a);
+  hipLaunchKernelGGL(k_lap_r2, dim3((N + R2_TOK - 1) / R2_TOK, units), dim3(R2_NT), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_lap_p, dim3(a.nchunks, units), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess) return e;

@@ -20,23 +20,15 @@
 // When one chunk covers every scope (chunk >= capacity) the score kernel's
 // workgroup picks and folds itself and the second kernel is not launched.
 //
-// Index permutation. The contraction index b and the output row a are both
-// permuted so that every lane reads 64 contiguous bytes of its key row and of
-// its value row: at MFMA step s the lane group g = lane / 16 carries
-// b = 32 g + s, and output row i of row tile rt is a = 32 (i % 4) + 4 rt + i / 4,
-// so the accumulator rows a lane holds (i = g + 4 r) are a = 32 g + 4 rt + r.
-#include "kvc_device.h"
+// The contraction runs on the float64 MFMA operator of kvc_f64mfma.h (the
+// model -A in LDS; each lane's B values and accumulator rows are the same 32
+// elements of its key and value rows).
+#include "kvc_f64mfma.h"
 #include "kvc_kernels.h"
 
 namespace kvc {
 namespace {
 
-typedef double d4 __attribute__((ext_vector_type(4)));
-typedef double d2 __attribute__((ext_vector_type(2)));
-
-constexpr int ME_TILE = 16;     // tokens per wave tile (MFMA N)
-constexpr int ME_RT = 8;        // 16-row tiles of the 128 output rows
-constexpr int ME_S2 = 16;       // pairs of MFMA k-steps (32 steps of 4)
 constexpr int ME_SWG = 512;     // score workgroup: 8 waves, two per SIMD, so one wave's
                                 // per-tile vector work overlaps the other's MFMAs
 constexpr int ME_SWAVES = ME_SWG / 64;
@@ -44,42 +36,16 @@ constexpr int ME_WAVES = WG / 64;
 constexpr int ME_CPAD = 36;     // c is stored [g][36]: the four lane groups read distinct banks
 
 struct MeLds {
-  d2 a[ME_S2][ME_RT][64];       // -A fragments, swizzled lane position (128 KB)
+  FmOperator op;                // -A (128 KB)
   double c[4 * ME_CPAD];        // c = v_bar - A k_bar (zero when n_e = 0), row a at (a/32)*36 + a%32
   double best[ME_SWAVES];
   int best_pos[ME_SWAVES], best_slot[ME_SWAVES];
 };
 
-// Swizzled position of lane l's fragment pair for pair-step s2: a bijection on
-// 0..63 that keeps each 16-lane phase of a read on distinct 16-byte bank groups
-// and spreads the staging writes.
-__device__ __forceinline__ int me_swz(int s2, int l) { return l ^ (((s2 >> 1) ^ ((l >> 4) << 2)) & 15); }
-
 // (score, pos) ascending; +inf for no candidate.
 __device__ __forceinline__ bool me_less(double s, int p, double s2, int p2) {
   return s < s2 || (s == s2 && p < p2);
 }
-
-template <typename T>
-struct MeRow;
-template <>
-struct MeRow<bf16_t> {
-  u32x4 w[4];   // 32 bf16
-  __device__ __forceinline__ void load(const char *base) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = ld16(base + 16 * q);
-  }
-  __device__ __forceinline__ double get(int e) const { return double(ElemTraits<bf16_t>::get(w[e >> 3], e & 7)); }
-};
-template <>
-struct MeRow<float> {
-  u32x4 w[8];   // 32 fp32
-  __device__ __forceinline__ void load(const char *base) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) w[q] = ld16(base + 16 * q);
-  }
-  __device__ __forceinline__ double get(int e) const { return double(ElemTraits<float>::get(w[e >> 2], e & 3)); }
-};
 
 // Algorithm 1 steps 12-13 for evicted slot e of scope sc (fp32 sums, one fused
 // multiply-add per element): s_k += k_e, s_v += v_e, S += v_e k_e^T, by NT threads.
@@ -146,7 +112,7 @@ __global__ __launch_bounds__(ME_SWG, 1) void k_me_score(MomentEvictArgs p, int i
       s4[it] = *reinterpret_cast<const float4 *>(S + (e4 >> 5) * HD + (e4 & 31) * 4);
     }
     // this thread's four columns are the same in every iteration
-    const int b0 = (tid & 31) * 4, g = b0 >> 5;
+    const int b0 = (tid & 31) * 4;
     float4 sk4 = *reinterpret_cast<const float4 *>(sk + b0);
     const double inv_n = n > 0 ? 1.0 / double(n) : 0.0;
     const double f = -p.scale * inv_n;
@@ -154,16 +120,13 @@ __global__ __launch_bounds__(ME_SWG, 1) void k_me_score(MomentEvictArgs p, int i
     for (int it = 0; it < PER; ++it) {
       const int a = (tid + it * ME_SWG) >> 5;
       const double sva = double(sv[a]) * inv_n;
-      const int i = (a >> 5) + 4 * (a & 3), rt = (a & 31) >> 2;
-      const int l = i + 16 * g;
       double dot = 0.0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int s = (b0 + t) & 31;
         const double skb = t == 0 ? sk4.x : t == 1 ? sk4.y : t == 2 ? sk4.z : sk4.w;
         const double sab = t == 0 ? s4[it].x : t == 1 ? s4[it].y : t == 2 ? s4[it].z : s4[it].w;
         const double an = n > 0 ? f * (sab - sva * skb) : 0.0;   // -A[a][b]
-        sh.a[s >> 1][rt][me_swz(s >> 1, l)][s & 1] = an;
+        fm_put(sh.op, a, b0 + t, an);
         dot = fma(an, skb * inv_n, dot);
       }
       // the 32 lanes of one row a hold its 128 columns: c[a] = v_bar[a] + sum_b (-A[a][b]) k_bar[b]
@@ -182,43 +145,30 @@ __global__ __launch_bounds__(ME_SWG, 1) void k_me_score(MomentEvictArgs p, int i
   const double *cg = sh.c + g * ME_CPAD;
   double best = __builtin_inf();
   int best_pos = 0x7fffffff, best_slot = -1;
-  const int n_tiles = (j_end - j_begin + ME_TILE - 1) / ME_TILE;
+  const int n_tiles = (j_end - j_begin + FM_TILE - 1) / FM_TILE;
   for (int tile = wave; tile < n_tiles; tile += ME_SWAVES) {
-    const int j = j_begin + tile * ME_TILE + jl;
+    const int j = j_begin + tile * FM_TILE + jl;
     const int jc = min(j, j_end - 1);
     const int64_t slot = int64_t(sc) * p.capacity + jc;
     const float al_t = p.alpha[slot];
     const int ps_t = p.pos[slot];
     const int ev_t = iter > 0 ? p.evict[slot] : 0;
     const int64_t off = ((row0 + jc) * HD + 32 * g) * ES;
-    MeRow<T> kr, vr;
+    FmRow<T> kr, vr;
     kr.load(kb + off);
     vr.load(vb + off);
     double x[32];
 #pragma unroll
     for (int s = 0; s < 32; ++s) x[s] = kr.get(s);
-    d4 acc[ME_RT];
+    fm_d4 acc[FM_RT];
 #pragma unroll
-    for (int rt = 0; rt < ME_RT; ++rt)
+    for (int rt = 0; rt < FM_RT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[rt][r] = vr.get(4 * rt + r) - cg[4 * rt + r];
-#pragma unroll
-    for (int s2 = 0; s2 < ME_S2; ++s2) {
-      d2 af[ME_RT];
-      const int pl = me_swz(s2, lane);
-#pragma unroll
-      for (int rt = 0; rt < ME_RT; ++rt) af[rt] = sh.a[s2][rt][pl];
-#pragma unroll
-      for (int rt = 0; rt < ME_RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rt].x, x[2 * s2], acc[rt], 0, 0, 0);
-#pragma unroll
-      for (int rt = 0; rt < ME_RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[rt].y, x[2 * s2 + 1], acc[rt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    fm_apply(sh.op, lane, x, acc);
     double ss = 0.0;
 #pragma unroll
-    for (int rt = 0; rt < ME_RT; ++rt)
+    for (int rt = 0; rt < FM_RT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) ss = fma(acc[rt][r], acc[rt][r], ss);
     ss += __shfl_xor(ss, 16);

@@ -258,14 +258,14 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
  *         window row j sits at position N - w + j and A_g[j, :] is the causal
  *         softmax of scale * q_{g,j} . k_i over i <= N - w + j;
  *   r_i = || v_i W_bar_h ||_2, W_bar_h = sum_{g in group(h)} W_O^g (d x D),
- *         computed on MFMA;
+ *         computed as r_i^2 = v_i M_h v_i^T with M_h = W_bar_h W_bar_h^T
+ *         (d x d), both on float64 MFMA;
  *   score[l][h][i] = c_i r_i / sum_{h', i'} c_{i'} r_{i'} over layer l.
  * q_win: [n_layers][H][w][d] bf16; k, v: [n_layers][n_kv][N][d] bf16;
  * w_o: [n_layers][H][d][D] bf16; score: [n_layers][n_kv][N] fp32.
  * Shapes: d = 128, G = H / n_kv in {1, 2, 4, 8}, G*w a multiple of 8,
- * 0 < w <= N, D a multiple of 64 (KVC_ERR_UNSUPPORTED otherwise). Logits are
- * float64; W_bar is summed in float64 and split into bf16 hi + lo for the
- * MFMA, whose fp32 accumulators feed float64 sums of squares.
+ * 0 < w <= N, D a multiple of 64 (KVC_ERR_UNSUPPORTED otherwise). Logits,
+ * W_bar, M_h and r_i^2 are float64.
  * The model-wide Top-K (key design 3) is kvc_select_evict on score with one
  * scope of n_layers*n_kv*N entries and budget K. */
 int32_t kvc_laprox_score(const void *q_win, const void *k, const void *v, const void *w_o,
