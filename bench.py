@@ -211,8 +211,8 @@ def run_laprox(args):
         stages[name] = {"ms": float(ms)}
     for name in ("window_pass1", "window_pass2"):
         ach = logit_flops / (stages[name]["ms"] / 1e3) / 1e12
-        stages[name].update(bound="alu", achieved=ach, peak=rf.MI355X_FP64_VALU_TFLOPS, unit="TFLOP/s",
-                            frac=ach / rf.MI355X_FP64_VALU_TFLOPS, flops="2 R N d per unit, float64 FMA")
+        stages[name].update(bound="mfma", achieved=ach, peak=rf.MI355X_FP64_TFLOPS, unit="TFLOP/s",
+                            frac=ach / rf.MI355X_FP64_TFLOPS, flops="2 R N d per unit, float64 MFMA")
     for name, fl, what in (("gram", gram_flops, "2 d^2 D per unit (W_bar W_bar^T), float64 MFMA"),
                            ("value_norms", r2_flops, "(2 d^2 + 2 d) N per unit (v M v^T), float64 MFMA")):
         ach = fl / (stages[name]["ms"] / 1e3) / 1e12
@@ -224,7 +224,7 @@ def run_laprox(args):
         "metric": "LaProx prefill: tokens scored/sec (model-wide scores of every layer and KV head)",
         "value": units * lw.N / (ms_per_call / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_call, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16 inputs; f64 logits; f64 MFMA value norms", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16 inputs; f64 MFMA logits and value norms", "data": "synthetic",
         "config": {"workload": lw.name, "layers": lw.n_layers, "q_heads": lw.H, "kv_heads": lw.n_kv,
                    "head_dim": lw.d, "hidden": lw.D, "prompt": lw.N, "window": lw.w,
                    "keep_total": lw.keep_total, "parallelism": "none (1 GPU)"},

@@ -60,6 +60,33 @@ __device__ __forceinline__ void fm_apply(const FmOperator &op, int lane, const d
   }
 }
 
+// The transposed use: X as the B operand, the tokens' rows as the A operand.
+// D[i][j] = sum_b y_i[b] X[16 ct + j][b] lands in lane l as
+// acc[ct][r] = (X y_{l / 16 + 4 r})[16 ct + l % 16]: each lane holds 8 rows of X
+// (one per column tile ct) for 4 tokens, and its A values x[s] = y_{l % 16}[32 g + s].
+__device__ __forceinline__ void fm_put_t(FmOperator &op, int a, int b, double v) {
+  const int ct = a >> 4, j = a & 15, g = b >> 5, s = b & 31;
+  op.a[s >> 1][ct][fm_swz(s >> 1, j + 16 * g)][s & 1] = v;
+}
+
+__device__ __forceinline__ void fm_apply_t(const FmOperator &op, int lane, const double (&x)[32],
+                                           fm_d4 (&acc)[FM_RT]) {
+#pragma unroll
+  for (int s2 = 0; s2 < FM_S2; ++s2) {
+    fm_d2 bf[FM_RT];
+    const int pl = fm_swz(s2, lane);
+#pragma unroll
+    for (int ct = 0; ct < FM_RT; ++ct) bf[ct] = op.a[s2][ct][pl];
+#pragma unroll
+    for (int ct = 0; ct < FM_RT; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[2 * s2], bf[ct].x, acc[ct], 0, 0, 0);
+#pragma unroll
+    for (int ct = 0; ct < FM_RT; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[2 * s2 + 1], bf[ct].y, acc[ct], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // 32 consecutive elements of a row in the cache dtype (64 or 128 bytes).
 template <typename T>
 struct FmRow;

@@ -10,13 +10,14 @@
 //                  W_bar = sum of the group's W_O^g blocks summed in float64
 //                  while its column blocks are staged in LDS; two halves of D
 //                  per unit, summed when M is staged.
-//   k_lap_window<1> per token tile: float64 logits of 8 rows per wave
-//                  (lane-permuted transposed reduction), per-row running max
-//                  and sum of exp -> partials per tile.
-//   k_lap_rowfin   combines the tile partials of every row (fixed order).
+//   k_lap_window<1> float64 logits of the block's 128 window rows against 16
+//                  keys at a time on v_mfma_f64_16x16x4 (tau Q as the operator
+//                  in LDS), per-row running max and sum of exp -> partials per
+//                  2048-token workgroup.
+//   k_lap_rowfin   combines the workgroup partials of every row (fixed order).
 //   k_lap_window<2> recomputes the logits; A = exp(l - M) / Z; the group mean
-//                  over the G heads of each window row by DPP sums; its square
-//                  summed over the rows of the workgroup -> c^2 partials.
+//                  over the G heads of each window row by DPP sums over adjacent
+//                  lanes; its square summed over the block's rows -> c^2.
 //   k_lap_r2       r_i^2 = ||v_i W_bar||^2 = v_i M v_i^T (the Gram identity:
 //                  a d x d instead of a d x D contraction per token) on the
 //                  float64 MFMA operator of kvc_f64mfma.h, M staged in LDS.
@@ -30,16 +31,10 @@ namespace kvc {
 namespace {
 
 // ---------------------------------------------------------------- geometry
-constexpr int LW = 8;               // waves per window workgroup
-constexpr int LNT = 64 * LW;        // window workgroup threads
-constexpr int RPW = 8;              // window rows per wave
-constexpr int RPG = LW * RPW;       // window rows per workgroup (64)
-constexpr int TILE = 1024;          // tokens per window workgroup
-constexpr int LLPT = 16;            // lanes per bf16 row (8 elements each)
-constexpr int LTPI = 4;             // tokens per wave iteration
-constexpr int LUNR = 4;             // iterations per sub-chunk (16 tokens)
-constexpr int LCH = LTPI * LUNR;
-constexpr int LPF = 2;              // sub-chunks of loads in flight
+constexpr int WM_NT = 512;          // window workgroup: 8 waves, two per SIMD
+constexpr int WM_TILE = 2048;       // tokens per window workgroup (16 tiles per wave)
+constexpr int WM_ROWS = 128;        // window rows per operator block
+constexpr int RPW = 8;              // the row count R = G w must be a multiple of this
 constexpr int RB = HD * 2;          // bytes per bf16 row
 
 constexpr int GR_KS = 2;            // halves of D per unit in the Gram kernel
@@ -168,135 +163,138 @@ __device__ __forceinline__ float block_sum(float x) {
 template <int G>
 __device__ __forceinline__ constexpr int ilog2c() { return G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0; }
 
-// PASS 1: row max / sum partials per tile. PASS 2: c^2 partials per token.
-// grid (ntiles, nh, units), 512 threads. Wave w of workgroup half `hf` owns
-// rows 64 hf + 8 w .. + 7 (row = j G + g); lanes hold them in the permuted
-// order of preduce and end with row perm_head(lane % 16).
+// Window passes on the float64 MFMA, transposed: tau Q (the block's 128 window
+// rows x d) is the operator in LDS as B fragments and 16 keys at a time are the
+// A operand, so lane l ends with the logits of rows 16 ct + l % 16 (ct = 0..7)
+// for tokens l / 16 + 4 r (r = 0..3) of the tile: 8 rows x 4 tokens per lane.
+// grid (ntiles, nh, units), 512 threads, wave w takes tiles w, w + 8, ...
+//   PASS 1: per row, the running max and sum of e^{l - max} over the lane's
+//           tokens; combined over the lane groups and waves -> one partial per
+//           (row, workgroup).
+//   PASS 2: A = e^{l - M} / Z; the mean over the G heads of a window row is a
+//           sum over G adjacent lanes (rows j G + g sit in consecutive lanes);
+//           its square summed over the block's window rows -> c^2 per token.
+// Rows past R (the last block) have a zero operator row and are masked.
 template <int G, int PASS>
-__global__ __launch_bounds__(LNT, 1) void k_lap_window(const LapArgs a) {
-  __shared__ float part[LW][TILE];
+__global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
+  __shared__ FmOperator qop;
+  __shared__ double redm[WM_NT / 64][128], redz[WM_NT / 64][128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x, hf = blockIdx.y, u = blockIdx.z;
+  const int tile = blockIdx.x, hb = blockIdx.y, u = blockIdx.z;
   const int l = u / a.n_kv, h = u % a.n_kv;
-  const int N = a.N, w = a.w;
-  const int row0 = hf * RPG + wave * RPW;
-  const bool active = row0 < a.R;      // R is a multiple of 8: a wave is all in or all out
-  const int cb = lane & (LLPT - 1), tg = lane >> 4;
-  const int myr = perm_head<LLPT, RPW>(cb);
-  const int rl = row0 + myr;           // the lane's reduced row
-  const int jl = rl / G;
-  const int plim = N - w + jl;         // last key the lane's row attends to
-  const int t0 = tile * TILE, t1 = min(N, t0 + TILE);
-
-  double qf[RPW][8];
+  const int N = a.N, w = a.w, R = a.R, rb = hb * 128;
+  const int t0 = tile * WM_TILE, t1 = min(N, t0 + WM_TILE);
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q);
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int row = active ? row0 + (i ^ myr) : 0;
-      const int j = row / G, g = row - (row / G) * G;
-      const int64_t head = int64_t(l) * a.H + h * G + g;
-      const uint16_t *qr = qb + (head * w + j) * HD + cb * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[i][e] = double(bf16_to_f32(qr[e])) * a.scale;
+    for (int e = tid; e < HD * HD; e += WM_NT) {
+      const int r = e >> 7, b = e & 127, row = rb + r;
+      double v = 0.0;
+      if (row < R) {
+        const int j = row / G, g = row - j * G;
+        const int64_t head = int64_t(l) * a.H + h * G + g;
+        v = double(bf16_to_f32(qb[(head * w + j) * HD + b])) * a.scale;
+      }
+      fm_put_t(qop, r, b, v);
     }
   }
-  double Mr = 0.0;
-  float izr = 0.f;
-  if (PASS == 2 && active) {
-    Mr = a.rM[int64_t(u) * a.R + rl];
-    const double Z = a.rZ[int64_t(u) * a.R + rl];
-    izr = Z > 0.0 ? float(1.0 / Z) : 0.f;
+  const int jl = lane & 15, tq = lane >> 4;
+  int plim[FM_RT];         // last key each of the lane's rows attends to (-1: not a row)
+  double Mrow[FM_RT], Zrow[FM_RT];
+  float iz[FM_RT];
+#pragma unroll
+  for (int ct = 0; ct < FM_RT; ++ct) {
+    const int row = rb + 16 * ct + jl;
+    plim[ct] = row < R ? N - w + row / G : -1;
+    if (PASS == 1) {
+      Mrow[ct] = -INFINITY;
+      Zrow[ct] = 0.0;
+    } else {
+      Mrow[ct] = row < R ? a.rM[int64_t(u) * R + row] : 0.0;
+      const double Z = row < R ? a.rZ[int64_t(u) * R + row] : 0.0;
+      iz[ct] = Z > 0.0 ? float(1.0 / Z) : 0.f;
+    }
   }
-  double Mrun = -INFINITY, Zrun = 0.0;
-  const int dup = lane & 1;
+  __syncthreads();
 
   const char *Kb = a.k + int64_t(u) * N * RB;
-  const int nsub = (t1 - t0 + LCH - 1) / LCH;
-  u32x4 kr[LPF][LUNR];
-  auto issue = [&](u32x4 (&r)[LUNR], int c) {
+  const int n16 = (t1 - t0 + FM_TILE - 1) / FM_TILE;
+  for (int t = wave; t < n16; t += WM_NT / 64) {
+    const int tb = t0 + t * FM_TILE;
+    FmRow<bf16_t> kr;
+    kr.load(Kb + int64_t(min(tb + jl, t1 - 1)) * RB + 64 * tq);
+    double x[32];
 #pragma unroll
-    for (int it = 0; it < LUNR; ++it) {
-      const int tok = min(t0 + c * LCH + it * LTPI + tg, N - 1);
-      r[it] = ld16(Kb + int64_t(tok) * RB + 16 * cb);
-    }
-  };
-  if (active) {
+    for (int s = 0; s < 32; ++s) x[s] = kr.get(s);
+    fm_d4 acc[FM_RT];
 #pragma unroll
-    for (int s = 0; s < LPF; ++s) issue(kr[s], s);
-  }
-  for (int base = 0; active && base < nsub; base += LPF) {
+    for (int ct = 0; ct < FM_RT; ++ct) acc[ct] = fm_d4{0.0, 0.0, 0.0, 0.0};
+    fm_apply_t(qop, lane, x, acc);
+    if (PASS == 1) {
 #pragma unroll
-    for (int s = 0; s < LPF; ++s) {
-      const int c = base + s;
-      if (c < nsub) {
-        double lg[LUNR];
+      for (int ct = 0; ct < FM_RT; ++ct) {
+        double lg[4], mx = -INFINITY;
 #pragma unroll
-        for (int it = 0; it < LUNR; ++it) {
-          double acc[RPW];
-#pragma unroll
-          for (int i = 0; i < RPW; ++i) acc[i] = 0.0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const double ke = double(ElemTraits<bf16_t>::get(kr[s][it], e));
-#pragma unroll
-            for (int i = 0; i < RPW; ++i) acc[i] = fma(qf[i][e], ke, acc[i]);
-          }
-          lg[it] = preduce<LLPT, RPW, 0>(acc);
-          const int tok = t0 + c * LCH + it * LTPI + tg;
-          if (tok >= t1 || tok > plim) lg[it] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int tok = tb + tq + 4 * r;
+          lg[r] = (tok < t1 && tok <= plim[ct]) ? acc[ct][r] : -INFINITY;
+          mx = fmax(mx, lg[r]);
         }
-        if (PASS == 1) {
-          // lane `dup` takes iterations dup and dup + 2 of its row
-          const double xa = lg[dup], xb = lg[dup + 2];
-          const double Mn = fmax(Mrun, fmax(xa, xb));
-          if (Mn > Mrun) {
-            if (Mrun > -INFINITY) Zrun *= exp(Mrun - Mn);
-            Mrun = Mn;
-          }
-          Zrun += double(exp_split(xa - Mrun)) + double(exp_split(xb - Mrun));
-        } else {
-#pragma unroll
-          for (int it = 0; it < LUNR; ++it) {
-            const float A = exp_split(lg[it] - Mr) * izr;
-            // mean over the G heads of the window row: blocks of 2G lanes, each head twice
-            const float ab = block_sum<0, ilog2c<G>() + 1>(A) * (1.f / float(2 * G));
-            const float sq = block_sum<ilog2c<G>() + 1, 4>(ab * ab) * (1.f / float(2 * G));
-            if (cb == 0) part[wave][c * LCH + it * LTPI + tg] = sq;
-          }
+        if (mx > Mrow[ct]) {
+          if (Mrow[ct] > -INFINITY) Zrow[ct] *= exp(Mrow[ct] - mx);
+          Mrow[ct] = mx;
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Zrow[ct] += double(exp_split(lg[r] - Mrow[ct]));
       }
-      issue(kr[s], base + s + LPF);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tb + tq + 4 * r;
+        float sq = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < FM_RT; ++ct) {
+          const float A = (tok < t1 && tok <= plim[ct]) ? exp_split(acc[ct][r] - Mrow[ct]) * iz[ct] : 0.f;
+          const float mean = block_sum<0, ilog2c<G>()>(A) * (1.f / float(G));
+          sq += mean * mean;
+        }
+        // each group of G lanes holds its window rows' means: sum once over the 16 / G groups
+        const float c2 = block_sum<ilog2c<G>(), 4>(sq);
+        if (jl == 0 && tok < t1) a.c2[(int64_t(u) * a.nh + hb) * N + tok] = c2;
+      }
     }
   }
 
   if (PASS == 1) {
-    // combine the lanes of each row: dup pair and the four token groups
+    // rows 16 ct + jl: combine the four token groups of the wave, then the waves
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      if (o != 1 && o != 16 && o != 32) continue;
-      const double M2 = __shfl_xor(Mrun, o), Z2 = __shfl_xor(Zrun, o);
-      const double Mn = fmax(Mrun, M2);
-      double Z = 0.0;
-      if (Mrun > -INFINITY) Z += Zrun * exp(Mrun - Mn);
-      if (M2 > -INFINITY) Z += Z2 * exp(M2 - Mn);
-      Mrun = Mn;
-      Zrun = Z;
+    for (int ct = 0; ct < FM_RT; ++ct) {
+#pragma unroll
+      for (int o = 16; o < 64; o <<= 1) {
+        const double M2 = __shfl_xor(Mrow[ct], o), Z2 = __shfl_xor(Zrow[ct], o);
+        const double Mn = fmax(Mrow[ct], M2);
+        double Z = 0.0;
+        if (Mrow[ct] > -INFINITY) Z += Zrow[ct] * exp(Mrow[ct] - Mn);
+        if (M2 > -INFINITY) Z += Z2 * exp(M2 - Mn);
+        Mrow[ct] = Mn;
+        Zrow[ct] = Z;
+      }
+      if (tq == 0) {
+        redm[wave][16 * ct + jl] = Mrow[ct];
+        redz[wave][16 * ct + jl] = Zrow[ct];
+      }
     }
-    if (active && tg == 0 && dup == 0) {
-      const int64_t o = (int64_t(u) * a.R + rl) * a.ntiles + tile;
-      a.tM[o] = Mrun;
-      a.tZ[o] = Zrun;
-    }
-  } else {
     __syncthreads();
-    const int nt = t1 - t0;
-    for (int t = tid; t < nt; t += LNT) {
-      double s = 0.0;
+    if (tid < 128 && rb + tid < R) {
+      double M = -INFINITY;
 #pragma unroll
-      for (int wv = 0; wv < LW; ++wv)
-        if (hf * RPG + wv * RPW < a.R) s += double(part[wv][t]);
-      a.c2[(int64_t(u) * a.nh + hf) * N + t0 + t] = float(s);
+      for (int wv = 0; wv < WM_NT / 64; ++wv) M = fmax(M, redm[wv][tid]);
+      double Z = 0.0;
+#pragma unroll
+      for (int wv = 0; wv < WM_NT / 64; ++wv)
+        if (redm[wv][tid] > -INFINITY) Z += redz[wv][tid] * exp(redm[wv][tid] - M);
+      const int64_t o = (int64_t(u) * R + rb + tid) * a.ntiles + tile;
+      a.tM[o] = M;
+      a.tZ[o] = Z;
     }
   }
 }
@@ -416,7 +414,7 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 LapLayout lap_layout(int n_layers, int H, int n_kv, int N, int w, int D) {
   const int64_t units = int64_t(n_layers) * n_kv;
   const int G = H / n_kv, R = G * w;
-  const int nh = (R + RPG - 1) / RPG, ntiles = (N + TILE - 1) / TILE, nchunks = (N + P_CHUNK - 1) / P_CHUNK;
+  const int nh = (R + WM_ROWS - 1) / WM_ROWS, ntiles = (N + WM_TILE - 1) / WM_TILE, nchunks = (N + P_CHUNK - 1) / P_CHUNK;
   LapLayout L{};
   size_t o = 0;
   L.gram = o;  o = align256(o + size_t(units) * GR_KS * HD * HD * 8);
@@ -433,8 +431,8 @@ LapLayout lap_layout(int n_layers, int H, int n_kv, int N, int w, int D) {
 
 template <int G>
 hipError_t launch_window(const LapArgs &a, dim3 grid, hipStream_t st, int pass) {
-  if (pass == 1) hipLaunchKernelGGL((k_lap_window<G, 1>), grid, dim3(LNT), 0, st, a);
-  else hipLaunchKernelGGL((k_lap_window<G, 2>), grid, dim3(LNT), 0, st, a);
+  if (pass == 1) hipLaunchKernelGGL((k_lap_window<G, 1>), grid, dim3(WM_NT), 0, st, a);
+  else hipLaunchKernelGGL((k_lap_window<G, 2>), grid, dim3(WM_NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -480,8 +478,8 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   a.D = D;
   a.G = H / n_kv;
   a.R = a.G * w;
-  a.nh = (a.R + RPG - 1) / RPG;
-  a.ntiles = (N + TILE - 1) / TILE;
+  a.nh = (a.R + WM_ROWS - 1) / WM_ROWS;
+  a.ntiles = (N + WM_TILE - 1) / WM_TILE;
   a.nchunks = (N + P_CHUNK - 1) / P_CHUNK;
   a.scale = scale;
   a.score = score;
