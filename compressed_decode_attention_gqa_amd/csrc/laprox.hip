@@ -163,36 +163,50 @@ __device__ __forceinline__ float block_sum(float x) {
 template <int G>
 __device__ __forceinline__ constexpr int ilog2c() { return G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0; }
 
-// Window passes on the float64 MFMA, transposed: tau Q (the block's 128 window
-// rows x d) is the operator in LDS as B fragments and 16 keys at a time are the
-// A operand, so lane l ends with the logits of rows 16 ct + l % 16 (ct = 0..7)
-// for tokens l / 16 + 4 r (r = 0..3) of the tile: 8 rows x 4 tokens per lane.
+// Window passes on the float64 MFMA, transposed: tau Q (a block of window rows
+// x d) is the operator in LDS as B fragments and 16 keys at a time are the A
+// operand, so lane l ends with the logits of operator rows 16 ct + l % 16
+// (ct = 0..7) for tokens l / 16 + 4 r (r = 0..3) of the tile. The operator rows
+// are head-major: row 16 ct + jl holds head g = ct / (8 / G) of window row
+// jj = hb 128 / G + (ct % (8 / G)) 16 + jl, so the G heads of a window row sit
+// in one lane and the group mean is an in-lane sum.
 // grid (ntiles, nh, units), 512 threads, wave w takes tiles w, w + 8, ...
 //   PASS 1: per row, the running max and sum of e^{l - max} over the lane's
-//           tokens; combined over the lane groups and waves -> one partial per
-//           (row, workgroup).
-//   PASS 2: A = e^{l - M} / Z; the mean over the G heads of a window row is a
-//           sum over G adjacent lanes (rows j G + g sit in consecutive lanes);
-//           its square summed over the block's window rows -> c^2 per token.
-// Rows past R (the last block) have a zero operator row and are masked.
+//           tokens (plain fp32 exp of the float64 difference, summed per tile
+//           in fp32 and across tiles in float64); combined over the lane groups
+//           and waves -> one partial per (row, workgroup).
+//   PASS 2: A = e^{l - M} / Z (split exp), the mean over the G heads, its square
+//           summed over the block's window rows -> c^2 per token.
+// Window rows past w have a zero operator row and are masked; tiles wholly
+// before the causal window and inside the chunk skip the per-logit mask.
+template <int G>
+__device__ __forceinline__ int win_row(int hb, int ct, int jl, int *jj) {
+  constexpr int CPG = 8 / G;          // column tiles per head
+  const int g = ct / CPG;
+  *jj = hb * (128 / G) + (ct % CPG) * 16 + jl;
+  return g;
+}
+
 template <int G, int PASS>
 __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
   __shared__ FmOperator qop;
   __shared__ double redm[WM_NT / 64][128], redz[WM_NT / 64][128];
+  constexpr int CPG = 8 / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x, hb = blockIdx.y, u = blockIdx.z;
   const int l = u / a.n_kv, h = u % a.n_kv;
-  const int N = a.N, w = a.w, R = a.R, rb = hb * 128;
+  const int N = a.N, w = a.w, R = a.R;
   const int t0 = tile * WM_TILE, t1 = min(N, t0 + WM_TILE);
   {
     const uint16_t *qb = reinterpret_cast<const uint16_t *>(a.q);
     for (int e = tid; e < HD * HD; e += WM_NT) {
-      const int r = e >> 7, b = e & 127, row = rb + r;
+      const int r = e >> 7, b = e & 127;
+      int jj;
+      const int g = win_row<G>(hb, r >> 4, r & 15, &jj);
       double v = 0.0;
-      if (row < R) {
-        const int j = row / G, g = row - j * G;
+      if (jj < w) {
         const int64_t head = int64_t(l) * a.H + h * G + g;
-        v = double(bf16_to_f32(qb[(head * w + j) * HD + b])) * a.scale;
+        v = double(bf16_to_f32(qb[(head * w + jj) * HD + b])) * a.scale;
       }
       fm_put_t(qop, r, b, v);
     }
@@ -203,14 +217,16 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
   float iz[FM_RT];
 #pragma unroll
   for (int ct = 0; ct < FM_RT; ++ct) {
-    const int row = rb + 16 * ct + jl;
-    plim[ct] = row < R ? N - w + row / G : -1;
+    int jj;
+    const int g = win_row<G>(hb, ct, jl, &jj);
+    const int row = jj * G + g;
+    plim[ct] = jj < w ? N - w + jj : -1;
     if (PASS == 1) {
       Mrow[ct] = -INFINITY;
       Zrow[ct] = 0.0;
     } else {
-      Mrow[ct] = row < R ? a.rM[int64_t(u) * R + row] : 0.0;
-      const double Z = row < R ? a.rZ[int64_t(u) * R + row] : 0.0;
+      Mrow[ct] = jj < w ? a.rM[int64_t(u) * R + row] : 0.0;
+      const double Z = jj < w ? a.rZ[int64_t(u) * R + row] : 0.0;
       iz[ct] = Z > 0.0 ? float(1.0 / Z) : 0.f;
     }
   }
@@ -229,22 +245,31 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
 #pragma unroll
     for (int ct = 0; ct < FM_RT; ++ct) acc[ct] = fm_d4{0.0, 0.0, 0.0, 0.0};
     fm_apply_t(qop, lane, x, acc);
-    if (PASS == 1) {
+    // every token of the tile is inside the chunk and before the first window row
+    const bool whole = tb + FM_TILE <= t1 && tb + FM_TILE - 1 <= N - w;
+    if (!whole) {
 #pragma unroll
-      for (int ct = 0; ct < FM_RT; ++ct) {
-        double lg[4], mx = -INFINITY;
+      for (int ct = 0; ct < FM_RT; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = tb + tq + 4 * r;
-          lg[r] = (tok < t1 && tok <= plim[ct]) ? acc[ct][r] : -INFINITY;
-          mx = fmax(mx, lg[r]);
+          if (!(tok < t1 && tok <= plim[ct])) acc[ct][r] = -INFINITY;
         }
+    }
+    if (PASS == 1) {
+#pragma unroll
+      for (int ct = 0; ct < FM_RT; ++ct) {
+        const double mx = fmax(fmax(acc[ct][0], acc[ct][1]), fmax(acc[ct][2], acc[ct][3]));
         if (mx > Mrow[ct]) {
           if (Mrow[ct] > -INFINITY) Zrow[ct] *= exp(Mrow[ct] - mx);
           Mrow[ct] = mx;
         }
+        if (Mrow[ct] > -INFINITY) {
+          float z = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Zrow[ct] += double(exp_split(lg[r] - Mrow[ct]));
+          for (int r = 0; r < 4; ++r) z += expf(float(acc[ct][r] - Mrow[ct]));
+          Zrow[ct] += double(z);
+        }
       }
     } else {
 #pragma unroll
@@ -252,20 +277,25 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
         const int tok = tb + tq + 4 * r;
         float sq = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < FM_RT; ++ct) {
-          const float A = (tok < t1 && tok <= plim[ct]) ? exp_split(acc[ct][r] - Mrow[ct]) * iz[ct] : 0.f;
-          const float mean = block_sum<0, ilog2c<G>()>(A) * (1.f / float(G));
+        for (int c8 = 0; c8 < CPG; ++c8) {
+          float sum = 0.f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const int ct = g * CPG + c8;
+            sum += exp_split(acc[ct][r] - Mrow[ct]) * iz[ct];
+          }
+          const float mean = sum * (1.f / float(G));
           sq += mean * mean;
         }
-        // each group of G lanes holds its window rows' means: sum once over the 16 / G groups
-        const float c2 = block_sum<ilog2c<G>(), 4>(sq);
+        // the 16 lanes of a row of lanes hold 16 window rows each
+        const float c2 = block_sum<0, 4>(sq);
         if (jl == 0 && tok < t1) a.c2[(int64_t(u) * a.nh + hb) * N + tok] = c2;
       }
     }
   }
 
   if (PASS == 1) {
-    // rows 16 ct + jl: combine the four token groups of the wave, then the waves
+    // operator rows 16 ct + jl: combine the four token groups of the wave, then the waves
 #pragma unroll
     for (int ct = 0; ct < FM_RT; ++ct) {
 #pragma unroll
@@ -284,17 +314,21 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
       }
     }
     __syncthreads();
-    if (tid < 128 && rb + tid < R) {
-      double M = -INFINITY;
+    if (tid < 128) {
+      int jj;
+      const int g = win_row<G>(hb, tid >> 4, tid & 15, &jj);
+      if (jj < w) {
+        double M = -INFINITY;
 #pragma unroll
-      for (int wv = 0; wv < WM_NT / 64; ++wv) M = fmax(M, redm[wv][tid]);
-      double Z = 0.0;
+        for (int wv = 0; wv < WM_NT / 64; ++wv) M = fmax(M, redm[wv][tid]);
+        double Z = 0.0;
 #pragma unroll
-      for (int wv = 0; wv < WM_NT / 64; ++wv)
-        if (redm[wv][tid] > -INFINITY) Z += redz[wv][tid] * exp(redm[wv][tid] - M);
-      const int64_t o = (int64_t(u) * R + rb + tid) * a.ntiles + tile;
-      a.tM[o] = M;
-      a.tZ[o] = Z;
+        for (int wv = 0; wv < WM_NT / 64; ++wv)
+          if (redm[wv][tid] > -INFINITY) Z += redz[wv][tid] * exp(redm[wv][tid] - M);
+        const int64_t o = (int64_t(u) * R + jj * G + g) * a.ntiles + tile;
+        a.tM[o] = M;
+        a.tZ[o] = Z;
+      }
     }
   }
 }
@@ -414,7 +448,7 @@ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 LapLayout lap_layout(int n_layers, int H, int n_kv, int N, int w, int D) {
   const int64_t units = int64_t(n_layers) * n_kv;
   const int G = H / n_kv, R = G * w;
-  const int nh = (R + WM_ROWS - 1) / WM_ROWS, ntiles = (N + WM_TILE - 1) / WM_TILE, nchunks = (N + P_CHUNK - 1) / P_CHUNK;
+  const int nh = (w + WM_ROWS / G - 1) / (WM_ROWS / G), ntiles = (N + WM_TILE - 1) / WM_TILE, nchunks = (N + P_CHUNK - 1) / P_CHUNK;
   LapLayout L{};
   size_t o = 0;
   L.gram = o;  o = align256(o + size_t(units) * GR_KS * HD * HD * 8);
@@ -478,7 +512,7 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   a.D = D;
   a.G = H / n_kv;
   a.R = a.G * w;
-  a.nh = (a.R + WM_ROWS - 1) / WM_ROWS;
+  a.nh = (w + WM_ROWS / a.G - 1) / (WM_ROWS / a.G);
   a.ntiles = (N + WM_TILE - 1) / WM_TILE;
   a.nchunks = (N + P_CHUNK - 1) / P_CHUNK;
   a.scale = scale;
