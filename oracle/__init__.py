@@ -14,8 +14,8 @@ the section or equation on it, that gives that definition:
     normalisation-corrected output (Algorithm 1, phase 2).
   * InertiaKV (translated article, arXiv 2609.03515) -- head-averaged
     last-query score and single / cumulative / EMA utility.
-  * KeepKV (reading notes, arXiv 2504.09936) -- vote-weighted attention and
-    ZIP-merging.
+  * KeepKV (reading notes, arXiv 2504.09936) -- vote-weighted attention,
+    ZIP-merging, and prefill compression by greedy all-pairs merging.
   * LaProx notes ("Reformulating KV Cache Eviction Problem for Long-Context
     LLM Inference", arXiv 2605.07234) -- prefill score, per-layer
     normalisation, model-wide top-K.
@@ -29,7 +29,8 @@ itself: textbook attention, duplicated-token brute force, the eviction
 identity o' = (o - A_e v_e)/(1 - A_e), the retained/evicted split, EMA closed
 forms, exhaustive subset enumeration, the centred-covariance identity, the
 moment model's exactness on affine values under an isotropic evicted set, the
-ZIP lossless property and the pages' worked numbers.
+ZIP lossless property (one merge and a whole greedy prefill compression) and
+the pages' worked numbers.
 
 Parity unpinned (these follow from readings of the pages, not from printed
 values or identities): the new-token utility start value (zero), the lazy
@@ -45,6 +46,7 @@ from .moment_correct import corrected_output, evicted_estimates  # noqa: F401
 from .moment_evict import moment_residuals, moment_scores, moment_informed_evict  # noqa: F401
 from .compaction import compact  # noqa: F401
 from .zip_merge import cosine_partner, zip_merge  # noqa: F401
+from .keepkv_prefill import prefill_merge, reference_logits  # noqa: F401
 from .decode_step import ScopeState, StepParams, decode_step  # noqa: F401
 from .laprox import (window_column_norms, value_output_norms, laprox_scores,  # noqa: F401
                      laprox_keep)
