@@ -350,6 +350,24 @@ MomentEvictLayout moment_evict_layout(int n_scopes, int cap) {
   return l;
 }
 
+// ------------------------------------------------------- KeepKV prefill merging
+struct PrefillLayout {
+  size_t status, norm, rowmax, rowarg, cand, total;
+};
+
+PrefillLayout prefill_layout(int n_scopes, int cap) {
+  PrefillLayout l{};
+  const size_t n = size_t(n_scopes) * cap;
+  size_t o = 0;
+  l.status = o; o = align_up(o + 256);
+  l.norm = o;   o = align_up(o + n * 8);
+  l.rowmax = o; o = align_up(o + n * 8);
+  l.rowarg = o; o = align_up(o + n * 4);
+  l.cand = o;   o = align_up(o + n);
+  l.total = o;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -533,6 +551,52 @@ int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const f
   p.cand_slot = at<int32_t>(ws, l.slot);
   p.status = at<int32_t>(ws, l.status);
   if (kvc::launch_moment_evict(p, cache->dtype, p.rounds, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+size_t kvc_keepkv_prefill_workspace_size(const kvc_cache *cache) {
+  if (validate_cache(cache)) return 0;
+  return prefill_layout(cache->n_scopes, cache->capacity).total;
+}
+
+int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge, int32_t budget,
+                                 int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,
+                                 void *ws, size_t ws_bytes, void *stream) {
+  int st = validate_cache(cache);
+  if (st) return st;
+  if (cache->units_per_scope != 1) return KVC_ERR_UNSUPPORTED;
+  if (!cache->votes || !merge || !merge->q || !evict || !ws) return KVC_ERR_ARG;
+  if (!valid_G(merge->G)) return KVC_ERR_UNSUPPORTED;
+  if (!aligned16(merge->q)) return KVC_ERR_ALIGN;
+  if (budget < 0) return KVC_ERR_CAPACITY;
+  const PrefillLayout l = prefill_layout(cache->n_scopes, cache->capacity);
+  if (ws_bytes < l.total) return KVC_ERR_WORKSPACE;
+  kvc::PrefillMergeArgs p{};
+  p.k = static_cast<char *>(cache->k);
+  p.v = static_cast<char *>(cache->v);
+  p.scope_stride = cache->scope_stride;
+  p.votes = cache->votes;
+  p.pos = cache->pos;
+  p.len = cache->len;
+  p.m = cache->m;
+  p.q = static_cast<const char *>(merge->q);
+  p.G = merge->G;
+  p.scale = double(merge->scale);
+  p.eps = merge->eps;
+  p.capacity = cache->capacity;
+  p.n_scopes = cache->n_scopes;
+  p.budget = budget;
+  p.protect_from = protect_from;
+  p.evict = evict;
+  p.pairs = pairs;
+  p.n_merged = n_merged;
+  p.norm = at<double>(ws, l.norm);
+  p.rowmax = at<double>(ws, l.rowmax);
+  p.rowarg = at<int32_t>(ws, l.rowarg);
+  p.cand = at<uint8_t>(ws, l.cand);
+  p.status = at<int32_t>(ws, l.status);
+  if (kvc::launch_prefill_merge(p, cache->dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KVC_ERR_DEVICE;
   return KVC_OK;
 }

@@ -54,6 +54,25 @@ struct MomentEvictArgs {
   int32_t *status;
 };
 
+// KeepKV prefill compression by greedy all-pairs ZIP merging (per-KV-head scopes).
+struct PrefillMergeArgs {
+  char *k, *v;
+  int64_t scope_stride;
+  int32_t *votes, *pos, *len;
+  float *m;
+  const char *q;            // [n_scopes][G][head_dim] in the cache dtype
+  int32_t G;
+  double scale;
+  float eps;
+  int32_t capacity, n_scopes, budget, protect_from;
+  uint8_t *evict;
+  int32_t *pairs, *n_merged;
+  double *norm, *rowmax;    // [n_scopes][capacity]
+  int32_t *rowarg;          // [n_scopes][capacity]
+  uint8_t *cand;            // [n_scopes][capacity]
+  int32_t *status;
+};
+
 size_t wide_state_bytes();
 // One scope of more than 2^20 keys (len = NULL): a device-wide radix select.
 hipError_t launch_select_wide(const float *key, const int32_t *pos, int cap, int budget, uint8_t *evict,
@@ -65,6 +84,7 @@ hipError_t launch_moment_update_mfma(const CacheArgs &c, const uint8_t *evict, i
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st);
 hipError_t launch_moment_correct(const MomentArgs &m, int n_units, const void *q, int dtype, int G, double scale,
                                  const float *f_R, const float *lse_R, float *out, hipStream_t st);
+hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st);
 hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);

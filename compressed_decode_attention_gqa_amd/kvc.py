@@ -21,9 +21,11 @@ RULES = {"single": 0, "cumulative": 1, "ema": 2}
 DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
 EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
-            "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
+            "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
+            "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
             "kvc_decode_workspace_size",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
+            "kvc_keepkv_prefill_workspace_size",
             "kvc_laprox_workspace_size",
             "kvc_workspace_status", "kvc_status_string", "kvc_version")
 
@@ -63,12 +65,14 @@ _SIGS = {
     "kvc_compact": (_I, [_P, _P, _P, _P, _SZ, _P]),
     "kvc_moment_correct": (_I, [_P, _I, _P, _I, _I, _F, _P, _P, _P, _P]),
     "kvc_moment_evict": (_I, [_P, _P, _P, _F, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "kvc_keepkv_prefill_merge": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "kvc_laprox_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
     "kvc_select_workspace_size": (_SZ, [_I, _I]),
     "kvc_compact_workspace_size": (_SZ, [_P]),
     "kvc_moment_evict_workspace_size": (_SZ, [_P]),
+    "kvc_keepkv_prefill_workspace_size": (_SZ, [_P]),
     "kvc_laprox_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "kvc_workspace_status": (_I, [_P, _P]),
     "kvc_status_string": (ctypes.c_char_p, [_I]),
@@ -189,6 +193,11 @@ def kvc_moment_evict_workspace_size(cache: Cache) -> int:
     return lib().kvc_moment_evict_workspace_size(ctypes.byref(d))
 
 
+def kvc_keepkv_prefill_workspace_size(cache: Cache) -> int:
+    d = cache.desc()
+    return lib().kvc_keepkv_prefill_workspace_size(ctypes.byref(d))
+
+
 def kvc_laprox_workspace_size(n_layers, H, n_kv, N, w, d, D) -> int:
     return lib().kvc_laprox_workspace_size(n_layers, H, n_kv, N, w, d, D)
 
@@ -258,6 +267,14 @@ def kvc_moment_evict(cache: Cache, moments: Moments, alpha, scale: float, budget
     _check("kvc_moment_evict", lib().kvc_moment_evict(
         ctypes.byref(d), ctypes.byref(mom), _ptr(alpha), scale, budget, max_len, _ptr(evict), _ptr(order),
         _ptr(score_out), _ptr(n_evict), _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def kvc_keepkv_prefill_merge(cache: Cache, merge: _Merge, budget: int, protect_from: int, evict, pairs=None,
+                             n_merged=None, ws: torch.Tensor = None, stream=None):
+    d = cache.desc()
+    _check("kvc_keepkv_prefill_merge", lib().kvc_keepkv_prefill_merge(
+        ctypes.byref(d), ctypes.byref(merge), budget, protect_from, _ptr(evict), _ptr(pairs), _ptr(n_merged),
+        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def kvc_compact(cache: Cache, evict, merge: _Merge | None, ws: torch.Tensor, stream=None):

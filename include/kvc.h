@@ -14,7 +14,8 @@
  *                budget §3.
  *   KeepKV    -- reading notes on "KeepKV: Achieving Periodic Lossless KV Cache
  *                Compression": attention eq. (1), votes eqs. (6)-(7), ZIP merge
- *                eqs. (8)-(12), numerical-stability guard, framework integration.
+ *                eqs. (8)-(12), numerical-stability guard, framework integration,
+ *                the inference algorithm's prefill compression.
  *   LaProx    -- notes on "Reformulating KV Cache Eviction Problem for
  *                Long-Context LLM Inference": key designs 1-3, GQA paragraph.
  *
@@ -203,6 +204,32 @@ int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const f
                          int32_t budget, int32_t max_len, uint8_t *evict, int32_t *order, float *score_out,
                          int32_t *n_evict, void *ws, size_t ws_bytes, void *stream);
 
+/* kvc_keepkv_prefill_merge -- KeepKV prefill compression by greedy all-pairs
+ * ZIP merging (reading notes on KeepKV: the inference algorithm's prefill steps
+ * 2-5, "candidate choice", eqs. (7), (10), (12) and the numerical-stability
+ * guard), per-KV-head scopes only (units_per_scope = 1, else
+ * KVC_ERR_UNSUPPORTED). While a scope holds more than `budget` live entries,
+ * the two entries whose keys have the largest cosine, both at positions below
+ * protect_from (the most recent tokens are never merged), are ZIP-merged with
+ * the reference logits of merge->q (the mean over its G query heads of
+ * scale * q_g . k, recomputed for a merged key) and votes added; the merged
+ * rows, rounded to the cache dtype, replace the older entry's rows in its slot
+ * (its utility becomes the sum of the two) and the other slot is flagged in
+ * evict (u8 [n_scopes][capacity]; 0 on every other slot < len). Remove the
+ * flagged slots with kvc_compact (merge NULL). Ties: cosine descending, then
+ * the pair's lower position, then its higher one; a zero key has cosine 0.
+ * pairs: [n_scopes][capacity][2] int32 or NULL, merge i of a scope as
+ * (surviving slot, removed slot); n_merged: [n_scopes] int32 or NULL. votes
+ * must be non-NULL. Cosines are float64 (exact products of the cache values).
+ * If fewer than two entries may merge before the budget is reached, the scope
+ * stops there and the workspace status becomes KVC_ERR_CAPACITY. One
+ * workgroup per scope runs the merges in sequence: each merge costs O(len d)
+ * plus O(len d) per entry whose best partner was one of the pair. Workspace:
+ * kvc_keepkv_prefill_workspace_size. */
+int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge, int32_t budget,
+                                 int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* kvc_compact -- remove the flagged entries of every scope (MomentKV Algorithm 1
  * step 14; InertiaKV §3: eviction is irreversible). Survivors end in slots
  * [0, len - n_evicted): the j-th evicted slot below the new length receives the
@@ -293,6 +320,7 @@ size_t kvc_decode_workspace_size(const kvc_cache *cache, int32_t G, int32_t max_
 size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity);
 size_t kvc_compact_workspace_size(const kvc_cache *cache);
 size_t kvc_moment_evict_workspace_size(const kvc_cache *cache);
+size_t kvc_keepkv_prefill_workspace_size(const kvc_cache *cache);
 size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,
                                  int32_t d, int32_t D);
 

@@ -51,20 +51,19 @@ def cosine_matrix(K):
 
 
 def best_pair(K, pos, cand):
-    """(i, j) of the candidate pair of largest cosine; ties to the lower (min pos, max pos)."""
+    """(i, j, cos) of the candidate pair of largest cosine; ties to the lower (min pos, max pos)."""
     idx = np.flatnonzero(cand)
     if idx.size < 2:
         return None
     C = cosine_matrix(np.asarray(K)[idx])
-    best = None
-    for a in range(idx.size):
-        for b in range(a + 1, idx.size):
-            i, j = idx[a], idx[b]
-            pi, pj = pos[i], pos[j]
-            key = (-C[a, b], min(pi, pj), max(pi, pj))
-            if best is None or key < best[0]:
-                best = (key, i, j)
-    return best[1], best[2], -best[0][0]
+    iu, ju = np.triu_indices(idx.size, k=1)
+    c = C[iu, ju]
+    top = np.flatnonzero(c == c.max())
+    p = np.asarray(pos)[idx]
+    lo = np.minimum(p[iu[top]], p[ju[top]])
+    hi = np.maximum(p[iu[top]], p[ju[top]])
+    t = top[np.lexsort((hi, lo))[0]]
+    return int(idx[iu[t]]), int(idx[ju[t]]), float(c[t])
 
 
 def prefill_merge(K, V, votes, pos, m, q, scale, budget, protect_from, eps=1e-6, row_dtype="f64",

@@ -120,6 +120,27 @@ def test_moment_evict_host_checks():
 
 
 @needs_lib
+def test_keepkv_prefill_host_checks():
+    L = kvc.lib()
+    c = _fake_cache(votes=0x7000)
+    mg = kvc._Merge(0x8000, 4, 0.1, 1e-6, 0)
+    need = L.kvc_keepkv_prefill_workspace_size(ctypes.byref(c))
+    assert need > 0
+
+    def call(cache=c, m=mg, budget=10, evict=0x600, ws=0x900, wsb=need):
+        return L.kvc_keepkv_prefill_merge(ctypes.byref(cache), ctypes.byref(m) if m is not None else None, budget,
+                                          90, evict, None, None, ws, wsb, None)
+    assert call(cache=_fake_cache(votes=0x7000, units_per_scope=2, unit_stride=100, scope_stride=200)) == -3
+    assert call(cache=_fake_cache()) == -1                    # no votes
+    assert call(m=None) == -1
+    assert call(m=kvc._Merge(0x8000, 3, 0.1, 1e-6, 0)) == -3
+    assert call(m=kvc._Merge(0x8008, 4, 0.1, 1e-6, 0)) == -5
+    assert call(evict=None) == -1
+    assert call(budget=-1) == -4
+    assert call(wsb=need - 1) == -6
+
+
+@needs_lib
 @pytest.mark.parametrize("H,n_kv,N,w,D,code", [
     (32, 8, 100, 1, 4096, -3),     # G w = 4: not a whole number of 8-row waves
     (32, 8, 100, 4, 4000, -3),     # D not a multiple of 64
