@@ -371,6 +371,74 @@ def run_moment_evict(args):
     print(json.dumps(result), flush=True)
 
 
+def run_prefill_merge(args):
+    """KeepKV prefill compression of every KV head: greedy all-pairs ZIP merging from the prompt
+    length down to the budget, the last 32 positions protected (kvc_keepkv_prefill_merge). The
+    cache is restored from an HBM copy before each repetition; events bracket the call alone."""
+    from oracle.keepkv_prefill import prefill_merge
+    import oracle
+    wl = synth.WORKLOADS["k1_keepkv_prefill_llama8b_4k"]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S, d, B, L0 = wl.n_scopes, wl.d, wl.budget, wl.context
+    protect_from = L0 - 32
+    t = synth.cache_tensors(wl, dev)
+    votes = torch.ones((S, L0 + 1), dtype=torch.int32, device=dev)
+    cache = kvc.Cache(k=t["k"], v=t["v"], pos=t["pos"], m=t["m"], length=t["length"], votes=votes)
+    q = synth.step_query(0, S, wl.G, d, wl.dtype, wl.seed, dev).contiguous()
+    merge = kvc.merge_desc(q, wl.G, float(np.float32(1 / np.sqrt(d))))
+    saved = [x.clone() for x in (cache.k, cache.v, cache.votes, cache.pos, cache.m, cache.length)]
+    fields = (cache.k, cache.v, cache.votes, cache.pos, cache.m, cache.length)
+    evict = torch.zeros((S, cache.capacity), dtype=torch.uint8, device=dev)
+    n_merged = torch.zeros((S,), dtype=torch.int32, device=dev)
+    ws = kvc.workspace(kvc.kvc_keepkv_prefill_workspace_size(cache), dev)
+    times = []
+    for rep in range(args.warmup + args.steps):
+        for x, y in zip(fields, saved):
+            x.copy_(y)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        kvc.kvc_keepkv_prefill_merge(cache, merge, B, protect_from, evict, None, n_merged, ws=ws)
+        end.record()
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            times.append(start.elapsed_time(end))
+    if kvc.kvc_workspace_status(ws) != 0 or int(n_merged.min()) != L0 - B:
+        raise SystemExit("prefill merge did not reach the budget")
+    ms = float(np.median(times))
+    # float64 work of the loop: the initial best partners (2 L0^2 d per head) and, per merge, the
+    # merged row against the live candidates (2 L d); recomputed orphan rows are not counted
+    cand0 = protect_from
+    flops = S * (2.0 * cand0 * cand0 * d + sum(2.0 * (cand0 - i) * d for i in range(L0 - B)))
+    ach = flops / (ms / 1e3) / 1e12
+    result = {"metric": "KeepKV prefill compression: prompt tokens compressed/sec (greedy all-pairs ZIP merging)",
+              "value": S * L0 / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16 cache; f64 cosines and merge weights", "data": "synthetic",
+              "config": {"workload": wl.name, "heads": S, "prompt": L0, "budget": B, "protected": L0 - protect_from,
+                         "merges_per_head": L0 - B, "G": wl.G},
+              "roofline": {"bound": "alu", "achieved": ach, "peak": rf.MI355X_FP64_VALU_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / rf.MI355X_FP64_VALU_TFLOPS, "traffic": None, "launch_ms": ms,
+                           "flops_per_launch": flops}}
+    if not args.no_cpu_baseline:
+        # the oracle on one head, for a bounded number of merges
+        sc = 0
+        Kh = oracle.to_f64(saved[0][sc, 0, :L0].view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        Vh = oracle.to_f64(saved[1][sc, 0, :L0].view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        qh = oracle.to_f64(q[sc].view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        n_steps = 12
+        t0 = time.perf_counter()
+        prefill_merge(Kh, Vh, np.ones(L0, dtype=np.int64), np.arange(L0), np.zeros(L0), qh,
+                      float(np.float32(1 / np.sqrt(d))), L0 - n_steps, protect_from, row_dtype="bf16")
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": n_steps / dt * L0 / (L0 - B), "unit": "tokens/s",
+                                  "cores": torch.get_num_threads(), "kind": "oracle",
+                                  "sample": f"the first {n_steps} merges of one head (L0={L0}) in {dt:.1f} s, "
+                                            "numpy float64 oracle, scaled to whole prompts per second"}
+    print(json.dumps(result), flush=True)
+
+
 def run_first_step(args):
     """The first decode step after prefill: attend and score over the whole context, then
     compress every KV head to its budget (k = context + 1 - budget evictions per head: select,
@@ -463,7 +531,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict"],
+    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict", "prefill_merge"],
                     help="step: the fused decode step (default); first_step: the bulk compression step "
                          "after prefill; moment_correct: MomentKV's corrected output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -477,6 +545,8 @@ def main():
 
     if args.op == "moment_evict":
         return run_moment_evict(args)
+    if args.op == "prefill_merge":
+        return run_prefill_merge(args)
     if args.op == "moment_correct":
         run_moment_correct(args)
         return

@@ -352,7 +352,7 @@ MomentEvictLayout moment_evict_layout(int n_scopes, int cap) {
 
 // ------------------------------------------------------- KeepKV prefill merging
 struct PrefillLayout {
-  size_t status, norm, rowmax, rowarg, cand, total;
+  size_t status, norm, rec, cand, total;
 };
 
 PrefillLayout prefill_layout(int n_scopes, int cap) {
@@ -361,8 +361,7 @@ PrefillLayout prefill_layout(int n_scopes, int cap) {
   size_t o = 0;
   l.status = o; o = align_up(o + 256);
   l.norm = o;   o = align_up(o + n * 8);
-  l.rowmax = o; o = align_up(o + n * 8);
-  l.rowarg = o; o = align_up(o + n * 4);
+  l.rec = o;    o = align_up(o + n * 64);
   l.cand = o;   o = align_up(o + n);
   l.total = o;
   return l;
@@ -592,8 +591,7 @@ int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge,
   p.pairs = pairs;
   p.n_merged = n_merged;
   p.norm = at<double>(ws, l.norm);
-  p.rowmax = at<double>(ws, l.rowmax);
-  p.rowarg = at<int32_t>(ws, l.rowarg);
+  p.rec = at<char>(ws, l.rec);
   p.cand = at<uint8_t>(ws, l.cand);
   p.status = at<int32_t>(ws, l.status);
   if (kvc::launch_prefill_merge(p, cache->dtype, static_cast<hipStream_t>(stream)) != hipSuccess)

@@ -7,17 +7,22 @@
 // slot of the older one. Ties: cosine descending, then the pair's lower
 // position, then its higher position.
 //
-// Kernels, in launch order:
+// Every candidate row keeps its PK best partners (cosine, then position),
+// sorted; every candidate outside a row's list ranks no higher than the list's
+// last entry. Kernels, in launch order:
 //   k_pm_prep    key norms (float64) and the candidate flags of every slot.
-//   k_pm_rows    each candidate's best partner: the block's 128 candidate keys
-//                are the float64 MFMA operator of kvc_f64mfma.h (transposed
-//                use), 16 keys per tile are the A operand, so a lane holds the
-//                dot products of 8 rows x 4 tokens; cos = dot / (|k_i| |k_j|).
+//   k_pm_rows    the initial lists: the block's 64 candidate keys are the
+//                float64 MFMA operator of kvc_f64mfma.h (transposed use), 16 keys
+//                per tile are the A operand, so a lane holds the dot products of
+//                4 rows x 4 tokens and keeps its own top PK per row; the lanes'
+//                lists are merged (their union holds every row's top PK).
 //   k_pm_loop    one workgroup per scope runs the greedy loop: the pair is the
-//                row of largest best-cosine (ties to the lower position) and its
-//                partner; after the merge only the merged row and the rows whose
-//                best partner was one of the pair are recomputed, and every other
-//                row takes the merged entry as partner when it beats its best.
+//                row whose list head is largest (ties to the lower position) and
+//                that head. After the merge the merged entry's cosine with every
+//                candidate is computed once: it gives the merged row its new list,
+//                every other row drops the two merged entries from its list and
+//                takes the merged one when it beats the list's last entry, and
+//                only a row whose list runs empty is recomputed in full.
 // Products of the cache's bf16 (or fp32) keys are exact in float64, so the
 // cosines equal the ones of the float64 oracle up to the rounding of the sums.
 #include "kvc_f64mfma.h"
@@ -26,13 +31,69 @@
 namespace kvc {
 namespace {
 
-constexpr int PM_NT = 512;       // k_pm_rows: 8 waves, two per SIMD
+constexpr int PK = 4;            // partners kept per row
+constexpr int PM_NT = 256;       // k_pm_rows: 4 waves
+constexpr int PM_CT = 4;         // k_pm_rows: 16-row column tiles of the operator in use
+constexpr int PM_ROWS = 16 * PM_CT;
 constexpr int PM_LOOP = 1024;    // k_pm_loop: 16 waves
-constexpr int PM_ORPH = 1024;    // orphan rows recomputed per batch
+constexpr int PM_ORPH = 1024;    // rows recomputed per batch
 
 // (cos, pos) order: higher cosine first, then the lower position.
 __device__ __forceinline__ bool pm_better(double c1, int p1, double c2, int p2) {
   return c1 > c2 || (c1 == c2 && p1 < p2);
+}
+
+// Sorted insertion (best first) of (c, pp, ss) into a list of PK entries; empty entries
+// (slot -1) sort last. An entry that would rank past the end is dropped. Branch-free:
+// the new entry's rank is the number of entries that stay ahead of it (a prefix).
+__device__ __forceinline__ void pk_insert(double (&lc)[PK], int (&lp)[PK], int (&ls)[PK], double c, int pp, int ss) {
+  int rank = 0;
+#pragma unroll
+  for (int k = 0; k < PK; ++k) rank += (ls[k] >= 0 && !pm_better(c, pp, lc[k], lp[k])) ? 1 : 0;
+#pragma unroll
+  for (int k = PK - 1; k > 0; --k) {
+    const bool take_new = k == rank, take_prev = k > rank;
+    lc[k] = take_new ? c : (take_prev ? lc[k - 1] : lc[k]);
+    lp[k] = take_new ? pp : (take_prev ? lp[k - 1] : lp[k]);
+    ls[k] = take_new ? ss : (take_prev ? ls[k - 1] : ls[k]);
+  }
+  if (rank == 0) {
+    lc[0] = c;
+    lp[0] = pp;
+    ls[0] = ss;
+  }
+}
+
+// A row's partner list: 64 bytes, read and written as four 16-byte vectors. Empty
+// entries have slot -1; slot[0] == -2 marks a row whose recomputation is pending.
+struct PmRec {
+  double c[PK];
+  int s[PK];
+  int p[PK];
+};
+static_assert(sizeof(PmRec) == 64, "partner record is 64 bytes");
+
+__device__ __forceinline__ void rec_load(const PrefillMergeArgs &a, int64_t row, double (&c)[PK], int (&pp)[PK],
+                                         int (&ss)[PK]) {
+  const PmRec *r = reinterpret_cast<const PmRec *>(a.rec) + row;
+  const u32x4 w0 = ld16(&r->c[0]), w1 = ld16(&r->c[2]), w2 = ld16(&r->s[0]), w3 = ld16(&r->p[0]);
+  c[0] = __hiloint2double(int(w0.y), int(w0.x));
+  c[1] = __hiloint2double(int(w0.w), int(w0.z));
+  c[2] = __hiloint2double(int(w1.y), int(w1.x));
+  c[3] = __hiloint2double(int(w1.w), int(w1.z));
+  ss[0] = int(w2.x); ss[1] = int(w2.y); ss[2] = int(w2.z); ss[3] = int(w2.w);
+  pp[0] = int(w3.x); pp[1] = int(w3.y); pp[2] = int(w3.z); pp[3] = int(w3.w);
+}
+
+__device__ __forceinline__ void rec_store(const PrefillMergeArgs &a, int64_t row, const double (&c)[PK],
+                                          const int (&pp)[PK], const int (&ss)[PK]) {
+  PmRec *r = reinterpret_cast<PmRec *>(a.rec) + row;
+  st16(&r->c[0], u32x4{uint32_t(__double2loint(c[0])), uint32_t(__double2hiint(c[0])),
+                       uint32_t(__double2loint(c[1])), uint32_t(__double2hiint(c[1]))});
+  st16(&r->c[2], u32x4{uint32_t(__double2loint(c[2])), uint32_t(__double2hiint(c[2])),
+                       uint32_t(__double2loint(c[3])), uint32_t(__double2hiint(c[3]))});
+  st16(&r->s[0], u32x4{uint32_t(ss[0]), uint32_t(ss[1]), uint32_t(ss[2]), uint32_t(ss[3])});
+  st16(&r->p[0], u32x4{uint32_t(pp[0]), uint32_t(pp[1]), uint32_t(pp[2]), uint32_t(pp[3])});
 }
 
 template <typename T>
@@ -52,143 +113,167 @@ __global__ __launch_bounds__(256) void k_pm_prep(PrefillMergeArgs p) {
   }
   p.norm[slot] = sqrt(n);
   p.cand[slot] = (i < L && p.pos[slot] < p.protect_from) ? 1 : 0;
-  p.rowarg[slot] = -1;
-  p.rowmax[slot] = -INFINITY;
+  const double nc[PK] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  const int np[PK] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff}, ns[PK] = {-1, -1, -1, -1};
+  rec_store(p, slot, nc, np, ns);
   if (i < L) p.evict[slot] = 0;
 }
 
-// grid (row blocks of 128, scopes), 512 threads; every token of the scope.
+struct RowsMerge {
+  double c[PM_NT / 64][PM_ROWS][PK];
+  int p[PM_NT / 64][PM_ROWS][PK], s[PM_NT / 64][PM_ROWS][PK];
+};
+union RowsLds {
+  FmOperator op;
+  RowsMerge m;
+};
+
+// grid (row blocks of 64, scopes), 256 threads; every token of the scope.
 template <typename T>
 __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
-  __shared__ FmOperator op;
-  __shared__ double bcos[PM_NT / 64][128];
-  __shared__ int bpos[PM_NT / 64][128], bslot[PM_NT / 64][128];
+  __shared__ RowsLds sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rb = blockIdx.x * 128, sc = blockIdx.y;
+  const int rb = blockIdx.x * PM_ROWS, sc = blockIdx.y;
   const int L = min(p.len[sc], p.capacity);
-  const int t0 = 0, t1 = L;
   if (rb >= L) return;
   const int64_t so = int64_t(sc) * p.capacity;
   const T *Kb = reinterpret_cast<const T *>(p.k) + int64_t(sc) * p.scope_stride * HD;
-  for (int e = tid; e < HD * HD; e += PM_NT) {
+  for (int e = tid; e < PM_ROWS * HD; e += PM_NT) {
     const int r = e >> 7, b = e & 127, row = rb + r;
     const double v = (row < L && p.cand[so + row]) ? double(load_elem<T>(Kb, int64_t(row) * HD + b)) : 0.0;
-    fm_put_t(op, r, b, v);
+    fm_put_t(sh.op, r, b, v);
   }
   const int jl = lane & 15, tq = lane >> 4;
-  double nrow[FM_RT], best[FM_RT];
-  int bp[FM_RT], bs[FM_RT];
-  bool rc[FM_RT];
+  double nrow[PM_CT];
+  bool rc[PM_CT];
+  double lc[PM_CT][PK];
+  int lp[PM_CT][PK], ls[PM_CT][PK];
 #pragma unroll
-  for (int ct = 0; ct < FM_RT; ++ct) {
+  for (int ct = 0; ct < PM_CT; ++ct) {
     const int row = rb + 16 * ct + jl;
     rc[ct] = row < L && p.cand[so + row];
     nrow[ct] = rc[ct] ? p.norm[so + row] : 0.0;
-    best[ct] = -INFINITY;
-    bp[ct] = 0x7fffffff;
-    bs[ct] = -1;
+#pragma unroll
+    for (int k = 0; k < PK; ++k) {
+      lc[ct][k] = -INFINITY;
+      lp[ct][k] = 0x7fffffff;
+      ls[ct][k] = -1;
+    }
   }
   __syncthreads();
   constexpr int ES = sizeof(T);
   const char *Kc = reinterpret_cast<const char *>(Kb);
-  const int n16 = (t1 - t0 + FM_TILE - 1) / FM_TILE;
+  const int n16 = (L + FM_TILE - 1) / FM_TILE;
   for (int t = wave; t < n16; t += PM_NT / 64) {
-    const int tb = t0 + t * FM_TILE;
+    const int tb = t * FM_TILE;
     FmRow<T> kr;
-    kr.load(Kc + (int64_t(min(tb + jl, t1 - 1)) * HD + 32 * tq) * ES);
+    kr.load(Kc + (int64_t(min(tb + jl, L - 1)) * HD + 32 * tq) * ES);
     double x[32];
 #pragma unroll
     for (int s = 0; s < 32; ++s) x[s] = kr.get(s);
-    fm_d4 acc[FM_RT];
+    fm_d4 acc[PM_CT];
 #pragma unroll
-    for (int ct = 0; ct < FM_RT; ++ct) acc[ct] = fm_d4{0.0, 0.0, 0.0, 0.0};
-    fm_apply_t(op, lane, x, acc);
+    for (int ct = 0; ct < PM_CT; ++ct) acc[ct] = fm_d4{0.0, 0.0, 0.0, 0.0};
+    fm_apply_t<PM_CT>(sh.op, lane, x, acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = tb + tq + 4 * r;
-      const int jc = min(j, t1 - 1);
-      const bool cj = j < t1 && p.cand[so + jc];
+      const int jc = min(j, L - 1);
+      const bool cj = j < L && p.cand[so + jc];
       const double nj = p.norm[so + jc];
       const int pj = p.pos[so + jc];
 #pragma unroll
-      for (int ct = 0; ct < FM_RT; ++ct) {
+      for (int ct = 0; ct < PM_CT; ++ct) {
         const int row = rb + 16 * ct + jl;
         if (rc[ct] && cj && j != row) {
           const double den = nrow[ct] * nj;
           const double c = den > 0.0 ? acc[ct][r] / den : 0.0;
-          if (pm_better(c, pj, best[ct], bp[ct])) {
-            best[ct] = c;
-            bp[ct] = pj;
-            bs[ct] = j;
-          }
+          pk_insert(lc[ct], lp[ct], ls[ct], c, pj, j);
         }
       }
     }
   }
-  // rows 16 ct + jl: combine the four token groups of the wave, then the waves
+  // merge the lists of the four token groups of the wave (rows 16 ct + jl)
 #pragma unroll
-  for (int ct = 0; ct < FM_RT; ++ct) {
+  for (int ct = 0; ct < PM_CT; ++ct) {
 #pragma unroll
     for (int o = 16; o < 64; o <<= 1) {
-      const double c2 = __shfl_xor(best[ct], o);
-      const int p2 = __shfl_xor(bp[ct], o), s2 = __shfl_xor(bs[ct], o);
-      if (s2 >= 0 && (bs[ct] < 0 || pm_better(c2, p2, best[ct], bp[ct]))) {
-        best[ct] = c2;
-        bp[ct] = p2;
-        bs[ct] = s2;
+      double oc[PK];
+      int op_[PK], os[PK];
+#pragma unroll
+      for (int k = 0; k < PK; ++k) {
+        oc[k] = __shfl_xor(lc[ct][k], o);
+        op_[k] = __shfl_xor(lp[ct][k], o);
+        os[k] = __shfl_xor(ls[ct][k], o);
       }
-    }
-    if (tq == 0) {
-      bcos[wave][16 * ct + jl] = best[ct];
-      bpos[wave][16 * ct + jl] = bp[ct];
-      bslot[wave][16 * ct + jl] = bs[ct];
+#pragma unroll
+      for (int k = 0; k < PK; ++k)
+        if (os[k] >= 0) pk_insert(lc[ct], lp[ct], ls[ct], oc[k], op_[k], os[k]);
     }
   }
-  __syncthreads();
-  if (tid < 128 && rb + tid < L && p.cand[so + rb + tid]) {
-    double c = -INFINITY;
-    int pp = 0x7fffffff, ss = -1;
-    for (int wv = 0; wv < PM_NT / 64; ++wv) {
-      const int s2 = bslot[wv][tid];
-      if (s2 >= 0 && (ss < 0 || pm_better(bcos[wv][tid], bpos[wv][tid], c, pp))) {
-        c = bcos[wv][tid];
-        pp = bpos[wv][tid];
-        ss = s2;
+  __syncthreads();   // the operator is no longer read: its LDS holds the waves' lists
+  if (tq == 0) {
+#pragma unroll
+    for (int ct = 0; ct < PM_CT; ++ct)
+#pragma unroll
+      for (int k = 0; k < PK; ++k) {
+        sh.m.c[wave][16 * ct + jl][k] = lc[ct][k];
+        sh.m.p[wave][16 * ct + jl][k] = lp[ct][k];
+        sh.m.s[wave][16 * ct + jl][k] = ls[ct][k];
       }
+  }
+  __syncthreads();
+  if (tid < PM_ROWS && rb + tid < L && p.cand[so + rb + tid]) {
+    double c[PK];
+    int pp[PK], ss[PK];
+#pragma unroll
+    for (int k = 0; k < PK; ++k) {
+      c[k] = sh.m.c[0][tid][k];
+      pp[k] = sh.m.p[0][tid][k];
+      ss[k] = sh.m.s[0][tid][k];
     }
-    p.rowmax[so + rb + tid] = c;
-    p.rowarg[so + rb + tid] = ss;
+    for (int wv = 1; wv < PM_NT / 64; ++wv)
+#pragma unroll
+      for (int k = 0; k < PK; ++k)
+        if (sh.m.s[wv][tid][k] >= 0) pk_insert(c, pp, ss, sh.m.c[wv][tid][k], sh.m.p[wv][tid][k], sh.m.s[wv][tid][k]);
+    rec_store(p, so + rb + tid, c, pp, ss);
   }
 }
 
 struct LoopLds {
   double kn[HD];            // the key whose row is being computed (float64)
   double red_c[PM_LOOP / 64];
-  int red_p[PM_LOOP / 64], red_s[PM_LOOP / 64];
+  int red_p[PM_LOOP / 64], red_s[PM_LOOP / 64], red_t[PM_LOOP / 64];
   double lbar[2];
   double wgt[4];
   int orph[PM_ORPH];
-  int n_orph, more, pick_i, pick_j;
+  int n_orph;
   double nk;
+  double top_c[PK];
+  int top_s[PK], top_p[PK];
 };
 
-// Workgroup-wide best (c, p, s) by pm_better over the threads' candidates; result in sh.
+// Workgroup-wide best (c, p) by pm_better over the threads' offers; winner's slot in
+// red_s[0] and thread in red_t[0].
 __device__ __forceinline__ void loop_argmax(LoopLds &sh, double c, int pp, int ss, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
+  int tt = tid;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const double c2 = __shfl_xor(c, o);
-    const int p2 = __shfl_xor(pp, o), s2 = __shfl_xor(ss, o);
+    const int p2 = __shfl_xor(pp, o), s2 = __shfl_xor(ss, o), t2 = __shfl_xor(tt, o);
     if (s2 >= 0 && (ss < 0 || pm_better(c2, p2, c, pp))) {
       c = c2;
       pp = p2;
       ss = s2;
+      tt = t2;
     }
   }
   if (lane == 0) {
     sh.red_c[wave] = c;
     sh.red_p[wave] = pp;
     sh.red_s[wave] = ss;
+    sh.red_t[wave] = tt;
   }
   __syncthreads();
   if (tid == 0) {
@@ -197,35 +282,84 @@ __device__ __forceinline__ void loop_argmax(LoopLds &sh, double c, int pp, int s
         sh.red_c[0] = sh.red_c[w];
         sh.red_p[0] = sh.red_p[w];
         sh.red_s[0] = sh.red_s[w];
+        sh.red_t[0] = sh.red_t[w];
       }
   }
   __syncthreads();
 }
 
-// Best partner of row `row` (its key in sh.kn, norm sh.nk) over the candidates.
+// The PK best of the threads' sorted local lists, by PK rounds of a workgroup argmax over the
+// lists' heads; written to row `row`'s list.
+__device__ __forceinline__ void loop_topk(const PrefillMergeArgs &p, LoopLds &sh, int64_t so, int row,
+                                          const double (&lc)[PK], const int (&lp)[PK], const int (&ls)[PK],
+                                          int tid) {
+  int h = 0;
+  for (int k = 0; k < PK; ++k) {
+    double c = -INFINITY;
+    int pp = 0x7fffffff, ss = -1;
+#pragma unroll
+    for (int q = 0; q < PK; ++q)
+      if (q == h) {
+        c = lc[q];
+        pp = lp[q];
+        ss = ls[q];
+      }
+    loop_argmax(sh, c, pp, ss, tid);
+    if (tid == 0) {
+      sh.top_c[k] = sh.red_c[0];
+      sh.top_s[k] = sh.red_s[0];
+      sh.top_p[k] = sh.red_p[0];
+    }
+    if (sh.red_s[0] >= 0 && sh.red_t[0] == tid) ++h;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    double c[PK];
+    int pp[PK], ss[PK];
+#pragma unroll
+    for (int k = 0; k < PK; ++k) {
+      c[k] = sh.top_c[k];
+      ss[k] = sh.top_s[k];
+      pp[k] = sh.top_s[k] >= 0 ? sh.top_p[k] : 0x7fffffff;
+    }
+    rec_store(p, so + row, c, pp, ss);
+  }
+}
+
+// cos(kn, k_j) for a candidate j (kn in LDS, norm sh.nk).
+template <typename T>
+__device__ __forceinline__ double loop_cos(const PrefillMergeArgs &p, const LoopLds &sh, const T *Kb, int64_t so,
+                                           int j) {
+  constexpr int EPV = ElemTraits<T>::EPV;
+  const char *row = reinterpret_cast<const char *>(Kb + int64_t(j) * HD);
+  double dot = 0.0;
+#pragma unroll 4
+  for (int v = 0; v < HD / EPV; ++v) {
+    const u32x4 w = ld16(row + 16 * v);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) dot = fma(sh.kn[v * EPV + e], double(ElemTraits<T>::get(w, e)), dot);
+  }
+  const double den = sh.nk * p.norm[so + j];
+  return den > 0.0 ? dot / den : 0.0;
+}
+
+// Full list of row `row` (its key in sh.kn, norm sh.nk) over the candidates.
 template <typename T>
 __device__ __forceinline__ void loop_row(const PrefillMergeArgs &p, LoopLds &sh, const T *Kb, int64_t so, int L,
                                          int row, int tid) {
-  double c = -INFINITY;
-  int pp = 0x7fffffff, ss = -1;
+  double lc[PK];
+  int lp[PK], ls[PK];
+#pragma unroll
+  for (int k = 0; k < PK; ++k) {
+    lc[k] = -INFINITY;
+    lp[k] = 0x7fffffff;
+    ls[k] = -1;
+  }
   for (int j = tid; j < L; j += PM_LOOP) {
     if (j == row || !p.cand[so + j]) continue;
-    double dot = 0.0;
-    for (int b = 0; b < HD; ++b) dot = fma(sh.kn[b], double(load_elem<T>(Kb, int64_t(j) * HD + b)), dot);
-    const double den = sh.nk * p.norm[so + j];
-    const double cs = den > 0.0 ? dot / den : 0.0;
-    const int pj = p.pos[so + j];
-    if (pm_better(cs, pj, c, pp)) {
-      c = cs;
-      pp = pj;
-      ss = j;
-    }
+    pk_insert(lc, lp, ls, loop_cos<T>(p, sh, Kb, so, j), p.pos[so + j], j);
   }
-  loop_argmax(sh, c, pp, ss, tid);
-  if (tid == 0) {
-    p.rowmax[so + row] = sh.red_s[0] >= 0 ? sh.red_c[0] : -INFINITY;
-    p.rowarg[so + row] = sh.red_s[0];
-  }
+  loop_topk(p, sh, so, row, lc, lp, ls, tid);
 }
 
 template <typename T>
@@ -239,13 +373,15 @@ __global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
   const T *Kb = Kw;
   int live = L, merged = 0;
   while (live > p.budget) {
-    // ---- the pair: the row of largest best-cosine (ties to the lower position) and its partner
+    // ---- the pair: the row whose list head is largest (ties to the lower position) and that head
     {
       double c = -INFINITY;
       int pp = 0x7fffffff, ss = -1;
       for (int i = tid; i < L; i += PM_LOOP) {
-        if (!p.cand[so + i] || p.rowarg[so + i] < 0) continue;
-        const double ci = p.rowmax[so + i];
+        if (!p.cand[so + i]) continue;
+        const PmRec *r = reinterpret_cast<const PmRec *>(p.rec) + so + i;
+        if (r->s[0] < 0) continue;
+        const double ci = r->c[0];
         const int pi = p.pos[so + i];
         if (pm_better(ci, pi, c, pp)) {
           c = ci;
@@ -260,7 +396,7 @@ __global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
       if (tid == 0) p.status[0] = -4;
       break;
     }
-    const int sj = p.rowarg[so + si];
+    const int sj = (reinterpret_cast<const PmRec *>(p.rec) + so + si)->s[0];
     // the older entry of the pair survives; the other is removed
     const bool older = p.pos[so + si] < p.pos[so + sj];
     const int surv = older ? si : sj, gone = older ? sj : si;
@@ -313,7 +449,6 @@ __global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
         p.pairs[(so + merged) * 2 + 1] = gone;
       }
       sh.n_orph = 0;
-      sh.more = 0;
     }
     __threadfence_block();
     __syncthreads();
@@ -328,43 +463,69 @@ __global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
       }
     }
     __syncthreads();
-    // ---- the merged row against every candidate; others adopt it when it beats their best,
-    // rows whose best partner was one of the pair become orphans
+    // ---- the merged entry against every candidate: its own list, and every other row drops the
+    // two merged entries and takes the merged one when it beats its last entry; rows left
+    // with an empty list are recomputed in full
     {
       const int ps = p.pos[so + surv];
-      double c = -INFINITY;
-      int pp = 0x7fffffff, ss = -1;
+      double lc[PK];
+      int lp[PK], ls[PK];
+#pragma unroll
+      for (int k = 0; k < PK; ++k) {
+        lc[k] = -INFINITY;
+        lp[k] = 0x7fffffff;
+        ls[k] = -1;
+      }
       for (int j = tid; j < L; j += PM_LOOP) {
         if (j == surv || !p.cand[so + j]) continue;
-        double dot = 0.0;
-        for (int b = 0; b < HD; ++b) dot = fma(sh.kn[b], double(load_elem<T>(Kb, int64_t(j) * HD + b)), dot);
-        const double den = sh.nk * p.norm[so + j];
-        const double cs = den > 0.0 ? dot / den : 0.0;
+        const double cs = loop_cos<T>(p, sh, Kb, so, j);
         const int pj = p.pos[so + j];
-        if (pm_better(cs, pj, c, pp)) {
-          c = cs;
-          pp = pj;
-          ss = j;
+        pk_insert(lc, lp, ls, cs, pj, j);
+        // row j's list without the two merged entries (the kept entries stay in order)
+        double oc[PK];
+        int opp[PK], os[PK];
+        rec_load(p, so + j, oc, opp, os);
+        double jc[PK];
+        int jp[PK], js[PK];
+#pragma unroll
+        for (int k = 0; k < PK; ++k) {
+          jc[k] = -INFINITY;
+          jp[k] = 0x7fffffff;
+          js[k] = -1;
         }
-        const int ra = p.rowarg[so + j];
-        if (ra == surv || ra == gone) {
+        int n = 0;
+        bool dropped = false;
+        double last_c = -INFINITY;
+        int last_p = 0x7fffffff;
+#pragma unroll
+        for (int k = 0; k < PK; ++k) {
+          if (os[k] < 0) continue;
+          if (os[k] == surv || os[k] == gone) {
+            dropped = true;
+            continue;
+          }
+          pk_insert(jc, jp, js, oc[k], opp[k], os[k]);
+          last_c = oc[k];
+          last_p = opp[k];
+          ++n;
+        }
+        if (n == 0) {
           const int k = atomicAdd(&sh.n_orph, 1);
           if (k < PM_ORPH) sh.orph[k] = j;
-          else p.rowarg[so + j] = -2;      // recomputed in a later batch
-        } else if (ra < 0 || pm_better(cs, ps, p.rowmax[so + j], p.pos[so + ra])) {
-          p.rowmax[so + j] = cs;
-          p.rowarg[so + j] = surv;
+          js[0] = -2;                      // recomputed below (in a later batch past PM_ORPH)
+          rec_store(p, so + j, jc, jp, js);
+          continue;
         }
+        // the merged entry joins the list when it ranks above the list's last entry
+        const bool joins = pm_better(cs, ps, last_c, last_p);
+        if (joins) pk_insert(jc, jp, js, cs, ps, surv);
+        if (joins || dropped) rec_store(p, so + j, jc, jp, js);
       }
-      loop_argmax(sh, c, pp, ss, tid);
-      if (tid == 0) {
-        p.rowmax[so + surv] = sh.red_s[0] >= 0 ? sh.red_c[0] : -INFINITY;
-        p.rowarg[so + surv] = sh.red_s[0];
-      }
+      loop_topk(p, sh, so, surv, lc, lp, ls, tid);
     }
     __threadfence_block();
     __syncthreads();
-    // ---- orphans, in batches of PM_ORPH
+    // ---- rows whose lists ran empty, in batches of PM_ORPH
     for (;;) {
       const int n = min(sh.n_orph, PM_ORPH);
       for (int k = 0; k < n; ++k) {
@@ -381,14 +542,16 @@ __global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
       if (!overflow) break;
       if (tid == 0) sh.n_orph = 0;
       __syncthreads();
-      for (int j = tid; j < L; j += PM_LOOP)
-        if (p.cand[so + j] && p.rowarg[so + j] == -2) {
+      for (int j = tid; j < L; j += PM_LOOP) {
+        PmRec *r = reinterpret_cast<PmRec *>(p.rec) + so + j;
+        if (p.cand[so + j] && r->s[0] == -2) {
           const int k = atomicAdd(&sh.n_orph, 1);
           if (k < PM_ORPH) {
             sh.orph[k] = j;
-            p.rowarg[so + j] = -1;
+            r->s[0] = -1;
           }
         }
+      }
       __syncthreads();
     }
     --live;
@@ -400,7 +563,7 @@ __global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
 }  // namespace
 
 hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st) {
-  const dim3 g1((p.capacity + 255) / 256, p.n_scopes), g2((p.capacity + 127) / 128, p.n_scopes);
+  const dim3 g1((p.capacity + 255) / 256, p.n_scopes), g2((p.capacity + PM_ROWS - 1) / PM_ROWS, p.n_scopes);
   if (dtype == 0) {
     hipLaunchKernelGGL(k_pm_prep<bf16_t>, g1, dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_pm_rows<bf16_t>, g2, dim3(PM_NT), 0, st, p);

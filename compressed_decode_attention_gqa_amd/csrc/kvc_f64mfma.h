@@ -69,19 +69,21 @@ __device__ __forceinline__ void fm_put_t(FmOperator &op, int a, int b, double v)
   op.a[s >> 1][ct][fm_swz(s >> 1, j + 16 * g)][s & 1] = v;
 }
 
+// NCT < 8 uses only the operator's first NCT column tiles (rows 0 .. 16 NCT - 1).
+template <int NCT = FM_RT>
 __device__ __forceinline__ void fm_apply_t(const FmOperator &op, int lane, const double (&x)[32],
-                                           fm_d4 (&acc)[FM_RT]) {
+                                           fm_d4 (&acc)[NCT]) {
 #pragma unroll
   for (int s2 = 0; s2 < FM_S2; ++s2) {
-    fm_d2 bf[FM_RT];
+    fm_d2 bf[NCT];
     const int pl = fm_swz(s2, lane);
 #pragma unroll
-    for (int ct = 0; ct < FM_RT; ++ct) bf[ct] = op.a[s2][ct][pl];
+    for (int ct = 0; ct < NCT; ++ct) bf[ct] = op.a[s2][ct][pl];
 #pragma unroll
-    for (int ct = 0; ct < FM_RT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
       acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[2 * s2], bf[ct].x, acc[ct], 0, 0, 0);
 #pragma unroll
-    for (int ct = 0; ct < FM_RT; ++ct)
+    for (int ct = 0; ct < NCT; ++ct)
       acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[2 * s2 + 1], bf[ct].y, acc[ct], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }

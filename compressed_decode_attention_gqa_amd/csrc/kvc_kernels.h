@@ -67,8 +67,8 @@ struct PrefillMergeArgs {
   int32_t capacity, n_scopes, budget, protect_from;
   uint8_t *evict;
   int32_t *pairs, *n_merged;
-  double *norm, *rowmax;    // [n_scopes][capacity]
-  int32_t *rowarg;          // [n_scopes][capacity]
+  double *norm;             // [n_scopes][capacity]
+  void *rec;                // [n_scopes][capacity] 64-byte partner lists (cosines, slots, positions)
   uint8_t *cand;            // [n_scopes][capacity]
   int32_t *status;
 };

@@ -115,6 +115,11 @@ WORKLOADS = {
 WORKLOADS["m1_momentkv_llama8b_32layers_b1024"] = Workload(
     name="m1_momentkv_llama8b_32layers_b1024", seed=6, dtype="bf16", d=128, G=4, n_layers=32, batch=1,
     n_kv=8, context=32768, budget=1024, steps=64, rule="single", alpha=0.0, moments=True, key_scales=True)
+# KeepKV prefill compression: every KV head of a Llama-3.1-8B-shaped model (32 layers x 8),
+# a 4K prompt merged down to 10% by greedy all-pairs ZIP merging, the last 32 positions kept.
+WORKLOADS["k1_keepkv_prefill_llama8b_4k"] = Workload(
+    name="k1_keepkv_prefill_llama8b_4k", seed=7, dtype="bf16", d=128, G=4, n_layers=32, batch=1, n_kv=8,
+    context=4096, budget=budget_for(4096), steps=1, rule="single", alpha=0.0, key_scales=True, merge=True)
 WORKLOADS["c3_llama8b_model_16k_lazy8"] = WORKLOADS["c3_llama8b_model_16k"].scaled(
     name="c3_llama8b_model_16k_lazy8", lazy_refresh=8)
 
