@@ -352,7 +352,7 @@ MomentEvictLayout moment_evict_layout(int n_scopes, int cap) {
 
 // ------------------------------------------------------- KeepKV prefill merging
 struct PrefillLayout {
-  size_t status, norm, rec, cand, total;
+  size_t status, meta, rec, total;
 };
 
 PrefillLayout prefill_layout(int n_scopes, int cap) {
@@ -360,9 +360,8 @@ PrefillLayout prefill_layout(int n_scopes, int cap) {
   const size_t n = size_t(n_scopes) * cap;
   size_t o = 0;
   l.status = o; o = align_up(o + 256);
-  l.norm = o;   o = align_up(o + n * 8);
+  l.meta = o;   o = align_up(o + n * 16);
   l.rec = o;    o = align_up(o + n * 64);
-  l.cand = o;   o = align_up(o + n);
   l.total = o;
   return l;
 }
@@ -564,7 +563,7 @@ int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge,
                                  void *ws, size_t ws_bytes, void *stream) {
   int st = validate_cache(cache);
   if (st) return st;
-  if (cache->units_per_scope != 1) return KVC_ERR_UNSUPPORTED;
+  if (cache->units_per_scope != 1 || cache->capacity > kvc::PREFILL_MAX_ROWS) return KVC_ERR_UNSUPPORTED;
   if (!cache->votes || !merge || !merge->q || !evict || !ws) return KVC_ERR_ARG;
   if (!valid_G(merge->G)) return KVC_ERR_UNSUPPORTED;
   if (!aligned16(merge->q)) return KVC_ERR_ALIGN;
@@ -590,9 +589,8 @@ int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge,
   p.evict = evict;
   p.pairs = pairs;
   p.n_merged = n_merged;
-  p.norm = at<double>(ws, l.norm);
+  p.meta = at<char>(ws, l.meta);
   p.rec = at<char>(ws, l.rec);
-  p.cand = at<uint8_t>(ws, l.cand);
   p.status = at<int32_t>(ws, l.status);
   if (kvc::launch_prefill_merge(p, cache->dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KVC_ERR_DEVICE;

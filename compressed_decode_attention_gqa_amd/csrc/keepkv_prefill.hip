@@ -7,22 +7,34 @@
 // slot of the older one. Ties: cosine descending, then the pair's lower
 // position, then its higher position.
 //
-// Every candidate row keeps its PK best partners (cosine, then position),
-// sorted; every candidate outside a row's list ranks no higher than the list's
-// last entry. Kernels, in launch order:
-//   k_pm_prep    key norms (float64) and the candidate flags of every slot.
-//   k_pm_rows    the initial lists: the block's 64 candidate keys are the
-//                float64 MFMA operator of kvc_f64mfma.h (transposed use), 16 keys
-//                per tile are the A operand, so a lane holds the dot products of
-//                4 rows x 4 tokens and keeps its own top PK per row; the lanes'
-//                lists are merged (their union holds every row's top PK).
-//   k_pm_loop    one workgroup per scope runs the greedy loop: the pair is the
-//                row whose list head is largest (ties to the lower position) and
-//                that head. After the merge the merged entry's cosine with every
-//                candidate is computed once: it gives the merged row its new list,
-//                every other row drops the two merged entries from its list and
-//                takes the merged one when it beats the list's last entry, and
-//                only a row whose list runs empty is recomputed in full.
+// Every candidate row keeps a list of its PK best partners (cosine, then
+// position), sorted, such that every candidate outside the list ranks no
+// higher than the list's last entry; a row's best pair is its list head. A row
+// whose list runs empty becomes stale and keeps a bound instead: the cosine of
+// its old last entry, which no partner outside the old list exceeds. Every pair
+// with a listed row in it is covered by that row's list, so the only pairs no
+// list covers join two stale rows, and their cosine is at most the second
+// largest stale bound: while that bound stays below the best list head, the
+// greedy choice from the heads is exact; otherwise the stale rows that could
+// reach the head are recomputed first, in batches.
+//
+// Kernels, in launch order:
+//   k_pm_prep   key norms (float64), positions and candidate flags of every
+//               slot; empty lists.
+//   k_pm_rows   the initial lists: the block's 64 candidate keys are the float64
+//               MFMA operator of kvc_f64mfma.h (transposed use), 16 keys per tile
+//               are the A operand, so a lane holds the dot products of 4 rows x 4
+//               tokens and keeps its own top PK per row; the lanes' lists are
+//               merged (their union holds every row's top PK).
+//   k_pm_loop   one workgroup per scope runs the greedy loop over the scope's
+//               candidates, listed in LDS. Per merge: a scan of the list heads
+//               and stale bounds; the merge itself (one wave); one pass of the
+//               merged key against every candidate, 16 lanes per key row (16
+//               bytes each) and 4 row steps of loads in flight, which gives the
+//               merged row its list and lets every other row drop the merged
+//               pair and take the merged entry when it beats an entry of its
+//               list (a wave ballot over the rows' list entries finds the few
+//               rows that change).
 // Products of the cache's bf16 (or fp32) keys are exact in float64, so the
 // cosines equal the ones of the float64 oracle up to the rounding of the sums.
 #include "kvc_f64mfma.h"
@@ -35,8 +47,15 @@ constexpr int PK = 4;            // partners kept per row
 constexpr int PM_NT = 256;       // k_pm_rows: 4 waves
 constexpr int PM_CT = 4;         // k_pm_rows: 16-row column tiles of the operator in use
 constexpr int PM_ROWS = 16 * PM_CT;
-constexpr int PM_LOOP = 1024;    // k_pm_loop: 16 waves
-constexpr int PM_ORPH = 1024;    // rows recomputed per batch
+constexpr int PL_NT = 512;       // k_pm_loop: 8 waves
+constexpr int PL_W = PL_NT / 64;
+constexpr int PL_NS = 8;         // row steps per batch of the merge pass (lane e < PL_NS of a group owns step e's row)
+constexpr int PL_NS_R = 4;       // the same in the recomputation pass (PL_NQ keys in registers)
+constexpr int PL_NQ = 2;         // stale rows recomputed per pass
+constexpr int PL_TODO = 256;     // stale rows collected per recomputation round
+constexpr int PL_SCAN = 8;       // rows per thread per load batch of the head scan
+constexpr int STALE = -2;        // slot value of a stale row's entries (entry 0 holds the bound)
+constexpr int NOPOS = 0x7fffffff;
 
 // (cos, pos) order: higher cosine first, then the lower position.
 __device__ __forceinline__ bool pm_better(double c1, int p1, double c2, int p2) {
@@ -64,36 +83,70 @@ __device__ __forceinline__ void pk_insert(double (&lc)[PK], int (&lp)[PK], int (
   }
 }
 
-// A row's partner list: 64 bytes, read and written as four 16-byte vectors. Empty
-// entries have slot -1; slot[0] == -2 marks a row whose recomputation is pending.
-struct PmRec {
-  double c[PK];
-  int s[PK];
-  int p[PK];
-};
-static_assert(sizeof(PmRec) == 64, "partner record is 64 bytes");
+__device__ __forceinline__ void list_clear(double (&lc)[PK], int (&lp)[PK], int (&ls)[PK]) {
+#pragma unroll
+  for (int k = 0; k < PK; ++k) {
+    lc[k] = -INFINITY;
+    lp[k] = NOPOS;
+    ls[k] = -1;
+  }
+}
+
+// Each lane takes the union's best PK of its list and the list of lane ^ o (disjoint rows).
+__device__ __forceinline__ void list_merge_xor(double (&lc)[PK], int (&lp)[PK], int (&ls)[PK], int o) {
+  double oc[PK];
+  int op[PK], os[PK];
+#pragma unroll
+  for (int k = 0; k < PK; ++k) {
+    oc[k] = __shfl_xor(lc[k], o);
+    op[k] = __shfl_xor(lp[k], o);
+    os[k] = __shfl_xor(ls[k], o);
+  }
+#pragma unroll
+  for (int k = 0; k < PK; ++k)
+    if (os[k] >= 0) pk_insert(lc, lp, ls, oc[k], op[k], os[k]);
+}
+
+// 16-byte entries {float64 value, int, int}: a list entry (cosine, slot, position) and a
+// row's metadata (key norm, position, candidate flag).
+__device__ __forceinline__ u32x4 ent_pack(double c, int a, int b) {
+  return u32x4{uint32_t(__double2loint(c)), uint32_t(__double2hiint(c)), uint32_t(a), uint32_t(b)};
+}
+__device__ __forceinline__ double ent_c(const u32x4 &w) { return __hiloint2double(int(w.y), int(w.x)); }
+
+__device__ __forceinline__ char *rec_at(const PrefillMergeArgs &a, int64_t row) {
+  return static_cast<char *>(a.rec) + row * 64;
+}
+__device__ __forceinline__ char *meta_at(const PrefillMergeArgs &a, int64_t row) {
+  return static_cast<char *>(a.meta) + row * 16;
+}
+__device__ __forceinline__ bool pm_cand(const PrefillMergeArgs &a, int64_t row) {
+  return reinterpret_cast<const int *>(meta_at(a, row))[3] != 0;
+}
+__device__ __forceinline__ double pm_norm(const PrefillMergeArgs &a, int64_t row) {
+  return *reinterpret_cast<const double *>(meta_at(a, row));
+}
 
 __device__ __forceinline__ void rec_load(const PrefillMergeArgs &a, int64_t row, double (&c)[PK], int (&pp)[PK],
                                          int (&ss)[PK]) {
-  const PmRec *r = reinterpret_cast<const PmRec *>(a.rec) + row;
-  const u32x4 w0 = ld16(&r->c[0]), w1 = ld16(&r->c[2]), w2 = ld16(&r->s[0]), w3 = ld16(&r->p[0]);
-  c[0] = __hiloint2double(int(w0.y), int(w0.x));
-  c[1] = __hiloint2double(int(w0.w), int(w0.z));
-  c[2] = __hiloint2double(int(w1.y), int(w1.x));
-  c[3] = __hiloint2double(int(w1.w), int(w1.z));
-  ss[0] = int(w2.x); ss[1] = int(w2.y); ss[2] = int(w2.z); ss[3] = int(w2.w);
-  pp[0] = int(w3.x); pp[1] = int(w3.y); pp[2] = int(w3.z); pp[3] = int(w3.w);
+#pragma unroll
+  for (int k = 0; k < PK; ++k) {
+    const u32x4 w = ld16(rec_at(a, row) + 16 * k);
+    c[k] = ent_c(w);
+    ss[k] = int(w.z);
+    pp[k] = int(w.w);
+  }
 }
 
 __device__ __forceinline__ void rec_store(const PrefillMergeArgs &a, int64_t row, const double (&c)[PK],
                                           const int (&pp)[PK], const int (&ss)[PK]) {
-  PmRec *r = reinterpret_cast<PmRec *>(a.rec) + row;
-  st16(&r->c[0], u32x4{uint32_t(__double2loint(c[0])), uint32_t(__double2hiint(c[0])),
-                       uint32_t(__double2loint(c[1])), uint32_t(__double2hiint(c[1]))});
-  st16(&r->c[2], u32x4{uint32_t(__double2loint(c[2])), uint32_t(__double2hiint(c[2])),
-                       uint32_t(__double2loint(c[3])), uint32_t(__double2hiint(c[3]))});
-  st16(&r->s[0], u32x4{uint32_t(ss[0]), uint32_t(ss[1]), uint32_t(ss[2]), uint32_t(ss[3])});
-  st16(&r->p[0], u32x4{uint32_t(pp[0]), uint32_t(pp[1]), uint32_t(pp[2]), uint32_t(pp[3])});
+#pragma unroll
+  for (int k = 0; k < PK; ++k) st16(rec_at(a, row) + 16 * k, ent_pack(c[k], ss[k], pp[k]));
+}
+
+__device__ __forceinline__ void rec_store_stale(const PrefillMergeArgs &a, int64_t row, double bound) {
+#pragma unroll
+  for (int k = 0; k < PK; ++k) st16(rec_at(a, row) + 16 * k, ent_pack(bound, STALE, NOPOS));
 }
 
 template <typename T>
@@ -111,11 +164,12 @@ __global__ __launch_bounds__(256) void k_pm_prep(PrefillMergeArgs p) {
       n = fma(x, x, n);
     }
   }
-  p.norm[slot] = sqrt(n);
-  p.cand[slot] = (i < L && p.pos[slot] < p.protect_from) ? 1 : 0;
-  const double nc[PK] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  const int np[PK] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff}, ns[PK] = {-1, -1, -1, -1};
-  rec_store(p, slot, nc, np, ns);
+  const int pos = p.pos[slot];
+  st16(meta_at(p, slot), ent_pack(sqrt(n), pos, (i < L && pos < p.protect_from) ? 1 : 0));
+  double c[PK];
+  int pp[PK], ss[PK];
+  list_clear(c, pp, ss);
+  rec_store(p, slot, c, pp, ss);
   if (i < L) p.evict[slot] = 0;
 }
 
@@ -140,7 +194,7 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
   const T *Kb = reinterpret_cast<const T *>(p.k) + int64_t(sc) * p.scope_stride * HD;
   for (int e = tid; e < PM_ROWS * HD; e += PM_NT) {
     const int r = e >> 7, b = e & 127, row = rb + r;
-    const double v = (row < L && p.cand[so + row]) ? double(load_elem<T>(Kb, int64_t(row) * HD + b)) : 0.0;
+    const double v = (row < L && pm_cand(p, so + row)) ? double(load_elem<T>(Kb, int64_t(row) * HD + b)) : 0.0;
     fm_put_t(sh.op, r, b, v);
   }
   const int jl = lane & 15, tq = lane >> 4;
@@ -151,8 +205,8 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
 #pragma unroll
   for (int ct = 0; ct < PM_CT; ++ct) {
     const int row = rb + 16 * ct + jl;
-    rc[ct] = row < L && p.cand[so + row];
-    nrow[ct] = rc[ct] ? p.norm[so + row] : 0.0;
+    rc[ct] = row < L && pm_cand(p, so + row);
+    nrow[ct] = rc[ct] ? pm_norm(p, so + row) : 0.0;
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
       lc[ct][k] = -INFINITY;
@@ -179,8 +233,8 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
     for (int r = 0; r < 4; ++r) {
       const int j = tb + tq + 4 * r;
       const int jc = min(j, L - 1);
-      const bool cj = j < L && p.cand[so + jc];
-      const double nj = p.norm[so + jc];
+      const bool cj = j < L && pm_cand(p, so + jc);
+      const double nj = pm_norm(p, so + jc);
       const int pj = p.pos[so + jc];
 #pragma unroll
       for (int ct = 0; ct < PM_CT; ++ct) {
@@ -223,7 +277,7 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
       }
   }
   __syncthreads();
-  if (tid < PM_ROWS && rb + tid < L && p.cand[so + rb + tid]) {
+  if (tid < PM_ROWS && rb + tid < L && pm_cand(p, so + rb + tid)) {
     double c[PK];
     int pp[PK], ss[PK];
 #pragma unroll
@@ -240,320 +294,566 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
   }
 }
 
-struct LoopLds {
-  double kn[HD];            // the key whose row is being computed (float64)
-  double red_c[PM_LOOP / 64];
-  int red_p[PM_LOOP / 64], red_s[PM_LOOP / 64], red_t[PM_LOOP / 64];
-  double lbar[2];
-  double wgt[4];
-  int orph[PM_ORPH];
-  int n_orph;
-  double nk;
-  double top_c[PK];
-  int top_s[PK], top_p[PK];
+// The 8 elements [8 e, 8 e + 8) of a key row (16 lanes per row).
+template <typename T>
+struct Chunk8;
+template <>
+struct Chunk8<bf16_t> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const char *row, int e) { w = ld16(row + 16 * e); }
+  __device__ __forceinline__ void zero() { w = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ double get(int u) const { return double(ElemTraits<bf16_t>::get(w, u)); }
+};
+template <>
+struct Chunk8<float> {
+  u32x4 w0, w1;
+  __device__ __forceinline__ void load(const char *row, int e) {
+    w0 = ld16(row + 32 * e);
+    w1 = ld16(row + 32 * e + 16);
+  }
+  __device__ __forceinline__ void zero() { w0 = w1 = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ double get(int u) const { return double(ElemTraits<float>::get(u < 4 ? w0 : w1, u & 3)); }
 };
 
-// Workgroup-wide best (c, p) by pm_better over the threads' offers; winner's slot in
-// red_s[0] and thread in red_t[0].
-__device__ __forceinline__ void loop_argmax(LoopLds &sh, double c, int pp, int ss, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  int tt = tid;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double c2 = __shfl_xor(c, o);
-    const int p2 = __shfl_xor(pp, o), s2 = __shfl_xor(ss, o), t2 = __shfl_xor(tt, o);
-    if (s2 >= 0 && (ss < 0 || pm_better(c2, p2, c, pp))) {
-      c = c2;
-      pp = p2;
-      ss = s2;
-      tt = t2;
-    }
+// A value rounded to the cache dtype, as a float.
+template <typename T>
+__device__ __forceinline__ float round_to(float x);
+template <>
+__device__ __forceinline__ float round_to<bf16_t>(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+template <>
+__device__ __forceinline__ float round_to<float>(float x) { return x; }
+
+struct LoopLds {
+  int live[PREFILL_MAX_ROWS];     // the scope's candidate slots (any order)
+  double qk[PL_NQ][HD];           // float64 keys of the pass's query rows
+  double qn[PL_NQ];
+  int qrow[PL_NQ], qpos[PL_NQ];
+  double hc[PL_W], hu1[PL_W], hu2[PL_W];              // per-wave head and stale-bound reductions
+  int hp[PL_W], hs[PL_W], hsj[PL_W], hpj[PL_W];
+  double lc[PL_NQ][PL_W][PK];                         // per-wave best partners of the query rows
+  int lp[PL_NQ][PL_W][PK], ls[PL_NQ][PL_W][PK];
+  int todo[PL_TODO];
+  int n_todo, n_live, gidx;
+};
+
+// The best list head (largest cosine, ties to the lower row position) and the two largest
+// stale bounds seen so far.
+struct Heads {
+  double c, u1, u2;
+  int p, s, sj, pj;   // row position, row slot, partner slot, partner position
+  __device__ __forceinline__ void clear() {
+    c = u1 = u2 = -INFINITY;
+    p = pj = NOPOS;
+    s = sj = -1;
   }
+  __device__ __forceinline__ void offer(double c0, int pi, int row, int s0, int p0) {
+    if (s >= 0 && !pm_better(c0, pi, c, p)) return;
+    c = c0;
+    p = pi;
+    s = row;
+    sj = s0;
+    pj = p0;
+  }
+  __device__ __forceinline__ void bound(double b) {
+    const double n1 = fmax(u1, b), n2 = fmax(u2, fmin(u1, b));
+    u1 = n1;
+    u2 = n2;
+  }
+  // a row's list as loaded or rewritten: entry 0 is its head, or its stale bound
+  __device__ __forceinline__ void row(double c0, int s0, int p0, int pi, int r) {
+    if (s0 >= 0) offer(c0, pi, r, s0, p0);
+    else if (s0 == STALE) bound(c0);
+  }
+  __device__ __forceinline__ void take(const Heads &o) {
+    if (o.s >= 0) offer(o.c, o.p, o.s, o.sj, o.pj);
+    const double n1 = fmax(u1, o.u1), n2 = fmax(fmin(u1, o.u1), fmax(u2, o.u2));
+    u1 = n1;
+    u2 = n2;
+  }
+  __device__ __forceinline__ Heads xor_lane(int o) const {
+    Heads h;
+    h.c = __shfl_xor(c, o);
+    h.u1 = __shfl_xor(u1, o);
+    h.u2 = __shfl_xor(u2, o);
+    h.p = __shfl_xor(p, o);
+    h.s = __shfl_xor(s, o);
+    h.sj = __shfl_xor(sj, o);
+    h.pj = __shfl_xor(pj, o);
+    return h;
+  }
+};
+
+// Wave reduction of the lanes' Heads, written to the LDS slot of the wave.
+__device__ __forceinline__ void heads_to_lds(LoopLds &sh, Heads h, int lane, int wave) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) h.take(h.xor_lane(o));
   if (lane == 0) {
-    sh.red_c[wave] = c;
-    sh.red_p[wave] = pp;
-    sh.red_s[wave] = ss;
-    sh.red_t[wave] = tt;
+    sh.hc[wave] = h.c;
+    sh.hu1[wave] = h.u1;
+    sh.hu2[wave] = h.u2;
+    sh.hp[wave] = h.p;
+    sh.hs[wave] = h.s;
+    sh.hsj[wave] = h.sj;
+    sh.hpj[wave] = h.pj;
   }
-  __syncthreads();
-  if (tid == 0) {
-    for (int w = 1; w < PM_LOOP / 64; ++w)
-      if (sh.red_s[w] >= 0 && (sh.red_s[0] < 0 || pm_better(sh.red_c[w], sh.red_p[w], sh.red_c[0], sh.red_p[0]))) {
-        sh.red_c[0] = sh.red_c[w];
-        sh.red_p[0] = sh.red_p[w];
-        sh.red_s[0] = sh.red_s[w];
-        sh.red_t[0] = sh.red_t[w];
-      }
-  }
-  __syncthreads();
 }
 
-// The PK best of the threads' sorted local lists, by PK rounds of a workgroup argmax over the
-// lists' heads; written to row `row`'s list.
-__device__ __forceinline__ void loop_topk(const PrefillMergeArgs &p, LoopLds &sh, int64_t so, int row,
-                                          const double (&lc)[PK], const int (&lp)[PK], const int (&ls)[PK],
-                                          int tid) {
-  int h = 0;
+// The waves' Heads from LDS, combined in wave order (every thread gets the same result).
+__device__ __forceinline__ void heads_from_lds(const LoopLds &sh, Heads &h) {
+#pragma unroll
+  for (int w = 0; w < PL_W; ++w) {
+    Heads o;
+    o.c = sh.hc[w];
+    o.u1 = sh.hu1[w];
+    o.u2 = sh.hu2[w];
+    o.p = sh.hp[w];
+    o.s = sh.hs[w];
+    o.sj = sh.hsj[w];
+    o.pj = sh.hpj[w];
+    h.take(o);
+  }
+}
+
+// The PK best entries of the union of the lanes' sorted lists (distinct rows), by PK
+// rounds of a wave argmax over the lists' heads; the winning lane drops its head. Every
+// lane receives the result.
+__device__ __forceinline__ void wave_topk(double (&lc)[PK], int (&lp)[PK], int (&ls)[PK], int lane,
+                                          double (&oc)[PK], int (&op)[PK], int (&os)[PK]) {
+#pragma unroll
   for (int k = 0; k < PK; ++k) {
-    double c = -INFINITY;
-    int pp = 0x7fffffff, ss = -1;
+    double c = lc[0];
+    int pp = lp[0], ss = ls[0], who = lane;
 #pragma unroll
-    for (int q = 0; q < PK; ++q)
-      if (q == h) {
-        c = lc[q];
-        pp = lp[q];
-        ss = ls[q];
+    for (int o = 1; o < 64; o <<= 1) {
+      const double c2 = __shfl_xor(c, o);
+      const int p2 = __shfl_xor(pp, o), s2 = __shfl_xor(ss, o), w2 = __shfl_xor(who, o);
+      if (s2 >= 0 && (ss < 0 || pm_better(c2, p2, c, pp))) {
+        c = c2;
+        pp = p2;
+        ss = s2;
+        who = w2;
       }
-    loop_argmax(sh, c, pp, ss, tid);
-    if (tid == 0) {
-      sh.top_c[k] = sh.red_c[0];
-      sh.top_s[k] = sh.red_s[0];
-      sh.top_p[k] = sh.red_p[0];
     }
-    if (sh.red_s[0] >= 0 && sh.red_t[0] == tid) ++h;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    double c[PK];
-    int pp[PK], ss[PK];
+    oc[k] = c;
+    op[k] = pp;
+    os[k] = ss;
+    const bool pop = ss >= 0 && who == lane;
 #pragma unroll
-    for (int k = 0; k < PK; ++k) {
-      c[k] = sh.top_c[k];
-      ss[k] = sh.top_s[k];
-      pp[k] = sh.top_s[k] >= 0 ? sh.top_p[k] : 0x7fffffff;
+    for (int x = 0; x < PK - 1; ++x) {
+      lc[x] = pop ? lc[x + 1] : lc[x];
+      lp[x] = pop ? lp[x + 1] : lp[x];
+      ls[x] = pop ? ls[x + 1] : ls[x];
     }
-    rec_store(p, so + row, c, pp, ss);
+    lc[PK - 1] = pop ? -INFINITY : lc[PK - 1];
+    lp[PK - 1] = pop ? NOPOS : lp[PK - 1];
+    ls[PK - 1] = pop ? -1 : ls[PK - 1];
   }
 }
 
-// cos(kn, k_j) for a candidate j (kn in LDS, norm sh.nk).
-template <typename T>
-__device__ __forceinline__ double loop_cos(const PrefillMergeArgs &p, const LoopLds &sh, const T *Kb, int64_t so,
-                                           int j) {
-  constexpr int EPV = ElemTraits<T>::EPV;
-  const char *row = reinterpret_cast<const char *>(Kb + int64_t(j) * HD);
-  double dot = 0.0;
-#pragma unroll 4
-  for (int v = 0; v < HD / EPV; ++v) {
-    const u32x4 w = ld16(row + 16 * v);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) dot = fma(sh.kn[v * EPV + e], double(ElemTraits<T>::get(w, e)), dot);
-  }
-  const double den = sh.nk * p.norm[so + j];
-  return den > 0.0 ? dot / den : 0.0;
-}
-
-// Full list of row `row` (its key in sh.kn, norm sh.nk) over the candidates.
-template <typename T>
-__device__ __forceinline__ void loop_row(const PrefillMergeArgs &p, LoopLds &sh, const T *Kb, int64_t so, int L,
-                                         int row, int tid) {
+// The final list of query row q from the waves' lists in LDS (every lane of the calling
+// wave receives it).
+__device__ __forceinline__ void final_list(const LoopLds &sh, int q, int lane, double (&c)[PK], int (&pp)[PK],
+                                           int (&ss)[PK]) {
   double lc[PK];
   int lp[PK], ls[PK];
+  list_clear(lc, lp, ls);
+  if (lane < PL_W * PK) {   // lane 4 w + k holds entry k of wave w's list
+    lc[0] = sh.lc[q][lane / PK][lane % PK];
+    lp[0] = sh.lp[q][lane / PK][lane % PK];
+    ls[0] = sh.ls[q][lane / PK][lane % PK];
+  }
+  wave_topk(lc, lp, ls, lane, c, pp, ss);
+}
+
+// Full scan of the candidates' records: heads and stale bounds (ends with a barrier; every
+// thread receives the result).
+__device__ __forceinline__ void scan_heads(const PrefillMergeArgs &p, LoopLds &sh, int64_t so, int n_live, int tid,
+                                           Heads &h) {
+  const int lane = tid & 63, wave = tid >> 6;
+  Heads m;
+  m.clear();
+  for (int k0 = 0; k0 < n_live; k0 += PL_NT * PL_SCAN) {
+    int jr[PL_SCAN];
+    u32x4 er[PL_SCAN], mr[PL_SCAN];
 #pragma unroll
-  for (int k = 0; k < PK; ++k) {
-    lc[k] = -INFINITY;
-    lp[k] = 0x7fffffff;
-    ls[k] = -1;
+    for (int u = 0; u < PL_SCAN; ++u) {
+      const int k = k0 + u * PL_NT + tid;
+      jr[u] = k < n_live ? sh.live[k] : -1;
+      if (jr[u] >= 0) {
+        er[u] = ld16(rec_at(p, so + jr[u]));
+        mr[u] = ld16(meta_at(p, so + jr[u]));
+      } else {
+        er[u] = mr[u] = u32x4{0u, 0u, 0xffffffffu, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PL_SCAN; ++u)
+      if (jr[u] >= 0) m.row(ent_c(er[u]), int(er[u].z), int(er[u].w), int(mr[u].z), jr[u]);
   }
-  for (int j = tid; j < L; j += PM_LOOP) {
-    if (j == row || !p.cand[so + j]) continue;
-    pk_insert(lc, lp, ls, loop_cos<T>(p, sh, Kb, so, j), p.pos[so + j], j);
+  heads_to_lds(sh, m, lane, wave);
+  __syncthreads();
+  h.clear();
+  heads_from_lds(sh, h);
+}
+
+// Stale rows recomputed in full against every candidate: sh.qk / qn / qrow / qpos hold
+// nq (<= PL_NQ) of them. Lane e < NS of a 16-lane group owns the row of step e of each batch.
+template <typename T>
+__device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLds &sh, const char *Kc, int64_t so,
+                                               int n_live, int nq, int tid) {
+  constexpr int ES = sizeof(T), NS = PL_NS_R;
+  const int lane = tid & 63, wave = tid >> 6, e = lane & 15, gi = lane >> 4;
+  double qv[PL_NQ][8], qn[PL_NQ];
+  int qr[PL_NQ];
+#pragma unroll
+  for (int q = 0; q < PL_NQ; ++q) {
+    qn[q] = q < nq ? sh.qn[q] : 0.0;
+    qr[q] = q < nq ? sh.qrow[q] : -1;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) qv[q][v] = q < nq ? sh.qk[q][8 * e + v] : 0.0;
   }
-  loop_topk(p, sh, so, row, lc, lp, ls, tid);
+  double lc[PL_NQ][PK];
+  int lp[PL_NQ][PK], ls[PL_NQ][PK];
+#pragma unroll
+  for (int q = 0; q < PL_NQ; ++q) list_clear(lc[q], lp[q], ls[q]);
+  for (int k0 = 0; k0 < n_live; k0 += PL_W * 4 * NS) {
+    Chunk8<T> kc[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int k = k0 + (wave * NS + u) * 4 + gi;
+      if (k < n_live) kc[u].load(Kc + int64_t(sh.live[k]) * HD * ES, e);
+      else kc[u].zero();
+    }
+    const int ko = k0 + (wave * NS + e) * 4 + gi;
+    const int jo = (e < NS && ko < n_live) ? sh.live[ko] : -1;
+    u32x4 mt = u32x4{0u, 0u, 0u, 0u};
+    if (jo >= 0) mt = ld16(meta_at(p, so + jo));
+    double mine[PL_NQ];
+#pragma unroll
+    for (int q = 0; q < PL_NQ; ++q) mine[q] = 0.0;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      double x[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) x[v] = kc[u].get(v);
+#pragma unroll
+      for (int q = 0; q < PL_NQ; ++q) {
+        double dot = 0.0;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) dot = fma(qv[q][v], x[v], dot);
+        dot = group_sum_f64<16>(dot);
+        mine[q] = e == u ? dot : mine[q];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one step's conversions live at a time
+    }
+    if (jo >= 0) {
+      const double nj = ent_c(mt);
+      const int pj = int(mt.z);
+#pragma unroll
+      for (int q = 0; q < PL_NQ; ++q) {
+        const double den = qn[q] * nj;
+        const double cs = den > 0.0 ? mine[q] / den : 0.0;
+        if (q < nq && jo != qr[q]) pk_insert(lc[q], lp[q], ls[q], cs, pj, jo);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < PL_NQ; ++q) {
+    double c[PK];
+    int pp[PK], ss[PK];
+    wave_topk(lc[q], lp[q], ls[q], lane, c, pp, ss);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < PK; ++k) {
+        sh.lc[q][wave][k] = c[k];
+        sh.lp[q][wave][k] = pp[k];
+        sh.ls[q][wave][k] = ss[k];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int q = 0; q < nq; ++q) {
+      double c[PK];
+      int pp[PK], ss[PK];
+      final_list(sh, q, lane, c, pp, ss);
+      if (lane == 0) rec_store(p, so + sh.qrow[q], c, pp, ss);
+    }
+  }
+  __syncthreads();
 }
 
 template <typename T>
-__global__ __launch_bounds__(PM_LOOP) void k_pm_loop(PrefillMergeArgs p) {
+__global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
   __shared__ LoopLds sh;
+  constexpr int ES = sizeof(T), NS = PL_NS;
   const int sc = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = lane & 15, gi = lane >> 4;
   const int L = min(p.len[sc], p.capacity);
   const int64_t so = int64_t(sc) * p.capacity;
   T *Kw = reinterpret_cast<T *>(p.k) + int64_t(sc) * p.scope_stride * HD;
   T *Vw = reinterpret_cast<T *>(p.v) + int64_t(sc) * p.scope_stride * HD;
   const T *Kb = Kw;
+  const char *Kc = reinterpret_cast<const char *>(Kb);
   int live = L, merged = 0;
+  if (live <= p.budget) {
+    if (tid == 0 && p.n_merged) p.n_merged[sc] = 0;
+    return;
+  }
+  // ---- the candidate list, then the heads of the initial lists
+  if (tid == 0) sh.n_live = 0;
+  __syncthreads();
+  for (int i = tid; i < L; i += PL_NT)
+    if (pm_cand(p, so + i)) {
+      const int k = atomicAdd(&sh.n_live, 1);
+      if (k < PREFILL_MAX_ROWS) sh.live[k] = i;
+    }
+  __syncthreads();
+  int n_live = min(sh.n_live, PREFILL_MAX_ROWS);
+  Heads h;
+  scan_heads(p, sh, so, n_live, tid, h);
+  int rounds = 0;   // recomputation rounds since the last merge (each one clears >= 2 stale rows)
   while (live > p.budget) {
-    // ---- the pair: the row whose list head is largest (ties to the lower position) and that head
-    {
-      double c = -INFINITY;
-      int pp = 0x7fffffff, ss = -1;
-      for (int i = tid; i < L; i += PM_LOOP) {
-        if (!p.cand[so + i]) continue;
-        const PmRec *r = reinterpret_cast<const PmRec *>(p.rec) + so + i;
-        if (r->s[0] < 0) continue;
-        const double ci = r->c[0];
-        const int pi = p.pos[so + i];
-        if (pm_better(ci, pi, c, pp)) {
-          c = ci;
-          pp = pi;
-          ss = i;
+    // ---- two stale rows might form a pair at least as good as the best head: recompute the
+    // stale rows whose bound reaches it, then scan again
+    if (h.u2 > -INFINITY && h.u2 >= h.c) {
+      if (++rounds > n_live) {   // cannot happen: stop rather than loop
+        if (tid == 0) p.status[0] = -7;
+        break;
+      }
+      if (tid == 0) sh.n_todo = 0;
+      __syncthreads();
+      for (int k = tid; k < n_live; k += PL_NT) {
+        const int j = sh.live[k];
+        const u32x4 w = ld16(rec_at(p, so + j));
+        if (int(w.z) == STALE && ent_c(w) >= h.c) {
+          const int t = atomicAdd(&sh.n_todo, 1);
+          if (t < PL_TODO) sh.todo[t] = j;
         }
       }
-      loop_argmax(sh, c, pp, ss, tid);
+      __syncthreads();
+      const int nt = min(sh.n_todo, PL_TODO);
+      for (int b = 0; b < nt; b += PL_NQ) {
+        const int nq = min(PL_NQ, nt - b);
+        if (tid < nq * HD) {
+          const int q = tid / HD, x = tid % HD, row = sh.todo[b + q];
+          sh.qk[q][x] = double(load_elem<T>(Kb, int64_t(row) * HD + x));
+          if (x == 0) {
+            const u32x4 m = ld16(meta_at(p, so + row));
+            sh.qn[q] = ent_c(m);
+            sh.qrow[q] = row;
+            sh.qpos[q] = int(m.z);
+          }
+        }
+        __syncthreads();
+        pass_recompute<T>(p, sh, Kc, so, n_live, nq, tid);
+      }
+      scan_heads(p, sh, so, n_live, tid, h);
+      continue;
     }
-    const int si = sh.red_s[0];
-    if (si < 0) {   // fewer than two entries may merge: the budget cannot be reached
+    if (h.s < 0) {   // fewer than two entries may merge: the budget cannot be reached
       if (tid == 0) p.status[0] = -4;
       break;
     }
-    const int sj = (reinterpret_cast<const PmRec *>(p.rec) + so + si)->s[0];
+    if (h.sj >= L) {   // cannot happen: every list entry is a live candidate
+      if (tid == 0) p.status[0] = -7;
+      break;
+    }
+    rounds = 0;
     // the older entry of the pair survives; the other is removed
-    const bool older = p.pos[so + si] < p.pos[so + sj];
-    const int surv = older ? si : sj, gone = older ? sj : si;
-    // ---- reference logits of the two entries (group-mean query)
-    if (wave < 2) {
-      const int x = wave == 0 ? gone : surv;
+    const bool older = h.p < h.pj;
+    const int surv = older ? h.s : h.sj, gone = older ? h.sj : h.s, ps = older ? h.p : h.pj;
+    // ---- the merge (wave 0; two elements per lane)
+    if (wave == 0) {
+      const int e0 = lane, e1 = lane + 64;
       const T *q = reinterpret_cast<const T *>(p.q) + int64_t(sc) * p.G * HD;
-      double acc = 0.0;
-      for (int j = lane; j < HD; j += 64) {
-        const double kx = double(load_elem<T>(Kb, int64_t(x) * HD + j));
-        double qs = 0.0;
-        for (int g = 0; g < p.G; ++g) qs += double(load_elem<T>(q, g * HD + j)) * kx;
-        acc += qs;
+      const double kg0 = double(load_elem<T>(Kb, int64_t(gone) * HD + e0));
+      const double kg1 = double(load_elem<T>(Kb, int64_t(gone) * HD + e1));
+      const double kc0 = double(load_elem<T>(Kb, int64_t(surv) * HD + e0));
+      const double kc1 = double(load_elem<T>(Kb, int64_t(surv) * HD + e1));
+      const double vg0 = double(load_elem<T>(Vw, int64_t(gone) * HD + e0));
+      const double vg1 = double(load_elem<T>(Vw, int64_t(gone) * HD + e1));
+      const double vc0 = double(load_elem<T>(Vw, int64_t(surv) * HD + e0));
+      const double vc1 = double(load_elem<T>(Vw, int64_t(surv) * HD + e1));
+      const int vote_e = p.votes[so + gone], vote_c = p.votes[so + surv];
+      const float m_e = p.m ? p.m[so + gone] : 0.0f, m_c = p.m ? p.m[so + surv] : 0.0f;
+      double ae = 0.0, ac = 0.0;
+      for (int g = 0; g < p.G; ++g) {
+        const double q0 = double(load_elem<T>(q, g * HD + e0)), q1 = double(load_elem<T>(q, g * HD + e1));
+        ae += q0 * kg0 + q1 * kg1;
+        ac += q0 * kc0 + q1 * kc1;
       }
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
-      if (lane == 0) sh.lbar[wave] = acc * p.scale / double(p.G);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      const double le = sh.lbar[0], lc = sh.lbar[1];
+      for (int o = 1; o < 64; o <<= 1) {
+        ae += __shfl_xor(ae, o);
+        ac += __shfl_xor(ac, o);
+      }
+      // reference logits of the two entries (group-mean query) and the ZIP weights
+      const double le = ae * p.scale / double(p.G), lc = ac * p.scale / double(p.G);
       const double mu = fmax(le, lc);
-      const double pe = double(p.votes[so + gone]), pc = double(p.votes[so + surv]);
+      const double pe = double(vote_e), pc = double(vote_c);
       const double we = pe * exp(le - mu), wc = pc * exp(lc - mu);
       const double num = mu + log(we + wc) - log(pe + pc);
       const double den = we * le + wc * lc;
       const bool guarded = fabs(den) < double(p.eps) * exp(-mu);
-      sh.wgt[0] = we / (we + wc);
-      sh.wgt[1] = wc / (we + wc);
-      sh.wgt[2] = guarded ? 0.5 : we * num / den;
-      sh.wgt[3] = guarded ? 0.5 : wc * num / den;
-    }
-    __syncthreads();
-    if (tid < HD) {   // element tid of the two rows; the merged row rounded to the cache dtype
-      const double kek = double(load_elem<T>(Kb, int64_t(gone) * HD + tid));
-      const double kck = double(load_elem<T>(Kb, int64_t(surv) * HD + tid));
-      const double vek = double(load_elem<T>(Vw, int64_t(gone) * HD + tid));
-      const double vck = double(load_elem<T>(Vw, int64_t(surv) * HD + tid));
-      store_elem<T>(Kw, int64_t(surv) * HD + tid, float(sh.wgt[2] * kek + sh.wgt[3] * kck));
-      store_elem<T>(Vw, int64_t(surv) * HD + tid, float(sh.wgt[0] * vek + sh.wgt[1] * vck));
-      sh.kn[tid] = double(load_elem<T>(Kw, int64_t(surv) * HD + tid));
-    }
-    if (tid == 0) {
-      p.votes[so + surv] += p.votes[so + gone];
-      if (p.m) p.m[so + surv] += p.m[so + gone];
-      p.cand[so + gone] = 0;
-      p.evict[so + gone] = 1;
-      if (p.pairs) {
-        p.pairs[(so + merged) * 2] = surv;
-        p.pairs[(so + merged) * 2 + 1] = gone;
-      }
-      sh.n_orph = 0;
-    }
-    __threadfence_block();
-    __syncthreads();
-    if (wave == 0) {
-      double n = 0.0;
-      for (int b = lane; b < HD; b += 64) n = fma(sh.kn[b], sh.kn[b], n);
+      const double wv0 = we / (we + wc), wv1 = wc / (we + wc);
+      const double wk0 = guarded ? 0.5 : we * num / den, wk1 = guarded ? 0.5 : wc * num / den;
+      // the merged rows, rounded to the cache dtype
+      const float k0 = round_to<T>(float(wk0 * kg0 + wk1 * kc0)), k1 = round_to<T>(float(wk0 * kg1 + wk1 * kc1));
+      store_elem<T>(Kw, int64_t(surv) * HD + e0, k0);
+      store_elem<T>(Kw, int64_t(surv) * HD + e1, k1);
+      store_elem<T>(Vw, int64_t(surv) * HD + e0, float(wv0 * vg0 + wv1 * vc0));
+      store_elem<T>(Vw, int64_t(surv) * HD + e1, float(wv0 * vg1 + wv1 * vc1));
+      sh.qk[0][e0] = double(k0);
+      sh.qk[0][e1] = double(k1);
+      double n2 = double(k0) * double(k0) + double(k1) * double(k1);
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) n += __shfl_xor(n, o);
+      for (int o = 1; o < 64; o <<= 1) n2 += __shfl_xor(n2, o);
       if (lane == 0) {
-        sh.nk = sqrt(n);
-        p.norm[so + surv] = sh.nk;
+        const double nk = sqrt(n2);
+        st16(meta_at(p, so + surv), ent_pack(nk, ps, 1));
+        reinterpret_cast<int *>(meta_at(p, so + gone))[3] = 0;
+        p.votes[so + surv] = vote_e + vote_c;
+        if (p.m) p.m[so + surv] = m_c + m_e;
+        p.evict[so + gone] = 1;
+        if (p.pairs) {
+          p.pairs[(so + merged) * 2] = surv;
+          p.pairs[(so + merged) * 2 + 1] = gone;
+        }
+        sh.qn[0] = nk;
       }
     }
     __syncthreads();
-    // ---- the merged entry against every candidate: its own list, and every other row drops the
-    // two merged entries and takes the merged one when it beats its last entry; rows left
-    // with an empty list are recomputed in full
+    // ---- the merged key against every candidate: its own list, the other rows' lists, and
+    // the heads for the next merge
     {
-      const int ps = p.pos[so + surv];
+      const double nk = sh.qn[0];
+      double qv[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) qv[v] = sh.qk[0][8 * e + v];
       double lc[PK];
       int lp[PK], ls[PK];
+      list_clear(lc, lp, ls);
+      Heads hn;
+      hn.clear();
+      for (int k0 = 0; k0 < n_live; k0 += PL_W * 4 * NS) {
+        Chunk8<T> kc[NS];
 #pragma unroll
-      for (int k = 0; k < PK; ++k) {
-        lc[k] = -INFINITY;
-        lp[k] = 0x7fffffff;
-        ls[k] = -1;
+        for (int u = 0; u < NS; ++u) {
+          const int k = k0 + (wave * NS + u) * 4 + gi;
+          if (k < n_live) kc[u].load(Kc + int64_t(sh.live[k]) * HD * ES, e);
+          else kc[u].zero();
+        }
+        // this lane's row: step e of its group
+        const int ko = k0 + (wave * NS + e) * 4 + gi;
+        const int jo = (e < NS && ko < n_live) ? sh.live[ko] : -1;
+        u32x4 mt = u32x4{0u, 0u, 0u, 0u}, r0, r1, r2, r3;
+        r0 = r1 = r2 = r3 = u32x4{0u, 0u, 0xffffffffu, 0u};
+        if (jo >= 0) {
+          mt = ld16(meta_at(p, so + jo));
+          r0 = ld16(rec_at(p, so + jo));
+          r1 = ld16(rec_at(p, so + jo) + 16);
+          r2 = ld16(rec_at(p, so + jo) + 32);
+          r3 = ld16(rec_at(p, so + jo) + 48);
+        }
+        double mine = 0.0;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          double dot = 0.0;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) dot = fma(qv[v], kc[u].get(v), dot);
+          dot = group_sum_f64<16>(dot);
+          mine = e == u ? dot : mine;
+          __builtin_amdgcn_sched_barrier(0);   // one step's conversions live at a time
+        }
+        if (jo == gone) sh.gidx = ko;
+        if (jo >= 0 && jo != surv && jo != gone) {
+          const double nj = ent_c(mt);
+          const int pj = int(mt.z);
+          const double den = nk * nj;
+          const double cs = den > 0.0 ? mine / den : 0.0;
+          pk_insert(lc, lp, ls, cs, pj, jo);
+          double oc[PK] = {ent_c(r0), ent_c(r1), ent_c(r2), ent_c(r3)};
+          int os[PK] = {int(r0.z), int(r1.z), int(r2.z), int(r3.z)};
+          int opp[PK] = {int(r0.w), int(r1.w), int(r2.w), int(r3.w)};
+          // does the list change: an entry of the merged pair in it, the merged entry above
+          // one of its entries, or a list without entries
+          bool change = os[0] == -1;
+#pragma unroll
+          for (int k = 0; k < PK; ++k)
+            change |= os[k] >= 0 && (os[k] == surv || os[k] == gone || pm_better(cs, ps, oc[k], opp[k]));
+          if (change) {
+            double jc[PK];
+            int jp[PK], js[PK];
+            list_clear(jc, jp, js);
+            int n = 0;
+            bool any = false;
+            double last_c = -INFINITY, kept_c = -INFINITY;
+            int last_p = NOPOS, kept_p = NOPOS;
+#pragma unroll
+            for (int k = 0; k < PK; ++k) {
+              if (os[k] < 0) continue;
+              any = true;
+              last_c = oc[k];
+              last_p = opp[k];
+              if (os[k] == surv || os[k] == gone) continue;
+              pk_insert(jc, jp, js, oc[k], opp[k], os[k]);
+              kept_c = oc[k];
+              kept_p = opp[k];
+              ++n;
+            }
+            bool stale = false;
+            if (n > 0) {
+              // the merged entry joins when it ranks above the kept list's last entry
+              if (pm_better(cs, ps, kept_c, kept_p)) pk_insert(jc, jp, js, cs, ps, surv);
+            } else if (any && pm_better(cs, ps, last_c, last_p)) {
+              // every other partner ranks below the old last entry, so below the merged one
+              pk_insert(jc, jp, js, cs, ps, surv);
+            } else {
+              stale = true;
+            }
+            if (stale) {
+              const double b = any ? last_c : INFINITY;
+              rec_store_stale(p, so + jo, b);
+              jc[0] = b;
+              js[0] = STALE;
+            } else {
+              rec_store(p, so + jo, jc, jp, js);
+            }
+            hn.row(jc[0], js[0], jp[0], pj, jo);
+          } else {
+            hn.row(oc[0], os[0], opp[0], pj, jo);
+          }
+        }
       }
-      for (int j = tid; j < L; j += PM_LOOP) {
-        if (j == surv || !p.cand[so + j]) continue;
-        const double cs = loop_cos<T>(p, sh, Kb, so, j);
-        const int pj = p.pos[so + j];
-        pk_insert(lc, lp, ls, cs, pj, j);
-        // row j's list without the two merged entries (the kept entries stay in order)
-        double oc[PK];
-        int opp[PK], os[PK];
-        rec_load(p, so + j, oc, opp, os);
-        double jc[PK];
-        int jp[PK], js[PK];
+      // the merged row's list: best PK of the wave, then of the waves
+      double wc_[PK];
+      int wp_[PK], ws_[PK];
+      wave_topk(lc, lp, ls, lane, wc_, wp_, ws_);
+      if (lane == 0) {
 #pragma unroll
         for (int k = 0; k < PK; ++k) {
-          jc[k] = -INFINITY;
-          jp[k] = 0x7fffffff;
-          js[k] = -1;
+          sh.lc[0][wave][k] = wc_[k];
+          sh.lp[0][wave][k] = wp_[k];
+          sh.ls[0][wave][k] = ws_[k];
         }
-        int n = 0;
-        bool dropped = false;
-        double last_c = -INFINITY;
-        int last_p = 0x7fffffff;
-#pragma unroll
-        for (int k = 0; k < PK; ++k) {
-          if (os[k] < 0) continue;
-          if (os[k] == surv || os[k] == gone) {
-            dropped = true;
-            continue;
-          }
-          pk_insert(jc, jp, js, oc[k], opp[k], os[k]);
-          last_c = oc[k];
-          last_p = opp[k];
-          ++n;
-        }
-        if (n == 0) {
-          const int k = atomicAdd(&sh.n_orph, 1);
-          if (k < PM_ORPH) sh.orph[k] = j;
-          js[0] = -2;                      // recomputed below (in a later batch past PM_ORPH)
-          rec_store(p, so + j, jc, jp, js);
-          continue;
-        }
-        // the merged entry joins the list when it ranks above the list's last entry
-        const bool joins = pm_better(cs, ps, last_c, last_p);
-        if (joins) pk_insert(jc, jp, js, cs, ps, surv);
-        if (joins || dropped) rec_store(p, so + j, jc, jp, js);
       }
-      loop_topk(p, sh, so, surv, lc, lp, ls, tid);
+      heads_to_lds(sh, hn, lane, wave);
+      __syncthreads();
+      double fc[PK];
+      int fp[PK], fs[PK];
+      final_list(sh, 0, lane, fc, fp, fs);
+      if (tid == 0) {
+        rec_store(p, so + surv, fc, fp, fs);
+        const int g = sh.gidx;
+        if (g >= 0 && g < n_live && sh.live[g] == gone) sh.live[g] = sh.live[n_live - 1];
+        else p.status[0] = -7;   // cannot happen: the removed slot was a listed candidate
+      }
+      h.clear();
+      h.row(fc[0], fs[0], fp[0], ps, surv);
+      heads_from_lds(sh, h);
     }
-    __threadfence_block();
-    __syncthreads();
-    // ---- rows whose lists ran empty, in batches of PM_ORPH
-    for (;;) {
-      const int n = min(sh.n_orph, PM_ORPH);
-      for (int k = 0; k < n; ++k) {
-        const int o = sh.orph[k];
-        if (tid < HD) sh.kn[tid] = double(load_elem<T>(Kb, int64_t(o) * HD + tid));
-        if (tid == 0) sh.nk = p.norm[so + o];
-        __syncthreads();
-        loop_row<T>(p, sh, Kb, so, L, o, tid);
-        __threadfence_block();
-        __syncthreads();
-      }
-      const bool overflow = sh.n_orph > PM_ORPH;
-      __syncthreads();
-      if (!overflow) break;
-      if (tid == 0) sh.n_orph = 0;
-      __syncthreads();
-      for (int j = tid; j < L; j += PM_LOOP) {
-        PmRec *r = reinterpret_cast<PmRec *>(p.rec) + so + j;
-        if (p.cand[so + j] && r->s[0] == -2) {
-          const int k = atomicAdd(&sh.n_orph, 1);
-          if (k < PM_ORPH) {
-            sh.orph[k] = j;
-            r->s[0] = -1;
-          }
-        }
-      }
-      __syncthreads();
-    }
+    --n_live;
     --live;
     ++merged;
   }
@@ -567,12 +867,12 @@ hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_
   if (dtype == 0) {
     hipLaunchKernelGGL(k_pm_prep<bf16_t>, g1, dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_pm_rows<bf16_t>, g2, dim3(PM_NT), 0, st, p);
+    hipLaunchKernelGGL(k_pm_loop<bf16_t>, dim3(p.n_scopes), dim3(PL_NT), 0, st, p);
   } else {
     hipLaunchKernelGGL(k_pm_prep<float>, g1, dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_pm_rows<float>, g2, dim3(PM_NT), 0, st, p);
+    hipLaunchKernelGGL(k_pm_loop<float>, dim3(p.n_scopes), dim3(PL_NT), 0, st, p);
   }
-  if (dtype == 0) hipLaunchKernelGGL(k_pm_loop<bf16_t>, dim3(p.n_scopes), dim3(PM_LOOP), 0, st, p);
-  else hipLaunchKernelGGL(k_pm_loop<float>, dim3(p.n_scopes), dim3(PM_LOOP), 0, st, p);
   return hipGetLastError();
 }
 

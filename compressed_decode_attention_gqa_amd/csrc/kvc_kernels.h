@@ -55,6 +55,9 @@ struct MomentEvictArgs {
 };
 
 // KeepKV prefill compression by greedy all-pairs ZIP merging (per-KV-head scopes).
+// Candidates per scope that the prefill merging loop keeps listed in LDS.
+constexpr int PREFILL_MAX_ROWS = 32768;
+
 struct PrefillMergeArgs {
   char *k, *v;
   int64_t scope_stride;
@@ -67,9 +70,8 @@ struct PrefillMergeArgs {
   int32_t capacity, n_scopes, budget, protect_from;
   uint8_t *evict;
   int32_t *pairs, *n_merged;
-  double *norm;             // [n_scopes][capacity]
-  void *rec;                // [n_scopes][capacity] 64-byte partner lists (cosines, slots, positions)
-  uint8_t *cand;            // [n_scopes][capacity]
+  void *meta;               // [n_scopes][capacity] 16 bytes: key norm (float64), position, candidate flag
+  void *rec;                // [n_scopes][capacity] 64-byte partner lists: 4 x (cosine, slot, position)
   int32_t *status;
 };
 

@@ -207,8 +207,8 @@ int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const f
 /* kvc_keepkv_prefill_merge -- KeepKV prefill compression by greedy all-pairs
  * ZIP merging (reading notes on KeepKV: the inference algorithm's prefill steps
  * 2-5, "candidate choice", eqs. (7), (10), (12) and the numerical-stability
- * guard), per-KV-head scopes only (units_per_scope = 1, else
- * KVC_ERR_UNSUPPORTED). While a scope holds more than `budget` live entries,
+ * guard), per-KV-head scopes only (units_per_scope = 1) of capacity at most
+ * 32768 (else KVC_ERR_UNSUPPORTED). While a scope holds more than `budget` live entries,
  * the two entries whose keys have the largest cosine, both at positions below
  * protect_from (the most recent tokens are never merged), are ZIP-merged with
  * the reference logits of merge->q (the mean over its G query heads of
@@ -223,8 +223,10 @@ int32_t kvc_moment_evict(const kvc_cache *cache, const kvc_moments *mom, const f
  * must be non-NULL. Cosines are float64 (exact products of the cache values).
  * If fewer than two entries may merge before the budget is reached, the scope
  * stops there and the workspace status becomes KVC_ERR_CAPACITY. One
- * workgroup per scope runs the merges in sequence: each merge costs O(len d)
- * plus O(len d) per entry whose best partner was one of the pair. Workspace:
+ * workgroup per scope runs the merges in sequence: each merge reads every
+ * candidate key once (O(len d)); an entry whose kept partners were all merged
+ * away is recomputed (another O(len d), several entries per pass) only when
+ * it could take part in the next pair. Workspace:
  * kvc_keepkv_prefill_workspace_size. */
 int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge, int32_t budget,
                                  int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,

@@ -131,6 +131,8 @@ def test_keepkv_prefill_host_checks():
         return L.kvc_keepkv_prefill_merge(ctypes.byref(cache), ctypes.byref(m) if m is not None else None, budget,
                                           90, evict, None, None, ws, wsb, None)
     assert call(cache=_fake_cache(votes=0x7000, units_per_scope=2, unit_stride=100, scope_stride=200)) == -3
+    big = _fake_cache(votes=0x7000, capacity=32769, scope_stride=32769)
+    assert call(cache=big, wsb=L.kvc_keepkv_prefill_workspace_size(ctypes.byref(big))) == -3   # > 32768 slots
     assert call(cache=_fake_cache()) == -1                    # no votes
     assert call(m=None) == -1
     assert call(m=kvc._Merge(0x8000, 3, 0.1, 1e-6, 0)) == -3
