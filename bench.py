@@ -392,35 +392,39 @@ def run_prefill_merge(args):
     evict = torch.zeros((S, cache.capacity), dtype=torch.uint8, device=dev)
     n_merged = torch.zeros((S,), dtype=torch.int32, device=dev)
     ws = kvc.workspace(kvc.kvc_keepkv_prefill_workspace_size(cache), dev)
-    times = []
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in marks:
+        e.record()   # torch creates the event at its first record
+    stages = []   # per repetition: key norms and flags, initial lists, merge loop (ms)
     for rep in range(args.warmup + args.steps):
         for x, y in zip(fields, saved):
             x.copy_(y)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        start.record()
-        kvc.kvc_keepkv_prefill_merge(cache, merge, B, protect_from, evict, None, n_merged, ws=ws)
-        end.record()
+        kvc.kvc_keepkv_prefill_merge(cache, merge, B, protect_from, evict, None, n_merged, ws=ws, events=marks)
         torch.cuda.synchronize()
         if rep >= args.warmup:
-            times.append(start.elapsed_time(end))
+            stages.append([marks[i].elapsed_time(marks[i + 1]) for i in range(3)])
     if kvc.kvc_workspace_status(ws) != 0 or int(n_merged.min()) != L0 - B:
         raise SystemExit("prefill merge did not reach the budget")
-    ms = float(np.median(times))
-    # float64 work of the loop: the initial best partners (2 L0^2 d per head) and, per merge, the
-    # merged row against the live candidates (2 L d); recomputed orphan rows are not counted
-    cand0 = protect_from
-    flops = S * (2.0 * cand0 * cand0 * d + sum(2.0 * (cand0 - i) * d for i in range(L0 - B)))
-    ach = flops / (ms / 1e3) / 1e12
+    st = np.median(np.array(stages), axis=0)
+    ms = float(st.sum())
+    # algorithmic bytes of the merge loop (the dominant kernel): each merge reads the keys of the
+    # candidates other than the merged pair once, to get their cosines with the merged key
+    cand0, es = protect_from, 2 if wl.dtype == "bf16" else 4
+    loop_bytes = S * sum((cand0 - t - 2) * d * es for t in range(L0 - B))
+    ach = loop_bytes / (st[2] / 1e3) / 1e9
+    rows_flops = S * 2.0 * cand0 * cand0 * d
     result = {"metric": "KeepKV prefill compression: prompt tokens compressed/sec (greedy all-pairs ZIP merging)",
               "value": S * L0 / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
               "vs_baseline": None, "dtype": "bf16 cache; f64 cosines and merge weights", "data": "synthetic",
               "config": {"workload": wl.name, "heads": S, "prompt": L0, "budget": B, "protected": L0 - protect_from,
                          "merges_per_head": L0 - B, "G": wl.G},
-              "roofline": {"bound": "alu", "achieved": ach, "peak": rf.MI355X_FP64_VALU_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / rf.MI355X_FP64_VALU_TFLOPS, "traffic": None, "launch_ms": ms,
-                           "flops_per_launch": flops}}
+              "roofline": {"bound": "hbm", "achieved": ach, "peak": rf.MI355X_HBM_GBPS, "unit": "GB/s",
+                           "frac": ach / rf.MI355X_HBM_GBPS, "traffic": None, "kernel": "k_pm_loop",
+                           "launch_ms": float(st[2]), "bytes_per_launch": loop_bytes},
+              "stages_ms": {"prep": float(st[0]), "initial_lists": float(st[1]), "merge_loop": float(st[2])},
+              "initial_lists_fp64_tflops": rows_flops / (st[1] / 1e3) / 1e12}
     if not args.no_cpu_baseline:
         # the oracle on one head, for a bounded number of merges
         sc = 0

@@ -561,6 +561,15 @@ size_t kvc_keepkv_prefill_workspace_size(const kvc_cache *cache) {
 int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge, int32_t budget,
                                  int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,
                                  void *ws, size_t ws_bytes, void *stream) {
+  return kvc_keepkv_prefill_merge_marked(cache, merge, budget, protect_from, evict, pairs, n_merged, ws, ws_bytes,
+                                         stream, nullptr, 0);
+}
+
+int32_t kvc_keepkv_prefill_merge_marked(const kvc_cache *cache, const kvc_merge *merge, int32_t budget,
+                                        int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,
+                                        void *ws, size_t ws_bytes, void *stream, void *const *events,
+                                        int32_t n_events) {
+  if (events && n_events != 4) return KVC_ERR_ARG;
   int st = validate_cache(cache);
   if (st) return st;
   if (cache->units_per_scope != 1 || cache->capacity > kvc::PREFILL_MAX_ROWS) return KVC_ERR_UNSUPPORTED;
@@ -592,7 +601,8 @@ int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge,
   p.meta = at<char>(ws, l.meta);
   p.rec = at<char>(ws, l.rec);
   p.status = at<int32_t>(ws, l.status);
-  if (kvc::launch_prefill_merge(p, cache->dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+  hipEvent_t *marks = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
+  if (kvc::launch_prefill_merge(p, cache->dtype, static_cast<hipStream_t>(stream), marks) != hipSuccess)
     return KVC_ERR_DEVICE;
   return KVC_OK;
 }

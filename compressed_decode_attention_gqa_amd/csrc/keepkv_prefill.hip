@@ -862,17 +862,19 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
 
 }  // namespace
 
-hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st) {
+hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st, hipEvent_t *marks) {
   const dim3 g1((p.capacity + 255) / 256, p.n_scopes), g2((p.capacity + PM_ROWS - 1) / PM_ROWS, p.n_scopes);
-  if (dtype == 0) {
-    hipLaunchKernelGGL(k_pm_prep<bf16_t>, g1, dim3(256), 0, st, p);
-    hipLaunchKernelGGL(k_pm_rows<bf16_t>, g2, dim3(PM_NT), 0, st, p);
-    hipLaunchKernelGGL(k_pm_loop<bf16_t>, dim3(p.n_scopes), dim3(PL_NT), 0, st, p);
-  } else {
-    hipLaunchKernelGGL(k_pm_prep<float>, g1, dim3(256), 0, st, p);
-    hipLaunchKernelGGL(k_pm_rows<float>, g2, dim3(PM_NT), 0, st, p);
-    hipLaunchKernelGGL(k_pm_loop<float>, dim3(p.n_scopes), dim3(PL_NT), 0, st, p);
-  }
+  const bool bf = dtype == 0;
+  if (marks) hipEventRecord(marks[0], st);
+  if (bf) hipLaunchKernelGGL(k_pm_prep<bf16_t>, g1, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL(k_pm_prep<float>, g1, dim3(256), 0, st, p);
+  if (marks) hipEventRecord(marks[1], st);
+  if (bf) hipLaunchKernelGGL(k_pm_rows<bf16_t>, g2, dim3(PM_NT), 0, st, p);
+  else hipLaunchKernelGGL(k_pm_rows<float>, g2, dim3(PM_NT), 0, st, p);
+  if (marks) hipEventRecord(marks[2], st);
+  if (bf) hipLaunchKernelGGL(k_pm_loop<bf16_t>, dim3(p.n_scopes), dim3(PL_NT), 0, st, p);
+  else hipLaunchKernelGGL(k_pm_loop<float>, dim3(p.n_scopes), dim3(PL_NT), 0, st, p);
+  if (marks) hipEventRecord(marks[3], st);
   return hipGetLastError();
 }
 

@@ -86,7 +86,8 @@ hipError_t launch_moment_update_mfma(const CacheArgs &c, const uint8_t *evict, i
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st);
 hipError_t launch_moment_correct(const MomentArgs &m, int n_units, const void *q, int dtype, int G, double scale,
                                  const float *f_R, const float *lse_R, float *out, hipStream_t st);
-hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st);
+// marks: NULL, or 4 events recorded before the first kernel and after each of the three.
+hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st, hipEvent_t *marks);
 hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);

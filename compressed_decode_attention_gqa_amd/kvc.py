@@ -22,6 +22,7 @@ DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
 EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
+            "kvc_keepkv_prefill_merge_marked",
             "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
             "kvc_decode_workspace_size",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
@@ -66,6 +67,7 @@ _SIGS = {
     "kvc_moment_correct": (_I, [_P, _I, _P, _I, _I, _F, _P, _P, _P, _P]),
     "kvc_moment_evict": (_I, [_P, _P, _P, _F, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "kvc_keepkv_prefill_merge": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "kvc_keepkv_prefill_merge_marked": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _I]),
     "kvc_laprox_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
@@ -270,11 +272,20 @@ def kvc_moment_evict(cache: Cache, moments: Moments, alpha, scale: float, budget
 
 
 def kvc_keepkv_prefill_merge(cache: Cache, merge: _Merge, budget: int, protect_from: int, evict, pairs=None,
-                             n_merged=None, ws: torch.Tensor = None, stream=None):
+                             n_merged=None, ws: torch.Tensor = None, stream=None, events=None):
+    """events: None, or 4 recorded-once torch.cuda.Event(enable_timing=True) objects, re-recorded
+    on the launch stream before the first kernel and after each of the three."""
     d = cache.desc()
-    _check("kvc_keepkv_prefill_merge", lib().kvc_keepkv_prefill_merge(
+    nbytes = ws.numel() if ws is not None else 0
+    if events is None:
+        _check("kvc_keepkv_prefill_merge", lib().kvc_keepkv_prefill_merge(
+            ctypes.byref(d), ctypes.byref(merge), budget, protect_from, _ptr(evict), _ptr(pairs), _ptr(n_merged),
+            _ptr(ws), nbytes, _stream(stream)))
+        return
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("kvc_keepkv_prefill_merge_marked", lib().kvc_keepkv_prefill_merge_marked(
         ctypes.byref(d), ctypes.byref(merge), budget, protect_from, _ptr(evict), _ptr(pairs), _ptr(n_merged),
-        _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+        _ptr(ws), nbytes, _stream(stream), handles, len(events)))
 
 
 def kvc_compact(cache: Cache, evict, merge: _Merge | None, ws: torch.Tensor, stream=None):

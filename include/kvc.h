@@ -232,6 +232,17 @@ int32_t kvc_keepkv_prefill_merge(const kvc_cache *cache, const kvc_merge *merge,
                                  int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/* kvc_keepkv_prefill_merge_marked -- kvc_keepkv_prefill_merge, plus stage timing
+ * for measurement: events (hipEvent_t handles created by the caller, n_events = 4)
+ * are recorded on `stream` before the first kernel and after each of the three
+ * (key norms and flags, initial partner lists, the merge loop). events NULL
+ * behaves as kvc_keepkv_prefill_merge; n_events other than 4 with events
+ * non-NULL is KVC_ERR_ARG. */
+int32_t kvc_keepkv_prefill_merge_marked(const kvc_cache *cache, const kvc_merge *merge, int32_t budget,
+                                        int32_t protect_from, uint8_t *evict, int32_t *pairs, int32_t *n_merged,
+                                        void *ws, size_t ws_bytes, void *stream, void *const *events,
+                                        int32_t n_events);
+
 /* kvc_compact -- remove the flagged entries of every scope (MomentKV Algorithm 1
  * step 14; InertiaKV §3: eviction is irreversible). Survivors end in slots
  * [0, len - n_evicted): the j-th evicted slot below the new length receives the
