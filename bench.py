@@ -371,6 +371,62 @@ def run_moment_evict(args):
     print(json.dumps(result), flush=True)
 
 
+def run_ema_init(args):
+    """KeepKV's window initialisation of the EMA utility at the end of a 4k prompt for every KV
+    head (kvc_keepkv_ema_init): 32 window queries (the page's w = 31) per KV head, G = 4 query
+    heads, alpha 0.9. Events are recorded between the four kernels of each call."""
+    from oracle.keepkv_ema_init import ema_window_init
+    import oracle
+    wl = synth.WORKLOADS["k1_keepkv_prefill_llama8b_4k"]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S, d, G, N, n_win, alpha = wl.n_scopes, wl.d, wl.G, wl.context, 32, 0.9
+    t = synth.cache_tensors(wl, dev)
+    cache = kvc.Cache(k=t["k"], v=t["v"], pos=t["pos"], m=t["m"], length=t["length"])
+    q = synth.window_queries(S, G, n_win, d, wl.seed, dev).contiguous()
+    scale = float(np.float32(1 / np.sqrt(d)))
+    ws = kvc.workspace(kvc.kvc_keepkv_ema_init_workspace_size(cache, G, n_win, N), dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in marks:
+        e.record()   # torch creates the event at its first record
+    for _ in range(args.warmup):
+        kvc.kvc_keepkv_ema_init(cache, q, G, n_win, N, scale, alpha, ws)
+    torch.cuda.synchronize()
+    stages = []
+    for _ in range(args.steps):
+        kvc.kvc_keepkv_ema_init(cache, q, G, n_win, N, scale, alpha, ws, events=marks)
+        torch.cuda.synchronize()
+        stages.append([marks[i].elapsed_time(marks[i + 1]) for i in range(4)])
+    st = np.median(np.array(stages), axis=0)
+    ms = float(st.sum())
+    # each window pass: 2 G n_win N d flops per head on the fp64 MFMA
+    pass_flops = S * 2.0 * G * n_win * N * d
+    ach = pass_flops / (st[2] / 1e3) / 1e12
+    result = {"metric": "KeepKV EMA window initialisation: prompt tokens scored/sec",
+              "value": S * N / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16 cache; f64 logits and softmax statistics", "data": "synthetic",
+              "config": {"workload": wl.name, "heads": S, "prompt": N, "window": n_win, "G": G, "alpha": alpha},
+              "roofline": {"bound": "mfma", "achieved": ach, "peak": rf.MI355X_FP64_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / rf.MI355X_FP64_TFLOPS, "traffic": None, "kernel": "k_lap_window<4, 2>",
+                           "launch_ms": float(st[2]), "flops_per_launch": pass_flops},
+              "stages_ms": {"window_pass1": float(st[0]), "row_combine": float(st[1]),
+                            "window_pass2": float(st[2]), "block_sum": float(st[3])}}
+    if not args.no_cpu_baseline:
+        Kh = oracle.to_f64(t["k"][0, 0, :N].view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        qh = oracle.to_f64(q[0].view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            ema_window_init(qh, Kh, scale, alpha)
+            reps += 1
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": reps * N / dt, "unit": "tokens/s", "cores": torch.get_num_threads(),
+                                  "kind": "oracle",
+                                  "sample": f"{reps} window initialisations of one KV head ({N} tokens, {n_win} "
+                                            f"window queries) in {dt:.1f} s, numpy float64 oracle"}
+    print(json.dumps(result), flush=True)
+
+
 def run_prefill_merge(args):
     """KeepKV prefill compression of every KV head: greedy all-pairs ZIP merging from the prompt
     length down to the budget, the last 32 positions protected (kvc_keepkv_prefill_merge). The
@@ -535,7 +591,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict", "prefill_merge"],
+    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict", "prefill_merge",
+                                                     "ema_init"],
                     help="step: the fused decode step (default); first_step: the bulk compression step "
                          "after prefill; moment_correct: MomentKV's corrected output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -549,6 +606,8 @@ def main():
 
     if args.op == "moment_evict":
         return run_moment_evict(args)
+    if args.op == "ema_init":
+        return run_ema_init(args)
     if args.op == "prefill_merge":
         return run_prefill_merge(args)
     if args.op == "moment_correct":

@@ -658,6 +658,38 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
   return KVC_OK;
 }
 
+size_t kvc_keepkv_ema_init_workspace_size(const kvc_cache *cache, int32_t G, int32_t n_win, int32_t n_tokens) {
+  if (validate_cache(cache) || !valid_G(G) || n_win <= 0 || n_tokens < n_win || n_tokens > cache->capacity)
+    return 0;
+  return kvc::ema_window_workspace_bytes(cache->n_scopes, G, n_tokens, n_win);
+}
+
+int32_t kvc_keepkv_ema_init(const kvc_cache *cache, const void *q_win, int32_t G, int32_t n_win, int32_t n_tokens,
+                            float scale, float alpha, void *ws, size_t ws_bytes, void *stream) {
+  return kvc_keepkv_ema_init_marked(cache, q_win, G, n_win, n_tokens, scale, alpha, ws, ws_bytes, stream, nullptr,
+                                    0);
+}
+
+int32_t kvc_keepkv_ema_init_marked(const kvc_cache *cache, const void *q_win, int32_t G, int32_t n_win,
+                                   int32_t n_tokens, float scale, float alpha, void *ws, size_t ws_bytes,
+                                   void *stream, void *const *events, int32_t n_events) {
+  if (events && n_events != kvc::kEmaStages + 1) return KVC_ERR_ARG;
+  int st = validate_cache(cache);
+  if (st) return st;
+  if (cache->units_per_scope != 1 || !valid_G(G)) return KVC_ERR_UNSUPPORTED;
+  if (cache->dtype != KVC_BF16) return KVC_ERR_DTYPE;
+  if (!q_win || !cache->m || !(alpha > 0.f && alpha < 1.f)) return KVC_ERR_ARG;
+  if (n_win <= 0 || n_tokens < n_win || n_tokens > cache->capacity) return KVC_ERR_CAPACITY;
+  if (!aligned16(q_win)) return KVC_ERR_ALIGN;
+  if (!ws || ws_bytes < kvc::ema_window_workspace_bytes(cache->n_scopes, G, n_tokens, n_win)) return KVC_ERR_WORKSPACE;
+  hipEvent_t *marks = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
+  if (kvc::launch_ema_window(q_win, cache->k, cache->scope_stride, cache->n_scopes, G, n_win, n_tokens, double(scale),
+                             double(alpha), cache->m, cache->capacity, ws, static_cast<hipStream_t>(stream),
+                             marks) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
 size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w, int32_t d,
                                  int32_t D) {
   return kvc::laprox_workspace_bytes(n_layers, H, n_kv, N, w, d, D);

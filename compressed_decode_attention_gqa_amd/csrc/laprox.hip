@@ -58,6 +58,13 @@ struct LapArgs {
   float *c2;                  // [units][nh][N]
   float *r2;                  // [units][N]
   double *psum;               // [units][nchunks]
+  int64_t kstride;            // rows from one unit's keys to the next (N for LaProx)
+  // KeepKV window initialisation of the EMA utility: pass 2 sums gamma_j * (group-mean
+  // weight) over the window rows instead of its square, gamma_j = (1 - alpha) alpha^(w-1-j)
+  int ema;
+  double alpha;
+  float *m_out;               // [units] x m_stride utilities (tokens [0, N))
+  int64_t m_stride;
 };
 
 // ---------------------------------------------------------------- Gram matrix
@@ -212,6 +219,12 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
     }
   }
   const int jl = lane & 15, tq = lane >> 4;
+  float gam[CPG];          // EMA weight of each of the lane's window rows (0 past the window)
+#pragma unroll
+  for (int c8 = 0; c8 < CPG; ++c8) {
+    const int jj = hb * (128 / G) + c8 * 16 + jl;
+    gam[c8] = (a.ema && jj < w) ? float((1.0 - a.alpha) * pow(a.alpha, double(w - 1 - jj))) : 0.f;
+  }
   int plim[FM_RT];         // last key each of the lane's rows attends to (-1: not a row)
   double Mrow[FM_RT], Zrow[FM_RT];
   float iz[FM_RT];
@@ -232,7 +245,7 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
   }
   __syncthreads();
 
-  const char *Kb = a.k + int64_t(u) * N * RB;
+  const char *Kb = a.k + int64_t(u) * a.kstride * RB;
   const int n16 = (t1 - t0 + FM_TILE - 1) / FM_TILE;
   for (int t = wave; t < n16; t += WM_NT / 64) {
     const int tb = t0 + t * FM_TILE;
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
             sum += exp_split(acc[ct][r] - Mrow[ct]) * iz[ct];
           }
           const float mean = sum * (1.f / float(G));
-          sq += mean * mean;
+          sq += a.ema ? gam[c8] * mean : mean * mean;
         }
         // the 16 lanes of a row of lanes hold 16 window rows each
         const float c2 = block_sum<0, 4>(sq);
@@ -331,6 +344,15 @@ __global__ __launch_bounds__(WM_NT, 1) void k_lap_window(const LapArgs a) {
       }
     }
   }
+}
+
+// grid (ceil(N / 256), units): the EMA utility of each token, summed over the window-row blocks.
+__global__ __launch_bounds__(256) void k_ema_fin(const LapArgs a) {
+  const int tok = blockIdx.x * 256 + threadIdx.x, u = blockIdx.y;
+  if (tok >= a.N) return;
+  float m = 0.f;
+  for (int hb = 0; hb < a.nh; ++hb) m += a.c2[(int64_t(u) * a.nh + hb) * a.N + tok];
+  a.m_out[int64_t(u) * a.m_stride + tok] = m;
 }
 
 // grid (ceil(units R / 256)), 256 threads: each thread combines one row's tiles in order.
@@ -525,6 +547,7 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   a.c2 = reinterpret_cast<float *>(base + L.c2);
   a.r2 = reinterpret_cast<float *>(base + L.r2);
   a.psum = reinterpret_cast<double *>(base + L.psum);
+  a.kstride = N;
   const int units = n_layers * n_kv;
 
   // marks (optional): an event before the first kernel and after each of the seven
@@ -546,6 +569,67 @@ hipError_t launch_laprox(const void *q_win, const void *k, const void *v, const 
   hipLaunchKernelGGL(k_lap_norm, dim3(a.nchunks, units), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(7);
+}
+
+struct EmaLayout {
+  size_t tM, tZ, rM, rZ, c2, total;
+};
+
+EmaLayout ema_layout(int units, int G, int N, int w) {
+  const int R = G * w, nh = (w + WM_ROWS / G - 1) / (WM_ROWS / G), ntiles = (N + WM_TILE - 1) / WM_TILE;
+  EmaLayout L{};
+  size_t o = 0;
+  L.tM = o;  o = align256(o + size_t(units) * R * ntiles * 8);
+  L.tZ = o;  o = align256(o + size_t(units) * R * ntiles * 8);
+  L.rM = o;  o = align256(o + size_t(units) * R * 8);
+  L.rZ = o;  o = align256(o + size_t(units) * R * 8);
+  L.c2 = o;  o = align256(o + size_t(units) * nh * N * 4);
+  L.total = o;
+  return L;
+}
+
+size_t ema_window_workspace_bytes(int units, int G, int N, int w) { return ema_layout(units, G, N, w).total; }
+
+hipError_t launch_ema_window(const void *q_win, const void *k, int64_t kstride, int units, int G, int w, int N,
+                             double scale, double alpha, float *m, int64_t m_stride, void *ws, hipStream_t st,
+                             hipEvent_t *marks) {
+  const EmaLayout L = ema_layout(units, G, N, w);
+  char *base = static_cast<char *>(ws);
+  LapArgs a{};
+  a.q = static_cast<const char *>(q_win);
+  a.k = static_cast<const char *>(k);
+  a.n_layers = units;
+  a.H = G;
+  a.n_kv = 1;
+  a.N = N;
+  a.w = w;
+  a.G = G;
+  a.R = G * w;
+  a.nh = (w + WM_ROWS / G - 1) / (WM_ROWS / G);
+  a.ntiles = (N + WM_TILE - 1) / WM_TILE;
+  a.scale = scale;
+  a.tM = reinterpret_cast<double *>(base + L.tM);
+  a.tZ = reinterpret_cast<double *>(base + L.tZ);
+  a.rM = reinterpret_cast<double *>(base + L.rM);
+  a.rZ = reinterpret_cast<double *>(base + L.rZ);
+  a.c2 = reinterpret_cast<float *>(base + L.c2);
+  a.kstride = kstride;
+  a.ema = 1;
+  a.alpha = alpha;
+  a.m_out = m;
+  a.m_stride = m_stride;
+  auto mark = [&](int i) { return marks ? hipEventRecord(marks[i], st) : hipSuccess; };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return e;
+  const dim3 wgrid(a.ntiles, a.nh, units);
+  if ((e = window_pass(a, wgrid, st, 1)) != hipSuccess || (e = mark(1)) != hipSuccess) return e;
+  const int n_rows = units * a.R;
+  hipLaunchKernelGGL(k_lap_rowfin, dim3((n_rows + 255) / 256), dim3(256), 0, st, a, n_rows);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess) return e;
+  if ((e = window_pass(a, wgrid, st, 2)) != hipSuccess || (e = mark(3)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_ema_fin, dim3((N + 255) / 256, units), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return mark(4);
 }
 
 }  // namespace kvc

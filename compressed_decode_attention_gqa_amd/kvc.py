@@ -22,11 +22,11 @@ DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
 EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
-            "kvc_keepkv_prefill_merge_marked",
+            "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
             "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
             "kvc_decode_workspace_size",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
-            "kvc_keepkv_prefill_workspace_size",
+            "kvc_keepkv_prefill_workspace_size", "kvc_keepkv_ema_init_workspace_size",
             "kvc_laprox_workspace_size",
             "kvc_workspace_status", "kvc_status_string", "kvc_version")
 
@@ -68,6 +68,8 @@ _SIGS = {
     "kvc_moment_evict": (_I, [_P, _P, _P, _F, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]),
     "kvc_keepkv_prefill_merge": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "kvc_keepkv_prefill_merge_marked": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _I]),
+    "kvc_keepkv_ema_init": (_I, [_P, _P, _I, _I, _I, _F, _F, _P, _SZ, _P]),
+    "kvc_keepkv_ema_init_marked": (_I, [_P, _P, _I, _I, _I, _F, _F, _P, _SZ, _P, _P, _I]),
     "kvc_laprox_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
@@ -75,6 +77,7 @@ _SIGS = {
     "kvc_compact_workspace_size": (_SZ, [_P]),
     "kvc_moment_evict_workspace_size": (_SZ, [_P]),
     "kvc_keepkv_prefill_workspace_size": (_SZ, [_P]),
+    "kvc_keepkv_ema_init_workspace_size": (_SZ, [_P, _I, _I, _I]),
     "kvc_laprox_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "kvc_workspace_status": (_I, [_P, _P]),
     "kvc_status_string": (ctypes.c_char_p, [_I]),
@@ -200,6 +203,11 @@ def kvc_keepkv_prefill_workspace_size(cache: Cache) -> int:
     return lib().kvc_keepkv_prefill_workspace_size(ctypes.byref(d))
 
 
+def kvc_keepkv_ema_init_workspace_size(cache: Cache, G: int, n_win: int, n_tokens: int) -> int:
+    d = cache.desc()
+    return lib().kvc_keepkv_ema_init_workspace_size(ctypes.byref(d), G, n_win, n_tokens)
+
+
 def kvc_laprox_workspace_size(n_layers, H, n_kv, N, w, d, D) -> int:
     return lib().kvc_laprox_workspace_size(n_layers, H, n_kv, N, w, d, D)
 
@@ -286,6 +294,26 @@ def kvc_keepkv_prefill_merge(cache: Cache, merge: _Merge, budget: int, protect_f
     _check("kvc_keepkv_prefill_merge_marked", lib().kvc_keepkv_prefill_merge_marked(
         ctypes.byref(d), ctypes.byref(merge), budget, protect_from, _ptr(evict), _ptr(pairs), _ptr(n_merged),
         _ptr(ws), nbytes, _stream(stream), handles, len(events)))
+
+
+def kvc_keepkv_ema_init(cache: Cache, q_win, G: int, n_win: int, n_tokens: int, scale: float, alpha: float,
+                        ws: torch.Tensor, stream=None, events=None):
+    """events: None, or 5 recorded-once torch.cuda.Event(enable_timing=True) objects."""
+    d = cache.desc()
+    if events is None:
+        _check("kvc_keepkv_ema_init", lib().kvc_keepkv_ema_init(
+            ctypes.byref(d), _ptr(q_win), G, n_win, n_tokens, scale, alpha, _ptr(ws), ws.numel(), _stream(stream)))
+        return
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("kvc_keepkv_ema_init_marked", lib().kvc_keepkv_ema_init_marked(
+        ctypes.byref(d), _ptr(q_win), G, n_win, n_tokens, scale, alpha, _ptr(ws), ws.numel(), _stream(stream),
+        handles, len(events)))
+
+
+def ema_bias_correction(alpha: float, t: int) -> float:
+    """KeepKV eq. (14): the factor 1 / (1 - alpha^t) that turns the EMA state S^t into the
+    predicted score (host arithmetic; it scales every utility of a step alike)."""
+    return 1.0 / (1.0 - alpha ** t)
 
 
 def kvc_compact(cache: Cache, evict, merge: _Merge | None, ws: torch.Tensor, stream=None):

@@ -15,7 +15,8 @@
  *   KeepKV    -- reading notes on "KeepKV: Achieving Periodic Lossless KV Cache
  *                Compression": attention eq. (1), votes eqs. (6)-(7), ZIP merge
  *                eqs. (8)-(12), numerical-stability guard, framework integration,
- *                the inference algorithm's prefill compression.
+ *                EMA score prediction eqs. (14)-(15), the inference algorithm's
+ *                prefill compression.
  *   LaProx    -- notes on "Reformulating KV Cache Eviction Problem for
  *                Long-Context LLM Inference": key designs 1-3, GQA paragraph.
  *
@@ -243,6 +244,36 @@ int32_t kvc_keepkv_prefill_merge_marked(const kvc_cache *cache, const kvc_merge 
                                         void *ws, size_t ws_bytes, void *stream, void *const *events,
                                         int32_t n_events);
 
+/* kvc_keepkv_ema_init -- KeepKV's window initialisation of the EMA utility at the
+ * end of prefill (reading notes on KeepKV: EMA score prediction, eq. (15) at t = L,
+ * and the inference algorithm's prefill step 4), per-KV-head scopes of a bf16 cache
+ * (units_per_scope = 1, else KVC_ERR_UNSUPPORTED; fp32 caches KVC_ERR_DTYPE).
+ * Slots [0, n_tokens) of every scope hold the prompt in position order; q_win
+ * ([n_scopes][G][n_win][128] bf16, 16-byte aligned) holds the queries of the last
+ * n_win prompt tokens, window row j at position n_tokens - n_win + j. For each
+ * row, s_j(i) is the mean over the G query heads of the softmax weight of key i
+ * under scale * q . k, causal (keys i <= the row's position; 0 beyond). Writes
+ * m[s][i] = sum_j (1 - alpha) alpha^(n_win - 1 - j) s_j(i) for i < n_tokens (the
+ * page's w is n_win - 1); other slots are untouched. This equals the EMA recursion
+ * m <- alpha m + (1 - alpha) s run from zero over the window rows. The bias-
+ * corrected prediction m / (1 - alpha^t) is one positive factor per step and
+ * changes no ranking, so it is left to the caller. Logits and softmax statistics
+ * are float64 (fp64 MFMA), weights and m fp32. 0 < alpha < 1, else KVC_ERR_ARG;
+ * 0 < n_win <= n_tokens <= capacity, else KVC_ERR_CAPACITY. Workspace:
+ * kvc_keepkv_ema_init_workspace_size. */
+int32_t kvc_keepkv_ema_init(const kvc_cache *cache, const void *q_win, int32_t G, int32_t n_win, int32_t n_tokens,
+                            float scale, float alpha, void *ws, size_t ws_bytes, void *stream);
+
+/* kvc_keepkv_ema_init_marked -- kvc_keepkv_ema_init, plus stage timing for
+ * measurement: events (hipEvent_t handles created by the caller, n_events = 5)
+ * are recorded on `stream` before the first kernel and after each of the four
+ * (window pass 1, row combine, window pass 2, sum over window-row blocks). events
+ * NULL behaves as kvc_keepkv_ema_init; n_events other than 5 with events non-NULL
+ * is KVC_ERR_ARG. */
+int32_t kvc_keepkv_ema_init_marked(const kvc_cache *cache, const void *q_win, int32_t G, int32_t n_win,
+                                   int32_t n_tokens, float scale, float alpha, void *ws, size_t ws_bytes,
+                                   void *stream, void *const *events, int32_t n_events);
+
 /* kvc_compact -- remove the flagged entries of every scope (MomentKV Algorithm 1
  * step 14; InertiaKV §3: eviction is irreversible). Survivors end in slots
  * [0, len - n_evicted): the j-th evicted slot below the new length receives the
@@ -334,6 +365,7 @@ size_t kvc_select_workspace_size(int32_t n_scopes, int32_t capacity);
 size_t kvc_compact_workspace_size(const kvc_cache *cache);
 size_t kvc_moment_evict_workspace_size(const kvc_cache *cache);
 size_t kvc_keepkv_prefill_workspace_size(const kvc_cache *cache);
+size_t kvc_keepkv_ema_init_workspace_size(const kvc_cache *cache, int32_t G, int32_t n_win, int32_t n_tokens);
 size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,
                                  int32_t d, int32_t D);
 

@@ -15,7 +15,8 @@ the section or equation on it, that gives that definition:
   * InertiaKV (translated article, arXiv 2609.03515) -- head-averaged
     last-query score and single / cumulative / EMA utility.
   * KeepKV (reading notes, arXiv 2504.09936) -- vote-weighted attention,
-    ZIP-merging, and prefill compression by greedy all-pairs merging.
+    ZIP-merging, prefill compression by greedy all-pairs merging, and the
+    window initialisation and bias correction of the EMA score state.
   * LaProx notes ("Reformulating KV Cache Eviction Problem for Long-Context
     LLM Inference", arXiv 2605.07234) -- prefill score, per-layer
     normalisation, model-wide top-K.
@@ -47,6 +48,7 @@ from .moment_evict import moment_residuals, moment_scores, moment_informed_evict
 from .compaction import compact  # noqa: F401
 from .zip_merge import cosine_partner, zip_merge  # noqa: F401
 from .keepkv_prefill import prefill_merge, reference_logits  # noqa: F401
+from .keepkv_ema_init import window_scores, ema_window_init, predicted_scores  # noqa: F401
 from .decode_step import ScopeState, StepParams, decode_step  # noqa: F401
 from .laprox import (window_column_norms, value_output_norms, laprox_scores,  # noqa: F401
                      laprox_keep)

@@ -143,6 +143,28 @@ def test_keepkv_prefill_host_checks():
 
 
 @needs_lib
+def test_keepkv_ema_init_host_checks():
+    L = kvc.lib()
+    c = _fake_cache()
+    need = L.kvc_keepkv_ema_init_workspace_size(ctypes.byref(c), 4, 33, 90)
+    assert need > 0
+
+    def call(cache=c, q=0x8000, G=4, n_win=33, n_tok=90, alpha=0.9, wsb=need, ev=None, n_ev=0):
+        return L.kvc_keepkv_ema_init_marked(ctypes.byref(cache), q, G, n_win, n_tok, 0.1, alpha, 0x900, wsb,
+                                            None, ev, n_ev)
+    assert call(cache=_fake_cache(units_per_scope=2, unit_stride=100, scope_stride=200)) == -3
+    assert call(G=3) == -3
+    assert call(cache=_fake_cache(dtype=1)) == -2              # fp32 caches
+    assert call(q=None) == -1
+    assert call(cache=_fake_cache(m=None)) == -1
+    assert call(alpha=1.0) == -1 and call(alpha=0.0) == -1
+    assert call(n_win=0) == -4 and call(n_tok=101) == -4 and call(n_win=91) == -4
+    assert call(q=0x8008) == -5
+    assert call(wsb=need - 1) == -6
+    assert call(ev=(ctypes.c_void_p * 2)(), n_ev=2) == -1     # five events or none
+
+
+@needs_lib
 @pytest.mark.parametrize("H,n_kv,N,w,D,code", [
     (32, 8, 100, 1, 4096, -3),     # G w = 4: not a whole number of 8-row waves
     (32, 8, 100, 4, 4000, -3),     # D not a multiple of 64
