@@ -366,6 +366,11 @@ PrefillLayout prefill_layout(int n_scopes, int cap) {
   return l;
 }
 
+// kvc_select_evict with an optional protection bound (defined below the C entry points).
+int32_t select_evict(const float *key, const int32_t *pos, const int32_t *len, int32_t n_scopes, int32_t capacity,
+                     int32_t budget, bool protect, int32_t protect_from, uint8_t *evict, int32_t *n_evict, void *ws,
+                     size_t ws_bytes, void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -445,6 +450,33 @@ int32_t kvc_ema_update(float *m, const float *s, const int32_t *len, int32_t n_s
 int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *len, int32_t n_scopes,
                          int32_t capacity, int32_t budget, uint8_t *evict, int32_t *n_evict, void *ws,
                          size_t ws_bytes, void *stream) {
+  return select_evict(key, pos, len, n_scopes, capacity, budget, false, 0, evict, n_evict, ws, ws_bytes, stream);
+}
+
+int32_t kvc_keep_jaccard(const uint8_t *keep_a, const uint8_t *keep_b, const int32_t *len, int32_t n_scopes,
+                         int32_t capacity, float *out, void *stream) {
+  if (!keep_a || !keep_b || !out || n_scopes <= 0 || capacity <= 0) return KVC_ERR_ARG;
+  if (kvc::launch_jaccard(keep_a, keep_b, len, n_scopes, capacity, out, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
+int32_t kvc_select_evict_protected(const float *key, const int32_t *pos, const int32_t *len, int32_t n_scopes,
+                                   int32_t capacity, int32_t budget, int32_t protect_from, uint8_t *evict,
+                                   int32_t *n_evict, void *ws, size_t ws_bytes, void *stream) {
+  if (n_scopes == 1 && len == nullptr && capacity > (1 << 20)) return KVC_ERR_UNSUPPORTED;
+  return select_evict(key, pos, len, n_scopes, capacity, budget, true, protect_from, evict, n_evict, ws, ws_bytes,
+                      stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int32_t select_evict(const float *key, const int32_t *pos, const int32_t *len, int32_t n_scopes, int32_t capacity,
+                     int32_t budget, bool protect, int32_t protect_from, uint8_t *evict, int32_t *n_evict, void *ws,
+                     size_t ws_bytes, void *stream) {
   if (!key || !evict || n_scopes <= 0 || capacity <= 0) return KVC_ERR_ARG;
   if (budget < 0) return KVC_ERR_CAPACITY;
   if (!ws || ws_bytes < kvc_select_workspace_size(n_scopes, capacity)) return KVC_ERR_WORKSPACE;
@@ -469,9 +501,15 @@ int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *le
   b.n_scopes = n_scopes;
   b.n_chunks = l.n_chunks;
   b.chunk = l.chunk;
+  b.protect = protect ? 1 : 0;
+  b.protect_from = protect_from;
   if (kvc::launch_bulk_select(b, hs) != hipSuccess) return KVC_ERR_DEVICE;
   return KVC_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int32_t kvc_moment_update(const kvc_cache *cache, const uint8_t *evict, const kvc_moments *mom,
                           void *stream) {

@@ -31,7 +31,11 @@ constexpr int FOLD_NB = 16;                     // evicted rows staged per batch
 constexpr int PART_STRIDE = HD * HD + 2 * HD;   // floats per fold partial: S, s_k, s_v
 
 __device__ __forceinline__ uint64_t slot_key(const BulkArgs &b, int64_t sc, int i) {
-  return order_key(b.key[sc + i], b.pos ? uint32_t(b.pos[sc + i]) : uint32_t(i));
+  const uint32_t p = b.pos ? uint32_t(b.pos[sc + i]) : uint32_t(i);
+  if (!b.protect) return order_key(b.key[sc + i], p);
+  // (protected, value, position) in 1 + 32 + 31 bits: positions are non-negative int32
+  const uint64_t prot = int32_t(p) >= b.protect_from ? 1ull : 0ull;
+  return (prot << 63) | (uint64_t(orderable_f32(b.key[sc + i])) << 31) | uint64_t(p & 0x7fffffffu);
 }
 
 // ------------------------------------------------------------ standalone set-up

@@ -35,6 +35,8 @@ struct BulkArgs {
   int32_t n_chunks, chunk; // slot chunks of the histogram, flag, count and list kernels
   int32_t fold_splits;     // workgroups folding one unit's evicted rows
   int32_t move_blocks;     // workgroups moving one scope's rows
+  int32_t protect;         // 1: entries at positions >= protect_from rank after every other entry
+  int32_t protect_from;
 };
 
 struct StepArgs {

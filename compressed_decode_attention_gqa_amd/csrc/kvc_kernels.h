@@ -91,5 +91,7 @@ hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_
 hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);
+hipError_t launch_jaccard(const uint8_t *a, const uint8_t *b, const int32_t *len, int n_scopes, int cap, float *out,
+                          hipStream_t st);
 
 }  // namespace kvc

@@ -369,3 +369,47 @@ hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n
   return hipGetLastError();
 }
 }  // namespace kvc
+
+// ------------------------------------------------------------ rank-stability diagnostic
+// InertiaKV's rank-inertia measure (§3.1, Fig. 1): the Jaccard similarity |A and B| / |A or B|
+// of two kept sets over the same slots. One workgroup per scope; lane counts by wave ballots.
+namespace kvc {
+namespace {
+__global__ __launch_bounds__(WG) void k_jaccard(const uint8_t *a, const uint8_t *b, const int32_t *len, int cap,
+                                                float *out) {
+  __shared__ int inter[WG / 64], uni[WG / 64];
+  const int sc = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = len ? min(max(len[sc], 0), cap) : cap;
+  const uint8_t *pa = a + int64_t(sc) * cap, *pb = b + int64_t(sc) * cap;
+  int ni = 0, nu = 0;
+  for (int i0 = 0; i0 < L; i0 += WG) {
+    const int i = i0 + tid;
+    const bool ka = i < L && pa[i] != 0, kb = i < L && pb[i] != 0;
+    const uint64_t bi = __ballot(ka && kb), bu = __ballot(ka || kb);
+    if (lane == 0) {
+      ni += __popcll(bi);
+      nu += __popcll(bu);
+    }
+  }
+  if (lane == 0) {
+    inter[wave] = ni;
+    uni[wave] = nu;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int ti = 0, tu = 0;
+    for (int w = 0; w < WG / 64; ++w) {
+      ti += inter[w];
+      tu += uni[w];
+    }
+    out[sc] = tu > 0 ? float(double(ti) / double(tu)) : 1.0f;
+  }
+}
+}  // namespace
+
+hipError_t launch_jaccard(const uint8_t *a, const uint8_t *b, const int32_t *len, int n_scopes, int cap, float *out,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_jaccard, dim3(n_scopes), dim3(WG), 0, st, a, b, len, cap, out);
+  return hipGetLastError();
+}
+}  // namespace kvc

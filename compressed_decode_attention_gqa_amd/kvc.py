@@ -20,7 +20,8 @@ KVC_BF16, KVC_F32 = 0, 1
 RULES = {"single": 0, "cumulative": 1, "ema": 2}
 DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
-EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_compact",
+EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_select_evict_protected",
+            "kvc_keep_jaccard", "kvc_compact",
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
             "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
             "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
@@ -62,6 +63,8 @@ _SIGS = {
                              _I, _I, _I, _P, _SZ, _P]),
     "kvc_ema_update": (_I, [_P, _P, _P, _I, _I, _I, _F, _P]),
     "kvc_select_evict": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "kvc_select_evict_protected": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "kvc_keep_jaccard": (_I, [_P, _P, _P, _I, _I, _P, _P]),
     "kvc_moment_update": (_I, [_P, _P, _P, _P]),
     "kvc_compact": (_I, [_P, _P, _P, _P, _SZ, _P]),
     "kvc_moment_correct": (_I, [_P, _I, _P, _I, _I, _F, _P, _P, _P, _P]),
@@ -254,6 +257,18 @@ def kvc_select_evict(key, pos, length, n_scopes: int, capacity: int, budget: int
     _check("kvc_select_evict", lib().kvc_select_evict(
         _ptr(key), _ptr(pos), _ptr(length), n_scopes, capacity, budget, _ptr(evict), _ptr(n_evict),
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kvc_select_evict_protected(key, pos, length, n_scopes: int, capacity: int, budget: int, protect_from: int,
+                               evict, n_evict, ws: torch.Tensor, stream=None):
+    _check("kvc_select_evict_protected", lib().kvc_select_evict_protected(
+        _ptr(key), _ptr(pos), _ptr(length), n_scopes, capacity, budget, protect_from, _ptr(evict), _ptr(n_evict),
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kvc_keep_jaccard(keep_a, keep_b, length, n_scopes: int, capacity: int, out, stream=None):
+    _check("kvc_keep_jaccard", lib().kvc_keep_jaccard(_ptr(keep_a), _ptr(keep_b), _ptr(length), n_scopes,
+                                                      capacity, _ptr(out), _stream(stream)))
 
 
 def kvc_moment_update(cache: Cache, evict, moments: Moments, stream=None):

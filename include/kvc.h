@@ -151,6 +151,30 @@ int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *le
                          uint8_t *evict, int32_t *n_evict, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* kvc_select_evict_protected -- kvc_select_evict where every entry at a position
+ * >= protect_from ranks after every other entry: the order is (protected, key,
+ * pos) ascending, so protected entries are evicted only when too few others are
+ * left to reach the budget. This is InertiaKV's third lazy-refresh alternative
+ * (§3.1, the lazy rule): entries appended since the last score refresh carry no
+ * score yet and are protected instead of being evicted on their stale zero
+ * utility; protect_from is the position of the first such entry. Positions must
+ * be non-negative. pos NULL uses the slot index. One scope of more than 2^20 slots with len NULL (the device-
+ * wide path of kvc_select_evict) is KVC_ERR_UNSUPPORTED. Workspace:
+ * kvc_select_workspace_size. */
+int32_t kvc_select_evict_protected(const float *key, const int32_t *pos, const int32_t *len,
+                                   int32_t n_scopes, int32_t capacity, int32_t budget,
+                                   int32_t protect_from, uint8_t *evict, int32_t *n_evict,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/* kvc_keep_jaccard -- rank-stability diagnostic (InertiaKV §3.1, the rank-inertia
+ * measure of Fig. 1): per scope, the Jaccard similarity |A and B| / |A or B| of two
+ * kept sets over the same slots, A = {slots < len with keep_a != 0}, likewise B
+ * (1 when both are empty). keep_a, keep_b: [n_scopes][capacity] u8 (e.g. the
+ * complement of two kvc_select_evict results on one state under two scorers);
+ * len NULL means every slot; out: [n_scopes] fp32. */
+int32_t kvc_keep_jaccard(const uint8_t *keep_a, const uint8_t *keep_b, const int32_t *len, int32_t n_scopes,
+                         int32_t capacity, float *out, void *stream);
+
 /* kvc_moment_update -- MomentKV §4.1 / Appendix A.1 / Algorithm 1 steps 11-13:
  * for every slot < len flagged in evict (u8 [n_scopes][capacity]), fold its
  * rows into every unit's sums: n += 1, sk += k, sv += v, S += v k^T (fp32).

@@ -13,7 +13,8 @@ the section or equation on it, that gives that definition:
     moment-informed eviction (§4.2, Algorithm 1 phase 1) and the
     normalisation-corrected output (Algorithm 1, phase 2).
   * InertiaKV (translated article, arXiv 2609.03515) -- head-averaged
-    last-query score and single / cumulative / EMA utility.
+    last-query score, single / cumulative / EMA utility, the lazy-refresh
+    alternatives and the rank-stability (Jaccard) measure.
   * KeepKV (reading notes, arXiv 2504.09936) -- vote-weighted attention,
     ZIP-merging, prefill compression by greedy all-pairs merging, and the
     window initialisation and bias correction of the EMA score state.
@@ -41,11 +42,12 @@ the group-summed W_O under GQA in LaProx.
 from .convert import to_f64, round_to_bf16, round_to_f32  # noqa: F401
 from .attention import attend_unit, scope_score  # noqa: F401
 from .utility import SINGLE, CUMULATIVE, EMA, RULES, update_utility  # noqa: F401
-from .selection import bottom_k, bottom_k_one_at_a_time, top_k_keep  # noqa: F401
+from .selection import bottom_k, bottom_k_protected, bottom_k_one_at_a_time, top_k_keep  # noqa: F401
 from .moments import fold_moments, centred_moments, empty_moments  # noqa: F401
 from .moment_correct import corrected_output, evicted_estimates  # noqa: F401
 from .moment_evict import moment_residuals, moment_scores, moment_informed_evict  # noqa: F401
 from .compaction import compact  # noqa: F401
+from .rank_stability import keep_jaccard  # noqa: F401
 from .zip_merge import cosine_partner, zip_merge  # noqa: F401
 from .keepkv_prefill import prefill_merge, reference_logits  # noqa: F401
 from .keepkv_ema_init import window_scores, ema_window_init, predicted_scores  # noqa: F401

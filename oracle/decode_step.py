@@ -20,7 +20,9 @@ after every compressed layer). A per-KV-head scope is one group of one unit.
 Readings (the pages leave these open):
   * a new entry's utility starts at 0 before its first update;
   * steps that do not refresh scores (lazy refresh) skip 3-4 and still hold
-    the budget with the stale utility;
+    the budget with the stale utility; optionally (InertiaKV's third lazy
+    alternative) the entries appended since the last refresh are protected
+    from selection;
   * merge mode handles one eviction per group step and scopes of one unit.
 """
 from __future__ import annotations
@@ -33,7 +35,7 @@ from .attention import attend_unit, scope_score
 from .compaction import compact
 from .convert import to_f64, round_to_bf16, round_to_f32
 from .moments import fold_moments
-from .selection import bottom_k
+from .selection import bottom_k, bottom_k_protected
 from .utility import update_utility
 from .zip_merge import cosine_partner, zip_merge
 
@@ -69,6 +71,7 @@ class StepParams:
     merge: bool = False
     eps: float = 1e-6
     row_dtype: str = "f64"   # cache dtype of rows written by a merge: "bf16", "f32" or "f64"
+    protect_from: int | None = None   # entries at positions >= this rank after all others in selection
 
 
 @dataclass
@@ -136,7 +139,10 @@ def decode_step(state: ScopeState, new_k, new_v, new_pos, q, prm: StepParams):
             res.evicted_pos.append(np.zeros(0, dtype=np.int64))
             res.merges.append(None)
             continue
-        E = bottom_k(st.m, st.pos, k)
+        if prm.protect_from is None:
+            E = bottom_k(st.m, st.pos, k)
+        else:
+            E = bottom_k_protected(st.m, st.pos, k, prm.protect_from)
         res.evicted_pos.append(np.sort(st.pos[E]))
         if st.moments is not None:
             st.moments = fold_moments(st.moments, st.K[:, E], st.V[:, E])

@@ -27,6 +27,18 @@ def bottom_k(values, pos, k: int) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int64)
 
 
+def bottom_k_protected(values, pos, k: int, protect_from) -> np.ndarray:
+    """Slot indices (sorted) of the k smallest entries under (protected, value, pos)
+    ascending, protected meaning pos >= protect_from: InertiaKV §3.1's third lazy-refresh
+    alternative, where entries not yet scored are kept while others can go."""
+    values = np.asarray(values, dtype=np.float64)
+    pos = np.asarray(pos)
+    if k <= 0:
+        return np.zeros(0, dtype=np.int64)
+    order = np.lexsort((pos, values, pos >= protect_from))
+    return np.sort(order[:k]).astype(np.int64)
+
+
 def bottom_k_one_at_a_time(values, pos, k: int) -> np.ndarray:
     """MomentKV Algorithm 1 phase 1 with a score that does not depend on the
     evicted set: repeatedly remove the minimum (ties to the lower position)."""

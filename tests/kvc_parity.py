@@ -88,8 +88,10 @@ def oracle_state(snap, j, dtype):
                              m=snap["m"][j, :L].astype(np.float64))
 
 
-def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, merge=False, report=None):
-    """Compare one GPU step on `scopes` with the oracle run on the GPU pre-state."""
+def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, merge=False, report=None,
+               protect_from=None):
+    """Compare one GPU step on `scopes` with the oracle run on the GPU pre-state (protect_from:
+    the selection's protection bound, for InertiaKV's third lazy alternative)."""
     wl = run.wl
     dtype = wl.dtype
     out = bits(run.out[torch.as_tensor(scopes, device=run.out.device)])
@@ -98,7 +100,7 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
     ev_gpu = bits(run.evict[torch.as_tensor(scopes, device=run.out.device)])
     qh, knh, vnh = bits(q), bits(kn), bits(vn)
     prm = oracle.StepParams(scale=run.scale, rule=wl.rule, alpha=run.alpha, budget=wl.budget,
-                            score=refresh, merge=merge, row_dtype=dtype)
+                            score=refresh, merge=merge, row_dtype=dtype, protect_from=protect_from)
     stats = {"max_do": 0.0, "max_dlse": 0.0, "max_rel_s": 0.0, "max_rel_m": 0.0, "near_tie_flips": 0}
     for j, sc in enumerate(scopes):
         st = oracle_state(pre, j, dtype)

@@ -7,7 +7,7 @@ import itertools
 import numpy as np
 import pytest
 
-from oracle import bottom_k, bottom_k_one_at_a_time, top_k_keep, update_utility
+from oracle import bottom_k, bottom_k_one_at_a_time, bottom_k_protected, keep_jaccard, top_k_keep, update_utility
 
 RNG = np.random.default_rng(99)
 
@@ -105,3 +105,48 @@ def test_top_k_keep_brute_force():
                  if not c or len(c) == n or min(keys[i] for i in c) > max(keys[j] for j in range(n) if j not in c)]
         assert len(found) == 1
         assert set(np.flatnonzero(keep)) == found[0]
+
+
+@pytest.mark.parametrize("trial", range(20))
+def test_protected_selection_matches_exhaustive_enumeration(trial):
+    """InertiaKV's third lazy alternative: entries at positions >= protect_from rank after all
+    others. Exhaustive: the unique k-subset whose keys (protected, value, pos) all beat the rest."""
+    n = int(RNG.integers(1, 10))
+    values = RNG.choice([0.0, 0.5, 1.0], size=n)
+    pos = RNG.permutation(n) + 3
+    k = int(RNG.integers(0, n + 1))
+    bound = int(RNG.integers(3, n + 4))
+    keys = [(int(pos[i] >= bound), values[i], pos[i]) for i in range(n)]
+    found = []
+    for E in itertools.combinations(range(n), k):
+        R = [i for i in range(n) if i not in E]
+        if not E or not R or max(keys[i] for i in E) < min(keys[i] for i in R):
+            found.append(E)
+    assert len(found) == 1
+    assert np.array_equal(bottom_k_protected(values, pos, k, bound), np.array(sorted(found[0]), dtype=np.int64))
+
+
+def test_protected_selection_special_cases():
+    values = RNG.random(30)
+    pos = RNG.permutation(30)
+    # nothing protected, or everything protected: the plain selection
+    assert np.array_equal(bottom_k_protected(values, pos, 7, 10 ** 6), bottom_k(values, pos, 7))
+    assert np.array_equal(bottom_k_protected(values, pos, 7, -1), bottom_k(values, pos, 7))
+    # enough unprotected entries: the plain selection among them
+    un = np.flatnonzero(pos < 20)
+    got = bottom_k_protected(values, pos, 5, 20)
+    assert np.array_equal(got, np.sort(un[bottom_k(values[un], pos[un], 5)]))
+
+
+def test_keep_jaccard():
+    """Jaccard of two kept sets: 1 for identical or two empty sets, 0 for disjoint ones, and
+    the count ratio written with plain loops otherwise."""
+    assert keep_jaccard(np.zeros(5), np.zeros(5)) == 1.0
+    a = RNG.random(40) < 0.5
+    assert keep_jaccard(a, a) == 1.0
+    assert keep_jaccard(a, ~a) == 0.0
+    for _ in range(10):
+        a, b = RNG.random(60) < 0.4, RNG.random(60) < 0.6
+        both = sum(1 for i in range(60) if a[i] and b[i])
+        either = sum(1 for i in range(60) if a[i] or b[i])
+        assert keep_jaccard(a, b) == both / either
