@@ -131,3 +131,59 @@ def test_prefill_merge_longer_prompt():
 def test_prefill_merge_stops_when_the_budget_cannot_be_reached():
     # positions >= 20 are protected: 60 - 20 = 40 entries never merge, so a budget of 30 is out of reach
     _run_and_check([60, 25], 60, budget=30, protect_from=20, dtype="bf16", G=4, seed=9, expect_status=-4)
+
+
+def test_prefill_merge_full_size_sampled():
+    """The benchmarked configuration: 256 KV heads x 4096-token prompts -> 409 entries, the last
+    32 positions protected, G = 4. Every head: exactly 3687 merges, votes conserved (sum 4096),
+    protected rows untouched, removed slots flagged once. Two sampled heads: the first 24 merges
+    replayed in the oracle (each GPU pair the largest cosine, or within 1e-6 of it)."""
+    wl = synth.WORKLOADS["k1_keepkv_prefill_llama8b_4k"]
+    S, L0, B = wl.n_scopes, wl.context, wl.budget
+    protect_from = L0 - 32
+    t = synth.cache_tensors(wl, "cuda")
+    votes = torch.ones((S, t["k"].shape[2]), dtype=torch.int32, device="cuda")
+    cache = kvc.Cache(k=t["k"], v=t["v"], pos=t["pos"], m=t["m"], length=t["length"], votes=votes)
+    cap = cache.capacity
+    q = synth.step_query(0, S, wl.G, D, wl.dtype, wl.seed, "cuda").contiguous()
+    pre_k = bits(cache.k[:, 0])
+    pre_pos = cache.pos.cpu().numpy()
+    evict = torch.zeros((S, cap), dtype=torch.uint8, device="cuda")
+    pairs = torch.full((S, cap, 2), -1, dtype=torch.int32, device="cuda")
+    n_merged = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_keepkv_prefill_workspace_size(cache))
+    kvc.kvc_keepkv_prefill_merge(cache, kvc.merge_desc(q, wl.G, SCALE), B, protect_from, evict, pairs, n_merged,
+                                 ws=ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_workspace_status(ws) == 0
+    nm, ev, pr = n_merged.cpu().numpy(), evict.cpu().numpy(), pairs.cpu().numpy()
+    vt = cache.votes.cpu().numpy()
+    post_k = bits(cache.k[:, 0])
+    assert np.all(nm == L0 - B)
+    for sc in range(S):
+        gone = ev[sc, :L0].astype(bool)
+        assert gone.sum() == L0 - B
+        assert vt[sc, :L0][~gone].sum() == L0
+        prot = pre_pos[sc, :L0] >= protect_from
+        assert not np.any(gone & prot)
+        assert np.array_equal(post_k[sc, :L0][prot], pre_k[sc, :L0][prot])
+        g = pr[sc, :L0 - B, 1]
+        assert np.array_equal(np.sort(g), np.flatnonzero(gone))
+    n_rep = 24
+    for sc in (0, 201):
+        K = oracle.to_f64(pre_k[sc, :L0], "bf16")
+        pos = pre_pos[sc, :L0]
+
+        def follow(step, Kc, cand):
+            s_, g_ = int(pr[sc, step, 0]), int(pr[sc, step, 1])
+            assert cand[s_] and cand[g_]
+            bi, bj, bc = best_pair(Kc, pos, cand)
+            cg = cosine_matrix(Kc[[s_, g_]])[0, 1]
+            assert {s_, g_} == {bi, bj} or cg >= bc - BAND * abs(bc), (sc, step, cg, bc)
+            return s_, g_
+
+        qh = oracle.to_f64(bits(q[sc]), "bf16")
+        res = prefill_merge(K, np.zeros_like(K), np.ones(L0, dtype=np.int64), pos, np.zeros(L0), qh, SCALE,
+                            L0 - n_rep, protect_from, row_dtype="bf16", choose=follow)
+        assert len(res["pairs"]) == n_rep
+        print(f"full-size prefill merge: head {sc}, first {n_rep} merges follow the oracle", flush=True)
