@@ -44,7 +44,7 @@ namespace kvc {
 namespace {
 
 constexpr int PK = 4;            // partners kept per row
-constexpr int PM_NT = 256;       // k_pm_rows: 4 waves
+constexpr int PM_NT = 512;       // k_pm_rows: 8 waves, two per SIMD
 constexpr int PM_CT = 4;         // k_pm_rows: 16-row column tiles of the operator in use
 constexpr int PM_ROWS = 16 * PM_CT;
 constexpr int PL_NT = 512;       // k_pm_loop: 8 waves
@@ -81,6 +81,12 @@ __device__ __forceinline__ void pk_insert(double (&lc)[PK], int (&lp)[PK], int (
     lp[0] = pp;
     ls[0] = ss;
   }
+}
+
+// pk_insert only when the entry ranks above the list's last entry (or the list has room): in a
+// stream of candidates most are rejected by this one comparison.
+__device__ __forceinline__ void pk_offer(double (&lc)[PK], int (&lp)[PK], int (&ls)[PK], double c, int pp, int ss) {
+  if (ls[PK - 1] < 0 || pm_better(c, pp, lc[PK - 1], lp[PK - 1])) pk_insert(lc, lp, ls, c, pp, ss);
 }
 
 __device__ __forceinline__ void list_clear(double (&lc)[PK], int (&lp)[PK], int (&ls)[PK]) {
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
         if (rc[ct] && cj && j != row) {
           const double den = nrow[ct] * nj;
           const double c = den > 0.0 ? acc[ct][r] / den : 0.0;
-          pk_insert(lc[ct], lp[ct], ls[ct], c, pj, j);
+          pk_offer(lc[ct], lp[ct], ls[ct], c, pj, j);
         }
       }
     }
@@ -553,7 +559,7 @@ __device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLd
       for (int q = 0; q < PL_NQ; ++q) {
         const double den = qn[q] * nj;
         const double cs = den > 0.0 ? mine[q] / den : 0.0;
-        if (q < nq && jo != qr[q]) pk_insert(lc[q], lp[q], ls[q], cs, pj, jo);
+        if (q < nq && jo != qr[q]) pk_offer(lc[q], lp[q], ls[q], cs, pj, jo);
       }
     }
   }
@@ -772,7 +778,7 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
           const int pj = int(mt.z);
           const double den = nk * nj;
           const double cs = den > 0.0 ? mine / den : 0.0;
-          pk_insert(lc, lp, ls, cs, pj, jo);
+          pk_offer(lc, lp, ls, cs, pj, jo);
           double oc[PK] = {ent_c(r0), ent_c(r1), ent_c(r2), ent_c(r3)};
           int os[PK] = {int(r0.z), int(r1.z), int(r2.z), int(r3.z)};
           int opp[PK] = {int(r0.w), int(r1.w), int(r2.w), int(r3.w)};
