@@ -50,8 +50,7 @@ constexpr int PM_ROWS = 16 * PM_CT;
 constexpr int PL_NT = 512;       // k_pm_loop: 8 waves
 constexpr int PL_W = PL_NT / 64;
 constexpr int PL_NS = 8;         // row steps per batch of the merge pass (lane e < PL_NS of a group owns step e's row)
-constexpr int PL_NS_R = 4;       // the same in the recomputation pass (PL_NQ keys in registers)
-constexpr int PL_NQ = 2;         // stale rows recomputed per pass
+constexpr int PL_NQ = 16;        // stale rows recomputed per pass: one 16-row MFMA operator tile
 constexpr int PL_TODO = 256;     // stale rows collected per recomputation round
 constexpr int PL_SCAN = 8;       // rows per thread per load batch of the head scan
 constexpr int STALE = -2;        // slot value of a stale row's entries (entry 0 holds the bound)
@@ -329,9 +328,33 @@ __device__ __forceinline__ float round_to<bf16_t>(float x) { return bf16_to_f32(
 template <>
 __device__ __forceinline__ float round_to<float>(float x) { return x; }
 
+// The keys of up to 16 rows as the B operand of v_mfma_f64_16x16x4 (the transposed use of
+// kvc_f64mfma.h restricted to its first column tile): 16 KB.
+struct FmOp16 {
+  fm_d2 a[FM_S2][64];
+};
+__device__ __forceinline__ void op16_put(FmOp16 &op, int j, int b, double v) {   // row j < 16, element b
+  const int g = b >> 5, s = b & 31;
+  op.a[s >> 1][fm_swz(s >> 1, j + 16 * g)][s & 1] = v;
+}
+// acc[r] += X[l % 16] . y_{l / 16 + 4 r}: lane l holds elements [32 g, 32 g + 32) of token
+// l % 16's row (kr, g = l / 16) as A values and ends with row l % 16 of X against tokens
+// l / 16 + 4 r. The A values are converted to float64 step by step.
+template <typename T>
+__device__ __forceinline__ void op16_apply(const FmOp16 &op, int lane, const FmRow<T> &kr, fm_d4 &acc) {
+#pragma unroll
+  for (int s2 = 0; s2 < FM_S2; ++s2) {
+    const fm_d2 bf = op.a[s2][fm_swz(s2, lane)];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kr.get(2 * s2), bf.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(kr.get(2 * s2 + 1), bf.y, acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 struct LoopLds {
-  int live[PREFILL_MAX_ROWS];     // the scope's candidate slots (any order)
-  double qk[PL_NQ][HD];           // float64 keys of the pass's query rows
+  uint16_t live[PREFILL_MAX_ROWS];  // the scope's candidate slots (any order)
+  FmOp16 rop;                     // keys of the rows being recomputed
+  double qk[1][HD];               // float64 merged key of the merge pass
   double qn[PL_NQ];
   int qrow[PL_NQ], qpos[PL_NQ];
   double hc[PL_W], hu1[PL_W], hu2[PL_W];              // per-wave head and stale-bound reductions
@@ -502,89 +525,70 @@ __device__ __forceinline__ void scan_heads(const PrefillMergeArgs &p, LoopLds &s
   heads_from_lds(sh, h);
 }
 
-// Stale rows recomputed in full against every candidate: sh.qk / qn / qrow / qpos hold
-// nq (<= PL_NQ) of them. Lane e < NS of a 16-lane group owns the row of step e of each batch.
+// Stale rows recomputed in full against every candidate, on the float64 MFMA: the keys of
+// nq (<= 16) rows are the operator sh.rop (rows nq.. zero), 16 candidates per tile are the A
+// operand, so lane l holds row l % 16 against candidates l / 16 + 4 r and keeps that row's
+// best PK; the lanes' and waves' lists are merged into each row's record. sh.qn / qrow hold
+// the rows' norms and slots.
 template <typename T>
 __device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLds &sh, const char *Kc, int64_t so,
                                                int n_live, int nq, int tid) {
-  constexpr int ES = sizeof(T), NS = PL_NS_R;
-  const int lane = tid & 63, wave = tid >> 6, e = lane & 15, gi = lane >> 4;
-  double qv[PL_NQ][8], qn[PL_NQ];
-  int qr[PL_NQ];
+  constexpr int ES = sizeof(T);
+  const int lane = tid & 63, wave = tid >> 6, jl = lane & 15, tq = lane >> 4;
+  const bool mine = jl < nq;
+  const double qnj = mine ? sh.qn[jl] : 0.0;
+  const int qrj = mine ? sh.qrow[jl] : -1;
+  double lc[PK];
+  int lp[PK], ls[PK];
+  list_clear(lc, lp, ls);
+  const int n16 = (n_live + FM_TILE - 1) / FM_TILE;
+  for (int t = wave; t < n16; t += PL_W) {
+    const int tb = t * FM_TILE;
+    FmRow<T> kr;
+    kr.load(Kc + (int64_t(sh.live[min(tb + jl, n_live - 1)]) * HD + 32 * tq) * ES);
+    int jr[4];
+    u32x4 mr[4];
 #pragma unroll
-  for (int q = 0; q < PL_NQ; ++q) {
-    qn[q] = q < nq ? sh.qn[q] : 0.0;
-    qr[q] = q < nq ? sh.qrow[q] : -1;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) qv[q][v] = q < nq ? sh.qk[q][8 * e + v] : 0.0;
-  }
-  double lc[PL_NQ][PK];
-  int lp[PL_NQ][PK], ls[PL_NQ][PK];
-#pragma unroll
-  for (int q = 0; q < PL_NQ; ++q) list_clear(lc[q], lp[q], ls[q]);
-  for (int k0 = 0; k0 < n_live; k0 += PL_W * 4 * NS) {
-    Chunk8<T> kc[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int k = k0 + (wave * NS + u) * 4 + gi;
-      if (k < n_live) kc[u].load(Kc + int64_t(sh.live[k]) * HD * ES, e);
-      else kc[u].zero();
+    for (int r = 0; r < 4; ++r) {
+      const int k = tb + tq + 4 * r;
+      jr[r] = k < n_live ? int(sh.live[k]) : -1;
+      mr[r] = jr[r] >= 0 ? ld16(meta_at(p, so + jr[r])) : u32x4{0u, 0u, 0u, 0u};
     }
-    const int ko = k0 + (wave * NS + e) * 4 + gi;
-    const int jo = (e < NS && ko < n_live) ? sh.live[ko] : -1;
-    u32x4 mt = u32x4{0u, 0u, 0u, 0u};
-    if (jo >= 0) mt = ld16(meta_at(p, so + jo));
-    double mine[PL_NQ];
+    fm_d4 acc = fm_d4{0.0, 0.0, 0.0, 0.0};
+    op16_apply<T>(sh.rop, lane, kr, acc);
 #pragma unroll
-    for (int q = 0; q < PL_NQ; ++q) mine[q] = 0.0;
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      double x[8];
-#pragma unroll
-      for (int v = 0; v < 8; ++v) x[v] = kc[u].get(v);
-#pragma unroll
-      for (int q = 0; q < PL_NQ; ++q) {
-        double dot = 0.0;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) dot = fma(qv[q][v], x[v], dot);
-        dot = group_sum_f64<16>(dot);
-        mine[q] = e == u ? dot : mine[q];
-      }
-      __builtin_amdgcn_sched_barrier(0);   // one step's conversions live at a time
-    }
-    if (jo >= 0) {
-      const double nj = ent_c(mt);
-      const int pj = int(mt.z);
-#pragma unroll
-      for (int q = 0; q < PL_NQ; ++q) {
-        const double den = qn[q] * nj;
-        const double cs = den > 0.0 ? mine[q] / den : 0.0;
-        if (q < nq && jo != qr[q]) pk_offer(lc[q], lp[q], ls[q], cs, pj, jo);
-      }
+    for (int r = 0; r < 4; ++r) {
+      if (!mine || jr[r] < 0 || jr[r] == qrj) continue;
+      const double den = qnj * ent_c(mr[r]);
+      pk_offer(lc, lp, ls, den > 0.0 ? acc[r] / den : 0.0, int(mr[r].z), jr[r]);
     }
   }
+  // lanes of equal row (the four token groups), then the waves
+  list_merge_xor(lc, lp, ls, 16);
+  list_merge_xor(lc, lp, ls, 32);
+  if (tq == 0 && mine) {
 #pragma unroll
-  for (int q = 0; q < PL_NQ; ++q) {
-    double c[PK];
-    int pp[PK], ss[PK];
-    wave_topk(lc[q], lp[q], ls[q], lane, c, pp, ss);
-    if (lane == 0) {
-#pragma unroll
-      for (int k = 0; k < PK; ++k) {
-        sh.lc[q][wave][k] = c[k];
-        sh.lp[q][wave][k] = pp[k];
-        sh.ls[q][wave][k] = ss[k];
-      }
+    for (int k = 0; k < PK; ++k) {
+      sh.lc[jl][wave][k] = lc[k];
+      sh.lp[jl][wave][k] = lp[k];
+      sh.ls[jl][wave][k] = ls[k];
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    for (int q = 0; q < nq; ++q) {
-      double c[PK];
-      int pp[PK], ss[PK];
-      final_list(sh, q, lane, c, pp, ss);
-      if (lane == 0) rec_store(p, so + sh.qrow[q], c, pp, ss);
+  if (tid < nq) {
+    double c[PK];
+    int pp[PK], ss[PK];
+#pragma unroll
+    for (int k = 0; k < PK; ++k) {
+      c[k] = sh.lc[tid][0][k];
+      pp[k] = sh.lp[tid][0][k];
+      ss[k] = sh.ls[tid][0][k];
     }
+    for (int w = 1; w < PL_W; ++w)
+#pragma unroll
+      for (int k = 0; k < PK; ++k)
+        if (sh.ls[tid][w][k] >= 0) pk_insert(c, pp, ss, sh.lc[tid][w][k], sh.lp[tid][w][k], sh.ls[tid][w][k]);
+    rec_store(p, so + sh.qrow[tid], c, pp, ss);
   }
   __syncthreads();
 }
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
   for (int i = tid; i < L; i += PL_NT)
     if (pm_cand(p, so + i)) {
       const int k = atomicAdd(&sh.n_live, 1);
-      if (k < PREFILL_MAX_ROWS) sh.live[k] = i;
+      if (k < PREFILL_MAX_ROWS) sh.live[k] = uint16_t(i);
     }
   __syncthreads();
   int n_live = min(sh.n_live, PREFILL_MAX_ROWS);
@@ -641,10 +645,11 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       const int nt = min(sh.n_todo, PL_TODO);
       for (int b = 0; b < nt; b += PL_NQ) {
         const int nq = min(PL_NQ, nt - b);
-        if (tid < nq * HD) {
-          const int q = tid / HD, x = tid % HD, row = sh.todo[b + q];
-          sh.qk[q][x] = double(load_elem<T>(Kb, int64_t(row) * HD + x));
-          if (x == 0) {
+        for (int e = tid; e < PL_NQ * HD; e += PL_NT) {
+          const int q = e / HD, x = e % HD;
+          const int row = q < nq ? sh.todo[b + q] : -1;
+          op16_put(sh.rop, q, x, row >= 0 ? double(load_elem<T>(Kb, int64_t(row) * HD + x)) : 0.0);
+          if (x == 0 && row >= 0) {
             const u32x4 m = ld16(meta_at(p, so + row));
             sh.qn[q] = ent_c(m);
             sh.qrow[q] = row;
