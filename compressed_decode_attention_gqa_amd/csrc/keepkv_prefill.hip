@@ -362,6 +362,8 @@ struct LoopLds {
   double lc[PL_NQ][PL_W][PK];                         // per-wave best partners of the query rows
   int lp[PL_NQ][PL_W][PK], ls[PL_NQ][PL_W][PK];
   int todo[PL_TODO];
+  double th_c[PL_TODO];           // the recomputed rows' new heads (cosine, partner slot and position)
+  int th_s[PL_TODO], th_p[PL_TODO], th_pos[PL_TODO];
   int n_todo, n_live, gidx;
 };
 
@@ -532,7 +534,7 @@ __device__ __forceinline__ void scan_heads(const PrefillMergeArgs &p, LoopLds &s
 // the rows' norms and slots.
 template <typename T>
 __device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLds &sh, const char *Kc, int64_t so,
-                                               int n_live, int nq, int tid) {
+                                               int n_live, int nq, int b, int tid) {
   constexpr int ES = sizeof(T);
   const int lane = tid & 63, wave = tid >> 6, jl = lane & 15, tq = lane >> 4;
   const bool mine = jl < nq;
@@ -589,6 +591,10 @@ __device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLd
       for (int k = 0; k < PK; ++k)
         if (sh.ls[tid][w][k] >= 0) pk_insert(c, pp, ss, sh.lc[tid][w][k], sh.lp[tid][w][k], sh.ls[tid][w][k]);
     rec_store(p, so + sh.qrow[tid], c, pp, ss);
+    sh.th_c[b + tid] = c[0];
+    sh.th_s[b + tid] = ss[0];
+    sh.th_p[b + tid] = pp[0];
+    sh.th_pos[b + tid] = sh.qpos[tid];
   }
   __syncthreads();
 }
@@ -633,15 +639,33 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       }
       if (tid == 0) sh.n_todo = 0;
       __syncthreads();
-      for (int k = tid; k < n_live; k += PL_NT) {
-        const int j = sh.live[k];
-        const u32x4 w = ld16(rec_at(p, so + j));
-        if (int(w.z) == STALE && ent_c(w) >= h.c) {
-          const int t = atomicAdd(&sh.n_todo, 1);
-          if (t < PL_TODO) sh.todo[t] = j;
+      // stale rows whose bound reaches the best head are recomputed; the others' bounds are kept
+      Heads rest;
+      rest.clear();
+      for (int k0 = 0; k0 < n_live; k0 += PL_NT * PL_SCAN) {
+        int jr[PL_SCAN];
+        u32x4 er[PL_SCAN];
+#pragma unroll
+        for (int u = 0; u < PL_SCAN; ++u) {
+          const int k = k0 + u * PL_NT + tid;
+          jr[u] = k < n_live ? int(sh.live[k]) : -1;
+          er[u] = jr[u] >= 0 ? ld16(rec_at(p, so + jr[u])) : u32x4{0u, 0u, 0xffffffffu, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < PL_SCAN; ++u) {
+          if (jr[u] < 0 || int(er[u].z) != STALE) continue;
+          if (ent_c(er[u]) >= h.c) {
+            const int t = atomicAdd(&sh.n_todo, 1);
+            if (t < PL_TODO) sh.todo[t] = jr[u];
+          } else {
+            rest.bound(ent_c(er[u]));
+          }
         }
       }
+      heads_to_lds(sh, rest, lane, wave);
       __syncthreads();
+      rest.clear();
+      heads_from_lds(sh, rest);
       const int nt = min(sh.n_todo, PL_TODO);
       for (int b = 0; b < nt; b += PL_NQ) {
         const int nq = min(PL_NQ, nt - b);
@@ -657,9 +681,18 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
           }
         }
         __syncthreads();
-        pass_recompute<T>(p, sh, Kc, so, n_live, nq, tid);
+        pass_recompute<T>(p, sh, Kc, so, n_live, nq, b, tid);
       }
-      scan_heads(p, sh, so, n_live, tid, h);
+      if (sh.n_todo > PL_TODO) {   // some reaching rows are still stale: rescan everything
+        __syncthreads();
+        scan_heads(p, sh, so, n_live, tid, h);
+      } else {
+        // only the recomputed rows changed: the best head so far or one of theirs; the stale
+        // bounds left are the rest's
+        h.u1 = rest.u1;
+        h.u2 = rest.u2;
+        for (int q = 0; q < nt; ++q) h.row(sh.th_c[q], sh.th_s[q], sh.th_p[q], sh.th_pos[q], sh.todo[q]);
+      }
       continue;
     }
     if (h.s < 0) {   // fewer than two entries may merge: the budget cannot be reached
