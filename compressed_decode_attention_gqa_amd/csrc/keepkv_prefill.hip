@@ -27,14 +27,18 @@
 //               tokens and keeps its own top PK per row; the lanes' lists are
 //               merged (their union holds every row's top PK).
 //   k_pm_loop   one workgroup per scope runs the greedy loop over the scope's
-//               candidates, listed in LDS. Per merge: a scan of the list heads
-//               and stale bounds; the merge itself (one wave); one pass of the
-//               merged key against every candidate, 16 lanes per key row (16
-//               bytes each) and 4 row steps of loads in flight, which gives the
-//               merged row its list and lets every other row drop the merged
-//               pair and take the merged entry when it beats an entry of its
-//               list (a wave ballot over the rows' list entries finds the few
-//               rows that change).
+//               candidates, listed in LDS. Per merge: the merge itself (one wave,
+//               float64 weights); then one pass of the merged key against every
+//               candidate, 16 lanes per key row (16 bytes each, 8 row steps of
+//               loads in flight), after which lane e of each 16-lane group owns
+//               the row of step e with its list in registers: the merged row's
+//               list is collected, every other row drops the merged pair or takes
+//               the merged entry when it beats an entry of its list (or goes
+//               stale), and the heads and stale bounds for the next pair choice
+//               are reduced on the way. When two stale bounds could reach the
+//               best head, the stale rows that could are recomputed on the
+//               float64 MFMA, 16 per pass (their keys as a 16-row operator tile),
+//               and only their new heads join the pair choice.
 // Products of the cache's bf16 (or fp32) keys are exact in float64, so the
 // cosines equal the ones of the float64 oracle up to the rounding of the sums.
 #include "kvc_f64mfma.h"
