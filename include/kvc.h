@@ -371,8 +371,9 @@ int32_t kvc_laprox_score(const void *q_win, const void *k, const void *v, const 
 /* kvc_laprox_score_marked -- kvc_laprox_score, plus stage timing for
  * measurement: events (hipEvent_t handles created by the caller, n_events = 8)
  * are recorded on `stream` before the first kernel and after each of the seven
- * stages (W_bar prep, window pass 1, row combine, window pass 2, V W_bar on
- * MFMA, product, normalisation). events NULL behaves as kvc_laprox_score;
+ * stages (Gram matrices W_bar W_bar^T, window pass 1, row combine, window pass
+ * 2, value-output norms v M v^T, product, normalisation). events NULL behaves as
+ * kvc_laprox_score;
  * n_events other than 8 with events non-NULL is KVC_ERR_ARG. */
 int32_t kvc_laprox_score_marked(const void *q_win, const void *k, const void *v, const void *w_o,
                                 int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,

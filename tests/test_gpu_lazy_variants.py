@@ -100,6 +100,15 @@ def test_select_evict_protected_matches_oracle():
         ref = np.zeros(L, dtype=np.uint8)
         ref[oracle.bottom_k_protected(key[s, :L], pos[s, :L], max(0, L - budgets), 50)] = 1
         assert np.array_equal(ev[s, :L], ref), s
+    # no positions: the slot index orders ties and sets the protection
+    kvc.kvc_select_evict_protected(kd, None, ld, S, C, budgets, 400, evict, n_ev, ws)
+    torch.cuda.synchronize()
+    ev = evict.cpu().numpy()
+    for s in range(S):
+        L = int(lens[s])
+        ref = np.zeros(L, dtype=np.uint8)
+        ref[oracle.bottom_k_protected(key[s, :L], np.arange(L), max(0, L - budgets), 400)] = 1
+        assert np.array_equal(ev[s, :L], ref), s
     # a bound below every position protects everything: the plain selection again
     kvc.kvc_select_evict_protected(kd, pd, ld, S, C, budgets, 0, evict, n_ev, ws)
     torch.cuda.synchronize()
@@ -164,6 +173,11 @@ def test_keep_jaccard_matches_oracle():
     for s in range(S):
         L = int(lens[s])
         assert got[s] == np.float32(oracle.keep_jaccard(a[s, :L], b[s, :L])), s
+    kvc.kvc_keep_jaccard(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), None, S, C, out)   # every slot
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for s in range(S):
+        assert got[s] == np.float32(oracle.keep_jaccard(a[s], b[s])), s
     # two scorers on one state
     wl = C2.scaled(context=1000, budget=100, steps=1, n_kv=3)
     run = DeviceRun(wl)
