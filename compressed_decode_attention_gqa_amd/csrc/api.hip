@@ -377,6 +377,11 @@ extern "C" {
 
 int32_t kvc_version(void) { return KVC_VERSION; }
 
+int32_t kvc_check(void *stream) {
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return KVC_ERR_DEVICE;
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_DEVICE;
+}
+
 const char *kvc_status_string(int32_t s) {
   switch (s) {
     case KVC_OK: return "ok";

@@ -29,7 +29,7 @@ EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
             "kvc_keepkv_prefill_workspace_size", "kvc_keepkv_ema_init_workspace_size",
             "kvc_laprox_workspace_size",
-            "kvc_workspace_status", "kvc_status_string", "kvc_version")
+            "kvc_workspace_status", "kvc_status_string", "kvc_check", "kvc_version")
 
 
 class KvcError(RuntimeError):
@@ -84,6 +84,7 @@ _SIGS = {
     "kvc_laprox_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "kvc_workspace_status": (_I, [_P, _P]),
     "kvc_status_string": (ctypes.c_char_p, [_I]),
+    "kvc_check": (_I, [_P]),
     "kvc_version": (_I, []),
 }
 
@@ -222,6 +223,11 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 def kvc_workspace_status(ws: torch.Tensor, stream=None) -> int:
     return lib().kvc_workspace_status(_ptr(ws), _stream(stream))
+
+
+def kvc_check(stream=None) -> int:
+    """Synchronises the stream; 0, or KVC_ERR_DEVICE after an asynchronous device error."""
+    return lib().kvc_check(_stream(stream))
 
 
 def kvc_decode_attn_score(cache: Cache, k_new, v_new, t: int, q, G: int, scale: float, out, lse, s,

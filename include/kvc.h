@@ -400,6 +400,10 @@ size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int3
 int32_t kvc_workspace_status(void *ws, void *stream);
 
 const char *kvc_status_string(int32_t status);
+
+/* Synchronises `stream` and reports an asynchronous device error of the work queued
+ * on it: KVC_ERR_DEVICE if the stream (or an earlier launch) failed, else KVC_OK. */
+int32_t kvc_check(void *stream);
 int32_t kvc_version(void);
 
 #ifdef __cplusplus

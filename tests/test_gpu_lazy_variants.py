@@ -208,3 +208,4 @@ def test_keep_jaccard_matches_oracle():
         keep_m[oracle.bottom_k(mv[s, :n], pv[s, :n], n - B2)] = False
         assert got[s] == np.float32(oracle.keep_jaccard(keep_s, keep_m)), s
     print("jaccard(single-step score, EMA utility) per KV head:", np.round(got, 4), flush=True)
+    assert kvc.kvc_check() == 0
