@@ -30,8 +30,10 @@
 //               candidates, listed in LDS. Per merge: the merge itself (one wave,
 //               float64 weights); then one pass of the merged key against every
 //               candidate, 16 lanes per key row (16 bytes each, 8 row steps of
-//               loads in flight), after which lane e of each 16-lane group owns
-//               the row of step e with its list in registers: the merged row's
+//               loads in flight; the 8 steps' partial dot products reduced over
+//               the 16 lanes by the lane-permuted transposed reduction), after
+//               which one lane per step owns that row with its list in
+//               registers: the merged row's
 //               list is collected, every other row drops the merged pair or takes
 //               the merged entry when it beats an entry of its list (or goes
 //               stale), and the heads and stale bounds for the next pair choice
@@ -53,7 +55,7 @@ constexpr int PM_CT = 4;         // k_pm_rows: 16-row column tiles of the operat
 constexpr int PM_ROWS = 16 * PM_CT;
 constexpr int PL_NT = 512;       // k_pm_loop: 8 waves
 constexpr int PL_W = PL_NT / 64;
-constexpr int PL_NS = 8;         // row steps per batch of the merge pass (lane e < PL_NS of a group owns step e's row)
+constexpr int PL_NS = 8;         // row steps per batch of the merge pass (a power of 2, <= 16)
 constexpr int PL_NQ = 16;        // stale rows recomputed per pass: one 16-row MFMA operator tile
 constexpr int PL_TODO = 256;     // stale rows collected per recomputation round
 constexpr int PL_SCAN = 8;       // rows per thread per load batch of the head scan
@@ -784,17 +786,22 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       list_clear(lc, lp, ls);
       Heads hn;
       hn.clear();
+      // lane-permuted transposed reduction of the NS steps' partial dot products over the 16
+      // lanes of a row group: slot i of lane e holds step i ^ own, and the lane ends with the
+      // total of step own (two lanes per step; the first of them takes the row)
+      const int own = perm_head<16, NS>(e);
+      const bool lead = perm_rep_lane<16, NS>(own) == e;
       for (int k0 = 0; k0 < n_live; k0 += PL_W * 4 * NS) {
         Chunk8<T> kc[NS];
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-          const int k = k0 + (wave * NS + u) * 4 + gi;
-          if (k < n_live) kc[u].load(Kc + int64_t(sh.live[k]) * HD * ES, e);
-          else kc[u].zero();
+        for (int i = 0; i < NS; ++i) {
+          const int k = k0 + (wave * NS + (i ^ own)) * 4 + gi;
+          if (k < n_live) kc[i].load(Kc + int64_t(sh.live[k]) * HD * ES, e);
+          else kc[i].zero();
         }
-        // this lane's row: step e of its group
-        const int ko = k0 + (wave * NS + e) * 4 + gi;
-        const int jo = (e < NS && ko < n_live) ? sh.live[ko] : -1;
+        // this lane's row: step own of its group
+        const int ko = k0 + (wave * NS + own) * 4 + gi;
+        const int jo = (lead && ko < n_live) ? sh.live[ko] : -1;
         u32x4 mt = u32x4{0u, 0u, 0u, 0u}, r0, r1, r2, r3;
         r0 = r1 = r2 = r3 = u32x4{0u, 0u, 0xffffffffu, 0u};
         if (jo >= 0) {
@@ -804,16 +811,16 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
           r2 = ld16(rec_at(p, so + jo) + 32);
           r3 = ld16(rec_at(p, so + jo) + 48);
         }
-        double mine = 0.0;
+        double part[NS];
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
+        for (int i = 0; i < NS; ++i) {
           double dot = 0.0;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) dot = fma(qv[v], kc[u].get(v), dot);
-          dot = group_sum_f64<16>(dot);
-          mine = e == u ? dot : mine;
+          for (int v = 0; v < 8; ++v) dot = fma(qv[v], kc[i].get(v), dot);
+          part[i] = dot;
           __builtin_amdgcn_sched_barrier(0);   // one step's conversions live at a time
         }
+        const double mine = preduce<16, NS, 0>(part);
         if (jo == gone) sh.gidx = ko;
         if (jo >= 0 && jo != surv && jo != gone) {
           const double nj = ent_c(mt);
