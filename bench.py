@@ -649,6 +649,7 @@ def main():
         # one call per layer (the layer's KV heads attend and score, the shared utility is
         # updated and the scope evicts); the first layer's call appends every layer's rows
         nkv = wl.n_kv
+        cap = cache.capacity
         q_layers = [[q[:, l * nkv:(l + 1) * nkv].contiguous() for l in range(wl.n_layers)] for q in q_all]
         out_layers = [torch.empty((S, nkv, G, d), device=dev) for _ in range(wl.n_layers)]
         lse_layers = [torch.empty((S, nkv, G), device=dev) for _ in range(wl.n_layers)]
@@ -656,8 +657,11 @@ def main():
         def step_call(i, max_len):
             refresh = wl.lazy_refresh == 0 or i % wl.lazy_refresh == 0
             for l in range(wl.n_layers):
+                # the first layer evicts to the budget; the later layers cannot evict, which the
+                # call says with budget = capacity (their finish launch is then skipped)
                 kvc.kvc_decode_step(cache, kn_all[i] if l == 0 else None, vn_all[i] if l == 0 else None,
-                                    pos0 + i, q_layers[i][l], G, scale, wl.rule, alpha, B, out_layers[l],
+                                    pos0 + i, q_layers[i][l], G, scale, wl.rule, alpha, B if l == 0 else cap,
+                                    out_layers[l],
                                     lse_layers[l], s, mom, None, None, refresh=refresh, attn_unit0=l * nkv,
                                     attn_units=nkv, max_len=max_len, ws=ws)
     else:

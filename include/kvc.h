@@ -330,7 +330,10 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
  * every unit of the scope. This is how one slot set shared by all layers of a
  * sequence is driven layer by layer (InertiaKV §3.1: the utility is updated
  * after every compressed layer); a call whose scope is already within budget
- * only attends, scores and updates the utility.
+ * only attends, scores and updates the utility. A call with budget >= capacity
+ * cannot evict; without an append, evict_out or merge its selection launch is
+ * skipped (the later layers of a model-scope step, after the first layer has
+ * evicted to the budget).
  *
  * Launches. max_len <= budget + 1 (at most one eviction per scope, the steady
  * state) runs the whole step in one launch. A larger max_len (e.g. the first

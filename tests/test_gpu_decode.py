@@ -271,10 +271,12 @@ def test_merge_keeps_the_reference_output():
 C3 = synth.WORKLOADS["c3_llama8b_model_16k"]
 
 
-def _c3_step(run, step, q, kn, vn, refresh, max_len=None):
+def _c3_step(run, step, q, kn, vn, refresh, max_len=None, later_within_budget=False):
     """One decode step of a model-scope cache: layer by layer, each layer's KV heads attend,
     score (mean over the layer's query heads), update the shared utility and evict; the new
-    token's rows of every layer are appended by the first layer's call."""
+    token's rows of every layer are appended by the first layer's call. later_within_budget:
+    the layers after the first are called with budget = capacity (they cannot evict, the first
+    layer having evicted to the budget), which lets the library skip their finish launch."""
     wl = run.wl
     S = wl.n_scopes
     out_l = torch.empty((S, wl.n_kv, run.G, wl.d), device="cuda")
@@ -282,7 +284,8 @@ def _c3_step(run, step, q, kn, vn, refresh, max_len=None):
     for l in range(wl.n_layers):
         u0 = l * wl.n_kv
         kvc.kvc_decode_step(run.cache, kn if l == 0 else None, vn if l == 0 else None, run.t,
-                            q[:, u0:u0 + wl.n_kv].contiguous(), run.G, run.scale, wl.rule, run.alpha, wl.budget,
+                            q[:, u0:u0 + wl.n_kv].contiguous(), run.G, run.scale, wl.rule, run.alpha,
+                            run.cache.capacity if (later_within_budget and l > 0) else wl.budget,
                             out_l, lse_l, run.s, run.mom, None, run.evict if l == 0 else None, refresh=refresh,
                             attn_unit0=u0, attn_units=wl.n_kv, max_len=max_len or 0, ws=run.ws)
         run.out[:, u0:u0 + wl.n_kv] = out_l
@@ -347,6 +350,25 @@ def test_decode_step_c3_model_scope_reduced(lazy):
         worst = max(worst, _c3_check(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, refresh))
     assert kvc.kvc_workspace_status(run.ws) == 0
     _say("c3 reduced lazy=%d: max rel dm %.2e" % (lazy, worst))
+
+
+def test_model_scope_calls_that_cannot_evict_leave_the_same_state():
+    """Layers after the first called with budget = capacity (no finish launch) give bit-identical
+    outputs, scores, utilities and slots to calls with the real budget, from the bulk first step on."""
+    wl = C3.scaled(n_layers=4, batch=3, n_kv=2, context=900, budget=90, steps=5)
+    runs = [DeviceRun(wl), DeviceRun(wl)]
+    scopes = list(range(wl.n_scopes))
+    for step in range(1, wl.steps + 1):
+        q, kn, vn = runs[0].inputs(step)
+        for flag, run in zip((False, True), runs):
+            _c3_step(run, step, q, kn, vn, True, later_within_budget=flag)
+        torch.cuda.synchronize()
+        a, b = runs[0].snapshot(scopes), runs[1].snapshot(scopes)
+        for key in ("len", "k", "v", "pos", "m"):
+            assert np.array_equal(a[key], b[key]), (step, key)
+        for x, y in ((runs[0].out, runs[1].out), (runs[0].lse, runs[1].lse), (runs[0].s, runs[1].s)):
+            assert np.array_equal(bits(x), bits(y)), step
+    assert kvc.kvc_workspace_status(runs[1].ws) == 0
 
 
 # ---------------------------------------------------------------- the entry points composed
