@@ -138,17 +138,6 @@ __device__ __forceinline__ double pm_norm(const PrefillMergeArgs &a, int64_t row
   return *reinterpret_cast<const double *>(meta_at(a, row));
 }
 
-__device__ __forceinline__ void rec_load(const PrefillMergeArgs &a, int64_t row, double (&c)[PK], int (&pp)[PK],
-                                         int (&ss)[PK]) {
-#pragma unroll
-  for (int k = 0; k < PK; ++k) {
-    const u32x4 w = ld16(rec_at(a, row) + 16 * k);
-    c[k] = ent_c(w);
-    ss[k] = int(w.z);
-    pp[k] = int(w.w);
-  }
-}
-
 __device__ __forceinline__ void rec_store(const PrefillMergeArgs &a, int64_t row, const double (&c)[PK],
                                           const int (&pp)[PK], const int (&ss)[PK]) {
 #pragma unroll
