@@ -128,7 +128,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.list = o;     o = align_up(o + size_t(c->n_scopes) * cap * 4);
   d.list2 = o;    o = align_up(o + size_t(c->n_scopes) * cap * 4);
   d.merge_cos = o;  o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 8);
-  d.merge_slot = o; o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 4);
+  d.merge_slot = o; o = align_up(o + size_t(c->n_scopes) * d.merge_splits * 8);
   d.n_score_chunks = ceil_div(c->capacity, kScoreChunkMin);
   d.cand_key = o;   o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 8);
   d.cand_slot = o;  o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 4);
@@ -322,7 +322,7 @@ CompactLayout compact_layout(const kvc_cache *c) {
   l.list = o;     o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
   l.list2 = o;    o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
   l.cos = o;      o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 8);
-  l.slot = o;     o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 4);
+  l.slot = o;     o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 8);
   l.sel = select_layout(c->n_scopes, c->capacity, o);
   l.total = l.sel.total;
   return l;

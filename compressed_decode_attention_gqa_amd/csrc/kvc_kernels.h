@@ -24,7 +24,7 @@ struct MergeArgs {
   float eps;
   int32_t n_splits;
   double *part_cos;
-  int32_t *part_slot;
+  int32_t *part_slot;       // (slot, position) of each range's partner
 };
 
 struct MomentArgs {

@@ -149,6 +149,7 @@ struct MergeLds {
   double ke[HD];
   double best_cos[4];
   int best_slot[4];
+  int best_pos[4];
   int e;
   double lbar[2];
   double wgt[4];
@@ -168,54 +169,94 @@ __device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &s
   return sh_e;
 }
 
+// Token slot order for the lane-permuted reduction of N per-token partial sums
+// over a token's row of lanes: slot i of lane l holds token i ^ merge_perm(l).
+// The exchange stages pair lane l with l ^ 16 (32-lane rows), l ^ 15, l ^ 7,
+// l ^ 2 and l ^ 1; a linear map taking the first log2(N) of those masks to
+// N/2, N/4, ..., 1 and the rest to 0 leaves lane l with the whole sums of
+// token merge_perm(l).
+template <int LPT, int N>
+__device__ __forceinline__ int merge_perm(int l) {
+  constexpr int o = LPT == 32 ? 1 : 0;
+  constexpr auto T = [](int s) { return (2 << s) <= N ? N >> (s + 1) : 0; };
+  constexpr int c0 = T(o + 3), c1 = T(o + 2), c2 = T(o + 1) ^ c0 ^ c1, c3 = T(o) ^ T(o + 1);
+  constexpr int c4 = LPT == 32 ? T(0) : 0;
+  return ((l & 1) ? c0 : 0) ^ ((l & 2) ? c1 : 0) ^ ((l & 4) ? c2 : 0) ^ ((l & 8) ? c3 : 0) ^ ((l & 16) ? c4 : 0);
+}
+
 template <typename T>
 __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *evict, MergeArgs mg) {
   __shared__ MergeLds sh;
-  constexpr int EPV = ElemTraits<T>::EPV, LPT = HD / EPV, TPI = 64 / LPT;
+  constexpr int EPV = ElemTraits<T>::EPV, LPT = HD / EPV, TPI = 64 / LPT, RB = HD * int(sizeof(T));
+  // A wave takes every STR-th group of TPI tokens of the workgroup's range, MU
+  // groups per batch with all their loads in flight (the whole range of a
+  // workgroup at the usual split count). The per-token sums are reduced so that
+  // each lane ends with one token's, which it alone turns into a cosine.
+  constexpr int STR = (WG / 64) * TPI, MU = 8;
   const int scope = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cb = lane % LPT, tg = lane / LPT, own = merge_perm<LPT, MU>(cb);
   const int64_t so = int64_t(scope) * c.capacity;
   const int L = c.len[scope];
-  const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
+  const char *Kb = reinterpret_cast<const char *>(c.k) + int64_t(scope) * c.scope_stride * RB;
+  const int per = (L + gridDim.x - 1) / gridDim.x;
+  const int t0 = blockIdx.x * per, t1 = min(L, t0 + per);
+
+  u32x4 kv[MU];
+  int pv;
+  auto issue = [&](int b0) {
+#pragma unroll
+    for (int i = 0; i < MU; ++i) {
+      const int tok = b0 + (i ^ own) * STR + tg;
+      kv[i] = tok < t1 ? ld16(Kb + int64_t(tok) * RB + 16 * cb) : u32x4(0u);
+    }
+    const int mine = b0 + own * STR + tg;
+    pv = mine < t1 ? c.pos[so + mine] : 0;
+  };
+  int base = t0 + wave * TPI;
+  issue(base);   // these loads do not depend on the flagged slot
   const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
-  if (e >= 0 && tid < HD) sh.ke[tid] = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
-  __syncthreads();
 
   double best = -INFINITY;
   int bslot = -1, bpos = 0x7fffffff;
   if (e >= 0) {
-    const int cb = lane % LPT, tg = lane / LPT;
+    const u32x4 kw = ld16(Kb + int64_t(e) * RB + 16 * cb);
     double ke[EPV];
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) ke[j] = sh.ke[cb * EPV + j];
     double ne = 0.0;
-    for (int j = 0; j < HD; ++j) ne += sh.ke[j] * sh.ke[j];
-    ne = sqrt(ne);
-    const int per = (L + gridDim.x - 1) / gridDim.x;
-    const int t0 = blockIdx.x * per, t1 = min(L, t0 + per);
-    for (int tok0 = t0 + wave * TPI; tok0 < t1; tok0 += 4 * TPI) {
-      const int tok = tok0 + tg;
-      double dot = 0.0, nn = 0.0;
-      if (tok < t1) {
-        const u32x4 kv = ld16(reinterpret_cast<const char *>(Kb + int64_t(tok) * HD) + 16 * cb);
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      ke[j] = double(ElemTraits<T>::get(kw, j));
+      ne = fma(ke[j], ke[j], ne);
+    }
+    ne = sqrt(group_sum_f64<LPT>(ne));
+    for (;;) {
+      double pd[MU], pn[MU];
+#pragma unroll
+      for (int i = 0; i < MU; ++i) {
+        double dot = 0.0, nn = 0.0;
 #pragma unroll
         for (int j = 0; j < EPV; ++j) {
-          const double x = double(ElemTraits<T>::get(kv, j));
+          const double x = double(ElemTraits<T>::get(kv[i], j));
           dot = fma(ke[j], x, dot);
           nn = fma(x, x, nn);
         }
+        pd[i] = dot;
+        pn[i] = nn;
       }
-      dot = group_sum_f64<LPT>(dot);
-      nn = group_sum_f64<LPT>(nn);
-      if (cb == 0 && tok < t1 && tok != e) {
+      const double dot = preduce<LPT, MU, 0>(pd);
+      const double nn = preduce<LPT, MU, 0>(pn);
+      const int tok = base + own * STR + tg;
+      if (tok < t1 && tok != e) {
         const double den = ne * sqrt(nn);
         const double cs = den > 0.0 ? dot / den : 0.0;
-        const int p = c.pos[so + tok];
-        if (cos_better(cs, p, best, bpos)) {
+        if (cos_better(cs, pv, best, bpos)) {
           best = cs;
           bslot = tok;
-          bpos = p;
+          bpos = pv;
         }
       }
+      base += MU * STR;
+      if (base >= t1) break;
+      issue(base);
     }
   }
   // workgroup argmax
@@ -232,6 +273,7 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
   if (lane == 0) {
     sh.best_cos[wave] = best;
     sh.best_slot[wave] = bslot;
+    sh.best_pos[wave] = bpos;
   }
   __syncthreads();
   if (tid == 0) {
@@ -240,7 +282,7 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
     for (int w = 0; w < 4; ++w) {
       const int sw = sh.best_slot[w];
       if (sw < 0) continue;
-      const int pw = c.pos[so + sw];
+      const int pw = sh.best_pos[w];
       if (s < 0 || cos_better(sh.best_cos[w], pw, b, p)) {
         b = sh.best_cos[w];
         s = sw;
@@ -249,7 +291,8 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
     }
     const int64_t pi = int64_t(scope) * gridDim.x + blockIdx.x;
     mg.part_cos[pi] = b;
-    mg.part_slot[pi] = s;
+    mg.part_slot[2 * pi] = s;
+    mg.part_slot[2 * pi + 1] = p;
   }
 }
 
@@ -268,9 +311,8 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     int s = -1, p = 0x7fffffff;
     for (int sp = lane; sp < mg.n_splits; sp += 64) {
       const int64_t pi = int64_t(scope) * mg.n_splits + sp;
-      const int sw = mg.part_slot[pi];
+      const int sw = mg.part_slot[2 * pi], pw = mg.part_slot[2 * pi + 1];
       if (sw < 0) continue;
-      const int pw = c.pos[so + sw];
       if (s < 0 || cos_better(mg.part_cos[pi], pw, b, p)) {
         b = mg.part_cos[pi];
         s = sw;
