@@ -23,6 +23,7 @@ constexpr int kMaxSubChunksPerSplit = 512;
 constexpr int kScoreWork = 2048;
 constexpr int kScoreChunkMin = 64;
 constexpr int kMergeSplitsMax = 64;
+static_assert(kMergeSplitsMax <= 64, "k_merge_finish reads one range partner per lane of one wave");
 // One workgroup per scope (no split-K) once there are this many single-unit
 // scopes to spread over the 256 CUs, each scope's live length is bounded so
 // its per-token state fits in LDS, and a step evicts at most one entry.

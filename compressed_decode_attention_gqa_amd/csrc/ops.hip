@@ -299,26 +299,26 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
 template <typename T>
 __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t *evict, MergeArgs mg) {
   __shared__ MergeLds sh;
+  constexpr int RB = HD * int(sizeof(T)), NV = RB / 16;
   const int scope = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t so = int64_t(scope) * c.capacity;
   const int L = c.len[scope];
   const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
   const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
+  // the ranges' partners (at most 64 ranges) load beside the flagged slot
+  double pc = -INFINITY;
+  int ps = -1, pp = 0x7fffffff;
+  if (wave == 0 && lane < mg.n_splits) {
+    const int64_t pi = int64_t(scope) * mg.n_splits + lane;
+    pc = mg.part_cos[pi];
+    ps = mg.part_slot[2 * pi];
+    pp = mg.part_slot[2 * pi + 1];
+  }
   const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
   if (e < 0) return;
-  if (wave == 0) {   // the partner over the ranges' partials: lanes take partials, then a wave argmax
-    double b = -INFINITY;
-    int s = -1, p = 0x7fffffff;
-    for (int sp = lane; sp < mg.n_splits; sp += 64) {
-      const int64_t pi = int64_t(scope) * mg.n_splits + sp;
-      const int sw = mg.part_slot[2 * pi], pw = mg.part_slot[2 * pi + 1];
-      if (sw < 0) continue;
-      if (s < 0 || cos_better(mg.part_cos[pi], pw, b, p)) {
-        b = mg.part_cos[pi];
-        s = sw;
-        p = pw;
-      }
-    }
+  if (wave == 0) {   // the partner over the ranges: a wave argmax
+    double b = ps >= 0 ? pc : -INFINITY;
+    int s = ps, p = ps >= 0 ? pp : 0x7fffffff;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const double b2 = __shfl_xor(b, o);
@@ -334,6 +334,43 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   __syncthreads();
   const int cs = sh.best_slot[0];
   if (cs < 0) return;   // a single live entry: nothing to merge into
+
+  // Dropping e lets the last live slot fill its hole. The merged entry goes
+  // straight to where it ends: slot e when the partner is that last slot (then
+  // nothing else moves), else the partner's slot, with the last slot's row
+  // moved into e unless e is the last slot itself.
+  const int last = L - 1;
+  const int dst = cs == last ? e : cs;
+  const bool move = e < last && cs != last;
+  // every row this call reads, before any of it is written
+  double kek = 0.0, kck = 0.0, vek = 0.0, vck = 0.0;
+  if (tid < HD) {
+    kek = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
+    kck = double(load_elem<T>(Kb, int64_t(cs) * HD + tid));
+    vek = double(load_elem<T>(Vb, int64_t(e) * HD + tid));
+    vck = double(load_elem<T>(Vb, int64_t(cs) * HD + tid));
+  }
+  const int mvc = tid - HD;   // threads HD .. HD + 2 NV - 1 carry the moved row
+  const bool mover = move && mvc >= 0 && mvc < 2 * NV;
+  const char *mrow = reinterpret_cast<const char *>(mvc < NV ? Kb : Vb) + int64_t(last) * RB + 16 * (mvc % NV);
+  u32x4 mvec = u32x4(0u);
+  if (mover) mvec = ld16(mrow);
+  int ve = 1, vc = 1, vl = 0, pcs = 0, pl = 0;
+  float me = 0.f, mc = 0.f, ml = 0.f;
+  if (tid == 0) {
+    if (c.votes) {
+      ve = c.votes[so + e];
+      vc = c.votes[so + cs];
+      vl = c.votes[so + last];
+    }
+    if (c.m) {
+      me = c.m[so + e];
+      mc = c.m[so + cs];
+      ml = c.m[so + last];
+    }
+    pcs = c.pos[so + cs];
+    pl = c.pos[so + last];
+  }
 
   // reference logits: mean over the G query heads of scale * q_g . k
   if (wave < 2) {
@@ -354,10 +391,10 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   if (tid == 0) {
     const double le = sh.lbar[0], lc = sh.lbar[1];
     const double mu = fmax(le, lc);
-    const double pe = c.votes ? double(c.votes[so + e]) : 1.0;
-    const double pc = c.votes ? double(c.votes[so + cs]) : 1.0;
-    const double we = pe * exp(le - mu), wc = pc * exp(lc - mu);
-    const double num = mu + log(we + wc) - log(pe + pc);
+    const double pe = c.votes ? double(ve) : 1.0;
+    const double pcv = c.votes ? double(vc) : 1.0;
+    const double we = pe * exp(le - mu), wc = pcv * exp(lc - mu);
+    const double num = mu + log(we + wc) - log(pe + pcv);
     const double den = we * le + wc * lc;
     const bool guarded = fabs(den) < double(mg.eps) * exp(-mu);
     sh.wgt[0] = we / (we + wc);
@@ -365,28 +402,25 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     sh.wgt[2] = guarded ? 0.5 : we * num / den;
     sh.wgt[3] = guarded ? 0.5 : wc * num / den;
   }
-  __syncthreads();
-  if (tid < HD) {   // each thread reads and rewrites only element tid of the two rows
+  __syncthreads();   // also orders every read above before the writes below
+  if (tid < HD) {
     T *Kw = reinterpret_cast<T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
     T *Vw = reinterpret_cast<T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
-    const double kek = double(load_elem<T>(Kb, int64_t(e) * HD + tid));
-    const double kck = double(load_elem<T>(Kb, int64_t(cs) * HD + tid));
-    const double vek = double(load_elem<T>(Vb, int64_t(e) * HD + tid));
-    const double vck = double(load_elem<T>(Vb, int64_t(cs) * HD + tid));
-    store_elem<T>(Kw, int64_t(cs) * HD + tid, float(sh.wgt[2] * kek + sh.wgt[3] * kck));
-    store_elem<T>(Vw, int64_t(cs) * HD + tid, float(sh.wgt[0] * vek + sh.wgt[1] * vck));
+    store_elem<T>(Kw, int64_t(dst) * HD + tid, float(sh.wgt[2] * kek + sh.wgt[3] * kck));
+    store_elem<T>(Vw, int64_t(dst) * HD + tid, float(sh.wgt[0] * vek + sh.wgt[1] * vck));
   }
+  if (mover) st16(const_cast<char *>(mrow) + int64_t(e - last) * RB, mvec);
   if (tid == 0) {
-    if (c.votes) c.votes[so + cs] = c.votes[so + e] + c.votes[so + cs];
-    if (c.m) c.m[so + cs] = c.m[so + cs] + c.m[so + e];
+    if (c.votes) c.votes[so + dst] = ve + vc;
+    if (c.m) c.m[so + dst] = mc + me;
+    c.pos[so + dst] = pcs;
+    if (move) {
+      if (c.votes) c.votes[so + e] = vl;
+      if (c.m) c.m[so + e] = ml;
+      c.pos[so + e] = pl;
+    }
+    c.len[scope] = last;
   }
-  __threadfence_block();
-  __syncthreads();
-  // drop e: the last live slot fills its hole
-  ScopeRows rows{c.k, c.v, int64_t(scope) * c.scope_stride, c.unit_stride, 1,
-                 HD * int(sizeof(T)), c.votes ? c.votes + so : nullptr, c.pos + so, c.m ? c.m + so : nullptr};
-  if (e < L - 1) move_slot_wg(rows, L - 1, e);
-  if (tid == 0) c.len[scope] = L - 1;
 }
 
 hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArgs &mg, hipStream_t st) {
