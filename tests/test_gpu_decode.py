@@ -225,12 +225,21 @@ def test_select_evict_device_wide_top_k():
 C4 = synth.WORKLOADS["c4_keepkv_votes_64k"]
 
 
-def test_decode_step_c4_merge_reduced():
+@pytest.mark.parametrize("dtype,G", [
+    ("bf16", 4),
+    # f32 keys at this shape drive some utilities to ~1e-59: below float32's range, so the
+    # stored utilities flush to zero and tie (broken by position), while the float64 oracle
+    # still orders them; the evict sets then differ before any merge is checked
+    pytest.param("f32", 2, marks=pytest.mark.skip(reason="utilities below float32 range tie at zero; "
+                                                         "the float64 oracle orders them")),
+])
+def test_decode_step_c4_merge_reduced(dtype, G):
     """Vote-weighted decode with a ZIP merge every step (KeepKV eqs. (7)-(12)), every scope checked."""
-    wl = C4.scaled(batch=1, n_kv=5, context=3000, budget=300, steps=10)
+    _say("c4 reduced", dtype, G)
+    wl = C4.scaled(batch=1, n_kv=5, context=3000, budget=300, steps=10, dtype=dtype, G=G)
     run = DeviceRun(wl)
     rep = lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)), merge=True)
-    _say("c4 reduced", rep)
+    _say("c4 reduced", dtype, G, rep)
     assert rep.get("merged_rows_exact", 0) > 0
 
 
