@@ -1,8 +1,9 @@
 """Fixed-budget KV-cache decode step and LaProx prefill scoring on MI355X.
 
 The computation lives in libkvc.so (hand-written HIP for gfx950, C ABI in
-include/kvc.h); `kvc` is its ctypes binding and `cache` builds device caches
-for the workloads. PyTorch provides device memory and streams only.
+include/kvc.h); `kvc` is its ctypes binding (argument marshalling only) and
+`roofline` holds the algorithmic byte and flop counts the benchmark prices
+against. PyTorch provides device memory and streams only.
 """
 from . import kvc  # noqa: F401
 from .kvc import (Cache, KvcError, Moments, kvc_compact, kvc_decode_attn_score,  # noqa: F401

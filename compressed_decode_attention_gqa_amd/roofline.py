@@ -73,13 +73,6 @@ def kv_cache_bytes(n_layers: int, kv_heads: int, d: int, tokens: int, batch: int
     return n_layers * kv_heads * d * 2 * elem * tokens * batch
 
 
-def laprox_flops(n_layers: int, n_kv: int, N: int, d: int, D: int, G: int, w: int) -> dict:
-    """Algorithmic flops of LaProx scoring: V x W_bar per KV head (2 N d D) and the
-    window logits and weights (2 G w N d per pass)."""
-    units = n_layers * n_kv
-    return {"vw": units * 2 * N * d * D, "window_qk_per_pass": units * 2 * G * w * N * d}
-
-
 def moment_evict_flops(heads: int, L: int, d: int = 128) -> int:
     """Algorithmic flops of one moment-informed eviction round: per head the model
     A = tau S_tilde / n_e and c = v_bar - A k_bar (3 d^2 + 2 d^2), then for every live
