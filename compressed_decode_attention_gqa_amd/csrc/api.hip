@@ -187,7 +187,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
     if (rule < KVC_RULE_SINGLE || rule > KVC_RULE_EMA) return KVC_ERR_ARG;
     if (mom && (!mom->n || !mom->sk || !mom->sv || !mom->S)) return KVC_ERR_ARG;
     if (merge) {
-      if (!merge->q || !aligned16(merge->q) || !valid_G(merge->G)) return KVC_ERR_ARG;
+      if (!merge->q || !aligned16(merge->q) || !valid_G(merge->G) || !c->votes) return KVC_ERR_ARG;
       if (c->units_per_scope != 1 || mom) return KVC_ERR_UNSUPPORTED;
     }
   } else if (!c->m && k_new) {
@@ -312,7 +312,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
 // ------------------------------------------------------------ compact workspace
 struct CompactLayout {
   int merge_splits;
-  size_t list, list2, cos, slot, total;
+  size_t status, list, list2, cos, slot, total;
   SelectLayout sel;
 };
 
@@ -320,6 +320,7 @@ CompactLayout compact_layout(const kvc_cache *c) {
   CompactLayout l{};
   l.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
   size_t o = 0;
+  l.status = o;   o = align_up(o + 256);
   l.list = o;     o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
   l.list2 = o;    o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
   l.cos = o;      o = align_up(o + size_t(c->n_scopes) * l.merge_splits * 8);
@@ -457,6 +458,16 @@ int32_t kvc_select_evict(const float *key, const int32_t *pos, const int32_t *le
                          int32_t capacity, int32_t budget, uint8_t *evict, int32_t *n_evict, void *ws,
                          size_t ws_bytes, void *stream) {
   return select_evict(key, pos, len, n_scopes, capacity, budget, false, 0, evict, n_evict, ws, ws_bytes, stream);
+}
+
+int32_t kvc_ema_predict(const float *m, const int32_t *len, int32_t n_scopes, int32_t capacity, float alpha,
+                        int32_t t, float *out, void *stream) {
+  if (!m || !out || n_scopes <= 0 || capacity <= 0 || t < 1) return KVC_ERR_ARG;
+  if (!(alpha > 0.f && alpha < 1.f)) return KVC_ERR_ARG;
+  if (kvc::launch_ema_predict(m, len, n_scopes, capacity, alpha, t, out, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
 }
 
 int32_t kvc_keep_jaccard(const uint8_t *keep_a, const uint8_t *keep_b, const int32_t *len, int32_t n_scopes,
@@ -661,9 +672,10 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
   if (ws_bytes < l.total) return KVC_ERR_WORKSPACE;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (merge) {
-    if (!merge->q || !aligned16(merge->q) || !valid_G(merge->G)) return KVC_ERR_ARG;
+    if (!merge->q || !aligned16(merge->q) || !valid_G(merge->G) || !cache->votes) return KVC_ERR_ARG;
     if (cache->units_per_scope != 1) return KVC_ERR_UNSUPPORTED;
     kvc::MergeArgs mg{};
+    mg.status = at<int32_t>(ws, l.status);
     mg.q = static_cast<const char *>(merge->q);
     mg.G = merge->G;
     mg.scale = double(merge->scale);

@@ -25,6 +25,7 @@ struct MergeArgs {
   int32_t n_splits;
   double *part_cos;
   int32_t *part_slot;       // (slot, position) of each range's partner
+  int32_t *status;          // standalone path: set to -3 for a scope with several flagged entries
 };
 
 struct MomentArgs {
@@ -91,6 +92,8 @@ hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_
 hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);
+hipError_t launch_ema_predict(const float *m, const int32_t *len, int n_scopes, int cap, float alpha, int t,
+                              float *out, hipStream_t st);
 hipError_t launch_jaccard(const uint8_t *a, const uint8_t *b, const int32_t *len, int n_scopes, int cap, float *out,
                           hipStream_t st);
 

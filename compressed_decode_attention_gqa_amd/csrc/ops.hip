@@ -150,7 +150,7 @@ struct MergeLds {
   double best_cos[4];
   int best_slot[4];
   int best_pos[4];
-  int e;
+  int e, n_flagged;
   double lbar[2];
   double wgt[4];
 };
@@ -159,13 +159,22 @@ __device__ __forceinline__ bool cos_better(double c1, int p1, double c2, int p2)
   return c1 > c2 || (c1 == c2 && p1 < p2);
 }
 
-// The flagged slot of the scope (the largest one if several), or -1.
-__device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &sh_e) {
-  if (threadIdx.x == 0) sh_e = -1;
+// The flagged slot of the scope (the largest one if several), or -1; *count
+// (if non-null) receives the number of flagged slots.
+__device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &sh_e, int *sh_n = nullptr,
+                                             int *count = nullptr) {
+  if (threadIdx.x == 0) {
+    sh_e = -1;
+    if (sh_n) *sh_n = 0;
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < L; i += WG)
-    if (flags[i]) atomicMax(&sh_e, i);
+    if (flags[i]) {
+      atomicMax(&sh_e, i);
+      if (sh_n) atomicAdd(sh_n, 1);
+    }
   __syncthreads();
+  if (count) *count = *sh_n;
   return sh_e;
 }
 
@@ -314,8 +323,14 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     ps = mg.part_slot[2 * pi];
     pp = mg.part_slot[2 * pi + 1];
   }
-  const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
+  int n_flagged = 1;
+  const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride]
+                          : merge_flagged(evict + so, L, sh.e, &sh.n_flagged, &n_flagged);
   if (e < 0) return;
+  if (n_flagged > 1) {   // one merge per scope and call: leave the scope as it is
+    if (tid == 0 && mg.status) mg.status[0] = -3;
+    return;
+  }
   if (wave == 0) {   // the partner over the ranges: a wave argmax
     double b = ps >= 0 ? pc : -INFINITY;
     int s = ps, p = ps >= 0 ? pp : 0x7fffffff;
@@ -438,6 +453,25 @@ hipError_t launch_merge(const CacheArgs &c, const uint8_t *evict, const MergeArg
 }  // namespace kvc
 
 namespace kvc {
+// KeepKV notes, EMA score prediction eq. (14): the bias-corrected predicted score
+// S^t / (1 - alpha^t) of the EMA state S^t after t updates from zero.
+__global__ __launch_bounds__(WG) void k_ema_predict(const float *m, const int32_t *len, int cap, double alpha,
+                                                   int t, float *out) {
+  const int scope = blockIdx.y;
+  const int i = blockIdx.x * WG + threadIdx.x;
+  const int L = len ? len[scope] : cap;
+  if (i >= L || i >= cap) return;
+  const int64_t o = int64_t(scope) * cap + i;
+  out[o] = float(double(m[o]) / (1.0 - pow(alpha, double(t))));
+}
+
+hipError_t launch_ema_predict(const float *m, const int32_t *len, int n_scopes, int cap, float alpha, int t,
+                              float *out, hipStream_t st) {
+  dim3 grid((cap + WG - 1) / WG, n_scopes);
+  hipLaunchKernelGGL(k_ema_predict, grid, dim3(WG), 0, st, m, len, cap, double(alpha), t, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st) {
   dim3 grid((cap + WG - 1) / WG, n_scopes);

@@ -20,7 +20,7 @@ KVC_BF16, KVC_F32 = 0, 1
 RULES = {"single": 0, "cumulative": 1, "ema": 2}
 DTYPES = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
 
-EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_select_evict", "kvc_select_evict_protected",
+EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_ema_predict", "kvc_select_evict", "kvc_select_evict_protected",
             "kvc_keep_jaccard", "kvc_compact",
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
             "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
@@ -62,6 +62,7 @@ _SIGS = {
     "kvc_decode_step": (_I, [_P, _P, _P, _I, _P, _I, _F, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P,
                              _I, _I, _I, _P, _SZ, _P]),
     "kvc_ema_update": (_I, [_P, _P, _P, _I, _I, _I, _F, _P]),
+    "kvc_ema_predict": (_I, [_P, _P, _I, _I, _F, _I, _P, _P]),
     "kvc_select_evict": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "kvc_select_evict_protected": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "kvc_keep_jaccard": (_I, [_P, _P, _P, _I, _I, _P, _P]),
@@ -331,10 +332,9 @@ def kvc_keepkv_ema_init(cache: Cache, q_win, G: int, n_win: int, n_tokens: int, 
         handles, len(events)))
 
 
-def ema_bias_correction(alpha: float, t: int) -> float:
-    """KeepKV eq. (14): the factor 1 / (1 - alpha^t) that turns the EMA state S^t into the
-    predicted score (host arithmetic; it scales every utility of a step alike)."""
-    return 1.0 / (1.0 - alpha ** t)
+def kvc_ema_predict(m, length, n_scopes: int, capacity: int, alpha: float, t: int, out, stream=None):
+    _check("kvc_ema_predict", lib().kvc_ema_predict(_ptr(m), _ptr(length), n_scopes, capacity, alpha, t, _ptr(out),
+                                                    _stream(stream)))
 
 
 def kvc_compact(cache: Cache, evict, merge: _Merge | None, ws: torch.Tensor, stream=None):

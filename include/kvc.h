@@ -280,13 +280,23 @@ int32_t kvc_keepkv_prefill_merge_marked(const kvc_cache *cache, const kvc_merge 
  * m[s][i] = sum_j (1 - alpha) alpha^(n_win - 1 - j) s_j(i) for i < n_tokens (the
  * page's w is n_win - 1); other slots are untouched. This equals the EMA recursion
  * m <- alpha m + (1 - alpha) s run from zero over the window rows. The bias-
- * corrected prediction m / (1 - alpha^t) is one positive factor per step and
- * changes no ranking, so it is left to the caller. Logits and softmax statistics
+ * corrected prediction m / (1 - alpha^t) is kvc_ema_predict. Logits and softmax statistics
  * are float64 (fp64 MFMA), weights and m fp32. 0 < alpha < 1, else KVC_ERR_ARG;
  * 0 < n_win <= n_tokens <= capacity, else KVC_ERR_CAPACITY. Workspace:
  * kvc_keepkv_ema_init_workspace_size. */
 int32_t kvc_keepkv_ema_init(const kvc_cache *cache, const void *q_win, int32_t G, int32_t n_win, int32_t n_tokens,
                             float scale, float alpha, void *ws, size_t ws_bytes, void *stream);
+
+/* kvc_ema_predict -- KeepKV notes, EMA score prediction eq. (14): the
+ * bias-corrected predicted score out = m / (1 - alpha^t) of an EMA state m that
+ * has taken t updates from zero (eq. (15); t counts the window rows of
+ * kvc_keepkv_ema_init plus the decode steps since). The factor is formed in
+ * float64; every entry of a step is scaled alike, so rankings are unchanged.
+ * m, out: [n_scopes][capacity] fp32 (out may equal m); len: [n_scopes] or NULL
+ * (every slot): slots [0, len) are written, others untouched. 0 < alpha < 1 and
+ * t >= 1, else KVC_ERR_ARG. */
+int32_t kvc_ema_predict(const float *m, const int32_t *len, int32_t n_scopes, int32_t capacity, float alpha,
+                        int32_t t, float *out, void *stream);
 
 /* kvc_keepkv_ema_init_marked -- kvc_keepkv_ema_init, plus stage timing for
  * measurement: events (hipEvent_t handles created by the caller, n_events = 5)
@@ -303,8 +313,11 @@ int32_t kvc_keepkv_ema_init_marked(const kvc_cache *cache, const void *q_win, in
  * [0, len - n_evicted): the j-th evicted slot below the new length receives the
  * j-th surviving slot at or above it (rows of every unit, vote, position and
  * utility move together; slot order is not preserved). len is updated.
- * With merge non-NULL each scope must hold exactly one flagged entry e (per-head
- * scopes only); it is first ZIP-merged into the live entry c of largest
+ * With merge non-NULL the cache must carry votes (KVC_ERR_ARG otherwise: the
+ * merged entry's vote p_e + p_c has to be stored) and each scope at most one
+ * flagged entry e (per-head scopes only; a scope with several flags is left
+ * untouched and the workspace status word becomes KVC_ERR_UNSUPPORTED); e is
+ * first ZIP-merged into the live entry c of largest
  * cos(k_e, k_c) (ties to the lower position): KeepKV eqs. (7), (10), (12):
  * v_c <- (w_e v_e + w_c v_c)/(w_e + w_c), k_c <- eq. (12) with the guard,
  * p_c <- p_e + p_c, m_c <- m_e + m_c, with w_x = p_x e^{l_x}. Merged rows are
@@ -321,7 +334,8 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
  * the budget with the stale utility; the appended entry has utility 0).
  * mom NULL skips the fold. evict_out: [n_scopes][capacity] u8 or NULL; when
  * given it receives the flags of the evicted slots as they were before
- * compaction. s may be NULL. Merge mode is kvc_compact's (merge non-NULL).
+ * compaction. s may be NULL. Merge mode is kvc_compact's (merge non-NULL; it
+ * needs votes, KVC_ERR_ARG otherwise, and one eviction per scope and step).
  *
  * Attention group. Only units [attn_unit0, attn_unit0 + attn_units) of each
  * scope attend and score in this call (attn_units <= 0: every unit); q, out and
@@ -383,8 +397,8 @@ int32_t kvc_laprox_score_marked(const void *q_win, const void *k, const void *v,
                                 int32_t d, int32_t D, float scale, float *score, void *ws,
                                 size_t ws_bytes, void *stream, void *const *events, int32_t n_events);
 
-/* Workspace sizes in bytes. The decode workspace must be zero-filled once
- * before its first use (its first word is the device status word, see
+/* Workspace sizes in bytes. The decode and compact workspaces must be zero-filled once
+ * before their first use (their first word is the device status word, see
  * kvc_workspace_status); every other byte is written by a call before that
  * call reads it, so one workspace can serve any number of calls on one
  * stream (concurrent calls need separate workspaces). */

@@ -93,6 +93,27 @@ def test_other_entry_points_reject_bad_arguments():
                               None) == -3
     assert L.kvc_laprox_score(0x10, 0x20, 0x30, 0x40, 1, 30, 8, 100, 4, 128, 4096, 0.1, 0x50, 0x60, 1 << 30,
                               None) == -3
+    # KeepKV eq. (14) prediction: 0 < alpha < 1, t >= 1, non-null arrays
+    assert L.kvc_ema_predict(None, None, 1, 10, 0.9, 3, 0x10, None) == -1
+    assert L.kvc_ema_predict(0x10, None, 1, 10, 0.9, 0, 0x10, None) == -1
+    assert L.kvc_ema_predict(0x10, None, 1, 10, 1.0, 3, 0x10, None) == -1
+    assert L.kvc_ema_predict(0x10, None, 0, 10, 0.9, 3, 0x10, None) == -1
+
+
+@needs_lib
+def test_merge_needs_votes():
+    """A ZIP merge stores p_e + p_c (KeepKV eq. (7)): without a votes array the step and the
+    standalone compaction reject merge mode before enqueuing anything."""
+    L = kvc.lib()
+    mg = kvc._Merge(0x8000, 4, 0.1, 1e-6, 0)
+    c = _fake_cache()
+    assert L.kvc_compact(ctypes.byref(c), 0x10, ctypes.byref(mg), 0x30, 1 << 30, None) == -1
+    r = L.kvc_decode_step(ctypes.byref(c), None, None, 0, 0x6000, 4, 0.1, 0, 0.9, 10, 1, 0x7000, 0x8000, None,
+                          None, ctypes.byref(mg), None, 0, 0, 0, 0x9000, 1 << 30, None)
+    assert r == -1
+    cv = _fake_cache(votes=0x7000)
+    assert L.kvc_compact(ctypes.byref(cv), 0x10, ctypes.byref(kvc._Merge(0x8000, 3, 0.1, 1e-6, 0)), 0x30,
+                         1 << 30, None) == -1
 
 
 @needs_lib

@@ -428,3 +428,73 @@ def test_decode_step_c3_full_size_sampled():
             _say("c3 full step %d: max rel dm %.2e" % (step, worst))
     assert int(run.cache.length.min()) == C3.budget == int(run.cache.length.max())
     assert kvc.kvc_workspace_status(run.ws) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compact_merge_standalone_matches_oracle(dtype):
+    """kvc_compact in merge mode (KeepKV eqs. (7), (10), (12)) on inputs far from underflow:
+    per scope the flagged entry is merged into its largest-cosine partner (oracle
+    cosine_partner, zip_merge on the group-mean logits), rows within one ulp of the oracle's
+    rounded rows, votes and utilities add, every other row keeps its bits; a scope with two
+    flagged entries is left untouched and the workspace status reports KVC_ERR_UNSUPPORTED."""
+    _say("compact merge", dtype)
+    rng = np.random.default_rng(21)
+    S, cap, G, d = 4, 520, 4, 128
+    lens = np.array([500, 333, 2, 480], dtype=np.int32)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    K = torch.from_numpy(rng.standard_normal((S, 1, cap, d)).astype(np.float32)).to(tdt).cuda()
+    V = torch.from_numpy(rng.standard_normal((S, 1, cap, d)).astype(np.float32)).to(tdt).cuda()
+    votes = torch.from_numpy(rng.integers(1, 5, (S, cap)).astype(np.int32)).cuda()
+    pos = torch.from_numpy(np.stack([rng.permutation(10000)[:cap] for _ in range(S)]).astype(np.int32)).cuda()
+    m = torch.from_numpy(rng.random((S, cap)).astype(np.float32)).cuda()
+    length = torch.from_numpy(lens).cuda()
+    cache = kvc.Cache(k=K, v=V, pos=pos, m=m, length=length, votes=votes)
+    q = torch.from_numpy(rng.standard_normal((S, 1, G, d)).astype(np.float32)).to(tdt).cuda()
+    evict = torch.zeros((S, cap), dtype=torch.uint8, device="cuda")
+    flagged = [int(rng.integers(0, L)) for L in lens]
+    for s, e in enumerate(flagged):
+        evict[s, e] = 1
+    evict[3, (flagged[3] + 7) % lens[3]] = 1          # two flags: unsupported, scope untouched
+    scale = f32(1 / np.sqrt(d))
+    pre = {k: bits(x) for k, x in (("k", K), ("v", V), ("votes", votes), ("pos", pos), ("m", m))}
+    ws = kvc.workspace(kvc.kvc_compact_workspace_size(cache))
+    kvc.kvc_compact(cache, evict, kvc.merge_desc(q, G, scale), ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_workspace_status(ws) == -3
+    assert kvc.kvc_workspace_status(ws) == 0
+    post = {k: bits(x) for k, x in (("k", K), ("v", V), ("votes", votes), ("pos", pos), ("m", m))}
+    plen = length.cpu().numpy()
+    qh = oracle.to_f64(bits(q), dtype)
+    for s in range(S):
+        L = int(lens[s])
+        if s == 3:
+            assert plen[s] == L
+            for key in pre:
+                assert np.array_equal(pre[key][s], post[key][s]), key
+            continue
+        assert plen[s] == L - 1
+        Kh = oracle.to_f64(pre["k"][s, 0, :L], dtype)
+        Vh = oracle.to_f64(pre["v"][s, 0, :L], dtype)
+        e = flagged[s]
+        c = oracle.cosine_partner(Kh, e, pre["pos"][s, :L])
+        lbar = (scale * (qh[s, 0] @ Kh.T)).mean(axis=0)
+        k_r, v_r, p_r, _ = oracle.zip_merge(Kh[e], Vh[e], pre["votes"][s, e], lbar[e], Kh[c], Vh[c],
+                                            pre["votes"][s, c], lbar[c])
+        ppos = post["pos"][s, :L - 1].tolist()
+        assert sorted(ppos) == sorted(set(pre["pos"][s, :L].tolist()) - {int(pre["pos"][s, e])})
+        ic = ppos.index(int(pre["pos"][s, c]))
+        ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -23
+        for got, want in ((post["k"][s, 0, ic], k_r), (post["v"][s, 0, ic], v_r)):
+            want_r = oracle.to_f64(oracle.round_to_bf16(want), "bf16") if dtype == "bf16" else \
+                oracle.round_to_f32(want).astype(np.float64)
+            assert np.all(np.abs(oracle.to_f64(got, dtype) - want_r) <= np.abs(want_r) * ulp + 1e-30)
+        assert int(post["votes"][s, ic]) == p_r
+        assert abs(float(post["m"][s, ic]) - (float(pre["m"][s, c]) + float(pre["m"][s, e]))) <= 1e-6
+        slot_of = {int(p): i for i, p in enumerate(pre["pos"][s, :L].tolist())}
+        for i, p in enumerate(ppos):
+            if i == ic:
+                continue
+            j = slot_of[p]
+            assert np.array_equal(post["k"][s, 0, i], pre["k"][s, 0, j])
+            assert np.array_equal(post["v"][s, 0, i], pre["v"][s, 0, j])
+            assert post["votes"][s, i] == pre["votes"][s, j] and post["m"][s, i] == pre["m"][s, j]

@@ -66,3 +66,38 @@ def test_ema_init_matches_oracle(S, N, cap, n_win, G, alpha):
 def test_ema_init_full_size_sampled():
     wl = synth.WORKLOADS["k1_keepkv_prefill_llama8b_4k"]
     _case(wl.n_scopes, wl.context, wl.context + 1, 33, wl.G, 0.9, seed=wl.seed, heads=[0, 1, 77, 128, 255])
+
+
+def test_ema_predict_matches_oracle():
+    """KeepKV eq. (14): kvc_ema_predict = m / (1 - alpha^t) on slots [0, len) of every scope
+    (oracle.predicted_scores on the same m), other slots untouched; in place; and after t EMA
+    updates from zero with a constant score, the prediction is that score."""
+    _say("ema predict")
+    rng = np.random.default_rng(17)
+    S, cap = 5, 1000
+    lens = torch.tensor([1000, 0, 517, 1, 999], dtype=torch.int32, device="cuda")
+    m = torch.from_numpy(rng.random((S, cap)).astype(np.float32) * 1e-3).cuda()
+    for alpha, t in ((0.9, 1), (0.9, 37), (0.8, 2000), (0.5, 3)):
+        out = torch.full((S, cap), -5.0, device="cuda")
+        kvc.kvc_ema_predict(m, lens, S, cap, alpha, t, out)
+        torch.cuda.synchronize()
+        got, mh = out.cpu().numpy().astype(np.float64), m.cpu().numpy()
+        a32 = float(np.float32(alpha))
+        for s, L in enumerate(lens.tolist()):
+            ref = oracle.predicted_scores(mh[s, :L].astype(np.float64), a32, t)
+            assert np.all(np.abs(got[s, :L] - ref) <= 1e-6 * ref + 1e-30), (alpha, t, s)
+            assert np.all(got[s, L:] == -5.0)
+    m2 = m.clone()
+    kvc.kvc_ema_predict(m2, None, S, cap, 0.9, 5, m2)
+    ref = oracle.predicted_scores(m.cpu().numpy().astype(np.float64), float(np.float32(0.9)), 5)
+    assert np.all(np.abs(m2.cpu().numpy() - ref) <= 1e-6 * ref)
+    # a constant score s: t EMA updates from zero give (1 - alpha^t) s; the prediction is s
+    s_const = torch.from_numpy(rng.random((S, cap)).astype(np.float32)).cuda()
+    full = torch.full((S,), cap, dtype=torch.int32, device="cuda")
+    state = torch.zeros((S, cap), device="cuda")
+    for t in range(1, 13):
+        kvc.kvc_ema_update(state, s_const, full, S, cap, "ema", 0.9)
+        pred = torch.empty_like(state)
+        kvc.kvc_ema_predict(state, full, S, cap, 0.9, t, pred)
+        torch.cuda.synchronize()
+        assert torch.allclose(pred, s_const, rtol=2e-6, atol=0), t

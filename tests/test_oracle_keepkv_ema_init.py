@@ -16,7 +16,6 @@ import math
 import numpy as np
 import torch
 
-from compressed_decode_attention_gqa_amd import kvc
 from oracle import attend_unit, update_utility
 from oracle.keepkv_ema_init import ema_window_init, predicted_scores
 
@@ -66,4 +65,3 @@ def test_bias_correction_recovers_a_constant_score():
     for t in range(1, 25):
         S = update_utility(S, s, "ema", alpha)
         np.testing.assert_allclose(predicted_scores(S, alpha, t), s, rtol=1e-12)
-        np.testing.assert_allclose(S * kvc.ema_bias_correction(alpha, t), s, rtol=1e-12)
