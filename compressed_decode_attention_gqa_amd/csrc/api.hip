@@ -62,7 +62,7 @@ bool valid_G(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
 struct DecodeLayout {
   int n_splits, nsub_cap, merge_splits;
   int bulk_chunks, bulk_chunk, fold_splits, move_blocks;
-  size_t status, partM, partZ, partO, fac, subM, ews, flags, list, list2, cand_key, cand_slot;
+  size_t status, partM, partZ, partO, fac, subM, ews, ewsh, m64, flags, list, list2, cand_key, cand_slot, cand_pos;
   int n_score_chunks;
   size_t merge_cos, merge_slot, bulk_state, bulk_cnt, bulk_hist, fpart, total;
 };
@@ -125,6 +125,8 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.fac = o;      o = align_up(o + size_t(nu) * d.n_splits * G * 4);
   d.subM = o;     o = align_up(o + size_t(nu) * d.nsub_cap * G * 8);
   d.ews = o;      o = align_up(o + size_t(nu) * G * cap * 4);
+  d.ewsh = o;     o = align_up(o + size_t(nu) * G * cap);
+  d.m64 = o;      o = align_up(o + size_t(c->n_scopes) * cap * 8);
   d.flags = o;    o = align_up(o + size_t(c->n_scopes) * cap);
   d.list = o;     o = align_up(o + size_t(c->n_scopes) * cap * 4);
   d.list2 = o;    o = align_up(o + size_t(c->n_scopes) * cap * 4);
@@ -133,6 +135,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.n_score_chunks = ceil_div(c->capacity, kScoreChunkMin);
   d.cand_key = o;   o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 8);
   d.cand_slot = o;  o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 4);
+  d.cand_pos = o;   o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 4);
   d.bulk_state = o; o = align_up(o + size_t(c->n_scopes) * sizeof(kvc::BulkScope));
   d.bulk_cnt = o;   o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 8);
   d.bulk_hist = o;  o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 256 * 4);
@@ -239,6 +242,8 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.fac = at<float>(ws, d.fac);
   a.subM = at<double>(ws, d.subM);
   a.ews = at<float>(ws, d.ews);
+  a.ewsh = at<uint8_t>(ws, d.ewsh);
+  a.m64 = at<double>(ws, d.m64);
   a.flags = at<uint8_t>(ws, d.flags);
   a.list = at<int32_t>(ws, d.list);
   a.list2 = at<int32_t>(ws, d.list2);
@@ -248,6 +253,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.n_score_chunks = d.n_score_chunks;
   a.cand_key = at<uint64_t>(ws, d.cand_key);
   a.cand_slot = at<int32_t>(ws, d.cand_slot);
+  a.cand_pos = at<int32_t>(ws, d.cand_pos);
   {
     const int heads = attn_units * G;   // <= 64
     const int chunk = std::max(kScoreChunkMin, kScoreWork / heads);
@@ -279,6 +285,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
       b.hpart = at<uint32_t>(ws, d.bulk_hist);
       b.fpart = at<float>(ws, d.fpart);
       b.key = c->m;
+      b.key64 = a.m64;   // the step ranks float64 utilities
       b.pos = c->pos;
       b.flags = a.flags;
       b.flags2 = evict_out;

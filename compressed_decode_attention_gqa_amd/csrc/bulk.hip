@@ -8,7 +8,9 @@
 //              per pass a 256-bin histogram of each chunk's keys under the
 //              current prefix, then one workgroup per scope sums the chunks and
 //              picks the digit (InertiaKV §3.1: lowest utility first, ties to
-//              the lower position)
+//              the lower position). The fused step ranks float64 utilities: 8
+//              passes over their 64-bit order key, then (only if equal values
+//              straddle the cut) 4 passes over the positions of the tied entries
 //   flags      evicted flags and per-chunk counts of evicted slots and movers
 //   lists      evicted slots ascending; survivors at or above L - k ascending
 //   fold       MomentKV §4.1 / Appendix A.1 moment sums of the evicted rows,
@@ -17,8 +19,10 @@
 //   move       hole filling: mover j goes to evicted slot j (the evicted slots
 //              below L - k come first in the ascending list), then len = L - k
 //
-// Keys are distinct because live positions are distinct, so the final cut
-// takes its bin whole: slot i is evicted iff (key(i) & mask) <= prefix.
+// (key, position) pairs are distinct because live positions are distinct, so
+// the final cut takes its bin whole: slot i is evicted iff (hi & mask) <
+// prefix, or (hi & mask) == prefix and (lo & lmask) <= lprefix, where hi is the
+// 64-bit key and lo the tie key (lmask = 0 when the 64-bit keys decided).
 #include "kvc_decode.h"
 #include "kvc_device.h"
 #include "kvc_kernels.h"
@@ -30,12 +34,18 @@ namespace {
 constexpr int FOLD_NB = 16;                     // evicted rows staged per batch
 constexpr int PART_STRIDE = HD * HD + 2 * HD;   // floats per fold partial: S, s_k, s_v
 
-__device__ __forceinline__ uint64_t slot_key(const BulkArgs &b, int64_t sc, int i) {
+struct SlotKey {
+  uint64_t hi;   // the 64-bit key
+  uint32_t lo;   // tie key of equal 64-bit keys (positions; 0 when hi holds the position)
+};
+
+__device__ __forceinline__ SlotKey slot_key(const BulkArgs &b, int64_t sc, int i) {
   const uint32_t p = b.pos ? uint32_t(b.pos[sc + i]) : uint32_t(i);
-  if (!b.protect) return order_key(b.key[sc + i], p);
+  if (b.key64) return SlotKey{orderable_f64(b.key64[sc + i]), p};
+  if (!b.protect) return SlotKey{order_key(b.key[sc + i], p), 0u};
   // (protected, value, position) in 1 + 32 + 31 bits: positions are non-negative int32
   const uint64_t prot = int32_t(p) >= b.protect_from ? 1ull : 0ull;
-  return (prot << 63) | (uint64_t(orderable_f32(b.key[sc + i])) << 31) | uint64_t(p & 0x7fffffffu);
+  return SlotKey{(prot << 63) | (uint64_t(orderable_f32(b.key[sc + i])) << 31) | uint64_t(p & 0x7fffffffu), 0u};
 }
 
 // ------------------------------------------------------------ standalone set-up
@@ -48,6 +58,8 @@ __global__ __launch_bounds__(WG) void k_bulk_sel_init(const BulkArgs b) {
   BulkScope &st = b.st[scope];
   st.prefix = 0;
   st.mask = 0;
+  st.lprefix = 0;
+  st.lmask = 0;
   st.krem = k;
   st.done = k == 0 ? 1 : 0;
   st.L = L;
@@ -122,13 +134,16 @@ __global__ __launch_bounds__(WG) void k_bulk_movers(const BulkArgs b) {
 // Each workgroup histograms the digit at `shift` of the keys of its chunk that
 // match the current prefix and stores the 256 counts (plain stores: no
 // device-scope atomics or fences); the pick kernel sums the chunks' counts.
-__global__ __launch_bounds__(WG) void k_bulk_hist(const BulkArgs b, const int shift) {
+// Phase 0 takes digits of the 64-bit key, phase 1 of the tie key among the
+// entries whose 64-bit key equals the whole prefix.
+__global__ __launch_bounds__(WG) void k_bulk_hist(const BulkArgs b, const int shift, const int phase) {
   __shared__ uint32_t hist[256];
   const int scope = blockIdx.y, tid = threadIdx.x;
   const BulkScope &st = b.st[scope];
   if (!st.run || st.done) return;     // the same for every workgroup of the scope
   const int L = st.L;
   const uint64_t prefix = st.prefix, mask = st.mask;
+  const uint32_t lprefix = st.lprefix, lmask = st.lmask;
   hist[tid] = 0u;
   __syncthreads();
   const int64_t sc = int64_t(scope) * b.cap;
@@ -139,9 +154,14 @@ __global__ __launch_bounds__(WG) void k_bulk_hist(const BulkArgs b, const int sh
     uint32_t bin = 0;
     bool hit = false;
     if (i < i1) {
-      const uint64_t key = slot_key(b, sc, i);
-      hit = (key & mask) == prefix;
-      bin = uint32_t(key >> shift) & 255u;
+      const SlotKey key = slot_key(b, sc, i);
+      if (phase == 0) {
+        hit = (key.hi & mask) == prefix;
+        bin = uint32_t(key.hi >> shift) & 255u;
+      } else {
+        hit = key.hi == prefix && (key.lo & lmask) == lprefix;
+        bin = (key.lo >> shift) & 255u;
+      }
     }
     // Keys crowd into a few bins in the leading passes (utilities share their
     // exponent): the wave first adds the counts of up to two shared bins with
@@ -163,12 +183,11 @@ __global__ __launch_bounds__(WG) void k_bulk_hist(const BulkArgs b, const int sh
 }
 
 // One workgroup per scope: the bin holding the krem-th key under the prefix.
-__global__ __launch_bounds__(WG) void k_bulk_pick(const BulkArgs b, const int shift) {
+__global__ __launch_bounds__(WG) void k_bulk_pick(const BulkArgs b, const int shift, const int phase) {
   __shared__ int red[8];
   const int scope = blockIdx.x, tid = threadIdx.x;
   BulkScope &st = b.st[scope];
   if (!st.run || st.done) return;
-  const uint64_t prefix = st.prefix, mask = st.mask;
   const int krem = st.krem;
   const uint32_t *h = b.hpart + int64_t(scope) * b.n_chunks * 256;
   int cnt = 0;
@@ -176,10 +195,18 @@ __global__ __launch_bounds__(WG) void k_bulk_pick(const BulkArgs b, const int sh
   int tot;
   const int excl = wg_exclusive_scan(cnt, red, &tot);
   if (excl < krem && krem <= excl + cnt) {
-    st.prefix = prefix | (uint64_t(tid) << shift);
-    st.mask = mask | (uint64_t(255) << shift);
+    if (phase == 0) {
+      st.prefix |= uint64_t(tid) << shift;
+      st.mask |= uint64_t(255) << shift;
+    } else {
+      st.lprefix |= uint32_t(tid) << shift;
+      st.lmask |= 255u << shift;
+    }
     st.krem = krem - excl;
-    if (cnt == krem - excl || shift == 0) st.done = 1;
+    // the last digit of the deciding key: float keys carry the position, float64
+    // keys hand equal values on to the position passes
+    const bool last = shift == 0 && (phase == 1 || b.key64 == nullptr);
+    if (cnt == krem - excl || last) st.done = 1;
   }
 }
 
@@ -192,11 +219,14 @@ __global__ __launch_bounds__(WG) void k_bulk_flags(const BulkArgs b) {
   const int L = st.L, B = st.B;
   const bool any = st.k > 0;
   const uint64_t prefix = st.prefix, mask = st.mask;
+  const uint32_t lprefix = st.lprefix, lmask = st.lmask;
   const int64_t sc = int64_t(scope) * b.cap;
   const int i0 = blockIdx.x * b.chunk, i1 = min(L, i0 + b.chunk);
   int n_ev = 0, n_mv = 0;
   for (int i = i0 + tid; i < i1; i += WG) {
-    const bool ev = any && (slot_key(b, sc, i) & mask) <= prefix;
+    const SlotKey key = slot_key(b, sc, i);
+    const uint64_t km = key.hi & mask;
+    const bool ev = any && (km < prefix || (km == prefix && (key.lo & lmask) <= lprefix));
     if (b.flags) b.flags[sc + i] = ev ? 1 : 0;
     if (b.flags2) b.flags2[sc + i] = ev ? 1 : 0;
     n_ev += ev ? 1 : 0;
@@ -700,8 +730,14 @@ __global__ __launch_bounds__(WG) void k_bulk_move(const StepArgs a, const BulkAr
 static void launch_radix(const BulkArgs &b, hipStream_t st) {
   const dim3 chunks(b.n_chunks, b.n_scopes);
   for (int shift = 56; shift >= 0; shift -= 8) {
-    hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, b, shift);
-    hipLaunchKernelGGL(k_bulk_pick, dim3(b.n_scopes), dim3(WG), 0, st, b, shift);
+    hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, b, shift, 0);
+    hipLaunchKernelGGL(k_bulk_pick, dim3(b.n_scopes), dim3(WG), 0, st, b, shift, 0);
+  }
+  if (b.key64) {   // positions of equal float64 keys (the kernels return at once once done)
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hipLaunchKernelGGL(k_bulk_hist, chunks, dim3(WG), 0, st, b, shift, 1);
+      hipLaunchKernelGGL(k_bulk_pick, dim3(b.n_scopes), dim3(WG), 0, st, b, shift, 1);
+    }
   }
   hipLaunchKernelGGL(k_bulk_flags, chunks, dim3(WG), 0, st, b);
 }

@@ -9,7 +9,8 @@
 // lane-permuted transposed reduction (one head's logit per lane, no selects);
 // a per-wave running maximum rescaled only when it moves; one weight
 // exp(l - M) per (token, head) formed by one lane. The per-token weights go to
-// the workspace (ews) with the running maximum of each sub-chunk (subM), so
+// the workspace (ews, with their shift counts in ewsh for weights below
+// float32's range) with the running maximum of each sub-chunk (subM), so
 // the epilogue can normalise them into attention weights; the waves'
 // (M, Z, value sums) are combined into the workgroup's split partial.
 //
@@ -85,6 +86,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
   const int myh = perm_head<LPT, G>(cb);
   const int dup = lane & (D - 1);
   float *ews = a.ews + int64_t(gu) * G * cap;
+  uint8_t *ewsh = a.ewsh + int64_t(gu) * G * cap;
   double *subM = a.subM + int64_t(gu) * a.nsub_cap * G;
 
   // queries scaled by tau (exact in float64), slot i holding head i ^ myh
@@ -167,13 +169,17 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
 #pragma unroll
             for (int i2 = 1; i2 < UNR; ++i2) x = it == i2 ? lg[i2] : x;
             const int tok = c * CHW + it * TPI + tg;
-            const float e = exp_split(x - Mrun);
+            int shc;
+            const float e = exp_shifted(x - Mrun, shc);
             float p = 1.f;
             if (VOTES) p = (a.append && tok == L - 1) ? 1.f : float(sh.st.vt[wave][min(tok, L - 1) - c * CHW]);
-            const float w = p * e;
+            const float w = shc ? 0.f : p * e;   // below exp(-SHIFT_STEP) of the maximum
             Zrun += double(w);
             sh.st.w[wave][it][tg][myh] = w;
-            if (tok < L) ews[int64_t(myh) * cap + tok] = e;
+            if (tok < L) {
+              ews[int64_t(myh) * cap + tok] = e;
+              ewsh[int64_t(myh) * cap + tok] = uint8_t(shc);
+            }
           }
         }
         __builtin_amdgcn_wave_barrier();

@@ -15,12 +15,14 @@
 // rescaled only when it moves; each lane forms one weight exp(l - M) (float64
 // argument split into float hi + lo), and the maximum of every sub-chunk is
 // kept so the epilogue can turn weights into normalised per-token weights.
-// Per-token weights, utilities and votes of the scope live in LDS.
+// Per-token weights (with their shift counts, for weights below float32's
+// range), utilities (float64) and votes of the scope live in LDS.
 //
 // Epilogue (same workgroup): combine the waves' partials (one lane per
 // (wave, head)), write o and lse, score every token, update the utility, take
 // the eviction by argmin over (m, slot) with a tie count carried through the
-// same reduction (ties are broken by position), fold it into the moments and
+// same reduction (the float64 utility is ranked before it is stored as
+// float32; ties are broken by position), fold it into the moments and
 // fill its slot with the last one. The moment sums and the last row are
 // loaded before scoring so the fold does not wait on memory. Barriers order
 // LDS only, so those loads (and the streaming's last, unused prefetches) stay
@@ -39,10 +41,11 @@ int decode_unit_chunk_tokens(int dtype) {
 }
 
 // Dynamic LDS: per-token weights e[G][ld], sub-chunk maxima [nsub][G] (double),
-// utilities m[ld] and votes[ld]; ld = lds_len rounded up to whole sub-chunks.
+// utilities m[ld] (double), votes[ld] and the weights' shift counts sh[ld][G]
+// (bytes); ld = lds_len rounded up to whole sub-chunks.
 struct UnitLdsLayout {
   int ld;
-  size_t e, f, m, v, total;
+  size_t e, f, m, v, sh, total;
 };
 
 __host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds_len, bool votes) {
@@ -55,11 +58,23 @@ __host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds
   l.f = o;
   o += size_t(l.ld / chw) * G * 8;
   l.m = o;
-  o += size_t(l.ld) * 4;
+  o += size_t(l.ld) * 8;
   l.v = o;
   if (votes) o += size_t(l.ld) * 4;
+  o = (o + 15) & ~size_t(15);
+  l.sh = o;
+  o += size_t(l.ld) * G;
   l.total = (o + 15) & ~size_t(15);
   return l;
+}
+
+// The G shift counts of one token (bytes sh[i*G .. i*G + G - 1]) as one integer.
+template <int G>
+__device__ __forceinline__ uint64_t token_shifts(const uint8_t *sh, int i) {
+  if constexpr (G == 1) return sh[i];
+  else if constexpr (G == 2) return *reinterpret_cast<const uint16_t *>(sh + 2 * i);
+  else if constexpr (G == 4) return *reinterpret_cast<const uint32_t *>(sh + 4 * i);
+  else return *reinterpret_cast<const uint64_t *>(sh + 8 * i);
 }
 
 template <typename T, int G>
@@ -72,7 +87,7 @@ struct UnitLds {
       float pO[Geo::NW][G][HD];
       double M[G], iZ[G];
       float fac[Geo::NW][G];
-      uint32_t wkey[Geo::NW];
+      uint64_t wkey[Geo::NW];
       int wslot[Geo::NW], wcnt[Geo::NW];
       int tie_pos, tie_slot;
       float rowk[HD], rowv[HD];
@@ -113,8 +128,9 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   const int ld = lay.ld;
   float *e_lds = reinterpret_cast<float *>(dyn + lay.e);
   double *f_lds = reinterpret_cast<double *>(dyn + lay.f);
-  float *m_lds = reinterpret_cast<float *>(dyn + lay.m);
+  double *m_lds = reinterpret_cast<double *>(dyn + lay.m);
   int *v_lds = reinterpret_cast<int *>(dyn + lay.v);
+  uint8_t *s_lds = reinterpret_cast<uint8_t *>(dyn + lay.sh);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int scope = blockIdx.x, gu = scope;
@@ -182,7 +198,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
         const bool tail = (c + 1) * CHW > L;
         // scope arrays of this sub-chunk into LDS
         if (lane < CHW) {
-          m_lds[c * CHW + lane] = mv[s];
+          m_lds[c * CHW + lane] = double(mv[s]);
           if (VOTES) v_lds[c * CHW + lane] = vv[s];
         }
         double lg[UNR];
@@ -228,13 +244,18 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
 #pragma unroll
             for (int i2 = 1; i2 < UNR; ++i2) x = it == i2 ? lg[i2] : x;
             const int tok = c * CHW + it * TPI + tg;
-            const float e = exp_split(x - Mrun);
+            int shc;
+            const float e = exp_shifted(x - Mrun, shc);
             float p = 1.f;
             if (VOTES) p = (a.append && tok == L - 1) ? 1.f : float(v_lds[min(tok, L - 1)]);
-            const float w = p * e;
+            // a shifted weight is below exp(-SHIFT_STEP) of the maximum: nothing in o or Z
+            const float w = shc ? 0.f : p * e;
             Zrun += double(w);
             sh.w[wave][it][tg][myh] = w;
-            if (tok < L) e_lds[myh * ld + tok] = e;
+            if (tok < L) {
+              e_lds[myh * ld + tok] = e;
+              s_lds[tok * G + myh] = uint8_t(shc);
+            }
           }
         }
         __builtin_amdgcn_wave_barrier();
@@ -361,24 +382,31 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   // ---- score, utility; per thread the smallest (m, slot) and how many slots hold that m
   const double inv_heads = 1.0 / double(G);
   const double alpha = double(a.alpha);
-  uint32_t bestm = 0xffffffffu;
+  uint64_t bestm = ~0ull;
   int bslot = 0x7fffffff, bcnt = 0;
   for (int i = tid; i < L; i += NT) {
     const bool isnew = a.append && i == L - 1;
-    float mval = isnew ? 0.f : m_lds[i];
+    double mval = isnew ? 0.0 : m_lds[i];
     if (score) {
       const int c = i / CHW;
+      const uint64_t shw = token_shifts<G>(s_lds, i);
       double acc = 0.0;
+      if (shw == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc += double(e_lds[g * ld + i]) * f_lds[c * G + g];
+        for (int g = 0; g < G; ++g) acc += double(e_lds[g * ld + i]) * f_lds[c * G + g];
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          acc += double(e_lds[g * ld + i]) * f_lds[c * G + g] * shift_scale(int((shw >> (8 * g)) & 255u));
+      }
       if (VOTES && !isnew) acc *= double(v_lds[i]);
       const double sv = acc * inv_heads;
       if (a.s) a.s[sc + i] = float(sv);
-      if (step) mval = float(apply_rule(a.rule, alpha, double(mval), sv));
+      if (step) mval = apply_rule(a.rule, alpha, mval, sv);
     }
-    if ((step && score) || isnew) a.m[sc + i] = mval;
+    if ((step && score) || isnew) a.m[sc + i] = float(mval);
     m_lds[i] = mval;
-    const uint32_t om = orderable_f32(mval);
+    const uint64_t om = orderable_f64(mval);
     if (om < bestm) {
       bestm = om;
       bslot = i;
@@ -391,7 +419,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   if (k == 1) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t m2 = __shfl_xor(bestm, o);
+      const uint64_t m2 = shfl_xor_u64(bestm, o);
       const int s2 = __shfl_xor(bslot, o);
       const int c2 = __shfl_xor(bcnt, o);
       if (m2 < bestm) {
@@ -413,11 +441,11 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       sh.ep.tie_slot = 0x7fffffff;
     }
     lds_barrier();
-    uint32_t mmin = sh.ep.wkey[0];
+    uint64_t mmin = sh.ep.wkey[0];
     int smin = sh.ep.wslot[0], ties = sh.ep.wcnt[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      const uint32_t m2 = sh.ep.wkey[w];
+      const uint64_t m2 = sh.ep.wkey[w];
       if (m2 < mmin) {
         mmin = m2;
         smin = sh.ep.wslot[w];
@@ -430,14 +458,14 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     if (ties > 1) {
       // exact utility ties: the smallest position among them goes
       for (int i = tid; i < L; i += NT) {
-        if (orderable_f32(m_lds[i]) == mmin) {
+        if (orderable_f64(m_lds[i]) == mmin) {
           const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
           atomicMin(&sh.ep.tie_pos, p);
         }
       }
       lds_barrier();
       for (int i = tid; i < L; i += NT) {
-        if (orderable_f32(m_lds[i]) == mmin) {
+        if (orderable_f64(m_lds[i]) == mmin) {
           const int p = (a.append && i == L - 1) ? a.t : a.pos[sc + i];
           if (p == sh.ep.tie_pos) atomicMin(&sh.ep.tie_slot, i);
         }
@@ -516,7 +544,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       a.pos[sc + e1] = last_pos;
     }
     // the thread that stored slot e1's utility in the score pass overwrites it
-    if (tid == e1 % NT) a.m[sc + e1] = m_lds[L - 1];
+    if (tid == e1 % NT) a.m[sc + e1] = float(m_lds[L - 1]);
   }
   if (tid == 0) a.len[scope] = L - 1;
 }

@@ -315,14 +315,6 @@ struct Chunk8<float> {
   __device__ __forceinline__ double get(int u) const { return double(ElemTraits<float>::get(u < 4 ? w0 : w1, u & 3)); }
 };
 
-// A value rounded to the cache dtype, as a float.
-template <typename T>
-__device__ __forceinline__ float round_to(float x);
-template <>
-__device__ __forceinline__ float round_to<bf16_t>(float x) { return bf16_to_f32(f32_to_bf16(x)); }
-template <>
-__device__ __forceinline__ float round_to<float>(float x) { return x; }
-
 // The keys of up to 16 rows as the B operand of v_mfma_f64_16x16x4 (the transposed use of
 // kvc_f64mfma.h restricted to its first column tile): 16 KB.
 struct FmOp16 {
@@ -738,11 +730,11 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       const double wv0 = we / (we + wc), wv1 = wc / (we + wc);
       const double wk0 = guarded ? 0.5 : we * num / den, wk1 = guarded ? 0.5 : wc * num / den;
       // the merged rows, rounded to the cache dtype
-      const float k0 = round_to<T>(float(wk0 * kg0 + wk1 * kc0)), k1 = round_to<T>(float(wk0 * kg1 + wk1 * kc1));
+      const float k0 = round_once<T>(wk0 * kg0 + wk1 * kc0), k1 = round_once<T>(wk0 * kg1 + wk1 * kc1);
       store_elem<T>(Kw, int64_t(surv) * HD + e0, k0);
       store_elem<T>(Kw, int64_t(surv) * HD + e1, k1);
-      store_elem<T>(Vw, int64_t(surv) * HD + e0, float(wv0 * vg0 + wv1 * vc0));
-      store_elem<T>(Vw, int64_t(surv) * HD + e1, float(wv0 * vg1 + wv1 * vc1));
+      store_elem<T>(Vw, int64_t(surv) * HD + e0, round_once<T>(wv0 * vg0 + wv1 * vc0));
+      store_elem<T>(Vw, int64_t(surv) * HD + e1, round_once<T>(wv0 * vg1 + wv1 * vc1));
       sh.qk[0][e0] = double(k0);
       sh.qk[0][e1] = double(k1);
       double n2 = double(k0) * double(k0) + double(k1) * double(k1);

@@ -10,7 +10,8 @@ namespace kvc {
 // radix select, evicted and mover lists, split fold and row moves run as
 // separate grid-wide kernels after the attention kernel).
 struct BulkScope {
-  uint64_t prefix, mask;   // cut: a slot is evicted iff (key & mask) <= prefix once done
+  uint64_t prefix, mask;   // cut on the 64-bit key (see the flags kernel)
+  uint32_t lprefix, lmask; // cut on the 32-bit tie key (positions) when 64-bit keys tie
   int32_t krem;            // rank of the k-th smallest key inside the current bin
   int32_t done;            // the cut is final
   int32_t L, k;            // live length before eviction, evicted count
@@ -27,6 +28,7 @@ struct BulkArgs {
   float *fpart;            // [n_scopes * units][fold_splits][HD*HD + 2*HD] fold partials (fold_splits > 1)
   const float *key;        // selection keys [n_scopes][cap] and positions (null: the slot index)
   const int32_t *pos;
+  const double *key64;     // non-null: float64 keys [n_scopes][cap] ranked as (key64, position)
   uint8_t *flags, *flags2; // [n_scopes][cap] evicted flags (selection writes both, if non-null)
   int32_t *list, *list2;   // [n_scopes][cap]: evicted slots ascending; movers ascending
   const int32_t *len;      // live lengths for the standalone paths (null: cap)
@@ -66,6 +68,8 @@ struct StepArgs {
   float *partO, *fac;
   double *subM;
   float *ews;
+  uint8_t *ewsh;     // shift counts of the stored weights (exp_shifted), beside ews
+  double *m64;       // float64 utilities of scopes that evict more than one entry [n_scopes][cap]
   uint8_t *flags;
   int32_t *list, *list2;
   int32_t n_splits, nsub_cap;
@@ -74,8 +78,8 @@ struct StepArgs {
   int32_t max_len;   // live length the launch is sized for (a longer device length is still handled)
   // split path: score chunks and each chunk's lowest (m, pos) key
   int32_t score_chunk, n_score_chunks;   // tokens per chunk; chunks per scope the arrays hold
-  uint64_t *cand_key;
-  int32_t *cand_slot;
+  uint64_t *cand_key;       // orderable float64 utility of each chunk's lowest entry
+  int32_t *cand_slot, *cand_pos;
   BulkScope *bulk;   // non-null: scopes evicting k > 1 stop after the utility update
 };
 

@@ -41,6 +41,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// double -> bf16 bits, one rounding to nearest even: the float conversion made
+// round-to-odd (truncated toward zero, last bit set when inexact) so the
+// second rounding cannot land on a tie the first one created.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  const float f = float(x);
+  uint32_t u = __float_as_uint(f);
+  const double fd = double(f);
+  if (fd != x) {
+    if (fabs(fd) > fabs(x)) u -= 1u;   // rounded away from zero: one step back (sign-magnitude)
+    u |= 1u;
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// A double rounded once to the cache dtype, as a float.
+template <typename T> __device__ __forceinline__ float round_once(double x);
+template <> __device__ __forceinline__ float round_once<bf16_t>(double x) { return bf16_to_f32(f64_to_bf16(x)); }
+template <> __device__ __forceinline__ float round_once<float>(double x) { return float(x); }
+
 template <typename T> __device__ __forceinline__ float load_elem(const T *p, int64_t i);
 template <> __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t *p, int64_t i) {
   return bf16_to_f32(p[i].b);
@@ -127,6 +147,40 @@ __device__ __forceinline__ float exp_split(double x) {
   float lo = float(x - double(hi));
   float eh = expf(hi);
   return fmaf(eh, lo, eh);
+}
+
+// Weights far below the running maximum. float32 keeps exp(x) only down to
+// x ~ -103 while float64 keeps it to x ~ -745, so a weight with x < -SHIFT_STEP
+// is stored as exp(x + SHIFT_STEP * sh) (sh = the shift count, kept in a byte
+// beside it, at most SHIFT_MAX) and stands for that value times
+// exp(-SHIFT_STEP * sh). Scores formed from such weights then rank as the
+// float64 ones do.
+constexpr double SHIFT_STEP = 80.0;
+constexpr int SHIFT_MAX = 9;
+
+__device__ __forceinline__ float exp_shifted(double x, int &sh) {
+  sh = 0;
+  if (x >= -SHIFT_STEP) return exp_split(x);
+  if (!(x > -1.0e30)) return 0.0f;
+  sh = min(SHIFT_MAX, int(-x * (1.0 / SHIFT_STEP)));
+  return exp_split(x + SHIFT_STEP * double(sh));
+}
+
+// exp(-SHIFT_STEP * sh), the factor a shifted weight stands for.
+__device__ __forceinline__ double shift_scale(int sh) { return sh == 0 ? 1.0 : exp(-SHIFT_STEP * double(sh)); }
+
+// Total order key of a float64 value: its bits mapped to an order-preserving
+// unsigned integer (-0 folded onto +0). Utilities are ranked on this key of
+// their float64 value, then by position.
+__device__ __forceinline__ uint64_t orderable_f64(double d) {
+  uint64_t b = uint64_t(__double_as_longlong(d));
+  if (b == 0x8000000000000000ull) b = 0ull;
+  return (b & 0x8000000000000000ull) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// (key, position) strictly before (key2, position2).
+__device__ __forceinline__ bool key_pos_less(uint64_t k1, uint32_t p1, uint64_t k2, uint32_t p2) {
+  return k1 < k2 || (k1 == k2 && p1 < p2);
 }
 
 // Total order key of (value, position): float bits mapped to an order-preserving

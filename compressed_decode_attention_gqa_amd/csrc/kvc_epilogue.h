@@ -31,7 +31,7 @@ struct ScoreLds {
   double pm[SCORE_PAIR_MAX];   // split maxima; then the splits' output weights exp(pm - M) / Z
   double pz[SCORE_PAIR_MAX];
   uint64_t wkey[WG / 64];
-  int wslot[WG / 64];
+  int wslot[WG / 64], wpos[WG / 64];
 };
 
 struct EpiLds {
@@ -40,8 +40,23 @@ struct EpiLds {
     FoldLds fold;
   };
   uint64_t ckey[WG / 64];
-  int cslot[WG / 64];
+  int cslot[WG / 64], cpos[WG / 64];
 };
+
+// Wave argmin of (key, position) carrying the slot.
+__device__ __forceinline__ void wave_min_key_pos(uint64_t &key, uint32_t &pos, int &slot) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t k2 = shfl_xor_u64(key, o);
+    const uint32_t p2 = __shfl_xor(pos, o);
+    const int s2 = __shfl_xor(slot, o);
+    if (key_pos_less(k2, p2, key, pos)) {
+      key = k2;
+      pos = p2;
+      slot = s2;
+    }
+  }
+}
 
 // M and Z of attention head (gu, g) over the split partials.
 template <int G>
@@ -59,10 +74,12 @@ __device__ __forceinline__ void combine_head(const StepArgs &a, int gu, int g, d
 // ---------------------------------------------------------------- score
 // InertiaKV §3.1 eq. (1): s(i) = mean over the scope's Ua*G attention heads of
 // a_{h,i} = p_i e_{h,i} F_{h,c(i)}, where e = exp(l - M_sub) is the weight the
-// attention kernel stored and F = exp(M_sub - M) / Z the factor of its
-// CH-token sub-chunk; then eqs. (2)-(4) for m(i). For a step that evicts one
-// entry, each chunk also reports its lowest (m, pos) key. Workgroups stride
-// over the scope's chunks, so any live length is covered.
+// attention kernel stored (times exp(-SHIFT_STEP * sh) for a shifted one) and
+// F = exp(M_sub - M) / Z the factor of its CH-token sub-chunk; then eqs.
+// (2)-(4) for m(i), in float64, stored as float32. For a step that evicts one
+// entry, each chunk also reports its lowest (float64 m, pos); a scope that
+// evicts more than one keeps the float64 utilities (m64) for the selection.
+// Workgroups stride over the scope's chunks, so any live length is covered.
 template <int G, int CH>
 __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,6 +95,8 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
   const double inv_heads = 1.0 / double(H);
   const double alpha = double(a.alpha);
   const float *ews = a.ews + int64_t(gu0) * G * cap;
+  const uint8_t *ewsh = a.ewsh + int64_t(gu0) * G * cap;
+  double *m64 = (step && k > 1 && a.m64) ? a.m64 + sc : nullptr;
   const int chunk = a.score_chunk;
 
   // per attention head M and Z over the split partials (staged in LDS when they fit)
@@ -151,62 +170,66 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
     }
     __syncthreads();
     uint64_t best = ~0ull;
+    uint32_t bpos = 0xffffffffu;
     int bslot = 0x7fffffff;
     for (int i = i0 + tid; i < i1; i += WG) {
       const bool isnew = a.append && i == L - 1;
-      float mval = 0.f;
+      double mval = 0.0;
       if (score) {
         const int pv = isnew ? 1 : (a.votes ? a.votes[sc + i] : 1);
         const double *f = sh.fac + (i / CH - c0) * H;
         double acc = 0.0;
         for (int ua = 0; ua < Ua; ++ua) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) acc += double(ews[(int64_t(ua) * G + g) * cap + i]) * f[ua * G + g];
+          for (int g = 0; g < G; ++g) {
+            const int64_t wi = (int64_t(ua) * G + g) * cap + i;
+            const int shv = ewsh[wi];
+            const double x = double(ews[wi]) * f[ua * G + g];
+            acc += shv ? x * shift_scale(shv) : x;
+          }
         }
         const double sv = double(pv) * acc * inv_heads;
         if (a.s) a.s[sc + i] = float(sv);
         if (step) {
           const double mo = isnew ? 0.0 : double(a.m[sc + i]);
-          mval = float(apply_rule(a.rule, alpha, mo, sv));
-          a.m[sc + i] = mval;
+          mval = apply_rule(a.rule, alpha, mo, sv);
+          a.m[sc + i] = float(mval);
         }
       } else if (step) {
-        mval = isnew ? 0.f : a.m[sc + i];
+        mval = isnew ? 0.0 : double(a.m[sc + i]);
       }
       if (isnew && !(score && step)) a.m[sc + i] = 0.f;
+      if (m64) m64[i] = mval;
       if (k == 1) {
-        const uint64_t key = order_key(mval, uint32_t(isnew ? a.t : a.pos[sc + i]));
-        if (key < best) {
+        const uint64_t key = orderable_f64(mval);
+        const uint32_t p = uint32_t(isnew ? a.t : a.pos[sc + i]);
+        if (key_pos_less(key, p, best, bpos)) {
           best = key;
+          bpos = p;
           bslot = i;
         }
       }
     }
-    if (k == 1) {   // keys are distinct (distinct positions): the minimum names one slot
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint64_t b2 = shfl_xor_u64(best, o);
-        const int s2 = __shfl_xor(bslot, o);
-        if (b2 < best) {
-          best = b2;
-          bslot = s2;
-        }
-      }
+    if (k == 1) {   // (utility, position) pairs are distinct: the minimum names one slot
+      wave_min_key_pos(best, bpos, bslot);
       if (lane == 0) {
         sh.wkey[wave] = best;
         sh.wslot[wave] = bslot;
+        sh.wpos[wave] = int(bpos);
       }
       __syncthreads();
       if (tid == 0) {
 #pragma unroll
         for (int w = 1; w < WG / 64; ++w) {
-          if (sh.wkey[w] < best) {
+          if (key_pos_less(sh.wkey[w], uint32_t(sh.wpos[w]), best, bpos)) {
             best = sh.wkey[w];
+            bpos = uint32_t(sh.wpos[w]);
             bslot = sh.wslot[w];
           }
         }
         const int64_t ci = int64_t(scope) * a.n_score_chunks + i0 / chunk;
         a.cand_key[ci] = best;
+        a.cand_pos[ci] = int(bpos);
         a.cand_slot[ci] = bslot;
       }
     }
@@ -253,6 +276,8 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
         BulkScope &b = a.bulk[scope];
         b.prefix = 0;
         b.mask = 0;
+        b.lprefix = 0;
+        b.lmask = 0;
         b.krem = k;
         b.done = 0;
         b.L = L;
@@ -296,34 +321,33 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
     // the lowest of the score chunks' keys
     const int nch = (L + a.score_chunk - 1) / a.score_chunk;
     uint64_t best = ~0ull;
+    uint32_t bpos = 0xffffffffu;
     int bslot = 0x7fffffff;
     for (int c = tid; c < nch; c += WG) {
-      const uint64_t key = a.cand_key[int64_t(scope) * a.n_score_chunks + c];
-      if (key < best) {
+      const int64_t ci = int64_t(scope) * a.n_score_chunks + c;
+      const uint64_t key = a.cand_key[ci];
+      const uint32_t p = uint32_t(a.cand_pos[ci]);
+      if (key_pos_less(key, p, best, bpos)) {
         best = key;
-        bslot = a.cand_slot[int64_t(scope) * a.n_score_chunks + c];
+        bpos = p;
+        bslot = a.cand_slot[ci];
       }
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t b2 = shfl_xor_u64(best, o);
-      const int s2 = __shfl_xor(bslot, o);
-      if (b2 < best) {
-        best = b2;
-        bslot = s2;
-      }
-    }
+    wave_min_key_pos(best, bpos, bslot);
     if (lane == 0) {
       sh.ckey[wave] = best;
       sh.cslot[wave] = bslot;
+      sh.cpos[wave] = int(bpos);
     }
     __syncthreads();
     best = sh.ckey[0];
+    bpos = uint32_t(sh.cpos[0]);
     e1 = sh.cslot[0];
 #pragma unroll
     for (int w = 1; w < WG / 64; ++w) {
-      if (sh.ckey[w] < best) {
+      if (key_pos_less(sh.ckey[w], uint32_t(sh.cpos[w]), best, bpos)) {
         best = sh.ckey[w];
+        bpos = uint32_t(sh.cpos[w]);
         e1 = sh.cslot[w];
       }
     }
@@ -332,12 +356,12 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
     if (tid == 0) list[0] = e1;
   } else {
     // more than one eviction without the bulk kernels (a launch sized for at most
-    // one, on a longer device length): one workgroup selects, folds and compacts
-    const float *mm = a.m + sc;
+    // one, on a longer device length): one workgroup selects, folds and compacts,
+    // ranking the float64 utilities the score kernel kept
+    const double *mm = a.m64 + sc;
     const int32_t *pp = a.pos + sc;
-    auto key = [&](int i) -> uint64_t { return order_key(mm[i], uint32_t(pp[i])); };
-    const SelectCut cut = wg_select_cut(key, L, k, sh.sel);
-    wg_apply_cut(key, L, cut, flags, a.evict_out ? a.evict_out + sc : nullptr, list, sh.sel);
+    wg_select_f64_pos([&](int i) { return mm[i]; }, [&](int i) { return pp[i]; }, L, k, flags,
+                      a.evict_out ? a.evict_out + sc : nullptr, list, sh.sel);
   }
   __threadfence_block();
   __syncthreads();

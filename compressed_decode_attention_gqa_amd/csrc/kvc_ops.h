@@ -91,6 +91,29 @@ __device__ int wg_apply_cut(KeyFn key, int n, const SelectCut &cut, uint8_t *fla
   return out_seen;
 }
 
+// The k lowest (value, position) of n entries with float64 values (1 <= k <= n):
+// a radix cut on the order key of the values; if the cut's bin holds equal
+// values beyond the ones it must give up, a second cut on those entries'
+// positions decides. Writes flags (and flags2) and the evicted slots
+// ascending to list; returns the evicted count.
+template <class ValFn, class PosFn>
+__device__ int wg_select_f64_pos(ValFn val, PosFn pos, int n, int k, uint8_t *flags, uint8_t *flags2,
+                                 int32_t *list, SelectLds &sh) {
+  auto key = [&](int i) -> uint64_t { return orderable_f64(val(i)); };
+  const SelectCut cut = wg_select_cut(key, n, k, sh);
+  if (cut.take_eq == cut.n_eq) return wg_apply_cut(key, n, cut, flags, flags2, list, sh);
+  auto tied = [&](int i) -> uint64_t {
+    return (key(i) & cut.mask) == cut.thr ? uint64_t(uint32_t(pos(i))) : ~0ull;
+  };
+  const SelectCut cut2 = wg_select_cut(tied, n, cut.take_eq, sh);   // distinct positions
+  auto evicted = [&](int i) -> uint64_t {
+    const uint64_t km = key(i) & cut.mask;
+    if (km < cut.thr) return 0ull;
+    return (km == cut.thr && (tied(i) & cut2.mask) <= cut2.thr) ? 0ull : 1ull;
+  };
+  return wg_apply_cut(evicted, n, SelectCut{1ull, ~0ull, 0, 0}, flags, flags2, list, sh);
+}
+
 // argmin of key over [0, n): returns the slot (lowest slot among equal keys).
 __device__ __forceinline__ int wg_argmin_finish(uint64_t best, int slot, SelectLds &sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -421,8 +421,8 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   if (tid < HD) {
     T *Kw = reinterpret_cast<T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
     T *Vw = reinterpret_cast<T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
-    store_elem<T>(Kw, int64_t(dst) * HD + tid, float(sh.wgt[2] * kek + sh.wgt[3] * kck));
-    store_elem<T>(Vw, int64_t(dst) * HD + tid, float(sh.wgt[0] * vek + sh.wgt[1] * vck));
+    store_elem<T>(Kw, int64_t(dst) * HD + tid, round_once<T>(sh.wgt[2] * kek + sh.wgt[3] * kck));
+    store_elem<T>(Vw, int64_t(dst) * HD + tid, round_once<T>(sh.wgt[0] * vek + sh.wgt[1] * vck));
   }
   if (mover) st16(const_cast<char *>(mrow) + int64_t(e - last) * RB, mvec);
   if (tid == 0) {

@@ -332,6 +332,11 @@ int32_t kvc_compact(const kvc_cache *cache, const uint8_t *evict, const kvc_merg
  * kvc_moment_update and kvc_compact applied in turn. refresh = 0 skips the
  * score and utility update for this step (lazy refresh: eviction still holds
  * the budget with the stale utility; the appended entry has utility 0).
+ * Ranking: the step computes scores and utilities in float64 and selects on
+ * (float64 utility, position) ascending before the utilities are stored as
+ * fp32, so entries whose utilities lie below float32's range (stored as 0)
+ * are still ranked by their float64 values; the selection of kvc_select_evict
+ * ranks the fp32 keys it is given.
  * mom NULL skips the fold. evict_out: [n_scopes][capacity] u8 or NULL; when
  * given it receives the flags of the evicted slots as they were before
  * compaction. s may be NULL. Merge mode is kvc_compact's (merge non-NULL; it

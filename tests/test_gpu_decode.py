@@ -225,16 +225,11 @@ def test_select_evict_device_wide_top_k():
 C4 = synth.WORKLOADS["c4_keepkv_votes_64k"]
 
 
-@pytest.mark.parametrize("dtype,G", [
-    ("bf16", 4),
-    # f32 keys at this shape drive some utilities to ~1e-59: below float32's range, so the
-    # stored utilities flush to zero and tie (broken by position), while the float64 oracle
-    # still orders them; the evict sets then differ before any merge is checked
-    pytest.param("f32", 2, marks=pytest.mark.skip(reason="utilities below float32 range tie at zero; "
-                                                         "the float64 oracle orders them")),
-])
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f32", 2)])
 def test_decode_step_c4_merge_reduced(dtype, G):
-    """Vote-weighted decode with a ZIP merge every step (KeepKV eqs. (7)-(12)), every scope checked."""
+    """Vote-weighted decode with a ZIP merge every step (KeepKV eqs. (7)-(12)), every scope checked.
+    The f32 case drives some single-step utilities to ~1e-59, below float32's range: they are
+    stored as float32 but ranked on their float64 values, as the oracle ranks them."""
     _say("c4 reduced", dtype, G)
     wl = C4.scaled(batch=1, n_kv=5, context=3000, budget=300, steps=10, dtype=dtype, G=G)
     run = DeviceRun(wl)
@@ -244,12 +239,14 @@ def test_decode_step_c4_merge_reduced(dtype, G):
 
 
 def test_decode_step_c4_full_size_sampled():
-    """64 scopes of 6553 voted entries (10% of 64K), merge every step; sampled scopes."""
+    """64 scopes of 6553 voted entries (10% of 64K), a merge every step for the workload's 64
+    steps; 12 sampled scopes checked at the first step and every 8th."""
     rng = np.random.default_rng(9)
     run = DeviceRun(C4)
-    rep = lockstep(run, 8, lambda t: sorted(rng.choice(C4.n_scopes, 12, replace=False).tolist())
-                   if t in (1, 2, 5, 8) else [], merge=True)
+    rep = lockstep(run, C4.steps, lambda t: sorted(rng.choice(C4.n_scopes, 12, replace=False).tolist())
+                   if t == 1 or t % 8 == 0 else [], merge=True)
     _say("c4 full", rep)
+    assert rep.get("merged_rows_exact", 0) > 0
 
 
 def test_merge_keeps_the_reference_output():
@@ -498,3 +495,77 @@ def test_compact_merge_standalone_matches_oracle(dtype):
             assert np.array_equal(post["k"][s, 0, i], pre["k"][s, 0, j])
             assert np.array_equal(post["v"][s, 0, i], pre["v"][s, 0, j])
             assert post["votes"][s, i] == pre["votes"][s, j] and post["m"][s, i] == pre["m"][s, j]
+
+
+@pytest.mark.parametrize("path", ["per_head", "split"])
+def test_weights_below_float32_range_rank_as_float64(path):
+    """A key of large norm along the step's group-mean query, planted at slot 0 (so the streaming
+    meets it first), puts every other logit some 280 below the maximum: their weights and
+    single-step utilities (~1e-120) lie below float32's range. They are stored as float32 zeros
+    but ranked on their float64 values (InertiaKV §3.1: lowest utility first), so each step evicts
+    what the float64 oracle evicts. per_head: 136 scopes at one eviction each (one workgroup per
+    head); split: 8 scopes (split-K attention and the score/finish kernels)."""
+    _say("underflow ranking", path)
+    wl = C2.scaled(n_layers=17 if path == "per_head" else 1, n_kv=8, context=400, budget=400, steps=4,
+                   rule="single", key_scales=True)
+    run = DeviceRun(wl, max_len=wl.budget + 1, moments=False)
+    rep = {}
+    for step in range(1, wl.steps + 1):
+        q, kn, vn = run.inputs(step)
+        qbar = q.float().mean(dim=2)                                    # [S, U, d]
+        run.cache.k[:, 0, 0] = (100.0 * qbar[:, 0]).to(run.cache.k.dtype)
+        scopes = list(range(0, wl.n_scopes, 3 if path == "per_head" else 1))
+        pre = run.snapshot(scopes)
+        t = run.t
+        run.step(step, q, kn, vn)
+        torch.cuda.synchronize()
+        check_step(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, report=rep)
+        # the weights really left float32's range: most stored utilities are zero
+        m = run.cache.m[scopes].cpu().numpy()[:, :wl.budget]
+        assert (m == 0).mean() > 0.5
+    assert kvc.kvc_workspace_status(run.ws) == 0
+    _say("underflow ranking", path, rep)
+
+
+def test_per_head_kernel_exact_ties_go_by_position():
+    """The per-head kernel (136 scopes, one eviction each) on a step that does not refresh scores
+    (lazy refresh: the stale utilities rank, the appended entry has 0): several utilities preset
+    exactly equal and lowest -- a negative value, +0 and -0 beside the appended entry's 0, a
+    negative value below float32's normal range -- so the eviction is the lowest position among
+    the tied entries (oracle bottom_k). Checked exactly: the near-tie band would accept any of them."""
+    _say("per-head exact ties")
+    wl = C2.scaled(n_layers=17, n_kv=8, context=300, budget=300, steps=2, key_scales=True)
+    run = DeviceRun(wl, max_len=wl.budget + 1)
+    assert wl.n_scopes >= 128
+    run.step(1, *run.inputs(1))        # one steady step first: slots no longer in position order
+    rng = np.random.default_rng(31)
+    m = run.cache.m.cpu().numpy().copy()
+    L = int(run.cache.length[0])
+    for sc in range(wl.n_scopes):
+        J = rng.choice(L, size=int(rng.integers(2, 7)), replace=False)
+        kind = sc % 4
+        if kind == 0:
+            m[sc, J] = -0.25
+        elif kind == 1:
+            m[sc, J] = np.where(np.arange(len(J)) % 2 == 0, 0.0, -0.0)   # tie the appended entry's 0
+        elif kind == 2:
+            m[sc, J] = -1e-40                                           # float32 subnormal
+        else:
+            m[sc, J[:1]] = -1.0                                         # a single lowest entry
+    run.cache.m.copy_(torch.from_numpy(m))
+    pos = run.cache.pos.cpu().numpy()
+    q, kn, vn = run.inputs(2)
+    scopes = list(range(wl.n_scopes))
+    pre = run.snapshot(scopes)
+    t = run.t
+    run.step(2, q, kn, vn, refresh=False)
+    torch.cuda.synchronize()
+    ev = bits(run.evict)
+    for sc in scopes:
+        mm = np.append(m[sc, :L].astype(np.float64), 0.0)
+        pp = np.append(pos[sc, :L].astype(np.int64), t)
+        E = oracle.bottom_k(mm, pp, 1)
+        got = np.flatnonzero(ev[sc, :L + 1])
+        assert got.tolist() == E.tolist(), (sc, got, E, mm[E], pp[E])
+    check_step(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, refresh=False)
+    assert kvc.kvc_workspace_status(run.ws) == 0
