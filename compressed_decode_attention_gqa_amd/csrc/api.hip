@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "kvc.h"
 #include "kvc_decode.h"
@@ -169,7 +170,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
                int32_t G, float scale, int mode, int rule, float alpha, int budget, int refresh,
                float *out, float *lse, float *s, const kvc_moments *mom, const kvc_merge *merge,
                uint8_t *evict_out, int attn_unit0, int attn_units, int32_t max_len, void *ws,
-               size_t ws_bytes, void *stream) {
+               size_t ws_bytes, void *stream, int32_t *status_out = nullptr) {
   int st = validate_cache(c);
   if (st) return st;
   if (!valid_G(G)) return KVC_ERR_UNSUPPORTED;
@@ -235,7 +236,7 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
     a.mom_S = mom->S;
   }
   a.evict_out = evict_out;
-  a.status = at<int32_t>(ws, d.status);
+  a.status = status_out ? status_out : at<int32_t>(ws, d.status);
   a.partM = at<double>(ws, d.partM);
   a.partZ = at<double>(ws, d.partZ);
   a.partO = at<float>(ws, d.partO);
@@ -375,6 +376,31 @@ PrefillLayout prefill_layout(int n_scopes, int cap) {
   return l;
 }
 
+// ------------------------------------------------------- allocation-free decode step
+// The workspace of kvc_decode_step_noalloc: one array per GPU, part of the loaded
+// code object (each device holds its own copy for the life of the process). Host
+// code never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+void *scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch array (looked up on the device's first call).
+int current_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVC_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KVC_ERR_DEVICE;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return KVC_OK;
+}
+
 // kvc_select_evict with an optional protection bound (defined below the C entry points).
 int32_t select_evict(const float *key, const int32_t *pos, const int32_t *len, int32_t n_scopes, int32_t capacity,
                      int32_t budget, bool protect, int32_t protect_from, uint8_t *evict, int32_t *n_evict, void *ws,
@@ -449,6 +475,23 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
                         size_t ws_bytes, void *stream) {
   return run_decode(cache, k_new, v_new, t, q, G, scale, 1, rule, alpha, budget, refresh, out, lse, s,
                     mom, merge, evict_out, attn_unit0, attn_units, max_len, ws, ws_bytes, stream);
+}
+
+int32_t kvc_decode_step_noalloc(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,
+                                const void *q, int32_t G, float scale, int32_t rule, float alpha, int32_t budget,
+                                int32_t refresh, float *out, float *lse, float *s, const kvc_moments *mom,
+                                const kvc_merge *merge, uint8_t *evict_out, int32_t attn_unit0,
+                                int32_t attn_units, int32_t max_len, int32_t *status, void *stream) {
+  const int st = validate_cache(cache);
+  if (st) return st;
+  if (!valid_G(G)) return KVC_ERR_UNSUPPORTED;
+  const int au = attn_units > 0 ? attn_units : cache->units_per_scope;
+  if (decode_layout(cache, G, au).total > kScratchBytes) return KVC_ERR_WORKSPACE;
+  void *ws = nullptr;
+  const int sst = current_scratch(&ws);
+  if (sst) return sst;
+  return run_decode(cache, k_new, v_new, t, q, G, scale, 1, rule, alpha, budget, refresh, out, lse, s, mom, merge,
+                    evict_out, attn_unit0, attn_units, max_len, ws, kScratchBytes, stream, status);
 }
 
 int32_t kvc_ema_update(float *m, const float *s, const int32_t *len, int32_t n_scopes, int32_t capacity,

@@ -24,7 +24,7 @@ EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_ema_predict", "kvc_s
             "kvc_keep_jaccard", "kvc_compact",
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
             "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
-            "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step",
+            "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step", "kvc_decode_step_noalloc",
             "kvc_decode_workspace_size",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
             "kvc_keepkv_prefill_workspace_size", "kvc_keepkv_ema_init_workspace_size",
@@ -61,6 +61,8 @@ _SIGS = {
     "kvc_decode_attn_score": (_I, [_P, _P, _P, _I, _P, _I, _F, _P, _P, _P, _I, _P, _SZ, _P]),
     "kvc_decode_step": (_I, [_P, _P, _P, _I, _P, _I, _F, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P,
                              _I, _I, _I, _P, _SZ, _P]),
+    "kvc_decode_step_noalloc": (_I, [_P, _P, _P, _I, _P, _I, _F, _I, _F, _I, _I, _P, _P, _P, _P, _P, _P,
+                                     _I, _I, _I, _P, _P]),
     "kvc_ema_update": (_I, [_P, _P, _P, _I, _I, _I, _F, _P]),
     "kvc_ema_predict": (_I, [_P, _P, _I, _I, _F, _I, _P, _P]),
     "kvc_select_evict": (_I, [_P, _P, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
@@ -251,6 +253,20 @@ def kvc_decode_step(cache: Cache, k_new, v_new, t: int, q, G: int, scale: float,
         _ptr(out), _ptr(lse), _ptr(s), ctypes.byref(mom) if mom is not None else None,
         ctypes.byref(merge) if merge is not None else None, _ptr(evict_out), attn_unit0, attn_units, max_len,
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kvc_decode_step_noalloc(cache: Cache, k_new, v_new, t: int, q, G: int, scale: float, rule, alpha: float,
+                            budget: int, out, lse, s=None, moments: Moments | None = None,
+                            merge: _Merge | None = None, evict_out=None, refresh: bool = True, attn_unit0: int = 0,
+                            attn_units: int = 0, max_len: int = 0, status=None, stream=None):
+    d = cache.desc()
+    mom = moments.desc() if moments is not None else None
+    rule = RULES.get(rule, rule)
+    _check("kvc_decode_step_noalloc", lib().kvc_decode_step_noalloc(
+        ctypes.byref(d), _ptr(k_new), _ptr(v_new), t, _ptr(q), G, scale, rule, alpha, budget, int(refresh),
+        _ptr(out), _ptr(lse), _ptr(s), ctypes.byref(mom) if mom is not None else None,
+        ctypes.byref(merge) if merge is not None else None, _ptr(evict_out), attn_unit0, attn_units, max_len,
+        _ptr(status), _stream(stream)))
 
 
 def kvc_ema_update(m, s, length, n_scopes: int, capacity: int, rule, alpha: float, stream=None):

@@ -368,6 +368,29 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
                         int32_t attn_unit0, int32_t attn_units, int32_t max_len,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* kvc_decode_step_noalloc -- kvc_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments and results, with the workspace
+ * replaced by a scratch array of KVC_NOALLOC_SCRATCH_BYTES (128 MiB) that the
+ * library's code object holds on each GPU it runs on, for the life of the
+ * process. The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks up that device's array.
+ * A cache whose decode workspace (kvc_decode_workspace_size) exceeds the scratch
+ * size is rejected with KVC_ERR_WORKSPACE before anything is enqueued. status:
+ * a caller-owned device int32 that receives the device-detected condition a
+ * workspace status word would (KVC_ERR_CAPACITY when a live length exceeds the
+ * capacity; the caller zeroes and reads it), or NULL (the condition is then not
+ * reported). Every call on one GPU shares that GPU's scratch: calls that can
+ * overlap on one GPU (different streams, or different host threads) race and
+ * must be serialised by the caller. */
+#define KVC_NOALLOC_SCRATCH_BYTES (128u << 20)
+int32_t kvc_decode_step_noalloc(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,
+                                const void *q, int32_t G, float scale, int32_t rule, float alpha,
+                                int32_t budget, int32_t refresh, float *out, float *lse, float *s,
+                                const kvc_moments *mom, const kvc_merge *merge, uint8_t *evict_out,
+                                int32_t attn_unit0, int32_t attn_units, int32_t max_len, int32_t *status,
+                                void *stream);
+
 /* kvc_laprox_score -- LaProx prefill score (key design 1), per-layer
  * normalisation (key design 2) and GQA group mean (training-strategy paragraph).
  * For layer l, KV head h, token i < N:

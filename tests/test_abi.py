@@ -254,3 +254,21 @@ def test_step_bytes_model():
     assert b.kv == 3277 * 512
     assert b.moments == 2 * 128 * 128 * 4 + 2 * 2 * 128 * 4 + 8
     assert 1_850_000 < b.total < 1_860_000          # ~566 bytes per cached token
+
+
+@needs_lib
+def test_noalloc_step_rejects_a_cache_beyond_its_scratch():
+    """kvc_decode_step_noalloc runs in a 128 MiB per-GPU scratch array: a cache whose decode
+    workspace is larger is refused on the host (KVC_ERR_WORKSPACE) before any device call, and
+    the usual argument checks come first."""
+    L = kvc.lib()
+
+    def call(c, G=4, q=0x6000):
+        return L.kvc_decode_step_noalloc(ctypes.byref(c), None, None, 0, q, G, 0.1, 2, 0.9, 10, 1, 0x7000, 0x8000,
+                                         None, None, None, None, 0, 0, 0, None, None)
+    big = _fake_cache(capacity=1 << 20, n_scopes=256, scope_stride=1 << 20)
+    assert L.kvc_decode_workspace_size(ctypes.byref(big), 4, 0) > (128 << 20)
+    assert call(big) == -6
+    assert call(_fake_cache(head_dim=64)) == -3
+    assert call(_fake_cache(), G=3) == -3
+    assert call(_fake_cache(k=0x1008)) == -5
