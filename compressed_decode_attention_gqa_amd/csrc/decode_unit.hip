@@ -4,19 +4,25 @@
 // fixed budget).
 //
 // Streaming: eight waves (two per SIMD, so one wave's arithmetic overlaps the
-// other's memory waits; four for eight-head groups) each take every NW-th
-// sub-chunk of CHW tokens and keep PF sub-chunks of 16-byte K/V loads in
-// flight. Full sub-chunks are
-// addressed as one uniform base plus the lane's 16-byte offset; only the last
-// sub-chunk clamps per lane and substitutes the appended row. Logits are
-// float64 (exact bf16/fp32 products); each lane keeps its query heads in the
-// lane-permuted order of preduce, so the transposed reduction leaves one
-// head's logit per lane without selects; the per-head running maximum is
-// rescaled only when it moves; each lane forms one weight exp(l - M) (float64
-// argument split into float hi + lo), and the maximum of every sub-chunk is
-// kept so the epilogue can turn weights into normalised per-token weights.
-// Per-token weights (with their shift counts, for weights below float32's
-// range), utilities (float64) and votes of the scope live in LDS.
+// other's memory waits; four for eight-head groups) keep PF sub-chunks of CHW
+// tokens of 16-byte K/V loads in flight each. Sub-chunks are handed out in
+// order by an LDS counter (a wave takes the next one when a load slot frees),
+// so every wave streams until the scope's last sub-chunk and the reads of a
+// workgroup stay close together; a step at an odd position walks the cache
+// from its end, so it first reads the rows the previous step read last, which
+// the memory-side cache still holds. Full sub-chunks are addressed as one
+// uniform base plus the lane's 16-byte offset; only the last sub-chunk clamps
+// per lane and substitutes the appended row. Logits are float64 (exact
+// bf16/fp32 products); each lane keeps its query heads in the lane-permuted
+// order of preduce, so the transposed reduction leaves one head's logit per
+// lane without selects. Each lane forms one weight exp(l - m_c) relative to
+// its sub-chunk's own maximum m_c (float64 argument split into float hi +
+// lo), and the sub-chunk's maximum and weight sum are kept per head: the
+// normaliser and the per-token weights then do not depend on which wave took
+// which sub-chunk (the epilogue sums the sub-chunks in a fixed order). The
+// value sums run against each wave's running maximum, rescaled only when it
+// moves. Per-token weights (with their shift counts, for weights below
+// float32's range), utilities (float64) and votes of the scope live in LDS.
 //
 // Epilogue (same workgroup): combine the waves' partials (one lane per
 // (wave, head)), write o and lse, score every token, update the utility, take
@@ -40,12 +46,12 @@ int decode_unit_chunk_tokens(int dtype) {
   return dtype == 0 ? UnitGeometry<bf16_t>::CHW : UnitGeometry<float>::CHW;
 }
 
-// Dynamic LDS: per-token weights e[G][ld], sub-chunk maxima [nsub][G] (double),
-// utilities m[ld] (double), votes[ld] and the weights' shift counts sh[ld][G]
-// (bytes); ld = lds_len rounded up to whole sub-chunks.
+// Dynamic LDS: per-token weights e[G][ld], sub-chunk maxima and weight sums
+// [nsub][G] (double each), utilities m[ld] (double), votes[ld] and the weights'
+// shift counts sh[ld][G] (bytes); ld = lds_len rounded up to whole sub-chunks.
 struct UnitLdsLayout {
   int ld;
-  size_t e, f, m, v, sh, total;
+  size_t e, f, z, m, v, sh, total;
 };
 
 __host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds_len, bool votes) {
@@ -56,6 +62,8 @@ __host__ __device__ inline UnitLdsLayout unit_lds_layout(int chw, int G, int lds
   o += size_t(G) * l.ld * 4;
   o = (o + 15) & ~size_t(15);
   l.f = o;
+  o += size_t(l.ld / chw) * G * 8;
+  l.z = o;
   o += size_t(l.ld / chw) * G * 8;
   l.m = o;
   o += size_t(l.ld) * 8;
@@ -83,7 +91,7 @@ struct UnitLds {
   union {
     float w[Geo::NW][Geo::UNR][Geo::TPI][G];      // streaming: weights for the value sums
     struct {
-      double pM[Geo::NW][G], pZ[Geo::NW][G];
+      double pM[Geo::NW][G], zw[Geo::NW][G];
       float pO[Geo::NW][G][HD];
       double M[G], iZ[G];
       float fac[Geo::NW][G];
@@ -93,6 +101,7 @@ struct UnitLds {
       float rowk[HD], rowv[HD];
     } ep;
   };
+  int next_sub;   // the next sub-chunk to hand out
 };
 
 template <typename T>
@@ -128,6 +137,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   const int ld = lay.ld;
   float *e_lds = reinterpret_cast<float *>(dyn + lay.e);
   double *f_lds = reinterpret_cast<double *>(dyn + lay.f);
+  double *z_lds = reinterpret_cast<double *>(dyn + lay.z);
   double *m_lds = reinterpret_cast<double *>(dyn + lay.m);
   int *v_lds = reinterpret_cast<int *>(dyn + lay.v);
   uint8_t *s_lds = reinterpret_cast<uint8_t *>(dyn + lay.sh);
@@ -180,21 +190,28 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int j = 0; j < EPV; ++j) oacc[g][j] = 0.f;
-  double Mrun = -INFINITY, Zrun = 0.0;
+  double Mrun = -INFINITY;
 
   const int nsub = L > 0 ? (L + CHW - 1) / CHW : 0;
+  const bool rev = (a.t & 1) != 0;   // walk order of this step
+  if (tid == 0) sh.next_sub = NW * PF;
+  __syncthreads();
   u32x4 kr[PF][UNR], vr[PF][UNR];
   float mv[PF];
   int vv[PF];
-  if (nsub > 0) {
+  int cs[PF];   // the sub-chunk (in walk order) of each load slot
 #pragma unroll
-    for (int s = 0; s < PF; ++s) W.issue(kr[s], vr[s], mv[s], vv[s], wave + NW * s);
+  for (int s = 0; s < PF; ++s) {
+    cs[s] = wave + NW * s;
+    if (cs[s] < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], rev ? nsub - 1 - cs[s] : cs[s]);
   }
-  for (int base = wave; base < nsub; base += NW * PF) {
+  for (;;) {
+    bool more = false;
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
-      const int c = base + NW * s;
-      if (c < nsub) {
+      if (cs[s] < nsub) {
+        more = true;
+        const int c = rev ? nsub - 1 - cs[s] : cs[s];
         const bool tail = (c + 1) * CHW > L;
         // scope arrays of this sub-chunk into LDS
         if (lane < CHW) {
@@ -224,7 +241,6 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
         if (__ballot(mx > Mrun)) {
           const double Mnew = fmax(Mrun, mx);
           const double f = Mrun > -INFINITY ? exp(Mrun - Mnew) : 0.0;
-          Zrun *= f;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             const float fg = float(readlane_f64(f, perm_rep_lane<LPT, G>(g)));
@@ -233,7 +249,10 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
           }
           Mrun = Mnew;
         }
-        if (tg == 0 && dup == 0) f_lds[c * G + myh] = Mrun;
+        // weights relative to the sub-chunk's maximum; the value sums take them
+        // times exp(m_c - Mrun) <= 1
+        const float rc = exp_split(mx - Mrun);
+        double zc = 0.0;
         __builtin_amdgcn_wave_barrier();
         // one weight per (token, head): lane `dup` takes iterations dup, dup + D, ...
 #pragma unroll
@@ -245,18 +264,27 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
             for (int i2 = 1; i2 < UNR; ++i2) x = it == i2 ? lg[i2] : x;
             const int tok = c * CHW + it * TPI + tg;
             int shc;
-            const float e = exp_shifted(x - Mrun, shc);
+            const float e = exp_shifted(x - mx, shc);
             float p = 1.f;
             if (VOTES) p = (a.append && tok == L - 1) ? 1.f : float(v_lds[min(tok, L - 1)]);
             // a shifted weight is below exp(-SHIFT_STEP) of the maximum: nothing in o or Z
-            const float w = shc ? 0.f : p * e;
-            Zrun += double(w);
-            sh.w[wave][it][tg][myh] = w;
+            const float pe = shc ? 0.f : p * e;
+            zc += double(pe);
+            sh.w[wave][it][tg][myh] = pe * rc;
             if (tok < L) {
               e_lds[myh * ld + tok] = e;
               s_lds[tok * G + myh] = uint8_t(shc);
             }
           }
+        }
+        // the sub-chunk's weight sum per head: over the lanes holding that head
+#pragma unroll
+        for (int o = 1; o < D; o <<= 1) zc += __shfl_xor(zc, o);
+#pragma unroll
+        for (int o = LPT; o < 64; o <<= 1) zc += __shfl_xor(zc, o);
+        if (tg == 0 && dup == 0) {
+          f_lds[c * G + myh] = mx;
+          z_lds[c * G + myh] = zc;
         }
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -272,17 +300,17 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
           }
         }
         __builtin_amdgcn_wave_barrier();
+        int got = 0;
+        if (lane == 0) got = atomicAdd(&sh.next_sub, 1);
+        const int nc = __builtin_amdgcn_readfirstlane(got);
+        cs[s] = nc;
+        if (nc < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], rev ? nsub - 1 - nc : nc);
       }
-      W.issue(kr[s], vr[s], mv[s], vv[s], c + NW * PF);
     }
+    if (!more) break;
   }
 
-  // ---- this wave's partials (M, Z per head; value sums) into LDS
-  double zt = Zrun;
-#pragma unroll
-  for (int o = 1; o < D; o <<= 1) zt += __shfl_xor(zt, o);
-#pragma unroll
-  for (int o = LPT; o < 64; o <<= 1) zt += __shfl_xor(zt, o);
+  // ---- this wave's partials (running maximum per head; value sums) into LDS
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -299,10 +327,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
 #pragma unroll
       for (int j = 0; j < EPV; ++j) sh.ep.pO[wave][g][cb * EPV + j] = oacc[g][j];
   }
-  if (tg == 0 && dup == 0) {
-    sh.ep.pM[wave][myh] = Mrun;
-    sh.ep.pZ[wave][myh] = zt;
-  }
+  if (tg == 0 && dup == 0) sh.ep.pM[wave][myh] = Mrun;
   lds_barrier();
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
@@ -340,22 +365,36 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   int last_pos = a.t;
   if (!a.append && L > 0) last_pos = a.pos[sc + L - 1];
 
-  // ---- combine the waves: lane w * G + g of wave 0 takes wave w's partials of head g
-  if (wave == 0) {
-    constexpr int NC = NW * G;
-    const int w = lane / G, g = lane % G;
-    const bool act = lane < NC;
-    const double pm = act ? sh.ep.pM[w][g] : -INFINITY;
-    double M = pm;
+  // ---- the head maxima M (over the waves' running maxima) and the normalisers
+  // Z = sum_c z_c exp(m_c - M) in a fixed order: thread t takes the (sub-chunk,
+  // head) entries t, t + NT, ... (its head is t % G), then a fixed tree over
+  // the threads of each head; f_lds becomes exp(m_c - M)
+  const int nsubL = (L + CHW - 1) / CHW;
+  {
+    const int g = tid % G;
+    double M = -INFINITY;
 #pragma unroll
-    for (int o = G; o < NC; o <<= 1) M = fmax(M, __shfl_xor(M, o));
-    const double ew = pm > -INFINITY ? exp(pm - M) : 0.0;
-    double Z = act ? sh.ep.pZ[w][g] * ew : 0.0;
+    for (int w = 0; w < NW; ++w) M = fmax(M, sh.ep.pM[w][g]);
+    double zp = 0.0;
+    for (int idx = tid; idx < nsubL * G; idx += NT) {
+      const double ex = M > -INFINITY ? exp(f_lds[idx] - M) : 0.0;
+      zp += z_lds[idx] * ex;
+      f_lds[idx] = ex;
+    }
 #pragma unroll
-    for (int o = G; o < NC; o <<= 1) Z += __shfl_xor(Z, o);
-    if (act) sh.ep.fac[w][g] = Z > 0.0 ? float(ew / Z) : 0.f;
-    if (lane < G) {
-      sh.ep.M[g] = M;
+    for (int o = G; o < 64; o <<= 1) zp += __shfl_xor(zp, o);
+    if (lane < G) sh.ep.zw[wave][lane] = zp;
+    if (tid < G) sh.ep.M[tid] = M;
+  }
+  lds_barrier();
+  if (tid < NW * G) {   // Z per head (the same sum in every thread of the head), the waves' factors
+    const int w = tid / G, g = tid % G;
+    double Z = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) Z += sh.ep.zw[w2][g];
+    const double M = sh.ep.M[g], pm = sh.ep.pM[w][g];
+    sh.ep.fac[w][g] = (Z > 0.0 && pm > -INFINITY) ? float(exp(pm - M) / Z) : 0.f;
+    if (w == 0) {
       sh.ep.iZ[g] = Z > 0.0 ? 1.0 / Z : 0.0;
       a.lse[int64_t(gu) * G + g] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
     }
@@ -369,15 +408,9 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     a.out[(int64_t(gu) * G + g) * HD + e] = acc;
   }
   const bool score = a.refresh && (step || a.s != nullptr);
-  const int nsubL = (L + CHW - 1) / CHW;
-  if (score) {
-    for (int idx = tid; idx < nsubL * G; idx += NT) {
-      const int g = idx % G;
-      const double iz = sh.ep.iZ[g];
-      f_lds[idx] = iz > 0.0 ? exp(f_lds[idx] - sh.ep.M[g]) * iz : 0.0;
-    }
-  }
-  lds_barrier();
+  double izr[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) izr[g] = sh.ep.iZ[g];
 
   // ---- score, utility; per thread the smallest (m, slot) and how many slots hold that m
   const double inv_heads = 1.0 / double(G);
@@ -393,11 +426,12 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
       double acc = 0.0;
       if (shw == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc += double(e_lds[g * ld + i]) * f_lds[c * G + g];
+        for (int g = 0; g < G; ++g) acc += double(e_lds[g * ld + i]) * (f_lds[c * G + g] * izr[g]);
       } else {
 #pragma unroll
         for (int g = 0; g < G; ++g)
-          acc += double(e_lds[g * ld + i]) * f_lds[c * G + g] * shift_scale(int((shw >> (8 * g)) & 255u));
+          acc += double(e_lds[g * ld + i]) * (f_lds[c * G + g] * izr[g]) *
+                 shift_scale(int((shw >> (8 * g)) & 255u));
       }
       if (VOTES && !isnew) acc *= double(v_lds[i]);
       const double sv = acc * inv_heads;
