@@ -34,6 +34,11 @@ from compressed_decode_attention_gqa_amd import kvc  # noqa: E402
 from compressed_decode_attention_gqa_amd import roofline as rf  # noqa: E402
 
 METRIC = "cached tokens attended+scored+evicted/sec and % peak HBM GB/s at 32K ctx"
+# Untimed warm-up runs the requested steps and then keeps going until this much time of
+# back-to-back steps has passed: under sustained load the step time settles some 8% below
+# that of the first steps (clocks ramp up over the first few hundred steps, and drop again
+# after a pause), and a decode loop runs sustained.
+MIN_WARMUP_S = 0.25
 KERNEL_SOURCES = ["decode_unit.hip", "kvc_stream.h", "kvc_epilogue.h", "kvc_ops.h", "kvc_device.h", "kvc_decode.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2x32_traffic.json")
 
@@ -80,32 +85,119 @@ def host_scopes(cache, scopes, dtype, q, kn, vn):
     return states, conv(q), conv(kn), conv(vn)
 
 
-def cpu_baseline(run_state, wl, seconds: float):
-    """The fp64 oracle's decode step timed on the host over a bounded sample."""
+def _oracle_scope_state(wl, j: int):
+    """A steady-state scope of the workload built on the host (the recipe of synth: key
+    scales, K/V rows, step inputs; utilities set to small positive values, moments zero) for
+    timing the oracle. Returns (state, new_k, new_v, q, position) as float64 arrays."""
     import oracle
-    from threadpoolctl import threadpool_info
-    states, q, kn, vn, t = run_state
+    U, d, L = wl.units_per_scope, wl.d, wl.budget
+    seed = wl.seed * 1000 + j
+    scales = synth.key_scales(U, d, seed, "cpu") if wl.key_scales else None
+    K, V = synth.kv_rows(U, L, d, wl.dtype, seed, "cpu", scales)
+    conv = lambda x: oracle.to_f64(x.view(torch.int16).numpy().view(np.uint16), "bf16") \
+        if x.dtype == torch.bfloat16 else x.double().numpy()
+    rng = np.random.default_rng(seed)
+    votes = (1 + rng.poisson(2.0, L)).astype(np.int64) if wl.prior_votes else np.ones(L, dtype=np.int64)
+    mom = {"n": 0, "sk": np.zeros((U, d)), "sv": np.zeros((U, d)), "S": np.zeros((U, d, d))} if wl.moments else None
+    st = oracle.ScopeState(K=conv(K), V=conv(V), votes=votes, pos=np.arange(L, dtype=np.int64),
+                           m=rng.random(L) / L, moments=mom)
+    q = conv(synth.step_query(1, U, wl.G, d, wl.dtype, seed, "cpu"))
+    kn, vn = synth.step_new_kv(1, U, d, wl.dtype, seed, "cpu", scales)
+    return st, conv(kn), conv(vn), q, wl.context
+
+
+def _oracle_worker(task):
+    """One host thread (BLAS limited to one thread) running the oracle's steady decode step on
+    its own scope for `seconds`; returns (steps, tokens, seconds)."""
+    name, j, seconds = task
+    import oracle
+    from threadpoolctl import threadpool_limits
+    wl = synth.WORKLOADS[name]
+    st, kn, vn, q, t = _oracle_scope_state(wl, j)
     prm = oracle.StepParams(scale=float(np.float32(1 / np.sqrt(wl.d))), rule=wl.rule,
                             alpha=float(np.float32(wl.alpha)), budget=wl.budget,
                             groups=wl.n_layers if wl.scope == "model" else 1, merge=wl.merge,
                             row_dtype=wl.dtype)
-    tokens, steps = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        for j, st in enumerate(states):
-            _, res = oracle.decode_step(st, kn[j], vn[j], t, q[j], prm)
-            tokens += scope_tokens(wl, st.length + 1)
+    steps = tokens = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds or steps == 0:
+            oracle.decode_step(st, kn, vn, t, q, prm)
             steps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+            tokens += scope_tokens(wl, st.length + 1)
+        return steps, tokens, time.perf_counter() - t0
+
+
+def cpu_baseline_pool(wl, seconds: float):
+    """The float64 oracle's steady decode step on the host, run before the GPU is touched:
+    one thread alone for a third of `seconds`, then one single-threaded worker process per
+    core (at most 16, the host share of one GPU; 4 for the large model-scope states) for the
+    rest, each on its own scope of the workload. value = tokens/s of the workers together."""
+    import multiprocessing as mp
+    nproc = os.cpu_count() or 1
+    workers = min(nproc, 4 if wl.scope == "model" else 16)
+    st1, tk1, dt1 = _oracle_worker((wl.name, 0, seconds / 3))
+    with mp.get_context("spawn").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_worker, [(wl.name, j, seconds * 2 / 3) for j in range(workers)])
+        wall = time.perf_counter() - t0
+    steps = sum(r[0] for r in res)
+    tokens = sum(r[1] for r in res)
+    span = max(r[2] for r in res)
     what = ("per-sequence steady steps (all layers, one slot set)" if wl.scope == "model"
             else "per-KV-head steady steps")
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": tokens / span, "unit": "tokens/s", "cores": workers, "nproc": nproc, "kind": "oracle",
+            "single_thread": {"value": tk1 / dt1, "unit": "tokens/s", "cores": 1, "steps": st1},
             "sample": f"{steps} {what} of {wl.name} (L={wl.budget + 1}, G={wl.G}, k=1, "
-                      f"moments {'on' if wl.moments else 'off'}{', ZIP merge' if wl.merge else ''}) "
-                      f"in {dt:.1f} s, numpy float64 oracle"}
+                      f"moments {'on' if wl.moments else 'off'}{', ZIP merge' if wl.merge else ''}) in "
+                      f"{span:.1f} s on {workers} worker processes with one BLAS thread each "
+                      f"(pool wall {wall:.1f} s incl. start-up), numpy float64 oracle; single thread: "
+                      f"{st1} steps in {dt1:.1f} s; host scopes built from the workload's recipe"}
+
+
+def warm_up(call, n_min: int, min_seconds: float = MIN_WARMUP_S, chunk: int = 256) -> int:
+    """Runs call(j) for j = 0, 1, ... back to back: at least n_min calls, and on until
+    min_seconds have passed (the host waits for the GPU once every `chunk` calls, a gap too
+    short to lower the clocks); returns the number of calls."""
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        n = min(chunk, n_min - done) if done < n_min else chunk
+        for _ in range(max(1, n)):
+            call(done)
+            done += 1
+        torch.cuda.synchronize()
+        if done >= n_min and time.perf_counter() - t0 >= min_seconds:
+            return done
+
+
+def read_ceiling(dev, nbytes: int, reps: int = 20):
+    """Streaming-read rate of the library's read probe (GB/s): the best over grid sizes of
+    (a) rereading one buffer of nbytes (as the decode step rereads its cache), (b) reading
+    four such buffers in turn (nothing left in the memory-side cache) and (c) one buffer read
+    alternately forwards and backwards (the decode step's walk order)."""
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for mode in ("same", "rotate", "zigzag"):
+        best = 0.0
+        for wg in (256, 512, 1024, 2048, 4096):
+            for j in range(4):
+                kvc.kvc_read_probe(bufs[0], wg, sink)
+            torch.cuda.synchronize()
+            e0.record()
+            for j in range(reps):
+                b = bufs[j % 4] if mode == "rotate" else bufs[0]
+                kvc.kvc_read_probe(b, wg, sink, reverse=(mode == "zigzag" and j % 2 == 1))
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9)
+        out[mode] = best
+    del bufs
+    return out
 
 
 def scope_tokens(wl, L: int) -> int:
@@ -584,6 +676,19 @@ def run_first_step(args):
     print(json.dumps(result), flush=True)
 
 
+def run_stream_ceiling(args):
+    """The streaming-read ceiling alone: the library's read probe over one decode step's
+    algorithmic bytes of the headline workload (and over 1 GiB), every grid size and order."""
+    wl = synth.WORKLOADS["c2x32_llama8b_32layers_32k"]
+    torch.cuda.set_device(0)
+    nbytes = step_bytes(wl, wl.budget + 1)
+    res = {"step_bytes": read_ceiling("cuda", nbytes, reps=50), "1GiB": read_ceiling("cuda", 1 << 30, reps=20)}
+    best = max(max(v.values()) for v in res.values())
+    print(json.dumps({"metric": "streaming-read ceiling (read probe)", "value": best, "unit": "GB/s",
+                      "n_gpus": 1, "higher_is_better": True, "detail": res,
+                      "peak": rf.MI355X_HBM_GBPS, "frac_of_peak": best / rf.MI355X_HBM_GBPS}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -592,10 +697,11 @@ def main():
     ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict", "prefill_merge",
-                                                     "ema_init"],
+                                                     "ema_init", "stream_ceiling"],
                     help="step: the fused decode step (default); first_step: the bulk compression step "
                          "after prefill; moment_correct: MomentKV's corrected output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read probe after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -604,6 +710,8 @@ def main():
               "MI355X; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.op == "stream_ceiling":
+        return run_stream_ceiling(args)
     if args.op == "moment_evict":
         return run_moment_evict(args)
     if args.op == "ema_init":
@@ -624,6 +732,8 @@ def main():
         run_laprox(args)
         return
     wl = synth.WORKLOADS[args.workload]
+    # the oracle's rate on the host cores, measured before the GPU is touched
+    cpu_base = None if args.no_cpu_baseline else cpu_baseline_pool(wl, args.cpu_seconds)
     dev = "cuda"
     torch.cuda.set_device(0)
     S, U, G, d, B = wl.n_scopes, wl.units_per_scope, wl.G, wl.d, wl.budget
@@ -643,7 +753,14 @@ def main():
         q_all.append(q)
         kn_all.append(kn)
         vn_all.append(vn)
-    pos0 = wl.context                           # the next token's position (prior entries lie below it)
+    pos_next = [wl.context]                     # the next token's position (prior entries lie below it)
+    n_calls = [0]
+
+    def next_pos():
+        t = pos_next[0]
+        pos_next[0] += 1
+        n_calls[0] += 1
+        return t
 
     if wl.scope == "model":
         # one call per layer (the layer's KV heads attend and score, the shared utility is
@@ -655,12 +772,13 @@ def main():
         lse_layers = [torch.empty((S, nkv, G), device=dev) for _ in range(wl.n_layers)]
 
         def step_call(i, max_len):
-            refresh = wl.lazy_refresh == 0 or i % wl.lazy_refresh == 0
+            refresh = wl.lazy_refresh == 0 or n_calls[0] % wl.lazy_refresh == 0
+            t = next_pos()
             for l in range(wl.n_layers):
                 # the first layer evicts to the budget; the later layers cannot evict, which the
                 # call says with budget = capacity (their finish launch is then skipped)
                 kvc.kvc_decode_step(cache, kn_all[i] if l == 0 else None, vn_all[i] if l == 0 else None,
-                                    pos0 + i, q_layers[i][l], G, scale, wl.rule, alpha, B if l == 0 else cap,
+                                    t, q_layers[i][l], G, scale, wl.rule, alpha, B if l == 0 else cap,
                                     out_layers[l],
                                     lse_layers[l], s, mom, None, None, refresh=refresh, attn_unit0=l * nkv,
                                     attn_units=nkv, max_len=max_len, ws=ws)
@@ -668,22 +786,25 @@ def main():
         merges = [kvc.merge_desc(q, G, scale) for q in q_all] if wl.merge else None
 
         def step_call(i, max_len):
-            kvc.kvc_decode_step(cache, kn_all[i], vn_all[i], pos0 + i, q_all[i], G, scale, wl.rule, alpha, B,
+            kvc.kvc_decode_step(cache, kn_all[i], vn_all[i], next_pos(), q_all[i], G, scale, wl.rule, alpha, B,
                                 out, lse, s, mom, merges[i] if merges else None, None, max_len=max_len, ws=ws)
 
     step_call(0, wl.initial_len + 1)            # first step: bulk compression to the budget
-    for i in range(1, 1 + args.warmup):
-        step_call(i, B + 1)
-    torch.cuda.synchronize()
-    assert int(cache.length.min()) == B and int(cache.length.max()) == B
+    # the requested warm-up steps, then on (cycling through their inputs) until the GPU has run
+    # MIN_WARMUP_S of back-to-back steps
+    warm = lambda j: step_call(1 + j % max(1, args.warmup), B + 1)
+    warm_steps = warm_up(warm, args.warmup, chunk=256 if wl.scope != "model" else 16)
 
     # The timed region is K back-to-back steps on the launch stream (torch's current
     # stream), bracketed by two HIP events: for the per-head workloads a step is one
     # kernel launch, so the region's length over K is that kernel's average duration
     # (events between launches would add their own cost to every step); a model-scope
-    # step is one call per layer.
+    # step is one call per layer. A last run of warm-up steps is queued right before the
+    # start event, so the GPU does not idle (and drop its clocks) between warm-up and timing.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    for j in range(256 if wl.scope != "model" else 16):
+        warm(j)
+        warm_steps += 1
     start.record()
     for j in range(args.steps):
         step_call(1 + args.warmup + j, B + 1)
@@ -691,6 +812,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     launch_ms = total_ms / args.steps
+    assert int(cache.length.min()) == B and int(cache.length.max()) == B
     status = kvc.kvc_workspace_status(ws)
     if status != 0:
         raise SystemExit(f"device status {status} after the timed steps")
@@ -704,7 +826,8 @@ def main():
     traffic = measured_traffic(wl.name)
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "warmup_steps_run": warm_steps, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "layers": wl.n_layers, "batch": wl.batch, "kv_heads": wl.n_kv,
                    "q_heads": wl.n_kv * G, "head_dim": d, "context": wl.context, "budget": B,
@@ -720,11 +843,13 @@ def main():
         y = torch.empty_like(x)
         y.copy_(x)
         torch.cuda.synchronize()
-    if not args.no_cpu_baseline:
-        i = 1 + args.warmup + args.steps     # inputs of the next step, applied to the current state
-        q, kn, vn = synth.step_inputs(wl, i + 1, t["scales"], dev)
-        state = host_scopes(cache, list(range(min(S, 2 if wl.scope == "model" else 32))), wl.dtype, q, kn, vn)
-        result["cpu_baseline"] = cpu_baseline(state + (pos0 + i,), wl, args.cpu_seconds)
+    if not args.no_ceiling:
+        ceil = read_ceiling(dev, bytes_per_launch)
+        result["roofline"]["measured_ceiling_GBps"] = max(ceil.values())
+        result["roofline"]["measured_ceiling"] = {k: round(v, 1) for k, v in ceil.items()}
+        result["roofline"]["frac_of_measured_ceiling"] = achieved / max(ceil.values())
+    if cpu_base is not None:
+        result["cpu_baseline"] = cpu_base
     print(json.dumps(result), flush=True)
 
 

@@ -520,6 +520,15 @@ int32_t kvc_ema_predict(const float *m, const int32_t *len, int32_t n_scopes, in
   return KVC_OK;
 }
 
+int32_t kvc_read_probe(const void *buf, size_t bytes, int32_t workgroups, int32_t reverse, uint32_t *sink,
+                       void *stream) {
+  if (!buf || !sink || workgroups <= 0 || bytes < 16) return KVC_ERR_ARG;
+  if (!aligned16(buf)) return KVC_ERR_ALIGN;
+  if (kvc::launch_read_probe(buf, bytes, workgroups, reverse, sink, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
 int32_t kvc_keep_jaccard(const uint8_t *keep_a, const uint8_t *keep_b, const int32_t *len, int32_t n_scopes,
                          int32_t capacity, float *out, void *stream) {
   if (!keep_a || !keep_b || !out || n_scopes <= 0 || capacity <= 0) return KVC_ERR_ARG;

@@ -377,7 +377,8 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     for (int w = 0; w < NW; ++w) M = fmax(M, sh.ep.pM[w][g]);
     double zp = 0.0;
     for (int idx = tid; idx < nsubL * G; idx += NT) {
-      const double ex = M > -INFINITY ? exp(f_lds[idx] - M) : 0.0;
+      // exp(m_c - M) <= 1 to about one float ulp (the per-token weights are floats too)
+      const double ex = double(exp_split(f_lds[idx] - M));
       zp += z_lds[idx] * ex;
       f_lds[idx] = ex;
     }
@@ -417,6 +418,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   const double alpha = double(a.alpha);
   uint64_t bestm = ~0ull;
   int bslot = 0x7fffffff, bcnt = 0;
+#pragma unroll 2
   for (int i = tid; i < L; i += NT) {
     const bool isnew = a.append && i == L - 1;
     double mval = isnew ? 0.0 : m_lds[i];

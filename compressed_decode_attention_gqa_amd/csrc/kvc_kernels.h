@@ -94,6 +94,9 @@ hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n
                              int rule, float alpha, hipStream_t st);
 hipError_t launch_ema_predict(const float *m, const int32_t *len, int n_scopes, int cap, float alpha, int t,
                               float *out, hipStream_t st);
+// Streaming-read probe (measurement aid).
+hipError_t launch_read_probe(const void *buf, size_t bytes, int workgroups, int reverse, uint32_t *sink,
+                             hipStream_t st);
 hipError_t launch_jaccard(const uint8_t *a, const uint8_t *b, const int32_t *len, int n_scopes, int cap, float *out,
                           hipStream_t st);
 

@@ -29,7 +29,7 @@ EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_ema_predict", "kvc_s
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
             "kvc_keepkv_prefill_workspace_size", "kvc_keepkv_ema_init_workspace_size",
             "kvc_laprox_workspace_size",
-            "kvc_workspace_status", "kvc_status_string", "kvc_check", "kvc_version")
+            "kvc_read_probe", "kvc_workspace_status", "kvc_status_string", "kvc_check", "kvc_version")
 
 
 class KvcError(RuntimeError):
@@ -85,6 +85,7 @@ _SIGS = {
     "kvc_keepkv_prefill_workspace_size": (_SZ, [_P]),
     "kvc_keepkv_ema_init_workspace_size": (_SZ, [_P, _I, _I, _I]),
     "kvc_laprox_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "kvc_read_probe": (_I, [_P, _SZ, _I, _I, _P, _P]),
     "kvc_workspace_status": (_I, [_P, _P]),
     "kvc_status_string": (ctypes.c_char_p, [_I]),
     "kvc_check": (_I, [_P]),
@@ -267,6 +268,13 @@ def kvc_decode_step_noalloc(cache: Cache, k_new, v_new, t: int, q, G: int, scale
         _ptr(out), _ptr(lse), _ptr(s), ctypes.byref(mom) if mom is not None else None,
         ctypes.byref(merge) if merge is not None else None, _ptr(evict_out), attn_unit0, attn_units, max_len,
         _ptr(status), _stream(stream)))
+
+
+def kvc_read_probe(buf: torch.Tensor, workgroups: int, sink: torch.Tensor, reverse: bool = False,
+                   nbytes: int | None = None, stream=None):
+    nb = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check("kvc_read_probe", lib().kvc_read_probe(_ptr(buf), nb, workgroups, int(reverse), _ptr(sink),
+                                                  _stream(stream)))
 
 
 def kvc_ema_update(m, s, length, n_scopes: int, capacity: int, rule, alpha: float, stream=None):

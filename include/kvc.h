@@ -446,6 +446,17 @@ int32_t kvc_workspace_status(void *ws, void *stream);
 
 const char *kvc_status_string(int32_t status);
 
+/* kvc_read_probe -- measurement aid, not part of the method: reads the first
+ * bytes / 16 16-byte vectors of buf (device memory, 16-byte aligned) once, each
+ * of `workgroups` workgroups (256 threads) one contiguous share with 8 loads in
+ * flight per thread (reverse != 0: each share from its end), and writes one
+ * word per workgroup to sink[workgroups]. Timing it gives the streaming-read
+ * rate a plain kernel attains on the device, the ceiling the decode kernels are
+ * compared with beside the published HBM peak. KVC_ERR_ARG for null pointers,
+ * workgroups <= 0 or bytes < 16; KVC_ERR_ALIGN for an unaligned buf. */
+int32_t kvc_read_probe(const void *buf, size_t bytes, int32_t workgroups, int32_t reverse, uint32_t *sink,
+                       void *stream);
+
 /* Synchronises `stream` and reports an asynchronous device error of the work queued
  * on it: KVC_ERR_DEVICE if the stream (or an earlier launch) failed, else KVC_OK. */
 int32_t kvc_check(void *stream);
