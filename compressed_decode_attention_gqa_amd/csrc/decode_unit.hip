@@ -310,39 +310,11 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     if (!more) break;
   }
 
-  // ---- this wave's partials (running maximum per head; value sums) into LDS
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) {
-      float x = oacc[g][j];
-#pragma unroll
-      for (int o = LPT; o < 64; o <<= 1) x += __shfl_xor(x, o);
-      oacc[g][j] = x;
-    }
-  lds_barrier();   // the weight scratch becomes the epilogue's space
-  if (lane < LPT) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < EPV; ++j) sh.ep.pO[wave][g][cb * EPV + j] = oacc[g][j];
-  }
-  if (tg == 0 && dup == 0) sh.ep.pM[wave][myh] = Mrun;
-  lds_barrier();
+  // ---- loads the epilogue needs, issued by each wave as its streaming ends (the
+  // other waves may still stream): its share of the moment sums, the last live row
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
-  if (overflow || k > 1) {
-    // k > 1 cannot happen: the host launches this kernel only when
-    // lds_len <= budget + 1, and L <= lds_len here
-    if (tid == 0) {
-      a.status[0] = overflow ? -4 : -3;
-      if (a.mode == 2) a.list[sc] = -1;
-    }
-    return;
-  }
-
-  // ---- loads the rest of the epilogue needs, issued before scoring
-  const bool fold = step && k == 1 && a.mom_S != nullptr;
+  const bool fold = !overflow && step && k == 1 && a.mom_S != nullptr;
   const int64_t mu = int64_t(scope) * a.units + unit;
   float4 Sreg[Geo::NS4];
   float skv = 0.f;
@@ -362,6 +334,37 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     const char *src = a.append ? (lastK ? W.Kn : W.Vn) : (lastK ? W.Kb : W.Vb) + int64_t(L - 1) * RB;
     lastrow = ld16(src + 16 * lastc);
   }
+
+  // ---- this wave's partials (running maximum per head; value sums) into LDS: the
+  // value sums over the token groups of the wave by lane swaps
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      float x = oacc[g][j];
+      if constexpr (LPT == 16) x += lane_xor16(x);
+      x += lane_xor32(x);
+      oacc[g][j] = x;
+    }
+  lds_barrier();   // the weight scratch becomes the epilogue's space
+  if (lane < LPT) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) sh.ep.pO[wave][g][cb * EPV + j] = oacc[g][j];
+  }
+  if (tg == 0 && dup == 0) sh.ep.pM[wave][myh] = Mrun;
+  lds_barrier();
+  if (overflow || k > 1) {
+    // k > 1 cannot happen: the host launches this kernel only when
+    // lds_len <= budget + 1, and L <= lds_len here
+    if (tid == 0) {
+      a.status[0] = overflow ? -4 : -3;
+      if (a.mode == 2) a.list[sc] = -1;
+    }
+    return;
+  }
+
   int last_pos = a.t;
   if (!a.append && L > 0) last_pos = a.pos[sc + L - 1];
 
@@ -377,8 +380,11 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
     for (int w = 0; w < NW; ++w) M = fmax(M, sh.ep.pM[w][g]);
     double zp = 0.0;
     for (int idx = tid; idx < nsubL * G; idx += NT) {
-      // exp(m_c - M) <= 1 to about one float ulp (the per-token weights are floats too)
-      const double ex = double(exp_split(f_lds[idx] - M));
+      // exp(m_c - M) <= 1: to about one float ulp (the per-token weights are floats
+      // too) in float32's normal range, in float64 below it, where the scores of a
+      // sub-chunk far below the head maximum still rank on their float64 values
+      const double d = f_lds[idx] - M;
+      const double ex = d >= -SHIFT_STEP ? double(exp_split(d)) : d > -1.0e30 ? exp(d) : 0.0;
       zp += z_lds[idx] * ex;
       f_lds[idx] = ex;
     }
@@ -394,7 +400,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) Z += sh.ep.zw[w2][g];
     const double M = sh.ep.M[g], pm = sh.ep.pM[w][g];
-    sh.ep.fac[w][g] = (Z > 0.0 && pm > -INFINITY) ? float(exp(pm - M) / Z) : 0.f;
+    sh.ep.fac[w][g] = (Z > 0.0 && pm > -INFINITY) ? float(double(exp_split(pm - M)) / Z) : 0.f;
     if (w == 0) {
       sh.ep.iZ[g] = Z > 0.0 ? 1.0 / Z : 0.0;
       a.lse[int64_t(gu) * G + g] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
@@ -453,11 +459,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   }
   int e1 = -1;
   if (k == 1) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint64_t m2 = shfl_xor_u64(bestm, o);
-      const int s2 = __shfl_xor(bslot, o);
-      const int c2 = __shfl_xor(bcnt, o);
+    wave_reduce_key_slot_cnt(bestm, bslot, bcnt, [&](uint64_t m2, int s2, int c2) {
       if (m2 < bestm) {
         bestm = m2;
         bslot = s2;
@@ -466,7 +468,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
         bslot = min(bslot, s2);
         bcnt += c2;
       }
-    }
+    });
     if (lane == 0) {
       sh.ep.wkey[wave] = bestm;
       sh.ep.wslot[wave] = bslot;

@@ -131,6 +131,52 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
   return x;
 }
 
+// The value of lane l ^ 32 (or l ^ 16) through the gfx950 lane swaps, without LDS: a swap of
+// x with itself leaves x[l ^ 32] in the first result on the upper half of the wave and in
+// the second on the lower half (likewise for 16-lane halves of each 32).
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ float lane_xor32(float x) { return __uint_as_float(lane_xor32(__float_as_uint(x))); }
+__device__ __forceinline__ float lane_xor16(float x) { return __uint_as_float(lane_xor16(__float_as_uint(x))); }
+__device__ __forceinline__ uint64_t lane_xor32(uint64_t x) {
+  return (uint64_t(lane_xor32(uint32_t(x >> 32))) << 32) | lane_xor32(uint32_t(x));
+}
+__device__ __forceinline__ uint64_t lane_xor16(uint64_t x) {
+  return (uint64_t(lane_xor16(uint32_t(x >> 32))) << 32) | lane_xor16(uint32_t(x));
+}
+__device__ __forceinline__ int lane_xor32(int x) { return int(lane_xor32(uint32_t(x))); }
+__device__ __forceinline__ int lane_xor16(int x) { return int(lane_xor16(uint32_t(x))); }
+
+// The value a DPP pattern moves into this lane (all patterns used stay inside a 16-lane row).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), CTRL, 0xf, 0xf, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  return (uint64_t(dpp_u32<CTRL>(uint32_t(x >> 32))) << 32) | dpp_u32<CTRL>(uint32_t(x));
+}
+
+// Wave reduction over lane pairings that reach all 64 lanes in six stages: quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror, then the 16- and 32-lane
+// swaps. f(partner values...) combines a partner into this lane's state; every lane ends
+// with the whole wave's result when f is associative and commutative.
+template <class F>
+__device__ __forceinline__ void wave_reduce_key_slot_cnt(uint64_t &key, int &slot, int &cnt, F f) {
+  f(dpp_u64<0xB1>(key), int(dpp_u32<0xB1>(uint32_t(slot))), int(dpp_u32<0xB1>(uint32_t(cnt))));
+  f(dpp_u64<0x4E>(key), int(dpp_u32<0x4E>(uint32_t(slot))), int(dpp_u32<0x4E>(uint32_t(cnt))));
+  f(dpp_u64<0x141>(key), int(dpp_u32<0x141>(uint32_t(slot))), int(dpp_u32<0x141>(uint32_t(cnt))));
+  f(dpp_u64<0x140>(key), int(dpp_u32<0x140>(uint32_t(slot))), int(dpp_u32<0x140>(uint32_t(cnt))));
+  f(lane_xor16(key), lane_xor16(slot), lane_xor16(cnt));
+  f(lane_xor32(key), lane_xor32(slot), lane_xor32(cnt));
+}
+
 // Exclusive prefix count of a 0/1 predicate within the wave, and the wave total.
 __device__ __forceinline__ int wave_prefix_count(bool pred, int *total) {
   uint64_t b = __ballot(pred);
