@@ -29,6 +29,10 @@ static_assert(kMergeSplitsMax <= 64, "k_merge_finish reads one range partner per
 // scopes to spread over the 256 CUs, each scope's live length is bounded so
 // its per-token state fits in LDS, and a step evicts at most one entry.
 constexpr int kUnitMinScopes = 128;
+// With fewer scopes the single launch still wins while one workgroup streams
+// its scope's rows (about 25 GB/s per CU) faster than the split path's three
+// dependent launches finish: up to this many K and V bytes per scope.
+constexpr int64_t kUnitFewScopesMaxBytes = 256 << 10;
 // Bulk eviction (k > 1): fold workgroups per launch to aim for, and the most per unit.
 constexpr int kFoldWorkgroups = 1024;
 constexpr int kFoldSplitsMax = 64;
@@ -166,6 +170,22 @@ kvc::CacheArgs cache_args(const kvc_cache *c) {
   return a;
 }
 
+// The kernels a decode call runs (max_len already resolved, > 0): the per-scope
+// kernel for steady steps of single-unit scopes whose per-token state fits in
+// LDS, once there are enough scopes to spread over the CUs or each scope's rows
+// are few; otherwise split-K attention with the score/finish kernels, plus the
+// bulk kernels when a step without merge may evict more than one entry per
+// scope (mode: 0 attend and score, 1 step, 2 step with merge).
+int decode_plan(const kvc_cache *c, int G, int mode, int budget, int max_len) {
+  const bool steady = mode == 0 || int64_t(max_len) <= int64_t(budget) + 1;
+  const int64_t scope_bytes = 2 * int64_t(max_len) * kHD * (c->dtype == KVC_BF16 ? 2 : 4);
+  if (c->units_per_scope == 1 && steady &&
+      (c->n_scopes >= kUnitMinScopes || scope_bytes <= kUnitFewScopesMaxBytes) &&
+      kvc::decode_unit_lds_bytes(c->dtype, G, max_len, c->votes != nullptr) <= device_lds_per_block())
+    return KVC_PLAN_ONE_LAUNCH;
+  return (mode == 1 && !steady) ? KVC_PLAN_SPLIT_BULK : KVC_PLAN_SPLIT;
+}
+
 int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t t, const void *q,
                int32_t G, float scale, int mode, int rule, float alpha, int budget, int refresh,
                float *out, float *lse, float *s, const kvc_moments *mom, const kvc_merge *merge,
@@ -262,20 +282,15 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   }
   const int CH = kvc::decode_chunk_tokens(c->dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  bool per_scope = c->units_per_scope == 1 && c->n_scopes >= kUnitMinScopes &&
-                   (a.mode == 0 || int64_t(max_len) <= int64_t(budget) + 1);
-  if (per_scope) {
-    const size_t lds = kvc::decode_unit_lds_bytes(c->dtype, G, max_len, c->votes != nullptr);
-    per_scope = lds <= device_lds_per_block();
-  }
-  if (per_scope) {
+  const int plan = decode_plan(c, G, a.mode, budget, max_len);
+  if (plan == KVC_PLAN_ONE_LAUNCH) {
     a.n_splits = 1;
     a.lds_len = max_len;
     if (kvc::launch_decode_unit(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
   } else {
     // a step that may evict more than one entry per scope hands those scopes to
     // the device-wide bulk kernels
-    const bool bulk = a.mode == 1 && int64_t(max_len) > int64_t(budget) + 1;
+    const bool bulk = plan == KVC_PLAN_SPLIT_BULK;
     if (bulk) a.bulk = at<kvc::BulkScope>(ws, d.bulk_state);
     a.n_splits = split_count(c->n_scopes * attn_units, ceil_div(max_len, CH));
     if (kvc::launch_decode(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
@@ -475,6 +490,17 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
                         size_t ws_bytes, void *stream) {
   return run_decode(cache, k_new, v_new, t, q, G, scale, 1, rule, alpha, budget, refresh, out, lse, s,
                     mom, merge, evict_out, attn_unit0, attn_units, max_len, ws, ws_bytes, stream);
+}
+
+int32_t kvc_decode_plan(const kvc_cache *cache, int32_t G, int32_t step, int32_t merge, int32_t budget,
+                        int32_t max_len) {
+  const int st = validate_cache(cache);
+  if (st) return st;
+  if (!valid_G(G)) return KVC_ERR_UNSUPPORTED;
+  if (max_len > cache->capacity) return KVC_ERR_CAPACITY;
+  if (max_len <= 0) max_len = cache->capacity;
+  if (step && budget < 0) return KVC_ERR_CAPACITY;
+  return decode_plan(cache, G, step ? (merge ? 2 : 1) : 0, budget, max_len);
 }
 
 int32_t kvc_decode_step_noalloc(const kvc_cache *cache, const void *k_new, const void *v_new, int32_t t,

@@ -25,7 +25,7 @@ EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_ema_predict", "kvc_s
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
             "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
             "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step", "kvc_decode_step_noalloc",
-            "kvc_decode_workspace_size",
+            "kvc_decode_workspace_size", "kvc_decode_plan",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
             "kvc_keepkv_prefill_workspace_size", "kvc_keepkv_ema_init_workspace_size",
             "kvc_laprox_workspace_size",
@@ -79,6 +79,7 @@ _SIGS = {
     "kvc_laprox_score": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P]),
     "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
+    "kvc_decode_plan": (_I, [_P, _I, _I, _I, _I, _I]),
     "kvc_select_workspace_size": (_SZ, [_I, _I]),
     "kvc_compact_workspace_size": (_SZ, [_P]),
     "kvc_moment_evict_workspace_size": (_SZ, [_P]),
@@ -190,6 +191,20 @@ def merge_desc(q: torch.Tensor, G: int, scale: float, eps: float = 1e-6) -> _Mer
 def kvc_decode_workspace_size(cache: Cache, G: int, max_len: int = 0) -> int:
     d = cache.desc()
     return lib().kvc_decode_workspace_size(ctypes.byref(d), G, max_len)
+
+
+PLAN_ONE_LAUNCH, PLAN_SPLIT, PLAN_SPLIT_BULK = 1, 2, 3
+
+
+def kvc_decode_plan(cache: Cache, G: int, step: bool = True, merge: bool = False, budget: int = 0,
+                    max_len: int = 0) -> int:
+    """PLAN_ONE_LAUNCH, PLAN_SPLIT or PLAN_SPLIT_BULK: the kernels kvc_decode_step (step) or
+    kvc_decode_attn_score (not step) runs for these shapes."""
+    d = cache.desc()
+    plan = lib().kvc_decode_plan(ctypes.byref(d), G, int(step), int(merge), budget, max_len)
+    if plan < 0:
+        raise KvcError("kvc_decode_plan", plan)
+    return plan
 
 
 def kvc_select_workspace_size(n_scopes: int, capacity: int) -> int:

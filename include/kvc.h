@@ -368,6 +368,23 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
                         int32_t attn_unit0, int32_t attn_units, int32_t max_len,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* kvc_decode_plan -- the kernels a call with these shapes runs, without running
+ * it: kvc_decode_step (step != 0, with this budget, merge != 0 for a call with a
+ * merge descriptor) or kvc_decode_attn_score (step == 0; budget and merge
+ * ignored) on `cache` with group size G and max_len (<= 0: capacity). Returns
+ *   KVC_PLAN_ONE_LAUNCH: one workgroup per scope does the whole step in one
+ *     launch (single-unit scopes, at most one eviction per scope, the per-token
+ *     state of max_len tokens fits in LDS, and either at least 128 scopes or at
+ *     most 256 KiB of K and V rows per scope);
+ *   KVC_PLAN_SPLIT: split-K attention, then the score and finish kernels;
+ *   KVC_PLAN_SPLIT_BULK: KVC_PLAN_SPLIT plus the device-wide eviction kernels
+ *     (max_len > budget + 1, no merge);
+ * or the (negative) error code the call would return for these shapes. Host
+ * only: reads the device's LDS size, enqueues nothing. */
+enum { KVC_PLAN_ONE_LAUNCH = 1, KVC_PLAN_SPLIT = 2, KVC_PLAN_SPLIT_BULK = 3 };
+int32_t kvc_decode_plan(const kvc_cache *cache, int32_t G, int32_t step, int32_t merge, int32_t budget,
+                        int32_t max_len);
+
 /* kvc_decode_step_noalloc -- kvc_decode_step for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same arguments and results, with the workspace

@@ -80,6 +80,23 @@ def test_decode_step_host_checks():
 
 
 @needs_lib
+def test_decode_plan_host_logic():
+    """The plan query: argument errors as the step returns them; a live-length bound above
+    budget + 1 takes the bulk kernels without merge and not with it (neither depends on the device)."""
+    L = kvc.lib()
+    c = _fake_cache()
+    plan = lambda G=4, step=1, merge=0, budget=10, max_len=0: L.kvc_decode_plan(ctypes.byref(c), G, step, merge,
+                                                                                 budget, max_len)
+    assert plan(G=3) == -3
+    assert plan(max_len=101) == -4
+    assert plan(budget=-1) == -4
+    assert plan() == kvc.PLAN_SPLIT_BULK
+    assert plan(merge=1) == kvc.PLAN_SPLIT
+    bad = _fake_cache(head_dim=64)
+    assert L.kvc_decode_plan(ctypes.byref(bad), 4, 1, 0, 10, 0) == -3
+
+
+@needs_lib
 def test_other_entry_points_reject_bad_arguments():
     L = kvc.lib()
     assert L.kvc_ema_update(None, 0x10, 0x20, 1, 10, 2, 0.9, None) == -1

@@ -87,11 +87,38 @@ def test_attn_score_without_utilities(layers):
     assert np.all(run.cache.length.cpu().numpy() == L)
 
 
-def test_decode_step_c1_lockstep():
-    """Single fp32 head, 4096 tokens to a 128 budget, 64 steps, every step checked."""
+@pytest.mark.parametrize("plan", ["one_launch", "split"])
+def test_decode_step_c1_lockstep(plan):
+    """Single fp32 head, 4096 tokens to a 128 budget, 64 steps, every step checked. one_launch: the
+    steady steps bound the live length by budget + 1, so the library runs them as one launch of
+    the per-scope kernel (129 rows of 512 bytes per scope); split: no bound (split-K attention and
+    the score/finish kernels every step)."""
     run = DeviceRun(C1)
-    rep = lockstep(run, C1.steps, lambda t: [0])
-    _say("c1", rep)
+    if plan == "one_launch":
+        ml = lambda t: C1.context + 1 if t == 1 else C1.budget + 1
+        assert kvc.kvc_decode_plan(run.cache, C1.G, budget=C1.budget, max_len=C1.budget + 1) == kvc.PLAN_ONE_LAUNCH
+    else:
+        ml = lambda t: None
+        assert kvc.kvc_decode_plan(run.cache, C1.G, budget=C1.budget) == kvc.PLAN_SPLIT_BULK
+    rep = lockstep(run, C1.steps, lambda t: [0], max_len_for_step=ml)
+    _say("c1", plan, rep)
+
+
+def test_decode_plan_choice():
+    """Steady steps of single-unit scopes run as one launch with >= 128 scopes or <= 256 KiB of rows
+    per scope; a literal C2 layer (8 heads of 3277 bf16 rows, 1.7 MB each) keeps split-K; a larger
+    live-length bound without merge adds the bulk eviction kernels, with merge it does not."""
+    c1 = DeviceRun(C1.scaled(context=300, budget=128, steps=1))
+    assert kvc.kvc_decode_plan(c1.cache, 1, budget=128, max_len=129) == kvc.PLAN_ONE_LAUNCH
+    assert kvc.kvc_decode_plan(c1.cache, 1, step=False, max_len=129) == kvc.PLAN_ONE_LAUNCH
+    assert kvc.kvc_decode_plan(c1.cache, 1, budget=128, max_len=301) == kvc.PLAN_SPLIT_BULK
+    c2 = DeviceRun(C2.scaled(steps=1))
+    B = C2.budget
+    assert kvc.kvc_decode_plan(c2.cache, 4, budget=B, max_len=B + 1) == kvc.PLAN_SPLIT
+    assert kvc.kvc_decode_plan(c2.cache, 4, budget=B, max_len=C2.context + 1) == kvc.PLAN_SPLIT_BULK
+    assert kvc.kvc_decode_plan(c2.cache, 4, budget=B, merge=True, max_len=C2.context + 1) == kvc.PLAN_SPLIT
+    c2x = DeviceRun(C2.scaled(n_layers=16, context=B + 8, steps=1))
+    assert kvc.kvc_decode_plan(c2x.cache, 4, budget=B, max_len=B + 1) == kvc.PLAN_ONE_LAUNCH
 
 
 def test_decode_step_c2_reduced_lockstep():
@@ -519,9 +546,12 @@ def test_weights_below_float32_range_rank_as_float64(path):
     what the float64 oracle evicts. per_head: 136 scopes at one eviction each (one workgroup per
     head); split: 8 scopes (split-K attention and the score/finish kernels)."""
     _say("underflow ranking", path)
-    wl = C2.scaled(n_layers=17 if path == "per_head" else 1, n_kv=8, context=400, budget=400, steps=4,
+    n = 400 if path == "per_head" else 600     # split: 601 rows of 512 bytes, beyond one launch's 256 KiB
+    wl = C2.scaled(n_layers=17 if path == "per_head" else 1, n_kv=8, context=n, budget=n, steps=4,
                    rule="single", key_scales=True)
     run = DeviceRun(wl, max_len=wl.budget + 1, moments=False)
+    want = kvc.PLAN_ONE_LAUNCH if path == "per_head" else kvc.PLAN_SPLIT
+    assert kvc.kvc_decode_plan(run.cache, wl.G, budget=wl.budget, max_len=wl.budget + 1) == want
     rep = {}
     for step in range(1, wl.steps + 1):
         q, kn, vn = run.inputs(step)
