@@ -700,6 +700,9 @@ def main():
                                                      "ema_init", "stream_ceiling"],
                     help="step: the fused decode step (default); first_step: the bulk compression step "
                          "after prefill; moment_correct: MomentKV's corrected output")
+    ap.add_argument("--model-path", default="groups", choices=["groups", "per_layer"],
+                    help="model-scope workloads: the layers after the first in one kvc_decode_groups call, "
+                         "or one call per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read probe after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -763,25 +766,42 @@ def main():
         return t
 
     if wl.scope == "model":
-        # one call per layer (the layer's KV heads attend and score, the shared utility is
-        # updated and the scope evicts); the first layer's call appends every layer's rows
+        # the first layer's call appends every layer's rows, attends, scores, updates the
+        # shared utility and evicts to the budget; the later layers cannot evict: one
+        # kvc_decode_groups call for all of them (utility chain in closed form), or with
+        # --model-path per_layer one kvc_decode_step per layer with budget = capacity
         nkv = wl.n_kv
         cap = cache.capacity
-        q_layers = [[q[:, l * nkv:(l + 1) * nkv].contiguous() for l in range(wl.n_layers)] for q in q_all]
-        out_layers = [torch.empty((S, nkv, G, d), device=dev) for _ in range(wl.n_layers)]
-        lse_layers = [torch.empty((S, nkv, G), device=dev) for _ in range(wl.n_layers)]
+        nl = wl.n_layers
+        q_first = [q[:, :nkv].contiguous() for q in q_all]
+        q_rest = [q[:, nkv:].contiguous() for q in q_all]
+        q_layers = [[q[:, l * nkv:(l + 1) * nkv].contiguous() for l in range(1, nl)] for q in q_all] \
+            if args.model_path == "per_layer" else None
+        out_first = torch.empty((S, nkv, G, d), device=dev)
+        lse_first = torch.empty((S, nkv, G), device=dev)
+        out_rest = torch.empty((S, (nl - 1) * nkv, G, d), device=dev)
+        lse_rest = torch.empty((S, (nl - 1) * nkv, G), device=dev)
+        # per-layer calls write [S][nkv][G][d] contiguously: one buffer per layer
+        out_layers = [torch.empty((S, nkv, G, d), device=dev) for _ in range(1, nl)] if q_layers else None
+        lse_layers = [torch.empty((S, nkv, G), device=dev) for _ in range(1, nl)] if q_layers else None
 
         def step_call(i, max_len):
             refresh = wl.lazy_refresh == 0 or n_calls[0] % wl.lazy_refresh == 0
             t = next_pos()
-            for l in range(wl.n_layers):
-                # the first layer evicts to the budget; the later layers cannot evict, which the
-                # call says with budget = capacity (their finish launch is then skipped)
-                kvc.kvc_decode_step(cache, kn_all[i] if l == 0 else None, vn_all[i] if l == 0 else None,
-                                    t, q_layers[i][l], G, scale, wl.rule, alpha, B if l == 0 else cap,
-                                    out_layers[l],
-                                    lse_layers[l], s, mom, None, None, refresh=refresh, attn_unit0=l * nkv,
-                                    attn_units=nkv, max_len=max_len, ws=ws)
+            kvc.kvc_decode_step(cache, kn_all[i], vn_all[i], t, q_first[i], G, scale, wl.rule, alpha, B,
+                                out_first, lse_first, s, mom, None, None, refresh=refresh, attn_unit0=0,
+                                attn_units=nkv, max_len=max_len, ws=ws)
+            if nl == 1:
+                return
+            if q_layers is None:
+                kvc.kvc_decode_groups(cache, q_rest[i], G, scale, wl.rule, alpha, nkv, nl - 1, nkv, out_rest,
+                                      lse_rest, s, refresh=refresh, max_len=max_len, ws=ws)
+                return
+            for l in range(1, nl):
+                kvc.kvc_decode_step(cache, None, None, t, q_layers[i][l - 1], G, scale, wl.rule, alpha, cap,
+                                    out_layers[l - 1], lse_layers[l - 1], s,
+                                    mom, None, None, refresh=refresh, attn_unit0=l * nkv, attn_units=nkv,
+                                    max_len=max_len, ws=ws)
     else:
         merges = [kvc.merge_desc(q, G, scale) for q in q_all] if wl.merge else None
 

@@ -9,6 +9,7 @@
 
 #include "kvc.h"
 #include "kvc_decode.h"
+#include "kvc_groups.h"
 #include "kvc_kernels.h"
 #include "kvc_laprox.h"
 
@@ -490,6 +491,95 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
                         size_t ws_bytes, void *stream) {
   return run_decode(cache, k_new, v_new, t, q, G, scale, 1, rule, alpha, budget, refresh, out, lse, s,
                     mom, merge, evict_out, attn_unit0, attn_units, max_len, ws, ws_bytes, stream);
+}
+
+int32_t kvc_decode_groups(const kvc_cache *cache, const void *q, int32_t G, float scale, int32_t rule,
+                          float alpha, int32_t refresh, int32_t unit0, int32_t n_groups, int32_t group_units,
+                          float *out, float *lse, float *s, int32_t max_len, void *ws, size_t ws_bytes,
+                          void *stream) {
+  const kvc_cache *c = cache;
+  const int st = validate_cache(c);
+  if (st) return st;
+  if (!valid_G(G)) return KVC_ERR_UNSUPPORTED;
+  if (!q || !out || !lse) return KVC_ERR_ARG;
+  if (!aligned16(q)) return KVC_ERR_ALIGN;
+  if (n_groups <= 0 || group_units <= 0 || unit0 < 0) return KVC_ERR_ARG;
+  const int64_t units64 = int64_t(n_groups) * group_units;
+  if (unit0 + units64 > c->units_per_scope) return KVC_ERR_ARG;
+  if (group_units * G > 64) return KVC_ERR_UNSUPPORTED;
+  const int units = int(units64);
+  if (rule < KVC_RULE_SINGLE || rule > KVC_RULE_EMA) return KVC_ERR_ARG;
+  if (refresh && !c->m) return KVC_ERR_ARG;
+  if (max_len > c->capacity) return KVC_ERR_CAPACITY;
+  if (max_len <= 0) max_len = c->capacity;
+  if (kvc::groups_score_lds_bytes(c->dtype, G, units) > (64u << 10)) return KVC_ERR_UNSUPPORTED;
+  if (!ws) return KVC_ERR_WORKSPACE;
+  const DecodeLayout d = decode_layout(c, G, units);
+  if (ws_bytes < d.total) return KVC_ERR_WORKSPACE;
+
+  kvc::StepArgs a{};
+  a.k = static_cast<char *>(c->k);
+  a.v = static_cast<char *>(c->v);
+  a.votes = c->votes;
+  a.pos = c->pos;
+  a.m = c->m;
+  a.len = c->len;
+  a.scope_stride = c->scope_stride;
+  a.unit_stride = c->unit_stride;
+  a.capacity = c->capacity;
+  a.n_scopes = c->n_scopes;
+  a.units = c->units_per_scope;
+  a.attn_unit0 = unit0;
+  a.attn_units = units;
+  a.append = 0;
+  a.t = 0;
+  a.q = static_cast<const char *>(q);
+  a.scale = double(scale);
+  a.out = out;
+  a.lse = lse;
+  a.status = at<int32_t>(ws, d.status);
+  a.partM = at<double>(ws, d.partM);
+  a.partZ = at<double>(ws, d.partZ);
+  a.partO = at<float>(ws, d.partO);
+  a.fac = at<float>(ws, d.fac);
+  a.subM = at<double>(ws, d.subM);
+  a.ews = at<float>(ws, d.ews);
+  a.ewsh = at<uint8_t>(ws, d.ewsh);
+  a.nsub_cap = d.nsub_cap;
+  a.row_bytes = kHD * (c->dtype == KVC_BF16 ? 2 : 4);
+  a.max_len = max_len;
+  // splits sized for the live-length bound, within what the workspace holds
+  const int CH = kvc::decode_chunk_tokens(c->dtype);
+  a.n_splits = std::min({split_count(c->n_scopes * units, ceil_div(max_len, CH)), d.n_splits, 64});
+
+  kvc::GroupsArgs g{};
+  g.n_scopes = c->n_scopes;
+  g.units = units;
+  g.group_units = group_units;
+  g.n_groups = n_groups;
+  g.capacity = c->capacity;
+  g.n_splits = a.n_splits;
+  g.nsub_cap = d.nsub_cap;
+  g.max_len = max_len;
+  g.len = c->len;
+  g.votes = c->votes;
+  g.m = c->m;
+  g.s = s;
+  g.out = out;
+  g.lse = lse;
+  g.partM = a.partM;
+  g.partZ = a.partZ;
+  g.partO = a.partO;
+  g.subM = a.subM;
+  g.ews = a.ews;
+  g.ewsh = a.ewsh;
+  g.rule = rule;
+  g.alpha = double(alpha);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (kvc::launch_decode_attention(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  if (kvc::launch_groups_epilogue(g, c->dtype, G, refresh != 0, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  return KVC_OK;
 }
 
 int32_t kvc_decode_plan(const kvc_cache *cache, int32_t G, int32_t step, int32_t merge, int32_t budget,

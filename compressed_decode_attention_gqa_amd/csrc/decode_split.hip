@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "kvc_epilogue.h"
+#include "kvc_groups.h"
 #include "kvc_stream.h"
 
 namespace kvc {
@@ -299,6 +300,30 @@ static hipError_t launch_split_g(const StepArgs &a, int G, hipStream_t st) {
 
 hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st) {
   return dtype == 0 ? launch_split_g<bf16_t>(a, G, st) : launch_split_g<float>(a, G, st);
+}
+
+template <typename T, int G>
+static hipError_t launch_attention_tg(const StepArgs &a, hipStream_t st) {
+  using Geo = UnitGeometry<T, G>;
+  const dim3 grid(a.n_splits, a.n_scopes * a.attn_units);
+  if (a.votes) hipLaunchKernelGGL((k_decode_split<T, G, true>), grid, dim3(Geo::NT), 0, st, a);
+  else hipLaunchKernelGGL((k_decode_split<T, G, false>), grid, dim3(Geo::NT), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_attention_g(const StepArgs &a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_attention_tg<T, 1>(a, st);
+    case 2: return launch_attention_tg<T, 2>(a, st);
+    case 4: return launch_attention_tg<T, 4>(a, st);
+    case 8: return launch_attention_tg<T, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_attention(const StepArgs &a, int dtype, int G, hipStream_t st) {
+  return dtype == 0 ? launch_attention_g<bf16_t>(a, G, st) : launch_attention_g<float>(a, G, st);
 }
 
 }  // namespace kvc

@@ -25,7 +25,7 @@ EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_ema_predict", "kvc_s
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
             "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
             "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step", "kvc_decode_step_noalloc",
-            "kvc_decode_workspace_size", "kvc_decode_plan",
+            "kvc_decode_workspace_size", "kvc_decode_plan", "kvc_decode_groups",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
             "kvc_keepkv_prefill_workspace_size", "kvc_keepkv_ema_init_workspace_size",
             "kvc_laprox_workspace_size",
@@ -80,6 +80,7 @@ _SIGS = {
     "kvc_laprox_score_marked": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P, _P, _I]),
     "kvc_decode_workspace_size": (_SZ, [_P, _I, _I]),
     "kvc_decode_plan": (_I, [_P, _I, _I, _I, _I, _I]),
+    "kvc_decode_groups": (_I, [_P, _P, _I, _F, _I, _F, _I, _I, _I, _I, _P, _P, _P, _I, _P, _SZ, _P]),
     "kvc_select_workspace_size": (_SZ, [_I, _I]),
     "kvc_compact_workspace_size": (_SZ, [_P]),
     "kvc_moment_evict_workspace_size": (_SZ, [_P]),
@@ -269,6 +270,16 @@ def kvc_decode_step(cache: Cache, k_new, v_new, t: int, q, G: int, scale: float,
         _ptr(out), _ptr(lse), _ptr(s), ctypes.byref(mom) if mom is not None else None,
         ctypes.byref(merge) if merge is not None else None, _ptr(evict_out), attn_unit0, attn_units, max_len,
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kvc_decode_groups(cache: Cache, q, G: int, scale: float, rule, alpha: float, unit0: int, n_groups: int,
+                      group_units: int, out, lse, s=None, refresh: bool = True, max_len: int = 0,
+                      ws: torch.Tensor = None, stream=None):
+    d = cache.desc()
+    rule = RULES.get(rule, rule)
+    _check("kvc_decode_groups", lib().kvc_decode_groups(
+        ctypes.byref(d), _ptr(q), G, scale, rule, alpha, int(refresh), unit0, n_groups, group_units,
+        _ptr(out), _ptr(lse), _ptr(s), max_len, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def kvc_decode_step_noalloc(cache: Cache, k_new, v_new, t: int, q, G: int, scale: float, rule, alpha: float,

@@ -368,6 +368,38 @@ int32_t kvc_decode_step(const kvc_cache *cache, const void *k_new, const void *v
                         int32_t attn_unit0, int32_t attn_units, int32_t max_len,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* kvc_decode_groups -- InertiaKV §3.1 (one slot set per sequence shared by
+ * every layer, the utility updated after every compressed layer) for the
+ * layers of a model-scope step that come after the one that evicted: n_groups
+ * consecutive attention groups of group_units units each, units
+ * [unit0, unit0 + n_groups * group_units) of every scope, attend over the live
+ * entries, score, and update the shared utility group after group, as
+ * n_groups calls of kvc_decode_step without append, flags or merge and with a
+ * budget no smaller than the live length (attn_unit0 = unit0 + j * group_units,
+ * attn_units = group_units, j = 0 .. n_groups - 1) would -- but in three
+ * launches for all the groups, with the utility chain in closed form:
+ *   single      m = s_{n-1}
+ *   cumulative  m = m + sum_j s_j
+ *   EMA         m = alpha^n m + sum_j (1 - alpha) alpha^(n-1-j) s_j
+ * evaluated in float64 and stored once as float32 (the calls it replaces
+ * store m after every group). s_j is group j's head-averaged score (the mean
+ * over its group_units * G heads of the vote-weighted attention weights).
+ * Nothing is appended, selected or moved; a scope's live length is whatever
+ * len holds. q: [n_scopes][n_groups * group_units][G][head_dim] in the cache
+ * dtype; out: the same shape, fp32; lse: [n_scopes][n_groups * group_units][G]
+ * fp32; s: [n_scopes][capacity] fp32 or NULL, receives the last group's scores
+ * (slots < len). refresh == 0 (a lazy step) attends only: m and s are left as
+ * they are. max_len (<= 0: capacity) sizes the launches; a longer device
+ * length is still covered. Workspace: kvc_decode_workspace_size(cache, G, 0)
+ * is enough. Errors: KVC_ERR_ARG for a unit range outside the scope, bad
+ * pointers or rule, or refresh without utilities; KVC_ERR_UNSUPPORTED for
+ * group_units * G > 64, or n_groups * group_units * G above 4096 (bf16 caches)
+ * or 2048 (fp32). */
+int32_t kvc_decode_groups(const kvc_cache *cache, const void *q, int32_t G, float scale, int32_t rule,
+                          float alpha, int32_t refresh, int32_t unit0, int32_t n_groups, int32_t group_units,
+                          float *out, float *lse, float *s, int32_t max_len, void *ws, size_t ws_bytes,
+                          void *stream);
+
 /* kvc_decode_plan -- the kernels a call with these shapes runs, without running
  * it: kvc_decode_step (step != 0, with this budget, merge != 0 for a call with a
  * merge descriptor) or kvc_decode_attn_score (step == 0; budget and merge

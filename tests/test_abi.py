@@ -97,6 +97,37 @@ def test_decode_plan_host_logic():
 
 
 @needs_lib
+def test_decode_groups_host_checks():
+    """kvc_decode_groups rejects a unit range outside the scope, group sizes beyond one call's
+    head limit, bad rules, refresh without utilities, null or misaligned pointers and a short
+    workspace before enqueuing anything."""
+    L = kvc.lib()
+
+    def call(c, q=0x6000, G=4, rule=2, refresh=1, unit0=2, n_groups=3, gu=2, out=0x7000, max_len=0, ws=0x9000,
+             wsb=1 << 30):
+        return L.kvc_decode_groups(ctypes.byref(c), q, G, 0.1, rule, 0.9, refresh, unit0, n_groups, gu, out, 0x8000,
+                                   None, max_len, ws, wsb, None)
+    c = _fake_cache(units_per_scope=8, unit_stride=100, scope_stride=800)
+    assert call(c, unit0=3) == -1                 # 3 + 3 * 2 > 8 units
+    assert call(c, n_groups=0) == -1
+    assert call(c, gu=0) == -1
+    assert call(c, unit0=-1) == -1
+    assert call(c, G=3) == -3
+    assert call(c, G=8, gu=16, n_groups=0) == -1
+    c1 = _fake_cache(units_per_scope=20, unit_stride=100, scope_stride=2000)
+    assert call(c1, G=8, unit0=0, n_groups=1, gu=9) == -3   # 72 heads in one group
+    assert call(c, rule=7) == -1
+    assert call(c, q=None) == -1
+    assert call(c, q=0x6004) == -5
+    assert call(c, out=None) == -1
+    assert call(c, max_len=101) == -4
+    assert call(c, ws=None) == -6
+    assert call(c, wsb=16) == -6
+    nm = _fake_cache(units_per_scope=8, unit_stride=100, scope_stride=800, m=None)
+    assert call(nm) == -1
+
+
+@needs_lib
 def test_other_entry_points_reject_bad_arguments():
     L = kvc.lib()
     assert L.kvc_ema_update(None, 0x10, 0x20, 1, 10, 2, 0.9, None) == -1

@@ -317,17 +317,18 @@ def test_merge_keeps_the_reference_output():
 C3 = synth.WORKLOADS["c3_llama8b_model_16k"]
 
 
-def _c3_step(run, step, q, kn, vn, refresh, max_len=None, later_within_budget=False):
+def _c3_step(run, step, q, kn, vn, refresh, max_len=None, later_within_budget=False, fused=False):
     """One decode step of a model-scope cache: layer by layer, each layer's KV heads attend,
     score (mean over the layer's query heads), update the shared utility and evict; the new
     token's rows of every layer are appended by the first layer's call. later_within_budget:
     the layers after the first are called with budget = capacity (they cannot evict, the first
-    layer having evicted to the budget), which lets the library skip their finish launch."""
+    layer having evicted to the budget), which lets the library skip their finish launch.
+    fused: the first layer's call, then one kvc_decode_groups call for all the later layers."""
     wl = run.wl
     S = wl.n_scopes
     out_l = torch.empty((S, wl.n_kv, run.G, wl.d), device="cuda")
     lse_l = torch.empty((S, wl.n_kv, run.G), device="cuda")
-    for l in range(wl.n_layers):
+    for l in range(1 if fused else wl.n_layers):
         u0 = l * wl.n_kv
         kvc.kvc_decode_step(run.cache, kn if l == 0 else None, vn if l == 0 else None, run.t,
                             q[:, u0:u0 + wl.n_kv].contiguous(), run.G, run.scale, wl.rule, run.alpha,
@@ -336,6 +337,15 @@ def _c3_step(run, step, q, kn, vn, refresh, max_len=None, later_within_budget=Fa
                             attn_unit0=u0, attn_units=wl.n_kv, max_len=max_len or 0, ws=run.ws)
         run.out[:, u0:u0 + wl.n_kv] = out_l
         run.lse[:, u0:u0 + wl.n_kv] = lse_l
+    if fused and wl.n_layers > 1:
+        nu = (wl.n_layers - 1) * wl.n_kv
+        out_g = torch.empty((S, nu, run.G, wl.d), device="cuda")
+        lse_g = torch.empty((S, nu, run.G), device="cuda")
+        kvc.kvc_decode_groups(run.cache, q[:, wl.n_kv:].contiguous(), run.G, run.scale, wl.rule, run.alpha,
+                              wl.n_kv, wl.n_layers - 1, wl.n_kv, out_g, lse_g, run.s, refresh=refresh,
+                              max_len=max_len or 0, ws=run.ws)
+        run.out[:, wl.n_kv:] = out_g
+        run.lse[:, wl.n_kv:] = lse_g
     run.t += 1
 
 
@@ -379,9 +389,11 @@ def _c3_check(run, scopes, pre, post, q, kn, vn, t, refresh):
     return worst
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("lazy", [0, 3])
-def test_decode_step_c3_model_scope_reduced(lazy):
-    """One slot set per sequence shared by every layer: score and evict after each layer."""
+def test_decode_step_c3_model_scope_reduced(lazy, fused):
+    """One slot set per sequence shared by every layer: score and evict after each layer
+    (fused: the layers after the first in one kvc_decode_groups call, utility chain in closed form)."""
     wl = C3.scaled(n_layers=4, batch=2, n_kv=3, context=700, budget=70, steps=7, lazy_refresh=lazy)
     run = DeviceRun(wl)
     worst = 0.0
@@ -391,11 +403,51 @@ def test_decode_step_c3_model_scope_reduced(lazy):
         scopes = list(range(wl.n_scopes))
         pre = run.snapshot(scopes)
         t = run.t
-        _c3_step(run, step, q, kn, vn, refresh)
+        _c3_step(run, step, q, kn, vn, refresh, fused=fused)
         torch.cuda.synchronize()
         worst = max(worst, _c3_check(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, refresh))
     assert kvc.kvc_workspace_status(run.ws) == 0
-    _say("c3 reduced lazy=%d: max rel dm %.2e" % (lazy, worst))
+    _say("c3 reduced lazy=%d fused=%d: max rel dm %.2e" % (lazy, fused, worst))
+
+
+@pytest.mark.parametrize("dtype,G,rule,votes", [("bf16", 4, "ema", False), ("f32", 2, "cumulative", True),
+                                                ("bf16", 8, "single", False), ("bf16", 1, "ema", True)])
+def test_decode_groups_matches_per_layer_calls(dtype, G, rule, votes):
+    """kvc_decode_groups against the per-layer calls it stands for (budget = capacity, so no
+    eviction), on the same state: outputs and lse within float32 summation-order differences,
+    the last group's scores, and the utility chain (float64 closed form stored once, against a
+    float32 store after every layer) within 1e-6 relative."""
+    _say("groups vs per layer", dtype, G, rule, votes)
+    wl = C3.scaled(n_layers=6, batch=3, n_kv=2, context=500, budget=500, steps=1, dtype=dtype, G=G, rule=rule,
+                   prior_votes=votes, key_scales=dtype == "bf16")
+    runs = [DeviceRun(wl), DeviceRun(wl)]
+    q, _, _ = runs[0].inputs(1)
+    nk, S, cap = wl.n_kv, wl.n_scopes, runs[0].cache.capacity
+    unit0, n_groups = nk, wl.n_layers - 1
+    qg = q[:, unit0:].contiguous()
+    outs = [torch.empty((S, n_groups * nk, G, wl.d), device="cuda") for _ in range(2)]
+    lses = [torch.empty((S, n_groups * nk, G), device="cuda") for _ in range(2)]
+    r0 = runs[0]
+    for j in range(n_groups):
+        u0 = unit0 + j * nk
+        o = torch.empty((S, nk, G, wl.d), device="cuda")
+        ls = torch.empty((S, nk, G), device="cuda")
+        kvc.kvc_decode_step(r0.cache, None, None, r0.t, q[:, u0:u0 + nk].contiguous(), G, r0.scale, rule, r0.alpha,
+                            cap, o, ls, r0.s, None, None, None, attn_unit0=u0, attn_units=nk, ws=r0.ws)
+        outs[0][:, j * nk:(j + 1) * nk] = o
+        lses[0][:, j * nk:(j + 1) * nk] = ls
+    r1 = runs[1]
+    kvc.kvc_decode_groups(r1.cache, qg, G, r1.scale, rule, r1.alpha, unit0, n_groups, nk, outs[1], lses[1], r1.s,
+                          ws=r1.ws)
+    torch.cuda.synchronize()
+    oa, ob = outs[0].double(), outs[1].double()
+    assert ((oa - ob).abs() <= 1e-6 * oa.abs().amax(dim=-1, keepdim=True) + 1e-30).all()
+    assert ((lses[0].double() - lses[1].double()).abs() <= 1e-6 * lses[0].double().abs() + 1e-6).all()
+    L = int(r0.cache.length[0])
+    for x, y in ((r0.s[:, :L], r1.s[:, :L]), (r0.cache.m[:, :L], r1.cache.m[:, :L])):
+        xd, yd = x.double(), y.double()
+        assert ((xd - yd).abs() <= 1e-6 * xd.abs() + 1e-30).all()
+    assert kvc.kvc_workspace_status(r1.ws) == 0
 
 
 def test_model_scope_calls_that_cannot_evict_leave_the_same_state():
@@ -448,9 +500,11 @@ def test_entry_points_compose_to_the_step(context, budget, steps, n_kv):
     _say("composed", rep)
 
 
-def test_decode_step_c3_full_size_sampled():
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_step_c3_full_size_sampled(fused):
     """16 sequences x 32 layers x 8 KV heads sharing one slot set per sequence, 16384 -> 1638:
-    the bulk first step and two steady steps, one sequence checked against the oracle."""
+    the bulk first step and two steady steps, one sequence checked against the oracle (fused:
+    layers 2-32 in one kvc_decode_groups call)."""
     run = DeviceRun(C3)
     for step in range(1, 4):
         q, kn, vn = run.inputs(step)
@@ -458,11 +512,11 @@ def test_decode_step_c3_full_size_sampled():
         if scopes:
             pre = run.snapshot(scopes)
         t = run.t
-        _c3_step(run, step, q, kn, vn, True)
+        _c3_step(run, step, q, kn, vn, True, fused=fused)
         if scopes:
             torch.cuda.synchronize()
             worst = _c3_check(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, True)
-            _say("c3 full step %d: max rel dm %.2e" % (step, worst))
+            _say("c3 full step %d fused=%d: max rel dm %.2e" % (step, fused, worst))
     assert int(run.cache.length.min()) == C3.budget == int(run.cache.length.max())
     assert kvc.kvc_workspace_status(run.ws) == 0
 
