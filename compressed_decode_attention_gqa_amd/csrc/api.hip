@@ -577,6 +577,26 @@ int32_t kvc_decode_groups(const kvc_cache *cache, const void *q, int32_t G, floa
   g.alpha = double(alpha);
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  // One workgroup per unit (the per-scope kernel's streaming, weights kept in LDS) when a
+  // unit's per-token state for max_len tokens fits in LDS and the per-token weight sums
+  // fit where the split path keeps its per-token weights; otherwise split-K attention.
+  const int64_t wstride = (int64_t(max_len) + 31) / 32 * 32;
+  const bool per_unit =
+      kvc::decode_unit_groups_lds_bytes(c->dtype, G, max_len, c->votes != nullptr) <= device_lds_per_block() &&
+      size_t(c->n_scopes) * units * wstride * sizeof(double) <= d.m64 - d.ews;
+  if (per_unit) {
+    a.mode = 0;
+    a.refresh = refresh ? 1 : 0;
+    a.n_splits = 1;
+    a.lds_len = max_len;
+    a.wsum = at<double>(ws, d.ews);
+    a.wsum_stride = int32_t(wstride);
+    g.wsum = a.wsum;
+    g.wsum_stride = a.wsum_stride;
+    if (kvc::launch_decode_unit_groups(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+    if (refresh && kvc::launch_groups_wscore(g, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
+    return KVC_OK;
+  }
   if (kvc::launch_decode_attention(a, c->dtype, G, hs) != hipSuccess) return KVC_ERR_DEVICE;
   if (kvc::launch_groups_epilogue(g, c->dtype, G, refresh != 0, hs) != hipSuccess) return KVC_ERR_DEVICE;
   return KVC_OK;

@@ -107,13 +107,28 @@ __global__ __launch_bounds__(WG) void k_groups_score(const GroupsArgs a) {
       const int cl = tok / CH;
       for (int j = part; j < n; j += PARTS) {
         double acc = 0.0;
-        for (int u = j * gsz; u < (j + 1) * gsz; ++u) {
+        // UB units' weights loaded before any is used (their loads overlap), then summed in order
+        constexpr int UB = G >= 4 ? 4 : 8 / G;
+        for (int u0 = j * gsz; u0 < (j + 1) * gsz; u0 += UB) {
+          float ev[UB][G];
+          int sv[UB][G];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const int64_t wi = ((int64_t(gu0) + u) * G + g) * cap + i;
-            const int shv = a.ewsh[wi];
-            const double x = double(a.ews[wi]) * fac[(u * G + g) * NSC + cl];
-            acc += shv ? x * shift_scale(shv) : x;
+          for (int uu = 0; uu < UB; ++uu)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const int u = min(u0 + uu, (j + 1) * gsz - 1);
+              const int64_t wi = ((int64_t(gu0) + u) * G + g) * cap + i;
+              ev[uu][g] = a.ews[wi];
+              sv[uu][g] = a.ewsh[wi];
+            }
+#pragma unroll
+          for (int uu = 0; uu < UB; ++uu) {
+            if (u0 + uu >= (j + 1) * gsz) break;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const double x = double(ev[uu][g]) * fac[((u0 + uu) * G + g) * NSC + cl];
+              acc += sv[uu][g] ? x * shift_scale(sv[uu][g]) : x;
+            }
           }
         }
         const double sj = acc * inv_heads;
@@ -134,6 +149,61 @@ __global__ __launch_bounds__(WG) void k_groups_score(const GroupsArgs a) {
       const double pv = a.votes ? double(a.votes[sc + i]) : 1.0;
       t *= pv;
       l *= pv;
+      const double mo = double(a.m[sc + i]);
+      const double mv = a.rule == 0 ? l : a.rule == 1 ? mo + t : pow(alpha, double(n)) * mo + t;
+      a.m[sc + i] = float(mv);
+      if (a.s) a.s[sc + i] = float(l);
+    }
+  }
+}
+
+// The same chain over the per-unit kernel's weight sums: s_j(i) = sum over the
+// group's units of wsum[unit][i] / (group_units * G) (votes already applied).
+__global__ __launch_bounds__(WG) void k_groups_wscore(const GroupsArgs a, int G) {
+  constexpr int CT = GROUPS_CT, PARTS = GROUPS_PARTS;
+  __shared__ double red_t[PARTS][CT], red_l[PARTS][CT];
+  const int tid = threadIdx.x, scope = blockIdx.y;
+  const int cap = a.capacity;
+  int L = a.len[scope];
+  if (L > cap || L > a.max_len) L = 0;   // the per-unit kernel wrote nothing (status reported there)
+  const int64_t sc = int64_t(scope) * cap;
+  const int64_t gu0 = int64_t(scope) * a.units;
+  const int tok = tid % CT, part = tid / CT;
+  const int n = a.n_groups, gsz = a.group_units;
+  const double alpha = a.alpha;
+  const double inv_heads = 1.0 / double(gsz * G);
+  for (int i0 = blockIdx.x * CT; i0 < L; i0 += gridDim.x * CT) {
+    __syncthreads();   // the previous chunk's reads of red are done
+    const int i = i0 + tok;
+    double tot = 0.0, last = 0.0;
+    if (i < L) {
+      for (int j = part; j < n; j += PARTS) {
+        const double *w = a.wsum + (gu0 + int64_t(j) * gsz) * a.wsum_stride + i;
+        double acc = 0.0;
+        constexpr int UB = 8;
+        for (int u0 = 0; u0 < gsz; u0 += UB) {
+          double x[UB];
+#pragma unroll
+          for (int uu = 0; uu < UB; ++uu) x[uu] = w[int64_t(min(u0 + uu, gsz - 1)) * a.wsum_stride];
+#pragma unroll
+          for (int uu = 0; uu < UB; ++uu)
+            if (u0 + uu < gsz) acc += x[uu];
+        }
+        const double sj = acc * inv_heads;
+        if (j == n - 1) last = sj;
+        tot += (a.rule == 2 ? (1.0 - alpha) * pow(alpha, double(n - 1 - j)) : 1.0) * sj;
+      }
+    }
+    red_t[part][tok] = tot;
+    red_l[part][tok] = last;
+    __syncthreads();
+    if (part == 0 && i < L) {
+      double t = 0.0, l = 0.0;
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) {
+        t += red_t[p][tok];
+        l += red_l[p][tok];
+      }
       const double mo = double(a.m[sc + i]);
       const double mv = a.rule == 0 ? l : a.rule == 1 ? mo + t : pow(alpha, double(n)) * mo + t;
       a.m[sc + i] = float(mv);
@@ -166,6 +236,12 @@ int groups_score_chunk(int) { return GROUPS_CT; }
 
 size_t groups_score_lds_bytes(int dtype, int G, int units) {
   return size_t(units) * G * (GROUPS_CT / decode_chunk_tokens(dtype)) * sizeof(double);
+}
+
+hipError_t launch_groups_wscore(const GroupsArgs &g, int G, hipStream_t st) {
+  const int n_chunks = std::max(1, (g.max_len + GROUPS_CT - 1) / GROUPS_CT);
+  hipLaunchKernelGGL(k_groups_wscore, dim3(n_chunks, g.n_scopes), dim3(WG), 0, st, g, G);
+  return hipGetLastError();
 }
 
 hipError_t launch_groups_epilogue(const GroupsArgs &g, int dtype, int G, bool score, hipStream_t st) {

@@ -34,6 +34,7 @@
 // LDS only, so those loads (and the streaming's last, unused prefetches) stay
 // in flight across them; no global location is written by one thread and
 // read or rewritten by another.
+#include <algorithm>
 #include <type_traits>
 
 #include "kvc_epilogue.h"
@@ -85,9 +86,18 @@ __device__ __forceinline__ uint64_t token_shifts(const uint8_t *sh, int i) {
   else return *reinterpret_cast<const uint64_t *>(sh + 8 * i);
 }
 
-template <typename T, int G>
+// Waves and prefetch depth of the per-unit (groups) kernel: four waves at depth
+// two, so two workgroups share a CU and one's epilogue overlaps the other's
+// streaming; eight-head groups need all of a SIMD's registers for one wave and
+// keep the default geometry (four waves, one workgroup per CU).
+template <int G>
+struct GrpGeo {
+  static constexpr int NW = G >= 8 ? 0 : 4, PF = G >= 8 ? 0 : 2, MINB = G >= 8 ? 1 : 2;
+};
+
+template <typename T, int G, int NWO = 0, int PFO = 0>
 struct UnitLds {
-  using Geo = UnitGeometry<T, G>;
+  using Geo = UnitGeometry<T, G, NWO, PFO>;
   union {
     float w[Geo::NW][Geo::UNR][Geo::TPI][G];      // streaming: weights for the value sums
     struct {
@@ -104,33 +114,47 @@ struct UnitLds {
   int next_sub;   // the next sub-chunk to hand out
 };
 
-template <typename T>
+template <typename T, int NWO, int PFO>
 static size_t unit_static_lds(int G) {
   switch (G) {
-    case 1: return sizeof(UnitLds<T, 1>);
-    case 2: return sizeof(UnitLds<T, 2>);
-    case 4: return sizeof(UnitLds<T, 4>);
-    default: return sizeof(UnitLds<T, 8>);
+    case 1: return sizeof(UnitLds<T, 1, NWO, PFO>);
+    case 2: return sizeof(UnitLds<T, 2, NWO, PFO>);
+    case 4: return sizeof(UnitLds<T, 4, NWO, PFO>);
+    default: return sizeof(UnitLds<T, 8, NWO, PFO>);
   }
 }
 
 size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes) {
-  const size_t st = dtype == 0 ? unit_static_lds<bf16_t>(G) : unit_static_lds<float>(G);
+  const size_t st = dtype == 0 ? unit_static_lds<bf16_t, 0, 0>(G) : unit_static_lds<float, 0, 0>(G);
+  return st + unit_lds_layout(decode_unit_chunk_tokens(dtype), G, lds_len, votes).total;
+}
+
+size_t decode_unit_groups_lds_bytes(int dtype, int G, int lds_len, bool votes) {
+  // the static part is largest for the four-wave geometry at every G
+  const size_t st = dtype == 0 ? std::max(unit_static_lds<bf16_t, 4, 2>(G), unit_static_lds<bf16_t, 0, 0>(G))
+                               : std::max(unit_static_lds<float, 4, 2>(G), unit_static_lds<float, 0, 0>(G));
   return st + unit_lds_layout(decode_unit_chunk_tokens(dtype), G, lds_len, votes).total;
 }
 
 
-template <typename T, int G, bool VOTES>
-__global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(const StepArgs a) {
+// GRP: one workgroup per attention unit of every scope (blockIdx.x = scope *
+// attn_units + unit), attending only, with no append: o, lse and, when scores are
+// refreshed, the unit's per-token sum over its heads of the vote-weighted
+// attention weights into wsum (the groups score kernel then averages them over
+// each group's units and chains the utility updates).
+template <typename T, int G, bool VOTES, bool GRP = false>
+__global__ __launch_bounds__((UnitGeometry<T, G, GRP ? GrpGeo<G>::NW : 0, GRP ? GrpGeo<G>::PF : 0>::NT),
+                             GRP ? GrpGeo<G>::MINB : 1)
+void k_decode_unit(const StepArgs a) {
   using TR = ElemTraits<T>;
-  using Geo = UnitGeometry<T, G>;
+  using Geo = UnitGeometry<T, G, GRP ? GrpGeo<G>::NW : 0, GRP ? GrpGeo<G>::PF : 0>;
   constexpr int EPV = Geo::EPV, LPT = Geo::LPT, TPI = Geo::TPI, UNR = Geo::UNR;
   constexpr int CHW = Geo::CHW, PF = Geo::PF, NW = Geo::NW, NT = Geo::NT, RB = Geo::RB;
   constexpr int D = LPT / G;                         // lanes sharing one (token, head) logit
   constexpr int ITL = (UNR + D - 1) / D;             // weights a lane forms per sub-chunk
   static_assert(NW * G <= 64, "the combine runs in one wave");
 
-  __shared__ UnitLds<T, G> sh;
+  __shared__ UnitLds<T, G, GRP ? GrpGeo<G>::NW : 0, GRP ? GrpGeo<G>::PF : 0> sh;
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int lds_len = a.lds_len;
   const UnitLdsLayout lay = unit_lds_layout(CHW, G, lds_len, VOTES);
@@ -143,8 +167,9 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   uint8_t *s_lds = reinterpret_cast<uint8_t *>(dyn + lay.sh);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int scope = blockIdx.x, gu = scope;
-  const int unit = a.attn_unit0;
+  const int gu = blockIdx.x;
+  const int scope = GRP ? gu / a.attn_units : gu;
+  const int unit = GRP ? a.attn_unit0 + (gu - scope * a.attn_units) : a.attn_unit0;
   const int cap = a.capacity;
   const int64_t sc = int64_t(scope) * cap;
   int L = a.len[scope] + a.append;
@@ -152,7 +177,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   if (overflow) L = 0;
   const int Lold = L - (L > 0 ? a.append : 0);
 
-  UnitStream<T, VOTES> W;
+  UnitStream<T, VOTES, !GRP> W;
   {
     const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(unit) * a.unit_stride;
     W.Kb = a.k + row0 * RB;
@@ -193,7 +218,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   double Mrun = -INFINITY;
 
   const int nsub = L > 0 ? (L + CHW - 1) / CHW : 0;
-  const bool rev = (a.t & 1) != 0;   // walk order of this step
+  const bool rev = !GRP && (a.t & 1) != 0;   // walk order of this step
   if (tid == 0) sh.next_sub = NW * PF;
   __syncthreads();
   u32x4 kr[PF][UNR], vr[PF][UNR];
@@ -215,7 +240,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
         const bool tail = (c + 1) * CHW > L;
         // scope arrays of this sub-chunk into LDS
         if (lane < CHW) {
-          m_lds[c * CHW + lane] = double(mv[s]);
+          if (!GRP) m_lds[c * CHW + lane] = double(mv[s]);
           if (VOTES) v_lds[c * CHW + lane] = vv[s];
         }
         double lg[UNR];
@@ -314,7 +339,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   // other waves may still stream): its share of the moment sums, the last live row
   const bool step = a.mode != 0;
   const int k = step ? max(0, L - a.budget) : 0;
-  const bool fold = !overflow && step && k == 1 && a.mom_S != nullptr;
+  const bool fold = !GRP && !overflow && step && k == 1 && a.mom_S != nullptr;
   const int64_t mu = int64_t(scope) * a.units + unit;
   float4 Sreg[Geo::NS4];
   float skv = 0.f;
@@ -330,7 +355,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   const int lastc = tid % NV;
   const bool lastK = tid < NV, lastV = tid >= NV && tid < 2 * NV;
   u32x4 lastrow = u32x4(0u);
-  if (L > 0 && (lastK || lastV)) {
+  if (!GRP && L > 0 && (lastK || lastV)) {
     const char *src = a.append ? (lastK ? W.Kn : W.Vn) : (lastK ? W.Kb : W.Vb) + int64_t(L - 1) * RB;
     lastrow = ld16(src + 16 * lastc);
   }
@@ -366,7 +391,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   }
 
   int last_pos = a.t;
-  if (!a.append && L > 0) last_pos = a.pos[sc + L - 1];
+  if (!GRP && !a.append && L > 0) last_pos = a.pos[sc + L - 1];
 
   // ---- the head maxima M (over the waves' running maxima) and the normalisers
   // Z = sum_c z_c exp(m_c - M) in a fixed order: thread t takes the (sub-chunk,
@@ -418,6 +443,26 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_unit(con
   double izr[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) izr[g] = sh.ep.iZ[g];
+
+  if constexpr (GRP) {
+    // the unit's per-token weight sums (the score's numerator over this unit's heads)
+    if (a.refresh) {
+      double *wrow = a.wsum + int64_t(gu) * a.wsum_stride;
+      for (int i = tid; i < L; i += NT) {
+        const int c = i / CHW;
+        const uint64_t shw = token_shifts<G>(s_lds, i);
+        double acc = 0.0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const double x = double(e_lds[g * ld + i]) * (f_lds[c * G + g] * izr[g]);
+          acc += shw == 0 ? x : x * shift_scale(int((shw >> (8 * g)) & 255u));
+        }
+        if (VOTES) acc *= double(v_lds[i]);
+        wrow[i] = acc;
+      }
+    }
+    return;
+  }
 
   // ---- score, utility; per thread the smallest (m, slot) and how many slots hold that m
   const double inv_heads = 1.0 / double(G);
@@ -616,6 +661,34 @@ static hipError_t launch_unit_g(const StepArgs &a, int G, hipStream_t st) {
 
 hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st) {
   return dtype == 0 ? launch_unit_g<bf16_t>(a, G, st) : launch_unit_g<float>(a, G, st);
+}
+
+template <typename T, int G, bool VOTES>
+static hipError_t launch_unit_groups_tgv(const StepArgs &a, hipStream_t st) {
+  using Geo = UnitGeometry<T, G, GrpGeo<G>::NW, GrpGeo<G>::PF>;
+  const size_t dyn = unit_lds_layout(Geo::CHW, G, a.lds_len, VOTES).total;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_decode_unit<T, G, VOTES, true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_decode_unit<T, G, VOTES, true>), dim3(a.n_scopes * a.attn_units), dim3(Geo::NT), dyn, st,
+                     a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_unit_groups_g(const StepArgs &a, int G, hipStream_t st) {
+  const bool v = a.votes != nullptr;
+  switch (G) {
+    case 1: return v ? launch_unit_groups_tgv<T, 1, true>(a, st) : launch_unit_groups_tgv<T, 1, false>(a, st);
+    case 2: return v ? launch_unit_groups_tgv<T, 2, true>(a, st) : launch_unit_groups_tgv<T, 2, false>(a, st);
+    case 4: return v ? launch_unit_groups_tgv<T, 4, true>(a, st) : launch_unit_groups_tgv<T, 4, false>(a, st);
+    case 8: return v ? launch_unit_groups_tgv<T, 8, true>(a, st) : launch_unit_groups_tgv<T, 8, false>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_unit_groups(const StepArgs &a, int dtype, int G, hipStream_t st) {
+  return dtype == 0 ? launch_unit_groups_g<bf16_t>(a, G, st) : launch_unit_groups_g<float>(a, G, st);
 }
 
 }  // namespace kvc

@@ -81,14 +81,22 @@ struct StepArgs {
   uint64_t *cand_key;       // orderable float64 utility of each chunk's lowest entry
   int32_t *cand_slot, *cand_pos;
   BulkScope *bulk;   // non-null: scopes evicting k > 1 stop after the utility update
+  // per-unit kernel over attention groups: per-token head-summed attention weights
+  // (vote-weighted) of unit gu at wsum[gu * wsum_stride + i]
+  double *wsum;
+  int32_t wsum_stride;
 };
 
 int decode_chunk_tokens(int dtype);
 int decode_unit_chunk_tokens(int dtype);
 hipError_t launch_decode(const StepArgs &a, int dtype, int G, hipStream_t st);
 hipError_t launch_decode_unit(const StepArgs &a, int dtype, int G, hipStream_t st);
+// The per-scope kernel with one workgroup per attention unit of every scope
+// (a.attn_units of them), attending only: o, lse and the per-token weight sums.
+hipError_t launch_decode_unit_groups(const StepArgs &a, int dtype, int G, hipStream_t st);
 // LDS (static + dynamic) of the per-scope kernel for lds_len live tokens
 size_t decode_unit_lds_bytes(int dtype, int G, int lds_len, bool votes);
+size_t decode_unit_groups_lds_bytes(int dtype, int G, int lds_len, bool votes);
 // Device-wide select -> flags -> lists -> fold -> moves for the scopes the
 // epilogue handed over (BulkScope::k > 1).
 hipError_t launch_bulk(const StepArgs &a, const BulkArgs &b, int dtype, hipStream_t st);

@@ -30,6 +30,7 @@ struct ScoreLds {
   double fac[SCORE_FAC_MAX];
   double pm[SCORE_PAIR_MAX];   // split maxima; then the splits' output weights exp(pm - M) / Z
   double pz[SCORE_PAIR_MAX];
+  double red[WG];              // per-(part, token) head sums when a chunk has fewer tokens than threads
   uint64_t wkey[WG / 64];
   int wslot[WG / 64], wpos[WG / 64];
 };
@@ -98,6 +99,10 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
   const uint8_t *ewsh = a.ewsh + int64_t(gu0) * G * cap;
   double *m64 = (step && k > 1 && a.m64) ? a.m64 + sc : nullptr;
   const int chunk = a.score_chunk;
+  // threads per token (a power of two): the units of a token are split over them when the
+  // chunk has fewer tokens than threads and there are units to split
+  int parts = 1;
+  while (parts < Ua && chunk * parts * 2 <= WG) parts *= 2;
 
   // per attention head M and Z over the split partials (staged in LDS when they fit)
   const int ns = a.n_splits, P = H * ns;
@@ -169,6 +174,26 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
       }
     }
     __syncthreads();
+    // a chunk of fewer tokens than threads: thread (token t, part p) sums the units p,
+    // p + parts, ... of token i0 + t; the parts are added in order below
+    if (score && parts > 1) {
+      const int span = WG / parts, i = i0 + tid % span, p = tid / span;
+      double acc = 0.0;
+      if (i < i1) {
+        const double *f = sh.fac + (i / CH - c0) * H;
+        for (int ua = p; ua < Ua; ua += parts) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const int64_t wi = (int64_t(ua) * G + g) * cap + i;
+            const int shv = ewsh[wi];
+            const double x = double(ews[wi]) * f[ua * G + g];
+            acc += shv ? x * shift_scale(shv) : x;
+          }
+        }
+      }
+      sh.red[tid] = acc;
+      __syncthreads();
+    }
     uint64_t best = ~0ull;
     uint32_t bpos = 0xffffffffu;
     int bslot = 0x7fffffff;
@@ -177,15 +202,19 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
       double mval = 0.0;
       if (score) {
         const int pv = isnew ? 1 : (a.votes ? a.votes[sc + i] : 1);
-        const double *f = sh.fac + (i / CH - c0) * H;
         double acc = 0.0;
-        for (int ua = 0; ua < Ua; ++ua) {
+        if (parts > 1) {
+          for (int p = 0; p < parts; ++p) acc += sh.red[p * (WG / parts) + tid];
+        } else {
+          const double *f = sh.fac + (i / CH - c0) * H;
+          for (int ua = 0; ua < Ua; ++ua) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const int64_t wi = (int64_t(ua) * G + g) * cap + i;
-            const int shv = ewsh[wi];
-            const double x = double(ews[wi]) * f[ua * G + g];
-            acc += shv ? x * shift_scale(shv) : x;
+            for (int g = 0; g < G; ++g) {
+              const int64_t wi = (int64_t(ua) * G + g) * cap + i;
+              const int shv = ewsh[wi];
+              const double x = double(ews[wi]) * f[ua * G + g];
+              acc += shv ? x * shift_scale(shv) : x;
+            }
           }
         }
         const double sv = double(pv) * acc * inv_heads;

@@ -23,6 +23,8 @@ struct GroupsArgs {
   const double *subM;
   const float *ews;
   const uint8_t *ewsh;
+  const double *wsum;     // per-unit kernel path: per-token head sums [gu][wsum_stride] (null: split path)
+  int32_t wsum_stride;
   int32_t rule;
   double alpha;
 };
@@ -36,5 +38,8 @@ hipError_t launch_decode_attention(const StepArgs &a, int dtype, int G, hipStrea
 // Per attention head: M, Z, lse and the output over the split partials; then
 // (score) the groups' scores and the closed-form utility update.
 hipError_t launch_groups_epilogue(const GroupsArgs &g, int dtype, int G, bool score, hipStream_t st);
+// After the per-unit kernel (which wrote o, lse and wsum): the groups' scores and
+// the closed-form utility update.
+hipError_t launch_groups_wscore(const GroupsArgs &g, int G, hipStream_t st);
 
 }  // namespace kvc

@@ -8,16 +8,17 @@ namespace kvc {
 
 // Eight waves (two per SIMD, at most 256 registers each) up to four heads per
 // group; eight heads need more query and accumulator registers than that and
-// run four waves with deeper prefetch.
-template <typename T, int G = 1>
+// run four waves with deeper prefetch. NWO, PFO (non-zero) set the waves and the
+// prefetch depth instead (four waves at depth two: two workgroups per CU).
+template <typename T, int G = 1, int NWO = 0, int PFO = 0>
 struct UnitGeometry {
   static constexpr int EPV = ElemTraits<T>::EPV;
   static constexpr int LPT = HD / EPV;     // lanes per token row
   static constexpr int TPI = 64 / LPT;     // tokens per wave iteration
   static constexpr int UNR = 4;            // iterations per sub-chunk
   static constexpr int CHW = TPI * UNR;    // tokens per sub-chunk
-  static constexpr int NW = G >= 8 ? 4 : 8;   // waves
-  static constexpr int PF = 16 / NW;       // sub-chunks of loads in flight per wave
+  static constexpr int NW = NWO ? NWO : G >= 8 ? 4 : 8;   // waves
+  static constexpr int PF = PFO ? PFO : 16 / NW;         // sub-chunks of loads in flight per wave
   // (Waves 0-3 finish streaming well before waves 4-7: a SIMD's issue
   // arbiter favours the older of its two waves. Giving them a larger share
   // of sub-chunks moves the imbalance without shortening the makespan.)

@@ -410,17 +410,21 @@ def test_decode_step_c3_model_scope_reduced(lazy, fused):
     _say("c3 reduced lazy=%d fused=%d: max rel dm %.2e" % (lazy, fused, worst))
 
 
+@pytest.mark.parametrize("path", ["per_unit", "split"])
 @pytest.mark.parametrize("dtype,G,rule,votes", [("bf16", 4, "ema", False), ("f32", 2, "cumulative", True),
                                                 ("bf16", 8, "single", False), ("bf16", 1, "ema", True)])
-def test_decode_groups_matches_per_layer_calls(dtype, G, rule, votes):
+def test_decode_groups_matches_per_layer_calls(dtype, G, rule, votes, path):
     """kvc_decode_groups against the per-layer calls it stands for (budget = capacity, so no
     eviction), on the same state: outputs and lse within float32 summation-order differences,
     the last group's scores, and the utility chain (float64 closed form stored once, against a
-    float32 store after every layer) within 1e-6 relative."""
-    _say("groups vs per layer", dtype, G, rule, votes)
+    float32 store after every layer) within 1e-6 relative. per_unit: one workgroup per unit
+    (a capacity whose per-token state fits in LDS); split: a capacity of 12000 slots, beyond
+    LDS, so the call runs split-K attention, the combine and the score kernel."""
+    _say("groups vs per layer", dtype, G, rule, votes, path)
     wl = C3.scaled(n_layers=6, batch=3, n_kv=2, context=500, budget=500, steps=1, dtype=dtype, G=G, rule=rule,
                    prior_votes=votes, key_scales=dtype == "bf16")
-    runs = [DeviceRun(wl), DeviceRun(wl)]
+    cap = 12000 if path == "split" else None
+    runs = [DeviceRun(wl, capacity=cap), DeviceRun(wl, capacity=cap)]
     q, _, _ = runs[0].inputs(1)
     nk, S, cap = wl.n_kv, wl.n_scopes, runs[0].cache.capacity
     unit0, n_groups = nk, wl.n_layers - 1
@@ -500,11 +504,13 @@ def test_entry_points_compose_to_the_step(context, budget, steps, n_kv):
     _say("composed", rep)
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_decode_step_c3_full_size_sampled(fused):
+@pytest.mark.parametrize("path", ["per_layer", "groups_split", "groups_per_unit"])
+def test_decode_step_c3_full_size_sampled(path):
     """16 sequences x 32 layers x 8 KV heads sharing one slot set per sequence, 16384 -> 1638:
-    the bulk first step and two steady steps, one sequence checked against the oracle (fused:
-    layers 2-32 in one kvc_decode_groups call)."""
+    the bulk first step and two steady steps, one sequence checked against the oracle. groups_*:
+    layers 2-32 in one kvc_decode_groups call; groups_per_unit bounds the steady steps' live
+    length by budget + 1 (one workgroup per unit), groups_split does not (split-K attention)."""
+    fused = path != "per_layer"
     run = DeviceRun(C3)
     for step in range(1, 4):
         q, kn, vn = run.inputs(step)
@@ -512,11 +518,12 @@ def test_decode_step_c3_full_size_sampled(fused):
         if scopes:
             pre = run.snapshot(scopes)
         t = run.t
-        _c3_step(run, step, q, kn, vn, True, fused=fused)
+        ml = C3.budget + 1 if (path == "groups_per_unit" and step > 1) else None
+        _c3_step(run, step, q, kn, vn, True, fused=fused, max_len=ml)
         if scopes:
             torch.cuda.synchronize()
             worst = _c3_check(run, scopes, pre, run.snapshot(scopes), q, kn, vn, t, True)
-            _say("c3 full step %d fused=%d: max rel dm %.2e" % (step, fused, worst))
+            _say("c3 full step %d %s: max rel dm %.2e" % (step, path, worst))
     assert int(run.cache.length.min()) == C3.budget == int(run.cache.length.max())
     assert kvc.kvc_workspace_status(run.ws) == 0
 
