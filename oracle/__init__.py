@@ -51,6 +51,7 @@ from .rank_stability import keep_jaccard  # noqa: F401
 from .zip_merge import cosine_partner, zip_merge  # noqa: F401
 from .keepkv_prefill import prefill_merge, reference_logits  # noqa: F401
 from .keepkv_ema_init import window_scores, ema_window_init, predicted_scores  # noqa: F401
+from .keepkv_refresh import refresh  # noqa: F401
 from .decode_step import ScopeState, StepParams, decode_step  # noqa: F401
 from .laprox import (window_column_norms, value_output_norms, laprox_scores,  # noqa: F401
                      laprox_keep)
