@@ -591,6 +591,95 @@ def run_prefill_merge(args):
     print(json.dumps(result), flush=True)
 
 
+def run_refresh(args):
+    """KeepKV's periodic refresh at k1's shape after T = 64 decode steps (kvc_keepkv_refresh_marked):
+    the full KV of 256 heads x 4160 tokens reloaded from pinned host memory, the EMA state restarted
+    over the last 32 steps' queries, greedy ZIP merging back to the budget (the last 32 positions
+    protected), compaction. Events between the four stages; the cache holds an unrelated state
+    before each repetition (the refresh overwrites it). Repetitions: at most one warm-up and five
+    timed (a call takes about a third of a second)."""
+    import oracle
+    wl = synth.WORKLOADS["k1_keepkv_prefill_llama8b_4k"]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    S, d, G, B, L0 = wl.n_scopes, wl.d, wl.G, wl.budget, wl.context
+    T, n_win = 64, 32
+    n = L0 + T
+    protect_from = n - 32
+    scale, alpha = float(np.float32(1 / np.sqrt(d))), float(np.float32(0.9))
+    # the full KV in pinned host memory
+    Kf, Vf = synth.kv_rows(S, n, d, "bf16", wl.seed, "cpu", synth.key_scales(S, d, wl.seed, "cpu"))
+    hk = torch.empty((S, n, d), dtype=torch.bfloat16, pin_memory=True)
+    hv = torch.empty((S, n, d), dtype=torch.bfloat16, pin_memory=True)
+    hp = torch.empty((S, n), dtype=torch.int32, pin_memory=True)
+    hk.copy_(Kf)
+    hv.copy_(Vf)
+    hp.copy_(torch.arange(n, dtype=torch.int32).repeat(S, 1))
+    del Kf, Vf
+    # the cache: capacity n, holding an unrelated compressed state
+    cache = kvc.Cache(k=torch.zeros((S, 1, n, d), dtype=torch.bfloat16, device=dev),
+                      v=torch.zeros((S, 1, n, d), dtype=torch.bfloat16, device=dev),
+                      pos=torch.zeros((S, n), dtype=torch.int32, device=dev),
+                      m=torch.zeros((S, n), device=dev), length=torch.full((S,), B, dtype=torch.int32, device=dev),
+                      votes=torch.ones((S, n), dtype=torch.int32, device=dev))
+    q_win = torch.stack([synth.step_query(L0 + T - n_win + 1 + j, S, G, d, "bf16", wl.seed, dev)
+                         for j in range(n_win)], dim=2).contiguous()
+    q_ref = q_win[:, :, -1, :].contiguous()
+    merge = kvc.merge_desc(q_ref, G, scale)
+    n_merged = torch.zeros((S,), dtype=torch.int32, device=dev)
+    ws = kvc.workspace(kvc.kvc_keepkv_refresh_workspace_size(cache, G, n_win, n), dev)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in marks:
+        e.record()
+    stages = []   # reload, EMA restart, merging, compaction (ms)
+    warm, reps = min(args.warmup, 1), max(1, min(args.steps, 5))
+    for rep in range(warm + reps):
+        cache.length.fill_(B)
+        torch.cuda.synchronize()
+        kvc.kvc_keepkv_refresh(cache, hk, hv, hp, n, q_win, n_win, merge, alpha, B, protect_from, None, n_merged,
+                               ws=ws, events=marks)
+        torch.cuda.synchronize()
+        if rep >= warm:
+            stages.append([marks[i].elapsed_time(marks[i + 1]) for i in range(4)])
+    if kvc.kvc_workspace_status(ws) != 0 or int(n_merged.min()) != n - B or int(cache.length.max()) != B:
+        raise SystemExit("refresh did not reach the budget")
+    st = np.median(np.array(stages), axis=0)
+    ms = float(st.sum())
+    reload_bytes = 2 * S * n * d * 2 + S * n * 4
+    loop_bytes = S * sum((protect_from - t - 2) * d * 2 for t in range(n - B))
+    ach = loop_bytes / (st[2] / 1e3) / 1e9
+    result = {"metric": "KeepKV periodic refresh: tokens reloaded and recompressed/sec",
+              "value": S * n / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": reps, "warmup": warm,
+              "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+              "dtype": "bf16 cache; f64 logits, cosines and merge weights", "data": "synthetic",
+              "config": {"workload": wl.name, "heads": S, "refresh_period": T, "tokens": n, "window": n_win,
+                         "budget": B, "protected": n - protect_from, "G": G},
+              "roofline": {"bound": "hbm", "achieved": ach, "peak": rf.MI355X_HBM_GBPS, "unit": "GB/s",
+                           "frac": ach / rf.MI355X_HBM_GBPS, "traffic": None, "kernel": "k_pm_loop",
+                           "launch_ms": float(st[2]), "bytes_per_launch": loop_bytes},
+              "stages_ms": {"reload_h2d": float(st[0]), "ema_restart": float(st[1]), "merging": float(st[2]),
+                            "compaction": float(st[3])},
+              "reload": {"bytes": reload_bytes, "GBps": reload_bytes / (st[0] / 1e3) / 1e9,
+                         "share_of_refresh": float(st[0] / ms)}}
+    if not args.no_cpu_baseline:
+        # the oracle's refresh of one head, bounded to its first 12 merges (the window restart in full)
+        h = lambda x: x.view(torch.int16).numpy().view(np.uint16)
+        Kh = oracle.to_f64(h(hk[0]), "bf16")
+        Vh = oracle.to_f64(h(hv[0]), "bf16")
+        qw = oracle.to_f64(h(q_win[0].cpu()), "bf16")
+        qr = oracle.to_f64(h(q_ref[0].cpu()), "bf16")
+        n_steps = 12
+        t0 = time.perf_counter()
+        oracle.refresh(Kh, Vh, np.arange(n), qw, qr, scale, alpha, n - n_steps, protect_from, row_dtype="bf16")
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": n_steps / dt * n / (n - B), "unit": "tokens/s",
+                                  "cores": torch.get_num_threads(), "kind": "oracle",
+                                  "sample": f"the window restart and the first {n_steps} merges of one head "
+                                            f"(n={n}) in {dt:.1f} s, numpy float64 oracle, scaled to whole "
+                                            "refreshes per second"}
+    print(json.dumps(result), flush=True)
+
+
 def run_first_step(args):
     """The first decode step after prefill: attend and score over the whole context, then
     compress every KV head to its budget (k = context + 1 - budget evictions per head: select,
@@ -696,7 +785,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2x32_llama8b_32layers_32k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict", "prefill_merge",
+    ap.add_argument("--op", default="step", choices=["step", "first_step", "moment_correct", "moment_evict", "prefill_merge", "refresh",
                                                      "ema_init", "stream_ceiling"],
                     help="step: the fused decode step (default); first_step: the bulk compression step "
                          "after prefill; moment_correct: MomentKV's corrected output")
@@ -721,6 +810,8 @@ def main():
         return run_ema_init(args)
     if args.op == "prefill_merge":
         return run_prefill_merge(args)
+    if args.op == "refresh":
+        return run_refresh(args)
     if args.op == "moment_correct":
         run_moment_correct(args)
         return

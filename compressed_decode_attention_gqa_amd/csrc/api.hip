@@ -941,6 +941,141 @@ int32_t kvc_keepkv_ema_init_marked(const kvc_cache *cache, const void *q_win, in
   return KVC_OK;
 }
 
+// ------------------------------------------------------- KeepKV periodic refresh
+// The prefill merging's workspace first (its status word is the refresh's), then
+// the EMA window initialisation's, the compaction's, and the merge flags.
+struct RefreshLayout {
+  size_t prefill, ema, compact, evict, total;
+};
+
+RefreshLayout refresh_layout(const kvc_cache *c, int G, int n_win, int n_tokens) {
+  RefreshLayout l{};
+  size_t o = 0;
+  l.prefill = o; o = align_up(o + prefill_layout(c->n_scopes, c->capacity).total);
+  l.ema = o;     o = align_up(o + kvc::ema_window_workspace_bytes(c->n_scopes, G, n_tokens, n_win));
+  l.compact = o; o = align_up(o + compact_layout(c).total);
+  l.evict = o;   o = align_up(o + size_t(c->n_scopes) * c->capacity);
+  l.total = o;
+  return l;
+}
+
+size_t kvc_keepkv_refresh_workspace_size(const kvc_cache *cache, int32_t G, int32_t n_win, int32_t n_tokens) {
+  if (validate_cache(cache) || !valid_G(G) || n_win <= 0 || n_tokens < n_win || n_tokens > cache->capacity)
+    return 0;
+  return refresh_layout(cache, G, n_win, n_tokens).total;
+}
+
+int32_t kvc_keepkv_refresh(const kvc_cache *cache, const void *host_k, const void *host_v, const int32_t *host_pos,
+                           int32_t n_tokens, const void *q_win, int32_t n_win, const kvc_merge *merge, float alpha,
+                           int32_t budget, int32_t protect_from, int32_t *pairs, int32_t *n_merged, void *ws,
+                           size_t ws_bytes, void *stream) {
+  return kvc_keepkv_refresh_marked(cache, host_k, host_v, host_pos, n_tokens, q_win, n_win, merge, alpha, budget,
+                                   protect_from, pairs, n_merged, ws, ws_bytes, stream, nullptr, 0);
+}
+
+int32_t kvc_keepkv_refresh_marked(const kvc_cache *cache, const void *host_k, const void *host_v,
+                                  const int32_t *host_pos, int32_t n_tokens, const void *q_win, int32_t n_win,
+                                  const kvc_merge *merge, float alpha, int32_t budget, int32_t protect_from,
+                                  int32_t *pairs, int32_t *n_merged, void *ws, size_t ws_bytes, void *stream,
+                                  void *const *events, int32_t n_events) {
+  if (events && n_events != 5) return KVC_ERR_ARG;
+  const int st = validate_cache(cache);
+  if (st) return st;
+  const kvc_cache *c = cache;
+  if (c->units_per_scope != 1 || c->capacity > kvc::PREFILL_MAX_ROWS) return KVC_ERR_UNSUPPORTED;
+  if (c->dtype != KVC_BF16) return KVC_ERR_DTYPE;
+  if (!host_k || !host_v || !host_pos || !q_win || !merge || !merge->q || !c->votes || !c->m) return KVC_ERR_ARG;
+  if (!valid_G(merge->G)) return KVC_ERR_UNSUPPORTED;
+  if (!aligned16(q_win) || !aligned16(merge->q)) return KVC_ERR_ALIGN;
+  if (!(alpha > 0.f && alpha < 1.f)) return KVC_ERR_ARG;
+  if (n_win <= 0 || n_tokens < n_win || n_tokens > c->capacity || budget < 0) return KVC_ERR_CAPACITY;
+  if (!ws) return KVC_ERR_WORKSPACE;
+  const int G = merge->G;
+  const RefreshLayout l = refresh_layout(c, G, n_win, n_tokens);
+  if (ws_bytes < l.total) return KVC_ERR_WORKSPACE;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipEvent_t *marks = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
+  auto mark = [&](int i) { return marks ? hipEventRecord(marks[i], hs) : hipSuccess; };
+  const size_t rb = size_t(kHD) * 2;   // bf16 row
+  const size_t width = size_t(n_tokens) * rb, dpitch = size_t(c->scope_stride) * rb;
+
+  // reload: rows and positions of the full KV into slots [0, n_tokens), votes 1, length n_tokens
+  if (mark(0) != hipSuccess) return KVC_ERR_DEVICE;
+  if (hipMemcpy2DAsync(c->k, dpitch, host_k, width, width, c->n_scopes, hipMemcpyHostToDevice, hs) != hipSuccess ||
+      hipMemcpy2DAsync(c->v, dpitch, host_v, width, width, c->n_scopes, hipMemcpyHostToDevice, hs) != hipSuccess ||
+      hipMemcpy2DAsync(c->pos, size_t(c->capacity) * 4, host_pos, size_t(n_tokens) * 4, size_t(n_tokens) * 4,
+                       c->n_scopes, hipMemcpyHostToDevice, hs) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  if (kvc::launch_reload_slots(c->votes, c->len, c->n_scopes, n_tokens, c->capacity, hs) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  if (mark(1) != hipSuccess) return KVC_ERR_DEVICE;
+
+  // the EMA state of every reloaded token: eq. (15)'s window form over the last n_win queries
+  if (kvc::launch_ema_window(q_win, c->k, c->scope_stride, c->n_scopes, G, n_win, n_tokens, double(merge->scale),
+                             double(alpha), c->m, c->capacity, at<char>(ws, l.ema), hs, nullptr) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  if (mark(2) != hipSuccess) return KVC_ERR_DEVICE;
+
+  // greedy ZIP merging with the current query's exact group-mean logits
+  const PrefillLayout pl = prefill_layout(c->n_scopes, c->capacity);
+  uint8_t *evict = at<uint8_t>(ws, l.evict);
+  kvc::PrefillMergeArgs p{};
+  p.k = static_cast<char *>(c->k);
+  p.v = static_cast<char *>(c->v);
+  p.scope_stride = c->scope_stride;
+  p.votes = c->votes;
+  p.pos = c->pos;
+  p.len = c->len;
+  p.m = c->m;
+  p.q = static_cast<const char *>(merge->q);
+  p.G = G;
+  p.scale = double(merge->scale);
+  p.eps = merge->eps;
+  p.capacity = c->capacity;
+  p.n_scopes = c->n_scopes;
+  p.budget = budget;
+  p.protect_from = protect_from;
+  p.evict = evict;
+  p.pairs = pairs;
+  p.n_merged = n_merged;
+  p.meta = at<char>(ws, l.prefill + pl.meta);
+  p.rec = at<char>(ws, l.prefill + pl.rec);
+  p.status = at<int32_t>(ws, l.prefill + pl.status);
+  if (kvc::launch_prefill_merge(p, c->dtype, hs, nullptr) != hipSuccess) return KVC_ERR_DEVICE;
+  if (mark(3) != hipSuccess) return KVC_ERR_DEVICE;
+
+  // the merged-away slots out
+  const CompactLayout cl = compact_layout(c);
+  char *cws = at<char>(ws, l.compact);
+  kvc::StepArgs a{};
+  a.k = static_cast<char *>(c->k);
+  a.v = static_cast<char *>(c->v);
+  a.votes = c->votes;
+  a.pos = c->pos;
+  a.m = c->m;
+  a.len = c->len;
+  a.scope_stride = c->scope_stride;
+  a.unit_stride = c->unit_stride;
+  a.capacity = c->capacity;
+  a.n_scopes = c->n_scopes;
+  a.units = c->units_per_scope;
+  kvc::BulkArgs b{};
+  b.st = reinterpret_cast<kvc::BulkScope *>(cws + cl.sel.state);
+  b.cnt = reinterpret_cast<int32_t *>(cws + cl.sel.cnt);
+  b.flags = evict;
+  b.list = reinterpret_cast<int32_t *>(cws + cl.list);
+  b.list2 = reinterpret_cast<int32_t *>(cws + cl.list2);
+  b.len = c->len;
+  b.cap = c->capacity;
+  b.n_scopes = c->n_scopes;
+  b.n_chunks = cl.sel.n_chunks;
+  b.chunk = cl.sel.chunk;
+  b.move_blocks = std::max(1, std::min(64, ceil_div(kTargetWorkgroups, c->n_scopes)));
+  if (kvc::launch_bulk_compact(a, b, c->dtype, hs) != hipSuccess) return KVC_ERR_DEVICE;
+  if (mark(4) != hipSuccess) return KVC_ERR_DEVICE;
+  return KVC_OK;
+}
+
 size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w, int32_t d,
                                  int32_t D) {
   return kvc::laprox_workspace_bytes(n_layers, H, n_kv, N, w, d, D);

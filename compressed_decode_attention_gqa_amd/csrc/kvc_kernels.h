@@ -89,6 +89,9 @@ hipError_t launch_moment_correct(const MomentArgs &m, int n_units, const void *q
                                  const float *f_R, const float *lse_R, float *out, hipStream_t st);
 // marks: NULL, or 4 events recorded before the first kernel and after each of the three.
 hipError_t launch_prefill_merge(const PrefillMergeArgs &p, int dtype, hipStream_t st, hipEvent_t *marks);
+
+// Periodic refresh: vote 1 on slots [0, n) of every scope and live length n.
+hipError_t launch_reload_slots(int32_t *votes, int32_t *len, int n_scopes, int n, int cap, hipStream_t st);
 hipError_t launch_moment_evict(const MomentEvictArgs &p, int dtype, int rounds, hipStream_t st);
 hipError_t launch_ema_update(float *m, const float *s, const int32_t *len, int n_scopes, int cap,
                              int rule, float alpha, hipStream_t st);

@@ -24,6 +24,7 @@ EXPORTED = ("kvc_decode_attn_score", "kvc_ema_update", "kvc_ema_predict", "kvc_s
             "kvc_keep_jaccard", "kvc_compact",
             "kvc_moment_update", "kvc_moment_correct", "kvc_moment_evict", "kvc_keepkv_prefill_merge",
             "kvc_keepkv_prefill_merge_marked", "kvc_keepkv_ema_init", "kvc_keepkv_ema_init_marked",
+            "kvc_keepkv_refresh", "kvc_keepkv_refresh_marked", "kvc_keepkv_refresh_workspace_size",
             "kvc_laprox_score", "kvc_laprox_score_marked", "kvc_decode_step", "kvc_decode_step_noalloc",
             "kvc_decode_workspace_size", "kvc_decode_plan", "kvc_decode_groups",
             "kvc_select_workspace_size", "kvc_compact_workspace_size", "kvc_moment_evict_workspace_size",
@@ -86,6 +87,9 @@ _SIGS = {
     "kvc_moment_evict_workspace_size": (_SZ, [_P]),
     "kvc_keepkv_prefill_workspace_size": (_SZ, [_P]),
     "kvc_keepkv_ema_init_workspace_size": (_SZ, [_P, _I, _I, _I]),
+    "kvc_keepkv_refresh_workspace_size": (_SZ, [_P, _I, _I, _I]),
+    "kvc_keepkv_refresh": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _F, _I, _I, _P, _P, _P, _SZ, _P]),
+    "kvc_keepkv_refresh_marked": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _F, _I, _I, _P, _P, _P, _SZ, _P, _P, _I]),
     "kvc_laprox_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "kvc_read_probe": (_I, [_P, _SZ, _I, _I, _P, _P]),
     "kvc_workspace_status": (_I, [_P, _P]),
@@ -366,6 +370,30 @@ def kvc_keepkv_prefill_merge(cache: Cache, merge: _Merge, budget: int, protect_f
     _check("kvc_keepkv_prefill_merge_marked", lib().kvc_keepkv_prefill_merge_marked(
         ctypes.byref(d), ctypes.byref(merge), budget, protect_from, _ptr(evict), _ptr(pairs), _ptr(n_merged),
         _ptr(ws), nbytes, _stream(stream), handles, len(events)))
+
+
+def kvc_keepkv_refresh_workspace_size(cache: Cache, G: int, n_win: int, n_tokens: int) -> int:
+    d = cache.desc()
+    return lib().kvc_keepkv_refresh_workspace_size(ctypes.byref(d), G, n_win, n_tokens)
+
+
+def kvc_keepkv_refresh(cache: Cache, host_k, host_v, host_pos, n_tokens: int, q_win, n_win: int, merge: _Merge,
+                       alpha: float, budget: int, protect_from: int, pairs=None, n_merged=None,
+                       ws: torch.Tensor = None, stream=None, events=None):
+    """host_k, host_v: pinned host tensors [n_scopes, n_tokens, 128] bf16; host_pos: pinned
+    [n_scopes, n_tokens] int32. events: None, or 5 recorded-once torch.cuda.Event(enable_timing=True)."""
+    for name, t in (("host_k", host_k), ("host_v", host_v), ("host_pos", host_pos)):
+        if t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous host tensor")
+    d = cache.desc()
+    args = (ctypes.byref(d), ctypes.c_void_p(host_k.data_ptr()), ctypes.c_void_p(host_v.data_ptr()),
+            ctypes.c_void_p(host_pos.data_ptr()), n_tokens, _ptr(q_win), n_win, ctypes.byref(merge), alpha, budget,
+            protect_from, _ptr(pairs), _ptr(n_merged), _ptr(ws), ws.numel(), _stream(stream))
+    if events is None:
+        _check("kvc_keepkv_refresh", lib().kvc_keepkv_refresh(*args))
+        return
+    handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _check("kvc_keepkv_refresh_marked", lib().kvc_keepkv_refresh_marked(*args, handles, len(events)))
 
 
 def kvc_keepkv_ema_init(cache: Cache, q_win, G: int, n_win: int, n_tokens: int, scale: float, alpha: float,

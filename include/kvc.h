@@ -268,6 +268,50 @@ int32_t kvc_keepkv_prefill_merge_marked(const kvc_cache *cache, const kvc_merge 
                                         void *ws, size_t ws_bytes, void *stream, void *const *events,
                                         int32_t n_events);
 
+/* kvc_keepkv_refresh -- KeepKV's periodic refresh (reading notes on KeepKV: the
+ * inference algorithm's decode step 6g, Figure 4 and the paragraph on periodic
+ * refresh): the full KV kept in host memory is loaded back and compressed again,
+ * which clears the error the EMA-predicted merges of the decode steps since the
+ * last compression have accumulated. Per-KV-head scopes of a bf16 cache
+ * (units_per_scope = 1 and capacity <= 32768, else KVC_ERR_UNSUPPORTED; fp32
+ * KVC_ERR_DTYPE) with votes and utilities. In stream order:
+ *   1. reload: host_k, host_v ([n_scopes][n_tokens][128] bf16, every token so far in
+ *      position order) and host_pos ([n_scopes][n_tokens] int32, increasing) are
+ *      copied into slots [0, n_tokens) of every scope; those slots get vote 1 and
+ *      the live length becomes n_tokens (whatever the cache held before);
+ *   2. the utility of every reloaded token is restarted with eq. (15)'s window
+ *      form, as kvc_keepkv_ema_init computes it, from q_win ([n_scopes][G][n_win]
+ *      [128] bf16, the queries of the last n_win steps, row j standing at the
+ *      position of slot n_tokens - n_win + j) and alpha;
+ *   3. greedy ZIP merging down to `budget`, as kvc_keepkv_prefill_merge does it,
+ *      with the exact group-mean logits of merge->q (the current step's G query
+ *      heads, [n_scopes][G][128] bf16) under merge->scale, which step 2 uses too;
+ *      entries at positions >= protect_from never merge;
+ *   4. the merged-away slots are removed (hole filling, as kvc_compact).
+ * pairs ([n_scopes][capacity][2] int32) and n_merged ([n_scopes] int32), or NULL,
+ * receive the merges as kvc_keepkv_prefill_merge reports them (slots before step 4).
+ * The host buffers should be pinned (hipHostMalloc) for the copies to run
+ * asynchronously; they must stay valid until the stream reaches this call's end.
+ * A scope that cannot reach its budget stops above it and the workspace status
+ * (its first word) becomes KVC_ERR_CAPACITY. 0 < alpha < 1, else KVC_ERR_ARG;
+ * 0 < n_win <= n_tokens <= capacity and budget >= 0, else KVC_ERR_CAPACITY.
+ * Workspace: kvc_keepkv_refresh_workspace_size, zero-filled once. */
+int32_t kvc_keepkv_refresh(const kvc_cache *cache, const void *host_k, const void *host_v, const int32_t *host_pos,
+                           int32_t n_tokens, const void *q_win, int32_t n_win, const kvc_merge *merge, float alpha,
+                           int32_t budget, int32_t protect_from, int32_t *pairs, int32_t *n_merged, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* kvc_keepkv_refresh_marked -- kvc_keepkv_refresh, plus stage timing for
+ * measurement: events (hipEvent_t handles created by the caller, n_events = 5) are
+ * recorded on `stream` before the reload and after each of its four steps. events
+ * NULL behaves as kvc_keepkv_refresh; n_events other than 5 with events non-NULL is
+ * KVC_ERR_ARG. */
+int32_t kvc_keepkv_refresh_marked(const kvc_cache *cache, const void *host_k, const void *host_v,
+                                  const int32_t *host_pos, int32_t n_tokens, const void *q_win, int32_t n_win,
+                                  const kvc_merge *merge, float alpha, int32_t budget, int32_t protect_from,
+                                  int32_t *pairs, int32_t *n_merged, void *ws, size_t ws_bytes, void *stream,
+                                  void *const *events, int32_t n_events);
+
 /* kvc_keepkv_ema_init -- KeepKV's window initialisation of the EMA utility at the
  * end of prefill (reading notes on KeepKV: EMA score prediction, eq. (15) at t = L,
  * and the inference algorithm's prefill step 4), per-KV-head scopes of a bf16 cache
@@ -485,6 +529,7 @@ size_t kvc_compact_workspace_size(const kvc_cache *cache);
 size_t kvc_moment_evict_workspace_size(const kvc_cache *cache);
 size_t kvc_keepkv_prefill_workspace_size(const kvc_cache *cache);
 size_t kvc_keepkv_ema_init_workspace_size(const kvc_cache *cache, int32_t G, int32_t n_win, int32_t n_tokens);
+size_t kvc_keepkv_refresh_workspace_size(const kvc_cache *cache, int32_t G, int32_t n_win, int32_t n_tokens);
 size_t kvc_laprox_workspace_size(int32_t n_layers, int32_t H, int32_t n_kv, int32_t N, int32_t w,
                                  int32_t d, int32_t D);
 

@@ -128,6 +128,35 @@ def test_decode_groups_host_checks():
 
 
 @needs_lib
+def test_keepkv_refresh_host_checks():
+    """kvc_keepkv_refresh: per-KV-head bf16 caches with votes and utilities only; window, token count,
+    alpha, pointers and workspace checked on the host before anything is enqueued."""
+    L = kvc.lib()
+    mg = kvc._Merge(q=0x6000, G=4, scale=0.1, eps=1e-6)
+
+    def call(c, hk=0x100, n=50, qw=0x7000, n_win=8, merge=mg, alpha=0.9, budget=10, ws=0x9000, wsb=1 << 30):
+        return L.kvc_keepkv_refresh(ctypes.byref(c), hk, 0x200, 0x300, n, qw, n_win,
+                                    ctypes.byref(merge) if merge is not None else None, alpha, budget, 40, None, None,
+                                    ws, wsb, None)
+    c = _fake_cache(votes=0x5100)
+    assert call(_fake_cache(votes=0x5100, dtype=1)) == -2
+    assert call(_fake_cache(votes=0x5100, units_per_scope=2, unit_stride=100, scope_stride=200)) == -3
+    assert call(_fake_cache()) == -1                     # no votes
+    assert call(c, hk=None) == -1
+    assert call(c, merge=None) == -1
+    assert call(c, qw=0x7004) == -5
+    assert call(c, alpha=1.0) == -1
+    assert call(c, n=101) == -4
+    assert call(c, n_win=0) == -4
+    assert call(c, n_win=60) == -4
+    assert call(c, budget=-1) == -4
+    assert call(c, ws=None) == -6
+    assert call(c, wsb=16) == -6
+    assert L.kvc_keepkv_refresh_workspace_size(ctypes.byref(c), 4, 8, 50) > 0
+    assert L.kvc_keepkv_refresh_workspace_size(ctypes.byref(c), 4, 60, 50) == 0
+
+
+@needs_lib
 def test_other_entry_points_reject_bad_arguments():
     L = kvc.lib()
     assert L.kvc_ema_update(None, 0x10, 0x20, 1, 10, 2, 0.9, None) == -1
