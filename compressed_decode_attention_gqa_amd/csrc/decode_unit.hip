@@ -103,7 +103,7 @@ struct UnitLds {
     struct {
       double pM[Geo::NW][G], zw[Geo::NW][G];
       float pO[Geo::NW][G][HD];
-      double M[G], iZ[G];
+      double M[G];
       float fac[Geo::NW][G];
       uint64_t wkey[Geo::NW];
       int wslot[Geo::NW], wcnt[Geo::NW];
@@ -136,6 +136,42 @@ size_t decode_unit_groups_lds_bytes(int dtype, int G, int lds_len, bool votes) {
   return st + unit_lds_layout(decode_unit_chunk_tokens(dtype), G, lds_len, votes).total;
 }
 
+
+// Token i's score numerator: sum over the G heads of its weight (token-major in
+// e_lds) times its sub-chunk's factor exp(m_c - M) / Z (f_lds), and for a weight
+// stored shifted, times exp(-SHIFT_STEP * shift). The shifted form is taken for a
+// whole wave only when one of its tokens needs it; a head without a shift
+// multiplies by exactly 1, so both forms agree.
+template <int G>
+__device__ __forceinline__ double token_score(const float *e_lds, const double *f_lds, const uint8_t *s_lds, int i,
+                                              int c) {
+  float ev[G];
+  if constexpr (G == 1) {
+    ev[0] = e_lds[i];
+  } else if constexpr (G == 2) {
+    const float2 v = *reinterpret_cast<const float2 *>(e_lds + 2 * i);
+    ev[0] = v.x; ev[1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < G / 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4 *>(e_lds + G * i + 4 * q);
+      ev[4 * q] = v.x; ev[4 * q + 1] = v.y; ev[4 * q + 2] = v.z; ev[4 * q + 3] = v.w;
+    }
+  }
+  const uint64_t shw = token_shifts<G>(s_lds, i);
+  double acc = 0.0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc += double(ev[g]) * f_lds[c * G + g];
+  if (__builtin_expect(__ballot(shw != 0) != 0, 0)) {
+    if (shw != 0) {
+      acc = 0.0;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        acc += double(ev[g]) * f_lds[c * G + g] * shift_scale(int((shw >> (8 * g)) & 255u));
+    }
+  }
+  return acc;
+}
 
 // GRP: one workgroup per attention unit of every scope (blockIdx.x = scope *
 // attn_units + unit), attending only, with no append: o, lse and, when scores are
@@ -297,7 +333,7 @@ void k_decode_unit(const StepArgs a) {
             zc += double(pe);
             sh.w[wave][it][tg][myh] = pe * rc;
             if (tok < L) {
-              e_lds[myh * ld + tok] = e;
+              e_lds[tok * G + myh] = e;
               s_lds[tok * G + myh] = uint8_t(shc);
             }
           }
@@ -419,6 +455,16 @@ void k_decode_unit(const StepArgs a) {
     if (tid < G) sh.ep.M[tid] = M;
   }
   lds_barrier();
+  {
+    // this thread's sub-chunk factors become exp(m_c - M) / Z (its entries all belong to
+    // head tid % G; Z summed over the waves in the same order as below)
+    const int g = tid % G;
+    double Z = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) Z += sh.ep.zw[w2][g];
+    const double iZ = Z > 0.0 ? 1.0 / Z : 0.0;
+    for (int idx = tid; idx < nsubL * G; idx += NT) f_lds[idx] *= iZ;
+  }
   if (tid < NW * G) {   // Z per head (the same sum in every thread of the head), the waves' factors
     const int w = tid / G, g = tid % G;
     double Z = 0.0;
@@ -427,7 +473,6 @@ void k_decode_unit(const StepArgs a) {
     const double M = sh.ep.M[g], pm = sh.ep.pM[w][g];
     sh.ep.fac[w][g] = (Z > 0.0 && pm > -INFINITY) ? float(double(exp_split(pm - M)) / Z) : 0.f;
     if (w == 0) {
-      sh.ep.iZ[g] = Z > 0.0 ? 1.0 / Z : 0.0;
       a.lse[int64_t(gu) * G + g] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
     }
   }
@@ -440,25 +485,14 @@ void k_decode_unit(const StepArgs a) {
     a.out[(int64_t(gu) * G + g) * HD + e] = acc;
   }
   const bool score = a.refresh && (step || a.s != nullptr);
-  double izr[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) izr[g] = sh.ep.iZ[g];
 
   if constexpr (GRP) {
     // the unit's per-token weight sums (the score's numerator over this unit's heads)
     if (a.refresh) {
       double *wrow = a.wsum + int64_t(gu) * a.wsum_stride;
       for (int i = tid; i < L; i += NT) {
-        const int c = i / CHW;
-        const uint64_t shw = token_shifts<G>(s_lds, i);
-        double acc = 0.0;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const double x = double(e_lds[g * ld + i]) * (f_lds[c * G + g] * izr[g]);
-          acc += shw == 0 ? x : x * shift_scale(int((shw >> (8 * g)) & 255u));
-        }
-        if (VOTES) acc *= double(v_lds[i]);
-        wrow[i] = acc;
+        const double acc = token_score<G>(e_lds, f_lds, s_lds, i, i / CHW);
+        wrow[i] = VOTES ? acc * double(v_lds[i]) : acc;
       }
     }
     return;
@@ -472,20 +506,10 @@ void k_decode_unit(const StepArgs a) {
 #pragma unroll 2
   for (int i = tid; i < L; i += NT) {
     const bool isnew = a.append && i == L - 1;
-    double mval = isnew ? 0.0 : m_lds[i];
+    const double mold = m_lds[i];
+    double mval = isnew ? 0.0 : mold;
     if (score) {
-      const int c = i / CHW;
-      const uint64_t shw = token_shifts<G>(s_lds, i);
-      double acc = 0.0;
-      if (shw == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) acc += double(e_lds[g * ld + i]) * (f_lds[c * G + g] * izr[g]);
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          acc += double(e_lds[g * ld + i]) * (f_lds[c * G + g] * izr[g]) *
-                 shift_scale(int((shw >> (8 * g)) & 255u));
-      }
+      double acc = token_score<G>(e_lds, f_lds, s_lds, i, i / CHW);
       if (VOTES && !isnew) acc *= double(v_lds[i]);
       const double sv = acc * inv_heads;
       if (a.s) a.s[sc + i] = float(sv);
