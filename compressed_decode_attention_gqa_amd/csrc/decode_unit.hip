@@ -8,9 +8,11 @@
 // tokens of 16-byte K/V loads in flight each. Sub-chunks are handed out in
 // order by an LDS counter (a wave takes the next one when a load slot frees),
 // so every wave streams until the scope's last sub-chunk and the reads of a
-// workgroup stay close together; a step at an odd position walks the cache
-// from its end, so it first reads the rows the previous step read last, which
-// the memory-side cache still holds. Full sub-chunks are addressed as one
+// workgroup stay close together; each workgroup starts at its own sub-chunk
+// (a hash of its index) and wraps around, so the workgroups' concurrent reads
+// spread over the memory channels; a step at an odd position walks the other
+// way, so it first reads the rows the previous step read last, which the
+// memory-side cache still holds. Full sub-chunks are addressed as one
 // uniform base plus the lane's 16-byte offset; only the last sub-chunk clamps
 // per lane and substitutes the appended row. Logits are float64 (exact
 // bf16/fp32 products); each lane keeps its query heads in the lane-permuted
@@ -255,6 +257,17 @@ void k_decode_unit(const StepArgs a) {
 
   const int nsub = L > 0 ? (L + CHW - 1) / CHW : 0;
   const bool rev = !GRP && (a.t & 1) != 0;   // walk order of this step
+  // Each workgroup starts its walk at its own sub-chunk (a multiplicative hash of its
+  // index, fixed across steps) and wraps around: workgroups that all started at the
+  // same offset of their regions read rows that collide in the memory channels. A
+  // forward walk from rot ends at rot - 1, where the next step's backward walk starts.
+  const int rot = nsub > 0 ? int((uint32_t(gu) * 2654435761u) % uint32_t(nsub)) : 0;
+  auto sub_of = [&](int n) {
+    int c = rev ? rot - 1 - n : rot + n;
+    c += c < 0 ? nsub : 0;
+    c -= c >= nsub ? nsub : 0;
+    return c;
+  };
   if (tid == 0) sh.next_sub = NW * PF;
   __syncthreads();
   u32x4 kr[PF][UNR], vr[PF][UNR];
@@ -264,7 +277,7 @@ void k_decode_unit(const StepArgs a) {
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
     cs[s] = wave + NW * s;
-    if (cs[s] < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], rev ? nsub - 1 - cs[s] : cs[s]);
+    if (cs[s] < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], sub_of(cs[s]));
   }
   for (;;) {
     bool more = false;
@@ -272,7 +285,7 @@ void k_decode_unit(const StepArgs a) {
     for (int s = 0; s < PF; ++s) {
       if (cs[s] < nsub) {
         more = true;
-        const int c = rev ? nsub - 1 - cs[s] : cs[s];
+        const int c = sub_of(cs[s]);
         const bool tail = (c + 1) * CHW > L;
         // scope arrays of this sub-chunk into LDS
         if (lane < CHW) {
@@ -365,7 +378,7 @@ void k_decode_unit(const StepArgs a) {
         if (lane == 0) got = atomicAdd(&sh.next_sub, 1);
         const int nc = __builtin_amdgcn_readfirstlane(got);
         cs[s] = nc;
-        if (nc < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], rev ? nsub - 1 - nc : nc);
+        if (nc < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], sub_of(nc));
       }
     }
     if (!more) break;
