@@ -324,6 +324,16 @@ def run_laprox(args):
                      "unit": d["unit"], "frac": d["frac"], "traffic": None, "launch_ms": d["ms"]},
         "stages": stages,
     }
+    # the plan's measure of the value-output norms: the explicit product V W_bar (N x d times
+    # d x D per unit) on bf16 MFMA; the Gram form computes the same norms with 2 d^2 per token
+    vw_flops = 2.0 * lw.N * lw.d * lw.D * units
+    result["value_norm_terms"] = {
+        "explicit_vw_flops": vw_flops, "gram_form_flops": gram_flops + r2_flops,
+        "effective_TFLOPs_value_norm_stages": vw_flops / ((stages["gram"]["ms"] + stages["value_norms"]["ms"]) / 1e3) / 1e12,
+        "effective_TFLOPs_whole_call": vw_flops / (ms_per_call / 1e3) / 1e12,
+        "bf16_dense_peak_TFLOPs": rf.MI355X_BF16_TFLOPS,
+        "note": "explicit V W_bar flops over the measured times, against the dense bf16 peak the explicit "
+                "product would run at; the Gram form reaches the same norms with about d/D of those flops, in float64"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = laprox_cpu_baseline(lw, inp, scale, args.cpu_seconds)
     print(json.dumps(result), flush=True)
