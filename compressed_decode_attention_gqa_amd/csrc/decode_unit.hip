@@ -49,7 +49,7 @@ int decode_unit_chunk_tokens(int dtype) {
   return dtype == 0 ? UnitGeometry<bf16_t>::CHW : UnitGeometry<float>::CHW;
 }
 
-// Dynamic LDS: per-token weights e[G][ld], sub-chunk maxima and weight sums
+// Dynamic LDS: per-token weights e[ld][G], sub-chunk maxima and weight sums
 // [nsub][G] (double each), utilities m[ld] (double), votes[ld] and the weights'
 // shift counts sh[ld][G] (bytes); ld = lds_len rounded up to whole sub-chunks.
 struct UnitLdsLayout {
@@ -100,19 +100,19 @@ struct GrpGeo {
 template <typename T, int G, int NWO = 0, int PFO = 0>
 struct UnitLds {
   using Geo = UnitGeometry<T, G, NWO, PFO>;
-  union {
-    float w[Geo::NW][Geo::UNR][Geo::TPI][G];      // streaming: weights for the value sums
-    struct {
-      double pM[Geo::NW][G], zw[Geo::NW][G];
-      float pO[Geo::NW][G][HD];
-      double M[G];
-      float fac[Geo::NW][G];
-      uint64_t wkey[Geo::NW];
-      int wslot[Geo::NW], wcnt[Geo::NW];
-      int tie_pos, tie_slot;
-      float rowk[HD], rowv[HD];
-    } ep;
-  };
+  float w[Geo::NW][Geo::UNR][Geo::TPI][G];      // streaming: weights for the value sums
+  // the epilogue's space (apart from the weights: a wave stores its partials as soon
+  // as its streaming ends, while other waves still use theirs)
+  struct {
+    double pM[Geo::NW][G], zw[Geo::NW][G];
+    float pO[Geo::NW][G][HD];
+    double M[G];
+    float fac[Geo::NW][G];
+    uint64_t wkey[Geo::NW];
+    int wslot[Geo::NW], wcnt[Geo::NW];
+    int tie_pos, tie_slot;
+    float rowk[HD], rowv[HD];
+  } ep;
   int next_sub;   // the next sub-chunk to hand out
 };
 
@@ -196,7 +196,6 @@ void k_decode_unit(const StepArgs a) {
   extern __shared__ __attribute__((aligned(16))) char dyn[];
   const int lds_len = a.lds_len;
   const UnitLdsLayout lay = unit_lds_layout(CHW, G, lds_len, VOTES);
-  const int ld = lay.ld;
   float *e_lds = reinterpret_cast<float *>(dyn + lay.e);
   double *f_lds = reinterpret_cast<double *>(dyn + lay.f);
   double *z_lds = reinterpret_cast<double *>(dyn + lay.z);
@@ -204,7 +203,8 @@ void k_decode_unit(const StepArgs a) {
   int *v_lds = reinterpret_cast<int *>(dyn + lay.v);
   uint8_t *s_lds = reinterpret_cast<uint8_t *>(dyn + lay.sh);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar (uniform per wave), so values derived from it stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gu = blockIdx.x;
   const int scope = GRP ? gu / a.attn_units : gu;
   const int unit = GRP ? a.attn_unit0 + (gu - scope * a.attn_units) : a.attn_unit0;
@@ -277,13 +277,15 @@ void k_decode_unit(const StepArgs a) {
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
     cs[s] = wave + NW * s;
-    if (cs[s] < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], sub_of(cs[s]));
+    const bool live = cs[s] < nsub;
+    W.issue(kr[s], vr[s], mv[s], vv[s], live ? sub_of(cs[s]) : 0, live);
   }
   for (;;) {
     bool more = false;
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
-      if (cs[s] < nsub) {
+      const bool cur = cs[s] < nsub;
+      if (cur) {
         more = true;
         const int c = sub_of(cs[s]);
         const bool tail = (c + 1) * CHW > L;
@@ -332,6 +334,9 @@ void k_decode_unit(const StepArgs a) {
 #pragma unroll
         for (int r = 0; r < ITL; ++r) {
           const int it = dup + D * r;
+          // the token's vote: lane tok - c * CHW loaded it with this sub-chunk (read
+          // with every lane active: the source lane may form no weight itself)
+          const int vt = VOTES ? __shfl(vv[s], min(it, UNR - 1) * TPI + tg) : 1;
           if (it < UNR) {
             double x = lg[0];
 #pragma unroll
@@ -339,8 +344,7 @@ void k_decode_unit(const StepArgs a) {
             const int tok = c * CHW + it * TPI + tg;
             int shc;
             const float e = exp_shifted(x - mx, shc);
-            float p = 1.f;
-            if (VOTES) p = (a.append && tok == L - 1) ? 1.f : float(v_lds[min(tok, L - 1)]);
+            const float p = (!VOTES || (a.append && tok == L - 1)) ? 1.f : float(vt);
             // a shifted weight is below exp(-SHIFT_STEP) of the maximum: nothing in o or Z
             const float pe = shc ? 0.f : p * e;
             zc += double(pe);
@@ -374,15 +378,46 @@ void k_decode_unit(const StepArgs a) {
           }
         }
         __builtin_amdgcn_wave_barrier();
+        // the refill's loads stay after the value sums: the slot's registers are free
+        // then and the loads can land in them
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the slot's next sub-chunk
+      int nc = cs[s];
+      if (cur) {
         int got = 0;
         if (lane == 0) got = atomicAdd(&sh.next_sub, 1);
-        const int nc = __builtin_amdgcn_readfirstlane(got);
-        cs[s] = nc;
-        if (nc < nsub) W.issue(kr[s], vr[s], mv[s], vv[s], sub_of(nc));
+        nc = __builtin_amdgcn_readfirstlane(got);
       }
+      cs[s] = nc;
+      // every pass refills every slot, a finished one with one row (see
+      // UnitStream::issue): the slot's registers then have one definition in the
+      // loop, which they keep without a copy that would wait for the loads
+      const bool live = nc < nsub;
+      W.issue(kr[s], vr[s], mv[s], vv[s], live ? sub_of(nc) : 0, live);
     }
     if (!more) break;
   }
+
+  // ---- this wave's partials (running maximum per head; value sums over the wave's
+  // token groups by lane swaps) into LDS (their space is the wave's own: no wait
+  // for the waves that still stream)
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) {
+      float x = oacc[g][j];
+      if constexpr (LPT == 16) x += lane_xor16(x);
+      x += lane_xor32(x);
+      oacc[g][j] = x;
+    }
+  if (lane < LPT) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < EPV; ++j) sh.ep.pO[wave][g][cb * EPV + j] = oacc[g][j];
+  }
+  if (tg == 0 && dup == 0) sh.ep.pM[wave][myh] = Mrun;
 
   // ---- loads the epilogue needs, issued by each wave as its streaming ends (the
   // other waves may still stream): its share of the moment sums, the last live row
@@ -408,26 +443,6 @@ void k_decode_unit(const StepArgs a) {
     const char *src = a.append ? (lastK ? W.Kn : W.Vn) : (lastK ? W.Kb : W.Vb) + int64_t(L - 1) * RB;
     lastrow = ld16(src + 16 * lastc);
   }
-
-  // ---- this wave's partials (running maximum per head; value sums) into LDS: the
-  // value sums over the token groups of the wave by lane swaps
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int j = 0; j < EPV; ++j) {
-      float x = oacc[g][j];
-      if constexpr (LPT == 16) x += lane_xor16(x);
-      x += lane_xor32(x);
-      oacc[g][j] = x;
-    }
-  lds_barrier();   // the weight scratch becomes the epilogue's space
-  if (lane < LPT) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < EPV; ++j) sh.ep.pO[wave][g][cb * EPV + j] = oacc[g][j];
-  }
-  if (tg == 0 && dup == 0) sh.ep.pM[wave][myh] = Mrun;
   lds_barrier();
   if (overflow || k > 1) {
     // k > 1 cannot happen: the host launches this kernel only when
@@ -497,6 +512,7 @@ void k_decode_unit(const StepArgs a) {
     for (int w = 0; w < NW; ++w) acc = fmaf(sh.ep.pO[w][g][e], sh.ep.fac[w][g], acc);
     a.out[(int64_t(gu) * G + g) * HD + e] = acc;
   }
+
   const bool score = a.refresh && (step || a.s != nullptr);
 
   if constexpr (GRP) {

@@ -74,6 +74,12 @@ template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_
 template <> __device__ __forceinline__ void store_elem<float>(float *p, int64_t i, float x) { p[i] = x; }
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// The same load through a global-memory pointer: where the address is selected among
+// several pointers the compiler cannot tell it is global and would emit a flat load,
+// which also holds up every wait for LDS results.
+__device__ __forceinline__ u32x4 ld16g(const void *p) {
+  return *(const __attribute__((address_space(1))) u32x4 *)(p);
+}
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 // ---------------------------------------------------------------- cross-lane

@@ -38,30 +38,47 @@ struct UnitStream {
   const int32_t *vrow;
   int L, Lold, append, lane, cb, tg;
 
-  __device__ __forceinline__ void issue(u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], float &mv, int &vv, int c) const {
-    if ((c + 1) * CHW <= Lold) {
+  // Loads sub-chunk c; a slot with nothing left (live false) loads one row, the
+  // same 16 bytes in every lane, so that every refill takes the same loads and
+  // their registers: a refill under a condition leaves the compiler two versions
+  // of the slot's registers to merge, and the merge waits for the loads.
+  __device__ __forceinline__ void issue(u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], float &mv, int &vv, int c,
+                                        bool live = true) const {
+    // the small loads first: they are used first, so waiting for them leaves the
+    // rows of this and later sub-chunks in flight
+    const int t1 = live ? min(c * CHW + (lane % CHW), max(Lold - 1, 0)) : 0;
+    mv = MROW ? mrow[t1] : 0.f;
+    if (VOTES) vv = vrow[t1];
+    const char *kp[UNR], *vp[UNR];
+    if (live && (c + 1) * CHW <= Lold) {
       // every token of the sub-chunk is an old, live entry: uniform base + lane offset
       const char *kb = Kb + int64_t(c) * CHW * RB + 16 * lane;
       const char *vb = Vb + int64_t(c) * CHW * RB + 16 * lane;
 #pragma unroll
       for (int it = 0; it < UNR; ++it) {
-        kr[it] = ld16(kb + it * TPI * RB);
-        vr[it] = ld16(vb + it * TPI * RB);
+        kp[it] = kb + it * TPI * RB;
+        vp[it] = vb + it * TPI * RB;
       }
-    } else {
+    } else if (live) {
 #pragma unroll
       for (int it = 0; it < UNR; ++it) {
         const int tok = min(c * CHW + it * TPI + tg, L - 1);
         const bool isnew = append && tok == L - 1;
-        const char *ks = isnew ? Kn : Kb + int64_t(tok) * RB;
-        const char *vs = isnew ? Vn : Vb + int64_t(tok) * RB;
-        kr[it] = ld16(ks + 16 * cb);
-        vr[it] = ld16(vs + 16 * cb);
+        kp[it] = (isnew ? Kn : Kb + int64_t(tok) * RB) + 16 * cb;
+        vp[it] = (isnew ? Vn : Vb + int64_t(tok) * RB) + 16 * cb;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < UNR; ++it) {
+        kp[it] = Kb;
+        vp[it] = Vb;
       }
     }
-    const int t1 = min(c * CHW + (lane % CHW), max(Lold - 1, 0));
-    mv = MROW ? mrow[t1] : 0.f;
-    if (VOTES) vv = vrow[t1];
+#pragma unroll
+    for (int it = 0; it < UNR; ++it) {
+      kr[it] = ld16g(kp[it]);
+      vr[it] = ld16g(vp[it]);
+    }
   }
 };
 
