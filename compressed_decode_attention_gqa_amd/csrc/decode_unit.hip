@@ -286,7 +286,6 @@ void k_decode_unit(const StepArgs a) {
     for (int s = 0; s < PF; ++s) {
       const bool cur = cs[s] < nsub;
       if (cur) {
-        more = true;
         const int c = sub_of(cs[s]);
         const bool tail = (c + 1) * CHW > L;
         // scope arrays of this sub-chunk into LDS
@@ -395,7 +394,9 @@ void k_decode_unit(const StepArgs a) {
       // loop, which they keep without a copy that would wait for the loads
       const bool live = nc < nsub;
       W.issue(kr[s], vr[s], mv[s], vv[s], live ? sub_of(nc) : 0, live);
+      more |= live;
     }
+    // out once no slot got a sub-chunk: the last pass's refills are all the one row
     if (!more) break;
   }
 
