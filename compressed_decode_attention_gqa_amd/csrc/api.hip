@@ -378,7 +378,7 @@ MomentEvictLayout moment_evict_layout(int n_scopes, int cap) {
 
 // ------------------------------------------------------- KeepKV prefill merging
 struct PrefillLayout {
-  size_t status, meta, rec, total;
+  size_t status, meta, rec, sum, total;
 };
 
 PrefillLayout prefill_layout(int n_scopes, int cap) {
@@ -388,6 +388,7 @@ PrefillLayout prefill_layout(int n_scopes, int cap) {
   l.status = o; o = align_up(o + 256);
   l.meta = o;   o = align_up(o + n * 16);
   l.rec = o;    o = align_up(o + n * 64);
+  l.sum = o;    o = align_up(o + n * 32);
   l.total = o;
   return l;
 }
@@ -850,6 +851,7 @@ int32_t kvc_keepkv_prefill_merge_marked(const kvc_cache *cache, const kvc_merge 
   p.n_merged = n_merged;
   p.meta = at<char>(ws, l.meta);
   p.rec = at<char>(ws, l.rec);
+  p.sum = at<char>(ws, l.sum);
   p.status = at<int32_t>(ws, l.status);
   hipEvent_t *marks = events ? reinterpret_cast<hipEvent_t *>(const_cast<void **>(events)) : nullptr;
   if (kvc::launch_prefill_merge(p, cache->dtype, static_cast<hipStream_t>(stream), marks) != hipSuccess)
@@ -1040,6 +1042,7 @@ int32_t kvc_keepkv_refresh_marked(const kvc_cache *cache, const void *host_k, co
   p.n_merged = n_merged;
   p.meta = at<char>(ws, l.prefill + pl.meta);
   p.rec = at<char>(ws, l.prefill + pl.rec);
+  p.sum = at<char>(ws, l.prefill + pl.sum);
   p.status = at<int32_t>(ws, l.prefill + pl.status);
   if (kvc::launch_prefill_merge(p, c->dtype, hs, nullptr) != hipSuccess) return KVC_ERR_DEVICE;
   if (mark(3) != hipSuccess) return KVC_ERR_DEVICE;

@@ -59,6 +59,7 @@ constexpr int PL_NS = 8;         // row steps per batch of the merge pass (a pow
 constexpr int PL_NQ = 16;        // stale rows recomputed per pass: one 16-row MFMA operator tile
 constexpr int PL_TODO = 256;     // stale rows collected per recomputation round
 constexpr int PL_SCAN = 8;       // rows per thread per load batch of the head scan
+constexpr int PL_CAND = 1024;    // rows whose list may change, queued per merge pass (more: handled in place)
 constexpr int STALE = -2;        // slot value of a stale row's entries (entry 0 holds the bound)
 constexpr int NOPOS = 0x7fffffff;
 
@@ -149,6 +150,53 @@ __device__ __forceinline__ void rec_store_stale(const PrefillMergeArgs &a, int64
   for (int k = 0; k < PK; ++k) st16(rec_at(a, row) + 16 * k, ent_pack(bound, STALE, NOPOS));
 }
 
+// 32-byte row summaries, what the merge loop reads of a row in every pass (the list itself
+// only when it may change): [0, 8) the key norm (float64), [8, 12) the position, [12, 16) the
+// cosine of the list's last entry rounded down to a float (-inf: no entry), [16, 24) the
+// head's cosine or a stale row's bound, [24, 32) the entries' partner slots (16 bits each;
+// SUM_NONE: no entry, SUM_STALE: a stale row). Slots fit 16 bits: at most
+// PREFILL_MAX_ROWS = 32768 of them.
+constexpr uint32_t SUM_NONE = 0xffffu, SUM_STALE = 0xfffeu;
+static_assert(PREFILL_MAX_ROWS <= 0xfffe, "slots of a scope fit 16 bits below the markers");
+
+__device__ __forceinline__ char *sum_at(const PrefillMergeArgs &a, int64_t row) {
+  return static_cast<char *>(a.sum) + row * 32;
+}
+
+// The largest float not above c.
+__device__ __forceinline__ float float_below(double c) {
+  const float f = float(c);
+  return double(f) > c ? nextafterf(f, -INFINITY) : f;
+}
+
+// The list-dependent half of a summary (and the last entry's bound) after a list is stored.
+__device__ __forceinline__ void sum_store_list(const PrefillMergeArgs &a, int64_t row, const double (&c)[PK],
+                                               const int (&ss)[PK]) {
+  double last = -INFINITY;
+  uint32_t part[PK];
+#pragma unroll
+  for (int k = 0; k < PK; ++k) {
+    if (ss[k] >= 0) last = c[k];
+    part[k] = ss[k] >= 0 ? uint32_t(ss[k]) : SUM_NONE;
+  }
+  const double hd = ss[0] >= 0 ? c[0] : -INFINITY;
+  reinterpret_cast<float *>(sum_at(a, row))[3] = float_below(last);
+  st16(sum_at(a, row) + 16, u32x4{uint32_t(__double2loint(hd)), uint32_t(__double2hiint(hd)),
+                                  part[0] | (part[1] << 16), part[2] | (part[3] << 16)});
+}
+
+__device__ __forceinline__ void sum_store_stale(const PrefillMergeArgs &a, int64_t row, double bound) {
+  reinterpret_cast<float *>(sum_at(a, row))[3] = -INFINITY;
+  st16(sum_at(a, row) + 16, u32x4{uint32_t(__double2loint(bound)), uint32_t(__double2hiint(bound)),
+                                  SUM_STALE | (SUM_STALE << 16), SUM_STALE | (SUM_STALE << 16)});
+}
+
+// Does a summary's partner field (two words) hold slot s?
+__device__ __forceinline__ bool sum_has(uint32_t pa, uint32_t pb, int s) {
+  const uint32_t u = uint32_t(s);
+  return (pa & 0xffffu) == u || (pa >> 16) == u || (pb & 0xffffu) == u || (pb >> 16) == u;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_pm_prep(PrefillMergeArgs p) {
   const int sc = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
@@ -170,6 +218,10 @@ __global__ __launch_bounds__(256) void k_pm_prep(PrefillMergeArgs p) {
   int pp[PK], ss[PK];
   list_clear(c, pp, ss);
   rec_store(p, slot, c, pp, ss);
+  // the summary: norm, position, an empty list
+  const u32x4 m0 = ent_pack(sqrt(n), pos, 0);
+  st16(sum_at(p, slot), u32x4{m0.x, m0.y, m0.z, uint32_t(__float_as_int(-INFINITY))});
+  sum_store_list(p, slot, c, ss);
   if (i < L) p.evict[slot] = 0;
 }
 
@@ -291,6 +343,7 @@ __global__ __launch_bounds__(PM_NT, 1) void k_pm_rows(PrefillMergeArgs p) {
       for (int k = 0; k < PK; ++k)
         if (sh.m.s[wv][tid][k] >= 0) pk_insert(c, pp, ss, sh.m.c[wv][tid][k], sh.m.p[wv][tid][k], sh.m.s[wv][tid][k]);
     rec_store(p, so + rb + tid, c, pp, ss);
+    sum_store_list(p, so + rb + tid, c, ss);
   }
 }
 
@@ -351,7 +404,11 @@ struct LoopLds {
   int todo[PL_TODO];
   double th_c[PL_TODO];           // the recomputed rows' new heads (cosine, partner slot and position)
   int th_s[PL_TODO], th_p[PL_TODO], th_pos[PL_TODO];
-  int n_todo, n_live, gidx;
+  double cand_c[PL_CAND];         // rows of a merge pass whose list may change: the merged key's cosine,
+  int cand_row[PL_CAND], cand_pos[PL_CAND];   // the row's slot and position
+  double xb[PL_NT];               // each thread's largest stale bound below the head, and its row
+  int xr[PL_NT];                  // (-1 once it is taken into the recomputation)
+  int n_todo, n_live, gidx, n_cand;
 };
 
 // The best list head (largest cosine, ties to the lower row position) and the two largest
@@ -381,6 +438,13 @@ struct Heads {
   __device__ __forceinline__ void row(double c0, int s0, int p0, int pi, int r) {
     if (s0 >= 0) offer(c0, pi, r, s0, p0);
     else if (s0 == STALE) bound(c0);
+  }
+  // the same from a row's summary (halves s0, s1); the head partner's position is not
+  // in it (the chosen head's is looked up afterwards)
+  __device__ __forceinline__ void sum_row(const u32x4 &s0, const u32x4 &s1, int r) {
+    const uint32_t h0 = s1.z & 0xffffu;
+    if (h0 == SUM_STALE) bound(ent_c(s1));
+    else if (h0 != SUM_NONE) offer(ent_c(s1), int(s0.z), r, int(h0), NOPOS);
   }
   __device__ __forceinline__ void take(const Heads &o) {
     if (o.s >= 0) offer(o.c, o.p, o.s, o.sj, o.pj);
@@ -492,26 +556,27 @@ __device__ __forceinline__ void scan_heads(const PrefillMergeArgs &p, LoopLds &s
   m.clear();
   for (int k0 = 0; k0 < n_live; k0 += PL_NT * PL_SCAN) {
     int jr[PL_SCAN];
-    u32x4 er[PL_SCAN], mr[PL_SCAN];
+    u32x4 s0[PL_SCAN], s1[PL_SCAN];
 #pragma unroll
     for (int u = 0; u < PL_SCAN; ++u) {
       const int k = k0 + u * PL_NT + tid;
       jr[u] = k < n_live ? sh.live[k] : -1;
       if (jr[u] >= 0) {
-        er[u] = ld16(rec_at(p, so + jr[u]));
-        mr[u] = ld16(meta_at(p, so + jr[u]));
+        s0[u] = ld16(sum_at(p, so + jr[u]));
+        s1[u] = ld16(sum_at(p, so + jr[u]) + 16);
       } else {
-        er[u] = mr[u] = u32x4{0u, 0u, 0xffffffffu, 0u};
+        s0[u] = s1[u] = u32x4{0u, 0u, SUM_NONE, SUM_NONE};
       }
     }
 #pragma unroll
     for (int u = 0; u < PL_SCAN; ++u)
-      if (jr[u] >= 0) m.row(ent_c(er[u]), int(er[u].z), int(er[u].w), int(mr[u].z), jr[u]);
+      if (jr[u] >= 0) m.sum_row(s0[u], s1[u], jr[u]);
   }
   heads_to_lds(sh, m, lane, wave);
   __syncthreads();
   h.clear();
   heads_from_lds(sh, h);
+  if (h.s >= 0) h.pj = p.pos[so + h.sj];   // the head partner's position (not in the summaries)
 }
 
 // Stale rows recomputed in full against every candidate, on the float64 MFMA: the keys of
@@ -541,7 +606,8 @@ __device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLd
     for (int r = 0; r < 4; ++r) {
       const int k = tb + tq + 4 * r;
       jr[r] = k < n_live ? int(sh.live[k]) : -1;
-      mr[r] = jr[r] >= 0 ? ld16(meta_at(p, so + jr[r])) : u32x4{0u, 0u, 0u, 0u};
+      // the summary's first half: norm and position
+      mr[r] = jr[r] >= 0 ? ld16(sum_at(p, so + jr[r])) : u32x4{0u, 0u, 0u, 0u};
     }
     fm_d4 acc = fm_d4{0.0, 0.0, 0.0, 0.0};
     op16_apply<T>(sh.rop, lane, kr, acc);
@@ -578,6 +644,7 @@ __device__ __forceinline__ void pass_recompute(const PrefillMergeArgs &p, LoopLd
       for (int k = 0; k < PK; ++k)
         if (sh.ls[tid][w][k] >= 0) pk_insert(c, pp, ss, sh.lc[tid][w][k], sh.lp[tid][w][k], sh.ls[tid][w][k]);
     rec_store(p, so + sh.qrow[tid], c, pp, ss);
+    sum_store_list(p, so + sh.qrow[tid], c, ss);
     sh.th_c[b + tid] = c[0];
     sh.th_s[b + tid] = ss[0];
     sh.th_p[b + tid] = pp[0];
@@ -627,8 +694,11 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       if (tid == 0) sh.n_todo = 0;
       __syncthreads();
       // stale rows whose bound reaches the best head are recomputed; the others' bounds are kept
+      // (each thread's three largest: its largest row may fill a spare row of the recomputation)
       Heads rest;
       rest.clear();
+      double xb1 = -INFINITY, xb2 = -INFINITY, xb3 = -INFINITY;
+      int xr1 = -1;
       for (int k0 = 0; k0 < n_live; k0 += PL_NT * PL_SCAN) {
         int jr[PL_SCAN];
         u32x4 er[PL_SCAN];
@@ -636,18 +706,79 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
         for (int u = 0; u < PL_SCAN; ++u) {
           const int k = k0 + u * PL_NT + tid;
           jr[u] = k < n_live ? int(sh.live[k]) : -1;
-          er[u] = jr[u] >= 0 ? ld16(rec_at(p, so + jr[u])) : u32x4{0u, 0u, 0xffffffffu, 0u};
+          // the summary's second half: head (a stale row's bound) and partner slots
+          er[u] = jr[u] >= 0 ? ld16(sum_at(p, so + jr[u]) + 16) : u32x4{0u, 0u, SUM_NONE, SUM_NONE};
         }
 #pragma unroll
         for (int u = 0; u < PL_SCAN; ++u) {
-          if (jr[u] < 0 || int(er[u].z) != STALE) continue;
-          if (ent_c(er[u]) >= h.c) {
+          if (jr[u] < 0 || (er[u].z & 0xffffu) != SUM_STALE) continue;
+          const double b = ent_c(er[u]);
+          if (b >= h.c) {
             const int t = atomicAdd(&sh.n_todo, 1);
             if (t < PL_TODO) sh.todo[t] = jr[u];
+          } else if (b > xb1) {
+            xb3 = xb2;
+            xb2 = xb1;
+            xb1 = b;
+            xr1 = jr[u];
+          } else if (b > xb2) {
+            xb3 = xb2;
+            xb2 = b;
           } else {
-            rest.bound(ent_c(er[u]));
+            xb3 = fmax(xb3, b);
           }
         }
+      }
+      // A recomputation pass streams every key for up to PL_NQ rows: when fewer rows must be
+      // recomputed, the stale rows with the largest bounds below the head (each thread's
+      // largest) fill the pass, since they are the next ones the choice may need.
+      sh.xb[tid] = xb1;
+      sh.xr[tid] = xr1;
+      __syncthreads();
+      if (wave == 0) {
+        const int nt0 = min(sh.n_todo, PL_TODO);
+        if (nt0 < PL_NQ) {
+          constexpr int PER = PL_NT / 64;
+          double v[PER];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) v[i] = sh.xr[lane + 64 * i] >= 0 ? sh.xb[lane + 64 * i] : -INFINITY;
+          int added = 0;
+          for (int r = nt0; r < PL_NQ; ++r) {
+            double bv = -INFINITY;
+            int bi = -1;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+              if (v[i] > bv) {
+                bv = v[i];
+                bi = lane + 64 * i;
+              }
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const double v2 = __shfl_xor(bv, o);
+              const int i2 = __shfl_xor(bi, o);
+              if (v2 > bv || (v2 == bv && i2 >= 0 && (bi < 0 || i2 < bi))) {
+                bv = v2;
+                bi = i2;
+              }
+            }
+            if (bi < 0) break;   // no stale row left
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+              if (bi == lane + 64 * i) v[i] = -INFINITY;
+            if (lane == 0) {
+              sh.todo[r] = sh.xr[bi];
+              sh.xr[bi] = -1;
+            }
+            ++added;
+          }
+          if (lane == 0) sh.n_todo = nt0 + added;
+        }
+      }
+      __syncthreads();
+      {
+        const bool taken = xr1 >= 0 && sh.xr[tid] < 0;
+        rest.bound(taken ? xb2 : xb1);
+        rest.bound(taken ? xb3 : xb2);
       }
       heads_to_lds(sh, rest, lane, wave);
       __syncthreads();
@@ -661,7 +792,7 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
           const int row = q < nq ? sh.todo[b + q] : -1;
           op16_put(sh.rop, q, x, row >= 0 ? double(load_elem<T>(Kb, int64_t(row) * HD + x)) : 0.0);
           if (x == 0 && row >= 0) {
-            const u32x4 m = ld16(meta_at(p, so + row));
+            const u32x4 m = ld16(sum_at(p, so + row));
             sh.qn[q] = ent_c(m);
             sh.qrow[q] = row;
             sh.qpos[q] = int(m.z);
@@ -743,6 +874,7 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       if (lane == 0) {
         const double nk = sqrt(n2);
         st16(meta_at(p, so + surv), ent_pack(nk, ps, 1));
+        *reinterpret_cast<double *>(sum_at(p, so + surv)) = nk;
         reinterpret_cast<int *>(meta_at(p, so + gone))[3] = 0;
         p.votes[so + surv] = vote_e + vote_c;
         if (p.m) p.m[so + surv] = m_c + m_e;
@@ -754,6 +886,7 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
         sh.qn[0] = nk;
       }
     }
+    if (tid == 0) sh.n_cand = 0;
     __syncthreads();
     // ---- the merged key against every candidate: its own list, the other rows' lists, and
     // the heads for the next merge
@@ -772,6 +905,64 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       // total of step own (two lanes per step; the first of them takes the row)
       const int own = perm_head<16, NS>(e);
       const bool lead = perm_rep_lane<16, NS>(own) == e;
+      // Row jo's list after the merge (cs: the merged key's cosine with it): it drops an entry
+      // of the merged pair, takes the merged entry when that beats one of its entries, or goes
+      // stale; the list and its summary are rewritten only when they change.
+      auto list_update = [&](int jo, int pj, double cs, Heads &hq) {
+        const u32x4 r0 = ld16(rec_at(p, so + jo)), r1 = ld16(rec_at(p, so + jo) + 16);
+        const u32x4 r2 = ld16(rec_at(p, so + jo) + 32), r3 = ld16(rec_at(p, so + jo) + 48);
+        double oc[PK] = {ent_c(r0), ent_c(r1), ent_c(r2), ent_c(r3)};
+        int os[PK] = {int(r0.z), int(r1.z), int(r2.z), int(r3.z)};
+        int opp[PK] = {int(r0.w), int(r1.w), int(r2.w), int(r3.w)};
+        bool change = os[0] == -1;
+#pragma unroll
+        for (int k = 0; k < PK; ++k)
+          change |= os[k] >= 0 && (os[k] == surv || os[k] == gone || pm_better(cs, ps, oc[k], opp[k]));
+        if (!change) {
+          hq.row(oc[0], os[0], opp[0], pj, jo);
+          return;
+        }
+        double jc[PK];
+        int jp[PK], js[PK];
+        list_clear(jc, jp, js);
+        int n = 0;
+        bool any = false;
+        double last_c = -INFINITY, kept_c = -INFINITY;
+        int last_p = NOPOS, kept_p = NOPOS;
+#pragma unroll
+        for (int k = 0; k < PK; ++k) {
+          if (os[k] < 0) continue;
+          any = true;
+          last_c = oc[k];
+          last_p = opp[k];
+          if (os[k] == surv || os[k] == gone) continue;
+          pk_insert(jc, jp, js, oc[k], opp[k], os[k]);
+          kept_c = oc[k];
+          kept_p = opp[k];
+          ++n;
+        }
+        bool stale = false;
+        if (n > 0) {
+          // the merged entry joins when it ranks above the kept list's last entry
+          if (pm_better(cs, ps, kept_c, kept_p)) pk_insert(jc, jp, js, cs, ps, surv);
+        } else if (any && pm_better(cs, ps, last_c, last_p)) {
+          // every other partner ranks below the old last entry, so below the merged one
+          pk_insert(jc, jp, js, cs, ps, surv);
+        } else {
+          stale = true;
+        }
+        if (stale) {
+          const double b = any ? last_c : INFINITY;
+          rec_store_stale(p, so + jo, b);
+          sum_store_stale(p, so + jo, b);
+          jc[0] = b;
+          js[0] = STALE;
+        } else {
+          rec_store(p, so + jo, jc, jp, js);
+          sum_store_list(p, so + jo, jc, js);
+        }
+        hq.row(jc[0], js[0], jp[0], pj, jo);
+      };
       for (int k0 = 0; k0 < n_live; k0 += PL_W * 4 * NS) {
         Chunk8<T> kc[NS];
 #pragma unroll
@@ -780,17 +971,13 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
           if (k < n_live) kc[i].load(Kc + int64_t(sh.live[k]) * HD * ES, e);
           else kc[i].zero();
         }
-        // this lane's row: step own of its group
+        // this lane's row: step own of its group; its summary (no list)
         const int ko = k0 + (wave * NS + own) * 4 + gi;
         const int jo = (lead && ko < n_live) ? sh.live[ko] : -1;
-        u32x4 mt = u32x4{0u, 0u, 0u, 0u}, r0, r1, r2, r3;
-        r0 = r1 = r2 = r3 = u32x4{0u, 0u, 0xffffffffu, 0u};
+        u32x4 s0 = u32x4{0u, 0u, 0u, 0u}, s1 = u32x4{0u, 0u, SUM_NONE, SUM_NONE};
         if (jo >= 0) {
-          mt = ld16(meta_at(p, so + jo));
-          r0 = ld16(rec_at(p, so + jo));
-          r1 = ld16(rec_at(p, so + jo) + 16);
-          r2 = ld16(rec_at(p, so + jo) + 32);
-          r3 = ld16(rec_at(p, so + jo) + 48);
+          s0 = ld16(sum_at(p, so + jo));
+          s1 = ld16(sum_at(p, so + jo) + 16);
         }
         double part[NS];
 #pragma unroll
@@ -804,63 +991,36 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
         const double mine = preduce<16, NS, 0>(part);
         if (jo == gone) sh.gidx = ko;
         if (jo >= 0 && jo != surv && jo != gone) {
-          const double nj = ent_c(mt);
-          const int pj = int(mt.z);
+          const double nj = ent_c(s0);
+          const int pj = int(s0.z);
           const double den = nk * nj;
           const double cs = den > 0.0 ? mine / den : 0.0;
           pk_offer(lc, lp, ls, cs, pj, jo);
-          double oc[PK] = {ent_c(r0), ent_c(r1), ent_c(r2), ent_c(r3)};
-          int os[PK] = {int(r0.z), int(r1.z), int(r2.z), int(r3.z)};
-          int opp[PK] = {int(r0.w), int(r1.w), int(r2.w), int(r3.w)};
-          // does the list change: an entry of the merged pair in it, the merged entry above
-          // one of its entries, or a list without entries
-          bool change = os[0] == -1;
-#pragma unroll
-          for (int k = 0; k < PK; ++k)
-            change |= os[k] >= 0 && (os[k] == surv || os[k] == gone || pm_better(cs, ps, oc[k], opp[k]));
-          if (change) {
-            double jc[PK];
-            int jp[PK], js[PK];
-            list_clear(jc, jp, js);
-            int n = 0;
-            bool any = false;
-            double last_c = -INFINITY, kept_c = -INFINITY;
-            int last_p = NOPOS, kept_p = NOPOS;
-#pragma unroll
-            for (int k = 0; k < PK; ++k) {
-              if (os[k] < 0) continue;
-              any = true;
-              last_c = oc[k];
-              last_p = opp[k];
-              if (os[k] == surv || os[k] == gone) continue;
-              pk_insert(jc, jp, js, oc[k], opp[k], os[k]);
-              kept_c = oc[k];
-              kept_p = opp[k];
-              ++n;
-            }
-            bool stale = false;
-            if (n > 0) {
-              // the merged entry joins when it ranks above the kept list's last entry
-              if (pm_better(cs, ps, kept_c, kept_p)) pk_insert(jc, jp, js, cs, ps, surv);
-            } else if (any && pm_better(cs, ps, last_c, last_p)) {
-              // every other partner ranks below the old last entry, so below the merged one
-              pk_insert(jc, jp, js, cs, ps, surv);
+          const uint32_t h0 = s1.z & 0xffffu;
+          if (h0 == SUM_STALE) {
+            hn.bound(ent_c(s1));   // a stale row keeps its bound
+          } else if (h0 == SUM_NONE || sum_has(s1.z, s1.w, surv) || sum_has(s1.z, s1.w, gone) ||
+                     cs >= double(__int_as_float(int(s0.w)))) {
+            // the list may change (no entry, an entry of the merged pair, or the merged entry
+            // at least as close as its last entry): after the pass
+            const int t = atomicAdd(&sh.n_cand, 1);
+            if (t < PL_CAND) {
+              sh.cand_c[t] = cs;
+              sh.cand_row[t] = jo;
+              sh.cand_pos[t] = pj;
             } else {
-              stale = true;
+              list_update(jo, pj, cs, hn);
             }
-            if (stale) {
-              const double b = any ? last_c : INFINITY;
-              rec_store_stale(p, so + jo, b);
-              jc[0] = b;
-              js[0] = STALE;
-            } else {
-              rec_store(p, so + jo, jc, jp, js);
-            }
-            hn.row(jc[0], js[0], jp[0], pj, jo);
           } else {
-            hn.row(oc[0], os[0], opp[0], pj, jo);
+            hn.sum_row(s0, s1, jo);   // unchanged
           }
         }
+      }
+      // ---- the rows whose list may change, with their lists loaded together
+      __syncthreads();
+      {
+        const int nc = min(sh.n_cand, PL_CAND);
+        for (int t = tid; t < nc; t += PL_NT) list_update(sh.cand_row[t], sh.cand_pos[t], sh.cand_c[t], hn);
       }
       // the merged row's list: best PK of the wave, then of the waves
       double wc_[PK];
@@ -881,6 +1041,7 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       final_list(sh, 0, lane, fc, fp, fs);
       if (tid == 0) {
         rec_store(p, so + surv, fc, fp, fs);
+        sum_store_list(p, so + surv, fc, fs);
         const int g = sh.gidx;
         if (g >= 0 && g < n_live && sh.live[g] == gone) sh.live[g] = sh.live[n_live - 1];
         else p.status[0] = -7;   // cannot happen: the removed slot was a listed candidate
@@ -888,6 +1049,8 @@ __global__ __launch_bounds__(PL_NT, 1) void k_pm_loop(PrefillMergeArgs p) {
       h.clear();
       h.row(fc[0], fs[0], fp[0], ps, surv);
       heads_from_lds(sh, h);
+      // the chosen head's partner position (summaries do not carry it)
+      if (h.s >= 0) h.pj = p.pos[so + h.sj];
     }
     --n_live;
     --live;

@@ -73,6 +73,7 @@ struct PrefillMergeArgs {
   int32_t *pairs, *n_merged;
   void *meta;               // [n_scopes][capacity] 16 bytes: key norm (float64), position, candidate flag
   void *rec;                // [n_scopes][capacity] 64-byte partner lists: 4 x (cosine, slot, position)
+  void *sum;                // [n_scopes][capacity] 32-byte row summaries the merge loop reads per pass
   int32_t *status;
 };
 
