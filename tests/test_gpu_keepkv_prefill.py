@@ -187,3 +187,63 @@ def test_prefill_merge_full_size_sampled():
                             L0 - n_rep, protect_from, row_dtype="bf16", choose=follow)
         assert len(res["pairs"]) == n_rep
         print(f"full-size prefill merge: head {sc}, first {n_rep} merges follow the oracle", flush=True)
+
+
+def test_prefill_merge_many_exact_ties():
+    """Heads whose keys take two values (1300 copies of one, 236 of the other): merging two copies
+    gives the same key, so every copy ties the merged key at its list's last entry and a merge
+    pass finds more rows whose list may change than it queues (they are handled in the pass).
+    Checked: exactly L - B merges per head, votes conserved, protected rows untouched, removed
+    slots flagged once; the first 16 merges of two heads replayed in the oracle (each GPU pair the
+    largest cosine, or within 1e-6 of it)."""
+    S, L0, B = 4, 1536, 600
+    protect_from = L0 - 32
+    gen = torch.Generator().manual_seed(77)
+    rows = torch.randn((S, 2, D), generator=gen).to(torch.bfloat16)
+    cls = torch.zeros((S, L0), dtype=torch.long)
+    for sc in range(S):
+        cls[sc, torch.randperm(L0, generator=gen)[:236]] = 1
+    K = torch.stack([rows[sc][cls[sc]] for sc in range(S)]).contiguous()
+    V = torch.randn((S, L0, D), generator=gen).to(torch.bfloat16)
+    cache = kvc.Cache(k=K.view(S, 1, L0, D).cuda(), v=V.view(S, 1, L0, D).cuda(),
+                      pos=torch.arange(L0, dtype=torch.int32).repeat(S, 1).cuda(),
+                      m=torch.zeros((S, L0), dtype=torch.float32).cuda(),
+                      length=torch.full((S,), L0, dtype=torch.int32).cuda(),
+                      votes=torch.ones((S, L0), dtype=torch.int32).cuda())
+    q = torch.randn((S, 4, D), generator=gen).to(torch.bfloat16).cuda().contiguous()
+    pre_k = bits(cache.k[:, 0])
+    evict = torch.zeros((S, L0), dtype=torch.uint8, device="cuda")
+    pairs = torch.full((S, L0, 2), -1, dtype=torch.int32, device="cuda")
+    n_merged = torch.zeros((S,), dtype=torch.int32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_keepkv_prefill_workspace_size(cache))
+    kvc.kvc_keepkv_prefill_merge(cache, kvc.merge_desc(q, 4, SCALE), B, protect_from, evict, pairs, n_merged, ws=ws)
+    torch.cuda.synchronize()
+    assert kvc.kvc_workspace_status(ws) == 0
+    nm, ev, pr = n_merged.cpu().numpy(), evict.cpu().numpy(), pairs.cpu().numpy()
+    vt = cache.votes.cpu().numpy()
+    post_k = bits(cache.k[:, 0])
+    assert np.all(nm == L0 - B)
+    for sc in range(S):
+        gone = ev[sc].astype(bool)
+        assert gone.sum() == L0 - B and vt[sc][~gone].sum() == L0
+        assert not np.any(gone[protect_from:])
+        assert np.array_equal(post_k[sc, protect_from:], pre_k[sc, protect_from:])
+        assert np.array_equal(np.sort(pr[sc, :L0 - B, 1]), np.flatnonzero(gone))
+    n_rep = 16
+    pos = np.arange(L0)
+    for sc in (0, 3):
+        Kh = oracle.to_f64(pre_k[sc], "bf16")
+
+        def follow(step, Kc, cand):
+            s_, g_ = int(pr[sc, step, 0]), int(pr[sc, step, 1])
+            assert cand[s_] and cand[g_]
+            bi, bj, bc = best_pair(Kc, pos, cand)
+            cg = cosine_matrix(Kc[[s_, g_]])[0, 1]
+            assert {s_, g_} == {bi, bj} or cg >= bc - BAND * abs(bc), (sc, step, cg, bc)
+            return s_, g_
+
+        qh = oracle.to_f64(bits(q[sc]), "bf16")
+        res = prefill_merge(Kh, np.zeros_like(Kh), np.ones(L0, dtype=np.int64), pos, np.zeros(L0), qh, SCALE,
+                            L0 - n_rep, protect_from, row_dtype="bf16", choose=follow)
+        assert len(res["pairs"]) == n_rep
+    print(f"prefill merge with exact ties: merges {list(nm)}", flush=True)
