@@ -284,6 +284,8 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   const int CH = kvc::decode_chunk_tokens(c->dtype);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int plan = decode_plan(c, G, a.mode, budget, max_len);
+  // split path, merge mode, no flags or moments out: the merge kernels select the entry
+  a.merge_select = plan != KVC_PLAN_ONE_LAUNCH && a.mode == 2 && !evict_out && !mom ? 1 : 0;
   if (plan == KVC_PLAN_ONE_LAUNCH) {
     a.n_splits = 1;
     a.lds_len = max_len;
@@ -328,6 +330,17 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
     mg.e_stride = c->capacity;
     mg.part_cos = at<double>(ws, d.merge_cos);
     mg.part_slot = at<int32_t>(ws, d.merge_slot);
+    if (a.merge_select) {
+      mg.cand_key = a.cand_key;
+      mg.cand_slot = a.cand_slot;
+      mg.cand_pos = a.cand_pos;
+      mg.n_score_chunks = a.n_score_chunks;
+      mg.score_chunk = a.score_chunk;
+      mg.append = a.append;
+      mg.budget = budget;
+      mg.status = a.status;
+      mg.cand_max = ceil_div(max_len, a.score_chunk);
+    }
     if (kvc::launch_merge(cache_args(c), a.flags, mg, hs) != hipSuccess) return KVC_ERR_DEVICE;
   }
   return KVC_OK;

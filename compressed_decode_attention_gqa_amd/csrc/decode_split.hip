@@ -282,7 +282,8 @@ static hipError_t launch_split_tg(const StepArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((k_epi_score<G, Geo::CHW>), dim3(chunks, a.n_scopes), dim3(WG), 0, st, a);
   // the finish kernel selects, folds and moves; a call that cannot evict (budget >= capacity),
   // appends nothing and reports no flags has nothing for it to do
-  const bool finish = a.append || a.mode == 2 || a.evict_out || a.bulk || (a.mode != 0 && a.budget < a.capacity);
+  const bool finish = !a.merge_select &&
+                      (a.append || a.mode == 2 || a.evict_out || a.bulk || (a.mode != 0 && a.budget < a.capacity));
   if (finish) hipLaunchKernelGGL((k_epi_finish<T, G>), dim3(a.n_scopes), dim3(WG), 0, st, a);
   return hipGetLastError();
 }

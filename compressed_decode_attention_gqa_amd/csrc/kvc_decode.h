@@ -85,6 +85,9 @@ struct StepArgs {
   // (vote-weighted) of unit gu at wsum[gu * wsum_stride + i]
   double *wsum;
   int32_t wsum_stride;
+  // split path in merge mode: the merge kernels take the selection from the chunk
+  // candidates, so no finish kernel runs (no flags reported, no moments folded)
+  int32_t merge_select;
 };
 
 int decode_chunk_tokens(int dtype);

@@ -293,6 +293,7 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
     if (tid == 0) {
       a.status[0] = -4;
       if (a.bulk) a.bulk[scope].run = 0;
+      if (a.mode == 2) a.list[sc] = -1;   // nothing for the merge kernels
     }
     return;
   }

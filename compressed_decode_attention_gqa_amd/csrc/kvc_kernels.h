@@ -25,7 +25,15 @@ struct MergeArgs {
   int32_t n_splits;
   double *part_cos;
   int32_t *part_slot;       // (slot, position) of each range's partner
-  int32_t *status;          // standalone path: set to -3 for a scope with several flagged entries
+  int32_t *status;          // set to -3 for a scope with several flagged entries (standalone path) or
+                            // more than one entry over the budget, -4 for a length over the capacity
+  // Non-null: the merge kernels take the decode step's selection themselves (no finish ran):
+  // the live length is len + append, and a scope then one entry over `budget` merges the entry
+  // of the lowest (utility, position) key over the score kernel's chunk candidates.
+  const uint64_t *cand_key;
+  const int32_t *cand_slot, *cand_pos;
+  int32_t n_score_chunks, score_chunk, append, budget;
+  int32_t cand_max;         // chunks of the live-length bound the launch was sized for (loaded at entry)
 };
 
 struct MomentArgs {

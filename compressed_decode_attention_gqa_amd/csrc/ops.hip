@@ -178,6 +178,68 @@ __device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &s
   return sh_e;
 }
 
+// The decode step's selection in the merge kernels (MergeArgs::cand_key set): the
+// entry of the lowest (utility, position) key over the scope's score-chunk
+// candidates when the live length L is exactly one over the budget, else -1.
+// Wave-level (all lanes active). The lane's first candidate is loaded at kernel
+// entry, beside the length, for the chunks of the launch's length bound (those
+// past the live length are masked once it is known); only chunks past 64 lanes
+// or past the bound load afterwards.
+struct MergeCand {
+  uint64_t key;
+  uint32_t pos;
+  int slot;
+};
+
+__device__ __forceinline__ MergeCand merge_cand_load(const MergeArgs &mg, int scope) {
+  const int lane = threadIdx.x & 63;
+  MergeCand m{~0ull, 0xffffffffu, -1};
+  if (lane < min(mg.cand_max, mg.n_score_chunks)) {
+    const int64_t ci = int64_t(scope) * mg.n_score_chunks + lane;
+    m.key = mg.cand_key[ci];
+    m.pos = uint32_t(mg.cand_pos[ci]);
+    m.slot = mg.cand_slot[ci];
+  }
+  return m;
+}
+
+__device__ int merge_step_pick(const MergeArgs &mg, MergeCand m, int scope, int L, int cap) {
+  if (L > cap || L - mg.budget != 1) return -1;
+  const int lane = threadIdx.x & 63;
+  const int nch = (L + mg.score_chunk - 1) / mg.score_chunk;
+  uint64_t best = ~0ull;
+  uint32_t bpos = 0xffffffffu;
+  int bslot = -1;
+  if (lane < nch && lane < mg.cand_max) {
+    best = m.key;
+    bpos = m.pos;
+    bslot = m.slot;
+  }
+  for (int ch = lane < mg.cand_max ? lane + 64 : lane; ch < nch; ch += 64) {
+    const int64_t ci = int64_t(scope) * mg.n_score_chunks + ch;
+    const uint64_t key = mg.cand_key[ci];
+    const uint32_t p = uint32_t(mg.cand_pos[ci]);
+    const int sl = mg.cand_slot[ci];
+    if (key_pos_less(key, p, best, bpos)) {
+      best = key;
+      bpos = p;
+      bslot = sl;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t k2 = shfl_xor_u64(best, o);
+    const uint32_t p2 = __shfl_xor(bpos, o);
+    const int s2 = __shfl_xor(bslot, o);
+    if (key_pos_less(k2, p2, best, bpos)) {
+      best = k2;
+      bpos = p2;
+      bslot = s2;
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(bslot);
+}
+
 // Token slot order for the lane-permuted reduction of N per-token partial sums
 // over a token's row of lanes: slot i of lane l holds token i ^ merge_perm(l).
 // The exchange stages pair lane l with l ^ 16 (32-lane rows), l ^ 15, l ^ 7,
@@ -205,29 +267,39 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
   const int scope = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cb = lane % LPT, tg = lane / LPT, own = merge_perm<LPT, MU>(cb);
   const int64_t so = int64_t(scope) * c.capacity;
-  const int L = c.len[scope];
+  // (a step's length over the capacity merges nothing: no token range then)
+  const MergeCand cand0 = mg.cand_key ? merge_cand_load(mg, scope) : MergeCand{};
+  const int Lstep = c.len[scope] + (mg.cand_key ? mg.append : 0);
+  const int L = Lstep <= c.capacity ? Lstep : 0;
   const char *Kb = reinterpret_cast<const char *>(c.k) + int64_t(scope) * c.scope_stride * RB;
   const int per = (L + gridDim.x - 1) / gridDim.x;
   const int t0 = blockIdx.x * per, t1 = min(L, t0 + per);
 
-  u32x4 kv[MU];
-  int pv;
-  auto issue = [&](int b0) {
+  // two batches of loads in flight per wave (A and B in turn); a load past the range reads the
+  // range's last row (a line already in L2), so every batch is issued the same way and its
+  // registers need no copy that would wait for it
+  u32x4 kvA[MU], kvB[MU];
+  int pvA, pvB;
+  auto issue = [&](u32x4 (&kv)[MU], int &pv, int b0) {
 #pragma unroll
     for (int i = 0; i < MU; ++i) {
-      const int tok = b0 + (i ^ own) * STR + tg;
-      kv[i] = tok < t1 ? ld16(Kb + int64_t(tok) * RB + 16 * cb) : u32x4(0u);
+      const int tok = min(b0 + (i ^ own) * STR + tg, t1 - 1);
+      kv[i] = ld16(Kb + int64_t(max(tok, 0)) * RB + 16 * cb);
     }
-    const int mine = b0 + own * STR + tg;
-    pv = mine < t1 ? c.pos[so + mine] : 0;
+    const int mine = min(b0 + own * STR + tg, t1 - 1);
+    pv = c.pos[so + max(mine, 0)];
   };
   int base = t0 + wave * TPI;
-  issue(base);   // these loads do not depend on the flagged slot
-  const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride] : merge_flagged(evict + so, L, sh.e);
+  // these loads do not depend on the flagged slot
+  issue(kvA, pvA, base);
+  issue(kvB, pvB, base + MU * STR);
+  const int e = mg.cand_key ? merge_step_pick(mg, cand0, scope, Lstep, c.capacity)
+                : mg.e_slot  ? mg.e_slot[int64_t(scope) * mg.e_stride]
+                             : merge_flagged(evict + so, L, sh.e);
 
   double best = -INFINITY;
   int bslot = -1, bpos = 0x7fffffff;
-  if (e >= 0) {
+  if (e >= 0 && t0 < t1) {
     const u32x4 kw = ld16(Kb + int64_t(e) * RB + 16 * cb);
     double ke[EPV];
     double ne = 0.0;
@@ -237,7 +309,8 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
       ne = fma(ke[j], ke[j], ne);
     }
     ne = sqrt(group_sum_f64<LPT>(ne));
-    for (;;) {
+    // the cosines of one batch with k_e; each lane ends with its token's (whole sums)
+    auto batch = [&](const u32x4 (&kv)[MU], int pv, int b0) {
       double pd[MU], pn[MU];
 #pragma unroll
       for (int i = 0; i < MU; ++i) {
@@ -253,7 +326,7 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
       }
       const double dot = preduce<LPT, MU, 0>(pd);
       const double nn = preduce<LPT, MU, 0>(pn);
-      const int tok = base + own * STR + tg;
+      const int tok = b0 + own * STR + tg;
       if (tok < t1 && tok != e) {
         const double den = ne * sqrt(nn);
         const double cs = den > 0.0 ? dot / den : 0.0;
@@ -263,9 +336,16 @@ __global__ __launch_bounds__(WG) void k_merge_part(CacheArgs c, const uint8_t *e
           bpos = pv;
         }
       }
+    };
+    for (;;) {
+      batch(kvA, pvA, base);
+      issue(kvA, pvA, base + 2 * MU * STR);
       base += MU * STR;
       if (base >= t1) break;
-      issue(base);
+      batch(kvB, pvB, base);
+      issue(kvB, pvB, base + 2 * MU * STR);
+      base += MU * STR;
+      if (base >= t1) break;
     }
   }
   // workgroup argmax
@@ -311,7 +391,8 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   constexpr int RB = HD * int(sizeof(T)), NV = RB / 16;
   const int scope = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t so = int64_t(scope) * c.capacity;
-  const int L = c.len[scope];
+  const MergeCand cand0 = mg.cand_key ? merge_cand_load(mg, scope) : MergeCand{};
+  const int L = c.len[scope] + (mg.cand_key ? mg.append : 0);
   const T *Kb = reinterpret_cast<const T *>(c.k) + int64_t(scope) * c.scope_stride * HD;
   const T *Vb = reinterpret_cast<const T *>(c.v) + int64_t(scope) * c.scope_stride * HD;
   // the ranges' partners (at most 64 ranges) load beside the flagged slot
@@ -324,9 +405,28 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     pp = mg.part_slot[2 * pi + 1];
   }
   int n_flagged = 1;
-  const int e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride]
-                          : merge_flagged(evict + so, L, sh.e, &sh.n_flagged, &n_flagged);
-  if (e < 0) return;
+  int e;
+  if (mg.cand_key) {
+    // the step's selection, and the length and status a finish would have set; the
+    // length is written after a barrier, once every wave has read it
+    if (L > c.capacity) {
+      if (tid == 0 && mg.status) mg.status[0] = -4;
+      return;
+    }
+    e = merge_step_pick(mg, cand0, scope, L, c.capacity);
+    if (e < 0) {
+      __syncthreads();
+      if (tid == 0) {
+        if (L - mg.budget > 1 && mg.status) mg.status[0] = -3;   // one merge per step
+        c.len[scope] = L;
+      }
+      return;
+    }
+  } else {
+    e = mg.e_slot ? mg.e_slot[int64_t(scope) * mg.e_stride]
+                  : merge_flagged(evict + so, L, sh.e, &sh.n_flagged, &n_flagged);
+    if (e < 0) return;
+  }
   if (n_flagged > 1) {   // one merge per scope and call: leave the scope as it is
     if (tid == 0 && mg.status) mg.status[0] = -3;
     return;
@@ -348,7 +448,10 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   }
   __syncthreads();
   const int cs = sh.best_slot[0];
-  if (cs < 0) return;   // a single live entry: nothing to merge into
+  if (cs < 0) {   // a single live entry: nothing to merge into
+    if (tid == 0 && mg.cand_key) c.len[scope] = L;
+    return;
+  }
 
   // Dropping e lets the last live slot fill its hole. The merged entry goes
   // straight to where it ends: slot e when the partner is that last slot (then

@@ -38,7 +38,9 @@ def f32(x) -> float:
 class DeviceRun:
     """A workload's cache on the GPU plus the buffers one decode step needs."""
 
-    def __init__(self, wl: synth.Workload, capacity=None, moments=None, device="cuda", max_len=0):
+    def __init__(self, wl: synth.Workload, capacity=None, moments=None, device="cuda", max_len=0, flags=True):
+        """flags: the step reports the evicted flags (evict_out); without them a merge-mode step on
+        the split path leaves the selection to the merge kernels."""
         self.wl = wl
         t = synth.cache_tensors(wl, device, capacity=capacity)
         self.scales = t["scales"]
@@ -50,7 +52,7 @@ class DeviceRun:
         self.out = torch.empty((S, U, wl.G, wl.d), device=device)
         self.lse = torch.empty((S, U, wl.G), device=device)
         self.s = torch.empty((S, C), device=device)
-        self.evict = torch.zeros((S, C), dtype=torch.uint8, device=device)
+        self.evict = torch.zeros((S, C), dtype=torch.uint8, device=device) if flags else None
         self.ws = kvc.workspace(kvc.kvc_decode_workspace_size(self.cache, wl.G, max_len), device)
         self.scale = f32(1.0 / np.sqrt(wl.d))
         self.alpha = f32(wl.alpha)
@@ -97,7 +99,7 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
     out = bits(run.out[torch.as_tensor(scopes, device=run.out.device)])
     lse = bits(run.lse[torch.as_tensor(scopes, device=run.out.device)])
     s_gpu = bits(run.s[torch.as_tensor(scopes, device=run.out.device)])
-    ev_gpu = bits(run.evict[torch.as_tensor(scopes, device=run.out.device)])
+    ev_gpu = None if run.evict is None else bits(run.evict[torch.as_tensor(scopes, device=run.out.device)])
     qh, knh, vnh = bits(q), bits(kn), bits(vn)
     prm = oracle.StepParams(scale=run.scale, rule=wl.rule, alpha=run.alpha, budget=wl.budget,
                             score=refresh, merge=merge, row_dtype=dtype, protect_from=protect_from)
@@ -130,7 +132,15 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
             stats["max_rel_s"] = max(stats["max_rel_s"], float((ds / (np.abs(s_ref) + 1e-30)).max()))
         # ---- evicted set
         E_ref = set(res.evicted_pos[0].tolist())
-        E_gpu = set(pos_all[ev_gpu[j, :L].astype(bool)].tolist())
+        Lp = int(post["len"][j])
+        ppos = post["pos"][j, :Lp].astype(np.int64)
+        E_gone = set(pos_all.tolist()) - set(ppos.tolist())      # positions the step removed
+        if ev_gpu is not None:
+            E_gpu = set(pos_all[ev_gpu[j, :L].astype(bool)].tolist())
+            assert E_gpu == E_gone, f"scope {sc}: flagged {sorted(E_gpu)} but removed {sorted(E_gone)}"
+        else:
+            E_gpu = E_gone
+        ev_slots = [i for i in range(L) if int(pos_all[i]) in E_gpu]
         assert len(E_gpu) == len(E_ref), f"scope {sc}: |E| {len(E_gpu)} vs {len(E_ref)}"
         m_ref = dict(zip(res.m_pos[0].tolist(), res.m_pre[0].tolist()))
         if E_ref != E_gpu:
@@ -140,9 +150,7 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
                     f"scope {sc}: evict sets differ at pos {p} (m {m_ref[p]!r}, cut {cut!r})")
                 stats["near_tie_flips"] += 1
         # ---- survivors: length, positions, utilities, rows, votes
-        Lp = int(post["len"][j])
         assert Lp == L - len(E_gpu), f"scope {sc}: len {Lp} vs {L - len(E_gpu)}"
-        ppos = post["pos"][j, :Lp].astype(np.int64)
         alive = sorted(set(pos_all.tolist()) - E_gpu)
         assert sorted(ppos.tolist()) == alive, f"scope {sc}: surviving positions differ"
         merged_pos = None
@@ -171,7 +179,7 @@ def check_step(run: DeviceRun, scopes, pre, post, q, kn, vn, t, refresh=True, me
                 assert int(post["votes"][j, i]) == exp_vote
         # ---- moments: fold of the GPU's own evicted rows into the GPU pre-state
         if run.mom is not None:
-            Eg = [i for i in range(L) if ev_gpu[j, i]]
+            Eg = ev_slots
             Kall = np.concatenate([oracle.to_f64(pre["k"][j][:, :L0], dtype), oracle.to_f64(knh[sc], dtype)[:, None]], 1)
             Vall = np.concatenate([oracle.to_f64(pre["v"][j][:, :L0], dtype), oracle.to_f64(vnh[sc], dtype)[:, None]], 1)
             mom_pre = {"n": 0, "sk": pre["sk"][j].astype(np.float64), "sv": pre["sv"][j].astype(np.float64),

@@ -265,28 +265,69 @@ def test_select_evict_device_wide_top_k():
 C4 = synth.WORKLOADS["c4_keepkv_votes_64k"]
 
 
-@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f32", 2)])
-def test_decode_step_c4_merge_reduced(dtype, G):
+@pytest.mark.parametrize("flags", [True, False])
+@pytest.mark.parametrize("dtype,G,budget", [("bf16", 4, 300), ("f32", 2, 300), ("bf16", 4, 700)])
+def test_decode_step_c4_merge_reduced(dtype, G, budget, flags):
     """Vote-weighted decode with a ZIP merge every step (KeepKV eqs. (7)-(12)), every scope checked.
     The f32 case drives some single-step utilities to ~1e-59, below float32's range: they are
-    stored as float32 but ranked on their float64 values, as the oracle ranks them."""
-    _say("c4 reduced", dtype, G)
-    wl = C4.scaled(batch=1, n_kv=5, context=3000, budget=300, steps=10, dtype=dtype, G=G)
-    run = DeviceRun(wl)
+    stored as float32 but ranked on their float64 values, as the oracle ranks them. 300 bf16
+    rows per scope take the one-launch kernel, the others the split path; without the flags
+    output the split path's merge kernels take the selection themselves."""
+    _say("c4 reduced", dtype, G, budget, flags)
+    wl = C4.scaled(batch=1, n_kv=5, context=3000, budget=budget, steps=10, dtype=dtype, G=G)
+    run = DeviceRun(wl, flags=flags)
     rep = lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)), merge=True)
-    _say("c4 reduced", dtype, G, rep)
+    _say("c4 reduced", dtype, G, budget, flags, rep)
     assert rep.get("merged_rows_exact", 0) > 0
 
 
-def test_decode_step_c4_full_size_sampled():
+@pytest.mark.parametrize("flags", [True, False])
+def test_decode_step_c4_full_size_sampled(flags):
     """64 scopes of 6553 voted entries (10% of 64K), a merge every step for the workload's 64
-    steps; 12 sampled scopes checked at the first step and every 8th."""
+    steps; 12 sampled scopes checked at the first step and every 8th (without the flags output
+    as the bench runs it, and with it)."""
     rng = np.random.default_rng(9)
-    run = DeviceRun(C4)
+    run = DeviceRun(C4, flags=flags)
     rep = lockstep(run, C4.steps, lambda t: sorted(rng.choice(C4.n_scopes, 12, replace=False).tolist())
                    if t == 1 or t % 8 == 0 else [], merge=True)
     _say("c4 full", rep)
     assert rep.get("merged_rows_exact", 0) > 0
+
+
+def test_merge_step_that_merges_nothing():
+    """Merge-mode steps on the split path that merge nothing (700 bf16 rows per scope): with the
+    live length after the append at most the budget the token is appended and nothing merges;
+    more than one entry over the budget reports KVC_ERR_UNSUPPORTED and keeps every entry (a
+    merge removes one per step); an append into a full cache reports KVC_ERR_CAPACITY and
+    leaves the cache as it was. The same with and without the flags output (the finish kernel's
+    bookkeeping, or the merge kernels' own), bit for bit."""
+    wl = C4.scaled(batch=1, n_kv=3, context=3000, budget=700, steps=1, G=4)
+    S = wl.n_scopes
+    for budget, capacity, status in ((702, None, 0), (698, None, -3), (690, 700, -4)):
+        states = []
+        for flags in (True, False):
+            run = DeviceRun(wl, capacity=capacity, flags=flags)
+            L0 = int(run.cache.length[0])
+            assert L0 == 700
+            assert kvc.kvc_decode_plan(run.cache, wl.G, budget=budget, merge=True) == kvc.PLAN_SPLIT
+            pre = run.snapshot(list(range(S)))
+            q, kn, vn = run.inputs(1)
+            kvc.kvc_decode_step(run.cache, kn, vn, run.t, q, wl.G, run.scale, wl.rule, run.alpha, budget, run.out,
+                                run.lse, run.s, None, kvc.merge_desc(q, wl.G, run.scale), run.evict, ws=run.ws)
+            assert kvc.kvc_workspace_status(run.ws) == status, (budget, flags)
+            post = run.snapshot(list(range(S)))
+            L = L0 if status == -4 else L0 + 1
+            assert np.all(post["len"] == L), (budget, flags)
+            for key in ("k", "v"):
+                assert np.array_equal(post[key][:, :, :L0], pre[key][:, :, :L0]), (budget, flags, key)
+            assert np.array_equal(post["pos"][:, :L0], pre["pos"][:, :L0])
+            assert np.array_equal(post["votes"][:, :L0], pre["votes"][:, :L0])
+            if L > L0:
+                assert np.array_equal(post["k"][:, 0, L0], bits(kn)[:, 0]) and np.all(post["pos"][:, L0] == run.t)
+                assert np.all(post["votes"][:, L0] == 1)
+            states.append([post[key] for key in ("len", "k", "v", "pos", "votes", "m")])
+        for a, b in zip(*states):
+            assert np.array_equal(a, b), budget
 
 
 def test_merge_keeps_the_reference_output():
