@@ -263,7 +263,10 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
 template <int G, int CH>
 __global__ __launch_bounds__(WG) void k_epi_score(const StepArgs a) {
   __shared__ ScoreLds sh;
-  epi_score<G, CH>(a, sh);
+  if (a.attn_units == 1 && a.units == 1 && a.score_chunk <= (8 / G) * WG)
+    epi_score_head<G, CH>(a, sh);
+  else
+    epi_score<G, CH>(a, sh);
 }
 
 template <typename T, int G>

@@ -280,6 +280,306 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
   }
 }
 
+// epi_score for scopes of one attention unit (per-KV-head caches), whose chunks
+// hold 2048 / G tokens, TPT = 8 / G per thread. Everything the workgroup's
+// first chunk reads -- the split partials, this workgroup's share of the output
+// partials, the chunk's sub-chunk maxima, each thread's tokens (weights, shift
+// counts, vote, utility, position) and the new token's rows -- is requested at
+// entry, beside the live length (bounded by the chunk's end within the capacity
+// and masked once the length is known), so the chunk waits on memory once. The
+// split terms exp(M_split - M) are formed one per thread and summed per head in
+// split order, so the arithmetic, its order and its results are epi_score's.
+// Chunks past the launch's first (a device length beyond the sized bound) load
+// as they go.
+template <int G, int CH>
+__device__ void epi_score_head(const StepArgs &a, ScoreLds &sh) {
+  constexpr int TPT = 8 / G;
+  constexpr int PPT = SCORE_PAIR_MAX / WG;                 // staged partials per thread
+  constexpr int SPT = (8 * WG / CH + G + WG - 1) / WG;     // sub-chunk maxima per thread
+  constexpr int OPT = 16;                                  // output partials per thread, prefetched
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.y;
+  const int cap = a.capacity;
+  const int64_t sc = int64_t(scope) * cap;
+  const bool step = a.mode != 0;
+  const bool score = a.refresh && (step || a.s != nullptr);
+  const double inv_heads = 1.0 / double(G);
+  const double alpha = double(a.alpha);
+  const float *ews = a.ews + int64_t(scope) * G * cap;
+  const uint8_t *ewsh = a.ewsh + int64_t(scope) * G * cap;
+  const int chunk = a.score_chunk;
+  const int ns = a.n_splits, P = G * ns;
+  const bool staged = P <= SCORE_PAIR_MAX;
+
+  // ---- requests at entry (none waits for the length)
+  const int Lraw = a.len[scope] + a.append;
+  double lpm[PPT], lpz[PPT];
+#pragma unroll
+  for (int r = 0; r < PPT; ++r) {
+    const int idx = tid + r * WG;
+    lpm[r] = -INFINITY;
+    lpz[r] = 0.0;
+    if (staged && idx < P) {
+      const int h = idx / ns, sp = idx - (idx / ns) * ns;
+      const int64_t pi = (int64_t(scope) * ns + sp) * G + h;
+      lpm[r] = a.partM[pi];
+      lpz[r] = a.partZ[pi];
+    }
+  }
+  // the output element (head blockIdx.x, element tid) when each workgroup has at most one head
+  const bool pre_out = staged && ns <= OPT && int(gridDim.x) >= G;
+  float po[OPT];
+  if (pre_out && int(blockIdx.x) < G && tid < HD) {
+#pragma unroll
+    for (int sp = 0; sp < OPT; ++sp)
+      po[sp] = sp < ns ? a.partO[((int64_t(scope) * ns + sp) * G + blockIdx.x) * HD + tid] : 0.f;
+  }
+  int i0 = blockIdx.x * chunk;
+  const int iend = min(cap, i0 + chunk);   // the chunk's end before the length is known
+  double lsm[SPT];
+  {
+    const int c0 = i0 / CH, nsc = i0 < iend ? (iend - 1) / CH - c0 + 1 : 0;
+#pragma unroll
+    for (int r = 0; r < SPT; ++r) {
+      const int idx = tid + r * WG;
+      lsm[r] = -INFINITY;
+      if (score && idx < nsc * G) lsm[r] = a.subM[(int64_t(scope) * a.nsub_cap + c0 + idx / G) * G + idx % G];
+    }
+  }
+  float ev[TPT][G];
+  int evs[TPT][G], pv[TPT], pp[TPT];
+  float mo[TPT];
+  auto load_tokens = [&](int j0, int j1) {
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+      const int i = j0 + tid + r * WG;
+      const bool ok = i < j1;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        ev[r][g] = (score && ok) ? ews[int64_t(g) * cap + i] : 0.f;
+        evs[r][g] = (score && ok) ? int(ewsh[int64_t(g) * cap + i]) : 0;
+      }
+      pv[r] = (score && ok && a.votes) ? a.votes[sc + i] : 1;
+      mo[r] = (step && ok) ? a.m[sc + i] : 0.f;
+      pp[r] = ok ? a.pos[sc + i] : 0;
+    }
+  };
+  load_tokens(i0, iend);
+  // the new token's rows (stored by the chunk that holds slot L - 1)
+  const int nv = a.row_bytes / 16;
+  const int64_t asrc = int64_t(scope) * a.units * a.row_bytes;
+  u32x4 ak = u32x4(0u), av = u32x4(0u);
+  if (a.append && a.units == 1 && tid < nv) {
+    ak = ld16(a.k_new + asrc + 16 * tid);
+    av = ld16(a.v_new + asrc + 16 * tid);
+  }
+  const int L = Lraw;
+  if (L > cap) return;   // reported by the finish kernel
+  const int k = step ? max(0, L - a.budget) : 0;
+  double *m64 = (step && k > 1 && a.m64) ? a.m64 + sc : nullptr;
+  int i1 = min(L, i0 + chunk);
+  int c0 = i0 / CH;
+  int nsc = i0 < L ? (i1 - 1) / CH - c0 + 1 : 0;
+
+  // ---- M per head; the split terms; Z, lse; the output weights and the chunk's factors
+  if (staged) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int idx = tid + r * WG;
+      if (idx < P) {
+        sh.pm[idx] = lpm[r];
+        sh.pz[idx] = lpz[r];
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      double M = -INFINITY;
+      for (int sp = 0; sp < ns; ++sp) M = fmax(M, sh.pm[tid * ns + sp]);
+      sh.M[tid] = M;
+    }
+    __syncthreads();
+    // exp(M_split - M) per split, and its term of Z
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int idx = tid + r * WG;
+      if (idx < P) {
+        const double pm = lpm[r];
+        const double e = pm > -INFINITY ? exp(pm - sh.M[idx / ns]) : 0.0;
+        sh.pm[idx] = e;
+        sh.pz[idx] = pm > -INFINITY ? lpz[r] * e : 0.0;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      double Z = 0.0;
+      for (int sp = 0; sp < ns; ++sp) Z += sh.pz[tid * ns + sp];
+      sh.iZ[tid] = Z > 0.0 ? 1.0 / Z : 0.0;
+      if (blockIdx.x == tid % gridDim.x) a.lse[int64_t(scope) * G + tid] = Z > 0.0 ? float(sh.M[tid] + log(Z)) : -INFINITY;
+    }
+  } else {
+    if (tid < G) {
+      double M, Z;
+      combine_head<G>(a, scope, tid, M, Z);
+      sh.M[tid] = M;
+      sh.iZ[tid] = Z > 0.0 ? 1.0 / Z : 0.0;
+      if (blockIdx.x == tid % gridDim.x) a.lse[int64_t(scope) * G + tid] = Z > 0.0 ? float(M + log(Z)) : -INFINITY;
+    }
+  }
+  __syncthreads();
+  if (staged) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int idx = tid + r * WG;
+      if (idx < P) {
+        const int h = idx / ns;
+        sh.pm[idx] = (sh.iZ[h] > 0.0 && lpm[r] > -INFINITY) ? sh.pm[idx] * sh.iZ[h] : 0.0;
+      }
+    }
+  }
+  if (score) {
+#pragma unroll
+    for (int r = 0; r < SPT; ++r) {
+      const int idx = tid + r * WG;
+      if (idx < nsc * G) {
+        const int h = idx % G;
+        sh.fac[idx] = sh.iZ[h] > 0.0 ? exp(lsm[r] - sh.M[h]) * sh.iZ[h] : 0.0;
+      }
+    }
+  }
+  __syncthreads();
+  if (pre_out) {
+    if (int(blockIdx.x) < G && tid < HD) {
+      const int h = blockIdx.x;
+      float acc = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < OPT; ++sp)
+        if (sp < ns) acc = fmaf(po[sp], float(sh.pm[h * ns + sp]), acc);
+      a.out[(int64_t(scope) * G + h) * HD + tid] = acc;
+    }
+  } else {
+    for (int idx = tid; idx < G * HD; idx += WG) {
+      const int h = idx / HD, e = idx - (idx / HD) * HD;
+      if (h % gridDim.x != blockIdx.x) continue;
+      float acc = 0.f;
+      for (int sp = 0; sp < ns; ++sp) {
+        const int64_t pi = (int64_t(scope) * ns + sp) * G + h;
+        double wgt;
+        if (staged) {
+          wgt = sh.pm[h * ns + sp];
+        } else {
+          const double pm = a.partM[pi];
+          wgt = (sh.iZ[h] > 0.0 && pm > -INFINITY) ? exp(pm - sh.M[h]) * sh.iZ[h] : 0.0;
+        }
+        acc = fmaf(a.partO[pi * HD + e], float(wgt), acc);
+      }
+      a.out[(int64_t(scope) * G + h) * HD + e] = acc;
+    }
+  }
+
+  // ---- chunks: the first from the values requested at entry, later ones load as they go
+  for (bool first = true; i0 < L; first = false) {
+    if (!first) {
+      __syncthreads();
+      if (score)
+        for (int idx = tid; idx < nsc * G; idx += WG) {
+          const int h = idx % G;
+          const double m = a.subM[(int64_t(scope) * a.nsub_cap + c0 + idx / G) * G + h];
+          sh.fac[idx] = sh.iZ[h] > 0.0 ? exp(m - sh.M[h]) * sh.iZ[h] : 0.0;
+        }
+      load_tokens(i0, i1);
+      __syncthreads();
+    }
+    uint64_t best = ~0ull;
+    uint32_t bpos = 0xffffffffu;
+    int bslot = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < TPT; ++r) {
+      const int i = i0 + tid + r * WG;
+      if (i >= i1) continue;
+      const bool isnew = a.append && i == L - 1;
+      double mval = 0.0;
+      if (score) {
+        const int p = isnew ? 1 : pv[r];
+        const double *f = sh.fac + (i / CH - c0) * G;
+        double acc = 0.0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const double x = double(ev[r][g]) * f[g];
+          acc += evs[r][g] ? x * shift_scale(evs[r][g]) : x;
+        }
+        const double sv = double(p) * acc * inv_heads;
+        if (a.s) a.s[sc + i] = float(sv);
+        if (step) {
+          const double m_old = isnew ? 0.0 : double(mo[r]);
+          mval = apply_rule(a.rule, alpha, m_old, sv);
+          a.m[sc + i] = float(mval);
+        }
+      } else if (step) {
+        mval = isnew ? 0.0 : double(mo[r]);
+      }
+      if (isnew && !(score && step)) a.m[sc + i] = 0.f;
+      if (m64) m64[i] = mval;
+      if (k == 1) {
+        const uint64_t key = orderable_f64(mval);
+        const uint32_t p = uint32_t(isnew ? a.t : pp[r]);
+        if (key_pos_less(key, p, best, bpos)) {
+          best = key;
+          bpos = p;
+          bslot = i;
+        }
+      }
+    }
+    if (k == 1) {   // (utility, position) pairs are distinct: the minimum names one slot
+      wave_min_key_pos(best, bpos, bslot);
+      if (lane == 0) {
+        sh.wkey[wave] = best;
+        sh.wslot[wave] = bslot;
+        sh.wpos[wave] = int(bpos);
+      }
+      __syncthreads();
+      if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < WG / 64; ++w) {
+          if (key_pos_less(sh.wkey[w], uint32_t(sh.wpos[w]), best, bpos)) {
+            best = sh.wkey[w];
+            bpos = uint32_t(sh.wpos[w]);
+            bslot = sh.wslot[w];
+          }
+        }
+        const int64_t ci = int64_t(scope) * a.n_score_chunks + i0 / chunk;
+        a.cand_key[ci] = best;
+        a.cand_pos[ci] = int(bpos);
+        a.cand_slot[ci] = bslot;
+      }
+    }
+    if (a.append && i0 <= L - 1 && L - 1 < i1) {
+      const int64_t arow = (int64_t(scope) * a.scope_stride + (L - 1)) * a.row_bytes;
+      if (first && a.units == 1) {
+        if (tid < nv) {
+          st16(a.k + arow + 16 * tid, ak);
+          st16(a.v + arow + 16 * tid, av);
+        }
+      } else {
+        for (int idx = tid; idx < a.units * nv; idx += WG) {
+          const int u = idx / nv, c = idx - (idx / nv) * nv;
+          const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * a.row_bytes;
+          const int64_t src = (int64_t(scope) * a.units + u) * a.row_bytes;
+          st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
+          st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
+        }
+      }
+      if (tid == 0) {
+        if (a.votes) a.votes[sc + L - 1] = 1;
+        a.pos[sc + L - 1] = a.t;
+      }
+    }
+    i0 += gridDim.x * chunk;
+    i1 = min(L, i0 + chunk);
+    c0 = i0 / CH;
+    nsc = i0 < L ? (i1 - 1) / CH - c0 + 1 : 0;
+  }
+}
+
 // ---------------------------------------------------------------- finish
 template <typename T, int G>
 __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
