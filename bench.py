@@ -804,6 +804,8 @@ def main():
                          "or one call per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read probe after the timed steps")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed timing of per-head workloads after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for counter scaling)")
     args = ap.parse_args()
@@ -959,6 +961,30 @@ def main():
                      "bytes_per_launch": bytes_per_launch, "launch_ms": launch_ms,
                      "wall_GBps": bytes_per_launch / (ms_per_step / 1e3) / 1e9},
     }
+    # The same steps replayed from a captured HIP graph (64 steps with their own inputs and
+    # positions; replays repeat them): the step's GPU time without per-call host submission,
+    # which bounds the eager rate of the latency-bound shapes. Reported beside the eager value.
+    if wl.scope != "model" and not args.no_graph:
+        gsteps = 64
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for j in range(gsteps):
+                step_call(1 + args.warmup + j % max(1, args.steps), B + 1)
+        for _ in range(3):
+            graph.replay()
+        replays = max(3, args.steps // gsteps)
+        start.record()
+        for _ in range(replays):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        g_ms = start.elapsed_time(end) / (replays * gsteps)
+        assert int(cache.length.min()) == B and int(cache.length.max()) == B
+        if kvc.kvc_workspace_status(ws) != 0:
+            raise SystemExit("device status after the graph replays")
+        result["graph"] = {"ms_per_step": g_ms, "value": tokens_per_step / (g_ms / 1e3), "steps_per_graph": gsteps,
+                           "replays": replays}
     if args.copy_calibration:
         x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         y = torch.empty_like(x)

@@ -272,7 +272,10 @@ __global__ __launch_bounds__(WG) void k_epi_score(const StepArgs a) {
 template <typename T, int G>
 __global__ __launch_bounds__(WG) void k_epi_finish(const StepArgs a) {
   __shared__ EpiLds sh;
-  epi_finish<T, G>(a, sh);
+  if (a.units == 1 && a.mode == 1)
+    epi_finish_head<T, G>(a, sh);
+  else
+    epi_finish<T, G>(a, sh);
 }
 
 template <typename T, int G>

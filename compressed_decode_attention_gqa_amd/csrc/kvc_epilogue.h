@@ -734,4 +734,141 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
   if (tid == 0) a.len[scope] = L - k;
 }
 
+// epi_finish for a full step (mode 1) on per-head scopes (one unit per scope):
+// the loads that do not depend on the evicted slot -- the score chunks'
+// candidates of the launch's length bound, the unit's moment sums, and (once
+// the length is known) the last slot's row, vote, position and utility, which
+// fill the hole -- are requested at entry, so a one-entry eviction waits on
+// memory for the candidates and then for the evicted rows only. The fold adds
+// fmaf(v_r, k_c, 0) to S and k, v to the sums as fold_slots / fold_commit do.
+// Any other case (no eviction, several, a length over the capacity) is
+// epi_finish's.
+template <typename T, int G>
+__device__ void epi_finish_head(const StepArgs &a, EpiLds &sh) {
+  constexpr int RB = HD * int(sizeof(T)), NV = RB / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int scope = blockIdx.x;
+  const int cap = a.capacity;
+  const int64_t sc = int64_t(scope) * cap;
+  // ---- requests at entry
+  const int ncmax = min(a.n_score_chunks, (a.max_len + a.score_chunk - 1) / a.score_chunk);
+  uint64_t pkey = ~0ull;
+  uint32_t ppos = 0xffffffffu;
+  int pslot = 0x7fffffff;
+  if (tid < ncmax) {
+    const int64_t ci = int64_t(scope) * a.n_score_chunks + tid;
+    pkey = a.cand_key[ci];
+    ppos = uint32_t(a.cand_pos[ci]);
+    pslot = a.cand_slot[ci];
+  }
+  const int col = 4 * (tid & 31), row0 = tid >> 5;
+  float *S = a.mom_S ? a.mom_S + int64_t(scope) * HD * HD : nullptr;
+  float4 s4[16];
+  float ssum = 0.f;
+  if (S) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s4[j] = *reinterpret_cast<const float4 *>(S + (row0 + 8 * j) * HD + col);
+    ssum = tid < HD ? a.mom_sk[int64_t(scope) * HD + tid] : a.mom_sv[int64_t(scope) * HD + tid - HD];
+  }
+  const int L = a.len[scope] + a.append;
+  if (L > cap || L - a.budget != 1 || a.mode != 1 || (a.bulk && L - a.budget > 1)) {
+    epi_finish<T, G>(a, sh);
+    return;
+  }
+  const char *Kb = a.k + int64_t(scope) * a.scope_stride * RB;
+  const char *Vb = a.v + int64_t(scope) * a.scope_stride * RB;
+  u32x4 lk = u32x4(0u), lv = u32x4(0u);
+  if (tid < NV) {
+    lk = ld16(Kb + int64_t(L - 1) * RB + 16 * tid);
+    lv = ld16(Vb + int64_t(L - 1) * RB + 16 * tid);
+  }
+  int lvote = 0, lpos = 0;
+  float lm = 0.f;
+  if (tid == 0) {
+    if (a.votes) lvote = a.votes[sc + L - 1];
+    lpos = a.pos[sc + L - 1];
+    lm = a.m[sc + L - 1];
+  }
+  if (a.bulk && tid == 0) a.bulk[scope].run = 0;
+
+  // ---- the evicted entry: the lowest (utility, position) key over the chunks
+  const int nch = (L + a.score_chunk - 1) / a.score_chunk;
+  uint64_t best = ~0ull;
+  uint32_t bpos = 0xffffffffu;
+  int bslot = 0x7fffffff;
+  if (tid < nch && tid < ncmax) {
+    best = pkey;
+    bpos = ppos;
+    bslot = pslot;
+  }
+  for (int c = tid < ncmax ? tid + WG : tid; c < nch; c += WG) {
+    const int64_t ci = int64_t(scope) * a.n_score_chunks + c;
+    const uint64_t key = a.cand_key[ci];
+    const uint32_t p = uint32_t(a.cand_pos[ci]);
+    const int sl = a.cand_slot[ci];
+    if (key_pos_less(key, p, best, bpos)) {
+      best = key;
+      bpos = p;
+      bslot = sl;
+    }
+  }
+  wave_min_key_pos(best, bpos, bslot);
+  if (lane == 0) {
+    sh.ckey[wave] = best;
+    sh.cslot[wave] = bslot;
+    sh.cpos[wave] = int(bpos);
+  }
+  __syncthreads();
+  best = sh.ckey[0];
+  bpos = uint32_t(sh.cpos[0]);
+  int e1 = sh.cslot[0];
+#pragma unroll
+  for (int w = 1; w < WG / 64; ++w) {
+    if (key_pos_less(sh.ckey[w], uint32_t(sh.cpos[w]), best, bpos)) {
+      best = sh.ckey[w];
+      bpos = uint32_t(sh.cpos[w]);
+      e1 = sh.cslot[w];
+    }
+  }
+  if (a.evict_out)
+    for (int i = tid; i < L; i += WG) a.evict_out[sc + i] = (i == e1);
+
+  // ---- fold of the evicted rows (read before the hole is filled)
+  if (S) {
+    const T *Kt = reinterpret_cast<const T *>(Kb), *Vt = reinterpret_cast<const T *>(Vb);
+    if (tid < HD) sh.fold.kb[0][tid] = load_elem<T>(Kt, int64_t(e1) * HD + tid);
+    else sh.fold.vb[0][tid - HD] = load_elem<T>(Vt, int64_t(e1) * HD + tid - HD);
+    __syncthreads();
+    const float4 k4 = *reinterpret_cast<const float4 *>(&sh.fold.kb[0][col]);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float va = sh.fold.vb[0][row0 + 8 * j];
+      float4 x = s4[j];
+      x.x += fmaf(va, k4.x, 0.f);
+      x.y += fmaf(va, k4.y, 0.f);
+      x.z += fmaf(va, k4.z, 0.f);
+      x.w += fmaf(va, k4.w, 0.f);
+      *reinterpret_cast<float4 *>(S + (row0 + 8 * j) * HD + col) = x;
+    }
+    const float add = 0.f + (tid < HD ? sh.fold.kb[0][tid] : sh.fold.vb[0][tid - HD]);
+    if (tid < HD) a.mom_sk[int64_t(scope) * HD + tid] = ssum + add;
+    else a.mom_sv[int64_t(scope) * HD + tid - HD] = ssum + add;
+    if (tid == 0) a.mom_n[scope] += 1;
+  }
+
+  // ---- the last slot fills the hole
+  if (e1 < L - 1) {
+    if (tid < NV) {
+      st16(const_cast<char *>(Kb) + int64_t(e1) * RB + 16 * tid, lk);
+      st16(const_cast<char *>(Vb) + int64_t(e1) * RB + 16 * tid, lv);
+    }
+    if (tid == 0) {
+      if (a.votes) a.votes[sc + e1] = lvote;
+      a.pos[sc + e1] = lpos;
+      a.m[sc + e1] = lm;
+    }
+  }
+  if (tid == 0) a.len[scope] = L - 1;
+}
+
 }  // namespace kvc
