@@ -161,6 +161,9 @@ __device__ __forceinline__ bool cos_better(double c1, int p1, double c2, int p2)
 
 // The flagged slot of the scope (the largest one if several), or -1; *count
 // (if non-null) receives the number of flagged slots.
+// The flags are read 16 bytes per load over the 16-byte-aligned middle of
+// [0, L) and byte by byte at its two ends; each thread reports its largest
+// flagged slot and its count once.
 __device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &sh_e, int *sh_n = nullptr,
                                              int *count = nullptr) {
   if (threadIdx.x == 0) {
@@ -168,11 +171,36 @@ __device__ __forceinline__ int merge_flagged(const uint8_t *flags, int L, int &s
     if (sh_n) *sh_n = 0;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < L; i += WG)
+  const int head = min(L, int((16u - (reinterpret_cast<uintptr_t>(flags) & 15u)) & 15u));
+  const int nvec = (L - head) / 16, body_end = head + 16 * nvec;
+  int e = -1, n = 0;
+  for (int i = threadIdx.x; i < head; i += WG)
     if (flags[i]) {
-      atomicMax(&sh_e, i);
-      if (sh_n) atomicAdd(sh_n, 1);
+      e = max(e, i);
+      ++n;
     }
+  for (int i = body_end + threadIdx.x; i < L; i += WG)
+    if (flags[i]) {
+      e = max(e, i);
+      ++n;
+    }
+  for (int v = threadIdx.x; v < nvec; v += WG) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(flags + head + 16 * v);
+    if ((x.x | x.y | x.z | x.w) != 0u) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const uint32_t w = b < 4 ? x.x : b < 8 ? x.y : b < 12 ? x.z : x.w;
+        if ((w >> (8 * (b & 3))) & 255u) {
+          e = max(e, head + 16 * v + b);
+          ++n;
+        }
+      }
+    }
+  }
+  if (e >= 0) {
+    atomicMax(&sh_e, e);
+    if (sh_n) atomicAdd(sh_n, n);
+  }
   __syncthreads();
   if (count) *count = *sh_n;
   return sh_e;

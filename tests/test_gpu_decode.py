@@ -569,14 +569,17 @@ def test_decode_step_c3_full_size_sampled(path):
     assert kvc.kvc_workspace_status(run.ws) == 0
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_compact_merge_standalone_matches_oracle(dtype):
+@pytest.mark.parametrize("dtype,placement", [("f32", "random"), ("bf16", "random"), ("bf16", "ends")])
+def test_compact_merge_standalone_matches_oracle(dtype, placement):
     """kvc_compact in merge mode (KeepKV eqs. (7), (10), (12)) on inputs far from underflow:
     per scope the flagged entry is merged into its largest-cosine partner (oracle
     cosine_partner, zip_merge on the group-mean logits), rows within one ulp of the oracle's
     rounded rows, votes and utilities add, every other row keeps its bits; a scope with two
-    flagged entries is left untouched and the workspace status reports KVC_ERR_UNSUPPORTED."""
-    _say("compact merge", dtype)
+    flagged entries is left untouched and the workspace status reports KVC_ERR_UNSUPPORTED.
+    Scope rows of 520 flag bytes start 8 bytes off a 16-byte boundary every other scope, so
+    the flag scan's 16-byte middle and byte-wise ends both run; "ends" puts the flags on the
+    first slot, the last slot and slot 9, and scope 3's two flags on its first and last."""
+    _say("compact merge", dtype, placement)
     rng = np.random.default_rng(21)
     S, cap, G, d = 4, 520, 4, 128
     lens = np.array([500, 333, 2, 480], dtype=np.int32)
@@ -590,10 +593,14 @@ def test_compact_merge_standalone_matches_oracle(dtype):
     cache = kvc.Cache(k=K, v=V, pos=pos, m=m, length=length, votes=votes)
     q = torch.from_numpy(rng.standard_normal((S, 1, G, d)).astype(np.float32)).to(tdt).cuda()
     evict = torch.zeros((S, cap), dtype=torch.uint8, device="cuda")
-    flagged = [int(rng.integers(0, L)) for L in lens]
+    if placement == "ends":
+        flagged = [0, int(lens[1]) - 1, min(9, int(lens[2]) - 1), 0]
+    else:
+        flagged = [int(rng.integers(0, L)) for L in lens]
     for s, e in enumerate(flagged):
         evict[s, e] = 1
-    evict[3, (flagged[3] + 7) % lens[3]] = 1          # two flags: unsupported, scope untouched
+    second = int(lens[3]) - 1 if placement == "ends" else (flagged[3] + 7) % lens[3]
+    evict[3, second] = 1                               # two flags: unsupported, scope untouched
     scale = f32(1 / np.sqrt(d))
     pre = {k: bits(x) for k, x in (("k", K), ("v", V), ("votes", votes), ("pos", pos), ("m", m))}
     ws = kvc.workspace(kvc.kvc_compact_workspace_size(cache))
