@@ -90,16 +90,15 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
   uint8_t *ewsh = a.ewsh + int64_t(gu) * G * cap;
   double *subM = a.subM + int64_t(gu) * a.nsub_cap * G;
 
-  // queries scaled by tau (exact in float64), slot i holding head i ^ myh
-  double qf[G][EPV];
+  // queries: one 16-byte load per head (slot i holding head i ^ myh), issued before the
+  // first row loads and converted after them, so waiting for them leaves the rows in flight
+  u32x4 qv[G];
   {
-    const T *qp = reinterpret_cast<const T *>(a.q) + int64_t(gu) * G * HD;
+    const char *qp = a.q + int64_t(gu) * G * HD * int(sizeof(T));
 #pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-      for (int j = 0; j < EPV; ++j)
-        qf[i][j] = double(load_elem<T>(qp, (i ^ myh) * HD + cb * EPV + j)) * a.scale;
+    for (int i = 0; i < G; ++i) qv[i] = ld16g(qp + ((i ^ myh) * HD + cb * EPV) * int(sizeof(T)));
   }
+  __builtin_amdgcn_sched_barrier(0);
   float oacc[G][EPV];
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -116,10 +115,18 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
   int vv[PF];
   // (every slot is issued once per sub-chunk it serves, clamped to the split's
   // last sub-chunk, so the loads past the range re-read lines already in L2)
-  if (c0 < c1) {
+  // (issued whether or not the split has sub-chunks -- an empty one loads the unit's first
+  // row -- so no path reaches the loop with fewer loads outstanding than another)
 #pragma unroll
-    for (int s = 0; s < PF; ++s) W.issue(kr[s], vr[s], mv[s], vv[s], min(c0 + wave + NW * s, c1 - 1));
-  }
+  for (int s = 0; s < PF; ++s)
+    W.issue(kr[s], vr[s], mv[s], vv[s], c0 < c1 ? min(c0 + wave + NW * s, c1 - 1) : 0, c0 < c1);
+  __builtin_amdgcn_sched_barrier(0);
+  // scaled by tau (exact in float64)
+  double qf[G][EPV];
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int j = 0; j < EPV; ++j) qf[i][j] = double(TR::get(qv[i], j)) * a.scale;
   for (int base = c0 + wave; base < c1; base += NW * PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
