@@ -16,7 +16,7 @@
 namespace {
 
 constexpr int kHD = 128;
-constexpr int kTargetWorkgroups = 2048;   // workgroups per launch to aim for (merge, bulk chunks)
+constexpr int kTargetWorkgroups = 2048;   // workgroups per launch to aim for (bulk chunks, moves)
 constexpr int kSplitWorkgroups = 256;     // split-K attention workgroups (512 threads) per launch
 constexpr int kMinSubChunksPerSplit = 16;
 constexpr int kMaxSubChunksPerSplit = 512;
@@ -25,6 +25,10 @@ constexpr int kMaxSubChunksPerSplit = 512;
 constexpr int kScoreWork = 2048;
 constexpr int kScoreChunkMin = 64;
 constexpr int kMergeSplitsMax = 64;
+// Cosine-pass ranges: about two workgroups per CU in one round, so each wave's two batches of
+// key loads stay in flight through a long range (2048 workgroups in two rounds took 25.5 us at
+// 64 heads x 6554 slots, 512 in one 20.2 us, 256 20.8 us).
+constexpr int kMergeWorkgroups = 512;
 static_assert(kMergeSplitsMax <= 64, "k_merge_finish reads one range partner per lane of one wave");
 // One workgroup per scope (no split-K) once there are this many single-unit
 // scopes to spread over the 256 CUs, each scope's live length is bounded so
@@ -116,7 +120,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   const int CHW = kvc::decode_unit_chunk_tokens(c->dtype);
   d.nsub_cap = ceil_div(c->capacity, std::min(CH, CHW));
   d.n_splits = split_count(int(nu), ceil_div(c->capacity, CH));
-  d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
+  d.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kMergeWorkgroups, c->n_scopes)));
   // bulk eviction: slot chunks per scope (<= 256), fold splits per unit, move blocks per scope
   bulk_chunking(c->n_scopes, c->capacity, d.bulk_chunks, d.bulk_chunk);
   const int64_t units_total = int64_t(c->n_scopes) * c->units_per_scope;
@@ -355,7 +359,7 @@ struct CompactLayout {
 
 CompactLayout compact_layout(const kvc_cache *c) {
   CompactLayout l{};
-  l.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kTargetWorkgroups, c->n_scopes)));
+  l.merge_splits = std::max(1, std::min(kMergeSplitsMax, ceil_div(kMergeWorkgroups, c->n_scopes)));
   size_t o = 0;
   l.status = o;   o = align_up(o + 256);
   l.list = o;     o = align_up(o + size_t(c->n_scopes) * c->capacity * 4);
