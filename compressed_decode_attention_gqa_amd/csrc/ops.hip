@@ -432,6 +432,33 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     ps = mg.part_slot[2 * pi];
     pp = mg.part_slot[2 * pi + 1];
   }
+  // what does not depend on the pair, requested before it is known: the last slot's row
+  // (threads HD .. HD + 2 NV - 1), vote, utility and position, which fill the dropped
+  // slot; the query heads' elements lane and lane + 64 (the two waves that form the
+  // reference logits)
+  const bool Lok = L >= 1 && L <= c.capacity;
+  const int last = L - 1;
+  const int mvc = tid - HD;   // threads HD .. HD + 2 NV - 1 carry the moved row
+  const bool mv_thread = mvc >= 0 && mvc < 2 * NV;
+  u32x4 mvec = u32x4(0u);
+  if (Lok && mv_thread)
+    mvec = ld16(reinterpret_cast<const char *>(mvc < NV ? Kb : Vb) + int64_t(last) * RB + 16 * (mvc % NV));
+  int vl = 0, pl = 0;
+  float ml = 0.f;
+  if (Lok && tid == 0) {
+    if (c.votes) vl = c.votes[so + last];
+    if (c.m) ml = c.m[so + last];
+    pl = c.pos[so + last];
+  }
+  constexpr int GQ = 8;   // query heads per KV head, at most
+  double qd[GQ][2];
+  if (wave < 2) {
+    const T *q = reinterpret_cast<const T *>(mg.q) + int64_t(scope) * mg.G * HD;
+#pragma unroll
+    for (int g = 0; g < GQ; ++g)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) qd[g][jj] = g < mg.G ? double(load_elem<T>(q, g * HD + lane + 64 * jj)) : 0.0;
+  }
   int n_flagged = 1;
   int e;
   if (mg.cand_key) {
@@ -485,7 +512,6 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
   // straight to where it ends: slot e when the partner is that last slot (then
   // nothing else moves), else the partner's slot, with the last slot's row
   // moved into e unless e is the last slot itself.
-  const int last = L - 1;
   const int dst = cs == last ? e : cs;
   const bool move = e < last && cs != last;
   // every row this call reads, before any of it is written
@@ -496,37 +522,34 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     vek = double(load_elem<T>(Vb, int64_t(e) * HD + tid));
     vck = double(load_elem<T>(Vb, int64_t(cs) * HD + tid));
   }
-  const int mvc = tid - HD;   // threads HD .. HD + 2 NV - 1 carry the moved row
-  const bool mover = move && mvc >= 0 && mvc < 2 * NV;
-  const char *mrow = reinterpret_cast<const char *>(mvc < NV ? Kb : Vb) + int64_t(last) * RB + 16 * (mvc % NV);
-  u32x4 mvec = u32x4(0u);
-  if (mover) mvec = ld16(mrow);
-  int ve = 1, vc = 1, vl = 0, pcs = 0, pl = 0;
-  float me = 0.f, mc = 0.f, ml = 0.f;
+  const bool mover = move && mv_thread;
+  char *mrow = reinterpret_cast<char *>(mvc < NV ? c.k : c.v) +
+               (int64_t(scope) * c.scope_stride * HD) * int(sizeof(T)) + int64_t(last) * RB + 16 * (mvc % NV);
+  int ve = 1, vc = 1, pcs = 0;
+  float me = 0.f, mc = 0.f;
   if (tid == 0) {
     if (c.votes) {
       ve = c.votes[so + e];
       vc = c.votes[so + cs];
-      vl = c.votes[so + last];
     }
     if (c.m) {
       me = c.m[so + e];
       mc = c.m[so + cs];
-      ml = c.m[so + last];
     }
     pcs = c.pos[so + cs];
-    pl = c.pos[so + last];
   }
 
   // reference logits: mean over the G query heads of scale * q_g . k
   if (wave < 2) {
     const int x = wave == 0 ? e : cs;
-    const T *q = reinterpret_cast<const T *>(mg.q) + int64_t(scope) * mg.G * HD;
     double acc = 0.0;
-    for (int j = lane; j < HD; j += 64) {
-      const double kx = double(load_elem<T>(Kb, int64_t(x) * HD + j));
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const double kx = double(load_elem<T>(Kb, int64_t(x) * HD + lane + 64 * jj));
       double qs = 0.0;
-      for (int g = 0; g < mg.G; ++g) qs += double(load_elem<T>(q, g * HD + j)) * kx;
+#pragma unroll
+      for (int g = 0; g < GQ; ++g)
+        if (g < mg.G) qs += qd[g][jj] * kx;
       acc += qs;
     }
 #pragma unroll
@@ -555,7 +578,7 @@ __global__ __launch_bounds__(WG) void k_merge_finish(CacheArgs c, const uint8_t 
     store_elem<T>(Kw, int64_t(dst) * HD + tid, round_once<T>(sh.wgt[2] * kek + sh.wgt[3] * kck));
     store_elem<T>(Vw, int64_t(dst) * HD + tid, round_once<T>(sh.wgt[0] * vek + sh.wgt[1] * vck));
   }
-  if (mover) st16(const_cast<char *>(mrow) + int64_t(e - last) * RB, mvec);
+  if (mover) st16(mrow + int64_t(e - last) * RB, mvec);
   if (tid == 0) {
     if (c.votes) c.votes[so + dst] = ve + vc;
     if (c.m) c.m[so + dst] = mc + me;
