@@ -74,7 +74,7 @@ struct DecodeLayout {
   int bulk_chunks, bulk_chunk, fold_splits, move_blocks;
   size_t status, partM, partZ, partO, fac, subM, ews, ewsh, m64, flags, list, list2, cand_key, cand_slot, cand_pos;
   int n_score_chunks;
-  size_t merge_cos, merge_slot, bulk_state, bulk_cnt, bulk_hist, fpart, total;
+  size_t merge_cos, merge_slot, bulk_state, bulk_cnt, bulk_hist, fpart, steplen, total;
 };
 
 // Split-K workgroups per attention unit: one round of workgroups over the CUs
@@ -147,6 +147,7 @@ DecodeLayout decode_layout(const kvc_cache *c, int G, int attn_units) {
   d.cand_slot = o;  o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 4);
   d.cand_pos = o;   o = align_up(o + size_t(c->n_scopes) * d.n_score_chunks * 4);
   d.bulk_state = o; o = align_up(o + size_t(c->n_scopes) * sizeof(kvc::BulkScope));
+  d.steplen = o;    o = align_up(o + size_t(c->n_scopes) * 4);
   d.bulk_cnt = o;   o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 8);
   d.bulk_hist = o;  o = align_up(o + size_t(c->n_scopes) * d.bulk_chunks * 256 * 4);
   d.fpart = o;
@@ -280,6 +281,10 @@ int run_decode(const kvc_cache *c, const void *k_new, const void *v_new, int32_t
   a.cand_key = at<uint64_t>(ws, d.cand_key);
   a.cand_slot = at<int32_t>(ws, d.cand_slot);
   a.cand_pos = at<int32_t>(ws, d.cand_pos);
+  // multi-unit scopes without moments: the hole fill's rows over up to 16 finish
+  // workgroups per scope (16 units each at least), with the score kernel's length copy
+  a.steplen = at<int32_t>(ws, d.steplen);
+  a.fin_blocks = (c->units_per_scope > 1 && !mom) ? std::max(1, std::min(16, c->units_per_scope / 16)) : 1;
   {
     const int heads = attn_units * G;   // <= 64
     const int chunk = std::max(kScoreChunkMin, kScoreWork / heads);

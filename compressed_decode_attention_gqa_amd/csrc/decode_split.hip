@@ -297,7 +297,9 @@ static hipError_t launch_split_tg(const StepArgs &a, hipStream_t st) {
   // appends nothing and reports no flags has nothing for it to do
   const bool finish = !a.merge_select &&
                       (a.append || a.mode == 2 || a.evict_out || a.bulk || (a.mode != 0 && a.budget < a.capacity));
-  if (finish) hipLaunchKernelGGL((k_epi_finish<T, G>), dim3(a.n_scopes), dim3(WG), 0, st, a);
+  // (several finish workgroups per scope only with the score kernel's length copy)
+  const int fin_blocks = a.steplen ? std::max(1, a.fin_blocks) : 1;
+  if (finish) hipLaunchKernelGGL((k_epi_finish<T, G>), dim3(a.n_scopes, fin_blocks), dim3(WG), 0, st, a);
   return hipGetLastError();
 }
 

@@ -88,6 +88,10 @@ struct StepArgs {
   // split path in merge mode: the merge kernels take the selection from the chunk
   // candidates, so no finish kernel runs (no flags reported, no moments folded)
   int32_t merge_select;
+  // finish workgroups per scope (> 1: multi-unit scopes without moments, the hole
+  // fill's rows spread over them) and the live length the score kernel saw
+  int32_t fin_blocks;
+  int32_t *steplen;
 };
 
 int decode_chunk_tokens(int dtype);

@@ -72,6 +72,23 @@ __device__ __forceinline__ void combine_head(const StepArgs &a, int gu, int g, d
   }
 }
 
+// The new token's K and V rows of units y, y + ny, ... of the scope into slot L - 1.
+__device__ __forceinline__ void append_rows_wg(const StepArgs &a, int scope, int L, int y = 0, int ny = 1) {
+  const int64_t rb = a.row_bytes;
+  copy_rows_wg(
+      (a.units - y + ny - 1) / ny, a.row_bytes / 16,
+      [&](int i, const char *&ks, const char *&vs) {
+        const int64_t off = (int64_t(scope) * a.units + y + i * ny) * rb;
+        ks = a.k_new + off;
+        vs = a.v_new + off;
+      },
+      [&](int i, char *&kd, char *&vd) {
+        const int64_t off = (int64_t(scope) * a.scope_stride + int64_t(y + i * ny) * a.unit_stride + (L - 1)) * rb;
+        kd = a.k + off;
+        vd = a.v + off;
+      });
+}
+
 // ---------------------------------------------------------------- score
 // InertiaKV §3.1 eq. (1): s(i) = mean over the scope's Ua*G attention heads of
 // a_{h,i} = p_i e_{h,i} F_{h,c(i)}, where e = exp(l - M_sub) is the weight the
@@ -87,6 +104,7 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
   const int scope = blockIdx.y;
   const int Ua = a.attn_units, cap = a.capacity, H = Ua * G;
   const int L = a.len[scope] + a.append;
+  if (a.steplen && blockIdx.x == 0 && tid == 0) a.steplen[scope] = L;   // for a split finish
   if (L > cap) return;   // reported by the finish kernel
   const int64_t sc = int64_t(scope) * cap;
   const int gu0 = scope * Ua;
@@ -262,22 +280,14 @@ __device__ void epi_score(const StepArgs &a, ScoreLds &sh) {
         a.cand_slot[ci] = bslot;
       }
     }
-    // the appended token's rows and slot arrays, by the chunk that holds it
-    if (a.append && i0 <= L - 1 && L - 1 < i1) {
-      const int row_bytes = a.row_bytes, nv = row_bytes / 16;
-      for (int idx = tid; idx < a.units * nv; idx += WG) {
-        const int u = idx / nv, c = idx - (idx / nv) * nv;
-        const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * row_bytes;
-        const int64_t src = (int64_t(scope) * a.units + u) * row_bytes;
-        st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
-        st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
-      }
-      if (tid == 0) {
-        if (a.votes) a.votes[sc + L - 1] = 1;
-        a.pos[sc + L - 1] = a.t;
-      }
+    // the appended token's vote and position, by the chunk that holds it
+    if (a.append && i0 <= L - 1 && L - 1 < i1 && tid == 0) {
+      if (a.votes) a.votes[sc + L - 1] = 1;
+      a.pos[sc + L - 1] = a.t;
     }
   }
+  // its rows: every workgroup of the scope copies units blockIdx.x, blockIdx.x + gridDim.x, ...
+  if (a.append && int(blockIdx.x) < a.units) append_rows_wg(a, scope, L, blockIdx.x, gridDim.x);
 }
 
 // epi_score for scopes of one attention unit (per-KV-head caches), whose chunks
@@ -374,6 +384,7 @@ __device__ void epi_score_head(const StepArgs &a, ScoreLds &sh) {
     av = ld16(a.v_new + asrc + 16 * tid);
   }
   const int L = Lraw;
+  if (a.steplen && blockIdx.x == 0 && tid == 0) a.steplen[scope] = L;   // for a split finish
   if (L > cap) return;   // reported by the finish kernel
   const int k = step ? max(0, L - a.budget) : 0;
   double *m64 = (step && k > 1 && a.m64) ? a.m64 + sc : nullptr;
@@ -560,13 +571,7 @@ __device__ void epi_score_head(const StepArgs &a, ScoreLds &sh) {
           st16(a.v + arow + 16 * tid, av);
         }
       } else {
-        for (int idx = tid; idx < a.units * nv; idx += WG) {
-          const int u = idx / nv, c = idx - (idx / nv) * nv;
-          const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * a.row_bytes;
-          const int64_t src = (int64_t(scope) * a.units + u) * a.row_bytes;
-          st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
-          st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
-        }
+        append_rows_wg(a, scope, L);
       }
       if (tid == 0) {
         if (a.votes) a.votes[sc + L - 1] = 1;
@@ -581,14 +586,85 @@ __device__ void epi_score_head(const StepArgs &a, ScoreLds &sh) {
 }
 
 // ---------------------------------------------------------------- finish
+// The evicted entry of a one-entry eviction: the lowest (utility, position) key
+// over the score chunks' candidates (the whole workgroup; every thread returns it).
+__device__ int finish_pick(const StepArgs &a, EpiLds &sh, int scope, int L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (L + a.score_chunk - 1) / a.score_chunk;
+  uint64_t best = ~0ull;
+  uint32_t bpos = 0xffffffffu;
+  int bslot = 0x7fffffff;
+  for (int c = tid; c < nch; c += WG) {
+    const int64_t ci = int64_t(scope) * a.n_score_chunks + c;
+    const uint64_t key = a.cand_key[ci];
+    const uint32_t p = uint32_t(a.cand_pos[ci]);
+    if (key_pos_less(key, p, best, bpos)) {
+      best = key;
+      bpos = p;
+      bslot = a.cand_slot[ci];
+    }
+  }
+  wave_min_key_pos(best, bpos, bslot);
+  if (lane == 0) {
+    sh.ckey[wave] = best;
+    sh.cslot[wave] = bslot;
+    sh.cpos[wave] = int(bpos);
+  }
+  __syncthreads();
+  best = sh.ckey[0];
+  bpos = uint32_t(sh.cpos[0]);
+  int e1 = sh.cslot[0];
+#pragma unroll
+  for (int w = 1; w < WG / 64; ++w) {
+    if (key_pos_less(sh.ckey[w], uint32_t(sh.cpos[w]), best, bpos)) {
+      best = sh.ckey[w];
+      bpos = uint32_t(sh.cpos[w]);
+      e1 = sh.cslot[w];
+    }
+  }
+  return e1;
+}
+
+// The rows of units y, y + ny, y + 2 ny, ... of the scope: slot src -> dst.
+__device__ __forceinline__ void move_unit_rows_wg(const ScopeRows &r, int src, int dst, int y, int ny) {
+  copy_rows_wg(
+      (r.units - y + ny - 1) / ny, r.row_bytes / 16,
+      [&](int i, const char *&ks, const char *&vs) {
+        const int64_t off = ((r.row0 + int64_t(y + i * ny) * r.unit_stride) + src) * r.row_bytes;
+        ks = r.k + off;
+        vs = r.v + off;
+      },
+      [&](int i, char *&kd, char *&vd) {
+        const int64_t off = ((r.row0 + int64_t(y + i * ny) * r.unit_stride) + dst) * r.row_bytes;
+        kd = r.k + off;
+        vd = r.v + off;
+      });
+}
+
+// One workgroup per scope, or (gridDim.y > 1: a full step on multi-unit scopes
+// without moments) gridDim.y of them: workgroup y moves the rows of units y,
+// y + gridDim.y, ... into the evicted slot, and workgroup 0 does everything
+// else. The live length then comes from the score kernel's copy (steplen),
+// since workgroup 0 rewrites len while the others may still read it.
 template <typename T, int G>
 __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int scope = blockIdx.x;
   const int cap = a.capacity;
   const int64_t sc = int64_t(scope) * cap;
   const int row_bytes = HD * int(sizeof(T));
-  const int L = a.len[scope] + a.append;
+  const int ny = gridDim.y, y = blockIdx.y;
+  const int L = ny > 1 ? a.steplen[scope] : a.len[scope] + a.append;
+  if (y > 0) {   // the move of this workgroup's units, when one entry is evicted
+    if (L > cap || a.mode != 1 || L - a.budget != 1) return;
+    const int e = finish_pick(a, sh, scope, L);
+    if (e < L - 1) {
+      ScopeRows rows{a.k, a.v, int64_t(scope) * a.scope_stride, a.unit_stride, a.units, row_bytes,
+                     nullptr, a.pos + sc, nullptr};
+      move_unit_rows_wg(rows, L - 1, e, y, ny);
+    }
+    return;
+  }
   if (L > cap) {
     if (tid == 0) {
       a.status[0] = -4;
@@ -648,39 +724,7 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
   int32_t *list = a.list + sc;
   int e1 = -1;
   if (k == 1) {
-    // the lowest of the score chunks' keys
-    const int nch = (L + a.score_chunk - 1) / a.score_chunk;
-    uint64_t best = ~0ull;
-    uint32_t bpos = 0xffffffffu;
-    int bslot = 0x7fffffff;
-    for (int c = tid; c < nch; c += WG) {
-      const int64_t ci = int64_t(scope) * a.n_score_chunks + c;
-      const uint64_t key = a.cand_key[ci];
-      const uint32_t p = uint32_t(a.cand_pos[ci]);
-      if (key_pos_less(key, p, best, bpos)) {
-        best = key;
-        bpos = p;
-        bslot = a.cand_slot[ci];
-      }
-    }
-    wave_min_key_pos(best, bpos, bslot);
-    if (lane == 0) {
-      sh.ckey[wave] = best;
-      sh.cslot[wave] = bslot;
-      sh.cpos[wave] = int(bpos);
-    }
-    __syncthreads();
-    best = sh.ckey[0];
-    bpos = uint32_t(sh.cpos[0]);
-    e1 = sh.cslot[0];
-#pragma unroll
-    for (int w = 1; w < WG / 64; ++w) {
-      if (key_pos_less(sh.ckey[w], uint32_t(sh.cpos[w]), best, bpos)) {
-        best = sh.ckey[w];
-        bpos = uint32_t(sh.cpos[w]);
-        e1 = sh.cslot[w];
-      }
-    }
+    e1 = finish_pick(a, sh, scope, L);
     if (a.evict_out)
       for (int i = tid; i < L; i += WG) a.evict_out[sc + i] = (i == e1);
     if (tid == 0) list[0] = e1;
@@ -727,7 +771,18 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
   ScopeRows rows{a.k, a.v, int64_t(scope) * a.scope_stride, a.unit_stride, a.units, row_bytes,
                  a.votes ? a.votes + sc : nullptr, a.pos + sc, a.m + sc};
   if (k == 1) {
-    if (e1 < L - 1) move_slot_wg(rows, L - 1, e1);
+    if (e1 < L - 1) {
+      if (ny > 1) {
+        move_unit_rows_wg(rows, L - 1, e1, 0, ny);
+        if (tid == 0) {
+          if (rows.votes) rows.votes[e1] = rows.votes[L - 1];
+          rows.pos[e1] = rows.pos[L - 1];
+          if (rows.m) rows.m[e1] = rows.m[L - 1];
+        }
+      } else {
+        move_slot_wg(rows, L - 1, e1);
+      }
+    }
   } else {
     wg_compact_flags(rows, flags, L, k, a.list2 + sc, sh.fold.red);
   }

@@ -272,15 +272,56 @@ __device__ __forceinline__ void move_slot_thread(const ScopeRows &r, int src, in
   if (r.m) r.m[dst] = r.m[src];
 }
 
+// Copy the 16-byte vectors of one K row and one V row per unit with the whole
+// workgroup: vector i of unit u from (ksrc, vsrc)(u) to (kdst, vdst)(u), byte
+// offsets given per unit by the callables. Each thread issues up to COPY_BATCH
+// K and V loads before it stores any, so a copy over many units waits on memory
+// once per batch instead of once per vector.
+constexpr int COPY_BATCH = 8;
+template <class Src, class Dst>
+__device__ __forceinline__ void copy_rows_wg(int units, int nv, Src src, Dst dst) {
+  const int total = units * nv;
+  for (int base = 0; base < total; base += COPY_BATCH * WG) {
+    u32x4 kx[COPY_BATCH], vx[COPY_BATCH];
+#pragma unroll
+    for (int b = 0; b < COPY_BATCH; ++b) {
+      const int idx = base + b * WG + int(threadIdx.x);
+      if (idx < total) {
+        const int u = idx / nv, c = idx - (idx / nv) * nv;
+        const char *ks, *vs;
+        src(u, ks, vs);
+        kx[b] = ld16(ks + 16 * c);
+        vx[b] = ld16(vs + 16 * c);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < COPY_BATCH; ++b) {
+      const int idx = base + b * WG + int(threadIdx.x);
+      if (idx < total) {
+        const int u = idx / nv, c = idx - (idx / nv) * nv;
+        char *kd, *vd;
+        dst(u, kd, vd);
+        st16(kd + 16 * c, kx[b]);
+        st16(vd + 16 * c, vx[b]);
+      }
+    }
+  }
+}
+
 // Copy slot src -> dst with the whole workgroup (one pair of slots).
 __device__ __forceinline__ void move_slot_wg(const ScopeRows &r, int src, int dst) {
-  const int nv = r.row_bytes / 16;
-  for (int idx = threadIdx.x; idx < r.units * nv; idx += WG) {
-    const int u = idx / nv, c = idx - (idx / nv) * nv;
-    const int64_t base = (r.row0 + int64_t(u) * r.unit_stride) * r.row_bytes;
-    st16(r.k + base + int64_t(dst) * r.row_bytes + 16 * c, ld16(r.k + base + int64_t(src) * r.row_bytes + 16 * c));
-    st16(r.v + base + int64_t(dst) * r.row_bytes + 16 * c, ld16(r.v + base + int64_t(src) * r.row_bytes + 16 * c));
-  }
+  copy_rows_wg(
+      r.units, r.row_bytes / 16,
+      [&](int u, const char *&ks, const char *&vs) {
+        const int64_t off = ((r.row0 + int64_t(u) * r.unit_stride) + src) * r.row_bytes;
+        ks = r.k + off;
+        vs = r.v + off;
+      },
+      [&](int u, char *&kd, char *&vd) {
+        const int64_t off = ((r.row0 + int64_t(u) * r.unit_stride) + dst) * r.row_bytes;
+        kd = r.k + off;
+        vd = r.v + off;
+      });
   if (threadIdx.x == 0) {
     if (r.votes) r.votes[dst] = r.votes[src];
     r.pos[dst] = r.pos[src];
