@@ -294,6 +294,19 @@ def test_decode_step_c4_full_size_sampled(flags):
     assert rep.get("merged_rows_exact", 0) > 0
 
 
+@pytest.mark.parametrize("flags", [True, False])
+def test_merge_step_longer_than_the_launch_bound(flags):
+    """ZIP-merge steps on the split path with the device length (1001) past the live-length bound
+    the launch is sized for (max_len 600): the score kernel's workgroups cover the chunks past
+    their first as they go, and the merge kernels read the candidates past those they load at
+    entry (G = 8: 256-token chunks, 3 loaded of 4). Lockstep against the oracle, every scope."""
+    wl = C4.scaled(batch=1, n_kv=3, context=3000, budget=1000, steps=4, G=8)
+    run = DeviceRun(wl, flags=flags)
+    assert kvc.kvc_decode_plan(run.cache, wl.G, budget=wl.budget, merge=True, max_len=600) == kvc.PLAN_SPLIT
+    rep = lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)), merge=True, max_len_for_step=lambda t: 600)
+    _say("merge past the launch bound", flags, rep)
+
+
 def test_merge_step_that_merges_nothing():
     """Merge-mode steps on the split path that merge nothing (700 bf16 rows per scope): with the
     live length after the append at most the budget the token is appended and nothing merges;
