@@ -294,6 +294,20 @@ def test_decode_step_c4_full_size_sampled(flags):
     assert rep.get("merged_rows_exact", 0) > 0
 
 
+def test_step_longer_than_the_launch_bound():
+    """Full steps with moments on the split path whose device length (1001) passes the launch's
+    live-length bound (max_len 600): the per-head score kernel covers the chunks past each
+    workgroup's first as it goes and the finish reads the candidates past those it requests at
+    entry (G = 8: 256-token chunks, 3 requested of 4). The first step compresses 3000 -> 1000
+    with the bound unset. Lockstep against the oracle, every scope."""
+    wl = C2.scaled(context=3000, budget=1000, n_kv=4, G=8, moments=True, steps=4)
+    run = DeviceRun(wl)
+    assert kvc.kvc_decode_plan(run.cache, wl.G, budget=wl.budget, max_len=600) == kvc.PLAN_SPLIT
+    rep = lockstep(run, wl.steps, lambda t: list(range(wl.n_scopes)),
+                   max_len_for_step=lambda t: None if t == 1 else 600)
+    _say("step past the launch bound", rep)
+
+
 @pytest.mark.parametrize("flags", [True, False])
 def test_merge_step_longer_than_the_launch_bound(flags):
     """ZIP-merge steps on the split path with the device length (1001) past the live-length bound
