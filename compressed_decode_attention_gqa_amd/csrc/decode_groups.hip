@@ -57,7 +57,7 @@ __global__ __launch_bounds__(HD) void k_groups_combine(const GroupsArgs a) {
   for (int g = 0; g < G; ++g) {
     float acc = 0.f;
     for (int sp = 0; sp < ns; ++sp) acc = fmaf(a.partO[((pb + sp) * G + g) * HD + tid], float(wgt[g][sp]), acc);
-    a.out[(int64_t(gu) * G + g) * HD + tid] = acc;
+    st_nt(&a.out[(int64_t(gu) * G + g) * HD + tid], acc);
   }
   // M and 1/Z for the score kernel, over split 0's partials (every read of them is above the barrier)
   if (tid < G) {
@@ -149,10 +149,10 @@ __global__ __launch_bounds__(WG) void k_groups_score(const GroupsArgs a) {
       const double pv = a.votes ? double(a.votes[sc + i]) : 1.0;
       t *= pv;
       l *= pv;
-      const double mo = double(a.m[sc + i]);
+      const double mo = double(ld_nt(&a.m[sc + i]));
       const double mv = a.rule == 0 ? l : a.rule == 1 ? mo + t : pow(alpha, double(n)) * mo + t;
-      a.m[sc + i] = float(mv);
-      if (a.s) a.s[sc + i] = float(l);
+      st_nt(&a.m[sc + i], float(mv));
+      if (a.s) st_nt(&a.s[sc + i], float(l));
     }
   }
 }
@@ -204,10 +204,10 @@ __global__ __launch_bounds__(WG) void k_groups_wscore(const GroupsArgs a, int G)
         t += red_t[p][tok];
         l += red_l[p][tok];
       }
-      const double mo = double(a.m[sc + i]);
+      const double mo = double(ld_nt(&a.m[sc + i]));
       const double mv = a.rule == 0 ? l : a.rule == 1 ? mo + t : pow(alpha, double(n)) * mo + t;
-      a.m[sc + i] = float(mv);
-      if (a.s) a.s[sc + i] = float(l);
+      st_nt(&a.m[sc + i], float(mv));
+      if (a.s) st_nt(&a.s[sc + i], float(l));
     }
   }
 }

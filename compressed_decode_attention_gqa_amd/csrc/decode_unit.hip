@@ -431,7 +431,7 @@ void k_decode_unit(const StepArgs a) {
   if (fold) {
     const float4 *S4 = reinterpret_cast<const float4 *>(a.mom_S + mu * HD * HD);
 #pragma unroll
-    for (int j = 0; j < Geo::NS4; ++j) Sreg[j] = S4[tid + NT * j];
+    for (int j = 0; j < Geo::NS4; ++j) Sreg[j] = ld_nt4(S4 + tid + NT * j);
     if (tid < 2 * HD) skv = tid < HD ? a.mom_sk[mu * HD + tid] : a.mom_sv[mu * HD + tid - HD];
   }
   // the last live row (the appended one when appending): one 16-byte vector per
@@ -511,7 +511,7 @@ void k_decode_unit(const StepArgs a) {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) acc = fmaf(sh.ep.pO[w][g][e], sh.ep.fac[w][g], acc);
-    a.out[(int64_t(gu) * G + g) * HD + e] = acc;
+    st_nt(&a.out[(int64_t(gu) * G + g) * HD + e], acc);
   }
 
   const bool score = a.refresh && (step || a.s != nullptr);
@@ -522,7 +522,7 @@ void k_decode_unit(const StepArgs a) {
       double *wrow = a.wsum + int64_t(gu) * a.wsum_stride;
       for (int i = tid; i < L; i += NT) {
         const double acc = token_score<G>(e_lds, f_lds, s_lds, i, i / CHW);
-        wrow[i] = VOTES ? acc * double(v_lds[i]) : acc;
+        st_nt(&wrow[i], VOTES ? acc * double(v_lds[i]) : acc);
       }
     }
     return;
@@ -542,10 +542,10 @@ void k_decode_unit(const StepArgs a) {
       double acc = token_score<G>(e_lds, f_lds, s_lds, i, i / CHW);
       if (VOTES && !isnew) acc *= double(v_lds[i]);
       const double sv = acc * inv_heads;
-      if (a.s) a.s[sc + i] = float(sv);
+      if (a.s) st_nt(&a.s[sc + i], float(sv));
       if (step) mval = apply_rule(a.rule, alpha, mval, sv);
     }
-    if ((step && score) || isnew) a.m[sc + i] = float(mval);
+    if ((step && score) || isnew) st_nt(&a.m[sc + i], float(mval));
     m_lds[i] = mval;
     const uint64_t om = orderable_f64(mval);
     if (om < bestm) {
@@ -663,10 +663,10 @@ void k_decode_unit(const StepArgs a) {
       x.y = fmaf(va, k4.y, x.y);
       x.z = fmaf(va, k4.z, x.z);
       x.w = fmaf(va, k4.w, x.w);
-      S4[tid + NT * j] = x;
+      st_nt4(S4 + tid + NT * j, x);
     }
-    if (tid < HD) a.mom_sk[mu * HD + tid] = skv + sh.ep.rowk[tid];
-    else if (tid < 2 * HD) a.mom_sv[mu * HD + tid - HD] = skv + sh.ep.rowv[tid - HD];
+    if (tid < HD) st_nt(&a.mom_sk[mu * HD + tid], skv + sh.ep.rowk[tid]);
+    else if (tid < 2 * HD) st_nt(&a.mom_sv[mu * HD + tid - HD], skv + sh.ep.rowv[tid - HD]);
     if (tid == 0) a.mom_n[mu] += 1;
   }
   if (a.mode == 2) {

@@ -82,6 +82,24 @@ __device__ __forceinline__ u32x4 ld16g(const void *p) {
 }
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// Non-temporal accesses, for results a kernel writes once at its end (scores,
+// utilities, outputs) and for the moment sums it reads and rewrites there: on
+// gfx950 these lines do not stay in the XCD's L2 as ordinary dirty lines, so the
+// L2 write-back that ends every kernel has little left to write. (Loads that a
+// latency-bound kernel waits on stay ordinary: non-temporal ones took longer.)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt(double *p, double v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st_nt4(float4 *p, const float4 &v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ float ld_nt(const float *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 ld_nt4(const float4 *p) {
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
 // ---------------------------------------------------------------- cross-lane
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
