@@ -571,7 +571,15 @@ __device__ void epi_score_head(const StepArgs &a, ScoreLds &sh) {
           st16(a.v + arow + 16 * tid, av);
         }
       } else {
-        append_rows_wg(a, scope, L);
+        // one vector at a time: the batched copy's registers would be allocated for the
+        // whole kernel, and this path (a later chunk, or several units) is rare here
+        for (int idx = tid; idx < a.units * nv; idx += WG) {
+          const int u = idx / nv, c = idx - (idx / nv) * nv;
+          const int64_t row = (int64_t(scope) * a.scope_stride + int64_t(u) * a.unit_stride + (L - 1)) * a.row_bytes;
+          const int64_t src = (int64_t(scope) * a.units + u) * a.row_bytes;
+          st16(a.k + row + 16 * c, ld16(a.k_new + src + 16 * c));
+          st16(a.v + row + 16 * c, ld16(a.v_new + src + 16 * c));
+        }
       }
       if (tid == 0) {
         if (a.votes) a.votes[sc + L - 1] = 1;
