@@ -267,22 +267,31 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
 }
 
 // ---------------------------------------------------------------- epilogue launches
+// The per-head score and finish kernels (one attention unit and one unit per scope,
+// chosen on the host from the same launch arguments) are separate kernels, so they
+// carry none of the general kernels' code for several units.
 template <int G, int CH>
 __global__ __launch_bounds__(WG) void k_epi_score(const StepArgs a) {
   __shared__ ScoreLds sh;
-  if (a.attn_units == 1 && a.units == 1 && a.score_chunk <= (8 / G) * WG)
-    epi_score_head<G, CH>(a, sh);
-  else
-    epi_score<G, CH>(a, sh);
+  epi_score<G, CH>(a, sh);
+}
+
+template <int G, int CH>
+__global__ __launch_bounds__(WG) void k_epi_score_head(const StepArgs a) {
+  __shared__ ScoreLds sh;
+  epi_score_head<G, CH>(a, sh);
 }
 
 template <typename T, int G>
 __global__ __launch_bounds__(WG) void k_epi_finish(const StepArgs a) {
   __shared__ EpiLds sh;
-  if (a.units == 1 && a.mode == 1)
-    epi_finish_head<T, G>(a, sh);
-  else
-    epi_finish<T, G>(a, sh);
+  epi_finish<T, G>(a, sh);
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(WG) void k_epi_finish_head(const StepArgs a) {
+  __shared__ EpiLds sh;
+  epi_finish_head<T, G>(a, sh);
 }
 
 template <typename T, int G>
@@ -292,14 +301,22 @@ static hipError_t launch_split_tg(const StepArgs &a, hipStream_t st) {
   if (a.votes) hipLaunchKernelGGL((k_decode_split<T, G, true>), grid, dim3(Geo::NT), 0, st, a);
   else hipLaunchKernelGGL((k_decode_split<T, G, false>), grid, dim3(Geo::NT), 0, st, a);
   const int chunks = std::max(1, std::min(a.n_score_chunks, (a.max_len + a.score_chunk - 1) / a.score_chunk));
-  hipLaunchKernelGGL((k_epi_score<G, Geo::CHW>), dim3(chunks, a.n_scopes), dim3(WG), 0, st, a);
+  if (a.attn_units == 1 && a.units == 1 && a.score_chunk <= (8 / G) * WG)
+    hipLaunchKernelGGL((k_epi_score_head<G, Geo::CHW>), dim3(chunks, a.n_scopes), dim3(WG), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_epi_score<G, Geo::CHW>), dim3(chunks, a.n_scopes), dim3(WG), 0, st, a);
   // the finish kernel selects, folds and moves; a call that cannot evict (budget >= capacity),
   // appends nothing and reports no flags has nothing for it to do
   const bool finish = !a.merge_select &&
                       (a.append || a.mode == 2 || a.evict_out || a.bulk || (a.mode != 0 && a.budget < a.capacity));
   // (several finish workgroups per scope only with the score kernel's length copy)
   const int fin_blocks = a.steplen ? std::max(1, a.fin_blocks) : 1;
-  if (finish) hipLaunchKernelGGL((k_epi_finish<T, G>), dim3(a.n_scopes, fin_blocks), dim3(WG), 0, st, a);
+  if (finish) {
+    if (a.units == 1 && a.mode == 1)
+      hipLaunchKernelGGL((k_epi_finish_head<T, G>), dim3(a.n_scopes), dim3(WG), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_epi_finish<T, G>), dim3(a.n_scopes, fin_blocks), dim3(WG), 0, st, a);
+  }
   return hipGetLastError();
 }
 

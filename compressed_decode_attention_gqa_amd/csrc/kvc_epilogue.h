@@ -654,14 +654,16 @@ __device__ __forceinline__ void move_unit_rows_wg(const ScopeRows &r, int src, i
 // y + gridDim.y, ... into the evicted slot, and workgroup 0 does everything
 // else. The live length then comes from the score kernel's copy (steplen),
 // since workgroup 0 rewrites len while the others may still read it.
-template <typename T, int G>
+// MULTI false: one workgroup per scope and one unit per scope (the per-head
+// finish kernel's fallback), without the code for several units.
+template <typename T, int G, bool MULTI = true>
 __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
   const int tid = threadIdx.x;
   const int scope = blockIdx.x;
   const int cap = a.capacity;
   const int64_t sc = int64_t(scope) * cap;
   const int row_bytes = HD * int(sizeof(T));
-  const int ny = gridDim.y, y = blockIdx.y;
+  const int ny = MULTI ? int(gridDim.y) : 1, y = MULTI ? int(blockIdx.y) : 0;
   const int L = ny > 1 ? a.steplen[scope] : a.len[scope] + a.append;
   if (y > 0) {   // the move of this workgroup's units, when one entry is evicted
     if (L > cap || a.mode != 1 || L - a.budget != 1) return;
@@ -787,8 +789,10 @@ __device__ void epi_finish(const StepArgs &a, EpiLds &sh) {
           rows.pos[e1] = rows.pos[L - 1];
           if (rows.m) rows.m[e1] = rows.m[L - 1];
         }
-      } else {
+      } else if (MULTI) {
         move_slot_wg(rows, L - 1, e1);
+      } else {
+        move_slot_wg<1>(rows, L - 1, e1);
       }
     }
   } else {
@@ -835,7 +839,7 @@ __device__ void epi_finish_head(const StepArgs &a, EpiLds &sh) {
   }
   const int L = a.len[scope] + a.append;
   if (L > cap || L - a.budget != 1 || a.mode != 1 || (a.bulk && L - a.budget > 1)) {
-    epi_finish<T, G>(a, sh);
+    epi_finish<T, G, false>(a, sh);
     return;
   }
   const char *Kb = a.k + int64_t(scope) * a.scope_stride * RB;

@@ -278,8 +278,9 @@ __device__ __forceinline__ void move_slot_thread(const ScopeRows &r, int src, in
 // K and V loads before it stores any, so a copy over many units waits on memory
 // once per batch instead of once per vector.
 constexpr int COPY_BATCH = 8;
-template <class Src, class Dst>
+template <int BATCH = COPY_BATCH, class Src, class Dst>
 __device__ __forceinline__ void copy_rows_wg(int units, int nv, Src src, Dst dst) {
+  constexpr int COPY_BATCH = BATCH;
   const int total = units * nv;
   for (int base = 0; base < total; base += COPY_BATCH * WG) {
     u32x4 kx[COPY_BATCH], vx[COPY_BATCH];
@@ -309,8 +310,9 @@ __device__ __forceinline__ void copy_rows_wg(int units, int nv, Src src, Dst dst
 }
 
 // Copy slot src -> dst with the whole workgroup (one pair of slots).
+template <int BATCH = COPY_BATCH>
 __device__ __forceinline__ void move_slot_wg(const ScopeRows &r, int src, int dst) {
-  copy_rows_wg(
+  copy_rows_wg<BATCH>(
       r.units, r.row_bytes / 16,
       [&](int u, const char *&ks, const char *&vs) {
         const int64_t off = ((r.row0 + int64_t(u) * r.unit_stride) + src) * r.row_bytes;
