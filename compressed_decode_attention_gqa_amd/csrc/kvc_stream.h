@@ -74,9 +74,14 @@ struct UnitStream {
         vp[it] = Vb;
       }
     }
+    // In the per-scope kernel (MROW) the key rows load non-temporally: the memory-side
+    // cache then keeps the value rows, about half of a step's bytes, which fit in it, and
+    // the next step (walking the other way) finds them there; with every row allocating,
+    // each step's rows evicted the ones the next step reads first.
 #pragma unroll
     for (int it = 0; it < UNR; ++it) {
-      kr[it] = ld16g(kp[it]);
+      if constexpr (MROW) kr[it] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(kp[it]));
+      else kr[it] = ld16g(kp[it]);
       vr[it] = ld16g(vp[it]);
     }
   }
