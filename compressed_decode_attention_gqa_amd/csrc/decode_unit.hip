@@ -215,7 +215,12 @@ void k_decode_unit(const StepArgs a) {
   if (overflow) L = 0;
   const int Lold = L - (L > 0 ? a.append : 0);
 
-  UnitStream<T, VOTES, !GRP> W;
+  // Key rows load non-temporally: for a per-scope step the memory-side cache then keeps
+  // the value rows, about half of a step's bytes, which fit in it, and the next step
+  // (walking the other way) finds them there (with every row allocating, each step's rows
+  // evicted the ones the next step reads first). A groups call streams every later layer
+  // of a model once, far more than that cache holds: none of its rows allocates.
+  UnitStream<T, VOTES, !GRP, true, GRP> W;
   {
     const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(unit) * a.unit_stride;
     W.Kb = a.k + row0 * RB;

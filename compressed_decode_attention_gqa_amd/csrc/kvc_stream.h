@@ -28,8 +28,8 @@ struct UnitGeometry {
 };
 
 // Loads of one sub-chunk: K and V rows, and (MROW) the per-token utility and
-// (VOTES) the vote.
-template <typename T, bool VOTES, bool MROW = true>
+// (VOTES) the vote. NTK, NTV: the key or value rows load non-temporally.
+template <typename T, bool VOTES, bool MROW = true, bool NTK = false, bool NTV = false>
 struct UnitStream {
   using Geo = UnitGeometry<T, 1>;
   static constexpr int UNR = Geo::UNR, TPI = Geo::TPI, CHW = Geo::CHW, RB = Geo::RB;
@@ -74,15 +74,12 @@ struct UnitStream {
         vp[it] = Vb;
       }
     }
-    // In the per-scope kernel (MROW) the key rows load non-temporally: the memory-side
-    // cache then keeps the value rows, about half of a step's bytes, which fit in it, and
-    // the next step (walking the other way) finds them there; with every row allocating,
-    // each step's rows evicted the ones the next step reads first.
 #pragma unroll
     for (int it = 0; it < UNR; ++it) {
-      if constexpr (MROW) kr[it] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(kp[it]));
+      if constexpr (NTK) kr[it] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(kp[it]));
       else kr[it] = ld16g(kp[it]);
-      vr[it] = ld16g(vp[it]);
+      if constexpr (NTV) vr[it] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(vp[it]));
+      else vr[it] = ld16g(vp[it]);
     }
   }
 };
