@@ -457,8 +457,9 @@ __device__ __forceinline__ void mf_load(u32x4 (&rk)[2], u32x4 (&rv)[2], const ch
   for (int h = 0; h < 2; ++h) {
     const int q = threadIdx.x + WG * h, e = q >> 4, c = q & 15;
     const int64_t off = int64_t(slots[e0 + (e < ne ? e : 0)]) * (HD * 2) + 16 * c;
-    rk[h] = ld16(Kb + off);
-    rv[h] = ld16(Vb + off);
+    // read once (the evicted rows of a whole prompt): non-temporal
+    rk[h] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(Kb + off));
+    rv[h] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4 *)(Vb + off));
   }
 }
 

@@ -46,7 +46,10 @@ struct SplitLds {
   };
 };
 
-template <typename T, int G, bool VOTES>
+// NTL: the rows load non-temporally (the bulk first step streams the whole prompt once,
+// far more than any cache holds; a steady step's keys stay cached for the ZIP merge's
+// cosine pass, which re-reads them).
+template <typename T, int G, bool VOTES, bool NTL = false>
 __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(const StepArgs a) {
   using TR = ElemTraits<T>;
   using Geo = UnitGeometry<T, G>;
@@ -67,7 +70,7 @@ __global__ __launch_bounds__((UnitGeometry<T, G>::NT), 1) void k_decode_split(co
   if (L > cap) L = 0;   // reported by the epilogue
   const int Lold = L - (L > 0 ? a.append : 0);
 
-  UnitStream<T, VOTES, false> W;
+  UnitStream<T, VOTES, false, NTL, NTL> W;
   {
     const int64_t row0 = int64_t(scope) * a.scope_stride + int64_t(unit) * a.unit_stride;
     W.Kb = a.k + row0 * RB;
@@ -298,8 +301,13 @@ template <typename T, int G>
 static hipError_t launch_split_tg(const StepArgs &a, hipStream_t st) {
   using Geo = UnitGeometry<T, G>;
   const dim3 grid(a.n_splits, a.n_scopes * a.attn_units);
-  if (a.votes) hipLaunchKernelGGL((k_decode_split<T, G, true>), grid, dim3(Geo::NT), 0, st, a);
-  else hipLaunchKernelGGL((k_decode_split<T, G, false>), grid, dim3(Geo::NT), 0, st, a);
+  if (a.bulk) {
+    if (a.votes) hipLaunchKernelGGL((k_decode_split<T, G, true, true>), grid, dim3(Geo::NT), 0, st, a);
+    else hipLaunchKernelGGL((k_decode_split<T, G, false, true>), grid, dim3(Geo::NT), 0, st, a);
+  } else {
+    if (a.votes) hipLaunchKernelGGL((k_decode_split<T, G, true>), grid, dim3(Geo::NT), 0, st, a);
+    else hipLaunchKernelGGL((k_decode_split<T, G, false>), grid, dim3(Geo::NT), 0, st, a);
+  }
   const int chunks = std::max(1, std::min(a.n_score_chunks, (a.max_len + a.score_chunk - 1) / a.score_chunk));
   if (a.attn_units == 1 && a.units == 1 && a.score_chunk <= (8 / G) * WG)
     hipLaunchKernelGGL((k_epi_score_head<G, Geo::CHW>), dim3(chunks, a.n_scopes), dim3(WG), 0, st, a);
